@@ -1,0 +1,293 @@
+"""Pins of the fp64 oracle to facts fixed outside itself (CPU only).
+
+Each test ties one oracle function to a closed form, an invariant, a brute-force
+construction or a hand-derived fixture (tests/golden/), chosen so that a plausible
+slip (a transposed factor, a dropped 1/2, a wrong vec order, a wrong tie-break) fails.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.conftest import read_golden
+
+RNG = np.random.default_rng(20260602)
+
+
+def _spd_stream(n, d, exponent, rng):
+    q, r = np.linalg.qr(rng.standard_normal((d, d)))
+    q = q * np.sign(np.diag(r))
+    lam = np.arange(1, d + 1, dtype=np.float64) ** (-exponent)
+    return (rng.standard_normal((n, d)) * np.sqrt(lam)) @ q.T
+
+
+# --------------------------------------------------------------------------- QAW
+def test_qaw_golden_rows():
+    for line in read_golden("qaw_rows.txt"):
+        parts = dict(p.strip().split(":", 1) for p in line.split("|"))
+        a = np.array([float(v) for v in parts["a"].split()], dtype=np.float32)[None, :]
+        q, s, ah = oracle.qaw_fake_quant(a)
+        assert s[0] == np.float32(float(parts["s"]))
+        assert q[0].tolist() == [int(v) for v in parts["q"].split()]
+        assert ah[0].tolist() == [float(v) for v in parts["ahat"].split()]
+
+
+def test_qaw_invariants():
+    a = (RNG.standard_normal((64, 37)) * np.exp(RNG.standard_normal((64, 1)))).astype(np.float32)
+    a[5] = 0.0
+    q, s, ah = oracle.qaw_fake_quant(a)
+    assert q.dtype == np.int8 and np.all(np.abs(q.astype(int)) <= 127)
+    nz = np.any(a != 0, axis=1)
+    assert np.all(np.max(np.abs(q[nz].astype(int)), axis=1) == 127)
+    assert np.all(q[~nz] == 0) and np.all(ah[~nz] == 0)
+    # |a_hat - a| <= s/2 up to the fp32 roundings of a/s and q*s
+    err = np.abs(ah.astype(np.float64) - a.astype(np.float64))
+    bound = s[:, None].astype(np.float64) * (0.5 + 1e-5) + 1e-6 * np.abs(a)
+    assert np.all(err <= bound)
+
+
+# --------------------------------------------------------------------------- covariance
+def test_covariance_is_mean_outer_product():
+    a = RNG.standard_normal((7, 4)).astype(np.float32)
+    brute = np.zeros((4, 4))
+    for t in range(7):
+        v = a[t].astype(np.float64)
+        for i in range(4):
+            for j in range(4):
+                brute[i, j] += v[i] * v[j]
+    np.testing.assert_allclose(oracle.covariance(a), brute / 7, rtol=1e-14, atol=1e-15)
+    # chunked aggregation (Swift-SVD 2A) equals one-shot
+    np.testing.assert_allclose(oracle.covariance_sum(a, block=3), brute, rtol=1e-14, atol=1e-14)
+
+
+# --------------------------------------------------------------------------- Cholesky
+def test_cholesky_golden():
+    g = {ln.split(":")[0]: ln.split(":", 1)[1] for ln in read_golden("cholesky_cases.txt")}
+
+    def mat(txt):
+        return np.array([[float(v) for v in row.split()] for row in txt.split(";")])
+
+    l, info = oracle.cholesky_lower(mat(g["pd_x"]))
+    assert info == 0
+    np.testing.assert_allclose(l, mat(g["pd_l"]), atol=1e-15)
+    _, info = oracle.cholesky_lower(mat(g["notpd_x"]))
+    assert info == int(g["notpd_info"])
+
+
+def test_cholesky_reconstructs():
+    x = oracle.covariance(RNG.standard_normal((50, 9)))
+    l, info = oracle.cholesky_lower(x)
+    assert info == 0 and np.allclose(np.triu(l, 1), 0)
+    np.testing.assert_allclose(l @ l.T, x, rtol=1e-13, atol=1e-14)
+
+
+# --------------------------------------------------------------------------- decomposition
+@pytest.mark.parametrize("shape", [(6, 6), (5, 8), (8, 3)])
+def test_identity_whitening_is_plain_truncated_svd(shape):
+    """X = G = I: the method reduces to a plain truncated SVD of W, and Eckart-Young
+    (named by UniRank 2.1) fixes the truncation error."""
+    d_out, d_in = shape
+    w = RNG.standard_normal(shape)
+    r = 2
+    res = oracle.whiten_decompose(w, np.eye(d_in), 1, np.eye(d_out), 1, rank=r)
+    # singular values from a different route: symmetric eigenvalues of W^T W
+    ev = np.sort(np.linalg.eigvalsh(w.T @ w))[::-1][: min(shape)]
+    np.testing.assert_allclose(res["sigma"] ** 2, np.maximum(ev, 0), rtol=1e-10, atol=1e-12)
+    wr = res["left"] @ res["right"]
+    assert np.linalg.matrix_rank(wr, tol=1e-9) == r
+    np.testing.assert_allclose(np.linalg.norm(w - wr) ** 2, np.sum(res["sigma"][r:] ** 2), rtol=1e-10)
+
+
+@pytest.mark.parametrize("d_out,d_in,r", [(3, 2, 1), (2, 4, 1), (4, 4, 2), (3, 5, 2), (2, 2, 0)])
+def test_kfac_loss_equals_discarded_whitened_energy_bruteforce(d_out, d_in, r):
+    """LASER Methodology 1: with the K-FAC surrogate 1/2 vec(dW)^T (G kron X) vec(dW),
+    truncating the SVD of the whitened weight costs 1/2 * sum of the discarded
+    sigma_tilde^2.  The Kronecker product is built explicitly (d_in*d_out <= 20)."""
+    a = _spd_stream(300, d_in, 1.0, RNG)
+    b = _spd_stream(300, d_out, 1.3, RNG)
+    w = RNG.standard_normal((d_out, d_in))
+    xs, gs = oracle.covariance_sum(a), oracle.covariance_sum(b)
+    res = oracle.whiten_decompose(w, xs, 300, gs, 300, rank=r)
+    x, g = xs / 300, gs / 300
+    dw = w - (res["left"] @ res["right"] if r else 0.0)
+    loss = oracle.kfac_loss(dw, x, g)
+    np.testing.assert_allclose(loss, 0.5 * np.sum(res["sigma"][r:] ** 2), rtol=1e-10)
+    # dropping one component alone costs exactly its K-FAC score 1/2 sigma_i^2
+    full = oracle.whiten_decompose(w, xs, 300, gs, 300, rank=min(d_out, d_in))
+    for i in range(min(d_out, d_in)):
+        comp = np.outer(full["left"][:, i], full["right"][i])
+        np.testing.assert_allclose(oracle.kfac_loss(comp, x, g), oracle.kfac_scores(full["sigma"])[i],
+                                   rtol=1e-9)
+
+
+def test_kfac_loss_orientation_would_catch_swap():
+    """A swapped whitening (L_x on the left side) must not satisfy the identity: this
+    keeps the brute-force pin sensitive to the orientation reading."""
+    d_out, d_in = 3, 3
+    a = _spd_stream(200, d_in, 1.0, RNG)
+    b = _spd_stream(200, d_out, 1.3, RNG)
+    w = RNG.standard_normal((d_out, d_in))
+    x, g = oracle.covariance(a), oracle.covariance(b)
+    lx, _ = oracle.cholesky_lower(x)
+    lg, _ = oracle.cholesky_lower(g)
+    wrong = lx.T @ w @ lg
+    u, s, vt = np.linalg.svd(wrong)
+    wr = np.linalg.solve(lx.T, u[:, :1] * s[:1]) @ np.linalg.solve(lg.T, vt[:1].T).T
+    assert abs(oracle.kfac_loss(w - wr, x, g) - 0.5 * np.sum(s[1:] ** 2)) > 1e-6
+
+
+def test_swift_svd_closed_form_and_optimality():
+    """Swift-SVD 2A: with G = I, the optimum of ||A W^T - A W_k^T|| is W V_k V_k^T in the
+    pages' orientation, V_k the top-k eigenvectors of the aggregated output covariance
+    C = sum_t y_t^T y_t; its loss is the discarded eigen-energy (the theoretical
+    minimum), and no other rank-k weight does better."""
+    n, d_out, d_in, r = 400, 6, 7, 3
+    a = _spd_stream(n, d_in, 1.2, RNG)
+    w = RNG.standard_normal((d_out, d_in))
+    res = oracle.whiten_decompose(w, oracle.covariance_sum(a), n, None, None, rank=r)
+    y = a @ w.T                              # outputs, tokens x d_out
+    c = np.zeros((d_out, d_out))
+    for t0 in range(0, n, 64):               # incremental aggregation
+        c += y[t0:t0 + 64].T @ y[t0:t0 + 64]
+    ev, evec = np.linalg.eigh(c)
+    ev, evec = ev[::-1], evec[:, ::-1]
+    np.testing.assert_allclose(ev[: min(d_out, d_in)] / n, res["sigma"] ** 2, rtol=1e-10)
+    wk = evec[:, :r] @ evec[:, :r].T @ w
+    wr = res["left"] @ res["right"]
+    np.testing.assert_allclose(wr, wk, rtol=1e-8, atol=1e-10)
+    loss = np.linalg.norm(y - a @ wr.T) ** 2
+    np.testing.assert_allclose(loss, n * np.sum(res["sigma"][r:] ** 2), rtol=1e-9)
+    for _ in range(20):
+        w2 = RNG.standard_normal((d_out, r)) @ RNG.standard_normal((r, d_in))
+        assert np.linalg.norm(y - a @ w2.T) ** 2 >= loss * (1 - 1e-12)
+
+
+@pytest.mark.parametrize("d_out,d_in", [(5, 7), (7, 5), (6, 6)])
+def test_back_map_invariants(d_out, d_in):
+    """The back-mapped factors are G- and X-orthogonal with the singular values on the
+    diagonal, and whiten back to the truncated whitened SVD."""
+    a = _spd_stream(500, d_in, 1.1, RNG)
+    b = _spd_stream(500, d_out, 1.4, RNG)
+    w = RNG.standard_normal((d_out, d_in))
+    r = 3
+    res = oracle.whiten_decompose(w, oracle.covariance_sum(a), 500, oracle.covariance_sum(b), 500, rank=r)
+    x, g = oracle.covariance(a), oracle.covariance(b)
+    left, right, s = res["left"], res["right"], res["sigma"]
+    np.testing.assert_allclose(left.T @ g @ left, np.diag(s[:r]), rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(right @ x @ right.T, np.diag(s[:r]), rtol=1e-9, atol=1e-11)
+    lx, lg = res["lx"], res["lg"]
+    wt_r = lg.T @ (left @ right) @ lx
+    u, vt = res["u"], res["vt"]
+    np.testing.assert_allclose(wt_r, (u[:, :r] * s[:r]) @ vt[:r], rtol=1e-9, atol=1e-11)
+
+
+def test_canonical_signs_rule():
+    w = RNG.standard_normal((4, 6))
+    res = oracle.whiten_decompose(w, None, None, None, None, rank=4)
+    for i in range(4):
+        v = res["u"][:, i]
+        assert v[np.argmax(np.abs(v))] > 0
+    res = oracle.whiten_decompose(w.T.copy(), None, None, None, None, rank=4)
+    for i in range(4):
+        v = res["vt"][i]
+        assert v[np.argmax(np.abs(v))] > 0
+
+
+def test_cholesky_failure_reported_not_patched():
+    a = RNG.standard_normal((3, 5))      # 3 tokens, 5 channels: X is singular
+    res = oracle.whiten_decompose(RNG.standard_normal((4, 5)), oracle.covariance_sum(a), 3, rank=1)
+    assert res["info"] > 0 and res["info_side"] == "x" and "sigma" not in res
+
+
+# --------------------------------------------------------------------------- scores
+@pytest.mark.parametrize("d_out,d_in", [(2, 3), (3, 2), (2, 2)])
+def test_fisher_score_equals_empirical_fisher_quadratic_bruteforce(d_out, d_in):
+    """LASER Methodology 2: the score is the component's contribution to the
+    empirical-Fisher quadratic 1/2 vec(D)^T F vec(D), F = mean_t g_t g_t^T with the
+    per-token gradient g_t = vec(b_t a_t^T).  F is built explicitly."""
+    n = 40
+    a = RNG.standard_normal((n, d_in))
+    b = RNG.standard_normal((n, d_out))
+    w = RNG.standard_normal((d_out, d_in))
+    res = oracle.whiten_decompose(w, oracle.covariance_sum(a), n, oracle.covariance_sum(b), n)
+    k = min(d_out, d_in)
+    f = np.zeros((d_out * d_in, d_out * d_in))
+    for t in range(n):
+        gt = np.outer(b[t], a[t]).reshape(-1)
+        f += np.outer(gt, gt)
+    f /= n
+    want = []
+    for i in range(k):
+        dlt = np.outer(res["left"][:, i], res["right"][i]).reshape(-1)
+        want.append(0.5 * dlt @ f @ dlt)
+    np.testing.assert_allclose(oracle.fisher_scores(a, b, res["left"], res["right"]), want, rtol=1e-10)
+
+
+def test_fisher_score_expectation_is_kfac_score():
+    """With independent Gaussian activations and gradients the empirical-Fisher score
+    of component i concentrates on the K-FAC score 1/2 sigma_i^2 (the empirical-Fisher
+    quadratic factorises in expectation into G kron X)."""
+    n, d_out, d_in = 60000, 5, 4
+    a = _spd_stream(n, d_in, 1.0, RNG)
+    b = _spd_stream(n, d_out, 1.5, RNG)
+    w = RNG.standard_normal((d_out, d_in))
+    res = oracle.whiten_decompose(w, oracle.covariance_sum(a), n, oracle.covariance_sum(b), n)
+    ratio = oracle.fisher_scores(a, b, res["left"], res["right"]) / oracle.kfac_scores(res["sigma"])
+    assert np.all(np.abs(ratio - 1) < 0.1), ratio
+
+
+# --------------------------------------------------------------------------- allocation
+def test_allocate_golden():
+    g = {ln.split(":")[0]: ln.split(":", 1)[1].split() for ln in read_golden("alloc_example.txt")}
+    costs = [int(v) for v in g["costs"]]
+    scores = [np.array([float(v) for v in g["scores0"]], np.float32),
+              np.array([float(v) for v in g["scores1"]], np.float32)]
+    order, n_kept, ranks, kept = oracle.allocate(scores, costs, int(g["budget"][0]))
+    assert order.tolist() == [int(v) for v in g["order"]]
+    assert n_kept == int(g["n_kept"][0])
+    assert ranks.tolist() == [int(v) for v in g["ranks"]]
+    assert kept.tolist() == [int(v) for v in g["kept_mask"]]
+
+
+def test_allocate_invariants_random():
+    for trial in range(30):
+        nm = int(RNG.integers(1, 5))
+        costs = [int(c) for c in RNG.integers(3, 12, nm)]
+        scores = []
+        for m in range(nm):
+            s = RNG.choice([0.5, 1.0, 2.0, 3.0], size=int(RNG.integers(1, 6))).astype(np.float32)
+            scores.append(s * np.float32(costs[m]) / np.float32(4.0))   # many exact ties
+        tot = sum(c * len(s) for c, s in zip(costs, scores))
+        budget = int(RNG.integers(0, tot + 5))
+        order, n_kept, ranks, kept = oracle.allocate(scores, costs, budget)
+        mat = np.concatenate([[m] * len(s) for m, s in enumerate(scores)]).astype(int)
+        idx = np.concatenate([np.arange(len(s)) for s in scores]).astype(int)
+        key = np.concatenate([s.astype(np.float64) / c for s, c in zip(scores, costs)])
+        cost = np.array([costs[m] for m in mat])
+        assert sorted(order.tolist()) == list(range(len(mat)))
+        for p, q in zip(order[:-1], order[1:]):
+            assert (key[p] > key[q]) or (key[p] == key[q] and (mat[p], idx[p]) < (mat[q], idx[q]))
+        used = int(cost[order[:n_kept]].sum())
+        assert used <= budget
+        if n_kept < len(order):
+            assert used + cost[order[n_kept]] > budget
+        assert ranks.tolist() == np.bincount(mat[kept.astype(bool)], minlength=nm).tolist()
+
+
+def test_allocate_equal_costs_is_optimal_subset():
+    """Equal costs: the kept set is the top-K scores, hence it minimises the summed
+    K-FAC loss of the discarded components over every subset of the same size."""
+    scores = [RNG.random(4).astype(np.float32), RNG.random(3).astype(np.float32)]
+    costs = [7, 7]
+    flat = np.concatenate(scores).astype(np.float64)
+    for budget in range(0, 7 * 7 + 1, 3):
+        _, n_kept, _, kept = oracle.allocate(scores, costs, budget)
+        assert n_kept == min(budget // 7, 7)
+        best = min(flat.sum() - flat[list(c)].sum() for c in itertools.combinations(range(7), n_kept))
+        np.testing.assert_allclose(flat.sum() - flat[kept.astype(bool)].sum(), best, rtol=1e-12)
+
+
+def test_allocate_rejects_nan():
+    with pytest.raises(ValueError):
+        oracle.allocate([np.array([1.0, np.nan], np.float32)], [3], 10)
