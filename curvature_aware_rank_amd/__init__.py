@@ -1,0 +1,227 @@
+"""Python binding of liblrc (argument marshalling only).
+
+Every computation runs in the HIP kernels of liblrc.so; this module checks tensor
+shapes and dtypes, allocates device workspace with torch, passes raw device pointers
+and torch's current HIP stream, and turns status codes into exceptions.  There is no
+fallback: if liblrc.so is missing or no GPU is present the calls raise.
+
+Names match the C ABI in include/lrc.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "LRC_OK", "LRC_EINVAL", "LRC_EDTYPE", "LRC_EWORKSPACE", "LRC_EHIP", "LRC_ENOTPD",
+    "LRC_ENOCONV", "LRC_ENONFINITE", "LRC_F32", "LRC_BF16", "LRC_COV_QUANT_INT8_TOKEN",
+    "LRC_SCORE_FISHER", "LRC_SCORE_KFAC", "LrcError", "lib", "library_path",
+    "lrc_accumulate_cov", "lrc_whiten_decompose", "lrc_score_components", "lrc_allocate_ranks",
+    "lrc_status_string",
+]
+
+LRC_OK, LRC_EINVAL, LRC_EDTYPE, LRC_EWORKSPACE, LRC_EHIP, LRC_ENOTPD, LRC_ENOCONV, LRC_ENONFINITE = range(8)
+LRC_F32, LRC_BF16 = 0, 1
+LRC_COV_QUANT_INT8_TOKEN = 0x1
+LRC_SCORE_FISHER = 0x1
+LRC_SCORE_KFAC = 0x2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "liblrc.so")
+
+_i64, _u32, _sz, _vp, _i32 = ctypes.c_int64, ctypes.c_uint32, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int
+
+_SIGS = {
+    "lrc_accumulate_cov": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _i64, _u32, _vp, _sz, _vp]),
+    "lrc_accumulate_cov_workspace": (_sz, [_i32, _i64, _i64, _u32]),
+    "lrc_whiten_decompose": (_i32, [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
+                                    _i64, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "lrc_whiten_decompose_workspace": (_sz, [_i64, _i64, _i64, _i64, _i32, _i32]),
+    "lrc_score_components": (_i32, [_vp, _vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _u32, _i32, _i32,
+                                    _i64, _vp, _vp, _sz, _vp]),
+    "lrc_score_components_workspace": (_sz, [_i64, _i64, _i64, _i64, _u32]),
+    "lrc_allocate_ranks": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "lrc_allocate_ranks_workspace": (_sz, [_i64, _i64]),
+    "lrc_status_string": (ctypes.c_char_p, [_i32]),
+    "lrc_last_hip_error": (_i32, []),
+}
+
+
+def _load():
+    if not os.path.exists(library_path):
+        raise ImportError(f"liblrc.so not built at {library_path}; run __graft_entry__.build()")
+    so = ctypes.CDLL(library_path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(so, name)
+        fn.restype = res
+        fn.argtypes = args
+    return so
+
+
+lib = _load()
+
+
+class LrcError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = lib.lrc_status_string(status).decode()
+        if status == LRC_EHIP:
+            msg += f" (hipError {lib.lrc_last_hip_error()})"
+        super().__init__(f"{where}: {msg}")
+        self.status = status
+
+
+def lrc_status_string(status: int) -> str:
+    return lib.lrc_status_string(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != LRC_OK:
+        raise LrcError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _workspace(nbytes: int, device):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return LRC_BF16
+    if t.dtype == torch.float32:
+        return LRC_F32
+    raise ValueError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _rowmajor_ld(t, name):
+    if t.dim() != 2 or t.stride(1) != 1 or t.stride(0) < t.shape[1]:
+        raise ValueError(f"{name} must be a row-major 2-D tensor")
+    return t.stride(0)
+
+
+def lrc_accumulate_cov(A: torch.Tensor, C: torch.Tensor, quant: bool = False) -> None:
+    """C[lower] += sum_t a_t^T a_t over the rows of A (fake-quantised per token if quant)."""
+    _dev(A, "A")
+    _dev(C, "C")
+    if C.dtype != torch.float32:
+        raise ValueError("C must be fp32")
+    n, d = A.shape
+    lda = _rowmajor_ld(A, "A")
+    ldc = _rowmajor_ld(C, "C")
+    if C.shape != (d, d):
+        raise ValueError("C must be d x d")
+    dt = _dtype_code(A)
+    flags = LRC_COV_QUANT_INT8_TOKEN if quant else 0
+    ws = _workspace(lib.lrc_accumulate_cov_workspace(dt, n, d, flags), A.device)
+    _check(lib.lrc_accumulate_cov(_ptr(A), dt, n, d, lda, _ptr(C), ldc, flags, _ptr(ws), ws.numel(), _stream()),
+           "lrc_accumulate_cov")
+
+
+def lrc_whiten_decompose(W: torch.Tensor, rank: int, Xsum=None, n_x: int = 0, Gsum=None, n_g: int = 0,
+                         damping: float = 0.0, check: bool = True):
+    """Whitened truncated decomposition.  W: (d_out, d_in) or (batch, d_out, d_in) fp32.
+
+    Returns (sigma, left, right, info): sigma (batch, k), left (batch, d_out, r),
+    right (batch, r, d_in), info (batch,) int32 -- batch dim dropped for 2-D W."""
+    _dev(W, "W")
+    if W.dtype != torch.float32:
+        raise ValueError("W must be fp32")
+    squeeze = W.dim() == 2
+    W3 = W.unsqueeze(0) if squeeze else W
+    if W3.dim() != 3 or W3.stride(2) != 1:
+        raise ValueError("W must be (d_out, d_in) or (batch, d_out, d_in), row-major")
+    batch, d_out, d_in = W3.shape
+    ldw, sw = W3.stride(1), W3.stride(0)
+    k = min(d_out, d_in)
+    dev = W.device
+    sigma = torch.empty(batch, k, dtype=torch.float32, device=dev)
+    left = torch.empty(batch, d_out, rank, dtype=torch.float32, device=dev)
+    right = torch.empty(batch, rank, d_in, dtype=torch.float32, device=dev)
+    info = torch.empty(batch, dtype=torch.int32, device=dev)
+    ldx = ldg = 0
+    if Xsum is not None:
+        _dev(Xsum, "Xsum")
+        ldx = _rowmajor_ld(Xsum, "Xsum")
+    if Gsum is not None:
+        _dev(Gsum, "Gsum")
+        ldg = _rowmajor_ld(Gsum, "Gsum")
+    nb = lib.lrc_whiten_decompose_workspace(d_out, d_in, batch, rank, Xsum is not None, Gsum is not None)
+    ws = _workspace(nb, dev)
+    st = lib.lrc_whiten_decompose(_ptr(W3), d_out, d_in, ldw, batch, sw, _ptr(Xsum), ldx, int(n_x), _ptr(Gsum), ldg,
+                                  int(n_g), int(rank), float(damping), _ptr(sigma), _ptr(left), _ptr(right),
+                                  _ptr(info), _ptr(ws), ws.numel(), _stream())
+    if check:
+        _check(st, "lrc_whiten_decompose")
+    if squeeze:
+        return sigma[0], left[0], right[0], info
+    return sigma, left, right, info
+
+
+def lrc_score_components(left: torch.Tensor, right: torch.Tensor, sigma=None, A=None, B=None, mode: str = "fisher",
+                         scores=None, accumulate: bool = False, finalize: bool = True, n_total=None):
+    """Per-component scores; returns the scores tensor (k,) fp32."""
+    _dev(left, "left")
+    d_out, k = left.shape
+    kk, d_in = right.shape
+    if kk != k:
+        raise ValueError("left and right disagree on k")
+    if scores is None:
+        scores = torch.empty(k, dtype=torch.float32, device=left.device)
+    if mode == "kfac":
+        _check(lib.lrc_score_components(None, None, LRC_F32, 0, d_in, d_out, _ptr(left), _ptr(right), _ptr(sigma), k,
+                                        LRC_SCORE_KFAC, 0, 1, 1, _ptr(scores), None, 0, _stream()),
+               "lrc_score_components")
+        return scores
+    if mode != "fisher":
+        raise ValueError("mode is 'fisher' or 'kfac'")
+    _dev(A, "A")
+    _dev(B, "B")
+    n = A.shape[0]
+    if A.shape != (n, d_in) or B.shape != (n, d_out) or A.dtype != B.dtype:
+        raise ValueError("A must be (n, d_in) and B (n, d_out), same dtype")
+    if not (A.is_contiguous() and B.is_contiguous() and left.is_contiguous() and right.is_contiguous()):
+        raise ValueError("contiguous tensors required")
+    dt = _dtype_code(A)
+    ws = _workspace(lib.lrc_score_components_workspace(n, d_in, d_out, k, LRC_SCORE_FISHER), A.device)
+    _check(lib.lrc_score_components(_ptr(A), _ptr(B), dt, n, d_in, d_out, _ptr(left), _ptr(right), None, k,
+                                    LRC_SCORE_FISHER, int(accumulate), int(finalize), int(n_total or n),
+                                    _ptr(scores), _ptr(ws), ws.numel(), _stream()), "lrc_score_components")
+    return scores
+
+
+def lrc_allocate_ranks(scores: torch.Tensor, offsets: torch.Tensor, cost: torch.Tensor, budget: int):
+    """Global sort-and-truncate.  scores: (M,) fp32; offsets: (n_mat+1,) int64; cost: (n_mat,) int64.
+
+    Returns (order int32 (M,), n_kept int64 (1,), ranks int32 (n_mat,), kept_mask uint8 (M,), info int32 (1,))."""
+    for t, nm in ((scores, "scores"), (offsets, "offsets"), (cost, "cost")):
+        _dev(t, nm)
+    if scores.dtype != torch.float32 or offsets.dtype != torch.int64 or cost.dtype != torch.int64:
+        raise ValueError("scores fp32, offsets and cost int64")
+    n_mat = cost.numel()
+    if offsets.numel() != n_mat + 1:
+        raise ValueError("offsets must have n_mat + 1 entries")
+    M = scores.numel()
+    dev = scores.device
+    order = torch.empty(M, dtype=torch.int32, device=dev)
+    n_kept = torch.empty(1, dtype=torch.int64, device=dev)
+    ranks = torch.empty(n_mat, dtype=torch.int32, device=dev)
+    kept = torch.empty(M, dtype=torch.uint8, device=dev)
+    info = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = _workspace(lib.lrc_allocate_ranks_workspace(n_mat, M), dev)
+    _check(lib.lrc_allocate_ranks(_ptr(scores.contiguous()), _ptr(offsets.contiguous()), _ptr(cost.contiguous()),
+                                  n_mat, M, int(budget), _ptr(order), _ptr(n_kept), _ptr(ranks), _ptr(kept),
+                                  _ptr(info), _ptr(ws), ws.numel(), _stream()), "lrc_allocate_ranks")
+    return order, n_kept, ranks, kept, info

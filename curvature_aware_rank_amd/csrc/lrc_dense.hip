@@ -1,0 +1,360 @@
+// Dense building blocks of the decomposition: fp32 GEMM on MFMA, fp64 Gram of the
+// whitened weight, blocked Cholesky (LASER Methodology 1, Transformation: S_x and S_g
+// are Cholesky factors of X and G) and blocked triangular solves for the back-map.
+#include "lrc_internal.h"
+#include "lrc_dense.h"
+
+namespace lrc {
+namespace {
+
+// ---------------------------------------------------------------------------------
+// fp32 GEMM: 64 x 64 output tile per workgroup, 4 waves in 2 x 2, each wave a 32 x 32
+// block as 2 x 2 v_mfma_f32_16x16x4f32 blocks.  Operands are staged k-major in LDS so
+// a lane reads its fragment element with one conflict-free 4-byte read.
+// Fragment layout (16x16x4): A[row = l%16][k = l/16], B[k = l/16][col = l%16],
+// D element r of lane l = D[4*(l/16) + r][l%16].
+// ---------------------------------------------------------------------------------
+constexpr int GT = 64;
+constexpr int GK = 16;
+
+__global__ __launch_bounds__(256) void gemm_f32_kernel(unsigned flags, int m, int n, int k, float alpha,
+                                                       const float* __restrict__ A, int64_t lda, int64_t sA,
+                                                       const float* __restrict__ B, int64_t ldb, int64_t sB,
+                                                       float beta, float* __restrict__ C, int64_t ldc, int64_t sC) {
+  __shared__ float As[GK][GT + 4];
+  __shared__ float Bs[GK][GT + 4];
+  A += blockIdx.z * sA;
+  B += blockIdx.z * sB;
+  C += blockIdx.z * sC;
+  const int row0 = blockIdx.y * GT, col0 = blockIdx.x * GT;
+  if (row0 >= m || col0 >= n) return;
+  if ((flags & GEMM_LOWER) && col0 > row0 + GT - 1) return;
+  int kb = 0, ke = k;
+  if (flags & GEMM_K_FROM_COL) kb = max(kb, col0);
+  if (flags & GEMM_K_FROM_ROW) kb = max(kb, row0);
+  if (flags & GEMM_K_TO_ROW) ke = min(ke, row0 + GT);
+  kb = (kb / GK) * GK;
+  const bool ta = flags & GEMM_TA, tb = flags & GEMM_TB;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int k0 = kb; k0 < ke; k0 += GK) {
+#pragma unroll
+    for (int it = 0; it < (GT * GK) / 256; ++it) {
+      const int e = tid + it * 256;
+      int r, kk;
+      if (ta) { kk = e / GT; r = e % GT; } else { r = e / GK; kk = e % GK; }
+      const int gr = row0 + r, gk = k0 + kk;
+      float v = 0.f;
+      if (gr < m && gk < ke) v = ta ? A[int64_t(gk) * lda + gr] : A[int64_t(gr) * lda + gk];
+      As[kk][r] = v;
+      int c;
+      if (tb) { c = e / GK; kk = e % GK; } else { kk = e / GT; c = e % GT; }
+      const int gc = col0 + c, gk2 = k0 + kk;
+      float w = 0.f;
+      if (gc < n && gk2 < ke) w = tb ? B[int64_t(gc) * ldb + gk2] : B[int64_t(gk2) * ldb + gc];
+      Bs[kk][c] = w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kq = 0; kq < GK; kq += 4) {
+      float a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) a[i] = As[kq + (lane >> 4)][wr * 32 + i * 16 + (lane & 15)];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = Bs[kq + (lane >> 4)][wc * 32 + j * 16 + (lane & 15)];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  const bool lower = flags & GEMM_LOWER, mirror = flags & GEMM_MIRROR;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = row0 + wr * 32 + i * 16 + 4 * (lane >> 4) + r;
+        const int col = col0 + wc * 32 + j * 16 + (lane & 15);
+        if (row >= m || col >= n) continue;
+        if (lower && row < col) continue;
+        float v = alpha * acc[i][j][r];
+        if (beta != 0.f) v += beta * C[int64_t(row) * ldc + col];
+        C[int64_t(row) * ldc + col] = v;
+        if (mirror && row != col) C[int64_t(col) * ldc + row] = v;
+      }
+}
+
+// ---------------------------------------------------------------------------------
+// fp64 Gram from an fp32 matrix (products exact in fp64): G = M M^T or M^T M, lower
+// tiles computed and mirrored.  64 x 64 tiles, 256 threads with 4 x 4 outputs each.
+// ---------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gram_f64_kernel(bool rows, int p, int q, const float* __restrict__ M,
+                                                       int64_t ldm, int64_t sM, double* __restrict__ G,
+                                                       int64_t ldg, int64_t sG) {
+  __shared__ double xs[16][65];
+  __shared__ double ys[16][65];
+  M += blockIdx.z * sM;
+  G += blockIdx.z * sG;
+  int lin = blockIdx.x, ti = 0;
+  while (lin > ti) { lin -= ti + 1; ++ti; }
+  const int tj = lin;
+  const int dim = rows ? p : q;     // Gram dimension
+  const int red = rows ? q : p;     // reduction length
+  if (ti * 64 >= dim) return;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  double acc[4][4] = {};
+  for (int k0 = 0; k0 < red; k0 += 16) {
+    for (int e = threadIdx.x; e < 16 * 64; e += 256) {
+      int kk, c;
+      if (rows) { c = e >> 4; kk = e & 15; } else { kk = e >> 6; c = e & 63; }
+      const int gk = k0 + kk;
+      const int ci = ti * 64 + c, cj = tj * 64 + c;
+      double vi = 0.0, vj = 0.0;
+      if (gk < red) {
+        if (rows) {
+          if (ci < dim) vi = M[int64_t(ci) * ldm + gk];
+          if (cj < dim) vj = M[int64_t(cj) * ldm + gk];
+        } else {
+          if (ci < dim) vi = M[int64_t(gk) * ldm + ci];
+          if (cj < dim) vj = M[int64_t(gk) * ldm + cj];
+        }
+      }
+      xs[kk][c] = vi;
+      ys[kk][c] = vj;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      double xv[4], yv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { xv[i] = xs[kk][ty * 4 + i]; yv[i] = ys[kk][tx * 4 + i]; }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fma(xv[i], yv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = ti * 64 + ty * 4 + i, c = tj * 64 + tx * 4 + j;
+      if (r < dim && c < dim && r >= c) {
+        G[int64_t(r) * ldg + c] = acc[i][j];
+        G[int64_t(c) * ldg + r] = acc[i][j];
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// Cholesky pieces (lower, in place on an fp32 n x n buffer whose strict upper part is 0)
+// ---------------------------------------------------------------------------------
+// L = lower(S) / cnt + damping * I ; strict upper part zeroed.  S is read lower only.
+__global__ void sym_scale_kernel(const float* __restrict__ S, int64_t lds_, int64_t n, double inv_cnt, float damping,
+                                 float* __restrict__ L, int64_t ldl) {
+  const int64_t i = blockIdx.y;
+  for (int64_t j = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; j < n; j += int64_t(gridDim.x) * blockDim.x) {
+    float v = 0.f;
+    if (j <= i) {
+      v = float(double(S[i * lds_ + j]) * inv_cnt);
+      if (j == i) v += damping;
+    }
+    L[i * ldl + j] = v;
+  }
+}
+
+constexpr int NB = 64;  // Cholesky / triangular-solve block size
+
+// unblocked factorisation of the diagonal block at k0 (one workgroup)
+__global__ __launch_bounds__(256) void potf2_kernel(float* __restrict__ L, int64_t ldl, int64_t n, int64_t k0,
+                                                    int* __restrict__ info) {
+  __shared__ float S[NB][NB + 1];
+  __shared__ int failed;
+  const int b = int(min<int64_t>(NB, n - k0));
+  if (*info != 0) return;
+  for (int e = threadIdx.x; e < NB * NB; e += 256) {
+    const int i = e / NB, j = e % NB;
+    S[i][j] = (i < b && j <= i) ? L[(k0 + i) * ldl + k0 + j] : 0.f;
+  }
+  if (threadIdx.x == 0) failed = 0;
+  __syncthreads();
+  for (int j = 0; j < b; ++j) {
+    if (threadIdx.x == 0) {
+      const float piv = S[j][j];
+      if (!(piv > 0.f) || !isfinite(piv)) {
+        failed = 1;
+        *info = int(k0 + j + 1);
+      } else {
+        S[j][j] = sqrtf(piv);
+      }
+    }
+    __syncthreads();
+    if (failed) return;
+    const float djj = S[j][j];
+    for (int i = j + 1 + threadIdx.x; i < b; i += 256) S[i][j] = S[i][j] / djj;
+    __syncthreads();
+    const int m = b - j - 1;
+    for (int e = threadIdx.x; e < m * m; e += 256) {
+      const int i = j + 1 + e / m, c = j + 1 + e % m;
+      if (c <= i) S[i][c] -= S[i][j] * S[c][j];
+    }
+    __syncthreads();
+  }
+  for (int e = threadIdx.x; e < b * b; e += 256) {
+    const int i = e / b, j = e % b;
+    L[(k0 + i) * ldl + k0 + j] = (j <= i) ? S[i][j] : 0.f;
+  }
+}
+
+// rows below the diagonal block: X <- X * L11^{-T}   (one wave handles 64 rows)
+__global__ __launch_bounds__(64) void trsm_panel_kernel(float* __restrict__ L, int64_t ldl, int64_t n, int64_t k0,
+                                                        const int* __restrict__ info) {
+  __shared__ float D[NB][NB + 1];
+  __shared__ float X[NB][NB + 1];
+  if (*info != 0) return;
+  const int64_t r0 = k0 + NB + int64_t(blockIdx.x) * 64;
+  const int lane = threadIdx.x;
+  for (int i = 0; i < NB; ++i) D[i][lane] = L[(k0 + i) * ldl + k0 + lane];
+  for (int i = 0; i < 64; ++i) {
+    const int64_t r = r0 + i;
+    X[i][lane] = (r < n) ? L[r * ldl + k0 + lane] : 0.f;
+  }
+  __syncthreads();
+  float x[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) x[j] = X[lane][j];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    float v = x[j];
+#pragma unroll
+    for (int c = 0; c < j; ++c) v -= x[c] * D[j][c];
+    x[j] = v / D[j][j];
+  }
+#pragma unroll
+  for (int j = 0; j < NB; ++j) X[lane][j] = x[j];
+  __syncthreads();
+  for (int i = 0; i < 64; ++i) {
+    const int64_t r = r0 + i;
+    if (r < n) L[r * ldl + k0 + lane] = X[i][lane];
+  }
+}
+
+// Diagonal-block back substitution of  L11^T Y = B  for the block rows at k0 (b rows),
+// one thread per right-hand-side column.
+__global__ __launch_bounds__(64) void trsm_upper_diag_kernel(const float* __restrict__ L, int64_t ldl, int64_t k0, int b,
+                                                             float* __restrict__ Bm, int64_t ldb, int64_t ncol) {
+  __shared__ float D[NB][NB + 1];
+  for (int e = threadIdx.x; e < NB * NB; e += 64) {
+    const int i = e / NB, j = e % NB;
+    D[i][j] = (i < b && j < b) ? L[(k0 + i) * ldl + k0 + j] : (i == j ? 1.f : 0.f);
+  }
+  __syncthreads();
+  const int64_t col = int64_t(blockIdx.x) * 64 + threadIdx.x;
+  if (col >= ncol) return;
+  float y[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) y[i] = (i < b) ? Bm[(k0 + i) * ldb + col] : 0.f;
+#pragma unroll
+  for (int i = NB - 1; i >= 0; --i) {
+    float v = y[i];
+#pragma unroll
+    for (int c = i + 1; c < NB; ++c) v -= D[c][i] * y[c];
+    y[i] = v / D[i][i];
+  }
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+    if (i < b) Bm[(k0 + i) * ldb + col] = y[i];
+}
+
+__global__ void transpose_f32_kernel(const float* __restrict__ S, int64_t lds_, float* __restrict__ D, int64_t ldd,
+                                     int rows, int cols) {
+  __shared__ float t[32][33];
+  const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
+  for (int i = threadIdx.y; i < 32; i += 8) {
+    const int r = r0 + i, c = c0 + threadIdx.x;
+    if (r < rows && c < cols) t[i][threadIdx.x] = S[int64_t(r) * lds_ + c];
+  }
+  __syncthreads();
+  for (int i = threadIdx.y; i < 32; i += 8) {
+    const int c = c0 + i, r = r0 + threadIdx.x;
+    if (r < rows && c < cols) D[int64_t(c) * ldd + r] = t[threadIdx.x][i];
+  }
+}
+
+}  // namespace
+
+lrc_status gemm_f32(hipStream_t st, unsigned flags, int64_t m, int64_t n, int64_t k, float alpha, const float* A,
+                    int64_t lda, int64_t sA, const float* B, int64_t ldb, int64_t sB, float beta, float* C,
+                    int64_t ldc, int64_t sC, int64_t batch) {
+  if (m <= 0 || n <= 0 || batch <= 0) return LRC_OK;
+  const dim3 grid(unsigned(cdiv(n, GT)), unsigned(cdiv(m, GT)), unsigned(batch));
+  gemm_f32_kernel<<<grid, 256, 0, st>>>(flags, int(m), int(n), int(k), alpha, A, lda, sA, B, ldb, sB, beta, C, ldc, sC);
+  LRC_LAUNCHED();
+  return LRC_OK;
+}
+
+lrc_status gram_f64(hipStream_t st, bool rows, int64_t p, int64_t q, const float* M, int64_t ldm, int64_t sM,
+                    double* G, int64_t ldg, int64_t sG, int64_t batch) {
+  const int64_t dim = rows ? p : q;
+  const int64_t t = cdiv(dim, 64);
+  const dim3 grid(unsigned(t * (t + 1) / 2), 1, unsigned(batch));
+  gram_f64_kernel<<<grid, 256, 0, st>>>(rows, int(p), int(q), M, ldm, sM, G, ldg, sG);
+  LRC_LAUNCHED();
+  return LRC_OK;
+}
+
+lrc_status cholesky_f32(hipStream_t st, const float* S, int64_t lds_, int64_t n, int64_t cnt, float damping, float* L,
+                        int* info) {
+  const dim3 g(unsigned(std::min<int64_t>(cdiv(n, 256), 64)), unsigned(n));
+  sym_scale_kernel<<<g, 256, 0, st>>>(S, lds_, n, 1.0 / double(cnt), damping, L, n);
+  LRC_LAUNCHED();
+  for (int64_t k0 = 0; k0 < n; k0 += NB) {
+    potf2_kernel<<<1, 256, 0, st>>>(L, n, n, k0, info);
+    LRC_LAUNCHED();
+    const int64_t below = n - k0 - NB;
+    if (below <= 0) break;
+    trsm_panel_kernel<<<unsigned(cdiv(below, 64)), 64, 0, st>>>(L, n, n, k0, info);
+    LRC_LAUNCHED();
+    float* p = L + (k0 + NB) * n + k0;
+    float* c = L + (k0 + NB) * n + (k0 + NB);
+    LRC_TRY(gemm_f32(st, GEMM_TB | GEMM_LOWER, below, below, NB, -1.f, p, n, 0, p, n, 0, 1.f, c, n, 0, 1));
+  }
+  return LRC_OK;
+}
+
+lrc_status trsm_lower_t(hipStream_t st, const float* L, int64_t n, float* Bm, int64_t ldb, int64_t ncol) {
+  const int64_t nblk = cdiv(n, NB);
+  for (int64_t ib = nblk - 1; ib >= 0; --ib) {
+    const int64_t k0 = ib * NB;
+    const int b = int(std::min<int64_t>(NB, n - k0));
+    const int64_t rest = n - (k0 + b);
+    if (rest > 0) {
+      // B[k0:k0+b] -= L[k0+b:n, k0:k0+b]^T * Y[k0+b:n]
+      LRC_TRY(gemm_f32(st, GEMM_TA, b, ncol, rest, -1.f, L + (k0 + b) * n + k0, n, 0, Bm + (k0 + b) * ldb, ldb, 0,
+                       1.f, Bm + k0 * ldb, ldb, 0, 1));
+    }
+    trsm_upper_diag_kernel<<<unsigned(cdiv(ncol, 64)), 64, 0, st>>>(L, n, k0, b, Bm, ldb, ncol);
+    LRC_LAUNCHED();
+  }
+  return LRC_OK;
+}
+
+lrc_status transpose_f32(hipStream_t st, const float* S, int64_t lds_, float* D, int64_t ldd, int64_t rows,
+                         int64_t cols) {
+  const dim3 grid(unsigned(cdiv(cols, 32)), unsigned(cdiv(rows, 32)));
+  transpose_f32_kernel<<<grid, dim3(32, 8), 0, st>>>(S, lds_, D, ldd, int(rows), int(cols));
+  LRC_LAUNCHED();
+  return LRC_OK;
+}
+
+}  // namespace lrc

@@ -1,0 +1,187 @@
+/*
+ * lrc.h -- C ABI of liblrc: whitened truncated decomposition of linear-layer weights
+ * and global rank allocation, on AMD Instinct MI355X (gfx950).
+ *
+ * The method (pages: gist.science explainers of three papers):
+ *   LASER: Loss-Aware Singular-value Decomposition and Rank Allocation for Efficient
+ *     Low-Precision Vision-Language Models -- technical summary, Methodology 1
+ *     (K-FAC surrogate, Transformation, QAW) and Methodology 2 (empirical-Fisher
+ *     importance score, global optimisation);
+ *   Swift-SVD: Theoretical Optimality Meets Practical Efficiency in Low-Rank LLM
+ *     Compression -- technical summary, section 2A (closed-form optimum from one
+ *     eigendecomposition of the incrementally aggregated output covariance);
+ *   UniRank: Unified Rank Allocation for Low-Rank LLM Compression -- technical summary,
+ *     section 2.1 (Sorting-and-Truncation: pooled sort, m+n parameters per component,
+ *     accumulate until the budget is reached).
+ *
+ * Conventions shared by every entry point
+ *   - Matrices are row-major with an explicit leading dimension (elements).
+ *   - A weight W is d_out x d_in (y = W x).  Calibration activations A are
+ *     n_tokens x d_in and output gradients B are n_tokens x d_out, token-major.
+ *   - Every pointer except the host scalars is DEVICE memory owned by the caller.  The
+ *     library allocates nothing and keeps no state between calls; scratch space comes
+ *     from the caller's workspace `ws` of at least the size the matching *_workspace
+ *     query returns (256-byte aligned, contents need not be initialised).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Kernels are enqueued on
+ *     it.  lrc_accumulate_cov, lrc_score_components and lrc_allocate_ranks do not block
+ *     the host.  lrc_whiten_decompose blocks the host on `stream` (it reads device
+ *     convergence flags between eigensolver sweeps), see below.
+ *   - Return value: LRC_OK, or an error found before or while enqueueing work.
+ *     Argument errors are detected on the host before any HIP call is made.
+ */
+#ifndef LRC_H
+#define LRC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LRC_OK = 0,
+  LRC_EINVAL = 1,       /* null pointer, negative or inconsistent size, bad leading dim */
+  LRC_EDTYPE = 2,       /* dtype or flag combination not supported */
+  LRC_EWORKSPACE = 3,   /* workspace missing or smaller than the query says */
+  LRC_EHIP = 4,         /* a HIP runtime call or launch failed (lrc_last_hip_error) */
+  LRC_ENOTPD = 5,       /* a covariance is not positive definite (Cholesky pivot <= 0) */
+  LRC_ENOCONV = 6,      /* the eigensolver did not converge within its sweep cap */
+  LRC_ENONFINITE = 7    /* a NaN or Inf was met */
+} lrc_status;
+
+typedef enum { LRC_F32 = 0, LRC_BF16 = 1 } lrc_dtype;
+
+/* lrc_accumulate_cov flags */
+#define LRC_COV_QUANT_INT8_TOKEN 0x1u  /* fake-quantise each token to int8 first (QAW) */
+
+/* lrc_score_components flags (exactly one) */
+#define LRC_SCORE_FISHER 0x1u          /* empirical-Fisher score, needs A and B */
+#define LRC_SCORE_KFAC 0x2u            /* 1/2 sigma^2, needs sigma only */
+
+/*
+ * lrc_accumulate_cov -- covariance streaming.
+ * LASER Methodology 1 (K-FAC surrogate): X and G are the activation and gradient
+ * covariances estimated on a calibration set; Swift-SVD 2A aggregates such a
+ * covariance incrementally, one batch of tokens at a time.
+ *
+ *   C[i][j] += sum_t a_t[i] * a_t[j]   for 0 <= j <= i < d   (lower triangle incl. diag)
+ *
+ * A: n_tokens x d, leading dim lda >= d, dtype `dt` (LRC_BF16 or LRC_F32).
+ * C: d x d fp32, leading dim ldc >= d; only the lower triangle is read and written
+ *    (the strict upper triangle is left untouched).  C holds a RAW sum: the caller
+ *    keeps the token count N and passes it to lrc_whiten_decompose, so a stream of
+ *    chunks is accumulated by calling this once per chunk.
+ * flags: 0 or LRC_COV_QUANT_INT8_TOKEN.  With the flag each token a_t is replaced by
+ *    its per-token symmetric int8 fake quantisation (LASER Methodology 1, QAW):
+ *    s_t = fl32(max_j |a_tj| / 127), q = clamp(round_half_even(fl32(a_tj / s_t)), -127,
+ *    127), a_hat = q * s_t (an all-zero token stays zero).  On the GPU the products are
+ *    formed as q_i * (s_t^2 q_j) with s_t^2 q_j split into two bf16 terms (error ~2^-17).
+ * Accumulation is fp32 with bf16 x bf16 products exact; the split of the token range
+ * over workgroups and its reduction order are fixed, so equal inputs give equal bits.
+ * n_tokens == 0 is a no-op (A may be NULL).
+ */
+lrc_status lrc_accumulate_cov(const void* A, lrc_dtype dt, int64_t n_tokens, int64_t d,
+                              int64_t lda, float* C, int64_t ldc, uint32_t flags,
+                              void* ws, size_t ws_bytes, void* stream);
+size_t lrc_accumulate_cov_workspace(lrc_dtype dt, int64_t n_tokens, int64_t d, uint32_t flags);
+
+/*
+ * lrc_whiten_decompose -- whitened truncated decomposition of one weight or a batch of
+ * weight slices sharing the same covariances.
+ * LASER Methodology 1 (Transformation): W is moved into the curvature-weighted space
+ * with the Cholesky factors of X and G, decomposed there, truncated, and the low-rank
+ * factors are mapped back; Swift-SVD 2A: the decomposition is one symmetric
+ * eigendecomposition of the aggregated covariance of the whitened outputs.
+ *
+ * With X = Xsum/n_x + damping*I = L_x L_x^T and G = Gsum/n_g + damping*I = L_g L_g^T
+ * (lower Cholesky; an absent sum means identity), the whitened weight is
+ *      W~ = L_g^T W L_x  = U~ S~ V~^T  (S~ descending, k = min(d_out, d_in))
+ * and the outputs are
+ *      sigma = diag(S~)                       (all k values)
+ *      Left  = L_g^-T U~_r S~_r^{1/2}         (d_out x r)
+ *      Right = S~_r^{1/2} V~_r^T L_x^-1       (r x d_in),   Left @ Right = W_r
+ * W_r minimises the K-FAC loss 1/2 tr((W - W_r) X (W - W_r)^T G) over rank r.
+ * The eigendecomposed Gram is the one of the smaller side (W~ W~^T if d_out <= d_in,
+ * else W~^T W~), formed and solved in fp64 from the fp32 whitened weight; each pair is
+ * signed so that the largest-magnitude entry of that side's singular vector is positive.
+ *
+ * W: batch slices, slice b at W + b*stride_w, each d_out x d_in fp32 with leading dim
+ *    ldw >= d_in.  Xsum: d_in x d_in fp32 (lower triangle read), leading dim ldx, or
+ *    NULL.  Gsum: d_out x d_out (lower read), leading dim ldg, or NULL.  n_x, n_g > 0
+ *    when the matching sum is given.  rank: 0 <= r <= k.  damping >= 0.
+ * Outputs (packed, fp32): sigma[batch][k], left[batch][d_out][r], right[batch][r][d_in].
+ * info (device int32[batch]): 0 ok; p in 1..d_in: pivot p of X not positive;
+ *    d_in + p: pivot p of G not positive; -1: eigensolver hit its sweep cap.
+ * Returns LRC_ENOTPD / LRC_ENOCONV when any info entry reports that (the outputs of the
+ * affected slices are then undefined).  Blocks the host on `stream`.
+ */
+lrc_status lrc_whiten_decompose(const float* W, int64_t d_out, int64_t d_in, int64_t ldw,
+                                int64_t batch, int64_t stride_w,
+                                const float* Xsum, int64_t ldx, int64_t n_x,
+                                const float* Gsum, int64_t ldg, int64_t n_g,
+                                int64_t rank, float damping,
+                                float* sigma, float* left, float* right, int32_t* info,
+                                void* ws, size_t ws_bytes, void* stream);
+size_t lrc_whiten_decompose_workspace(int64_t d_out, int64_t d_in, int64_t batch, int64_t rank,
+                                      int has_x, int has_g);
+
+/*
+ * lrc_score_components -- importance score of every singular component.
+ * LASER Methodology 2 (empirical-Fisher importance score): a component's contribution
+ * to the empirical-Fisher quadratic loss, combining its size with its alignment to the
+ * calibration gradients in the original parameter space.  With per-token gradient
+ * samples b_t a_t^T and the component left_i right_i^T:
+ *   FISHER: scores[i] = 1/(2 n_total) * sum_t (b_t . left_i)^2 (a_t . right_i)^2
+ *   KFAC:   scores[i] = 1/2 sigma_i^2   (its K-FAC loss alone; no data needed)
+ * A: n_tokens x d_in (lda = d_in), B: n_tokens x d_out (ldb = d_out), dtype `dt`.
+ * left: d_out x k (leading dim k), right: k x d_in (leading dim d_in), fp32, as written
+ * by lrc_whiten_decompose with rank k.  sigma: k floats (KFAC only).
+ * FISHER streams the tokens in chunks: the first call of a stream passes accumulate=0
+ * (scores are overwritten by this chunk's sum), later calls accumulate=1; the call with
+ * finalize=1 scales the running sum by 1/(2*n_total).  KFAC ignores A, B, accumulate.
+ * The per-token products are formed on fp32 values; the reduction order is fixed.
+ */
+lrc_status lrc_score_components(const void* A, const void* B, lrc_dtype dt, int64_t n_tokens,
+                                int64_t d_in, int64_t d_out, const float* left,
+                                const float* right, const float* sigma, int64_t k,
+                                uint32_t flags, int accumulate, int finalize, int64_t n_total,
+                                float* scores, void* ws, size_t ws_bytes, void* stream);
+size_t lrc_score_components_workspace(int64_t n_tokens, int64_t d_in, int64_t d_out, int64_t k,
+                                      uint32_t flags);
+
+/*
+ * lrc_allocate_ranks -- global sort-and-truncate under a parameter budget.
+ * LASER Methodology 2 (global optimisation: greedy by importance per parameter cost
+ * until the target parameter budget is reached) and UniRank 2.1 (pool all components,
+ * sort descending, accumulate while the total stays within the budget; a component of
+ * an m x n matrix costs m + n parameters).
+ *
+ * scores: M = offsets[n_mat] fp32 values, matrix m owning scores[offsets[m] ..
+ *   offsets[m+1]) in component order.  offsets: int64[n_mat + 1] (device, offsets[0]=0,
+ *   non-decreasing).  cost: int64[n_mat] (device, > 0; normally d_out + d_in).
+ * key_j = fp64(score_j) / fp64(cost of j's matrix), IEEE round-to-nearest.  Items are
+ * sorted by key descending, equal keys keeping the input order (matrix id, then
+ * component index).  The kept set is the longest prefix of that order whose int64
+ * cumulative cost is <= budget.
+ * Outputs (device): order[M] (int32 item ids in sorted order), n_kept (one int64),
+ *   ranks[n_mat] (int32 kept count per matrix), kept_mask[M] (uint8 0/1),
+ *   info (one int32: 0 ok, LRC_ENONFINITE if a score is NaN/Inf or negative,
+ *   LRC_EINVAL if a cost is <= 0 or offsets are inconsistent).
+ * Identical inputs give identical outputs bit for bit.  M must be < 2^31.
+ */
+lrc_status lrc_allocate_ranks(const float* scores, const int64_t* offsets, const int64_t* cost,
+                              int64_t n_mat, int64_t n_items, int64_t budget, int32_t* order,
+                              int64_t* n_kept, int32_t* ranks, uint8_t* kept_mask, int32_t* info,
+                              void* ws, size_t ws_bytes, void* stream);
+size_t lrc_allocate_ranks_workspace(int64_t n_mat, int64_t n_items);
+
+/* Human-readable name of a status code (static string). */
+const char* lrc_status_string(lrc_status s);
+/* The hipError_t value of the last LRC_EHIP returned on this thread (0 if none). */
+int lrc_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LRC_H */

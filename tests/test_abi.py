@@ -1,0 +1,101 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol that
+include/lrc.h declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "curvature_aware_rank_amd", "liblrc.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="liblrc.so not built")
+
+EINVAL, EDTYPE, EWORKSPACE = 1, 2, 3
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation returns first
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "lrc.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lrc_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import curvature_aware_rank_amd as m   # sets argtypes / restypes
+    return m.lib
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_symbols()
+    assert {"lrc_accumulate_cov", "lrc_whiten_decompose", "lrc_score_components", "lrc_allocate_ranks"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        assert lib.lrc_status_string(code).decode().startswith("LRC_")
+
+
+def test_accumulate_cov_validation(lib):
+    f = lib.lrc_accumulate_cov
+    assert f(FAKE, 7, 10, 4, 4, FAKE, 4, 0, FAKE, 1 << 30, None) == EDTYPE          # dtype
+    assert f(FAKE, 1, 10, 4, 4, FAKE, 4, 0x8, FAKE, 1 << 30, None) == EDTYPE        # flags
+    assert f(None, 1, 10, 4, 4, FAKE, 4, 0, FAKE, 1 << 30, None) == EINVAL          # A null
+    assert f(FAKE, 1, 10, 4, 4, None, 4, 0, FAKE, 1 << 30, None) == EINVAL          # C null
+    assert f(FAKE, 1, 10, 4, 3, FAKE, 4, 0, FAKE, 1 << 30, None) == EINVAL          # lda < d
+    assert f(FAKE, 1, 10, 4, 4, FAKE, 3, 0, FAKE, 1 << 30, None) == EINVAL          # ldc < d
+    assert f(FAKE, 1, -1, 4, 4, FAKE, 4, 0, FAKE, 1 << 30, None) == EINVAL          # n < 0
+    assert f(None, 1, 0, 4, 4, FAKE, 4, 0, None, 0, None) == 0                      # empty: no-op
+    need = lib.lrc_accumulate_cov_workspace(1, 4096, 256, 0)
+    assert need > 0
+    assert f(FAKE, 1, 4096, 256, 256, FAKE, 256, 0, FAKE, need - 1, None) == EWORKSPACE
+    # QAW needs more scratch than plain accumulation
+    assert lib.lrc_accumulate_cov_workspace(1, 4096, 256, 1) > need
+
+
+def test_whiten_decompose_validation(lib):
+    f = lib.lrc_whiten_decompose
+    ok = dict(W=FAKE, d_out=8, d_in=6, ldw=6, batch=1, stride_w=48, X=FAKE, ldx=6, nx=10, G=None, ldg=0, ng=0,
+              rank=3, damping=0.0, sigma=FAKE, left=FAKE, right=FAKE, info=FAKE)
+
+    def call(ws_bytes=1 << 40, **over):
+        a = dict(ok, **over)
+        return f(a["W"], a["d_out"], a["d_in"], a["ldw"], a["batch"], a["stride_w"], a["X"], a["ldx"], a["nx"],
+                 a["G"], a["ldg"], a["ng"], a["rank"], a["damping"], a["sigma"], a["left"], a["right"], a["info"],
+                 FAKE, ws_bytes, None)
+
+    assert call(W=None) == EINVAL
+    assert call(rank=7) == EINVAL            # rank > min(d_out, d_in)
+    assert call(rank=-1) == EINVAL
+    assert call(ldw=5) == EINVAL
+    assert call(ldx=5) == EINVAL
+    assert call(nx=0) == EINVAL
+    assert call(G=FAKE, ldg=8, ng=0) == EINVAL
+    assert call(damping=-1.0) == EINVAL
+    assert call(batch=2, stride_w=10) == EINVAL
+    assert call(left=None) == EINVAL
+    need = lib.lrc_whiten_decompose_workspace(8, 6, 1, 3, 1, 0)
+    assert need > 0
+    assert call(ws_bytes=need - 1) == EWORKSPACE
+
+
+def test_score_components_validation(lib):
+    f = lib.lrc_score_components
+    assert f(FAKE, FAKE, 1, 10, 4, 4, FAKE, FAKE, None, 4, 0x3, 0, 1, 10, FAKE, FAKE, 1 << 30, None) == EDTYPE
+    assert f(FAKE, FAKE, 1, 10, 4, 4, FAKE, FAKE, None, 0, 0x1, 0, 1, 10, FAKE, FAKE, 1 << 30, None) == EINVAL
+    assert f(None, None, 0, 0, 4, 4, FAKE, FAKE, None, 4, 0x2, 0, 1, 1, FAKE, None, 0, None) == EINVAL  # KFAC no sigma
+    assert f(FAKE, FAKE, 1, 10, 4, 4, FAKE, FAKE, None, 4, 0x1, 0, 1, 0, FAKE, FAKE, 1 << 30, None) == EINVAL
+    need = lib.lrc_score_components_workspace(1000, 4, 4, 4, 0x1)
+    assert f(FAKE, FAKE, 1, 1000, 4, 4, FAKE, FAKE, None, 4, 0x1, 0, 1, 1000, FAKE, FAKE, need - 1, None) == EWORKSPACE
+
+
+def test_allocate_ranks_validation(lib):
+    f = lib.lrc_allocate_ranks
+    assert f(FAKE, FAKE, FAKE, 0, 10, 5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == EINVAL
+    assert f(FAKE, FAKE, FAKE, 2, 10, -1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == EINVAL
+    assert f(FAKE, None, FAKE, 2, 10, 5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == EINVAL
+    need = lib.lrc_allocate_ranks_workspace(2, 10)
+    assert f(FAKE, FAKE, FAKE, 2, 10, 5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == EWORKSPACE

@@ -1,0 +1,406 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the same
+seeded inputs, at sizes the oracle finishes in seconds (several tiles, ragged tails).
+
+Tolerances (floating point) follow from the arithmetic, see each test; integer and
+index results are compared bit for bit.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+U32 = 2.0 ** -24     # fp32 unit roundoff
+
+
+@pytest.fixture(scope="module")
+def lrc():
+    import curvature_aware_rank_amd as m
+    return m
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def to_np(t):
+    return t.detach().float().cpu().numpy() if t.dtype == torch.bfloat16 else t.detach().cpu().numpy()
+
+
+def lower(c):
+    return np.tril(c)
+
+
+def bf16_stream(n, d, exponent, seed, outlier_frac=0.0):
+    return synth.activation_stream(n, d, exponent, seed, outlier_frac=outlier_frac, dtype=torch.bfloat16,
+                                   device="cpu")
+
+
+# ----------------------------------------------------------------------------- a1 covariance
+@pytest.mark.parametrize("n,d", [(700, 8), (1000, 300), (4100, 520), (130, 1100)])
+def test_cov_bf16_exact_on_small_integers(lrc, n, d):
+    """bf16 inputs in {-3..3}: every product and partial sum is an integer below 2^24, so
+    fp32 accumulation is exact in any order -> bit-exact against the oracle.  Catches a
+    dropped, repeated or misplaced token, channel or tile."""
+    g = torch.Generator().manual_seed(n * 7 + d)
+    a = torch.randint(-3, 4, (n, d), generator=g).to(torch.bfloat16)
+    c = torch.zeros(d, d, dtype=torch.float32, device=dev())
+    lrc.lrc_accumulate_cov(a.to(dev()), c)
+    want = lower(oracle.covariance_sum(to_np(a)))
+    got = lower(to_np(c))
+    assert np.array_equal(got, want)
+    # the strict upper triangle is left untouched
+    assert np.all(np.triu(to_np(c), 1) == 0)
+
+
+@pytest.mark.parametrize("n,d", [(4096, 256), (3000, 520)])
+def test_cov_bf16_gaussian(lrc, n, d):
+    """fp32 accumulation of exact bf16 products: per-entry error modelled as
+    sqrt(depth) * u * (|A|^T |A|)_ij with depth = n (+splits), times a safety factor 10."""
+    a = bf16_stream(n, d, 1.0, 1234 + d, outlier_frac=0.01)
+    c = torch.zeros(d, d, dtype=torch.float32, device=dev())
+    lrc.lrc_accumulate_cov(a.to(dev()), c)
+    an = to_np(a).astype(np.float64)
+    want = an.T @ an
+    absmag = np.abs(an).T @ np.abs(an)
+    tol = 10 * math.sqrt(n + 64) * U32 * absmag + 1e-30
+    err = np.abs(lower(to_np(c)) - lower(want))
+    assert np.all(err <= lower(tol)), float(np.max(err / lower(tol + 1e-300)))
+
+
+def test_cov_streaming_chunks_match_one_shot(lrc):
+    """Swift-SVD 2A aggregation: summing chunks equals one pass up to rounding, and the
+    same chunking twice gives the same bits."""
+    a = bf16_stream(5000, 264, 1.0, 77).to(dev())
+    c1 = torch.zeros(264, 264, device=dev())
+    lrc.lrc_accumulate_cov(a, c1)
+    c2 = torch.zeros(264, 264, device=dev())
+    for t0 in range(0, 5000, 1234):
+        lrc.lrc_accumulate_cov(a[t0:t0 + 1234], c2)
+    c3 = torch.zeros(264, 264, device=dev())
+    for t0 in range(0, 5000, 1234):
+        lrc.lrc_accumulate_cov(a[t0:t0 + 1234], c3)
+    assert torch.equal(c2, c3)
+    ref = to_np(c1).astype(np.float64)
+    np.testing.assert_allclose(np.tril(to_np(c2)), np.tril(ref), rtol=1e-5, atol=1e-5 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("n,d", [(1000, 96), (4096, 256)])
+def test_cov_fp32(lrc, n, d):
+    a = synth.activation_stream(n, d, 1.2, 99 + d, dtype=torch.float32)
+    c = torch.zeros(d, d, device=dev())
+    lrc.lrc_accumulate_cov(a.to(dev()), c)
+    an = to_np(a).astype(np.float64)
+    absmag = np.abs(an).T @ np.abs(an)
+    tol = 10 * math.sqrt(n) * U32 * absmag + 2 * U32 * np.abs(an.T @ an)
+    err = np.abs(lower(to_np(c)) - lower(an.T @ an))
+    assert np.all(err <= lower(tol))
+
+
+# ----------------------------------------------------------------------------- a0 QAW
+def test_qaw_cov_exact_with_power_of_two_scales(lrc):
+    """Rows whose max |a| is 127 * 2^e have an exact scale s = 2^e, so q, s^2 q (one bf16
+    term, the low term is 0) and every product are exact; with 48 tokens, |values| <= 127
+    and s >= 1/4 every partial sum is a multiple of 1/16 below 2^20, so fp32 accumulation
+    is exact in any order and the GPU must equal the oracle bit for bit."""
+    g = torch.Generator().manual_seed(5)
+    n, d = 48, 136
+    a = torch.randint(-7, 8, (n, d), generator=g).float()
+    a[:, 3] = 127.0                                   # row max exactly 127 -> s = 1
+    scale = 2.0 ** torch.randint(-2, 1, (n, 1), generator=g).float()
+    a = a * scale
+    a[17] = 0.0                                       # an all-zero token
+    a = a.to(torch.bfloat16)                          # exact
+    c = torch.zeros(d, d, device=dev())
+    lrc.lrc_accumulate_cov(a.to(dev()), c, quant=True)
+    _, _, ahat = oracle.qaw_fake_quant(to_np(a))
+    assert np.array_equal(lower(to_np(c)), lower(oracle.covariance_sum(ahat)))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_qaw_cov_gaussian(lrc, dtype):
+    """Products q_i (s^2 q_j) with s^2 q_j carried as bf16 hi + lo (relative 2^-16) against
+    fl32(q s) products in fp64: tolerance 2^-15 |A_hat|^T |A_hat| + accumulation term."""
+    n, d = 3000, 200
+    a = synth.activation_stream(n, d, 1.0, 4242, outlier_frac=0.02, dtype=dtype)
+    c = torch.zeros(d, d, device=dev())
+    lrc.lrc_accumulate_cov(a.to(dev()), c, quant=True)
+    _, _, ahat = oracle.qaw_fake_quant(to_np(a).astype(np.float32))
+    ah = ahat.astype(np.float64)
+    absmag = np.abs(ah).T @ np.abs(ah)
+    tol = (2.0 ** -15 + 10 * math.sqrt(n) * U32) * absmag
+    err = np.abs(lower(to_np(c)) - lower(ah.T @ ah))
+    assert np.all(err <= lower(tol) + 1e-30)
+
+
+# ----------------------------------------------------------------------------- a2..a5
+def _decompose_case(lrc, d_out, d_in, n, rank, two_sided, seed, dtype=torch.float32, quant=False):
+    a = synth.activation_stream(n, d_in, 1.2, seed, dtype=dtype)
+    b = synth.activation_stream(n, d_out, 1.2, seed + 1, dtype=dtype) if two_sided else None
+    w = synth.weight(d_out, d_in, seed + 2)
+    xs = torch.zeros(d_in, d_in, device=dev())
+    lrc.lrc_accumulate_cov(a.to(dev()), xs, quant=quant)
+    gs = None
+    if two_sided:
+        gs = torch.zeros(d_out, d_out, device=dev())
+        lrc.lrc_accumulate_cov(b.to(dev()), gs)
+    sig, left, right, info = lrc.lrc_whiten_decompose(w.to(dev()), rank, xs, n, gs, n if two_sided else 0)
+    an = to_np(a).astype(np.float32)
+    if quant:
+        an = oracle.qaw_fake_quant(an)[2]
+    ref = oracle.whiten_decompose(to_np(w), oracle.covariance_sum(an), n,
+                                  oracle.covariance_sum(to_np(b)) if two_sided else None, n if two_sided else None,
+                                  rank=rank)
+    return dict(a=an, b=None if b is None else to_np(b), w=to_np(w), sig=to_np(sig), left=to_np(left),
+                right=to_np(right), info=to_np(info), ref=ref, n=n)
+
+
+def _check_decomposition(case, rank, sig_rtol=1e-4, angle_tol=1e-3):
+    ref, sig = case["ref"], case["sig"].astype(np.float64)
+    s_ref = ref["sigma"]
+    assert np.all(case["info"] == 0)
+    # retained singular values: relative error (spec bound 1e-4)
+    rel = np.abs(sig[:rank] - s_ref[:rank]) / s_ref[:rank]
+    assert rel.max() <= sig_rtol, rel.max()
+    # discarded tail: absolute error in sigma^2 relative to sigma_1^2 (fp32 whitened weight)
+    assert np.max(np.abs(sig ** 2 - s_ref ** 2)) <= 1e-5 * s_ref[0] ** 2
+    # K-FAC loss of the truncation (the objective, independent of signs and rotations)
+    x = oracle.covariance(case["a"])
+    dw = case["w"].astype(np.float64) - case["left"].astype(np.float64) @ case["right"].astype(np.float64)
+    lx = np.linalg.cholesky(x)
+    if case["b"] is not None:
+        lg = np.linalg.cholesky(oracle.covariance(case["b"]))
+        loss = 0.5 * np.linalg.norm(lg.T @ dw @ lx) ** 2
+    else:
+        loss = 0.5 * np.linalg.norm(dw @ lx) ** 2
+    want = 0.5 * np.sum(s_ref[rank:] ** 2)
+    assert abs(loss - want) <= 1e-3 * want + 1e-6 * 0.5 * s_ref[0] ** 2
+    # leading subspaces where the spectral gap exceeds 1e-3 sigma_1 (whitened coordinates)
+    lg_ = ref["lg"]
+    lx_ = ref["lx"]
+    u_gpu = case["left"].astype(np.float64)
+    v_gpu = case["right"].astype(np.float64).T
+    u_gpu = (lg_.T @ u_gpu) if lg_ is not None else u_gpu          # = U~ S^1/2
+    v_gpu = (lx_.T @ v_gpu) if lx_ is not None else v_gpu           # = V~ S^1/2
+    for j in range(1, rank + 1):
+        if j < len(s_ref) and s_ref[j - 1] - s_ref[j] <= 1e-3 * s_ref[0]:
+            continue
+        for g, r in ((u_gpu[:, :j], ref["u"][:, :j]), (v_gpu[:, :j], ref["vt"][:j].T)):
+            q, _ = np.linalg.qr(g)
+            cosines = np.linalg.svd(q.T @ r, compute_uv=False)
+            ang = np.arccos(np.clip(cosines.min(), -1, 1))
+            assert ang <= angle_tol, (j, ang)
+
+
+def test_decompose_two_sided_fp32_config0_shape(lrc):
+    """The single-linear-layer workload: 256 x 256, 4096 fp32 tokens, two-sided, r = 64."""
+    case = _decompose_case(lrc, 256, 256, 4096, 64, True, 11)
+    _check_decomposition(case, 64)
+    # signs follow the canonical rule on the output side (d_out <= d_in): compare
+    # factor columns whose singular value is isolated by > 1e-3 sigma_1
+    s = case["ref"]["sigma"]
+    ref_left = case["ref"]["left"]
+    for i in range(64):
+        gap = min(s[i - 1] - s[i] if i else np.inf, s[i] - s[i + 1])
+        if gap > 1e-3 * s[0]:
+            np.testing.assert_allclose(case["left"][:, i], ref_left[:, i], rtol=0,
+                                       atol=2e-3 * np.abs(ref_left[:, i]).max())
+
+
+@pytest.mark.parametrize("d_out,d_in,rank", [(100, 150, 30), (150, 100, 40), (64, 64, 64), (300, 200, 7),
+                                             (33, 1, 1)])
+def test_decompose_ragged_shapes(lrc, d_out, d_in, rank):
+    case = _decompose_case(lrc, d_out, d_in, 2000, rank, True, 23 + d_out)
+    _check_decomposition(case, rank)
+
+
+def test_decompose_activation_only_bf16(lrc):
+    case = _decompose_case(lrc, 320, 256, 3000, 64, False, 31, dtype=torch.bfloat16)
+    _check_decomposition(case, 64)
+
+
+def test_decompose_qaw_two_sided(lrc):
+    case = _decompose_case(lrc, 192, 128, 3000, 64, True, 41, dtype=torch.bfloat16, quant=True)
+    _check_decomposition(case, 64)
+
+
+def test_decompose_batched_heads(lrc):
+    """Batched slices sharing one X (the per-head workload at small size)."""
+    heads, hd, d_in, n, rank = 6, 24, 200, 3000, 10
+    a = synth.activation_stream(n, d_in, 1.0, 55, outlier_frac=0.02, dtype=torch.bfloat16)
+    w = synth.weight(heads * hd, d_in, 56)
+    xs = torch.zeros(d_in, d_in, device=dev())
+    lrc.lrc_accumulate_cov(a.to(dev()), xs)
+    w3 = w.view(heads, hd, d_in).to(dev())
+    sig, left, right, info = lrc.lrc_whiten_decompose(w3, rank, xs, n)
+    assert torch.all(info == 0)
+    an = to_np(a)
+    xsum = oracle.covariance_sum(an)
+    for h in range(heads):
+        ref = oracle.whiten_decompose(to_np(w)[h * hd:(h + 1) * hd], xsum, n, rank=rank)
+        case = dict(a=an, b=None, w=to_np(w)[h * hd:(h + 1) * hd], sig=to_np(sig[h]), left=to_np(left[h]),
+                    right=to_np(right[h]), info=to_np(info[h:h + 1]), ref=ref, n=n)
+        _check_decomposition(case, rank)
+
+
+def test_decompose_identity_covariances_is_plain_svd(lrc):
+    """X = G = I (identity sums with count 1): plain truncated SVD of W (Eckart-Young)."""
+    w = synth.weight(96, 130, 3)
+    eye_in = torch.eye(130, device=dev())
+    eye_out = torch.eye(96, device=dev())
+    sig, left, right, info = lrc.lrc_whiten_decompose(w.to(dev()), 20, eye_in, 1, eye_out, 1)
+    s = np.linalg.svd(to_np(w).astype(np.float64), compute_uv=False)
+    np.testing.assert_allclose(to_np(sig), s, rtol=1e-5, atol=1e-6 * s[0])
+    wr = to_np(left).astype(np.float64) @ to_np(right).astype(np.float64)
+    np.testing.assert_allclose(np.linalg.norm(to_np(w) - wr) ** 2, np.sum(s[20:] ** 2), rtol=1e-4)
+
+
+@pytest.mark.parametrize("side", ["x", "g"])
+def test_decompose_not_positive_definite(lrc, side):
+    """A negative pivot is reported (info = pivot, or d_in + pivot for G), never patched."""
+    d_out, d_in, n = 40, 70, 500
+    a = synth.activation_stream(n, d_in, 1.0, 8, dtype=torch.float32)
+    b = synth.activation_stream(n, d_out, 1.0, 9, dtype=torch.float32)
+    an, bn = to_np(a).astype(np.float64), to_np(b).astype(np.float64)
+    xs = torch.tensor(an.T @ an, dtype=torch.float32, device=dev())
+    gs = torch.tensor(bn.T @ bn, dtype=torch.float32, device=dev())
+    p = 37 if side == "x" else 21
+    (xs if side == "x" else gs)[p, p] = -1.0
+    w = synth.weight(d_out, d_in, 10).to(dev())
+    _, _, _, info = lrc.lrc_whiten_decompose(w, 5, xs, n, gs, n, check=False)
+    ref = oracle.whiten_decompose(to_np(w), to_np(xs), n, to_np(gs), n, rank=5)
+    assert ref["info_side"] == side and ref["info"] == p + 1
+    want = p + 1 if side == "x" else d_in + p + 1
+    assert int(info[0]) == want
+    with pytest.raises(lrc.LrcError) as e:
+        lrc.lrc_whiten_decompose(w, 5, xs, n, gs, n)
+    assert e.value.status == lrc.LRC_ENOTPD
+
+
+def test_decompose_deterministic(lrc):
+    w = synth.weight(128, 200, 5).to(dev())
+    a = synth.activation_stream(1500, 200, 1.0, 6, dtype=torch.bfloat16).to(dev())
+    xs = torch.zeros(200, 200, device=dev())
+    lrc.lrc_accumulate_cov(a, xs)
+    r1 = lrc.lrc_whiten_decompose(w, 32, xs, 1500)
+    r2 = lrc.lrc_whiten_decompose(w, 32, xs, 1500)
+    for x, y in zip(r1, r2):
+        assert torch.equal(x, y)
+
+
+# ----------------------------------------------------------------------------- a6 scores
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("n,d_out,d_in,k", [(1000, 70, 90, 50), (4096, 256, 128, 128), (65, 16, 300, 16)])
+def test_fisher_scores(lrc, dtype, n, d_out, d_in, k):
+    """Same synthetic factors and streams into both sides.  fp32 projections then
+    squares: relative error per token term ~ 4 * sqrt(d) u on well-scaled terms; the sum
+    of non-negative terms keeps that relative bound -> rtol 2e-4."""
+    a = synth.activation_stream(n, d_in, 1.0, 300 + n, dtype=dtype)
+    b = synth.activation_stream(n, d_out, 1.5, 301 + n, dtype=dtype)
+    g = torch.Generator().manual_seed(k)
+    left = torch.randn(d_out, k, generator=g)
+    right = torch.randn(k, d_in, generator=g)
+    got = lrc.lrc_score_components(left.to(dev()), right.to(dev()), A=a.to(dev()), B=b.to(dev()))
+    want = oracle.fisher_scores(to_np(a), to_np(b), left.numpy(), right.numpy())
+    np.testing.assert_allclose(to_np(got), want, rtol=2e-4)
+
+
+def test_fisher_scores_streamed_chunks(lrc):
+    n, d_out, d_in, k = 3000, 40, 60, 30
+    a = synth.activation_stream(n, d_in, 1.0, 1, dtype=torch.bfloat16).to(dev())
+    b = synth.activation_stream(n, d_out, 1.5, 2, dtype=torch.bfloat16).to(dev())
+    g = torch.Generator().manual_seed(3)
+    left = torch.randn(d_out, k, generator=g).to(dev())
+    right = torch.randn(k, d_in, generator=g).to(dev())
+    one = lrc.lrc_score_components(left, right, A=a, B=b)
+    s = torch.empty(k, device=dev())
+    cuts = [0, 1000, 2100, 3000]
+    for i in range(3):
+        lrc.lrc_score_components(left, right, A=a[cuts[i]:cuts[i + 1]], B=b[cuts[i]:cuts[i + 1]], scores=s,
+                                 accumulate=i > 0, finalize=i == 2, n_total=n)
+    np.testing.assert_allclose(to_np(s), to_np(one), rtol=1e-5)
+
+
+def test_kfac_scores(lrc):
+    sig = torch.rand(77) * 3
+    left = torch.zeros(5, 77, device=dev())
+    right = torch.zeros(77, 4, device=dev())
+    got = lrc.lrc_score_components(left, right, sigma=sig.to(dev()), mode="kfac")
+    np.testing.assert_allclose(to_np(got), oracle.kfac_scores(sig.numpy()), rtol=2 * U32 * 4)
+
+
+# ----------------------------------------------------------------------------- a7 allocation
+def _alloc_case(lrc, scores_list, costs, budget):
+    offs = np.concatenate([[0], np.cumsum([len(s) for s in scores_list])]).astype(np.int64)
+    flat = np.concatenate(scores_list).astype(np.float32) if scores_list else np.zeros(0, np.float32)
+    order, n_kept, ranks, kept, info = lrc.lrc_allocate_ranks(
+        torch.tensor(flat, device=dev()), torch.tensor(offs, device=dev()),
+        torch.tensor(np.asarray(costs, np.int64), device=dev()), budget)
+    ref = oracle.allocate(scores_list, costs, budget)
+    return (to_np(order), int(to_np(n_kept)[0]), to_np(ranks), to_np(kept), int(to_np(info)[0])), ref
+
+
+def test_allocate_golden_fixture(lrc):
+    got, ref = _alloc_case(lrc, [np.array([10, 1], np.float32), np.array([16, 8, 8, 0.8], np.float32)], [5, 8], 22)
+    assert got[4] == 0
+    assert got[0].tolist() == [0, 2, 3, 4, 1, 5] == ref[0].tolist()
+    assert got[1] == 3 and got[2].tolist() == [1, 2] and got[3].tolist() == [1, 0, 1, 1, 0, 0]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_allocate_bit_exact_random(lrc, seed):
+    """Identical fp32 score arrays into both sides: order, n_kept, ranks and mask equal."""
+    rng = np.random.default_rng(seed)
+    nm = int(rng.integers(1, 40))
+    sizes = rng.integers(0, 700, nm)
+    costs = [int(c) for c in rng.integers(1, 20000, nm)]
+    lst = []
+    for m in range(nm):
+        s = (rng.standard_exponential(sizes[m]) ** 3).astype(np.float32)
+        if seed % 2:       # force many exact key ties across matrices and within
+            s = np.round(s * 4).astype(np.float32) * np.float32(costs[m] % 7 + 1)
+        lst.append(s)
+    total = sum(int(c) * int(z) for c, z in zip(costs, sizes))
+    budget = int(rng.integers(0, total + 1)) if total else 0
+    got, ref = _alloc_case(lrc, lst, costs, budget)
+    assert got[4] == 0
+    assert got[0].tolist() == ref[0].tolist()
+    assert got[1] == ref[1]
+    assert got[2].tolist() == ref[2].tolist()
+    assert got[3].tolist() == ref[3].tolist()
+
+
+def test_allocate_large_ties(lrc):
+    """Tens of thousands of items (several sort tiles), keys drawn from 50 values."""
+    rng = np.random.default_rng(9)
+    lst = [rng.integers(0, 50, 9000).astype(np.float32) for _ in range(7)]
+    costs = [8192, 8192, 8192, 8192, 15104, 15104, 15104]
+    got, ref = _alloc_case(lrc, lst, costs, 200_000_000)
+    assert got[0].tolist() == ref[0].tolist() and got[1] == ref[1] and got[2].tolist() == ref[2].tolist()
+
+
+def test_allocate_edge_cases(lrc):
+    # zero budget keeps nothing, a budget above the total keeps everything
+    lst = [np.array([1, 2, 3], np.float32), np.zeros(0, np.float32), np.array([5], np.float32)]
+    got, ref = _alloc_case(lrc, lst, [3, 4, 5], 0)
+    assert got[1] == 0 == ref[1] and got[2].tolist() == [0, 0, 0]
+    got, ref = _alloc_case(lrc, lst, [3, 4, 5], 10 ** 12)
+    assert got[1] == 4 == ref[1] and got[2].tolist() == [3, 0, 1]
+    # -0.0 and +0.0 are the same key
+    got, ref = _alloc_case(lrc, [np.array([0.0, -0.0, 0.0], np.float32)], [2], 4)
+    assert got[0].tolist() == ref[0].tolist() == [0, 1, 2]
+
+
+def test_allocate_rejects_nan_and_bad_cost(lrc):
+    flat = torch.tensor([1.0, float("nan"), 2.0], device=dev())
+    offs = torch.tensor([0, 3], dtype=torch.int64, device=dev())
+    _, _, _, _, info = lrc.lrc_allocate_ranks(flat, offs, torch.tensor([4], dtype=torch.int64, device=dev()), 10)
+    assert int(info[0]) == lrc.LRC_ENONFINITE
+    flat = torch.tensor([1.0, 2.0, 2.0], device=dev())
+    _, _, _, _, info = lrc.lrc_allocate_ranks(flat, offs, torch.tensor([0], dtype=torch.int64, device=dev()), 10)
+    assert int(info[0]) == lrc.LRC_EINVAL
