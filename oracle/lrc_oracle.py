@@ -116,8 +116,12 @@ def whiten(w, lx=None, lg=None):
 # a4: decomposition of the whitened weight
 # ---------------------------------------------------------------------------
 def truncated_svd(wt):
-    """Thin SVD of the whitened weight with LAPACK dgesvd, singular values descending."""
-    u, s, vt = scipy.linalg.svd(wt, full_matrices=False, lapack_driver="gesvd")
+    """Thin SVD of the whitened weight (LAPACK dgesdd), singular values descending.
+
+    The pages only say that the whitened weight is decomposed by SVD; any backward-
+    stable thin SVD is that definition.  dgesdd is used because the host's dgesvd
+    takes minutes at 4096 x 4096."""
+    u, s, vt = scipy.linalg.svd(wt, full_matrices=False, lapack_driver="gesdd")
     order = np.argsort(-s, kind="stable")
     return u[:, order], s[order], vt[order, :]
 
