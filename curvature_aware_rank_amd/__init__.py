@@ -170,9 +170,23 @@ def lrc_whiten_decompose(W: torch.Tensor, rank: int, Xsum=None, n_x: int = 0, Gs
     return sigma, left, right, info
 
 
-def lrc_score_components(left: torch.Tensor, right: torch.Tensor, sigma=None, A=None, B=None, mode: str = "fisher",
+def lrc_score_components(left=None, right=None, sigma=None, A=None, B=None, mode: str = "fisher",
                          scores=None, accumulate: bool = False, finalize: bool = True, n_total=None):
-    """Per-component scores; returns the scores tensor (k,) fp32."""
+    """Per-component scores; returns the scores tensor (k,) fp32.
+
+    mode="fisher": needs left (d_out, k), right (k, d_in), A (n, d_in), B (n, d_out).
+    mode="kfac":   needs sigma (k,) only."""
+    if mode == "kfac":
+        _dev(sigma, "sigma")
+        k = sigma.numel()
+        if scores is None:
+            scores = torch.empty(k, dtype=torch.float32, device=sigma.device)
+        _check(lib.lrc_score_components(None, None, LRC_F32, 0, 1, 1, None, None, _ptr(sigma), k,
+                                        LRC_SCORE_KFAC, 0, 1, 1, _ptr(scores), None, 0, _stream()),
+               "lrc_score_components")
+        return scores
+    if mode != "fisher":
+        raise ValueError("mode is 'fisher' or 'kfac'")
     _dev(left, "left")
     d_out, k = left.shape
     kk, d_in = right.shape
@@ -180,13 +194,6 @@ def lrc_score_components(left: torch.Tensor, right: torch.Tensor, sigma=None, A=
         raise ValueError("left and right disagree on k")
     if scores is None:
         scores = torch.empty(k, dtype=torch.float32, device=left.device)
-    if mode == "kfac":
-        _check(lib.lrc_score_components(None, None, LRC_F32, 0, d_in, d_out, _ptr(left), _ptr(right), _ptr(sigma), k,
-                                        LRC_SCORE_KFAC, 0, 1, 1, _ptr(scores), None, 0, _stream()),
-               "lrc_score_components")
-        return scores
-    if mode != "fisher":
-        raise ValueError("mode is 'fisher' or 'kfac'")
     _dev(A, "A")
     _dev(B, "B")
     n = A.shape[0]

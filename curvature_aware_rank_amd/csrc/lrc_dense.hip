@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(unsigned flags, int m, in
 
 // ---------------------------------------------------------------------------------
 // fp64 Gram from an fp32 matrix (products exact in fp64): G = M M^T or M^T M, lower
-// tiles computed and mirrored.  64 x 64 tiles, 256 threads with 4 x 4 outputs each.
+// triangle only.  64 x 64 tiles, 256 threads with 4 x 4 outputs each.
 // ---------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void gram_f64_kernel(bool rows, int p, int q, const float* __restrict__ M,
                                                        int64_t ldm, int64_t sM, double* __restrict__ G,
@@ -149,10 +149,7 @@ __global__ __launch_bounds__(256) void gram_f64_kernel(bool rows, int p, int q, 
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = ti * 64 + ty * 4 + i, c = tj * 64 + tx * 4 + j;
-      if (r < dim && c < dim && r >= c) {
-        G[int64_t(r) * ldg + c] = acc[i][j];
-        G[int64_t(c) * ldg + r] = acc[i][j];
-      }
+      if (r < dim && c < dim && r >= c) G[int64_t(r) * ldg + c] = acc[i][j];
     }
 }
 

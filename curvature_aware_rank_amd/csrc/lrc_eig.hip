@@ -2,17 +2,22 @@
 // fp64 (Swift-SVD technical summary 2A: one eigendecomposition of the aggregated output
 // covariance yields the singular values and vectors of the whitened weight).
 //
-// The k x k Gram is padded to kp = multiple of 64 with decoupled diagonal entries
-// -(trace + 1) (they stay exactly decoupled and sort last), cut into 32-wide blocks,
-// and swept with a round-robin (circle) ordering of block pairs.  Per round:
-//   * one workgroup per pair loads the 64 x 64 pair block into LDS and runs a few
-//     cyclic Jacobi sweeps on it (32 disjoint rotations per step, the rotated 2 x 2
-//     entries set exactly), accumulating the pair rotation J (64 x 64);
+// The k x k Gram (lower triangle stored) is padded to kp = multiple of 64 with
+// decoupled diagonal entries -(trace + 1) (they stay exactly decoupled and sort last),
+// cut into 32-wide blocks, and swept with a round-robin (circle) ordering of block pairs.
+// Per round:
+//   * one workgroup per pair loads the 64 x 64 pair block into LDS; if any entry is
+//     above threshold it runs one cyclic Jacobi sweep on it (32 disjoint rotations per
+//     step, the rotated 2 x 2 entries set exactly), accumulating the pair rotation J,
+//     and orders the pair's eigenvalues descending (the larger half to the lower block:
+//     fewer outer sweeps, and the blocks end up sorted);
 //   * C <- J^T C J and V <- V J are applied tile by tile with fp64 MFMA
-//     (v_mfma_f64_16x16x4f64); diagonal pair tiles take the pair solver's result.
+//     (v_mfma_f64_16x16x4f64); diagonal pair tiles take the pair solver's result, and
+//     a pair that needed nothing contributes the identity.
 // A sweep in which no pair needed a rotation ends the iteration; the host reads one
 // counter per sweep.  Rotations are skipped when |a_pq| <= max(tol_r sqrt|a_pp a_qq|,
 // floor_rel * trace), which bounds what is left off the diagonal.
+#include <stdio.h>
 #include <stdlib.h>
 
 #include <vector>
@@ -25,8 +30,8 @@ namespace {
 constexpr int JB = 32;       // block width
 constexpr int PD = 2 * JB;   // pair dimension
 constexpr int PP = PD + 1;   // LDS row pitch in doubles
-constexpr double TOL_R = 1e-12;
-constexpr double FLOOR_REL = 1e-13;
+constexpr double TOL_R_DEFAULT = 1e-10;
+constexpr double FLOOR_REL_DEFAULT = 1e-12;
 constexpr int MAX_SWEEPS = 40;
 
 __device__ __forceinline__ int rr_pos(int pos, int r, int n) { return pos == 0 ? 0 : 1 + ((pos - 1 + r) % (n - 1)); }
@@ -41,7 +46,7 @@ __device__ __forceinline__ int gidx(int i, int p, int q) { return i < JB ? p * J
 
 // trace, pad value and rotation floor per batch item
 __global__ void jacobi_scalars_kernel(const double* __restrict__ A, int k, int kp, int64_t sA, double* __restrict__ pad,
-                                      double* __restrict__ floor_v) {
+                                      double* __restrict__ floor_v, double floor_rel) {
   __shared__ double red[256];
   const double* a = A + blockIdx.x * sA;
   double s = 0.0;
@@ -54,7 +59,7 @@ __global__ void jacobi_scalars_kernel(const double* __restrict__ A, int k, int k
   }
   if (threadIdx.x == 0) {
     pad[blockIdx.x] = -(red[0] + 1.0);
-    floor_v[blockIdx.x] = FLOOR_REL * red[0];
+    floor_v[blockIdx.x] = floor_rel * red[0];
   }
 }
 
@@ -79,36 +84,55 @@ __global__ void zero_i32_kernel(int* p, int n) {
 __global__ __launch_bounds__(256) void pair_eig_kernel(const double* __restrict__ Ad, int kp, int64_t sA, int nb,
                                                        int round, double* __restrict__ Jbuf, double* __restrict__ Sbuf,
                                                        int* __restrict__ changed, int* __restrict__ sweep_count,
-                                                       const double* __restrict__ floors, int max_inner) {
+                                                       const double* __restrict__ floors, double tol_r,
+                                                       int max_inner) {
   __shared__ double S[PD][PP];
   __shared__ double J[PD][PP];
   __shared__ double rc[32], rs[32], rt[32], rapp[32], raqq[32], rapq[32];
   __shared__ int rp[32], rq[32], ract[32];
   __shared__ int nrot[2];
-  __shared__ int nsweep;
-  __shared__ int any_rot;
+  __shared__ int perm[PD];
   const int pair = blockIdx.x, bt = blockIdx.y, tid = threadIdx.x;
   const int npairs = nb / 2;
   const double* A = Ad + bt * sA;
   int p, q;
   pair_of(pair, round, nb, p, q);
+  // the pair block's lower triangle is stored (p < q keeps local and global order equal)
   for (int e = tid; e < PD * PD; e += 256) {
     const int i = e / PD, j = e % PD;
-    S[i][j] = A[int64_t(gidx(i, p, q)) * kp + gidx(j, p, q)];
-    J[i][j] = (i == j) ? 1.0 : 0.0;
+    if (i >= j) {
+      const double v = A[int64_t(gidx(i, p, q)) * kp + gidx(j, p, q)];
+      S[i][j] = v;
+      S[j][i] = v;
+    }
   }
-  if (tid == 0) any_rot = 0;
+  __syncthreads();
   const double floor_v = floors[bt];
+  // nothing to do when every off-diagonal entry is below its threshold and the
+  // diagonal is already descending
+  int need = 0;
+  for (int e = tid; e < PD * PD; e += 256) {
+    const int i = e / PD, j = e % PD;
+    if (i > j) need |= fabs(S[i][j]) > fmax(tol_r * sqrt(fabs(S[i][i] * S[j][j])), floor_v);
+  }
+  if (tid < PD - 1) need |= S[tid][tid] < S[tid + 1][tid + 1];
+  need = __syncthreads_or(need);
+  if (!need) {
+    if (tid == 0) changed[bt * npairs + pair] = 0;
+    return;
+  }
+  for (int e = tid; e < PD * PD; e += 256) J[e / PD][e % PD] = (e / PD == e % PD) ? 1.0 : 0.0;
+  __syncthreads();
+  // update role: wave wv owns rotations 8*wv .. 8*wv+7; lane = row / column index
+  const int lane = tid & 63, wv = tid >> 6;
   for (int sw = 0; sw < max_inner; ++sw) {
-    __syncthreads();
-    if (tid == 0) nsweep = 0;
-    __syncthreads();
+    int sweep_rot = 0;
     for (int r = 0; r < PD - 1; ++r) {
       if (tid < 32) {
         const int a = rr_pos(tid, r, PD), c = rr_pos(PD - 1 - tid, r, PD);
         const int pi = min(a, c), qi = max(a, c);
         const double apq = S[pi][qi], app = S[pi][pi], aqq = S[qi][qi];
-        const double thr = fmax(TOL_R * sqrt(fabs(app * aqq)), floor_v);
+        const double thr = fmax(tol_r * sqrt(fabs(app * aqq)), floor_v);
         const bool act = fabs(apq) > thr;
         double t = 0.0, cc = 1.0, ss = 0.0;
         if (act) {
@@ -125,29 +149,33 @@ __global__ __launch_bounds__(256) void pair_eig_kernel(const double* __restrict_
       __syncthreads();
       const int nr = nrot[r & 1];
       if (nr == 0) continue;
-      for (int e = tid; e < 32 * PD; e += 256) {
-        const int w = e / PD, j = e % PD;
+      sweep_rot += nr;
+      // rows p, q of S (lane = column)
+      for (int u = 0; u < 8; ++u) {
+        const int w = wv * 8 + u;
         if (!ract[w]) continue;
-        const int pi = rp[w], qi = rq[w];
-        const double cc = rc[w], ss = rs[w];
-        const double sp = S[pi][j], sq = S[qi][j];
-        S[pi][j] = cc * sp - ss * sq;
-        S[qi][j] = ss * sp + cc * sq;
+        const int pw = rp[w], qw = rq[w];
+        const double cw = rc[w], sn = rs[w];
+        const double sp = S[pw][lane], sq = S[qw][lane];
+        S[pw][lane] = cw * sp - sn * sq;
+        S[qw][lane] = sn * sp + cw * sq;
       }
       __syncthreads();
-      for (int e = tid; e < 32 * PD; e += 256) {
-        const int w = e / PD, i = e % PD;
+      // columns p, q of S and J (lane = row)
+      for (int u = 0; u < 8; ++u) {
+        const int w = wv * 8 + u;
         if (!ract[w]) continue;
-        const int pi = rp[w], qi = rq[w];
-        const double cc = rc[w], ss = rs[w];
-        const double sp = S[i][pi], sq = S[i][qi];
-        S[i][pi] = cc * sp - ss * sq;
-        S[i][qi] = ss * sp + cc * sq;
-        const double jp = J[i][pi], jq = J[i][qi];
-        J[i][pi] = cc * jp - ss * jq;
-        J[i][qi] = ss * jp + cc * jq;
+        const int pw = rp[w], qw = rq[w];
+        const double cw = rc[w], sn = rs[w];
+        const double sp = S[lane][pw], sq = S[lane][qw];
+        S[lane][pw] = cw * sp - sn * sq;
+        S[lane][qw] = sn * sp + cw * sq;
+        const double jp = J[lane][pw], jq = J[lane][qw];
+        J[lane][pw] = cw * jp - sn * jq;
+        J[lane][qw] = sn * jp + cw * jq;
       }
       __syncthreads();
+      // the rotated 2x2 entries exactly (same wave computes the next round's rotations)
       if (tid < 32 && ract[tid]) {
         const int pi = rp[tid], qi = rq[tid];
         S[pi][qi] = 0.0;
@@ -155,25 +183,30 @@ __global__ __launch_bounds__(256) void pair_eig_kernel(const double* __restrict_
         S[pi][pi] = rapp[tid] - rt[tid] * rapq[tid];
         S[qi][qi] = raqq[tid] + rt[tid] * rapq[tid];
       }
-      if (tid == 0) {
-        nsweep += nr;
-        any_rot = 1;
-      }
-      __syncthreads();
     }
-    __syncthreads();
-    if (nsweep == 0) break;
+    if (sweep_rot == 0) break;
+  }
+  __syncthreads();
+  // eigenvalues of the pair descending: the larger half moves to the lower block index
+  if (tid < PD) {
+    const double di = S[tid][tid];
+    int rank = 0;
+    for (int j = 0; j < PD; ++j) {
+      const double dj = S[j][j];
+      rank += (dj > di) || (dj == di && j < tid);
+    }
+    perm[rank] = tid;
   }
   __syncthreads();
   const int64_t slot = (int64_t(bt) * npairs + pair) * (PD * PD);
   for (int e = tid; e < PD * PD; e += 256) {
     const int i = e / PD, j = e % PD;
-    Jbuf[slot + e] = J[i][j];
-    Sbuf[slot + e] = S[i][j];
+    Jbuf[slot + e] = J[i][perm[j]];
+    Sbuf[slot + e] = S[perm[i]][perm[j]];
   }
   if (tid == 0) {
-    changed[bt * npairs + pair] = any_rot;
-    if (any_rot) atomicAdd(&sweep_count[bt], 1);
+    changed[bt * npairs + pair] = 1;
+    atomicAdd(&sweep_count[bt], 1);
   }
 }
 
@@ -219,6 +252,29 @@ __device__ __forceinline__ void acc_to_lds(const f64x4 (&acc)[2][2], double (*D)
       for (int r = 0; r < 4; ++r) D[wi * 32 + i * 16 + 4 * r + (lane >> 4)][wj * 32 + j * 16 + (lane & 15)] = acc[i][j][r];
 }
 
+// Block (bp, bq) of the symmetric matrix whose lower triangle is stored: element (i, j)
+// of a 32 x 32 sub-block lives at row max, column min of its global indices.  Sub-blocks
+// of two different blocks are wholly above or below the diagonal, so each is read or
+// written in one orientation with the contiguous index running fastest.
+template <bool LOAD>
+__device__ __forceinline__ void sym_tile_io(double* __restrict__ A, int kp, int p1, int p2, int q1, int q2,
+                                            double (*T)[PP]) {
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb) {
+    const int a = sb >> 1, b = sb & 1;
+    const int bp = a ? p2 : p1, bq = b ? q2 : q1;
+    const bool direct = bp > bq;
+    for (int e = threadIdx.x; e < JB * JB; e += 256) {
+      const int u = e / JB, v = e % JB;                 // v runs fastest
+      const int i = direct ? u : v, j = direct ? v : u;   // local row in P, local col in Q
+      const int gi = bp * JB + i, gj = bq * JB + j;
+      double* cell = direct ? &A[int64_t(gi) * kp + gj] : &A[int64_t(gj) * kp + gi];
+      if (LOAD) T[a * JB + i][b * JB + j] = *cell;
+      else *cell = T[a * JB + i][b * JB + j];
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void jacobi_apply_kernel(double* __restrict__ Ad, double* __restrict__ Vd, int kp,
                                                            int64_t sA, int nb, int round,
                                                            const double* __restrict__ Jbuf,
@@ -243,35 +299,33 @@ __global__ __launch_bounds__(256) void jacobi_apply_kernel(double* __restrict__ 
     pair_of(P, round, nb, p1, p2);
     pair_of(Q, round, nb, q1, q2);
     if (P == Q) {
+      // the pair solver's rotated block; its lower triangle is stored
       const double* s = Sbuf + jbase + int64_t(P) * PD * PD;
       for (int e = tid; e < PD * PD; e += 256) {
         const int i = e / PD, j = e % PD;
-        A[int64_t(gidx(i, p1, p2)) * kp + gidx(j, p1, p2)] = s[e];
+        if (i >= j) A[int64_t(gidx(i, p1, p2)) * kp + gidx(j, p1, p2)] = s[e];
       }
       return;
     }
-    const double* jq = Jbuf + jbase + int64_t(Q) * PD * PD;
-    const double* jp = Jbuf + jbase + int64_t(P) * PD * PD;
-    for (int e = tid; e < PD * PD; e += 256) {
-      const int i = e / PD, j = e % PD;
-      T0[i][j] = A[int64_t(gidx(i, p1, p2)) * kp + gidx(j, q1, q2)];
-      T1[i][j] = jq[e];
+    sym_tile_io<true>(A, kp, p1, p2, q1, q2, T0);
+    if (chQ) {
+      const double* jq = Jbuf + jbase + int64_t(Q) * PD * PD;
+      for (int e = tid; e < PD * PD; e += 256) T1[e / PD][e % PD] = jq[e];
+      __syncthreads();
+      mm64<false>(T0, T1, acc);   // C_PQ J_Q
+      __syncthreads();
+      acc_to_lds(acc, T0);
+    }
+    if (chP) {
+      const double* jp = Jbuf + jbase + int64_t(P) * PD * PD;
+      for (int e = tid; e < PD * PD; e += 256) T1[e / PD][e % PD] = jp[e];
+      __syncthreads();
+      mm64<true>(T1, T0, acc);    // J_P^T (C_PQ J_Q)
+      __syncthreads();
+      acc_to_lds(acc, T0);
     }
     __syncthreads();
-    mm64<false>(T0, T1, acc);  // C_PQ J_Q
-    __syncthreads();
-    acc_to_lds(acc, T0);
-    for (int e = tid; e < PD * PD; e += 256) T1[e / PD][e % PD] = jp[e];
-    __syncthreads();
-    mm64<true>(T1, T0, acc);   // J_P^T (C_PQ J_Q)
-    __syncthreads();
-    acc_to_lds(acc, T0);
-    __syncthreads();
-    for (int e = tid; e < PD * PD; e += 256) {
-      const int i = e / PD, j = e % PD;
-      A[int64_t(gidx(i, p1, p2)) * kp + gidx(j, q1, q2)] = T0[i][j];
-      A[int64_t(gidx(i, q1, q2)) * kp + gidx(j, p1, p2)] = T0[j][i];
-    }
+    sym_tile_io<false>(A, kp, p1, p2, q1, q2, T0);
   } else {
     t -= n_ctiles;
     const int rb = t / npairs, Q = t % npairs;
@@ -296,24 +350,29 @@ __global__ __launch_bounds__(256) void jacobi_apply_kernel(double* __restrict__ 
   }
 }
 
-// diagonal -> dvec; rank by value (descending, index breaks ties) -> perm, lam
-__global__ void diag_kernel(const double* __restrict__ A, int k, int kp, int64_t sA, double* __restrict__ dvec) {
+// diagonal -> dvec (all kp positions: the in-pair sorting moves the decoupled padding
+// entries around, and they rank last because they are below every eigenvalue of the
+// positive semi-definite Gram); rank descending, index breaks ties -> perm, sigma
+__global__ void diag_kernel(const double* __restrict__ A, int kp, int64_t sA, double* __restrict__ dvec) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < k) dvec[int64_t(blockIdx.y) * k + i] = A[blockIdx.y * sA + int64_t(i) * kp + i];
+  if (i < kp) dvec[int64_t(blockIdx.y) * kp + i] = A[blockIdx.y * sA + int64_t(i) * kp + i];
 }
 
-__global__ void rank_kernel(const double* __restrict__ dvec, int k, int* __restrict__ perm, float* __restrict__ sigma) {
+__global__ void rank_kernel(const double* __restrict__ dvec, int k, int kp, int* __restrict__ perm,
+                            float* __restrict__ sigma) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  const double* d = dvec + int64_t(blockIdx.y) * k;
-  if (i >= k) return;
+  const double* d = dvec + int64_t(blockIdx.y) * kp;
+  if (i >= kp) return;
   const double di = d[i];
   int rank = 0;
-  for (int j = 0; j < k; ++j) {
+  for (int j = 0; j < kp; ++j) {
     const double dj = d[j];
     rank += (dj > di) || (dj == di && j < i);
   }
-  perm[int64_t(blockIdx.y) * k + rank] = i;
-  sigma[int64_t(blockIdx.y) * k + rank] = float(sqrt(fmax(di, 0.0)));
+  if (rank < k) {
+    perm[int64_t(blockIdx.y) * k + rank] = i;
+    sigma[int64_t(blockIdx.y) * k + rank] = float(sqrt(fmax(di, 0.0)));
+  }
 }
 
 __global__ void transpose_f64_kernel(const double* __restrict__ S, double* __restrict__ D, int n, int64_t sS) {
@@ -373,17 +432,24 @@ JWs carve_jacobi(Carve& cv, int64_t k, int64_t batch) {
   w.S = cv.take<double>(size_t(batch * npairs * PD * PD));
   w.pad = cv.take<double>(size_t(batch));
   w.floor_v = cv.take<double>(size_t(batch));
-  w.dvec = cv.take<double>(size_t(batch * k));
+  w.dvec = cv.take<double>(size_t(batch * kp));
   w.changed = cv.take<int>(size_t(batch * npairs));
   w.count = cv.take<int>(size_t(batch));
   w.perm = cv.take<int>(size_t(batch * k));
   return w;
 }
 
+// tuning overrides (measurement only): LRC_JACOBI_TOL, LRC_JACOBI_FLOOR, LRC_JACOBI_INNER
+double env_double(const char* name, double dflt) {
+  const char* e = getenv(name);
+  const double v = e ? atof(e) : 0.0;
+  return v > 0.0 ? v : dflt;
+}
+
 int inner_sweeps() {
   const char* e = getenv("LRC_JACOBI_INNER");
   const int v = e ? atoi(e) : 0;
-  return v > 0 ? v : 4;
+  return v > 0 ? v : 1;
 }
 
 }  // namespace
@@ -407,8 +473,11 @@ lrc_status jacobi_eig(hipStream_t st, double* A, int64_t k, int64_t batch, int64
   const int n_ctiles = npairs * (npairs + 1) / 2;
   const int n_vtiles = int(kp / 64) * npairs;
   const int max_inner = inner_sweeps();
+  const double tol_r = env_double("LRC_JACOBI_TOL", TOL_R_DEFAULT);
+  const double floor_rel = env_double("LRC_JACOBI_FLOOR", FLOOR_REL_DEFAULT);
+  const bool debug = getenv("LRC_DEBUG") != nullptr;
 
-  jacobi_scalars_kernel<<<unsigned(batch), 256, 0, st>>>(A, int(k), int(kp), sA, w.pad, w.floor_v);
+  jacobi_scalars_kernel<<<unsigned(batch), 256, 0, st>>>(A, int(k), int(kp), sA, w.pad, w.floor_v, floor_rel);
   LRC_LAUNCHED();
   jacobi_init_kernel<<<dim3(unsigned(kp), unsigned(batch)), 256, 0, st>>>(A, w.V, int(k), int(kp), sA, w.pad);
   LRC_LAUNCHED();
@@ -420,7 +489,8 @@ lrc_status jacobi_eig(hipStream_t st, double* A, int64_t k, int64_t batch, int64
     LRC_LAUNCHED();
     for (int r = 0; r < nb - 1; ++r) {
       pair_eig_kernel<<<dim3(unsigned(npairs), unsigned(batch)), 256, 0, st>>>(A, int(kp), sA, nb, r, w.J, w.S,
-                                                                              w.changed, w.count, w.floor_v, max_inner);
+                                                                              w.changed, w.count, w.floor_v, tol_r,
+                                                                              max_inner);
       LRC_LAUNCHED();
       jacobi_apply_kernel<<<dim3(unsigned(n_ctiles + n_vtiles), unsigned(batch)), 256, 0, st>>>(
           A, w.V, int(kp), sA, nb, r, w.J, w.S, w.changed, n_ctiles);
@@ -430,15 +500,17 @@ lrc_status jacobi_eig(hipStream_t st, double* A, int64_t k, int64_t batch, int64
     LRC_HIP(hipStreamSynchronize(st));
     bool any = false;
     for (int c : counts) any |= (c != 0);
+    if (debug) fprintf(stderr, "lrc jacobi k=%lld sweep %d: pairs rotated %d (item 0)\n", (long long)k, sweep, counts[0]);
     if (!any) {
       converged = true;
       break;
     }
   }
 
-  diag_kernel<<<dim3(unsigned(cdiv(k, 256)), unsigned(batch)), 256, 0, st>>>(A, int(k), int(kp), sA, w.dvec);
+  diag_kernel<<<dim3(unsigned(cdiv(kp, 256)), unsigned(batch)), 256, 0, st>>>(A, int(kp), sA, w.dvec);
   LRC_LAUNCHED();
-  rank_kernel<<<dim3(unsigned(cdiv(k, 256)), unsigned(batch)), 256, 0, st>>>(w.dvec, int(k), w.perm, sigma);
+  rank_kernel<<<dim3(unsigned(cdiv(kp, 256)), unsigned(batch)), 256, 0, st>>>(w.dvec, int(k), int(kp), w.perm,
+                                                                            sigma);
   LRC_LAUNCHED();
   // V^T into A's storage (A is no longer needed)
   transpose_f64_kernel<<<dim3(unsigned(kp / 32), unsigned(kp / 32), unsigned(batch)), dim3(32, 8), 0, st>>>(w.V, A,

@@ -328,9 +328,7 @@ def test_fisher_scores_streamed_chunks(lrc):
 
 def test_kfac_scores(lrc):
     sig = torch.rand(77) * 3
-    left = torch.zeros(5, 77, device=dev())
-    right = torch.zeros(77, 4, device=dev())
-    got = lrc.lrc_score_components(left, right, sigma=sig.to(dev()), mode="kfac")
+    got = lrc.lrc_score_components(sigma=sig.to(dev()), mode="kfac")
     np.testing.assert_allclose(to_np(got), oracle.kfac_scores(sig.numpy()), rtol=2 * U32 * 4)
 
 
