@@ -81,135 +81,6 @@ __global__ void zero_i32_kernel(int* p, int n) {
   if (i < n) p[i] = 0;
 }
 
-__global__ __launch_bounds__(256) void pair_eig_kernel(const double* __restrict__ Ad, int kp, int64_t sA, int nb,
-                                                       int round, double* __restrict__ Jbuf, double* __restrict__ Sbuf,
-                                                       int* __restrict__ changed, int* __restrict__ sweep_count,
-                                                       const double* __restrict__ floors, double tol_r,
-                                                       int max_inner) {
-  __shared__ double S[PD][PP];
-  __shared__ double J[PD][PP];
-  __shared__ double rc[32], rs[32], rt[32], rapp[32], raqq[32], rapq[32];
-  __shared__ int rp[32], rq[32], ract[32];
-  __shared__ int nrot[2];
-  __shared__ int perm[PD];
-  const int pair = blockIdx.x, bt = blockIdx.y, tid = threadIdx.x;
-  const int npairs = nb / 2;
-  const double* A = Ad + bt * sA;
-  int p, q;
-  pair_of(pair, round, nb, p, q);
-  // the pair block's lower triangle is stored (p < q keeps local and global order equal)
-  for (int e = tid; e < PD * PD; e += 256) {
-    const int i = e / PD, j = e % PD;
-    if (i >= j) {
-      const double v = A[int64_t(gidx(i, p, q)) * kp + gidx(j, p, q)];
-      S[i][j] = v;
-      S[j][i] = v;
-    }
-  }
-  __syncthreads();
-  const double floor_v = floors[bt];
-  // nothing to do when every off-diagonal entry is below its threshold and the
-  // diagonal is already descending
-  int need = 0;
-  for (int e = tid; e < PD * PD; e += 256) {
-    const int i = e / PD, j = e % PD;
-    if (i > j) need |= fabs(S[i][j]) > fmax(tol_r * sqrt(fabs(S[i][i] * S[j][j])), floor_v);
-  }
-  if (tid < PD - 1) need |= S[tid][tid] < S[tid + 1][tid + 1];
-  need = __syncthreads_or(need);
-  if (!need) {
-    if (tid == 0) changed[bt * npairs + pair] = 0;
-    return;
-  }
-  for (int e = tid; e < PD * PD; e += 256) J[e / PD][e % PD] = (e / PD == e % PD) ? 1.0 : 0.0;
-  __syncthreads();
-  // update role: wave wv owns rotations 8*wv .. 8*wv+7; lane = row / column index
-  const int lane = tid & 63, wv = tid >> 6;
-  for (int sw = 0; sw < max_inner; ++sw) {
-    int sweep_rot = 0;
-    for (int r = 0; r < PD - 1; ++r) {
-      if (tid < 32) {
-        const int a = rr_pos(tid, r, PD), c = rr_pos(PD - 1 - tid, r, PD);
-        const int pi = min(a, c), qi = max(a, c);
-        const double apq = S[pi][qi], app = S[pi][pi], aqq = S[qi][qi];
-        const double thr = fmax(tol_r * sqrt(fabs(app * aqq)), floor_v);
-        const bool act = fabs(apq) > thr;
-        double t = 0.0, cc = 1.0, ss = 0.0;
-        if (act) {
-          const double tau = (aqq - app) / (2.0 * apq);
-          t = (tau >= 0.0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
-          cc = 1.0 / sqrt(1.0 + t * t);
-          ss = t * cc;
-        }
-        rp[tid] = pi; rq[tid] = qi; rc[tid] = cc; rs[tid] = ss; rt[tid] = t;
-        rapp[tid] = app; raqq[tid] = aqq; rapq[tid] = apq; ract[tid] = act ? 1 : 0;
-        const unsigned long long bal = __ballot(act);
-        if (tid == 0) nrot[r & 1] = __popcll(bal);
-      }
-      __syncthreads();
-      const int nr = nrot[r & 1];
-      if (nr == 0) continue;
-      sweep_rot += nr;
-      // rows p, q of S (lane = column)
-      for (int u = 0; u < 8; ++u) {
-        const int w = wv * 8 + u;
-        if (!ract[w]) continue;
-        const int pw = rp[w], qw = rq[w];
-        const double cw = rc[w], sn = rs[w];
-        const double sp = S[pw][lane], sq = S[qw][lane];
-        S[pw][lane] = cw * sp - sn * sq;
-        S[qw][lane] = sn * sp + cw * sq;
-      }
-      __syncthreads();
-      // columns p, q of S and J (lane = row)
-      for (int u = 0; u < 8; ++u) {
-        const int w = wv * 8 + u;
-        if (!ract[w]) continue;
-        const int pw = rp[w], qw = rq[w];
-        const double cw = rc[w], sn = rs[w];
-        const double sp = S[lane][pw], sq = S[lane][qw];
-        S[lane][pw] = cw * sp - sn * sq;
-        S[lane][qw] = sn * sp + cw * sq;
-        const double jp = J[lane][pw], jq = J[lane][qw];
-        J[lane][pw] = cw * jp - sn * jq;
-        J[lane][qw] = sn * jp + cw * jq;
-      }
-      __syncthreads();
-      // the rotated 2x2 entries exactly (same wave computes the next round's rotations)
-      if (tid < 32 && ract[tid]) {
-        const int pi = rp[tid], qi = rq[tid];
-        S[pi][qi] = 0.0;
-        S[qi][pi] = 0.0;
-        S[pi][pi] = rapp[tid] - rt[tid] * rapq[tid];
-        S[qi][qi] = raqq[tid] + rt[tid] * rapq[tid];
-      }
-    }
-    if (sweep_rot == 0) break;
-  }
-  __syncthreads();
-  // eigenvalues of the pair descending: the larger half moves to the lower block index
-  if (tid < PD) {
-    const double di = S[tid][tid];
-    int rank = 0;
-    for (int j = 0; j < PD; ++j) {
-      const double dj = S[j][j];
-      rank += (dj > di) || (dj == di && j < tid);
-    }
-    perm[rank] = tid;
-  }
-  __syncthreads();
-  const int64_t slot = (int64_t(bt) * npairs + pair) * (PD * PD);
-  for (int e = tid; e < PD * PD; e += 256) {
-    const int i = e / PD, j = e % PD;
-    Jbuf[slot + e] = J[i][perm[j]];
-    Sbuf[slot + e] = S[perm[i]][perm[j]];
-  }
-  if (tid == 0) {
-    changed[bt * npairs + pair] = 1;
-    atomicAdd(&sweep_count[bt], 1);
-  }
-}
-
 // D(64x64) = op(X) * Y with X, Y in LDS (pitch PP).  transX: X element (i,k) read as X[k][i].
 // Wave w computes the 32 x 32 quadrant (w>>1, w&1) as 2 x 2 blocks of 16 x 16.
 // Fragment layout of v_mfma_f64_16x16x4f64 (checked on gfx950): A[i = l%16][k = l/16],
@@ -275,79 +146,261 @@ __device__ __forceinline__ void sym_tile_io(double* __restrict__ A, int kp, int 
   }
 }
 
-__global__ __launch_bounds__(256) void jacobi_apply_kernel(double* __restrict__ Ad, double* __restrict__ Vd, int kp,
-                                                           int64_t sA, int nb, int round,
-                                                           const double* __restrict__ Jbuf,
-                                                           const double* __restrict__ Sbuf,
-                                                           const int* __restrict__ changed, int n_ctiles) {
+struct PairScratch {
+  double2 cs[32];            // cos, sin of the round's rotations (identity when inactive)
+  int meta[32];              // p | q << 8 | active << 16
+  uint16_t sched[PD - 1][32];  // round-robin schedule: p | q << 8 for each round and slot
+  int nrot[2];
+  int perm[PD];
+};
+
+// One pair of a round: load its 64 x 64 block, one cyclic Jacobi sweep if anything is
+// above threshold, descending order; writes J, the rotated block and the changed flag.
+__device__ __forceinline__ void pair_solve(double (*S)[PP], double (*J)[PP], PairScratch& ps,
+                                           const double* __restrict__ Ad, int kp, int64_t sA, int nb, int round,
+                                           int pair, double* __restrict__ Jbuf, double* __restrict__ Sbuf,
+                                           int* __restrict__ changed, int* __restrict__ sweep_count,
+                                           const double* __restrict__ floors, double tol_r, int max_inner) {
+  int* nrot = ps.nrot; int* perm = ps.perm;
+  const int bt = blockIdx.y, tid = threadIdx.x;
+  const int npairs = nb / 2;
+  const double* A = Ad + bt * sA;
+  int p, q;
+  pair_of(pair, round, nb, p, q);
+  // the pair block's lower triangle is stored (p < q keeps local and global order equal)
+  for (int e = tid; e < PD * PD; e += 256) {
+    const int i = e / PD, j = e % PD;
+    if (i >= j) {
+      const double v = A[int64_t(gidx(i, p, q)) * kp + gidx(j, p, q)];
+      S[i][j] = v;
+      S[j][i] = v;
+    }
+  }
+  __syncthreads();
+  const double floor_v = floors[bt];
+  // nothing to do when every off-diagonal entry is below its threshold and the
+  // diagonal is already descending
+  int need = 0;
+  for (int e = tid; e < PD * PD; e += 256) {
+    const int i = e / PD, j = e % PD;
+    if (i > j) {
+      const double v = S[i][j];
+      need |= (v * v > tol_r * tol_r * fabs(S[i][i] * S[j][j])) && (fabs(v) > floor_v);
+    }
+  }
+  if (tid < PD - 1) need |= S[tid][tid] < S[tid + 1][tid + 1];
+  need = __syncthreads_or(need);
+  if (!need) {
+    if (tid == 0) changed[bt * npairs + pair] = 0;
+    return;
+  }
+  for (int e = tid; e < PD * PD; e += 256) J[e / PD][e % PD] = (e / PD == e % PD) ? 1.0 : 0.0;
+  __syncthreads();
+  for (int e = tid; e < (PD - 1) * 32; e += 256) {
+    const int r = e / 32, i = e % 32;
+    const int a = rr_pos(i, r, PD), c = rr_pos(PD - 1 - i, r, PD);
+    ps.sched[r][i] = uint16_t(min(a, c) | (max(a, c) << 8));
+  }
+  __syncthreads();
+  for (int sw = 0; sw < max_inner; ++sw) {
+    int sweep_rot = 0;
+    for (int r = 0; r < PD - 1; ++r) {
+      if (tid < 32) {
+        const int pq = ps.sched[r][tid];
+        const int pi = pq & 0xff, qi = pq >> 8;
+        const double apq = S[pi][qi], app = S[pi][pi], aqq = S[qi][qi];
+        // rotate when |a_pq| > max(tol_r sqrt|a_pp a_qq|, floor)  (squared, no sqrt)
+        const bool act = (apq * apq > tol_r * tol_r * fabs(app * aqq)) && (fabs(apq) > floor_v);
+        double cc = 1.0, ss = 0.0;
+        if (act) {
+          // tangent of the angle that zeroes a_pq, t = y sgn(x) / (|x| + sqrt(x^2 + y^2)) with
+          // x = a_qq - a_pp, y = 2 a_pq: x and y are formed in fp64 and rescaled, the ratio
+          // is taken in fp32 (t to ~1e-7 relative: the rotation then leaves a_pq ~1e-7 of
+          // itself, removed by later sweeps); c = 1/sqrt(1+t^2) and s = t c are fp64, so the
+          // rotation is orthogonal to fp64 precision and S, J stay consistent.
+          const double x = aqq - app, y = 2.0 * apq;
+          const double sc = __builtin_amdgcn_rcp(fmax(fabs(x), fabs(y)));
+          const float xf = float(x * sc), yf = float(y * sc);
+          const float tf = (xf >= 0.f ? yf : -yf) * __builtin_amdgcn_rcpf(fabsf(xf) + __builtin_amdgcn_sqrtf(xf * xf + yf * yf));
+          const double t = double(tf);
+          // v_rsq_f64 is an approximation: two Newton steps c <- c (3/2 - (u/2) c^2) square its
+          // relative error twice, to fp64 rounding
+          const double u = 1.0 + t * t, hu = 0.5 * u;
+          double c0 = __builtin_amdgcn_rsq(u);
+          c0 = c0 * fma(-hu * c0, c0, 1.5);
+          c0 = c0 * fma(-hu * c0, c0, 1.5);
+          cc = c0;
+          ss = t * cc;
+        }
+        ps.cs[tid] = make_double2(cc, ss);
+        ps.meta[tid] = pi | (qi << 8) | (act ? (1 << 16) : 0);
+        const unsigned long long bal = __ballot(act);
+        if (tid == 0) nrot[r & 1] = __popcll(bal);
+      }
+      __syncthreads();
+      const int nr = nrot[r & 1];
+      if (nr == 0) continue;
+      sweep_rot += nr;
+      // S <- R^T S R: a thread owns whole 2 x 2 groups (rows {p, q} of rotation w, columns
+      // {p', q'} of rotation w2), so it reads, rotates on both sides and writes them back
+      // with no barrier in between (the pair's own 2 x 2 block included).  Rotation w acts
+      // as row p <- c p - s q, q <- s p + c q.
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int combo = tid + 256 * k;
+        const int w = combo >> 5, w2 = combo & 31;
+        const int m = ps.meta[w], m2 = ps.meta[w2];
+        const bool a1 = (m >> 16) & 1, a2 = (m2 >> 16) & 1;
+        if (!a1 && !a2) continue;
+        const int p = m & 0xff, q = (m >> 8) & 0xff, p2 = m2 & 0xff, q2 = (m2 >> 8) & 0xff;
+        const double2 r1 = ps.cs[w], r2 = ps.cs[w2];
+        const double spp = S[p][p2], spq = S[p][q2], sqp = S[q][p2], sqq = S[q][q2];
+        // rows
+        const double tpp = r1.x * spp - r1.y * sqp, tqp = r1.y * spp + r1.x * sqp;
+        const double tpq = r1.x * spq - r1.y * sqq, tqq = r1.y * spq + r1.x * sqq;
+        // columns
+        S[p][p2] = r2.x * tpp - r2.y * tpq;
+        S[p][q2] = r2.y * tpp + r2.x * tpq;
+        S[q][p2] = r2.x * tqp - r2.y * tqq;
+        S[q][q2] = r2.y * tqp + r2.x * tqq;
+      }
+      // J <- J R (columns p, q; lane = row)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int item = tid + 256 * k;
+        const int i = item & 63, w = item >> 6;
+        const int m = ps.meta[w];
+        if (!((m >> 16) & 1)) continue;
+        const int p = m & 0xff, q = (m >> 8) & 0xff;
+        const double2 r1 = ps.cs[w];
+        const double jp = J[i][p], jq = J[i][q];
+        J[i][p] = r1.x * jp - r1.y * jq;
+        J[i][q] = r1.y * jp + r1.x * jq;
+      }
+      __syncthreads();
+    }
+    if (sweep_rot == 0) break;
+  }
+  __syncthreads();
+  // eigenvalues of the pair descending: the larger half moves to the lower block index
+  if (tid < PD) {
+    const double di = S[tid][tid];
+    int rank = 0;
+    for (int j = 0; j < PD; ++j) {
+      const double dj = S[j][j];
+      rank += (dj > di) || (dj == di && j < tid);
+    }
+    perm[rank] = tid;
+  }
+  __syncthreads();
+  const int64_t slot = (int64_t(bt) * npairs + pair) * (PD * PD);
+  for (int e = tid; e < PD * PD; e += 256) {
+    const int i = e / PD, j = e % PD;
+    Jbuf[slot + e] = J[i][perm[j]];
+    Sbuf[slot + e] = S[perm[i]][perm[j]];
+  }
+  if (tid == 0) {
+    changed[bt * npairs + pair] = 1;
+    atomicAdd(&sweep_count[bt], 1);
+  }
+}
+
+// V <- V J_Q for one 64-row block of V and one pair of a finished round
+__device__ __forceinline__ void v_update(double (*T0)[PP], double (*T1)[PP], double* __restrict__ V, int kp, int nb,
+                                         int round, int rb, int Q, const double* __restrict__ jq) {
+  int q1, q2;
+  pair_of(Q, round, nb, q1, q2);
+  const int tid = threadIdx.x;
+  for (int e = tid; e < PD * PD; e += 256) {
+    const int i = e / PD, j = e % PD;
+    T0[i][j] = V[int64_t(rb * 64 + i) * kp + gidx(j, q1, q2)];
+    T1[i][j] = jq[e];
+  }
+  __syncthreads();
+  f64x4 acc[2][2];
+  mm64<false>(T0, T1, acc);
+  __syncthreads();
+  acc_to_lds(acc, T0);
+  __syncthreads();
+  for (int e = tid; e < PD * PD; e += 256) {
+    const int i = e / PD, j = e % PD;
+    V[int64_t(rb * 64 + i) * kp + gidx(j, q1, q2)] = T0[i][j];
+  }
+}
+
+// Round g: workgroups [0, npair_wg) solve the pairs of round `round` (buffers *cur);
+// the others apply round g-1's rotations to V (buffers *prev).  V is not read by the
+// pair solves, so the V work of one round overlaps the pair solves of the next.
+__global__ __launch_bounds__(256) void jacobi_pairs_v_kernel(
+    const double* __restrict__ Ad, double* __restrict__ Vd, int kp, int64_t sA, int nb, int npair_wg, int round,
+    double* __restrict__ Jcur, double* __restrict__ Scur, int* __restrict__ chcur, int prev_round,
+    const double* __restrict__ Jprev, const int* __restrict__ chprev, int* __restrict__ sweep_count,
+    const double* __restrict__ floors, double tol_r, int max_inner) {
+  __shared__ double L0[PD][PP];
+  __shared__ double L1[PD][PP];
+  __shared__ PairScratch ps;
+  const int npairs = nb / 2, bt = blockIdx.y;
+  const int t = blockIdx.x;
+  if (t < npair_wg) {
+    pair_solve(L0, L1, ps, Ad, kp, sA, nb, round, t, Jcur, Scur, chcur, sweep_count, floors, tol_r, max_inner);
+    return;
+  }
+  const int v = t - npair_wg;
+  const int rb = v / npairs, Q = v % npairs;
+  if (!chprev[bt * npairs + Q]) return;
+  const double* jq = Jprev + (int64_t(bt) * npairs + Q) * (PD * PD);
+  v_update(L0, L1, Vd + bt * sA, kp, nb, prev_round, rb, Q, jq);
+}
+
+// C <- J^T C J for the pair tiles (P >= Q) of a round
+__global__ __launch_bounds__(256) void jacobi_apply_c_kernel(double* __restrict__ Ad, int kp, int64_t sA, int nb,
+                                                             int round, const double* __restrict__ Jbuf,
+                                                             const double* __restrict__ Sbuf,
+                                                             const int* __restrict__ changed) {
   __shared__ double T0[PD][PP];
   __shared__ double T1[PD][PP];
   const int bt = blockIdx.y, tid = threadIdx.x;
   const int npairs = nb / 2;
   double* A = Ad + bt * sA;
-  double* V = Vd + bt * sA;
   const int64_t jbase = int64_t(bt) * npairs * (PD * PD);
   int t = blockIdx.x;
   f64x4 acc[2][2];
-  if (t < n_ctiles) {
-    int P = 0;
-    while (t > P) { t -= P + 1; ++P; }
-    const int Q = t;
-    const int chP = changed[bt * npairs + P], chQ = changed[bt * npairs + Q];
-    if (!chP && !chQ) return;
-    int p1, p2, q1, q2;
-    pair_of(P, round, nb, p1, p2);
-    pair_of(Q, round, nb, q1, q2);
-    if (P == Q) {
-      // the pair solver's rotated block; its lower triangle is stored
-      const double* s = Sbuf + jbase + int64_t(P) * PD * PD;
-      for (int e = tid; e < PD * PD; e += 256) {
-        const int i = e / PD, j = e % PD;
-        if (i >= j) A[int64_t(gidx(i, p1, p2)) * kp + gidx(j, p1, p2)] = s[e];
-      }
-      return;
-    }
-    sym_tile_io<true>(A, kp, p1, p2, q1, q2, T0);
-    if (chQ) {
-      const double* jq = Jbuf + jbase + int64_t(Q) * PD * PD;
-      for (int e = tid; e < PD * PD; e += 256) T1[e / PD][e % PD] = jq[e];
-      __syncthreads();
-      mm64<false>(T0, T1, acc);   // C_PQ J_Q
-      __syncthreads();
-      acc_to_lds(acc, T0);
-    }
-    if (chP) {
-      const double* jp = Jbuf + jbase + int64_t(P) * PD * PD;
-      for (int e = tid; e < PD * PD; e += 256) T1[e / PD][e % PD] = jp[e];
-      __syncthreads();
-      mm64<true>(T1, T0, acc);    // J_P^T (C_PQ J_Q)
-      __syncthreads();
-      acc_to_lds(acc, T0);
-    }
-    __syncthreads();
-    sym_tile_io<false>(A, kp, p1, p2, q1, q2, T0);
-  } else {
-    t -= n_ctiles;
-    const int rb = t / npairs, Q = t % npairs;
-    if (!changed[bt * npairs + Q]) return;
-    int q1, q2;
-    pair_of(Q, round, nb, q1, q2);
-    const double* jq = Jbuf + jbase + int64_t(Q) * PD * PD;
+  int P = 0;
+  while (t > P) { t -= P + 1; ++P; }
+  const int Q = t;
+  const int chP = changed[bt * npairs + P], chQ = changed[bt * npairs + Q];
+  if (!chP && !chQ) return;
+  int p1, p2, q1, q2;
+  pair_of(P, round, nb, p1, p2);
+  pair_of(Q, round, nb, q1, q2);
+  if (P == Q) {
+    // the pair solver's rotated block; its lower triangle is stored
+    const double* sb = Sbuf + jbase + int64_t(P) * PD * PD;
     for (int e = tid; e < PD * PD; e += 256) {
       const int i = e / PD, j = e % PD;
-      T0[i][j] = V[int64_t(rb * 64 + i) * kp + gidx(j, q1, q2)];
-      T1[i][j] = jq[e];
+      if (i >= j) A[int64_t(gidx(i, p1, p2)) * kp + gidx(j, p1, p2)] = sb[e];
     }
+    return;
+  }
+  sym_tile_io<true>(A, kp, p1, p2, q1, q2, T0);
+  if (chQ) {
+    const double* jq = Jbuf + jbase + int64_t(Q) * PD * PD;
+    for (int e = tid; e < PD * PD; e += 256) T1[e / PD][e % PD] = jq[e];
     __syncthreads();
-    mm64<false>(T0, T1, acc);
+    mm64<false>(T0, T1, acc);   // C_PQ J_Q
     __syncthreads();
     acc_to_lds(acc, T0);
-    __syncthreads();
-    for (int e = tid; e < PD * PD; e += 256) {
-      const int i = e / PD, j = e % PD;
-      V[int64_t(rb * 64 + i) * kp + gidx(j, q1, q2)] = T0[i][j];
-    }
   }
+  if (chP) {
+    const double* jp = Jbuf + jbase + int64_t(P) * PD * PD;
+    for (int e = tid; e < PD * PD; e += 256) T1[e / PD][e % PD] = jp[e];
+    __syncthreads();
+    mm64<true>(T1, T0, acc);    // J_P^T (C_PQ J_Q)
+    __syncthreads();
+    acc_to_lds(acc, T0);
+  }
+  __syncthreads();
+  sym_tile_io<false>(A, kp, p1, p2, q1, q2, T0);
 }
 
 // diagonal -> dvec (all kp positions: the in-pair sorting moves the decoupled padding
@@ -428,12 +481,12 @@ JWs carve_jacobi(Carve& cv, int64_t k, int64_t batch) {
   const int64_t npairs = kp / PD;
   JWs w;
   w.V = cv.take<double>(size_t(batch * kp * kp));
-  w.J = cv.take<double>(size_t(batch * npairs * PD * PD));
-  w.S = cv.take<double>(size_t(batch * npairs * PD * PD));
+  w.J = cv.take<double>(size_t(2 * batch * npairs * PD * PD));   // by round parity
+  w.S = cv.take<double>(size_t(2 * batch * npairs * PD * PD));
   w.pad = cv.take<double>(size_t(batch));
   w.floor_v = cv.take<double>(size_t(batch));
   w.dvec = cv.take<double>(size_t(batch * kp));
-  w.changed = cv.take<int>(size_t(batch * npairs));
+  w.changed = cv.take<int>(size_t(2 * batch * npairs));
   w.count = cv.take<int>(size_t(batch));
   w.perm = cv.take<int>(size_t(batch * k));
   return w;
@@ -484,28 +537,41 @@ lrc_status jacobi_eig(hipStream_t st, double* A, int64_t k, int64_t batch, int64
 
   std::vector<int> counts(size_t(batch), 0);
   bool converged = false;
-  for (int sweep = 0; sweep < MAX_SWEEPS; ++sweep) {
+  const size_t jslot = size_t(batch) * npairs * PD * PD;
+  const size_t cslot = size_t(batch) * npairs;
+  int64_t g = 0;            // rounds launched so far, over all sweeps
+  int prev_round = 0;       // round-robin index of round g-1
+  auto launch_pairs_v = [&](int npair_wg, int round) -> lrc_status {
+    const int cur = int(g & 1), prv = int((g + 1) & 1);
+    const int nv = g > 0 ? n_vtiles : 0;
+    if (npair_wg + nv == 0) return LRC_OK;
+    jacobi_pairs_v_kernel<<<dim3(unsigned(npair_wg + nv), unsigned(batch)), 256, 0, st>>>(
+        A, w.V, int(kp), sA, nb, npair_wg, round, w.J + cur * jslot, w.S + cur * jslot, w.changed + cur * cslot,
+        prev_round, w.J + prv * jslot, w.changed + prv * cslot, w.count, w.floor_v, tol_r, max_inner);
+    LRC_LAUNCHED();
+    return LRC_OK;
+  };
+  for (int sweep = 0; sweep < MAX_SWEEPS && !converged; ++sweep) {
     zero_i32_kernel<<<unsigned(cdiv(batch, 256)), 256, 0, st>>>(w.count, int(batch));
     LRC_LAUNCHED();
     for (int r = 0; r < nb - 1; ++r) {
-      pair_eig_kernel<<<dim3(unsigned(npairs), unsigned(batch)), 256, 0, st>>>(A, int(kp), sA, nb, r, w.J, w.S,
-                                                                              w.changed, w.count, w.floor_v, tol_r,
-                                                                              max_inner);
+      LRC_TRY(launch_pairs_v(npairs, r));
+      const int cur = int(g & 1);
+      jacobi_apply_c_kernel<<<dim3(unsigned(n_ctiles), unsigned(batch)), 256, 0, st>>>(
+          A, int(kp), sA, nb, r, w.J + cur * jslot, w.S + cur * jslot, w.changed + cur * cslot);
       LRC_LAUNCHED();
-      jacobi_apply_kernel<<<dim3(unsigned(n_ctiles + n_vtiles), unsigned(batch)), 256, 0, st>>>(
-          A, w.V, int(kp), sA, nb, r, w.J, w.S, w.changed, n_ctiles);
-      LRC_LAUNCHED();
+      prev_round = r;
+      ++g;
     }
     LRC_HIP(hipMemcpyAsync(counts.data(), w.count, sizeof(int) * size_t(batch), hipMemcpyDeviceToHost, st));
     LRC_HIP(hipStreamSynchronize(st));
     bool any = false;
     for (int c : counts) any |= (c != 0);
     if (debug) fprintf(stderr, "lrc jacobi k=%lld sweep %d: pairs rotated %d (item 0)\n", (long long)k, sweep, counts[0]);
-    if (!any) {
-      converged = true;
-      break;
-    }
+    converged = !any;
   }
+  // the last round's rotations still have to reach V
+  LRC_TRY(launch_pairs_v(0, 0));
 
   diag_kernel<<<dim3(unsigned(cdiv(kp, 256)), unsigned(batch)), 256, 0, st>>>(A, int(kp), sA, w.dvec);
   LRC_LAUNCHED();
