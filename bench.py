@@ -25,6 +25,24 @@ METRIC = "calib tokens/s into cov (4096-d) + whitened-SVD layers/s at 4096×4096
 HBM_PEAK_GBS = 8000.0
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "f64": 78.6}
 
+# roofline class of each instrumented kernel: MFMA contractions against the dense peak of
+# their input type, the fp64 Jacobi kernels against the fp64 peak (vector and matrix fp64
+# peaks are equal on MI355X), streaming passes against HBM
+ROOFLINE = {
+    "syrk_bf16_kernel": {"bound": "mfma", "dtype": "bf16", "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s"},
+    "syrk_f32_kernel": {"bound": "mfma", "dtype": "f32", "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s"},
+    "gemm_f32_kernel": {"bound": "mfma", "dtype": "f32", "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s"},
+    "gram_f64_kernel": {"bound": "alu", "dtype": "f64", "peak": PEAK_TFLOPS["f64"], "unit": "TFLOP/s"},
+    "jacobi_pairs_v_kernel": {"bound": "alu", "dtype": "f64", "peak": PEAK_TFLOPS["f64"], "unit": "TFLOP/s"},
+    "jacobi_apply_c_kernel": {"bound": "mfma", "dtype": "f64", "peak": PEAK_TFLOPS["f64"], "unit": "TFLOP/s"},
+    "fisher_partial_kernel": {"bound": "alu", "dtype": "f32", "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s"},
+    "qaw_prepass_kernel": {"bound": "hbm", "dtype": "bf16", "peak": HBM_PEAK_GBS, "unit": "GB/s"},
+}
+
+# HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE on this
+# workload, scaled by the copy-kernel calibration; None until taken for the current kernel
+TRAFFIC = {}
+
 
 def parse():
     p = argparse.ArgumentParser()
@@ -35,14 +53,13 @@ def parse():
     p.add_argument("--d", type=int, default=4096)
     p.add_argument("--rank", type=int, default=1024)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cov-reps", type=int, default=10, help="extra timed SYRK launches for its event timing")
     return p.parse_args()
 
 
 def cpu_baseline(d, n, rank):
-    """The fp64 oracle on host cores, on a bounded sample of the same workload:
-    covariance of 8192 tokens (scaled by tokens) + the decomposition of a d/2 x d/2
-    layer at rank/2 (scaled by the cube of the size)."""
+    """The fp64 oracle on host cores, on a bounded sample of the same workload: the
+    covariance of 16384 of the n tokens (scaled by n / 16384), then the full-size
+    Cholesky, whitening, SVD, back-map, K-FAC scores and allocation of the layer."""
     import numpy as np
     import torch
 
@@ -54,25 +71,23 @@ def cpu_baseline(d, n, rank):
         threads = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    ns = min(8192, n)
+    ns = min(16384, n)
     a = synth.activation_stream(ns, d, 1.0, 31, outlier_frac=0.01, dtype=torch.bfloat16).float().numpy()
     t0 = time.perf_counter()
-    oracle.covariance_sum(a)
-    t_cov = (time.perf_counter() - t0) * (n / ns)
-    ds, rs = d // 2, rank // 2
-    a2 = synth.activation_stream(4 * ds, ds, 1.0, 32, outlier_frac=0.01, dtype=torch.bfloat16).float().numpy()
-    xs = oracle.covariance_sum(a2)
-    w = synth.weight(ds, ds, 33).numpy()
+    xs = oracle.covariance_sum(a)
+    t_cov_meas = time.perf_counter() - t0
+    del a
+    w = synth.weight(d, d, 35).numpy()
     t0 = time.perf_counter()
-    res = oracle.whiten_decompose(w, xs, 4 * ds, rank=rs)
+    res = oracle.whiten_decompose(w, xs, ns, rank=rank)
     sc = oracle.kfac_scores(res["sigma"])
-    oracle.allocate([sc.astype(np.float32)], [2 * ds], rs * 2 * ds)
-    t_dec = (time.perf_counter() - t0) * (d / ds) ** 3
-    step = t_cov + t_dec
-    return {"value": 1.0 / step, "unit": "layers/s", "cores": threads, "kind": "oracle",
-            "sample": f"fp64 covariance of {ns} of {n} tokens (x{n / ns:g}) + Cholesky/whiten/SVD/back-map/"
-                      f"scores/allocation at {ds}x{ds} r={rs} (x{(d / ds) ** 3:g} by d^3)",
-            "cov_tokens_per_s": n / t_cov, "seconds_measured": round(t_cov * ns / n + t_dec / (d / ds) ** 3, 2)}
+    oracle.allocate([sc.astype(np.float32)], [2 * d], rank * 2 * d)
+    t_dec = time.perf_counter() - t0
+    t_cov = t_cov_meas * (n / ns)
+    return {"value": 1.0 / (t_cov + t_dec), "unit": "layers/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 covariance of {ns} of {n} tokens (time x{n / ns:g}) + full {d}x{d} "
+                      f"Cholesky/whitening/SVD/back-map/K-FAC scores/allocation at rank {rank}",
+            "cov_tokens_per_s": round(n / t_cov, 1), "seconds_measured": round(t_cov_meas + t_dec, 2)}
 
 
 def main():
@@ -106,32 +121,40 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # timed region: K whole steps; the library brackets every instrumented launch with HIP
+    # events on the stream it is enqueued on and counts the work each launch performed
+    lrc.lrc_profile_start()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         out = step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    lrc.lrc_profile_stop()
+    prof = lrc.lrc_profile_kernels()
     n_kept = int(out[1][0])
     ms = 1e3 * elapsed / args.steps
 
-    # live event timing of the covariance SYRK launch on the stream it runs on
-    st = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.cov_reps)]
-    for e0, e1 in ev:
-        cov.zero_()
-        e0.record(st)
-        lrc.lrc_accumulate_cov(a, cov)
-        e1.record(st)
-    torch.cuda.synchronize()
-    cov_ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[len(ev) // 2]
-    cov_flop = float(n) * d * (d + 1)          # lower triangle incl. diagonal, 2 flop per product
-    cov_bytes = float(n) * d * 2               # each token row read once (bf16)
-    t1 = time.perf_counter()
-    for _ in range(args.steps):
-        lrc.lrc_whiten_decompose(w, r, cov, n)
-    torch.cuda.synchronize()
-    dec_s = (time.perf_counter() - t1) / args.steps
+    kernels = {}
+    for name, k in prof.items():
+        avg_ms = k["total_ms"] / max(k["launches"], 1)
+        per_launch_flops = k["flops"] / max(k["launches"], 1)
+        per_launch_bytes = k["bytes"] / max(k["launches"], 1)
+        kernels[name] = {
+            "launches_per_step": k["launches"] / args.steps,
+            "ms_per_step": round(k["total_ms"] / args.steps, 3),
+            "avg_launch_ms": round(avg_ms, 5),
+            "TFLOP/s": round(per_launch_flops / (avg_ms * 1e-3) / 1e12, 3) if avg_ms > 0 else None,
+            "GB/s": round(per_launch_bytes / (avg_ms * 1e-3) / 1e9, 1) if avg_ms > 0 else None,
+        }
+    dom = max(prof, key=lambda nm: prof[nm]["total_ms"])
+    roof = ROOFLINE[dom]
+    dk = prof[dom]
+    avg_s = dk["total_ms"] / dk["launches"] * 1e-3
+    work = (dk["flops"] if roof["unit"] == "TFLOP/s" else dk["bytes"]) / dk["launches"]
+    achieved = work / avg_s / (1e12 if roof["unit"] == "TFLOP/s" else 1e9)
 
+    syrk = prof["syrk_bf16_kernel"]
+    syrk_s = syrk["total_ms"] * 1e-3 / args.steps        # one launch per step here
     res = {
         "metric": METRIC,
         "value": round(1e3 / ms, 4),
@@ -148,15 +171,15 @@ def main():
         "config": {"workload": f"attention projection W {d}x{d} fp32, {n} bf16 calibration tokens "
                                f"(power-law spectrum, 1% outlier channels x20), activation-only whitening, rank {r}",
                    "tokens_per_layer": n, "d": d, "rank": r},
-        "cov_tokens_per_s": round(n / (cov_ms * 1e-3), 1),
+        "cov_tokens_per_s": round(n / syrk_s, 1),
         "step_tokens_per_s": round(n * 1e3 / ms, 1),
-        "decomp_layers_per_s": round(1.0 / dec_s, 4),
         "n_kept": n_kept,
-        "roofline": {"bound": "mfma", "kernel": "syrk_bf16_kernel", "achieved": round(cov_flop / (cov_ms * 1e-3) / 1e12, 2),
-                     "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
-                     "frac": round(cov_flop / (cov_ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
-                     "traffic": None, "launch_ms": round(cov_ms, 4),
-                     "hbm_GBps_min_bytes": round(cov_bytes / (cov_ms * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": roof["bound"], "kernel": dom, "dtype": roof["dtype"],
+                     "achieved": round(achieved, 3), "peak": roof["peak"], "unit": roof["unit"],
+                     "frac": round(achieved / roof["peak"], 4), "traffic": TRAFFIC.get(dom),
+                     "avg_launch_ms": round(dk["total_ms"] / dk["launches"], 5),
+                     "launches_per_step": dk["launches"] / args.steps},
+        "kernels": kernels,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(d, n, r)

@@ -19,7 +19,7 @@ __all__ = [
     "LRC_ENOCONV", "LRC_ENONFINITE", "LRC_F32", "LRC_BF16", "LRC_COV_QUANT_INT8_TOKEN",
     "LRC_SCORE_FISHER", "LRC_SCORE_KFAC", "LrcError", "lib", "library_path",
     "lrc_accumulate_cov", "lrc_whiten_decompose", "lrc_score_components", "lrc_allocate_ranks",
-    "lrc_status_string",
+    "lrc_status_string", "lrc_profile_start", "lrc_profile_stop", "lrc_profile_kernels",
 ]
 
 LRC_OK, LRC_EINVAL, LRC_EDTYPE, LRC_EWORKSPACE, LRC_EHIP, LRC_ENOTPD, LRC_ENOCONV, LRC_ENONFINITE = range(8)
@@ -46,6 +46,12 @@ _SIGS = {
     "lrc_allocate_ranks_workspace": (_sz, [_i64, _i64]),
     "lrc_status_string": (ctypes.c_char_p, [_i32]),
     "lrc_last_hip_error": (_i32, []),
+    "lrc_profile_start": (_i32, []),
+    "lrc_profile_stop": (_i32, []),
+    "lrc_profile_kernels": (_i32, []),
+    "lrc_profile_kernel": (_i32, [_i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(_i64),
+                                  ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+                                  ctypes.POINTER(ctypes.c_double)]),
 }
 
 
@@ -232,3 +238,27 @@ def lrc_allocate_ranks(scores: torch.Tensor, offsets: torch.Tensor, cost: torch.
                                   n_mat, M, int(budget), _ptr(order), _ptr(n_kept), _ptr(ranks), _ptr(kept),
                                   _ptr(info), _ptr(ws), ws.numel(), _stream()), "lrc_allocate_ranks")
     return order, n_kept, ranks, kept, info
+
+
+def lrc_profile_start() -> None:
+    """Start recording HIP events around every instrumented kernel launch (clears totals)."""
+    _check(lib.lrc_profile_start(), "lrc_profile_start")
+
+
+def lrc_profile_stop() -> None:
+    """Stop recording; waits for the recorded events and folds their times into the totals."""
+    _check(lib.lrc_profile_stop(), "lrc_profile_stop")
+
+
+def lrc_profile_kernels() -> dict:
+    """Totals per kernel name since the last start: launches, total_ms, flops, bytes."""
+    out = {}
+    for i in range(lib.lrc_profile_kernels()):
+        name = ctypes.c_char_p()
+        launches = _i64()
+        ms, fl, by = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+        _check(lib.lrc_profile_kernel(i, ctypes.byref(name), ctypes.byref(launches), ctypes.byref(ms),
+                                      ctypes.byref(fl), ctypes.byref(by)), "lrc_profile_kernel")
+        out[name.value.decode()] = {"launches": launches.value, "total_ms": ms.value, "flops": fl.value,
+                                    "bytes": by.value}
+    return out

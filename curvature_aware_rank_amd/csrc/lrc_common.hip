@@ -1,4 +1,8 @@
 // Status strings, last HIP error, device properties.
+#include <cstring>
+#include <mutex>
+#include <vector>
+
 #include "lrc_internal.h"
 
 namespace lrc {
@@ -18,7 +22,118 @@ int device_cu_count() {
   return v;
 }
 
+// ---- measurement support
+namespace {
+struct ProfEvent {
+  const char* name;
+  hipEvent_t e0, e1;
+};
+struct ProfTotal {
+  const char* name;
+  int64_t launches = 0;
+  double ms = 0.0, flops = 0.0, bytes = 0.0;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfEvent> g_prof_events;
+std::vector<ProfTotal> g_prof_totals;
+std::vector<hipEvent_t> g_prof_pool;  // recorded events are recycled after lrc_profile_stop
+
+hipEvent_t acquire_event() {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+ProfTotal& total_for(const char* name) {
+  for (auto& t : g_prof_totals)
+    if (std::strcmp(t.name, name) == 0) return t;
+  g_prof_totals.push_back(ProfTotal{name});
+  return g_prof_totals.back();
+}
+}  // namespace
+
+bool prof_enabled() { return g_prof_on; }
+
+void prof_add_work(const char* name, double flops, double bytes) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on) return;
+  ProfTotal& t = total_for(name);
+  t.flops += flops;
+  t.bytes += bytes;
+}
+
+ProfScope::ProfScope(const char* n, hipStream_t s, double f, double b) : name(n), st(s), flops(f), bytes(b) {
+  if (!g_prof_on) return;
+  e0 = acquire_event();
+  if (e0) (void)hipEventRecord(e0, st);
+}
+
+ProfScope::~ProfScope() {
+  if (!e0) return;
+  hipEvent_t e1 = acquire_event();
+  if (!e1) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_pool.push_back(e0);
+    return;
+  }
+  (void)hipEventRecord(e1, st);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_events.push_back(ProfEvent{name, e0, e1});
+  ProfTotal& t = total_for(name);
+  t.launches += 1;
+  t.flops += flops;
+  t.bytes += bytes;
+}
+
 }  // namespace lrc
+
+extern "C" lrc_status lrc_profile_start(void) {
+  std::lock_guard<std::mutex> lk(lrc::g_prof_mu);
+  for (auto& e : lrc::g_prof_events) {
+    lrc::g_prof_pool.push_back(e.e0);
+    lrc::g_prof_pool.push_back(e.e1);
+  }
+  lrc::g_prof_events.clear();
+  lrc::g_prof_totals.clear();
+  lrc::g_prof_on = true;
+  return LRC_OK;
+}
+
+extern "C" lrc_status lrc_profile_stop(void) {
+  std::lock_guard<std::mutex> lk(lrc::g_prof_mu);
+  lrc::g_prof_on = false;
+  for (auto& e : lrc::g_prof_events) {
+    LRC_HIP(hipEventSynchronize(e.e1));
+    float ms = 0.f;
+    LRC_HIP(hipEventElapsedTime(&ms, e.e0, e.e1));
+    lrc::total_for(e.name).ms += ms;
+    lrc::g_prof_pool.push_back(e.e0);
+    lrc::g_prof_pool.push_back(e.e1);
+  }
+  lrc::g_prof_events.clear();
+  return LRC_OK;
+}
+
+extern "C" int lrc_profile_kernels(void) { return int(lrc::g_prof_totals.size()); }
+
+extern "C" lrc_status lrc_profile_kernel(int index, const char** name, int64_t* launches, double* total_ms,
+                                         double* flops, double* bytes) {
+  if (index < 0 || index >= int(lrc::g_prof_totals.size())) return LRC_EINVAL;
+  const auto& t = lrc::g_prof_totals[size_t(index)];
+  if (name) *name = t.name;
+  if (launches) *launches = t.launches;
+  if (total_ms) *total_ms = t.ms;
+  if (flops) *flops = t.flops;
+  if (bytes) *bytes = t.bytes;
+  return LRC_OK;
+}
 
 extern "C" const char* lrc_status_string(lrc_status s) {
   switch (s) {

@@ -372,6 +372,12 @@ lrc_status launch_syrk_bf16(hipStream_t st, const uint16_t* X, const uint16_t* Y
   const bool vec = (d % 8 == 0) && (ldx % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0) &&
                    ((reinterpret_cast<uintptr_t>(Y) & 15) == 0);
   const dim3 grid(unsigned(NXCD * p.tiles_per_xcd * p.splits));
+  // algorithmic work: n d (d + 1) / 2 products and adds for the lower triangle incl. the
+  // diagonal; bytes: the token block once (twice when the two operands differ) plus one
+  // read and one write of the fp32 lower triangle
+  const double tri = double(d) * double(d + 1) / 2;
+  ProfScope scope("syrk_bf16_kernel", st, 2.0 * double(n) * tri,
+                  double(n) * double(d) * 2.0 * (X == Y ? 1 : 2) + 8.0 * tri);
   if (vec)
     syrk_bf16_kernel<true><<<grid, NTH, 0, st>>>(X, Y, ldx, n, int(d), p.n1, p.n_tiles, p.tiles_per_xcd,
                                                  p.splits, p.steps_per_split, C, ldc, partial, counters);
@@ -452,6 +458,8 @@ extern "C" lrc_status lrc_accumulate_cov(const void* A, lrc_dtype dt, int64_t n_
 
   if (!quant && dt == LRC_F32) {
     const int tiles = int(cdiv(d, 64) * (cdiv(d, 64) + 1) / 2);
+    const double tri = double(d) * double(d + 1) / 2;
+    ProfScope scope("syrk_f32_kernel", st, 2.0 * double(n_tokens) * tri, double(n_tokens) * double(d) * 4.0 + 8.0 * tri);
     syrk_f32_kernel<<<tiles, 256, 0, st>>>(static_cast<const float*>(A), lda, n_tokens, int(d), C, ldc);
     LRC_LAUNCHED();
     return LRC_OK;
@@ -464,6 +472,8 @@ extern "C" lrc_status lrc_accumulate_cov(const void* A, lrc_dtype dt, int64_t n_
   }
   for (int64_t t0 = 0; t0 < n_tokens; t0 += chunk) {
     const int64_t nb = std::min(chunk, n_tokens - t0);
+    {
+    ProfScope scope("qaw_prepass_kernel", st, 0.0, double(nb) * double(d) * ((dt == LRC_BF16 ? 2 : 4) + 6));
     if (dt == LRC_BF16)
       qaw_prepass_kernel<uint16_t><<<unsigned(nb), 256, 0, st>>>(static_cast<const uint16_t*>(A) + t0 * lda, lda,
                                                                  int(d), q, h, l, d);
@@ -471,6 +481,7 @@ extern "C" lrc_status lrc_accumulate_cov(const void* A, lrc_dtype dt, int64_t n_
       qaw_prepass_kernel<float><<<unsigned(nb), 256, 0, st>>>(static_cast<const float*>(A) + t0 * lda, lda,
                                                               int(d), q, h, l, d);
     LRC_LAUNCHED();
+    }
     LRC_TRY(launch_syrk_bf16(st, q, h, d, nb, d, C, ldc, partial, counters, cap));
     LRC_TRY(launch_syrk_bf16(st, q, l, d, nb, d, C, ldc, partial, counters, cap));
   }

@@ -295,6 +295,11 @@ lrc_status gemm_f32(hipStream_t st, unsigned flags, int64_t m, int64_t n, int64_
                     int64_t ldc, int64_t sC, int64_t batch) {
   if (m <= 0 || n <= 0 || batch <= 0) return LRC_OK;
   const dim3 grid(unsigned(cdiv(n, GT)), unsigned(cdiv(m, GT)), unsigned(batch));
+  // algorithmic flops: 2 m n k, halved for a triangular operand and for a triangular output
+  double fl = 2.0 * double(m) * double(n) * double(k) * double(batch);
+  if (flags & (GEMM_K_FROM_COL | GEMM_K_FROM_ROW | GEMM_K_TO_ROW)) fl *= 0.5;
+  if (flags & GEMM_LOWER) fl *= 0.5;
+  ProfScope scope("gemm_f32_kernel", st, fl, 4.0 * double(batch) * (double(m) * k + double(k) * n + 2.0 * double(m) * n));
   gemm_f32_kernel<<<grid, 256, 0, st>>>(flags, int(m), int(n), int(k), alpha, A, lda, sA, B, ldb, sB, beta, C, ldc, sC);
   LRC_LAUNCHED();
   return LRC_OK;
@@ -305,6 +310,9 @@ lrc_status gram_f64(hipStream_t st, bool rows, int64_t p, int64_t q, const float
   const int64_t dim = rows ? p : q;
   const int64_t t = cdiv(dim, 64);
   const dim3 grid(unsigned(t * (t + 1) / 2), 1, unsigned(batch));
+  const double other = rows ? double(q) : double(p);
+  ProfScope scope("gram_f64_kernel", st, double(batch) * double(dim) * double(dim + 1) * other,
+                  double(batch) * (4.0 * double(p) * double(q) + 4.0 * double(dim) * double(dim + 1)));
   gram_f64_kernel<<<grid, 256, 0, st>>>(rows, int(p), int(q), M, ldm, sM, G, ldg, sG);
   LRC_LAUNCHED();
   return LRC_OK;

@@ -34,6 +34,15 @@ constexpr double TOL_R_DEFAULT = 1e-10;
 constexpr double FLOOR_REL_DEFAULT = 1e-12;
 constexpr int MAX_SWEEPS = 40;
 
+// work counters, filled only while measurement is on (see lrc_profile_start)
+enum : int { PROF_ROTATIONS, PROF_PAIRS_ACTIVE, PROF_V_TILES, PROF_C_TILES, PROF_C_PRODUCTS, PROF_C_DIAG, PROF_N };
+// algorithmic work: a plane rotation of a pair block updates two rows and two columns of the
+// 64 x 64 block and two columns of its 64 x 64 accumulated rotation, 3 flops per element
+// (2 multiplies, 1 add); a 64 x 64 x 64 tile product is 2 * 64^3 flops
+constexpr double FLOPS_PER_ROTATION = 3.0 * 2 * PD * 3;
+constexpr double FLOPS_PER_TILE_PRODUCT = 2.0 * PD * PD * PD;
+constexpr double TILE_BYTES = 8.0 * PD * PD;
+
 __device__ __forceinline__ int rr_pos(int pos, int r, int n) { return pos == 0 ? 0 : 1 + ((pos - 1 + r) % (n - 1)); }
 
 __device__ __forceinline__ void pair_of(int pair, int r, int nb, int& p, int& q) {
@@ -160,7 +169,8 @@ __device__ __forceinline__ void pair_solve(double (*S)[PP], double (*J)[PP], Pai
                                            const double* __restrict__ Ad, int kp, int64_t sA, int nb, int round,
                                            int pair, double* __restrict__ Jbuf, double* __restrict__ Sbuf,
                                            int* __restrict__ changed, int* __restrict__ sweep_count,
-                                           const double* __restrict__ floors, double tol_r, int max_inner) {
+                                           const double* __restrict__ floors, double tol_r, int max_inner,
+                                           unsigned long long* __restrict__ prof) {
   int* nrot = ps.nrot; int* perm = ps.perm;
   const int bt = blockIdx.y, tid = threadIdx.x;
   const int npairs = nb / 2;
@@ -202,6 +212,7 @@ __device__ __forceinline__ void pair_solve(double (*S)[PP], double (*J)[PP], Pai
     ps.sched[r][i] = uint16_t(min(a, c) | (max(a, c) << 8));
   }
   __syncthreads();
+  int total_rot = 0;
   for (int sw = 0; sw < max_inner; ++sw) {
     int sweep_rot = 0;
     for (int r = 0; r < PD - 1; ++r) {
@@ -279,6 +290,7 @@ __device__ __forceinline__ void pair_solve(double (*S)[PP], double (*J)[PP], Pai
       }
       __syncthreads();
     }
+    total_rot += sweep_rot;
     if (sweep_rot == 0) break;
   }
   __syncthreads();
@@ -302,6 +314,10 @@ __device__ __forceinline__ void pair_solve(double (*S)[PP], double (*J)[PP], Pai
   if (tid == 0) {
     changed[bt * npairs + pair] = 1;
     atomicAdd(&sweep_count[bt], 1);
+    if (prof) {
+      atomicAdd(&prof[PROF_ROTATIONS], (unsigned long long)total_rot);
+      atomicAdd(&prof[PROF_PAIRS_ACTIVE], 1ull);
+    }
   }
 }
 
@@ -335,14 +351,15 @@ __global__ __launch_bounds__(256) void jacobi_pairs_v_kernel(
     const double* __restrict__ Ad, double* __restrict__ Vd, int kp, int64_t sA, int nb, int npair_wg, int round,
     double* __restrict__ Jcur, double* __restrict__ Scur, int* __restrict__ chcur, int prev_round,
     const double* __restrict__ Jprev, const int* __restrict__ chprev, int* __restrict__ sweep_count,
-    const double* __restrict__ floors, double tol_r, int max_inner) {
+    const double* __restrict__ floors, double tol_r, int max_inner, unsigned long long* __restrict__ prof) {
   __shared__ double L0[PD][PP];
   __shared__ double L1[PD][PP];
   __shared__ PairScratch ps;
   const int npairs = nb / 2, bt = blockIdx.y;
   const int t = blockIdx.x;
   if (t < npair_wg) {
-    pair_solve(L0, L1, ps, Ad, kp, sA, nb, round, t, Jcur, Scur, chcur, sweep_count, floors, tol_r, max_inner);
+    pair_solve(L0, L1, ps, Ad, kp, sA, nb, round, t, Jcur, Scur, chcur, sweep_count, floors, tol_r, max_inner,
+               prof);
     return;
   }
   const int v = t - npair_wg;
@@ -350,13 +367,15 @@ __global__ __launch_bounds__(256) void jacobi_pairs_v_kernel(
   if (!chprev[bt * npairs + Q]) return;
   const double* jq = Jprev + (int64_t(bt) * npairs + Q) * (PD * PD);
   v_update(L0, L1, Vd + bt * sA, kp, nb, prev_round, rb, Q, jq);
+  if (prof && threadIdx.x == 0) atomicAdd(&prof[PROF_V_TILES], 1ull);
 }
 
 // C <- J^T C J for the pair tiles (P >= Q) of a round
 __global__ __launch_bounds__(256) void jacobi_apply_c_kernel(double* __restrict__ Ad, int kp, int64_t sA, int nb,
                                                              int round, const double* __restrict__ Jbuf,
                                                              const double* __restrict__ Sbuf,
-                                                             const int* __restrict__ changed) {
+                                                             const int* __restrict__ changed,
+                                                             unsigned long long* __restrict__ prof) {
   __shared__ double T0[PD][PP];
   __shared__ double T1[PD][PP];
   const int bt = blockIdx.y, tid = threadIdx.x;
@@ -380,6 +399,7 @@ __global__ __launch_bounds__(256) void jacobi_apply_c_kernel(double* __restrict_
       const int i = e / PD, j = e % PD;
       if (i >= j) A[int64_t(gidx(i, p1, p2)) * kp + gidx(j, p1, p2)] = sb[e];
     }
+    if (prof && tid == 0) atomicAdd(&prof[PROF_C_DIAG], 1ull);
     return;
   }
   sym_tile_io<true>(A, kp, p1, p2, q1, q2, T0);
@@ -401,6 +421,10 @@ __global__ __launch_bounds__(256) void jacobi_apply_c_kernel(double* __restrict_
   }
   __syncthreads();
   sym_tile_io<false>(A, kp, p1, p2, q1, q2, T0);
+  if (prof && tid == 0) {
+    atomicAdd(&prof[PROF_C_TILES], 1ull);
+    atomicAdd(&prof[PROF_C_PRODUCTS], (unsigned long long)(chP + chQ));
+  }
 }
 
 // diagonal -> dvec (all kp positions: the in-pair sorting moves the decoupled padding
@@ -474,6 +498,7 @@ __global__ __launch_bounds__(256) void gather_sign_kernel(const double* __restri
 struct JWs {
   double *V, *J, *S, *pad, *floor_v, *dvec;
   int *changed, *count, *perm;
+  unsigned long long* prof;
 };
 
 JWs carve_jacobi(Carve& cv, int64_t k, int64_t batch) {
@@ -489,6 +514,7 @@ JWs carve_jacobi(Carve& cv, int64_t k, int64_t batch) {
   w.changed = cv.take<int>(size_t(2 * batch * npairs));
   w.count = cv.take<int>(size_t(batch));
   w.perm = cv.take<int>(size_t(batch * k));
+  w.prof = cv.take<unsigned long long>(PROF_N);
   return w;
 }
 
@@ -530,6 +556,13 @@ lrc_status jacobi_eig(hipStream_t st, double* A, int64_t k, int64_t batch, int64
   const double floor_rel = env_double("LRC_JACOBI_FLOOR", FLOOR_REL_DEFAULT);
   const bool debug = getenv("LRC_DEBUG") != nullptr;
 
+  const bool prof_on = prof_enabled();
+  unsigned long long* prof = prof_on ? w.prof : nullptr;
+  if (prof_on) {
+    zero_i32_kernel<<<1, 256, 0, st>>>(reinterpret_cast<int*>(w.prof), 2 * PROF_N);
+    LRC_LAUNCHED();
+  }
+  int64_t pair_wgs = 0;  // pair-solve workgroups launched (each reads its pair block)
   jacobi_scalars_kernel<<<unsigned(batch), 256, 0, st>>>(A, int(k), int(kp), sA, w.pad, w.floor_v, floor_rel);
   LRC_LAUNCHED();
   jacobi_init_kernel<<<dim3(unsigned(kp), unsigned(batch)), 256, 0, st>>>(A, w.V, int(k), int(kp), sA, w.pad);
@@ -545,10 +578,12 @@ lrc_status jacobi_eig(hipStream_t st, double* A, int64_t k, int64_t batch, int64
     const int cur = int(g & 1), prv = int((g + 1) & 1);
     const int nv = g > 0 ? n_vtiles : 0;
     if (npair_wg + nv == 0) return LRC_OK;
+    ProfScope scope("jacobi_pairs_v_kernel", st, 0.0, 0.0);  // work is counted on the device
     jacobi_pairs_v_kernel<<<dim3(unsigned(npair_wg + nv), unsigned(batch)), 256, 0, st>>>(
         A, w.V, int(kp), sA, nb, npair_wg, round, w.J + cur * jslot, w.S + cur * jslot, w.changed + cur * cslot,
-        prev_round, w.J + prv * jslot, w.changed + prv * cslot, w.count, w.floor_v, tol_r, max_inner);
+        prev_round, w.J + prv * jslot, w.changed + prv * cslot, w.count, w.floor_v, tol_r, max_inner, prof);
     LRC_LAUNCHED();
+    pair_wgs += int64_t(npair_wg) * batch;
     return LRC_OK;
   };
   for (int sweep = 0; sweep < MAX_SWEEPS && !converged; ++sweep) {
@@ -557,9 +592,12 @@ lrc_status jacobi_eig(hipStream_t st, double* A, int64_t k, int64_t batch, int64
     for (int r = 0; r < nb - 1; ++r) {
       LRC_TRY(launch_pairs_v(npairs, r));
       const int cur = int(g & 1);
-      jacobi_apply_c_kernel<<<dim3(unsigned(n_ctiles), unsigned(batch)), 256, 0, st>>>(
-          A, int(kp), sA, nb, r, w.J + cur * jslot, w.S + cur * jslot, w.changed + cur * cslot);
-      LRC_LAUNCHED();
+      {
+        ProfScope scope("jacobi_apply_c_kernel", st, 0.0, 0.0);
+        jacobi_apply_c_kernel<<<dim3(unsigned(n_ctiles), unsigned(batch)), 256, 0, st>>>(
+            A, int(kp), sA, nb, r, w.J + cur * jslot, w.S + cur * jslot, w.changed + cur * cslot, prof);
+        LRC_LAUNCHED();
+      }
       prev_round = r;
       ++g;
     }
@@ -585,6 +623,22 @@ lrc_status jacobi_eig(hipStream_t st, double* A, int64_t k, int64_t batch, int64
   gather_sign_kernel<<<dim3(unsigned(ncols), unsigned(batch)), 256, 0, st>>>(A, int(k), int(kp), sA, w.perm, Qt,
                                                                              int(ncols));
   LRC_LAUNCHED();
+  if (prof_on) {
+    unsigned long long c[PROF_N];
+    LRC_HIP(hipMemcpyAsync(c, w.prof, sizeof(c), hipMemcpyDeviceToHost, st));
+    LRC_HIP(hipStreamSynchronize(st));
+    // pair solves read the lower half of their block; active ones write J and the block;
+    // a V tile update reads V and J and writes V; a C tile is read and written, plus one J
+    // per product; a diagonal pair block is copied from the solver's output
+    const double lower_bytes = 8.0 * PD * (PD + 1) / 2;
+    prof_add_work("jacobi_pairs_v_kernel",
+                  double(c[PROF_ROTATIONS]) * FLOPS_PER_ROTATION + double(c[PROF_V_TILES]) * FLOPS_PER_TILE_PRODUCT,
+                  double(pair_wgs) * lower_bytes + double(c[PROF_PAIRS_ACTIVE]) * 2 * TILE_BYTES +
+                      double(c[PROF_V_TILES]) * 3 * TILE_BYTES);
+    prof_add_work("jacobi_apply_c_kernel", double(c[PROF_C_PRODUCTS]) * FLOPS_PER_TILE_PRODUCT,
+                  double(c[PROF_C_TILES]) * 2 * TILE_BYTES + double(c[PROF_C_PRODUCTS]) * TILE_BYTES +
+                      double(c[PROF_C_DIAG]) * 2 * lower_bytes);
+  }
   if (!converged) {
     // mark every item that still rotated in the last sweep
     std::vector<int32_t> inf(size_t(batch), 0);

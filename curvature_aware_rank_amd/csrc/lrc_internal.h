@@ -51,6 +51,18 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int device_cu_count();  // compute units of the current device (cached per device)
 
+// measurement support (see lrc_profile_start): a scope around one kernel launch
+bool prof_enabled();
+void prof_add_work(const char* name, double flops, double bytes);
+struct ProfScope {
+  const char* name;
+  hipStream_t st;
+  double flops, bytes;
+  hipEvent_t e0 = nullptr;
+  ProfScope(const char* n, hipStream_t s, double f, double b);
+  ~ProfScope();
+};
+
 // ---------------------------------------------------------------------------------
 // device-side types and conversions
 // ---------------------------------------------------------------------------------

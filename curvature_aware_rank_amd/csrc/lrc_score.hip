@@ -160,6 +160,14 @@ extern "C" lrc_status lrc_score_components(const void* A, const void* B, lrc_dty
   const int ntb = int(cdiv(n_tokens, ST));
   if (ntb > 0) {
     const dim3 grid(unsigned(cdiv(k, ST)), unsigned(ntb));
+    // algorithmic work: the two projections (2 N k (d_in + d_out)) and 3 flops per
+    // (token, component) for the squares and the product; A and B read once, the factors
+    // once, one fp32 partial per (64-token block, component) written
+    const double esz = dt == LRC_BF16 ? 2.0 : 4.0;
+    ProfScope scope("fisher_partial_kernel", st,
+                    2.0 * double(n_tokens) * double(k) * double(d_in + d_out) + 3.0 * double(n_tokens) * double(k),
+                    esz * double(n_tokens) * double(d_in + d_out) + 4.0 * double(k) * double(d_in + d_out) +
+                        4.0 * double(ntb) * double(k));
     if (dt == LRC_BF16)
       fisher_partial_kernel<uint16_t><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(A),
                                                             static_cast<const uint16_t*>(B), n_tokens, int(d_in),

@@ -176,6 +176,22 @@ lrc_status lrc_allocate_ranks(const float* scores, const int64_t* offsets, const
                               void* ws, size_t ws_bytes, void* stream);
 size_t lrc_allocate_ranks_workspace(int64_t n_mat, int64_t n_items);
 
+/*
+ * Measurement support (benchmarks and profilers; not needed for results).
+ * Between lrc_profile_start and lrc_profile_stop every launch of an instrumented kernel
+ * is bracketed by two HIP events recorded on the stream it runs on, and the work it
+ * performed is added to its kernel's totals: algorithmic flops and HBM bytes computed
+ * from the launch shape, or, for the eigensolver kernels, counted on the device (tile
+ * products and rotations actually executed).  lrc_profile_stop waits for the recorded
+ * events; then lrc_profile_kernels / lrc_profile_kernel return one entry per kernel
+ * name (name is a static string).  Host-side state, one profiling session per process.
+ */
+lrc_status lrc_profile_start(void);
+lrc_status lrc_profile_stop(void);
+int lrc_profile_kernels(void);
+lrc_status lrc_profile_kernel(int index, const char** name, int64_t* launches, double* total_ms,
+                              double* flops, double* bytes);
+
 /* Human-readable name of a status code (static string). */
 const char* lrc_status_string(lrc_status s);
 /* The hipError_t value of the last LRC_EHIP returned on this thread (0 if none). */

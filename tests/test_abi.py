@@ -99,3 +99,11 @@ def test_allocate_ranks_validation(lib):
     assert f(FAKE, None, FAKE, 2, 10, 5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == EINVAL
     need = lib.lrc_allocate_ranks_workspace(2, 10)
     assert f(FAKE, FAKE, FAKE, 2, 10, 5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == EWORKSPACE
+
+
+def test_profile_session_without_work(lib):
+    # no kernel launched: the session records nothing and out-of-range queries fail
+    assert lib.lrc_profile_start() == 0
+    assert lib.lrc_profile_stop() == 0
+    assert lib.lrc_profile_kernels() == 0
+    assert lib.lrc_profile_kernel(0, None, None, None, None, None) == EINVAL
