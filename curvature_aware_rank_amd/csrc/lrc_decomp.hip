@@ -8,12 +8,27 @@
 // W~ itself, so only products with W (never a second decomposition) are needed:
 //   Gram on the output side (k = d_out):  Left = L_g^-T U S^1/2,  Right = S^-1/2 (L_g U)^T W
 //   Gram on the input side  (k = d_in) :  Right = S^1/2 V^T L_x^-1, Left = W (L_x V) S^-1/2
+#include <stdlib.h>
+#include <string.h>
+
 #include <vector>
 
 #include "lrc_dense.h"
 
 namespace lrc {
 namespace {
+
+// Eigensolver choice: a single Gram of size >= 512 goes through tridiagonalisation +
+// inverse iteration (O(k^3) once); batches of small Grams through block Jacobi, whose
+// rounds process every item of the batch at once.  LRC_EIGENSOLVER=jacobi|tridiag
+// overrides the choice (tridiag only applies to batch 1).
+bool use_tridiag(int64_t k, int64_t batch) {
+  if (batch != 1) return false;
+  const char* e = getenv("LRC_EIGENSOLVER");
+  if (e && strcmp(e, "jacobi") == 0) return false;
+  if (e && strcmp(e, "tridiag") == 0) return true;
+  return k >= 512;
+}
 
 __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
   const int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x;
@@ -63,7 +78,10 @@ DWs carve_decomp(Carve& cv, int64_t d_out, int64_t d_in, int64_t batch, int64_t 
   w.qt = cv.take<float>(size_t(batch * std::max<int64_t>(rank, 1) * k));
   w.u = cv.take<float>(size_t(k * std::max<int64_t>(rank, 1)));
   w.p = cv.take<float>(size_t(big * std::max<int64_t>(rank, 1)));
-  const size_t jb = jacobi_workspace(k, batch);
+  // the two eigensolvers run one after the other at most (a clustered spectrum falls back
+  // from the tridiagonal route to Jacobi), so they share one region
+  size_t jb = jacobi_workspace(k, batch);
+  if (use_tridiag(k, batch)) jb = std::max(jb, tridiag_workspace(k, std::max<int64_t>(rank, 1)));
   w.jac = cv.take<char>(jb);
   return w;
 }
@@ -148,8 +166,18 @@ extern "C" lrc_status lrc_whiten_decompose(const float* W, int64_t d_out, int64_
   const bool left_side = d_out <= d_in;
   LRC_TRY(gram_f64(st, left_side, d_out, d_in, cur, ldc, scur, w.gram, kp, kp * kp, batch));
   const int64_t ncols = std::max<int64_t>(rank, 1);
-  const lrc_status es = jacobi_eig(st, w.gram, k, batch, ncols, sigma, w.qt, info, w.jac);
-  if (es != LRC_OK) return es;
+  bool jacobi = true;
+  if (use_tridiag(k, batch)) {
+    bool clustered = false;
+    LRC_TRY(tridiag_eig(st, w.gram, k, kp, ncols, sigma, w.qt, w.jac, &clustered));
+    jacobi = clustered;
+    // the tridiagonalisation consumed the Gram: form it again for the Jacobi solver
+    if (clustered) LRC_TRY(gram_f64(st, left_side, d_out, d_in, cur, ldc, scur, w.gram, kp, kp * kp, batch));
+  }
+  if (jacobi) {
+    const lrc_status es = jacobi_eig(st, w.gram, k, batch, ncols, sigma, w.qt, info, w.jac);
+    if (es != LRC_OK) return es;
+  }
   if (rank == 0) return LRC_OK;
 
   // a5: back-map to weight space

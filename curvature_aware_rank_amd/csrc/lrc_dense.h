@@ -27,4 +27,13 @@ size_t jacobi_workspace(int64_t k, int64_t batch);
 lrc_status jacobi_eig(hipStream_t st, double* A, int64_t k, int64_t batch, int64_t ncols, float* sigma,
                       float* Qt, int32_t* info, void* ws);
 
+// Symmetric eigendecomposition of one fp64 k x k Gram (lower triangle of A, leading
+// dimension lda; destroyed): Householder tridiagonalisation, Sturm multisection for all
+// eigenvalues, inverse iteration for the ncols largest, blocked back-transformation.
+// Same outputs as jacobi_eig (batch 1).  When the wanted eigenvalues contain a cluster
+// too large for inverse iteration, *clustered is set and nothing past sigma is written.
+size_t tridiag_workspace(int64_t k, int64_t ncols);
+lrc_status tridiag_eig(hipStream_t st, double* A, int64_t k, int64_t lda, int64_t ncols, float* sigma, float* Qt,
+                       void* ws, bool* clustered);
+
 }  // namespace lrc

@@ -5,6 +5,7 @@ Tolerances (floating point) follow from the arithmetic, see each test; integer a
 index results are compared bit for bit.
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -197,7 +198,19 @@ def _check_decomposition(case, rank, sig_rtol=1e-4, angle_tol=1e-3):
             assert ang <= angle_tol, (j, ang)
 
 
-def test_decompose_two_sided_fp32_config0_shape(lrc):
+@pytest.fixture(params=["jacobi", "tridiag"])
+def solver(request):
+    """Run a decomposition test through each eigensolver of the library."""
+    old = os.environ.get("LRC_EIGENSOLVER")
+    os.environ["LRC_EIGENSOLVER"] = request.param
+    yield request.param
+    if old is None:
+        del os.environ["LRC_EIGENSOLVER"]
+    else:
+        os.environ["LRC_EIGENSOLVER"] = old
+
+
+def test_decompose_two_sided_fp32_config0_shape(lrc, solver):
     """The single-linear-layer workload: 256 x 256, 4096 fp32 tokens, two-sided, r = 64."""
     case = _decompose_case(lrc, 256, 256, 4096, 64, True, 11)
     _check_decomposition(case, 64)
@@ -214,17 +227,17 @@ def test_decompose_two_sided_fp32_config0_shape(lrc):
 
 @pytest.mark.parametrize("d_out,d_in,rank", [(100, 150, 30), (150, 100, 40), (64, 64, 64), (300, 200, 7),
                                              (33, 1, 1)])
-def test_decompose_ragged_shapes(lrc, d_out, d_in, rank):
+def test_decompose_ragged_shapes(lrc, solver, d_out, d_in, rank):
     case = _decompose_case(lrc, d_out, d_in, 2000, rank, True, 23 + d_out)
     _check_decomposition(case, rank)
 
 
-def test_decompose_activation_only_bf16(lrc):
+def test_decompose_activation_only_bf16(lrc, solver):
     case = _decompose_case(lrc, 320, 256, 3000, 64, False, 31, dtype=torch.bfloat16)
     _check_decomposition(case, 64)
 
 
-def test_decompose_qaw_two_sided(lrc):
+def test_decompose_qaw_two_sided(lrc, solver):
     case = _decompose_case(lrc, 192, 128, 3000, 64, True, 41, dtype=torch.bfloat16, quant=True)
     _check_decomposition(case, 64)
 
@@ -248,7 +261,7 @@ def test_decompose_batched_heads(lrc):
         _check_decomposition(case, rank)
 
 
-def test_decompose_identity_covariances_is_plain_svd(lrc):
+def test_decompose_identity_covariances_is_plain_svd(lrc, solver):
     """X = G = I (identity sums with count 1): plain truncated SVD of W (Eckart-Young)."""
     w = synth.weight(96, 130, 3)
     eye_in = torch.eye(130, device=dev())
@@ -282,7 +295,7 @@ def test_decompose_not_positive_definite(lrc, side):
     assert e.value.status == lrc.LRC_ENOTPD
 
 
-def test_decompose_deterministic(lrc):
+def test_decompose_deterministic(lrc, solver):
     w = synth.weight(128, 200, 5).to(dev())
     a = synth.activation_stream(1500, 200, 1.0, 6, dtype=torch.bfloat16).to(dev())
     xs = torch.zeros(200, 200, device=dev())
@@ -291,6 +304,44 @@ def test_decompose_deterministic(lrc):
     r2 = lrc.lrc_whiten_decompose(w, 32, xs, 1500)
     for x, y in zip(r1, r2):
         assert torch.equal(x, y)
+
+
+def _spectrum_weight(d_out, d_in, sigmas, seed):
+    """W = U diag(sigmas) V^T with Haar U, V (fp32)."""
+    u = synth.haar_rotation(d_out, seed)[:, :len(sigmas)].double()
+    v = synth.haar_rotation(d_in, seed + 1)[:, :len(sigmas)].double()
+    return ((u * torch.tensor(sigmas, dtype=torch.float64)) @ v.T).float()
+
+
+@pytest.mark.parametrize("mult", [8, 200])
+def test_decompose_repeated_singular_values(lrc, mult):
+    """A block of `mult` equal singular values: inverse iteration orthogonalises within the
+    cluster (8), or the library falls back to Jacobi (200 > its cluster limit).  Checked:
+    sigma, the truncation loss, and the leading subspaces outside the cluster."""
+    d = 600
+    sig = np.linspace(2.0, 0.5, d)
+    sig[100:100 + mult] = sig[100]      # stays descending; the cluster sits at 100 .. 100 + mult - 1
+    w = _spectrum_weight(d, d, sig, 77 + mult)
+    eye = torch.eye(d, device=dev())
+    rank = 150 + mult
+    s_gpu, left, right, info = lrc.lrc_whiten_decompose(w.to(dev()), rank, eye, 1)
+    assert int(info[0]) == 0
+    s_ref = np.linalg.svd(to_np(w).astype(np.float64), compute_uv=False)
+    np.testing.assert_allclose(to_np(s_gpu), s_ref, rtol=1e-5, atol=1e-6 * s_ref[0])
+    wr = to_np(left).astype(np.float64) @ to_np(right).astype(np.float64)
+    np.testing.assert_allclose(np.linalg.norm(to_np(w).astype(np.float64) - wr) ** 2, np.sum(s_ref[rank:] ** 2),
+                               rtol=1e-4)
+    u_ref = np.linalg.svd(to_np(w).astype(np.float64))[0]
+    for j in (50, rank):
+        q, _ = np.linalg.qr(to_np(left).astype(np.float64)[:, :j])
+        cosines = np.linalg.svd(q.T @ u_ref[:, :j], compute_uv=False)
+        assert np.arccos(np.clip(cosines.min(), -1, 1)) <= 1e-3
+
+
+def test_decompose_default_solver_mid_size(lrc):
+    """k >= 512 takes the tridiagonal route by default."""
+    case = _decompose_case(lrc, 640, 600, 4000, 100, False, 91, dtype=torch.bfloat16)
+    _check_decomposition(case, 100)
 
 
 # ----------------------------------------------------------------------------- a6 scores
