@@ -54,12 +54,15 @@ __device__ __forceinline__ void tile_of(int t, int& b, int& c) {
   c = t - bb * (bb + 1) / 2;
 }
 
-// Householder scalars of column i from its squared-norm partials (rows >= i + 2) and
-// x0 = C[i+1][i]: H = I - tau v v^T, H x = beta e1, v = [1, x2 * scale].
-__device__ __forceinline__ void house_scalars(const double* __restrict__ npart, int np, double x0, double& tau,
-                                              double& beta, double& scale) {
-  double xn2 = 0.0;
-  for (int b = 0; b < np; ++b) xn2 += npart[b];
+// sum of the squared-norm partials of a column, strided over 256 threads then a fixed
+// tree (the symv and w kernels call this with the same arguments and get the same bits)
+__device__ __forceinline__ double npart_sum_part(const double* __restrict__ npart, int np) {
+  double s = 0.0;
+  for (int b = threadIdx.x; b < np; b += 256) s += npart[b];
+  return s;
+}
+
+__device__ __forceinline__ void house_from_sum(double xn2, double x0, double& tau, double& beta, double& scale) {
   if (xn2 == 0.0) {
     tau = 0.0;
     beta = x0;
@@ -70,6 +73,28 @@ __device__ __forceinline__ void house_scalars(const double* __restrict__ npart, 
   beta = x0 >= 0.0 ? -nrm : nrm;
   tau = (beta - x0) / beta;
   scale = 1.0 / (x0 - beta);
+}
+
+// sum over the 64 lanes of a wave with a fixed butterfly (every lane gets the same bits)
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// block-wide sums (256 threads) of two values: wave butterflies, then the four wave
+// results in order; results to all threads
+__device__ __forceinline__ void block_sum2_fast(double& v0, double& v1, double (*red)[4]) {
+  const int tid = threadIdx.x;
+  v0 = wave_sum(v0);
+  v1 = wave_sum(v1);
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = v0;
+    red[1][tid >> 6] = v1;
+  }
+  __syncthreads();
+  v0 = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
+  v1 = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
 }
 
 // block-wide sum of one value per thread (256 threads), fixed tree; result to all
@@ -104,51 +129,59 @@ __global__ __launch_bounds__(256) void tri_colstart_kernel(const double* __restr
   if (tid == 0) npart[blockIdx.x] = s;
 }
 
-// ---- 1b. symv over the trailing matrix (rows/cols i+1 .. n-1), one 64 x 64 lower tile
-// per workgroup.  P[x][y][*]: contribution to y-block x from the tile pairing x and y.
+// ---- 1b. symv over the trailing matrix (rows/cols i+1 .. n-1) with the raw column
+// x = C[i+1:, i] (the reflector is v = scale x + (1 - scale x0) e_{i+1}; the w kernel
+// applies that), one 64 x 64 lower tile per workgroup.  Outputs: P[x][y][*], the
+// contribution to y-block x from the tile pairing x and y; S[t] = tile part of x^T C x;
+// on diagonal tiles the panel products V^T x, W^T x over the block's rows.
 __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict__ A, int64_t lda, int n, int i, int i0,
                                                        int jj, const double* __restrict__ Wp,
-                                                       const double* __restrict__ npart, const double* __restrict__ x0p,
                                                        double* __restrict__ P, double* __restrict__ S,
-                                                       double* __restrict__ SV, double* __restrict__ SW,
-                                                       double* __restrict__ e, double* __restrict__ tau_out) {
+                                                       double* __restrict__ SV, double* __restrict__ SW) {
   __shared__ double T[TS][TS + 1];
   __shared__ double vb[TS], vc[TS], rs[TS], cs[TS];
   __shared__ double red[8][2][NB];
-  __shared__ double sc[3];
   const int tid = threadIdx.x;
   const int s0 = i + 1;
   const int m = n - s0;
   const int nbt = (m + TS - 1) / TS;
   int b, c;
   tile_of(blockIdx.x, b, c);
-  if (tid == 0) {
-    double tau, beta, scale;
-    house_scalars(npart, (n - i + TS - 1) / TS, *x0p, tau, beta, scale);
-    sc[0] = tau;
-    sc[1] = beta;
-    sc[2] = scale;
-    if (blockIdx.x == 0) {
-      e[i] = beta;
-      tau_out[i] = tau;
-    }
-  }
-  __syncthreads();
-  const double scale = sc[2];
   const int R0 = s0 + b * TS, C0 = s0 + c * TS;
-  if (tid < TS) {
-    const int r = R0 + tid;
-    vb[tid] = r >= n ? 0.0 : (r == s0 ? 1.0 : A[int64_t(r) * lda + i] * scale);
-  } else if (tid < 2 * TS) {
-    const int r = C0 + tid - TS;
-    vc[tid - TS] = r >= n ? 0.0 : (r == s0 ? 1.0 : A[int64_t(r) * lda + i] * scale);
-  }
   const bool diag = b == c;
-  for (int q = tid; q < TS * TS; q += 256) {
-    const int lr = q / TS, lc = q % TS;
+  double tv[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int q = tid + 256 * j;
+    const int lr = q >> 6, lc = q & 63;
     const int r = R0 + lr, cc = C0 + lc;
     const bool ok = r < n && cc < n && (!diag || lr >= lc);
-    T[lr][lc] = ok ? A[int64_t(r) * lda + cc] : 0.0;
+    tv[j] = ok ? A[int64_t(r) * lda + cc] : 0.0;
+  }
+  if (tid < TS) {
+    const int r = R0 + tid;
+    vb[tid] = r < n ? A[int64_t(r) * lda + i] : 0.0;
+  } else if (tid < 2 * TS) {
+    const int r = C0 + tid - TS;
+    vc[tid - TS] = r < n ? A[int64_t(r) * lda + i] : 0.0;
+  }
+  // panel rows for V^T x, W^T x (diagonal tiles): 32 columns x 8 groups of 8 rows
+  const int pc = tid & 31, pg = tid >> 5;
+  double va[8], wa[8];
+  const bool pan = diag && jj > 0;
+  if (pan) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int r = R0 + pg * 8 + q;
+      const bool ok = pc < jj && r < n;
+      va[q] = ok ? A[int64_t(r) * lda + i0 + pc] : 0.0;
+      wa[q] = ok ? Wp[int64_t(r) * NB + pc] : 0.0;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int q = tid + 256 * j;
+    T[q >> 6][q & 63] = tv[j];
   }
   __syncthreads();
   {
@@ -159,8 +192,8 @@ __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict_
       const int q = part * 16 + j;
       srow += T[x][q] * vc[q];
       // column sums: strictly lower rows in a diagonal tile
-      const double tv = (diag && q == x) ? 0.0 : T[q][x];
-      scol += tv * vb[q];
+      const double t = (diag && q == x) ? 0.0 : T[q][x];
+      scol += t * vb[q];
     }
     srow += __shfl_xor(srow, 1);
     srow += __shfl_xor(srow, 2);
@@ -171,78 +204,83 @@ __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict_
       cs[x] = scol;
     }
   }
+  if (pan) {
+    double sv = 0.0, sw = 0.0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      sv += va[q] * vb[pg * 8 + q];
+      sw += wa[q] * vb[pg * 8 + q];
+    }
+    red[pg][0][pc] = sv;
+    red[pg][1][pc] = sw;
+  }
   __syncthreads();
   if (tid < TS) {
+    const double r_ = rs[tid], c_ = cs[tid];
     if (diag) {
-      P[(int64_t(b) * nbt + b) * TS + tid] = rs[tid] + cs[tid];
+      P[(int64_t(b) * nbt + b) * TS + tid] = r_ + c_;
     } else {
-      P[(int64_t(b) * nbt + c) * TS + tid] = rs[tid];
-      P[(int64_t(c) * nbt + b) * TS + tid] = cs[tid];
+      P[(int64_t(b) * nbt + c) * TS + tid] = r_;
+      P[(int64_t(c) * nbt + b) * TS + tid] = c_;
     }
-  }
-  if (tid == 0) {
-    double s = 0.0;
-    if (diag) {
-      for (int x = 0; x < TS; ++x) s += vb[x] * (rs[x] + cs[x]);
-    } else {
-      for (int x = 0; x < TS; ++x) s += vb[x] * rs[x];
-      s *= 2.0;
-    }
-    S[blockIdx.x] = s;
-  }
-  if (diag && jj > 0) {
-    // panel products over this row block: V^T v and W^T v
-    const int cc = tid & 31, g = tid >> 5;
-    double sv = 0.0, sw = 0.0;
+    // x_b^T (tile contribution), fixed butterfly over the first wave
+    const double sacc = wave_sum(diag ? vb[tid] * (r_ + c_) : 2.0 * (vb[tid] * r_));
+    if (tid == 0) S[blockIdx.x] = sacc;
+  } else if (pan && tid < TS + NB) {
+    const int cc = tid - TS;
     if (cc < jj) {
-      for (int q = 0; q < 8; ++q) {
-        const int x = g * 8 + q;
-        const int r = R0 + x;
-        if (r < n) {
-          sv += A[int64_t(r) * lda + i0 + cc] * vb[x];
-          sw += Wp[int64_t(r) * NB + cc] * vb[x];
-        }
-      }
-    }
-    red[g][0][cc] = sv;
-    red[g][1][cc] = sw;
-    __syncthreads();
-    if (tid < jj) {
       double a0 = 0.0, a1 = 0.0;
+#pragma unroll
       for (int q = 0; q < 8; ++q) {
-        a0 += red[q][0][tid];
-        a1 += red[q][1][tid];
+        a0 += red[q][0][cc];
+        a1 += red[q][1][cc];
       }
-      SV[b * NB + tid] = a0;
-      SW[b * NB + tid] = a1;
+      SV[b * NB + cc] = a0;
+      SW[b * NB + cc] = a1;
     }
   }
 }
 
-// y of trailing row r (block xb, local xl): partial sums, then the panel corrections
-__device__ __forceinline__ double tri_yrow(const double* __restrict__ A, int64_t lda, int i0, int jj,
-                                           const double* __restrict__ Wp, const double* __restrict__ P, int nbt,
-                                           int r, int xb, int xl, const double* sv, const double* sw) {
+// fixed-structure sum of the symv partials of trailing row (xb, xl), split over the 4
+// lanes part = 0..3 of a quad (partials c = part, part + 4, ...), combined as
+// (p0 + p1) + (p2 + p3) in every lane
+__device__ __forceinline__ double tri_yraw_quad(const double* __restrict__ P, int nbt, int xb, int xl, int part) {
   double y = 0.0;
-  for (int c = 0; c < nbt; ++c) y += P[(int64_t(xb) * nbt + c) * TS + xl];
-  double corr = 0.0;
-  for (int c = 0; c < jj; ++c) corr += Wp[int64_t(r) * NB + c] * sv[c] + A[int64_t(r) * lda + i0 + c] * sw[c];
-  return y - corr;
+  for (int c0 = part; c0 < nbt; c0 += 32) {
+    double t[8];   // eight loads in flight, then summed in order
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = c0 + 4 * u;
+      t[u] = c < nbt ? P[(int64_t(xb) * nbt + c) * TS + xl] : 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) y += t[u];
+  }
+  y += __shfl_xor(y, 1);
+  y += __shfl_xor(y, 2);
+  return y;
 }
 
-// ---- 1c. w = tau y + alpha v for one 64-row block of the trailing rows; store v and w;
-// then bring column i+1 up to date with the panel's reflectors 0..jj (if it is in the panel)
+// ---- 1c. for one 64-row block of the trailing rows: the Householder scalars of column i,
+// v = scale x + c e_{s0} (c = 1 - scale x0), C v = scale (C x) + c C e_{s0},
+// w = tau (C v - W V^T v - V W^T v) + alpha v with alpha = -tau^2/2 (v^T C v - 2 (V^T v).(W^T v));
+// store v (column i) and w (column jj of W); then bring column s0 up to date with the
+// panel's reflectors 0..jj (if it is in the panel) and write its squared-norm partials.
+// All global loads are issued up front; reductions are fixed butterflies.
 __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int64_t lda, int n, int i, int i0, int jj,
                                                     int do_next, double* __restrict__ Wp,
                                                     const double* __restrict__ npart, const double* __restrict__ x0p,
                                                     const double* __restrict__ P, const double* __restrict__ S,
                                                     const double* __restrict__ SV, const double* __restrict__ SW,
                                                     double* __restrict__ npart_next, double* __restrict__ x0_next,
-                                                    double* __restrict__ d) {
-  __shared__ double sv[NB], sw[NB], vrow[TS], wrow[TS];
-  __shared__ double vn[NB + 1], wn[NB + 1];
-  __shared__ double red[256];
-  __shared__ double sc[4];
+                                                    double* __restrict__ d, double* __restrict__ e,
+                                                    double* __restrict__ tau_out) {
+  __shared__ double Vs[TS][NB + 1], Ws[TS][NB + 1];
+  __shared__ double vn[NB], wn[NB];
+  __shared__ double sv[NB], sw[NB], yr[TS];
+  __shared__ double red8[8][2][NB];
+  __shared__ double red4[2][4];
+  __shared__ double sc[6];
   const int tid = threadIdx.x;
   const int s0 = i + 1;
   const int m = n - s0;
@@ -250,76 +288,137 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
   const int ntile = nbt * (nbt + 1) / 2;
   const int b = blockIdx.x;
   const int R0 = s0 + b * TS;
-  if (tid < jj) {
+  // panel rows of this block (V from C's panel columns, W) and of row s0
+#pragma unroll
+  for (int q = tid; q < TS * NB; q += 256) {
+    const int x = q >> 5, c = q & 31;
+    const int r = R0 + x;
+    const bool ok = c < jj && r < n;
+    Vs[x][c] = ok ? A[int64_t(r) * lda + i0 + c] : 0.0;
+    Ws[x][c] = ok ? Wp[int64_t(r) * NB + c] : 0.0;
+  }
+  if (tid < NB) {
+    vn[tid] = tid < jj ? A[int64_t(s0) * lda + i0 + tid] : 0.0;
+    wn[tid] = tid < jj ? Wp[int64_t(s0) * NB + tid] : 0.0;
+  }
+  // this block's rows of column i (x) and column s0 (C e_{s0}, also the next column)
+  const int x = tid >> 2, part = tid & 3;
+  const int r = R0 + x;
+  double coli = 0.0, cols0 = 0.0;
+  if (part == 0 && r < n) {
+    coli = A[int64_t(r) * lda + i];
+    cols0 = A[int64_t(r) * lda + s0];
+  }
+  const double x0v = *x0p;
+  const double a00 = A[int64_t(s0) * lda + s0];
+  // V^T x and W^T x: 32 columns x 8 groups of row blocks
+  {
+    const int cc = tid & 31, g = tid >> 5;
     double a0 = 0.0, a1 = 0.0;
-    for (int q = 0; q < nbt; ++q) {
-      a0 += SV[q * NB + tid];
-      a1 += SW[q * NB + tid];
-    }
-    sv[tid] = a0;
-    sw[tid] = a1;
+    if (cc < jj)
+      for (int q0 = g; q0 < nbt; q0 += 64) {
+        double t0[8], t1[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int q = q0 + 8 * u;
+          t0[u] = q < nbt ? SV[q * NB + cc] : 0.0;
+          t1[u] = q < nbt ? SW[q * NB + cc] : 0.0;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          a0 += t0[u];
+          a1 += t1[u];
+        }
+      }
+    red8[g][0][cc] = a0;
+    red8[g][1][cc] = a1;
   }
-  // v^T C v: fixed-order sum of the tile partials
-  double part = 0.0;
-  for (int t = tid; t < ntile; t += 256) part += S[t];
-  const double vav = block_sum256(part, red);   // (contains the barrier that publishes sv, sw)
-  if (tid == 0) {
-    double tau, beta, scale;
-    house_scalars(npart, (n - i + TS - 1) / TS, *x0p, tau, beta, scale);
-    double dsw = 0.0;
-    for (int c = 0; c < jj; ++c) dsw += sv[c] * sw[c];
-    const double yv = vav - 2.0 * dsw;
-    sc[0] = tau;
-    sc[1] = scale;
-    sc[2] = -0.5 * tau * tau * yv;   // alpha
-    // w of row s0 (needed by every block for the next column's update)
-    const double y0 = tri_yrow(A, lda, i0, jj, Wp, P, nbt, s0, 0, 0, sv, sw);
-    sc[3] = tau * y0 + sc[2];
+  // raw y = (C x) of this block's rows (4 lanes per row), and of row s0 by the first quad
+  const double yraw = tri_yraw_quad(P, nbt, b, x, part);
+  double y0raw = 0.0;
+  if (tid < 4) y0raw = tri_yraw_quad(P, nbt, 0, 0, tid);
+  // squared norm of column i below row s0 and x^T C x
+  double v0 = npart_sum_part(npart, (n - i + TS - 1) / TS);
+  double v1 = 0.0;
+  for (int t0 = tid; t0 < ntile; t0 += 2048) {
+    double tt[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int t = t0 + 256 * u;
+      tt[u] = t < ntile ? S[t] : 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v1 += tt[u];
+  }
+  block_sum2_fast(v0, v1, red4);   // barrier: also publishes Vs, Ws, vn, wn, red8
+  double tau, beta, scale;
+  house_from_sum(v0, x0v, tau, beta, scale);
+  const double cfac = 1.0 - scale * x0v;
+  if (b == 0 && tid == 0) {
+    e[i] = beta;
+    tau_out[i] = tau;
+  }
+  if (tid < 64) {
+    // lanes c < jj: V^T v, W^T v; then (V^T v).(W^T v) and row s0's correction by butterflies
+    double svc = 0.0, swc = 0.0;
+    if (tid < jj) {
+      double a0 = 0.0, a1 = 0.0;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        a0 += red8[g][0][tid];
+        a1 += red8[g][1][tid];
+      }
+      svc = scale * a0 + cfac * vn[tid];
+      swc = scale * a1 + cfac * wn[tid];
+      sv[tid] = svc;
+      sw[tid] = swc;
+    }
+    const double dsw = wave_sum(svc * swc);
+    const double corr0 = wave_sum(tid < jj ? wn[tid] * svc + vn[tid] * swc : 0.0);
+    if (tid == 0) {
+      const double y0 = scale * y0raw + cfac * a00;
+      const double vav = scale * scale * v1 + 2.0 * scale * cfac * y0raw + cfac * cfac * a00;
+      const double alpha = -0.5 * tau * tau * (vav - 2.0 * dsw);
+      sc[0] = alpha;
+      sc[1] = tau * (y0 - corr0) + alpha;   // w of row s0 (v = 1 there)
+    }
   }
   __syncthreads();
-  const double tau = sc[0], scale = sc[1], alpha = sc[2];
-  if (tid < TS) {
-    const int r = R0 + tid;
-    if (r < n) {
-      const double y = tri_yrow(A, lda, i0, jj, Wp, P, nbt, r, b, tid, sv, sw);
-      const double v = r == s0 ? 1.0 : A[int64_t(r) * lda + i] * scale;
-      const double w = tau * y + alpha * v;
-      vrow[tid] = v;
-      wrow[tid] = w;
-    }
-  }
-  if (do_next && tid <= jj) {
-    // row s0 of the panel's V and W, reflectors 0..jj
-    vn[tid] = tid == jj ? 1.0 : A[int64_t(s0) * lda + i0 + tid];
-    wn[tid] = tid == jj ? sc[3] : Wp[int64_t(s0) * NB + tid];
-  }
-  __syncthreads();
-  if (tid < TS) {
-    const int r = R0 + tid;
-    if (r < n) {
-      Wp[int64_t(r) * NB + jj] = wrow[tid];
-      A[int64_t(r) * lda + i] = vrow[tid];
+  const double alpha = sc[0], w0 = sc[1];
+  // rows: corrections split over the quad's 4 lanes (c = part, part + 4, ...)
+  double corr = 0.0;
+  for (int c = part; c < jj; c += 4) corr += Ws[x][c] * sv[c] + Vs[x][c] * sw[c];
+  corr += __shfl_xor(corr, 1);
+  corr += __shfl_xor(corr, 2);
+  const double colsv = __shfl(cols0, (tid & 63) & ~3);   // lane part 0 loaded the row's values
+  const double colx = __shfl(coli, (tid & 63) & ~3);
+  double v = 0.0, w = 0.0;
+  if (r < n) {
+    const double y = scale * yraw + cfac * colsv - corr;
+    v = r == s0 ? 1.0 : colx * scale;
+    w = r == s0 ? w0 : tau * y + alpha * v;   // row s0: the value every block uses
+    if (part == 0) {
+      Wp[int64_t(r) * NB + jj] = w;
+      A[int64_t(r) * lda + i] = v;
     }
   }
   if (!do_next) return;
-  // column i' = s0: rows s0.., C[r][i'] -= sum_c V[r][c] W[i'][c] + W[r][c] V[i'][c]
+  // column s0: rows s0.., C[r][s0] -= sum_c V[r][c] W[s0][c] + W[r][c] V[s0][c], c = 0..jj
+  double c2 = 0.0;
+  for (int c = part; c < jj; c += 4) c2 += Vs[x][c] * wn[c] + Ws[x][c] * vn[c];
+  c2 += __shfl_xor(c2, 1);
+  c2 += __shfl_xor(c2, 2);
   double sq = 0.0;
-  if (tid < TS) {
-    const int r = R0 + tid;
-    if (r < n) {
-      double corr = 0.0;
-      for (int c = 0; c < jj; ++c)
-        corr += A[int64_t(r) * lda + i0 + c] * wn[c] + Wp[int64_t(r) * NB + c] * vn[c];
-      corr += vrow[tid] * wn[jj] + wrow[tid] * vn[jj];
-      const double val = A[int64_t(r) * lda + s0] - corr;
-      A[int64_t(r) * lda + s0] = val;
-      if (r == s0) d[s0] = val;
-      if (r == s0 + 1) *x0_next = val;
-      if (r >= s0 + 2) sq = val * val;
-    }
+  if (r < n && part == 0) {
+    const double val = colsv - (c2 + (v * w0 + w));
+    A[int64_t(r) * lda + s0] = val;
+    if (r == s0) d[s0] = val;
+    if (r == s0 + 1) *x0_next = val;
+    if (r >= s0 + 2) sq = val * val;
   }
-  const double s = block_sum256(sq, red);
-  if (tid == 0) npart_next[b] = s;
+  double dummy = 0.0;
+  block_sum2_fast(sq, dummy, red4 + 0);
+  if (tid == 0) npart_next[b] = sq;
 }
 
 // ---- 1d. trailing rank-2 panel update, lower tiles of rows/cols j1 .. n-1:
@@ -431,7 +530,16 @@ __global__ __launch_bounds__(256) void tri_bisect_kernel(const double* __restric
       }
       __syncthreads();
       for (int k = 0; k < kn; ++k) {
-        q = (k0 + k == 0) ? sd[k] - x : (sd[k] - x) - se2[k] / q;
+        if (k0 + k == 0) {
+          q = sd[k] - x;
+        } else {
+          // e^2 / q via the hardware reciprocal refined by two Newton steps (each squares
+          // its relative error): the count is insensitive to last-bit differences
+          double rq = __builtin_amdgcn_rcp(q);
+          rq = fma(rq, fma(-q, rq, 1.0), rq);
+          rq = fma(rq, fma(-q, rq, 1.0), rq);
+          q = fma(-se2[k], rq, sd[k] - x);
+        }
         if (fabs(q) < pivmin) q = -pivmin;
         cnt += q < 0.0;
       }
@@ -505,10 +613,19 @@ __global__ __launch_bounds__(64) void tri_inviter_kernel(const double* __restric
     lprev = lmb;
     // factor T - lmb I = P L U, U with two superdiagonals
     double cd = d[0] - lmb, cs = n > 1 ? e[0] : 0.0;
-    for (int k = 0; k < n - 1; ++k) {
-      const double sub = e[k];
-      const double nd = d[k + 1] - lmb;
-      const double ns = k + 1 < n - 1 ? e[k + 1] : 0.0;
+    for (int k0 = 0; k0 < n - 1; k0 += 8) {
+     double eb[9], db[8];
+#pragma unroll
+     for (int u = 0; u < 9; ++u) eb[u] = k0 + u < n - 1 ? e[k0 + u] : 0.0;
+#pragma unroll
+     for (int u = 0; u < 8; ++u) db[u] = k0 + u + 1 < n ? d[k0 + u + 1] : 0.0;
+#pragma unroll
+     for (int u = 0; u < 8; ++u) {
+      const int k = k0 + u;
+      if (k >= n - 1) break;
+      const double sub = eb[u];
+      const double nd = db[u] - lmb;
+      const double ns = eb[u + 1];   // 0 past the end
       const int64_t o = int64_t(k) * nc + j;
       if (fabs(cd) >= fabs(sub)) {
         const double dd = cd == 0.0 ? tiny : cd;
@@ -530,53 +647,103 @@ __global__ __launch_bounds__(64) void tri_inviter_kernel(const double* __restric
         cd = cs - l * nd;
         cs = -l * ns;
       }
+     }
     }
     u0[int64_t(n - 1) * nc + j] = cd;
     u1[int64_t(n - 1) * nc + j] = 0.0;
     u2[int64_t(n - 1) * nc + j] = 0.0;
     double* z = Z + jv;
     for (int k = 0; k < n; ++k) z[int64_t(k) * nc] = start_value(jv, k);
+    // every pass walks the vector in batches of 8 with all loads of a batch issued first
+    double sc = 1.0;   // scale of the stored vector (applied on the fly)
     for (int it = 0; it < INV_ITERS; ++it) {
-      // apply P and L^-1
-      for (int k = 0; k < n - 1; ++k) {
-        const int64_t o = int64_t(k) * nc + j;
-        double yk = z[int64_t(k) * nc], yk1 = z[int64_t(k + 1) * nc];
-        if (piv[o]) {
-          const double t = yk;
-          yk = yk1;
-          yk1 = t;
+      // apply P and L^-1 to sc * z (the running element stays in a register)
+      double ycur = z[0] * sc;
+      for (int k0 = 0; k0 < n - 1; k0 += 8) {
+        double zn[8], lm[8];
+        int pv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int k = k0 + u;
+          const bool ok = k < n - 1;
+          zn[u] = ok ? z[int64_t(k + 1) * nc] * sc : 0.0;
+          lm[u] = ok ? ml[int64_t(k) * nc + j] : 0.0;
+          pv[u] = ok ? piv[int64_t(k) * nc + j] : 0;
         }
-        z[int64_t(k) * nc] = yk;
-        z[int64_t(k + 1) * nc] = yk1 - ml[o] * yk;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int k = k0 + u;
+          if (k < n - 1) {
+            double ynext = zn[u], yk = ycur;
+            if (pv[u]) {
+              yk = ynext;
+              ynext = ycur;
+            }
+            z[int64_t(k) * nc] = yk;
+            ycur = ynext - lm[u] * yk;
+          }
+        }
       }
-      // back-substitution with U (tiny pivots replaced by +-tiny)
-      double x1 = 0.0, x2 = 0.0;
-      for (int k = n - 1; k >= 0; --k) {
-        const int64_t o = int64_t(k) * nc + j;
-        double p = u0[o];
-        if (fabs(p) < tiny) p = p < 0.0 ? -tiny : tiny;
-        const double xk = (z[int64_t(k) * nc] - u1[o] * x1 - u2[o] * x2) / p;
-        z[int64_t(k) * nc] = xk;
-        x2 = x1;
-        x1 = xk;
+      z[int64_t(n - 1) * nc] = ycur;
+      // back-substitution with U (tiny pivots replaced by +-tiny), squared norm on the way
+      double x1 = 0.0, x2 = 0.0, nrm2 = 0.0;
+      for (int k1 = n - 1; k1 >= 0; k1 -= 8) {
+        double zz[8], a0[8], a1[8], a2[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int k = k1 - u;
+          const bool ok = k >= 0;
+          const int64_t o = int64_t(k) * nc + j;
+          zz[u] = ok ? z[int64_t(k) * nc] : 0.0;
+          a0[u] = ok ? u0[o] : 1.0;
+          a1[u] = ok ? u1[o] : 0.0;
+          a2[u] = ok ? u2[o] : 0.0;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int k = k1 - u;
+          if (k >= 0) {
+            double p = a0[u];
+            if (fabs(p) < tiny) p = p < 0.0 ? -tiny : tiny;
+            const double xk = (zz[u] - a1[u] * x1 - a2[u] * x2) / p;
+            z[int64_t(k) * nc] = xk;
+            nrm2 += xk * xk;
+            x2 = x1;
+            x1 = xk;
+          }
+        }
       }
-      // orthogonalise against the cluster's earlier vectors, normalise
+      // orthogonalise against the cluster's earlier (unit) vectors
       for (int p = 0; p < q; ++p) {
         const double* zp = Z + (j + p);
         double dot = 0.0;
         for (int k = 0; k < n; ++k) dot += zp[int64_t(k) * nc] * z[int64_t(k) * nc];
-        for (int k = 0; k < n; ++k) z[int64_t(k) * nc] -= dot * zp[int64_t(k) * nc];
+        nrm2 = 0.0;
+        for (int k = 0; k < n; ++k) {
+          const double zk = z[int64_t(k) * nc] - dot * zp[int64_t(k) * nc];
+          z[int64_t(k) * nc] = zk;
+          nrm2 += zk * zk;
+        }
       }
-      double mx = 0.0;
-      for (int k = 0; k < n; ++k) mx = fmax(mx, fabs(z[int64_t(k) * nc]));
-      const double inv_mx = mx > 0.0 ? 1.0 / mx : 1.0;
-      double nrm2 = 0.0;
-      for (int k = 0; k < n; ++k) {
-        const double v = z[int64_t(k) * nc] * inv_mx;
-        nrm2 += v * v;
+      // the solve's growth is at most ~1/tiny: squares stay finite for sane scalings
+      sc = nrm2 > 0.0 && nrm2 < 1e300 ? 1.0 / sqrt(nrm2) : 0.0;
+      if (sc == 0.0) {
+        // badly scaled input: scale by the largest entry first
+        double mx = 0.0;
+        for (int k = 0; k < n; ++k) mx = fmax(mx, fabs(z[int64_t(k) * nc]));
+        const double inv_mx = mx > 0.0 && mx < 1e308 ? 1.0 / mx : 1.0;
+        nrm2 = 0.0;
+        for (int k = 0; k < n; ++k) {
+          const double zk = z[int64_t(k) * nc] * inv_mx;
+          nrm2 += zk * zk;
+        }
+        sc = nrm2 > 0.0 ? inv_mx / sqrt(nrm2) : 1.0;
       }
-      const double sfac = inv_mx / sqrt(nrm2);
-      for (int k = 0; k < n; ++k) z[int64_t(k) * nc] *= sfac;
+    }
+    for (int k0 = 0; k0 < n; k0 += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (k0 + u < n) z[int64_t(k0 + u) * nc] *= sc;
     }
   }
 }
@@ -914,13 +1081,20 @@ lrc_status tridiag_eig(hipStream_t st, double* A, int64_t k, int64_t lda, int64_
       {
         ProfScope scope("tri_symv_kernel", st, 2.0 * double(m) * double(m),
                         8.0 * double(m) * double(m + 1) / 2);
-        tri_symv_kernel<<<unsigned(nbt * (nbt + 1) / 2), 256, 0, st>>>(A, lda, n, i, i0, jj, w.Wp, np_cur,
-                                                                        w.x0 + par, w.P, w.S, w.SV, w.SW, w.e, w.tau);
+        tri_symv_kernel<<<unsigned(nbt * (nbt + 1) / 2), 256, 0, st>>>(A, lda, n, i, i0, jj, w.Wp, w.P, w.S,
+                                                                        w.SV, w.SW);
         LRC_LAUNCHED();
       }
-      tri_w_kernel<<<unsigned(nbt), 256, 0, st>>>(A, lda, n, i, i0, jj, jj + 1 < pb ? 1 : 0, w.Wp, np_cur,
-                                                  w.x0 + par, w.P, w.S, w.SV, w.SW, np_next, w.x0 + npar, w.d);
-      LRC_LAUNCHED();
+      {
+        // bytes: the symv partials, the panel rows of V and W, column i (and i+1) read and
+        // written, the new column of W
+        ProfScope scope("tri_w_kernel", st, 4.0 * double(m) * (jj + 1),
+                        8.0 * (double(nbt) * nbt * TS + 2.0 * double(m) * jj + 5.0 * double(m)));
+        tri_w_kernel<<<unsigned(nbt), 256, 0, st>>>(A, lda, n, i, i0, jj, jj + 1 < pb ? 1 : 0, w.Wp, np_cur,
+                                                    w.x0 + par, w.P, w.S, w.SV, w.SW, np_next, w.x0 + npar, w.d,
+                                                    w.e, w.tau);
+        LRC_LAUNCHED();
+      }
     }
     const int j1 = i0 + pb;
     if (j1 < n) {
