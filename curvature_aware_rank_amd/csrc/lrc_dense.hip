@@ -173,81 +173,90 @@ __global__ void sym_scale_kernel(const float* __restrict__ S, int64_t lds_, int6
 constexpr int NB = 64;  // Cholesky / triangular-solve block size
 
 // unblocked factorisation of the diagonal block at k0 (one workgroup)
-__global__ __launch_bounds__(256) void potf2_kernel(float* __restrict__ L, int64_t ldl, int64_t n, int64_t k0,
-                                                    int* __restrict__ info) {
-  __shared__ float S[NB][NB + 1];
-  __shared__ int failed;
+// Unblocked Cholesky of one diagonal block (b <= 64), a single wave: lane i keeps row i
+// in registers; per column j the pivot comes from lane j, the scaled column goes through
+// LDS to every lane, and each lane updates its own row.
+__global__ __launch_bounds__(64) void potf2_kernel(float* __restrict__ L, int64_t ldl, int64_t n, int64_t k0,
+                                                   int* __restrict__ info) {
+  __shared__ float col[NB];
+  const int lane = threadIdx.x;
   const int b = int(min<int64_t>(NB, n - k0));
   if (*info != 0) return;
-  for (int e = threadIdx.x; e < NB * NB; e += 256) {
-    const int i = e / NB, j = e % NB;
-    S[i][j] = (i < b && j <= i) ? L[(k0 + i) * ldl + k0 + j] : 0.f;
-  }
-  if (threadIdx.x == 0) failed = 0;
-  __syncthreads();
-  for (int j = 0; j < b; ++j) {
-    if (threadIdx.x == 0) {
-      const float piv = S[j][j];
+  const int rr = min(lane, b - 1);
+  float a[NB];
+#pragma unroll
+  for (int c = 0; c < NB; ++c) a[c] = L[(k0 + rr) * ldl + k0 + min(c, b - 1)];
+#pragma unroll
+  for (int c = 0; c < NB; ++c) a[c] = (c <= lane && lane < b && c < b) ? a[c] : 0.f;
+  int fail = 0;   // uniform: the pivot is broadcast from lane j
+  // fully unrolled (static register indices); finished or failed columns are skipped
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    if (j < b && fail == 0) {
+      const float piv = __shfl(a[j], j);
       if (!(piv > 0.f) || !isfinite(piv)) {
-        failed = 1;
-        *info = int(k0 + j + 1);
+        fail = j + 1;
       } else {
-        S[j][j] = sqrtf(piv);
+        const float djj = sqrtf(piv);
+        const float inv = 1.0f / djj;
+        a[j] = lane == j ? djj : (lane > j ? a[j] * inv : a[j]);
+        col[lane] = a[j];
+        __syncthreads();
+        const float lij = a[j];
+#pragma unroll
+        for (int c = j + 1; c < NB; ++c) a[c] = (c <= lane) ? fmaf(-lij, col[c], a[c]) : a[c];
+        __syncthreads();
       }
     }
-    __syncthreads();
-    if (failed) return;
-    const float djj = S[j][j];
-    for (int i = j + 1 + threadIdx.x; i < b; i += 256) S[i][j] = S[i][j] / djj;
-    __syncthreads();
-    const int m = b - j - 1;
-    for (int e = threadIdx.x; e < m * m; e += 256) {
-      const int i = j + 1 + e / m, c = j + 1 + e % m;
-      if (c <= i) S[i][c] -= S[i][j] * S[c][j];
-    }
-    __syncthreads();
   }
-  for (int e = threadIdx.x; e < b * b; e += 256) {
-    const int i = e / b, j = e % b;
-    L[(k0 + i) * ldl + k0 + j] = (j <= i) ? S[i][j] : 0.f;
+  if (fail) {
+    if (lane == 0) *info = int(k0 + fail);
+    return;
+  }
+  if (lane < b) {
+#pragma unroll
+    for (int c = 0; c < NB; ++c)
+      if (c < b) L[(k0 + lane) * ldl + k0 + c] = c <= lane ? a[c] : 0.f;
   }
 }
 
-// rows below the diagonal block: X <- X * L11^{-T}   (one wave handles 64 rows)
+// Rows below a factored diagonal block: X <- X D^-T (one lane per row, 64 rows per wave)
 __global__ __launch_bounds__(64) void trsm_panel_kernel(float* __restrict__ L, int64_t ldl, int64_t n, int64_t k0,
                                                         const int* __restrict__ info) {
   __shared__ float D[NB][NB + 1];
-  __shared__ float X[NB][NB + 1];
+  __shared__ float rdiag[NB];
   if (*info != 0) return;
-  const int64_t r0 = k0 + NB + int64_t(blockIdx.x) * 64;
   const int lane = threadIdx.x;
-  for (int i = 0; i < NB; ++i) D[i][lane] = L[(k0 + i) * ldl + k0 + lane];
-  for (int i = 0; i < 64; ++i) {
-    const int64_t r = r0 + i;
-    X[i][lane] = (r < n) ? L[r * ldl + k0 + lane] : 0.f;
-  }
-  __syncthreads();
-  float x[NB];
+  const int64_t r = k0 + NB + int64_t(blockIdx.x) * 64 + lane;
+  const int64_t rc = r < n ? r : n - 1;
+  float x[NB], dcol[NB];
+  // all loads first: row `lane` of the diagonal block (column of D^T) and this lane's row
 #pragma unroll
-  for (int j = 0; j < NB; ++j) x[j] = X[lane][j];
+  for (int c = 0; c < NB; ++c) {
+    dcol[c] = L[(k0 + lane) * ldl + k0 + c];
+    x[c] = L[rc * ldl + k0 + c];
+  }
+  float dl = 1.f;
+#pragma unroll
+  for (int c = 0; c < NB; ++c) {
+    D[lane][c] = dcol[c];
+    dl = c == lane ? dcol[c] : dl;   // static register index, lane-selected
+  }
+  rdiag[lane] = 1.0f / dl;
+  __syncthreads();
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     float v = x[j];
 #pragma unroll
-    for (int c = 0; c < j; ++c) v -= x[c] * D[j][c];
-    x[j] = v / D[j][j];
+    for (int c = 0; c < j; ++c) v = fmaf(-x[c], D[j][c], v);
+    x[j] = v * rdiag[j];
   }
+  if (r < n) {
 #pragma unroll
-  for (int j = 0; j < NB; ++j) X[lane][j] = x[j];
-  __syncthreads();
-  for (int i = 0; i < 64; ++i) {
-    const int64_t r = r0 + i;
-    if (r < n) L[r * ldl + k0 + lane] = X[i][lane];
+    for (int c = 0; c < NB; ++c) L[r * ldl + k0 + c] = x[c];
   }
 }
 
-// Diagonal-block back substitution of  L11^T Y = B  for the block rows at k0 (b rows),
-// one thread per right-hand-side column.
 __global__ __launch_bounds__(64) void trsm_upper_diag_kernel(const float* __restrict__ L, int64_t ldl, int64_t k0, int b,
                                                              float* __restrict__ Bm, int64_t ldb, int64_t ncol) {
   __shared__ float D[NB][NB + 1];
@@ -324,7 +333,7 @@ lrc_status cholesky_f32(hipStream_t st, const float* S, int64_t lds_, int64_t n,
   sym_scale_kernel<<<g, 256, 0, st>>>(S, lds_, n, 1.0 / double(cnt), damping, L, n);
   LRC_LAUNCHED();
   for (int64_t k0 = 0; k0 < n; k0 += NB) {
-    potf2_kernel<<<1, 256, 0, st>>>(L, n, n, k0, info);
+    potf2_kernel<<<1, 64, 0, st>>>(L, n, n, k0, info);
     LRC_LAUNCHED();
     const int64_t below = n - k0 - NB;
     if (below <= 0) break;

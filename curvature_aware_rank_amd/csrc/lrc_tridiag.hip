@@ -14,7 +14,7 @@
 //      The reflector of column i (v[i+1] = 1) is stored in column i below the diagonal.
 //   2. All eigenvalues of T by Sturm-count multisection (16 points per step, 14 steps).
 //   3. Eigenvectors of the wanted (largest) eigenvalues by inverse iteration on T with
-//      partial pivoting, one thread per vector; eigenvalues closer than 1e-7 ||T|| form a
+//      partial pivoting (two solves), one thread per vector; eigenvalues closer than 1e-7 ||T|| form a
 //      cluster whose vectors one thread computes in turn, orthogonalised against each
 //      other (modified Gram-Schmidt).  Clusters larger than 32 are reported to the caller,
 //      which then uses the Jacobi solver.
@@ -42,7 +42,7 @@ constexpr int BIS_ITERS = 14;   // 17^14 > 2^57: the interval shrinks below fp64
 constexpr int BIS_STAGE = 2048; // d, e^2 staged through LDS in chunks of this many
 constexpr int CL_MAX = 32;      // largest cluster inverse iteration handles
 constexpr double CL_TOL = 1e-7; // eigenvalues closer than CL_TOL ||T|| share a cluster
-constexpr int INV_ITERS = 3;    // inverse-iteration solves per vector
+constexpr int INV_ITERS = 2;    // inverse-iteration solves per vector (eigenvalues are accurate to ~eps ||T||)
 constexpr double EPS = 2.220446049250313e-16;
 
 __device__ __forceinline__ void tile_of(int t, int& b, int& c) {
@@ -149,40 +149,51 @@ __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict_
   tile_of(blockIdx.x, b, c);
   const int R0 = s0 + b * TS, C0 = s0 + c * TS;
   const bool diag = b == c;
+  // every load below is unconditional from a clamped (valid) address and masked after,
+  // so that all of them are in flight together
   double tv[16];
+  const int lc = tid & 63, cc = C0 + lc, ccc = min(cc, n - 1);
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const int q = tid + 256 * j;
-    const int lr = q >> 6, lc = q & 63;
-    const int r = R0 + lr, cc = C0 + lc;
-    const bool ok = r < n && cc < n && (!diag || lr >= lc);
-    tv[j] = ok ? A[int64_t(r) * lda + cc] : 0.0;
+    const int lr = (tid >> 6) + 4 * j;
+    const int r = R0 + lr;
+    tv[j] = A[int64_t(min(r, n - 1)) * lda + ccc];
   }
-  if (tid < TS) {
-    const int r = R0 + tid;
-    vb[tid] = r < n ? A[int64_t(r) * lda + i] : 0.0;
-  } else if (tid < 2 * TS) {
-    const int r = C0 + tid - TS;
-    vc[tid - TS] = r < n ? A[int64_t(r) * lda + i] : 0.0;
+  double colv;
+  {
+    const int r = tid < TS ? R0 + tid : C0 + (tid & 63);
+    colv = A[int64_t(min(r, n - 1)) * lda + i];
+    if (r >= n) colv = 0.0;
   }
   // panel rows for V^T x, W^T x (diagonal tiles): 32 columns x 8 groups of 8 rows
   const int pc = tid & 31, pg = tid >> 5;
   double va[8], wa[8];
   const bool pan = diag && jj > 0;
   if (pan) {
+    const int pcc = min(pc, jj - 1);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const int r = R0 + pg * 8 + q;
-      const bool ok = pc < jj && r < n;
-      va[q] = ok ? A[int64_t(r) * lda + i0 + pc] : 0.0;
-      wa[q] = ok ? Wp[int64_t(r) * NB + pc] : 0.0;
+      const int r = min(R0 + pg * 8 + q, n - 1);
+      va[q] = A[int64_t(r) * lda + i0 + pcc];
+      wa[q] = Wp[int64_t(r) * NB + pcc];
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const bool ok = pc < jj && R0 + pg * 8 + q < n;
+      va[q] = ok ? va[q] : 0.0;
+      wa[q] = ok ? wa[q] : 0.0;
     }
   }
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const int q = tid + 256 * j;
-    T[q >> 6][q & 63] = tv[j];
+    const int lr = (tid >> 6) + 4 * j;
+    const bool ok = R0 + lr < n && cc < n && (!diag || lr >= lc);
+    tv[j] = ok ? tv[j] : 0.0;
   }
+  if (tid < TS) vb[tid] = colv;
+  else if (tid < 2 * TS) vc[tid - TS] = colv;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) T[(tid >> 6) + 4 * j][lc] = tv[j];
   __syncthreads();
   {
     const int x = tid >> 2, part = tid & 3;
@@ -241,32 +252,15 @@ __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict_
   }
 }
 
-// fixed-structure sum of the symv partials of trailing row (xb, xl), split over the 4
-// lanes part = 0..3 of a quad (partials c = part, part + 4, ...), combined as
-// (p0 + p1) + (p2 + p3) in every lane
-__device__ __forceinline__ double tri_yraw_quad(const double* __restrict__ P, int nbt, int xb, int xl, int part) {
-  double y = 0.0;
-  for (int c0 = part; c0 < nbt; c0 += 32) {
-    double t[8];   // eight loads in flight, then summed in order
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int c = c0 + 4 * u;
-      t[u] = c < nbt ? P[(int64_t(xb) * nbt + c) * TS + xl] : 0.0;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) y += t[u];
-  }
-  y += __shfl_xor(y, 1);
-  y += __shfl_xor(y, 2);
-  return y;
-}
-
 // ---- 1c. for one 64-row block of the trailing rows: the Householder scalars of column i,
 // v = scale x + c e_{s0} (c = 1 - scale x0), C v = scale (C x) + c C e_{s0},
 // w = tau (C v - W V^T v - V W^T v) + alpha v with alpha = -tau^2/2 (v^T C v - 2 (V^T v).(W^T v));
 // store v (column i) and w (column jj of W); then bring column s0 up to date with the
 // panel's reflectors 0..jj (if it is in the panel) and write its squared-norm partials.
-// All global loads are issued up front; reductions are fixed butterflies.
+// Every global load of the kernel is issued in one phase (clamped addresses, masked
+// after), so the kernel makes one round trip to memory before its stores.
+constexpr int WB = 64;   // row blocks (and tile partials per row) covered by the single load phase
+
 __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int64_t lda, int n, int i, int i0, int jj,
                                                     int do_next, double* __restrict__ Wp,
                                                     const double* __restrict__ npart, const double* __restrict__ x0p,
@@ -277,78 +271,105 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
                                                     double* __restrict__ tau_out) {
   __shared__ double Vs[TS][NB + 1], Ws[TS][NB + 1];
   __shared__ double vn[NB], wn[NB];
-  __shared__ double sv[NB], sw[NB], yr[TS];
+  __shared__ double sv[NB], sw[NB];
   __shared__ double red8[8][2][NB];
   __shared__ double red4[2][4];
-  __shared__ double sc[6];
+  __shared__ double sc[2];
   const int tid = threadIdx.x;
   const int s0 = i + 1;
   const int m = n - s0;
   const int nbt = (m + TS - 1) / TS;
   const int ntile = nbt * (nbt + 1) / 2;
+  const int np = (n - i + TS - 1) / TS;
   const int b = blockIdx.x;
   const int R0 = s0 + b * TS;
-  // panel rows of this block (V from C's panel columns, W) and of row s0
-#pragma unroll
-  for (int q = tid; q < TS * NB; q += 256) {
-    const int x = q >> 5, c = q & 31;
-    const int r = R0 + x;
-    const bool ok = c < jj && r < n;
-    Vs[x][c] = ok ? A[int64_t(r) * lda + i0 + c] : 0.0;
-    Ws[x][c] = ok ? Wp[int64_t(r) * NB + c] : 0.0;
-  }
-  if (tid < NB) {
-    vn[tid] = tid < jj ? A[int64_t(s0) * lda + i0 + tid] : 0.0;
-    wn[tid] = tid < jj ? Wp[int64_t(s0) * NB + tid] : 0.0;
-  }
-  // this block's rows of column i (x) and column s0 (C e_{s0}, also the next column)
+  const int jc = max(jj - 1, 0);
+  const int c32 = tid & 31, g8 = tid >> 5, c32c = min(c32, jc);
   const int x = tid >> 2, part = tid & 3;
-  const int r = R0 + x;
-  double coli = 0.0, cols0 = 0.0;
-  if (part == 0 && r < n) {
-    coli = A[int64_t(r) * lda + i];
-    cols0 = A[int64_t(r) * lda + s0];
+  const int r = R0 + x, rc = min(r, n - 1);
+
+  // ---- load phase
+  double pvv[8], pww[8], tsv[8], tsw[8], tp[16], tp0[16], ts[9];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int rr = min(R0 + g8 + 8 * u, n - 1);
+    pvv[u] = A[int64_t(rr) * lda + i0 + c32c];
+    pww[u] = Wp[int64_t(rr) * NB + c32c];
   }
+  const double vnl = A[int64_t(s0) * lda + i0 + c32c];
+  const double wnl = Wp[int64_t(s0) * NB + c32c];
+  double coli = A[int64_t(rc) * lda + i];
+  double cols0 = A[int64_t(rc) * lda + s0];
   const double x0v = *x0p;
   const double a00 = A[int64_t(s0) * lda + s0];
-  // V^T x and W^T x: 32 columns x 8 groups of row blocks
-  {
-    const int cc = tid & 31, g = tid >> 5;
-    double a0 = 0.0, a1 = 0.0;
-    if (cc < jj)
-      for (int q0 = g; q0 < nbt; q0 += 64) {
-        double t0[8], t1[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int q = q0 + 8 * u;
-          t0[u] = q < nbt ? SV[q * NB + cc] : 0.0;
-          t1[u] = q < nbt ? SW[q * NB + cc] : 0.0;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          a0 += t0[u];
-          a1 += t1[u];
-        }
-      }
-    red8[g][0][cc] = a0;
-    red8[g][1][cc] = a1;
+  for (int u = 0; u < 8; ++u) {
+    const int q = min(g8 + 8 * u, nbt - 1);
+    tsv[u] = SV[q * NB + c32c];
+    tsw[u] = SW[q * NB + c32c];
   }
-  // raw y = (C x) of this block's rows (4 lanes per row), and of row s0 by the first quad
-  const double yraw = tri_yraw_quad(P, nbt, b, x, part);
-  double y0raw = 0.0;
-  if (tid < 4) y0raw = tri_yraw_quad(P, nbt, 0, 0, tid);
-  // squared norm of column i below row s0 and x^T C x
-  double v0 = npart_sum_part(npart, (n - i + TS - 1) / TS);
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int c = min(part + 4 * u, nbt - 1);
+    tp[u] = P[(int64_t(b) * nbt + c) * TS + x];
+    tp0[u] = P[int64_t(c) * TS];   // row s0 = block 0, local 0
+  }
+  const double tnp = npart[min(tid, np - 1)];
+#pragma unroll
+  for (int u = 0; u < 9; ++u) ts[u] = S[min(tid + 256 * u, ntile - 1)];
+
+  // ---- reductions (fixed order: sequential within a lane, then butterflies)
+  double yraw = 0.0, y0raw = 0.0;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const bool ok = part + 4 * u < nbt;
+    yraw += ok ? tp[u] : 0.0;
+    y0raw += ok ? tp0[u] : 0.0;
+  }
+  for (int c0 = part + 4 * 16; c0 < nbt; c0 += 4) {   // more than 64 row blocks
+    yraw += P[(int64_t(b) * nbt + c0) * TS + x];
+    y0raw += P[int64_t(c0) * TS];
+  }
+  yraw += __shfl_xor(yraw, 1);
+  yraw += __shfl_xor(yraw, 2);
+  y0raw += __shfl_xor(y0raw, 1);
+  y0raw += __shfl_xor(y0raw, 2);
+  double a0 = 0.0, a1 = 0.0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const bool ok = c32 < jj && g8 + 8 * u < nbt;
+    a0 += ok ? tsv[u] : 0.0;
+    a1 += ok ? tsw[u] : 0.0;
+  }
+  if (c32 < jj)
+    for (int q = g8 + 64; q < nbt; q += 8) {
+      a0 += SV[q * NB + c32];
+      a1 += SW[q * NB + c32];
+    }
+  red8[g8][0][c32] = a0;
+  red8[g8][1][c32] = a1;
+  double v0 = tid < np ? tnp : 0.0;
+  for (int t = tid + 256; t < np; t += 256) v0 += npart[t];
   double v1 = 0.0;
-  for (int t0 = tid; t0 < ntile; t0 += 2048) {
-    double tt[8];
+#pragma unroll
+  for (int u = 0; u < 9; ++u) v1 += tid + 256 * u < ntile ? ts[u] : 0.0;
+  for (int t = tid + 256 * 9; t < ntile; t += 256) v1 += S[t];
+  {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int t = t0 + 256 * u;
-      tt[u] = t < ntile ? S[t] : 0.0;
+      const int xr = g8 + 8 * u;
+      const bool ok = c32 < jj && R0 + xr < n;
+      Vs[xr][c32] = ok ? pvv[u] : 0.0;
+      Ws[xr][c32] = ok ? pww[u] : 0.0;
     }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v1 += tt[u];
+  }
+  if (tid < NB) {
+    vn[tid] = tid < jj ? vnl : 0.0;
+    wn[tid] = tid < jj ? wnl : 0.0;
+  }
+  if (r >= n) {
+    coli = 0.0;
+    cols0 = 0.0;
   }
   block_sum2_fast(v0, v1, red4);   // barrier: also publishes Vs, Ws, vn, wn, red8
   double tau, beta, scale;
@@ -362,14 +383,14 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
     // lanes c < jj: V^T v, W^T v; then (V^T v).(W^T v) and row s0's correction by butterflies
     double svc = 0.0, swc = 0.0;
     if (tid < jj) {
-      double a0 = 0.0, a1 = 0.0;
+      double b0 = 0.0, b1 = 0.0;
 #pragma unroll
       for (int g = 0; g < 8; ++g) {
-        a0 += red8[g][0][tid];
-        a1 += red8[g][1][tid];
+        b0 += red8[g][0][tid];
+        b1 += red8[g][1][tid];
       }
-      svc = scale * a0 + cfac * vn[tid];
-      swc = scale * a1 + cfac * wn[tid];
+      svc = scale * b0 + cfac * vn[tid];
+      swc = scale * b1 + cfac * wn[tid];
       sv[tid] = svc;
       sw[tid] = swc;
     }
@@ -386,16 +407,20 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
   __syncthreads();
   const double alpha = sc[0], w0 = sc[1];
   // rows: corrections split over the quad's 4 lanes (c = part, part + 4, ...)
-  double corr = 0.0;
-  for (int c = part; c < jj; c += 4) corr += Ws[x][c] * sv[c] + Vs[x][c] * sw[c];
+  double corr = 0.0, c2 = 0.0;
+  for (int c = part; c < jj; c += 4) {
+    const double vr = Vs[x][c], wr = Ws[x][c];
+    corr += wr * sv[c] + vr * sw[c];
+    c2 += vr * wn[c] + wr * vn[c];
+  }
   corr += __shfl_xor(corr, 1);
   corr += __shfl_xor(corr, 2);
-  const double colsv = __shfl(cols0, (tid & 63) & ~3);   // lane part 0 loaded the row's values
-  const double colx = __shfl(coli, (tid & 63) & ~3);
+  c2 += __shfl_xor(c2, 1);
+  c2 += __shfl_xor(c2, 2);
   double v = 0.0, w = 0.0;
   if (r < n) {
-    const double y = scale * yraw + cfac * colsv - corr;
-    v = r == s0 ? 1.0 : colx * scale;
+    const double y = scale * yraw + cfac * cols0 - corr;
+    v = r == s0 ? 1.0 : coli * scale;
     w = r == s0 ? w0 : tau * y + alpha * v;   // row s0: the value every block uses
     if (part == 0) {
       Wp[int64_t(r) * NB + jj] = w;
@@ -404,20 +429,16 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
   }
   if (!do_next) return;
   // column s0: rows s0.., C[r][s0] -= sum_c V[r][c] W[s0][c] + W[r][c] V[s0][c], c = 0..jj
-  double c2 = 0.0;
-  for (int c = part; c < jj; c += 4) c2 += Vs[x][c] * wn[c] + Ws[x][c] * vn[c];
-  c2 += __shfl_xor(c2, 1);
-  c2 += __shfl_xor(c2, 2);
   double sq = 0.0;
   if (r < n && part == 0) {
-    const double val = colsv - (c2 + (v * w0 + w));
+    const double val = cols0 - (c2 + (v * w0 + w));
     A[int64_t(r) * lda + s0] = val;
     if (r == s0) d[s0] = val;
     if (r == s0 + 1) *x0_next = val;
     if (r >= s0 + 2) sq = val * val;
   }
   double dummy = 0.0;
-  block_sum2_fast(sq, dummy, red4 + 0);
+  block_sum2_fast(sq, dummy, red4);
   if (tid == 0) npart_next[b] = sq;
 }
 
@@ -529,20 +550,34 @@ __global__ __launch_bounds__(256) void tri_bisect_kernel(const double* __restric
         se2[k] = (k0 + k > 0) ? e[k0 + k - 1] * e[k0 + k - 1] : 0.0;
       }
       __syncthreads();
-      for (int k = 0; k < kn; ++k) {
-        if (k0 + k == 0) {
-          q = sd[k] - x;
-        } else {
-          // e^2 / q via the hardware reciprocal refined by two Newton steps (each squares
-          // its relative error): the count is insensitive to last-bit differences
-          double rq = __builtin_amdgcn_rcp(q);
-          rq = fma(rq, fma(-q, rq, 1.0), rq);
-          rq = fma(rq, fma(-q, rq, 1.0), rq);
-          q = fma(-se2[k], rq, sd[k] - x);
-        }
+      int k = 0;
+      if (k0 == 0) {
+        q = sd[0] - x;
         if (fabs(q) < pivmin) q = -pivmin;
         cnt += q < 0.0;
+        k = 1;
       }
+      // e^2 / q via the hardware reciprocal refined by one Newton step (which squares its
+      // relative error): a count is insensitive to last-bit differences.  LDS operands are
+      // read 8 steps at a time, off the recurrence's critical path.
+      auto step = [&](double dk, double e2k) {
+        double rq = __builtin_amdgcn_rcp(q);
+        rq = fma(rq, fma(-q, rq, 1.0), rq);
+        q = fma(-e2k, rq, dk - x);
+        if (fabs(q) < pivmin) q = -pivmin;
+        cnt += q < 0.0;
+      };
+      for (; k + 8 <= kn; k += 8) {
+        double dk[8], ek[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          dk[u] = sd[k + u];
+          ek[u] = se2[k + u];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) step(dk[u], ek[u]);
+      }
+      for (; k < kn; ++k) step(sd[k], se2[k]);
     }
     // smallest point whose count exceeds mi bounds the eigenvalue from above
     const unsigned long long bal = __ballot(cnt > mi);
@@ -587,7 +622,11 @@ __device__ __forceinline__ double start_value(int j, int k) {
 }
 
 // one thread per cluster: LU (partial pivoting) of T - lambda I, INV_ITERS solves, MGS
-// within the cluster; Z[k][j] (n x ncols) receives eigenvector j of T
+// within the cluster; Z[k][j] (n x ncols) receives eigenvector j of T.  Per-thread arrays
+// live at [k][j] (coalesced across the wave); every pass runs in unguarded batches of IB
+// elements (all loads of a batch in flight together) followed by a guarded tail.
+constexpr int IB = 16;
+
 __global__ __launch_bounds__(64) void tri_inviter_kernel(const double* __restrict__ d, const double* __restrict__ e,
                                                          int n, const double* __restrict__ lam, int ncols,
                                                          const double* __restrict__ bounds,
@@ -601,36 +640,26 @@ __global__ __launch_bounds__(64) void tri_inviter_kernel(const double* __restric
   const double tnorm = bounds[3];
   const double tiny = EPS * tnorm;
   const int64_t nc = ncols;
-  double* u0 = U;
-  double* u1 = U + int64_t(n) * nc;
-  double* u2 = U + 2 * int64_t(n) * nc;
-  double* ml = U + 3 * int64_t(n) * nc;
+  double* __restrict__ r0 = U;                       // 1 / pivot (tiny pivots replaced by +-tiny)
+  double* __restrict__ u1 = U + int64_t(n) * nc;     // first superdiagonal of U
+  double* __restrict__ u2 = U + 2 * int64_t(n) * nc; // second superdiagonal (fill from pivoting)
+  double* __restrict__ ml = U + 3 * int64_t(n) * nc; // multipliers
+  const int nm1 = n - 1;
   double lprev = 0.0;
   for (int q = 0; q < len; ++q) {
     const int jv = j + q;
     double lmb = lam[n - 1 - jv];
     if (q > 0) lmb = fmin(lmb, lprev - 10.0 * EPS * tnorm);
     lprev = lmb;
-    // factor T - lmb I = P L U, U with two superdiagonals
+    // ---- factor T - lmb I = P L U
     double cd = d[0] - lmb, cs = n > 1 ? e[0] : 0.0;
-    for (int k0 = 0; k0 < n - 1; k0 += 8) {
-     double eb[9], db[8];
-#pragma unroll
-     for (int u = 0; u < 9; ++u) eb[u] = k0 + u < n - 1 ? e[k0 + u] : 0.0;
-#pragma unroll
-     for (int u = 0; u < 8; ++u) db[u] = k0 + u + 1 < n ? d[k0 + u + 1] : 0.0;
-#pragma unroll
-     for (int u = 0; u < 8; ++u) {
-      const int k = k0 + u;
-      if (k >= n - 1) break;
-      const double sub = eb[u];
-      const double nd = db[u] - lmb;
-      const double ns = eb[u + 1];   // 0 past the end
+    auto fstep = [&](int k, double sub, double nd, double ns) {
       const int64_t o = int64_t(k) * nc + j;
+      double piv_u0;
       if (fabs(cd) >= fabs(sub)) {
         const double dd = cd == 0.0 ? tiny : cd;
         const double l = sub / dd;
-        u0[o] = dd;
+        piv_u0 = dd;
         u1[o] = cs;
         u2[o] = 0.0;
         ml[o] = l;
@@ -639,7 +668,7 @@ __global__ __launch_bounds__(64) void tri_inviter_kernel(const double* __restric
         cs = ns;
       } else {
         const double l = cd / sub;
-        u0[o] = sub;
+        piv_u0 = sub;
         u1[o] = nd;
         u2[o] = ns;
         ml[o] = l;
@@ -647,81 +676,96 @@ __global__ __launch_bounds__(64) void tri_inviter_kernel(const double* __restric
         cd = cs - l * nd;
         cs = -l * ns;
       }
-     }
+      if (fabs(piv_u0) < tiny) piv_u0 = piv_u0 < 0.0 ? -tiny : tiny;
+      r0[o] = 1.0 / piv_u0;
+    };
+    int k0 = 0;
+    for (; k0 + IB < nm1; k0 += IB) {   // e[k0 .. k0+IB] and d[k0+1 .. k0+IB] all valid
+      double eb[IB + 1], db[IB];
+#pragma unroll
+      for (int u = 0; u <= IB; ++u) eb[u] = e[k0 + u];
+#pragma unroll
+      for (int u = 0; u < IB; ++u) db[u] = d[k0 + u + 1];
+#pragma unroll
+      for (int u = 0; u < IB; ++u) fstep(k0 + u, eb[u], db[u] - lmb, eb[u + 1]);
     }
-    u0[int64_t(n - 1) * nc + j] = cd;
-    u1[int64_t(n - 1) * nc + j] = 0.0;
-    u2[int64_t(n - 1) * nc + j] = 0.0;
-    double* z = Z + jv;
-    for (int k = 0; k < n; ++k) z[int64_t(k) * nc] = start_value(jv, k);
-    // every pass walks the vector in batches of 8 with all loads of a batch issued first
+    for (int k = k0; k < nm1; ++k) fstep(k, e[k], d[k + 1] - lmb, k + 1 < nm1 ? e[k + 1] : 0.0);
+    {
+      double p0 = cd;
+      if (fabs(p0) < tiny) p0 = p0 < 0.0 ? -tiny : tiny;
+      const int64_t o = int64_t(nm1) * nc + j;
+      r0[o] = 1.0 / p0;
+      u1[o] = 0.0;
+      u2[o] = 0.0;
+    }
+    double* __restrict__ z = Z + jv;
     double sc = 1.0;   // scale of the stored vector (applied on the fly)
     for (int it = 0; it < INV_ITERS; ++it) {
-      // apply P and L^-1 to sc * z (the running element stays in a register)
-      double ycur = z[0] * sc;
-      for (int k0 = 0; k0 < n - 1; k0 += 8) {
-        double zn[8], lm[8];
-        int pv[8];
+      // ---- apply P and L^-1 to sc * z (the running element stays in a register); the
+      // first solve starts from the pseudo-random vector, generated on the fly
+      const bool first = it == 0;
+      auto zin = [&](int k) { return first ? start_value(jv, k) : z[int64_t(k) * nc] * sc; };
+      double ycur = zin(0);
+      auto lstep = [&](int k, double ynext, double l, int pv) {
+        double yk = ycur;
+        if (pv) {
+          yk = ynext;
+          ynext = ycur;
+        }
+        z[int64_t(k) * nc] = yk;
+        ycur = ynext - l * yk;
+      };
+      int k = 0;
+      for (; k + IB <= nm1; k += IB) {
+        double zn[IB], lm[IB];
+        int pv[IB];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int k = k0 + u;
-          const bool ok = k < n - 1;
-          zn[u] = ok ? z[int64_t(k + 1) * nc] * sc : 0.0;
-          lm[u] = ok ? ml[int64_t(k) * nc + j] : 0.0;
-          pv[u] = ok ? piv[int64_t(k) * nc + j] : 0;
+        for (int u = 0; u < IB; ++u) {
+          zn[u] = zin(k + u + 1);
+          lm[u] = ml[int64_t(k + u) * nc + j];
+          pv[u] = piv[int64_t(k + u) * nc + j];
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int k = k0 + u;
-          if (k < n - 1) {
-            double ynext = zn[u], yk = ycur;
-            if (pv[u]) {
-              yk = ynext;
-              ynext = ycur;
-            }
-            z[int64_t(k) * nc] = yk;
-            ycur = ynext - lm[u] * yk;
-          }
-        }
+        for (int u = 0; u < IB; ++u) lstep(k + u, zn[u], lm[u], pv[u]);
       }
-      z[int64_t(n - 1) * nc] = ycur;
-      // back-substitution with U (tiny pivots replaced by +-tiny), squared norm on the way
+      for (; k < nm1; ++k) lstep(k, zin(k + 1), ml[int64_t(k) * nc + j], piv[int64_t(k) * nc + j]);
+      z[int64_t(nm1) * nc] = ycur;
+      // ---- back-substitution with U, squared norm on the way
       double x1 = 0.0, x2 = 0.0, nrm2 = 0.0;
-      for (int k1 = n - 1; k1 >= 0; k1 -= 8) {
-        double zz[8], a0[8], a1[8], a2[8];
+      auto ustep = [&](int kk, double zk, double rp, double a1, double a2) {
+        const double xk = (zk - a1 * x1 - a2 * x2) * rp;
+        z[int64_t(kk) * nc] = xk;
+        nrm2 += xk * xk;
+        x2 = x1;
+        x1 = xk;
+      };
+      int k1 = nm1;
+      for (; k1 - IB + 1 >= 0; k1 -= IB) {
+        double zz[IB], a0[IB], a1[IB], a2[IB];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int k = k1 - u;
-          const bool ok = k >= 0;
-          const int64_t o = int64_t(k) * nc + j;
-          zz[u] = ok ? z[int64_t(k) * nc] : 0.0;
-          a0[u] = ok ? u0[o] : 1.0;
-          a1[u] = ok ? u1[o] : 0.0;
-          a2[u] = ok ? u2[o] : 0.0;
+        for (int u = 0; u < IB; ++u) {
+          const int64_t o = int64_t(k1 - u) * nc + j;
+          zz[u] = z[int64_t(k1 - u) * nc];
+          a0[u] = r0[o];
+          a1[u] = u1[o];
+          a2[u] = u2[o];
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int k = k1 - u;
-          if (k >= 0) {
-            double p = a0[u];
-            if (fabs(p) < tiny) p = p < 0.0 ? -tiny : tiny;
-            const double xk = (zz[u] - a1[u] * x1 - a2[u] * x2) / p;
-            z[int64_t(k) * nc] = xk;
-            nrm2 += xk * xk;
-            x2 = x1;
-            x1 = xk;
-          }
-        }
+        for (int u = 0; u < IB; ++u) ustep(k1 - u, zz[u], a0[u], a1[u], a2[u]);
       }
-      // orthogonalise against the cluster's earlier (unit) vectors
+      for (; k1 >= 0; --k1) {
+        const int64_t o = int64_t(k1) * nc + j;
+        ustep(k1, z[int64_t(k1) * nc], r0[o], u1[o], u2[o]);
+      }
+      // ---- orthogonalise against the cluster's earlier (unit) vectors
       for (int p = 0; p < q; ++p) {
         const double* zp = Z + (j + p);
         double dot = 0.0;
-        for (int k = 0; k < n; ++k) dot += zp[int64_t(k) * nc] * z[int64_t(k) * nc];
+        for (int kk = 0; kk < n; ++kk) dot += zp[int64_t(kk) * nc] * z[int64_t(kk) * nc];
         nrm2 = 0.0;
-        for (int k = 0; k < n; ++k) {
-          const double zk = z[int64_t(k) * nc] - dot * zp[int64_t(k) * nc];
-          z[int64_t(k) * nc] = zk;
+        for (int kk = 0; kk < n; ++kk) {
+          const double zk = z[int64_t(kk) * nc] - dot * zp[int64_t(kk) * nc];
+          z[int64_t(kk) * nc] = zk;
           nrm2 += zk * zk;
         }
       }
@@ -730,21 +774,25 @@ __global__ __launch_bounds__(64) void tri_inviter_kernel(const double* __restric
       if (sc == 0.0) {
         // badly scaled input: scale by the largest entry first
         double mx = 0.0;
-        for (int k = 0; k < n; ++k) mx = fmax(mx, fabs(z[int64_t(k) * nc]));
+        for (int kk = 0; kk < n; ++kk) mx = fmax(mx, fabs(z[int64_t(kk) * nc]));
         const double inv_mx = mx > 0.0 && mx < 1e308 ? 1.0 / mx : 1.0;
         nrm2 = 0.0;
-        for (int k = 0; k < n; ++k) {
-          const double zk = z[int64_t(k) * nc] * inv_mx;
+        for (int kk = 0; kk < n; ++kk) {
+          const double zk = z[int64_t(kk) * nc] * inv_mx;
           nrm2 += zk * zk;
         }
         sc = nrm2 > 0.0 ? inv_mx / sqrt(nrm2) : 1.0;
       }
     }
-    for (int k0 = 0; k0 < n; k0 += 8) {
+    int kk = 0;
+    for (; kk + IB <= n; kk += IB) {
+      double t[IB];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (k0 + u < n) z[int64_t(k0 + u) * nc] *= sc;
+      for (int u = 0; u < IB; ++u) t[u] = z[int64_t(kk + u) * nc];
+#pragma unroll
+      for (int u = 0; u < IB; ++u) z[int64_t(kk + u) * nc] = t[u] * sc;
     }
+    for (; kk < n; ++kk) z[int64_t(kk) * nc] *= sc;
   }
 }
 
