@@ -924,45 +924,47 @@ __global__ __launch_bounds__(256) void bt_vtz_kernel(const double* __restrict__ 
     }
 }
 
-// Y2 = T * sum_ch Yp[ch]   (64 columns per workgroup)
-__global__ __launch_bounds__(256) void bt_ty_kernel(const double* __restrict__ Yp, int nch,
-                                                    const double* __restrict__ T, int ncols,
-                                                    double* __restrict__ Y2) {
-  __shared__ double Y[BW][64 + 1];
+// Y[a][c] = sum_ch Yp[ch][a][c]  (one element per thread, partials in order)
+__global__ __launch_bounds__(256) void bt_reduce_kernel(const double* __restrict__ Yp, int nch, int ncols,
+                                                        double* __restrict__ Y) {
+  const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t tot = int64_t(BW) * ncols;
+  if (e >= tot) return;
+  double t[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) t[u] = Yp[int64_t(min(u, nch - 1)) * tot + e];
+  double sacc = 0.0;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) sacc += u < nch ? t[u] : 0.0;
+  for (int ch = 16; ch < nch; ++ch) sacc += Yp[int64_t(ch) * tot + e];
+  Y[e] = sacc;
+}
+
+// Y2 = T Y for 16 rows x 64 columns per workgroup (T upper triangular)
+__global__ __launch_bounds__(256) void bt_ty_kernel(const double* __restrict__ Y, const double* __restrict__ T,
+                                                    int ncols, double* __restrict__ Y2) {
+  __shared__ double sy[BW][64 + 1];
+  __shared__ double st[16][BW + 1];
   const int tid = threadIdx.x;
-  const int c0 = blockIdx.x * 64;
+  const int c0 = blockIdx.x * 64, a0 = blockIdx.y * 16;
   for (int q = tid; q < BW * 64; q += 256) {
-    const int a = q / 64, cc = q % 64;
-    double s = 0.0;
-    if (c0 + cc < ncols)
-      for (int ch = 0; ch < nch; ++ch) s += Yp[(int64_t(ch) * BW + a) * ncols + c0 + cc];
-    Y[a][cc] = s;
+    const int l = q >> 6, cc = q & 63;
+    sy[l][cc] = c0 + cc < ncols ? Y[int64_t(l) * ncols + c0 + cc] : 0.0;
   }
+  for (int q = tid; q < 16 * BW; q += 256) st[q / BW][q % BW] = T[(a0 + q / BW) * BW + q % BW];
   __syncthreads();
-  const int ty = tid >> 4, tx = tid & 15;   // a = ty*8.., c = tx*4..
-  double acc[8][4];
+  const int ar = tid >> 4, cq = (tid & 15) * 4;
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int l = a0 + ar; l < BW; ++l) {
+    const double t = st[ar][l];
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) acc[a][q] = 0.0;
-  for (int l = 0; l < BW; ++l) {
-    double t8[8], y4[4];
-#pragma unroll
-    for (int a = 0; a < 8; ++a) t8[a] = T[(ty * 8 + a) * BW + l];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) y4[q] = Y[l][tx * 4 + q];
-#pragma unroll
-    for (int a = 0; a < 8; ++a)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) acc[a][q] += t8[a] * y4[q];
+    for (int q = 0; q < 4; ++q) acc[q] += t * sy[l][cq + q];
   }
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int cc = c0 + tx * 4 + q;
-      if (cc < ncols) Y2[int64_t(ty * 8 + a) * ncols + cc] = acc[a][q];
-    }
+  for (int q = 0; q < 4; ++q) {
+    const int cc = c0 + cq + q;
+    if (cc < ncols) Y2[int64_t(a0 + ar) * ncols + cc] = acc[q];
+  }
 }
 
 // Z[r][c] -= sum_a V[r][a] Y2[a][c]   (64 x 64 tile of rows g0+1.. per workgroup)
@@ -1054,7 +1056,7 @@ __global__ __launch_bounds__(256) void tri_out_kernel(const double* __restrict__
 }
 
 struct TWs {
-  double *P, *S, *SV, *SW, *npart, *x0, *d, *e, *tau, *Wp, *lam, *bounds, *U, *Z, *Gp, *T, *Yp, *Y2;
+  double *P, *S, *SV, *SW, *npart, *x0, *d, *e, *tau, *Wp, *lam, *bounds, *U, *Z, *Gp, *T, *Yp, *Yr, *Y2;
   int *clen, *flag;
   uint8_t* piv;
 };
@@ -1084,6 +1086,7 @@ TWs carve_tri(Carve& cv, int64_t n, int64_t ncols) {
   w.Gp = cv.take<double>(size_t(ngroups * ngc * BW * BW));
   w.T = cv.take<double>(size_t(ngroups * BW * BW));
   w.Yp = cv.take<double>(size_t(nbc * BW * ncols));
+  w.Yr = cv.take<double>(size_t(BW * ncols));
   w.Y2 = cv.take<double>(size_t(BW * ncols));
   w.clen = cv.take<int>(size_t(ncols));
   w.flag = cv.take<int>(1);
@@ -1209,7 +1212,9 @@ lrc_status tridiag_eig(hipStream_t st, double* A, int64_t k, int64_t lda, int64_
         bt_vtz_kernel<<<dim3(ctiles, unsigned(nch)), 256, 0, st>>>(A, lda, n, nref, g0, w.Z, ncols, w.Yp);
         LRC_LAUNCHED();
       }
-      bt_ty_kernel<<<ctiles, 256, 0, st>>>(w.Yp, nch, w.T + int64_t(g) * BW * BW, ncols, w.Y2);
+      bt_reduce_kernel<<<unsigned(cdiv(int64_t(BW) * ncols, 256)), 256, 0, st>>>(w.Yp, nch, ncols, w.Yr);
+      LRC_LAUNCHED();
+      bt_ty_kernel<<<dim3(ctiles, BW / 16), 256, 0, st>>>(w.Yr, w.T + int64_t(g) * BW * BW, ncols, w.Y2);
       LRC_LAUNCHED();
       {
         ProfScope scope("bt_update_kernel", st, fl, 0.0);
