@@ -7,16 +7,16 @@
 //
 // bf16 path (the hot one).  The reduction axis is the token axis, which is the strided
 // axis of the token-major input, while an MFMA operand wants 8 consecutive reduction
-// elements per lane.  Each thread therefore loads an 8 tokens x 8 channels block with
-// eight 16-byte loads, transposes it in registers (v_perm-style half-word shuffles) and
-// stores it channel-major into LDS, from where a lane reads a whole MFMA fragment with
-// one 16-byte LDS read.  Tiles are 256 x 256 of the lower triangle, 8 waves each own a
-// 128 x 64 block computed with v_mfma_f32_32x32x16_bf16 (fp32 accumulation of exact
-// bf16 products).  Tokens are split S ways so that the launch fills the chip; partial
-// tiles are summed in split order by whichever workgroup of a tile finishes last (an
-// arrival counter, no waiting), so results are bit-reproducible.  Workgroups of one
-// split are mapped so that each XCD works on one compact group of tiles over the same
-// token range: the operand panels they share stay in that XCD's L2.
+// elements per lane.  Token rows are therefore copied unchanged (16-byte chunks) into
+// LDS, and each lane reads its fragment with two LDS transpose reads
+// (ds_read_b64_tr_b16), which hand every lane 4 consecutive tokens of one channel.
+// Tiles are 256 x 256 of the lower triangle; 4 waves each own a 128 x 128 block computed
+// with v_mfma_f32_32x32x16_bf16 (fp32 accumulation of exact bf16 products; the
+// accumulators fill the waves' accumulation registers).  Global loads run one stage ahead
+// in registers from clamped addresses (range masking happens at the LDS store, so the
+// loads stay unpredicated and in flight together).  Tokens are split S ways so that the
+// launch fills the chip; every split writes its partial tile and a second kernel adds the
+// partials to C in split order, so results are bit-reproducible.
 #include "lrc_internal.h"
 
 namespace lrc {
@@ -24,9 +24,9 @@ namespace {
 
 constexpr int TB = 256;              // tile edge in channels
 constexpr int KS = 64;               // tokens per LDS stage
-constexpr int PITCH = KS + 8;        // bf16 per channel row in LDS: 144 B
-constexpr int NTH = 512;             // threads per workgroup
-constexpr int OPER = TB * PITCH;     // bf16 per operand per stage
+constexpr int RP = TB + 32;          // bf16 per token row in LDS: 576 B (rows shift by 16 banks)
+constexpr int NTH = 256;             // threads per workgroup (4 waves, 2 x 2 blocks of 128 x 128)
+constexpr int OPER = KS * RP;        // bf16 per operand per stage
 constexpr int NXCD = 8;              // XCDs on MI355X
 constexpr int QAW_CHUNK = 32768;     // tokens per QAW pre-pass chunk
 
@@ -57,57 +57,64 @@ __device__ __forceinline__ TileRC tile_of(int lin, int n1) {
   return {-1, -1};
 }
 
+// One 16-byte chunk (8 channels of one token) per load, always from a clamped in-range
+// address.  Out-of-range tokens and channels are zeroed when the chunk is stored to LDS,
+// one pipeline stage later: zeroing next to the load would make the compiler predicate
+// the load and wait for it (and for every earlier load) right there.
 template <bool VEC>
-__device__ __forceinline__ void load_block(const uint16_t* __restrict__ X, int64_t ldx, int64_t t0,
-                                           int64_t t_end, int c, int d, uint4 (&r)[8]) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int64_t t = t0 + j;
-    if (VEC) {
-      if (t < t_end && c < d)
-        r[j] = *reinterpret_cast<const uint4*>(X + t * ldx + c);
-      else
-        r[j] = make_uint4(0u, 0u, 0u, 0u);
-    } else {
-      uint32_t h[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) h[e] = (t < t_end && c + e < d) ? X[t * ldx + c + e] : 0u;
-      r[j] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                        h[6] | (h[7] << 16));
-    }
+__device__ __forceinline__ uint4 load_chunk(const uint16_t* __restrict__ X, int64_t ldx, int64_t t, int64_t t_end,
+                                            int c, int d) {
+  const int64_t tc = t < t_end ? t : t_end - 1;
+  if (VEC) {
+    const int cc = c < d ? c : d - 8;
+    return *reinterpret_cast<const uint4*>(X + tc * ldx + cc);
   }
+  uint32_t h[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) h[e] = X[tc * ldx + (c + e < d ? c + e : d - 1)];
+  return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
 }
 
-// r[j] holds channels 0..7 of token j (two per word); o[c] receives tokens 0..7 of channel c
-__device__ __forceinline__ void transpose8(const uint4 (&r)[8], uint4 (&o)[8]) {
-  uint32_t in[32];
+// zero the halves of a chunk whose token or channel is out of range
+__device__ __forceinline__ uint4 mask_chunk(uint4 v, bool ok_t, int c, int d) {
+  if (!ok_t || c >= d) return make_uint4(0u, 0u, 0u, 0u);
+  if (c + 8 <= d) return v;
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    in[4 * j + 0] = r[j].x; in[4 * j + 1] = r[j].y; in[4 * j + 2] = r[j].z; in[4 * j + 3] = r[j].w;
-  }
-  uint32_t out[32];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t a = in[(2 * p) * 4 + (c >> 1)];
-      const uint32_t b = in[(2 * p + 1) * 4 + (c >> 1)];
-      out[4 * c + p] = (c & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
-    }
-  }
-#pragma unroll
-  for (int c = 0; c < 8; ++c) o[c] = make_uint4(out[4 * c], out[4 * c + 1], out[4 * c + 2], out[4 * c + 3]);
+  for (int e = 0; e < 8; ++e)
+    if (c + e >= d) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// MFMA operand fragment from token-major LDS rows (row pitch RP bf16): lane l of the wave
+// receives channel ch0 + l % 32, tokens k0 + 8 (l / 32) .. + 7, via two LDS transpose
+// reads.  Within each 16-lane group, lane s addresses token (s / 4) and channels
+// 4 (s % 4) .. + 3 of its 16 channels; lane i of the group then holds 4 tokens of channel i.
+__device__ __forceinline__ bf16x8 frag_tr(const uint16_t* base, int ch0, int k0, int lane) {
+  const int g = lane >> 4, sl = lane & 15;
+  const int ch = ch0 + 16 * (g & 1) + 4 * (sl & 3);
+  const int tk = k0 + 8 * (g >> 1) + (sl >> 2);
+  const uint16_t* p = base + tk * RP + ch;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 4 * RP));
+  const short tmp[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  bf16x8 f;
+  __builtin_memcpy(&f, tmp, sizeof(f));
+  return f;
 }
 
 // C[lower] += X^T Y over tokens [0, n) (X, Y: n x d bf16 bits, leading dim ldx).
-// grid.x = NXCD * tiles_per_xcd * splits.
+// Workgroup -> (split, tile): consecutive workgroups land on consecutive XCDs, and XCD x
+// takes one compact group of tiles for every split (grid.x = NXCD * tiles_per_xcd *
+// splits), so the operand panels its tiles share are read through its own L2.
 template <bool VEC>
 __global__ __launch_bounds__(NTH, 1) void syrk_bf16_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Y, int64_t ldx, int64_t n, int d,
-    int n1, int n_tiles, int tiles_per_xcd, int splits, int steps_per_split, float* __restrict__ C,
-    int64_t ldc, float* __restrict__ partial, unsigned* __restrict__ counters) {
+    int n1, int n_tiles, int tiles_per_xcd, int splits, int steps_per_split, float* __restrict__ partial) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * OPER];
-  __shared__ int s_last;
 
   const int b = blockIdx.x;
   const int xcd = b % NXCD;
@@ -120,139 +127,138 @@ __global__ __launch_bounds__(NTH, 1) void syrk_bf16_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wr = wave >> 2, wc = wave & 3;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
+  const int wr = wave >> 1, wc = wave & 1;
+  // on a diagonal tile the wave owning rows 0..127 x columns 128..255 lies entirely above
+  // the diagonal and skips its MFMAs; every other block is computed (products above the
+  // diagonal are valid and ignored by the reduction), so the MFMA stream has no branches
+  const bool wave_dead = (ti == tj) && (wr < wc);
 
-  // loader role: operand, channel group, token group
-  const int op = tid >> 8;
-  const int u = tid & 255;
-  const int cg = u >> 3, tg = u & 7;
+  // loader role: operand, 16-byte channel chunk, first token (tokens tok0 + 4 i, i < 16)
+  const int op = tid >> 7;
+  const int u = tid & 127;
+  const int chunk = u & 31, tok0 = u >> 5;
   const uint16_t* src = op ? Y : X;
-  const int chan = (op ? tj : ti) * TB + cg * 8;
+  const int chan = (op ? tj : ti) * TB + chunk * 8;
 
   const int64_t tok_begin = int64_t(split) * steps_per_split * KS;
   const int64_t tok_end = min<int64_t>(n, tok_begin + int64_t(steps_per_split) * KS);
   const int nsteps = tok_end > tok_begin ? int((tok_end - tok_begin + KS - 1) / KS) : 0;
 
-  // wave-level skip of 32x32 blocks strictly above the diagonal of a diagonal tile
-  bool live[4][2];
+  f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      live[i][j] = (ti != tj) || (wr * 128 + i * 32 + 31 >= wc * 64 + j * 32);
-
-  f32x16 acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  uint4 pre[8];
-  auto stage_store = [&](int buf) {
-    uint4 o[8];
-    transpose8(pre, o);
-    uint16_t* dst = lds + (buf * 2 + op) * OPER + (cg * 8) * PITCH + tg * 8;
+  // two stages of token rows in flight in registers, two in LDS
+  uint4 pa[16], pb[16];
+  auto load_stage = [&](uint4 (&r)[16], int64_t t0) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(dst + c * PITCH) = o[c];
+    for (int i = 0; i < 16; ++i) r[i] = load_chunk<VEC>(src, ldx, t0 + tok0 + 4 * i, tok_end, chan, d);
   };
-
-  if (nsteps > 0) {
-    load_block<VEC>(src, ldx, tok_begin + tg * 8, tok_end, chan, d, pre);
-    stage_store(0);
-  }
-  __syncthreads();
-
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nsteps) load_block<VEC>(src, ldx, tok_begin + int64_t(s + 1) * KS + tg * 8, tok_end, chan, d, pre);
-
+  auto store_stage = [&](const uint4 (&r)[16], int buf, int64_t t0) {
+    uint16_t* dst = lds + (buf * 2 + op) * OPER + tok0 * RP + chunk * 8;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      *reinterpret_cast<uint4*>(dst + 4 * i * RP) = mask_chunk(r[i], t0 + tok0 + 4 * i < tok_end, chan, d);
+  };
+  auto compute = [&](int buf) {
+    if (wave_dead) return;
     const uint16_t* xa = lds + (buf * 2 + 0) * OPER;
     const uint16_t* yb = lds + (buf * 2 + 1) * OPER;
 #pragma unroll
     for (int kk = 0; kk < KS / 16; ++kk) {
-      const int koff = kk * 16 + (lane >> 5) * 8;
-      bf16x8 fa[4], fb[2];
+      bf16x8 fa[4], fb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8*>(xa + (wr * 128 + i * 32 + (lane & 31)) * PITCH + koff);
+      for (int i = 0; i < 4; ++i) fa[i] = frag_tr(xa, wr * 128 + i * 32, kk * 16, lane);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        fb[j] = *reinterpret_cast<const bf16x8*>(yb + (wc * 64 + j * 32 + (lane & 31)) * PITCH + koff);
+      for (int j = 0; j < 4; ++j) fb[j] = frag_tr(yb, wc * 128 + j * 32, kk * 16, lane);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          if (live[i][j]) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
-    if (s + 1 < nsteps) stage_store(buf ^ 1);
+  };
+
+  // Stage s computes from LDS buffer s & 1.  At its end the registers holding stage s + 1
+  // (loaded two stages earlier, the oldest loads in flight) go to the other buffer and are
+  // refilled with stage s + 3, so the loads of stage s + 2 stay in flight throughout.
+  if (nsteps > 0) load_stage(pa, tok_begin);
+  if (nsteps > 1) load_stage(pb, tok_begin + KS);
+  if (nsteps > 0) store_stage(pa, 0, tok_begin);
+  if (nsteps > 2) load_stage(pa, tok_begin + 2 * KS);
+  __syncthreads();
+  for (int s = 0; s < nsteps; s += 2) {
+    compute(0);
+    if (s + 1 < nsteps) store_stage(pb, 1, tok_begin + int64_t(s + 1) * KS);
+    if (s + 3 < nsteps) load_stage(pb, tok_begin + int64_t(s + 3) * KS);
+    __syncthreads();
+    if (s + 1 >= nsteps) break;
+    compute(1);
+    if (s + 2 < nsteps) store_stage(pa, 0, tok_begin + int64_t(s + 2) * KS);
+    if (s + 4 < nsteps) load_stage(pa, tok_begin + int64_t(s + 4) * KS);
     __syncthreads();
   }
 
-  // ---- epilogue.  Output layout of a 32x32 block: lane l, element e ->
-  //      row 8*(e/4) + 4*(l/32) + e%4, column l%32.
-  const int r_base = wr * 128, c_base = wc * 64;
-  if (splits == 1) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        if (!live[i][j]) continue;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int lr = r_base + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-          const int lc = c_base + j * 32 + (lane & 31);
-          const int row = ti * TB + lr, col = tj * TB + lc;
-          if (row < d && col < d && (ti != tj || row >= col)) C[int64_t(row) * ldc + col] += acc[i][j][e];
-        }
-      }
-    return;
-  }
-
+  // ---- epilogue: this split's partial tile.  Output layout of a 32x32 block: lane l,
+  //      element e -> row 8*(e/4) + 4*(l/32) + e%4, column l%32.
+  const int r_base = wr * 128, c_base = wc * 128;
   float* part = partial + (int64_t(split) * n_tiles + tile) * (TB * TB);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int lr = r_base + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
         const int lc = c_base + j * 32 + (lane & 31);
         part[lr * TB + lc] = acc[i][j][e];
       }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = atomicAdd(&counters[tile], 1u);
-    s_last = (prev == unsigned(splits - 1));
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  // last arriving split: sum all splits in split order, add into C
-  for (int idx = tid; idx < TB * TB / 4; idx += NTH) {
-    const int lr = (idx * 4) / TB, lc = (idx * 4) % TB;
-    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-    for (int s2 = 0; s2 < splits; ++s2) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(partial + (int64_t(s2) * n_tiles + tile) * (TB * TB) + lr * TB + lc);
-      sum += v;
-    }
-    const int row = ti * TB + lr;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int col = tj * TB + lc + e;
-      if (row < d && col < d && (ti != tj || row >= col)) C[int64_t(row) * ldc + col] += sum[e];
-    }
-  }
-  if (tid == 0) counters[tile] = 0u;
 }
 
-__global__ void zero_u32_kernel(unsigned* p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
+// C[lower] += sum over splits of the partial tiles, in split order (bit-reproducible).
+// Block (tile, q) handles 256 consecutive float4 of the tile; loads are batched 8 splits
+// at a time from clamped addresses, then masked.
+__global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restrict__ partial, int splits, int n_tiles,
+                                                          int n1, int d, float* __restrict__ C, int64_t ldc,
+                                                          int vec4) {
+  const int tile = blockIdx.x;
+  const TileRC tc = tile_of(tile, n1);
+  const int idx = blockIdx.y * 256 + threadIdx.x;   // float4 index within the tile
+  const int lr = (idx * 4) / TB, lc = (idx * 4) % TB;
+  const int row = tc.ti * TB + lr, col0 = tc.tj * TB + lc;
+  if (row >= d || col0 >= d) return;
+  if (tc.ti == tc.tj && col0 > row) return;   // entirely above the diagonal
+  const int64_t pstride = int64_t(n_tiles) * TB * TB;
+  const float* pb = partial + int64_t(tile) * TB * TB + idx * 4;
+  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < splits; s0 += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x4*>(pb + int64_t(min(s0 + u, splits - 1)) * pstride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      sum += (s0 + u < splits) ? v[u] : z;
+    }
+  }
+  float* c = C + int64_t(row) * ldc + col0;
+  if (vec4 && col0 + 3 < d && (tc.ti != tc.tj || col0 + 3 <= row)) {
+    f32x4 cv = *reinterpret_cast<const f32x4*>(c);
+    *reinterpret_cast<f32x4*>(c) = cv + sum;
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int col = col0 + e;
+    if (col < d && (tc.ti != tc.tj || col <= row)) c[e] += sum[e];
+  }
 }
+
 
 // ---- QAW pre-pass: per token scale, integer code q, and s^2 q split into bf16 hi + lo
 template <typename T>
@@ -332,6 +338,7 @@ __global__ __launch_bounds__(256) void syrk_f32_kernel(const float* __restrict__
 
 struct SyrkPlan {
   int n1, n_tiles, tiles_per_xcd, splits, steps_per_split;
+  int64_t grid;
 };
 
 SyrkPlan plan_syrk(int64_t n, int64_t d, int max_splits = 64) {
@@ -343,35 +350,33 @@ SyrkPlan plan_syrk(int64_t n, int64_t d, int max_splits = 64) {
   // The plan depends on the shape only (a 256-CU MI355X is assumed), so that workspace
   // sizes are known without a device and equal inputs give equal bits on any device.
   const int cus = 256;
-  // cost model: workgroup rounds x (steps per workgroup + partial write/reduce overhead)
+  // cost model: workgroup rounds x (steps per workgroup + partial write overhead; a
+  // split's 256 KB partial tile costs about as much time as 16 steps of MFMA work)
   int best = 1;
   double best_cost = 1e300;
   const int smax = int(std::min<int64_t>(std::max(1, max_splits), std::max<int64_t>(1, nsteps)));
   for (int s = 1; s <= smax; ++s) {
-    const int64_t wgs = int64_t(NXCD) * p.tiles_per_xcd * s;
-    const double rounds = double(cdiv(wgs, cus));
-    const double cost = rounds * (double(cdiv(nsteps, s)) + (s > 1 ? 4.0 : 0.0));
+    const double rounds = double(cdiv(int64_t(NXCD) * p.tiles_per_xcd * s, cus));
+    const double cost = rounds * (double(cdiv(nsteps, s)) + 16.0);
     if (cost < best_cost - 1e-9) { best_cost = cost; best = s; }
   }
-  p.splits = best;
   p.steps_per_split = int(cdiv(nsteps, best));
   p.splits = int(cdiv(nsteps, p.steps_per_split));  // drop empty splits
   if (p.splits < 1) p.splits = 1;
+  p.grid = int64_t(NXCD) * p.tiles_per_xcd * p.splits;
   return p;
 }
 
-size_t syrk_partial_floats(const SyrkPlan& p) {
-  return p.splits > 1 ? size_t(p.splits) * p.n_tiles * TB * TB : 0;
-}
+size_t syrk_partial_floats(const SyrkPlan& p) { return size_t(p.splits) * p.n_tiles * TB * TB; }
 
 // bf16 SYRK launch over a token block, partial/counter space from the carve
 lrc_status launch_syrk_bf16(hipStream_t st, const uint16_t* X, const uint16_t* Y, int64_t ldx, int64_t n,
-                            int64_t d, float* C, int64_t ldc, float* partial, unsigned* counters, int split_cap) {
+                            int64_t d, float* C, int64_t ldc, float* partial, int split_cap) {
   if (n <= 0) return LRC_OK;
   const SyrkPlan p = plan_syrk(n, d, split_cap);  // never more splits than the partial buffer holds
   const bool vec = (d % 8 == 0) && (ldx % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0) &&
                    ((reinterpret_cast<uintptr_t>(Y) & 15) == 0);
-  const dim3 grid(unsigned(NXCD * p.tiles_per_xcd * p.splits));
+  const dim3 grid(unsigned(p.grid));
   // algorithmic work: n d (d + 1) / 2 products and adds for the lower triangle incl. the
   // diagonal; bytes: the token block once (twice when the two operands differ) plus one
   // read and one write of the fp32 lower triangle
@@ -380,22 +385,26 @@ lrc_status launch_syrk_bf16(hipStream_t st, const uint16_t* X, const uint16_t* Y
                   double(n) * double(d) * 2.0 * (X == Y ? 1 : 2) + 8.0 * tri);
   if (vec)
     syrk_bf16_kernel<true><<<grid, NTH, 0, st>>>(X, Y, ldx, n, int(d), p.n1, p.n_tiles, p.tiles_per_xcd,
-                                                 p.splits, p.steps_per_split, C, ldc, partial, counters);
+                                                 p.splits, p.steps_per_split, partial);
   else
     syrk_bf16_kernel<false><<<grid, NTH, 0, st>>>(X, Y, ldx, n, int(d), p.n1, p.n_tiles, p.tiles_per_xcd,
-                                                  p.splits, p.steps_per_split, C, ldc, partial, counters);
+                                                  p.splits, p.steps_per_split, partial);
+  LRC_LAUNCHED();
+  const int vec4 = (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & 15) == 0);
+  syrk_reduce_kernel<<<dim3(unsigned(p.n_tiles), unsigned(TB * TB / 4 / 256)), 256, 0, st>>>(
+      partial, p.splits, p.n_tiles, p.n1, int(d), C, ldc, vec4);
   LRC_LAUNCHED();
   return LRC_OK;
 }
 
 size_t cov_workspace(lrc_dtype dt, int64_t n, int64_t d, uint32_t flags, void* base, float** partial,
-                     unsigned** counters, uint16_t** q, uint16_t** h, uint16_t** l, int64_t* chunk, int* split_cap) {
+                     uint16_t** q, uint16_t** h, uint16_t** l, int64_t* chunk, int* split_cap) {
   Carve cv(base);
   const bool quant = flags & LRC_COV_QUANT_INT8_TOKEN;
   int64_t nb = n;
   if (quant) nb = std::min<int64_t>(n, QAW_CHUNK);
   size_t pf = 0;
-  int nt = 0, cap = 1;
+  int cap = 1;
   if (dt == LRC_BF16 || quant) {
     // launches see token blocks of nb tokens and, for QAW, one final block of n % nb
     SyrkPlan p = plan_syrk(std::max<int64_t>(nb, 1), d);
@@ -403,10 +412,8 @@ size_t cov_workspace(lrc_dtype dt, int64_t n, int64_t d, uint32_t flags, void* b
     if (quant && n % nb) cap = std::max(cap, plan_syrk(n % nb, d).splits);
     p.splits = cap;
     pf = syrk_partial_floats(p);
-    nt = p.n_tiles;
   }
   float* pp = cv.take<float>(pf);
-  unsigned* cc = cv.take<unsigned>(size_t(std::max(nt, 1)));
   uint16_t *qq = nullptr, *hh = nullptr, *ll = nullptr;
   if (quant) {
     qq = cv.take<uint16_t>(size_t(nb) * d);
@@ -414,7 +421,6 @@ size_t cov_workspace(lrc_dtype dt, int64_t n, int64_t d, uint32_t flags, void* b
     ll = cv.take<uint16_t>(size_t(nb) * d);
   }
   if (partial) *partial = pp;
-  if (counters) *counters = cc;
   if (q) *q = qq;
   if (h) *h = hh;
   if (l) *l = ll;
@@ -430,7 +436,7 @@ using namespace lrc;
 
 extern "C" size_t lrc_accumulate_cov_workspace(lrc_dtype dt, int64_t n_tokens, int64_t d, uint32_t flags) {
   if (n_tokens < 0 || d <= 0) return 0;
-  return cov_workspace(dt, n_tokens, d, flags, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+  return cov_workspace(dt, n_tokens, d, flags, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
 }
 
 extern "C" lrc_status lrc_accumulate_cov(const void* A, lrc_dtype dt, int64_t n_tokens, int64_t d, int64_t lda,
@@ -447,14 +453,11 @@ extern "C" lrc_status lrc_accumulate_cov(const void* A, lrc_dtype dt, int64_t n_
   hipStream_t st = static_cast<hipStream_t>(stream);
 
   float* partial = nullptr;
-  unsigned* counters = nullptr;
   uint16_t *q = nullptr, *h = nullptr, *l = nullptr;
   int64_t chunk = 0;
   int cap = 1;
-  cov_workspace(dt, n_tokens, d, flags, ws, &partial, &counters, &q, &h, &l, &chunk, &cap);
+  cov_workspace(dt, n_tokens, d, flags, ws, &partial, &q, &h, &l, &chunk, &cap);
   const bool quant = flags & LRC_COV_QUANT_INT8_TOKEN;
-  const int n1 = int(cdiv(d, TB));
-  const int nt = n1 * (n1 + 1) / 2;
 
   if (!quant && dt == LRC_F32) {
     const int tiles = int(cdiv(d, 64) * (cdiv(d, 64) + 1) / 2);
@@ -464,11 +467,9 @@ extern "C" lrc_status lrc_accumulate_cov(const void* A, lrc_dtype dt, int64_t n_
     LRC_LAUNCHED();
     return LRC_OK;
   }
-  zero_u32_kernel<<<unsigned(cdiv(nt, 256)), 256, 0, st>>>(counters, nt);
-  LRC_LAUNCHED();
   if (!quant) {
     const uint16_t* a = static_cast<const uint16_t*>(A);
-    return launch_syrk_bf16(st, a, a, lda, n_tokens, d, C, ldc, partial, counters, cap);
+    return launch_syrk_bf16(st, a, a, lda, n_tokens, d, C, ldc, partial, cap);
   }
   for (int64_t t0 = 0; t0 < n_tokens; t0 += chunk) {
     const int64_t nb = std::min(chunk, n_tokens - t0);
@@ -482,8 +483,8 @@ extern "C" lrc_status lrc_accumulate_cov(const void* A, lrc_dtype dt, int64_t n_
                                                               int(d), q, h, l, d);
     LRC_LAUNCHED();
     }
-    LRC_TRY(launch_syrk_bf16(st, q, h, d, nb, d, C, ldc, partial, counters, cap));
-    LRC_TRY(launch_syrk_bf16(st, q, l, d, nb, d, C, ldc, partial, counters, cap));
+    LRC_TRY(launch_syrk_bf16(st, q, h, d, nb, d, C, ldc, partial, cap));
+    LRC_TRY(launch_syrk_bf16(st, q, l, d, nb, d, C, ldc, partial, cap));
   }
   return LRC_OK;
 }
