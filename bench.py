@@ -39,6 +39,7 @@ ROOFLINE = {
     "qaw_prepass_kernel": {"bound": "hbm", "dtype": "bf16", "peak": HBM_PEAK_GBS, "unit": "GB/s"},
     "tri_symv_kernel": {"bound": "hbm", "dtype": "f64", "peak": HBM_PEAK_GBS, "unit": "GB/s"},
     "tri_w_kernel": {"bound": "hbm", "dtype": "f64", "peak": HBM_PEAK_GBS, "unit": "GB/s"},
+    "tri_fused_kernel": {"bound": "hbm", "dtype": "f64", "peak": HBM_PEAK_GBS, "unit": "GB/s"},
     "tri_syr2k_kernel": {"bound": "alu", "dtype": "f64", "peak": PEAK_TFLOPS["f64"], "unit": "TFLOP/s"},
     "bt_vtz_kernel": {"bound": "alu", "dtype": "f64", "peak": PEAK_TFLOPS["f64"], "unit": "TFLOP/s"},
     "bt_update_kernel": {"bound": "alu", "dtype": "f64", "peak": PEAK_TFLOPS["f64"], "unit": "TFLOP/s"},
@@ -58,6 +59,7 @@ def parse():
     p.add_argument("--d", type=int, default=4096)
     p.add_argument("--rank", type=int, default=1024)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-secondary", action="store_true", help="skip the scoring / allocation measurements")
     return p.parse_args()
 
 
@@ -93,6 +95,58 @@ def cpu_baseline(d, n, rank):
             "sample": f"fp64 covariance of {ns} of {n} tokens (time x{n / ns:g}) + full {d}x{d} "
                       f"Cholesky/whitening/SVD/back-map/K-FAC scores/allocation at rank {rank}",
             "cov_tokens_per_s": round(n / t_cov, 1), "seconds_measured": round(t_cov_meas + t_dec, 2)}
+
+
+def _time(fn, torch, reps):
+    """median wall time of fn() over reps runs, each bracketed by device synchronisation"""
+    ts = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        ts.append(time.perf_counter() - t0)
+    return sorted(ts)[len(ts) // 2]
+
+
+def secondary(lrc, torch, dev):
+    """Throughput of the scoring and allocation passes at the decoder-stack workload's
+    shapes (synthetic inputs): empirical-Fisher scores of one 4096 x 4096 matrix over
+    32768 tokens with all 4096 components, and the global sort-and-truncate over the
+    stack's 917,504 components and over a scaled 64M-component pool."""
+    import synth
+    out = {}
+    n, d, k = 32768, 4096, 4096
+    a = synth.activation_stream(n, d, 1.0, 41, dtype=torch.bfloat16, device=dev)
+    b = synth.activation_stream(n, d, 1.5, 42, dtype=torch.bfloat16, device=dev)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(43)
+    left = torch.randn(d, k, generator=g, device=dev) / d ** 0.5
+    right = torch.randn(k, d, generator=g, device=dev) / d ** 0.5
+    lrc.lrc_score_components(left=left, right=right, A=a, B=b, mode="fisher")   # warm-up
+    t = _time(lambda: lrc.lrc_score_components(left=left, right=right, A=a, B=b, mode="fisher"), torch, 3)
+    flops = 2.0 * n * k * (d + d) + 3.0 * n * k
+    out["fisher_scores"] = {"workload": f"{n} bf16 tokens, {d}x{d} matrix, {k} components", "ms": round(t * 1e3, 3),
+                            "TFLOP/s": round(flops / t / 1e12, 2)}
+    del a, b, left, right
+    for m_items, label in ((917504, "decoder stack: 224 matrices"), (64 * 1024 * 1024, "scaled pool")):
+        n_mat = 224 if m_items == 917504 else 16384
+        per = m_items // n_mat
+        offs = torch.arange(0, m_items + 1, per, dtype=torch.int64, device=dev)
+        cost = torch.where(torch.arange(n_mat, device=dev) % 7 < 4, 8192, 15104).to(torch.int64)
+        scores = torch.rand(m_items, generator=g, device=dev)
+        budget = int(0.6 * float((cost * per).sum()))
+        lrc.lrc_allocate_ranks(scores, offs, cost, budget)
+        t = _time(lambda: lrc.lrc_allocate_ranks(scores, offs, cost, budget), torch, 5)
+        # bytes a sort-and-truncate must move at least: scores in, order out, per item
+        # cost gather/scan and mask (24 B), the 8 radix passes of 64-bit keys + 32-bit
+        # ids read and written (8 x 2 x 12 B)
+        byt = m_items * (24.0 + 8 * 2 * 12.0)
+        out[f"allocation_{m_items}"] = {"workload": f"{m_items} components ({label})", "ms": round(t * 1e3, 3),
+                                        "items_per_s": round(m_items / t, 1),
+                                        "GB/s": round(byt / t / 1e9, 1),
+                                        "hbm_frac": round(byt / t / 1e9 / HBM_PEAK_GBS, 4)}
+    return out
 
 
 def main():
@@ -195,6 +249,8 @@ def main():
                      "launches_per_step": dk["launches"] / args.steps},
         "kernels": kernels,
     }
+    if not args.no_secondary:
+        res["secondary"] = secondary(lrc, torch, dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(d, n, r)
     print(json.dumps(res), flush=True)

@@ -75,11 +75,36 @@ __device__ __forceinline__ void house_from_sum(double xn2, double x0, double& ta
   scale = 1.0 / (x0 - beta);
 }
 
-// sum over the 64 lanes of a wave with a fixed butterfly (every lane gets the same bits)
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+// Cross-lane moves of a double with DPP (register-to-register, no LDS round trip)
+template <int CTRL>
+__device__ __forceinline__ double dpp_mov(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xF, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+constexpr int DPP_QUAD_XOR1 = 0xB1;   // quad_perm [1, 0, 3, 2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;   // quad_perm [2, 3, 0, 1]
+constexpr int DPP_HALF_MIRROR = 0x141;
+constexpr int DPP_MIRROR = 0x140;
+
+// sum over the 4 lanes of a quad (every lane of the quad gets the same bits)
+__device__ __forceinline__ double quad_sum(double v) {
+  v += dpp_mov<DPP_QUAD_XOR1>(v);
+  v += dpp_mov<DPP_QUAD_XOR2>(v);
   return v;
+}
+
+// sum over the 64 lanes of a wave in a fixed order (quads, 8-lane halves, 16-lane rows,
+// then the four rows); every lane gets the same bits
+__device__ __forceinline__ double wave_sum(double v) {
+  v = quad_sum(v);
+  v += dpp_mov<DPP_HALF_MIRROR>(v);
+  v += dpp_mov<DPP_MIRROR>(v);
+  auto lane_val = [&](int l) {
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
+                            __builtin_amdgcn_readlane(__double2loint(v), l));
+  };
+  return (lane_val(0) + lane_val(16)) + (lane_val(32) + lane_val(48));
 }
 
 // block-wide sums (256 threads) of two values: wave butterflies, then the four wave
@@ -206,10 +231,8 @@ __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict_
       const double t = (diag && q == x) ? 0.0 : T[q][x];
       scol += t * vb[q];
     }
-    srow += __shfl_xor(srow, 1);
-    srow += __shfl_xor(srow, 2);
-    scol += __shfl_xor(scol, 1);
-    scol += __shfl_xor(scol, 2);
+    srow = quad_sum(srow);
+    scol = quad_sum(scol);
     if (part == 0) {
       rs[x] = srow;
       cs[x] = scol;
@@ -330,10 +353,8 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
     yraw += P[(int64_t(b) * nbt + c0) * TS + x];
     y0raw += P[int64_t(c0) * TS];
   }
-  yraw += __shfl_xor(yraw, 1);
-  yraw += __shfl_xor(yraw, 2);
-  y0raw += __shfl_xor(y0raw, 1);
-  y0raw += __shfl_xor(y0raw, 2);
+  yraw = quad_sum(yraw);
+  y0raw = quad_sum(y0raw);
   double a0 = 0.0, a1 = 0.0;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
@@ -413,10 +434,8 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
     corr += wr * sv[c] + vr * sw[c];
     c2 += vr * wn[c] + wr * vn[c];
   }
-  corr += __shfl_xor(corr, 1);
-  corr += __shfl_xor(corr, 2);
-  c2 += __shfl_xor(c2, 1);
-  c2 += __shfl_xor(c2, 2);
+  corr = quad_sum(corr);
+  c2 = quad_sum(c2);
   double v = 0.0, w = 0.0;
   if (r < n) {
     const double y = scale * yraw + cfac * cols0 - corr;
