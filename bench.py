@@ -60,6 +60,9 @@ def parse():
     p.add_argument("--rank", type=int, default=1024)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true", help="skip the scoring / allocation measurements")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="before the steps, run a plain elementwise copy (neg) of this many MiB three times: "
+                        "the known-size kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
     return p.parse_args()
 
 
@@ -168,6 +171,12 @@ def main():
     offs = torch.tensor([0, d], dtype=torch.int64, device=dev)
     cost = torch.tensor([2 * d], dtype=torch.int64, device=dev)
     budget = r * 2 * d
+    if args.copy_probe_mib:
+        src = torch.ones(args.copy_probe_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        del src, dst
     torch.cuda.synchronize()
 
     def step():

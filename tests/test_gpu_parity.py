@@ -433,6 +433,25 @@ def test_allocate_large_ties(lrc):
     assert got[0].tolist() == ref[0].tolist() and got[1] == ref[1] and got[2].tolist() == ref[2].tolist()
 
 
+def test_allocate_many_tiles_skewed(lrc):
+    """About a million items (hundreds of sort tiles and a ragged last tile): half the keys
+    share one value, the rest are spread over a few hundred values, so whole tiles fall
+    into one digit and the stable order of equal keys spans tiles."""
+    rng = np.random.default_rng(21)
+    sizes = rng.integers(20000, 50000, 30)
+    costs = [int(c) for c in rng.integers(1000, 16000, 30)]
+    lst = []
+    for m in range(30):
+        s = rng.integers(0, 300, sizes[m]).astype(np.float32) * np.float32(0.25)
+        s[rng.random(sizes[m]) < 0.5] = np.float32(costs[m])   # key exactly 1.0
+        lst.append(s)
+    total = sum(c * int(z) for c, z in zip(costs, sizes))
+    got, ref = _alloc_case(lrc, lst, costs, total // 3)
+    assert got[4] == 0
+    assert got[0].tolist() == ref[0].tolist()
+    assert got[1] == ref[1] and got[2].tolist() == ref[2].tolist() and got[3].tolist() == ref[3].tolist()
+
+
 def test_allocate_edge_cases(lrc):
     # zero budget keeps nothing, a budget above the total keeps everything
     lst = [np.array([1, 2, 3], np.float32), np.zeros(0, np.float32), np.array([5], np.float32)]
