@@ -36,6 +36,7 @@ ROOFLINE = {
     "jacobi_pairs_v_kernel": {"bound": "alu", "dtype": "f64", "peak": PEAK_TFLOPS["f64"], "unit": "TFLOP/s"},
     "jacobi_apply_c_kernel": {"bound": "mfma", "dtype": "f64", "peak": PEAK_TFLOPS["f64"], "unit": "TFLOP/s"},
     "fisher_partial_kernel": {"bound": "alu", "dtype": "f32", "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s"},
+    "fisher_mfma_kernel": {"bound": "mfma", "dtype": "bf16", "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s"},
     "qaw_prepass_kernel": {"bound": "hbm", "dtype": "bf16", "peak": HBM_PEAK_GBS, "unit": "GB/s"},
     "tri_symv_kernel": {"bound": "hbm", "dtype": "f64", "peak": HBM_PEAK_GBS, "unit": "GB/s"},
     "tri_w_kernel": {"bound": "hbm", "dtype": "f64", "peak": HBM_PEAK_GBS, "unit": "GB/s"},
@@ -130,7 +131,8 @@ def secondary(lrc, torch, dev):
     t = _time(lambda: lrc.lrc_score_components(left=left, right=right, A=a, B=b, mode="fisher"), torch, 3)
     flops = 2.0 * n * k * (d + d) + 3.0 * n * k
     out["fisher_scores"] = {"workload": f"{n} bf16 tokens, {d}x{d} matrix, {k} components", "ms": round(t * 1e3, 3),
-                            "TFLOP/s": round(flops / t / 1e12, 2)}
+                            "TFLOP/s": round(flops / t / 1e12, 2),
+                            "mfma_bf16_frac": round(flops / t / 1e12 / PEAK_TFLOPS["bf16"], 4)}
     del a, b, left, right
     for m_items, label in ((917504, "decoder stack: 224 matrices"), (64 * 1024 * 1024, "scaled pool")):
         n_mat = 224 if m_items == 917504 else 16384

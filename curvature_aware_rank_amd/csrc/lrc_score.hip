@@ -3,10 +3,18 @@
 //
 //   FISHER: s_i = 1/(2N) sum_t (b_t . left_i)^2 (a_t . right_i)^2
 //
-// A workgroup owns 64 tokens x 64 components: it forms both projections P = A Right^T and
-// Q = B Left for its tile in registers (LDS-staged operands), squares and multiplies
-// them, and sums its 64 tokens in a fixed order; a second pass adds the token-tile
-// partial sums in order (fp64), so the result is bit-reproducible.
+// Both projections P = A Right^T (N x k) and Q = B Left (N x k) are formed tile by tile
+// and never stored: a workgroup squares and multiplies its P and Q tiles and sums its
+// tokens in a fixed order; a second pass adds the token-tile partial sums in order
+// (fp64), so the result is bit-reproducible.
+//
+// bf16 activations (widths a multiple of 8) run on MFMA: each fp32 factor f is split into
+// bf16 parts f = hi + lo + r with hi = bf16(f), lo = bf16(f - hi), |r| <= 2^-16 |f|, and
+// a . f is taken as (a . hi) + (a . lo) with bf16 x bf16 products (exact) accumulated in
+// fp32.  A workgroup owns 256 tokens x 128 components; each of its four waves holds the
+// P and Q accumulators of 64 tokens x 128 components, reads its own activation rows
+// straight from memory into registers and shares the factor tile (hi and lo) through
+// LDS.  fp32 activations use a VALU kernel of 64 x 64 tiles.
 #include "lrc_internal.h"
 
 namespace lrc {
@@ -103,6 +111,193 @@ __global__ __launch_bounds__(256) void fisher_partial_kernel(const T* __restrict
   }
 }
 
+// ---------------------------------------------------------------------------------
+// MFMA path (bf16 activations)
+// ---------------------------------------------------------------------------------
+constexpr int FT = 256;      // tokens per workgroup (4 waves x 64)
+constexpr int FC = 128;      // components per workgroup
+constexpr int FK = 64;       // reduction chunk
+constexpr int FP = FK + 8;   // LDS row pitch of a factor tile (bf16): 144 B, conflict-free 16-B reads
+
+// hi/lo bf16 split of fp32 values, element-wise (row-major kept)
+__global__ void split_kernel(const float* __restrict__ F, int64_t total, uint16_t* __restrict__ hi,
+                             uint16_t* __restrict__ lo) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += int64_t(gridDim.x) * blockDim.x) {
+    const float f = F[i];
+    const uint16_t h = f32_to_bf16_bits(f);
+    hi[i] = h;
+    lo[i] = f32_to_bf16_bits(f - bf16_bits_to_f32(h));
+  }
+}
+
+// hi/lo bf16 split with a transpose: F is rows x cols, hi and lo are cols x rows
+__global__ __launch_bounds__(256) void split_transpose_kernel(const float* __restrict__ F, int rows, int cols,
+                                                              uint16_t* __restrict__ hi, uint16_t* __restrict__ lo) {
+  __shared__ float t[64][65];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    t[i][tx] = (r < rows && c < cols) ? F[int64_t(r) * cols + c] : 0.f;
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (c < cols && r < rows) {
+      const float f = t[tx][i];
+      const uint16_t h = f32_to_bf16_bits(f);
+      hi[int64_t(c) * rows + r] = h;
+      lo[int64_t(c) * rows + r] = f32_to_bf16_bits(f - bf16_bits_to_f32(h));
+    }
+  }
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// acc[f][nf] (32 tokens x 32 components each) += X[tokens, 0:d] . F[components, 0:d]^T
+// with F given as bf16 hi and lo parts (components x d, row-major).  X rows are this
+// wave's 64 tokens; the factor tile goes through LDS buffers fs (2 stages x hi/lo).
+__device__ __forceinline__ void fisher_phase(const uint16_t* __restrict__ X, int d, int64_t n, int64_t tw,
+                                             const uint16_t* __restrict__ Fh, const uint16_t* __restrict__ Fl,
+                                             int k, int c0, uint16_t* fs, f32x16 (&acc)[2][4]) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int lr = lane & 31, lh = lane >> 5;
+  const int nch = (d + FK - 1) / FK;
+  // activation addresses: row tw + f * 32 + lr (clamped), 16 B at column s * 16 + lh * 8
+  const uint16_t* xrow[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) xrow[f] = X + min<int64_t>(tw + f * 32 + lr, n - 1) * d;
+  auto load_a = [&](u32x4 (&a)[2][4], int kc) {
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int col = min(kc + s4 * 16 + lh * 8, d - 8);
+        a[f][s4] = *reinterpret_cast<const u32x4*>(xrow[f] + col);
+      }
+  };
+  // factor staging: thread takes 16-B groups g = tid + 256 q: row g / 8, column group g % 8
+  const int grow = tid >> 3, gcol = (tid & 7) * 8;
+  auto load_f = [&](u32x4 (&g)[2][4], int kc) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t row = min(c0 + grow + 32 * q, k - 1);
+      const int col = min(kc + gcol, d - 8);
+      g[0][q] = *reinterpret_cast<const u32x4*>(Fh + row * d + col);
+      g[1][q] = *reinterpret_cast<const u32x4*>(Fl + row * d + col);
+    }
+  };
+  auto store_f = [&](const u32x4 (&g)[2][4], int buf, int kc) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool ok = c0 + grow + 32 * q < k && kc + gcol < d;
+#pragma unroll
+      for (int hl = 0; hl < 2; ++hl)
+        *reinterpret_cast<u32x4*>(fs + (buf * 2 + hl) * (FC * FP) + (grow + 32 * q) * FP + gcol) = ok ? g[hl][q] : z;
+    }
+  };
+  // one chunk from LDS buffer buf; each 16-wide step's activation registers are refilled
+  // with the next chunk's (column nkc) as soon as the step's MFMAs have been issued
+  auto compute = [&](int buf, u32x4 (&a)[2][4], int nkc, bool next) {
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+#pragma unroll
+      for (int nf = 0; nf < 4; ++nf) {
+        const int off = (nf * 32 + lr) * FP + s4 * 16 + lh * 8;
+        const u32x4 fh = *reinterpret_cast<const u32x4*>(fs + (buf * 2 + 0) * (FC * FP) + off);
+        const u32x4 fl = *reinterpret_cast<const u32x4*>(fs + (buf * 2 + 1) * (FC * FP) + off);
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          acc[f][nf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[f][s4]), as_bf16x8(fh), acc[f][nf],
+                                                               0, 0, 0);
+          acc[f][nf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[f][s4]), as_bf16x8(fl), acc[f][nf],
+                                                               0, 0, 0);
+        }
+      }
+      if (next) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const int col = min(nkc + s4 * 16 + lh * 8, d - 8);
+          a[f][s4] = *reinterpret_cast<const u32x4*>(xrow[f] + col);
+        }
+      }
+    }
+  };
+  u32x4 g[2][4], a[2][4];
+  load_f(g, 0);
+  load_a(a, 0);
+  store_f(g, 0, 0);
+  if (nch > 1) load_f(g, FK);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int buf = c & 1;
+    compute(buf, a, (c + 1) * FK, c + 1 < nch);
+    if (c + 1 < nch) store_f(g, buf ^ 1, (c + 1) * FK);
+    if (c + 2 < nch) load_f(g, (c + 2) * FK);
+    __syncthreads();
+  }
+}
+
+// Workgroups are numbered so that the components tiles of one token tile share an XCD
+// (consecutive workgroup ids go to consecutive XCDs): the activation rows of a token
+// tile are then fetched into one L2 only.
+__global__ __launch_bounds__(256) void fisher_mfma_kernel(const uint16_t* __restrict__ A,
+                                                          const uint16_t* __restrict__ B, int64_t n, int d_in,
+                                                          int d_out, const uint16_t* __restrict__ Rh,
+                                                          const uint16_t* __restrict__ Rl,
+                                                          const uint16_t* __restrict__ Lh,
+                                                          const uint16_t* __restrict__ Ll, int k, int n_ct, int n_tt,
+                                                          float* __restrict__ partial) {
+  __shared__ __attribute__((aligned(16))) uint16_t fs[2 * 2 * FC * FP];
+  __shared__ float red[4][FC];
+  const int xcd = blockIdx.x & 7;
+  const int i = blockIdx.x >> 3;
+  const int ct = i % n_ct;
+  const int tt = (i / n_ct) * 8 + xcd;
+  if (tt >= n_tt) return;
+  const int c0 = ct * FC;
+  const int64_t t0 = int64_t(tt) * FT;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t tw = t0 + wave * 64;
+  f32x16 accp[2][4], accq[2][4];
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int nf = 0; nf < 4; ++nf)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        accp[f][nf][e] = 0.f;
+        accq[f][nf][e] = 0.f;
+      }
+  fisher_phase(A, d_in, n, tw, Rh, Rl, k, c0, fs, accp);
+  fisher_phase(B, d_out, n, tw, Lh, Ll, k, c0, fs, accq);
+  // output layout of a 32 x 32 block: lane l, element e -> token row 8 (e / 4) + 4 (l / 32) + e % 4,
+  // component column l % 32
+  const int lr = lane & 31, lh = lane >> 5;
+#pragma unroll
+  for (int nf = 0; nf < 4; ++nf) {
+    float sum = 0.f;
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t t = tw + f * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
+        const float pv = accp[f][nf][e], qv = accq[f][nf][e];
+        // rows past the last token hold a copy of it (clamped loads): they add exactly 0
+        sum = fmaf(t < n ? pv * pv : 0.f, qv * qv, sum);
+      }
+    sum += __shfl_xor(sum, 32);
+    if (lh == 0) red[wave][nf * 32 + lr] = sum;
+  }
+  __syncthreads();
+  if (tid < FC && c0 + tid < k)
+    partial[int64_t(tt) * k + c0 + tid] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+}
+
 __global__ void fisher_final_kernel(const float* __restrict__ partial, int ntb, int k, int accumulate, int finalize,
                                     double inv2n, float* __restrict__ scores) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -123,15 +318,39 @@ __global__ void kfac_kernel(const float* __restrict__ sigma, int k, float* __res
 
 using namespace lrc;
 
+namespace {
+// workspace of the MFMA path: token-tile partials, then the hi/lo parts of Right
+// (k x d_in) and of Left^T (k x d_out)
+struct FisherWs {
+  float* partial;
+  uint16_t *rh, *rl, *lh, *ll;
+};
+FisherWs carve_fisher_mfma(Carve& cv, int64_t n_tokens, int64_t d_in, int64_t d_out, int64_t k) {
+  FisherWs w;
+  w.partial = cv.take<float>(size_t(std::max<int64_t>(1, cdiv(n_tokens, FT)) * k));
+  w.rh = cv.take<uint16_t>(size_t(k * d_in));
+  w.rl = cv.take<uint16_t>(size_t(k * d_in));
+  w.lh = cv.take<uint16_t>(size_t(k * d_out));
+  w.ll = cv.take<uint16_t>(size_t(k * d_out));
+  return w;
+}
+// the MFMA kernel reads activation rows in 16-byte pieces
+bool fisher_use_mfma(lrc_dtype dt, const void* A, const void* B, int64_t d_in, int64_t d_out) {
+  return dt == LRC_BF16 && d_in % 8 == 0 && d_out % 8 == 0 && reinterpret_cast<uintptr_t>(A) % 16 == 0 &&
+         reinterpret_cast<uintptr_t>(B) % 16 == 0;
+}
+}  // namespace
+
 extern "C" size_t lrc_score_components_workspace(int64_t n_tokens, int64_t d_in, int64_t d_out, int64_t k,
                                                  uint32_t flags) {
-  (void)d_in;
-  (void)d_out;
-  if (n_tokens < 0 || k <= 0) return 0;
+  if (n_tokens < 0 || k <= 0 || d_in <= 0 || d_out <= 0) return 0;
   if (!(flags & LRC_SCORE_FISHER)) return 0;
-  Carve cv(nullptr);
-  cv.take<float>(size_t(cdiv(n_tokens, ST) * k));
-  return cv.bytes();
+  // enough for either kernel (the activation type is not known here)
+  Carve valu(nullptr);
+  valu.take<float>(size_t(cdiv(n_tokens, ST) * k));
+  Carve mfma(nullptr);
+  carve_fisher_mfma(mfma, n_tokens, d_in, d_out, k);
+  return std::max(valu.bytes(), mfma.bytes());
 }
 
 extern "C" lrc_status lrc_score_components(const void* A, const void* B, lrc_dtype dt, int64_t n_tokens, int64_t d_in,
@@ -156,6 +375,40 @@ extern "C" lrc_status lrc_score_components(const void* A, const void* B, lrc_dty
   if (n_tokens > (int64_t(65535) * ST)) return LRC_EINVAL;  // one chunk per call at most 4M tokens
   const size_t need = lrc_score_components_workspace(n_tokens, d_in, d_out, k, flags);
   if (need > 0 && (ws == nullptr || ws_bytes < need)) return LRC_EWORKSPACE;
+  const double inv2n = finalize ? 1.0 / (2.0 * double(n_total)) : 1.0;
+  if (fisher_use_mfma(dt, A, B, d_in, d_out)) {
+    Carve cv(ws);
+    const FisherWs w = carve_fisher_mfma(cv, n_tokens, d_in, d_out, k);
+    const int n_tt = int(cdiv(n_tokens, FT));
+    if (n_tt > 0) {
+      {
+        const int64_t tot = k * d_in;
+        split_kernel<<<unsigned(std::min<int64_t>(cdiv(tot, 256), 8192)), 256, 0, st>>>(right, tot, w.rh, w.rl);
+        LRC_LAUNCHED();
+        const dim3 g(unsigned(cdiv(k, 64)), unsigned(cdiv(d_out, 64)));
+        split_transpose_kernel<<<g, 256, 0, st>>>(left, int(d_out), int(k), w.lh, w.ll);
+        LRC_LAUNCHED();
+      }
+      const int n_ct = int(cdiv(k, FC));
+      const int64_t nblk = int64_t(n_ct) * cdiv(n_tt, 8) * 8;
+      if (nblk > (int64_t(1) << 31) - 1) return LRC_EINVAL;
+      // algorithmic work as for the VALU kernel below; the bytes count the bf16 hi/lo
+      // factor copies this kernel reads
+      ProfScope scope("fisher_mfma_kernel", st,
+                      2.0 * double(n_tokens) * double(k) * double(d_in + d_out) + 3.0 * double(n_tokens) * double(k),
+                      2.0 * double(n_tokens) * double(d_in + d_out) + 4.0 * double(k) * double(d_in + d_out) +
+                          4.0 * double(n_tt) * double(k));
+      fisher_mfma_kernel<<<unsigned(nblk), 256, 0, st>>>(static_cast<const uint16_t*>(A),
+                                                         static_cast<const uint16_t*>(B), n_tokens, int(d_in),
+                                                         int(d_out), w.rh, w.rl, w.lh, w.ll, int(k), n_ct, n_tt,
+                                                         w.partial);
+      LRC_LAUNCHED();
+    }
+    fisher_final_kernel<<<unsigned(cdiv(k, 256)), 256, 0, st>>>(w.partial, n_tt, int(k), accumulate, finalize, inv2n,
+                                                                 scores);
+    LRC_LAUNCHED();
+    return LRC_OK;
+  }
   float* partial = static_cast<float*>(ws);
   const int ntb = int(cdiv(n_tokens, ST));
   if (ntb > 0) {
@@ -177,7 +430,6 @@ extern "C" lrc_status lrc_score_components(const void* A, const void* B, lrc_dty
                                                          n_tokens, int(d_in), int(d_out), left, right, int(k), partial);
     LRC_LAUNCHED();
   }
-  const double inv2n = finalize ? 1.0 / (2.0 * double(n_total)) : 1.0;
   fisher_final_kernel<<<unsigned(cdiv(k, 256)), 256, 0, st>>>(partial, ntb, int(k), accumulate, finalize, inv2n,
                                                                scores);
   LRC_LAUNCHED();
