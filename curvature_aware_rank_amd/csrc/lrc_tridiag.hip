@@ -777,14 +777,41 @@ __global__ __launch_bounds__(64) void tri_inviter_kernel(const double* __restric
         ustep(k1, z[int64_t(k1) * nc], r0[o], u1[o], u2[o]);
       }
       // ---- orthogonalise against the cluster's earlier (unit) vectors
+      // (loads in batches of IB, all in flight together; sums in element order)
       for (int p = 0; p < q; ++p) {
         const double* zp = Z + (j + p);
         double dot = 0.0;
-        for (int kk = 0; kk < n; ++kk) dot += zp[int64_t(kk) * nc] * z[int64_t(kk) * nc];
+        int kb = 0;
+        for (; kb + IB <= n; kb += IB) {
+          double ta[IB], tb[IB];
+#pragma unroll
+          for (int u = 0; u < IB; ++u) {
+            ta[u] = zp[int64_t(kb + u) * nc];
+            tb[u] = z[int64_t(kb + u) * nc];
+          }
+#pragma unroll
+          for (int u = 0; u < IB; ++u) dot += ta[u] * tb[u];
+        }
+        for (; kb < n; ++kb) dot += zp[int64_t(kb) * nc] * z[int64_t(kb) * nc];
         nrm2 = 0.0;
-        for (int kk = 0; kk < n; ++kk) {
-          const double zk = z[int64_t(kk) * nc] - dot * zp[int64_t(kk) * nc];
-          z[int64_t(kk) * nc] = zk;
+        kb = 0;
+        for (; kb + IB <= n; kb += IB) {
+          double ta[IB], tb[IB];
+#pragma unroll
+          for (int u = 0; u < IB; ++u) {
+            ta[u] = zp[int64_t(kb + u) * nc];
+            tb[u] = z[int64_t(kb + u) * nc];
+          }
+#pragma unroll
+          for (int u = 0; u < IB; ++u) {
+            const double zk = tb[u] - dot * ta[u];
+            z[int64_t(kb + u) * nc] = zk;
+            nrm2 += zk * zk;
+          }
+        }
+        for (; kb < n; ++kb) {
+          const double zk = z[int64_t(kb) * nc] - dot * zp[int64_t(kb) * nc];
+          z[int64_t(kb) * nc] = zk;
           nrm2 += zk * zk;
         }
       }
