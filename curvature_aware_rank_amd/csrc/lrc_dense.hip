@@ -97,11 +97,18 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(unsigned flags, int m, in
 // fp64 Gram from an fp32 matrix (products exact in fp64): G = M M^T or M^T M, lower
 // triangle only.  64 x 64 tiles, 256 threads with 4 x 4 outputs each.
 // ---------------------------------------------------------------------------------
+// Gram in fp64 on MFMA (v_mfma_f64_16x16x4): one 64 x 64 lower tile per workgroup, four
+// waves of 32 x 32 (2 x 2 MFMA blocks).  fp32 inputs are widened exactly; products of two
+// fp32 values are exact in fp64, sums are fp64.  The reduction runs in chunks of GRK
+// staged through LDS as doubles; the next chunk's loads are in flight during the MFMAs.
+constexpr int GRK = 32;
+constexpr int GRP = 64 + 2;   // LDS pitch (doubles) of a k row
+
 __global__ __launch_bounds__(256) void gram_f64_kernel(bool rows, int p, int q, const float* __restrict__ M,
                                                        int64_t ldm, int64_t sM, double* __restrict__ G,
                                                        int64_t ldg, int64_t sG) {
-  __shared__ double xs[16][65];
-  __shared__ double ys[16][65];
+  __shared__ double xs[GRK][GRP];
+  __shared__ double ys[GRK][GRP];
   M += blockIdx.z * sM;
   G += blockIdx.z * sG;
   int lin = blockIdx.x, ti = 0;
@@ -110,47 +117,74 @@ __global__ __launch_bounds__(256) void gram_f64_kernel(bool rows, int p, int q, 
   const int dim = rows ? p : q;     // Gram dimension
   const int red = rows ? q : p;     // reduction length
   if (ti * 64 >= dim) return;
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  double acc[4][4] = {};
-  for (int k0 = 0; k0 < red; k0 += 16) {
-    for (int e = threadIdx.x; e < 16 * 64; e += 256) {
-      int kk, c;
-      if (rows) { c = e >> 4; kk = e & 15; } else { kk = e >> 6; c = e & 63; }
-      const int gk = k0 + kk;
-      const int ci = ti * 64 + c, cj = tj * 64 + c;
-      double vi = 0.0, vj = 0.0;
-      if (gk < red) {
-        if (rows) {
-          if (ci < dim) vi = M[int64_t(ci) * ldm + gk];
-          if (cj < dim) vj = M[int64_t(cj) * ldm + gk];
-        } else {
-          if (ci < dim) vi = M[int64_t(gk) * ldm + ci];
-          if (cj < dim) vj = M[int64_t(gk) * ldm + cj];
-        }
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave >> 1, wc = wave & 1;
+  // staging: 8 elements per thread per operand.  rows: element (c, kk) at M[c * ldm + k];
+  // thread takes c = tid / 4 (0..63), kk = (tid % 4) * 8 + u.  cols: element at
+  // M[k * ldm + c]; thread takes kk = tid / 64 + 4 u, c = tid % 64.
+  float gx[8], gy[8];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      int c, kk;
+      if (rows) { c = tid >> 2; kk = (tid & 3) * 8 + u; } else { kk = (tid >> 6) + 4 * u; c = tid & 63; }
+      const int gk = min(k0 + kk, red - 1);
+      const int ci = min(ti * 64 + c, dim - 1), cj = min(tj * 64 + c, dim - 1);
+      if (rows) {
+        gx[u] = M[int64_t(ci) * ldm + gk];
+        gy[u] = M[int64_t(cj) * ldm + gk];
+      } else {
+        gx[u] = M[int64_t(gk) * ldm + ci];
+        gy[u] = M[int64_t(gk) * ldm + cj];
       }
-      xs[kk][c] = vi;
-      ys[kk][c] = vj;
     }
-    __syncthreads();
+  };
+  auto store = [&](int k0) {
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      double xv[4], yv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { xv[i] = xs[kk][ty * 4 + i]; yv[i] = ys[kk][tx * 4 + i]; }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma(xv[i], yv[j], acc[i][j]);
+    for (int u = 0; u < 8; ++u) {
+      int c, kk;
+      if (rows) { c = tid >> 2; kk = (tid & 3) * 8 + u; } else { kk = (tid >> 6) + 4 * u; c = tid & 63; }
+      const bool okk = k0 + kk < red;
+      xs[kk][c] = (okk && ti * 64 + c < dim) ? double(gx[u]) : 0.0;
+      ys[kk][c] = (okk && tj * 64 + c < dim) ? double(gy[u]) : 0.0;
     }
+  };
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+  const int l16 = lane & 15, lq = lane >> 4;
+  load(0);
+  for (int k0 = 0; k0 < red; k0 += GRK) {
     __syncthreads();
+    store(k0);
+    __syncthreads();
+    if (k0 + GRK < red) load(k0 + GRK);
+#pragma unroll
+    for (int kk = 0; kk < GRK; kk += 4) {
+      double a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) a[i] = xs[kk + lq][wr * 32 + i * 16 + l16];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = ys[kk + lq][wc * 32 + j * 16 + l16];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
   }
+  // output of an fp64 16 x 16 block: lane l, element e -> row l / 16 + 4 e, column l % 16
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = ti * 64 + ty * 4 + i, c = tj * 64 + tx * 4 + j;
-      if (r < dim && c < dim && r >= c) G[int64_t(r) * ldg + c] = acc[i][j];
-    }
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = ti * 64 + wr * 32 + i * 16 + lq + 4 * e, c = tj * 64 + wc * 32 + j * 16 + l16;
+        if (r < dim && c < dim && r >= c) G[int64_t(r) * ldg + c] = acc[i][j][e];
+      }
 }
 
 // ---------------------------------------------------------------------------------
