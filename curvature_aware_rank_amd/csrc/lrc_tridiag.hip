@@ -462,53 +462,87 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
 }
 
 // ---- 1d. trailing rank-2 panel update, lower tiles of rows/cols j1 .. n-1:
-// C -= V W^T + W V^T  (V rows in C's panel columns i0 .. i0+pb-1)
+// C -= V W^T + W V^T  (V rows in C's panel columns i0 .. i0+pb-1), as one product of
+// K = 2 NB on fp64 MFMA: [V_r | W_r] [W_c | V_c]^T.  One 64 x 64 tile per workgroup, four
+// waves of 32 x 32; the tile's old values are loaded at the start, with the operands.
+constexpr int SYP = 64 + 2;   // LDS pitch (doubles) of an operand k row
+
 __global__ __launch_bounds__(256) void tri_syr2k_kernel(double* __restrict__ A, int64_t lda, int n, int i0, int pb,
                                                         int j1, const double* __restrict__ Wp) {
-  __shared__ double Vr[TS][NB + 1], Wr[TS][NB + 1], Vc[TS][NB + 1], Wc[TS][NB + 1];
-  const int tid = threadIdx.x;
+  __shared__ double opa[2 * NB][SYP], opb[2 * NB][SYP];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave >> 1, wc = wave & 1;
+  const int l16 = lane & 15, lq = lane >> 4;
   int b, c;
   tile_of(blockIdx.x, b, c);
   const int R0 = j1 + b * TS, C0 = j1 + c * TS;
-  for (int q = tid; q < TS * NB; q += 256) {
-    const int x = q / NB, t = q % NB;
-    const int r = R0 + x, cc = C0 + x;
-    const bool tr = t < pb;
-    Vr[x][t] = (tr && r < n) ? A[int64_t(r) * lda + i0 + t] : 0.0;
-    Wr[x][t] = (tr && r < n) ? Wp[int64_t(r) * NB + t] : 0.0;
-    Vc[x][t] = (tr && cc < n) ? A[int64_t(cc) * lda + i0 + t] : 0.0;
-    Wc[x][t] = (tr && cc < n) ? Wp[int64_t(cc) * NB + t] : 0.0;
+  // old tile values this thread updates (fp64 16 x 16 output: lane l, element e -> row
+  // l / 16 + 4 e, column l % 16)
+  double old[2][2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = min(R0 + wr * 32 + i * 16 + lq + 4 * e, n - 1);
+        const int cc = min(C0 + wc * 32 + j * 16 + l16, n - 1);
+        old[i][j][e] = A[int64_t(r) * lda + cc];
+      }
+  // operands: thread takes row x = tid / 4 and panel columns (tid % 4) * 8 .. + 7
+  const int x = tid >> 2, t0 = (tid & 3) * 8;
+  double vr[8], wr8[8], vc[8], wc8[8];
+  {
+    const int r = min(R0 + x, n - 1), cc = min(C0 + x, n - 1);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int tc = min(t0 + u, pb - 1);   // panel columns past pb are masked below
+      vr[u] = A[int64_t(r) * lda + i0 + tc];
+      wr8[u] = Wp[int64_t(r) * NB + tc];
+      vc[u] = A[int64_t(cc) * lda + i0 + tc];
+      wc8[u] = Wp[int64_t(cc) * NB + tc];
+    }
+  }
+  {
+    const bool okr = R0 + x < n, okc = C0 + x < n;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool okt = t0 + u < pb;
+      opa[t0 + u][x] = okr && okt ? vr[u] : 0.0;        // k < NB: V_r
+      opa[NB + t0 + u][x] = okr && okt ? wr8[u] : 0.0;  // k >= NB: W_r
+      opb[t0 + u][x] = okc && okt ? wc8[u] : 0.0;       // k < NB: W_c
+      opb[NB + t0 + u][x] = okc && okt ? vc[u] : 0.0;   // k >= NB: V_c
+    }
   }
   __syncthreads();
-  const int ty = tid >> 4, tx = tid & 15;
-  double acc[4][4];
+  f64x4 acc[2][2];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[a][q] = 0.0;
-  for (int t = 0; t < NB; ++t) {
-    double vr[4], wr[4], vc[4], wc[4];
+    for (int j = 0; j < 2; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      vr[a] = Vr[ty * 4 + a][t];
-      wr[a] = Wr[ty * 4 + a][t];
-      vc[a] = Vc[tx * 4 + a][t];
-      wc[a] = Wc[tx * 4 + a][t];
-    }
+  for (int kk = 0; kk < 2 * NB; kk += 4) {
+    double a[2], bb[2];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int i = 0; i < 2; ++i) a[i] = opa[kk + lq][wr * 32 + i * 16 + l16];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[a][q] += vr[a] * wc[q] + wr[a] * vc[q];
+    for (int j = 0; j < 2; ++j) bb[j] = opb[kk + lq][wc * 32 + j * 16 + l16];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], bb[j], acc[i][j], 0, 0, 0);
   }
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int lr = ty * 4 + a, r = R0 + lr;
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int lc = tx * 4 + q, cc = C0 + lc;
-      if (r < n && cc < n && (b != c || lr >= lc)) A[int64_t(r) * lda + cc] -= acc[a][q];
-    }
-  }
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int lr = wr * 32 + i * 16 + lq + 4 * e, lc = wc * 32 + j * 16 + l16;
+        const int r = R0 + lr, cc = C0 + lc;
+        if (r < n && cc < n && (b != c || lr >= lc)) A[int64_t(r) * lda + cc] = old[i][j][e] - acc[i][j][e];
+      }
 }
 
 // ---- 2. eigenvalues of T
