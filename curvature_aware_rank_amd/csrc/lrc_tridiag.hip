@@ -954,54 +954,79 @@ __global__ __launch_bounds__(BW) void bt_t_kernel(const double* __restrict__ Gp,
 }
 
 // Yp[ch][a][c] = sum over the chunk's rows of V[r][a] Z[r][c]   (64 columns per workgroup)
+// on fp64 MFMA: four waves of 32 reflectors x 64 columns, rows staged 32 at a time through
+// LDS (the next rows' loads in flight during the MFMAs)
+constexpr int BVP = BW + 2;   // LDS pitch of the staged reflector rows
+constexpr int BZP = 64 + 2;   // LDS pitch of the staged Z rows
+
 __global__ __launch_bounds__(256) void bt_vtz_kernel(const double* __restrict__ A, int64_t lda, int n, int nref,
                                                      int g0, const double* __restrict__ Z, int ncols,
                                                      double* __restrict__ Yp) {
-  __shared__ double sv[32][BW + 1];
-  __shared__ double sz[32][64 + 1];
-  const int tid = threadIdx.x;
+  __shared__ double sv[32][BVP];
+  __shared__ double sz[32][BZP];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, lq = lane >> 4;
   const int c0 = blockIdx.x * 64, ch = blockIdx.y;
   const int rbase = g0 + 1 + ch * BT_CHUNK;
   const int rend = min(n, rbase + BT_CHUNK);
-  const int ty = tid >> 4, tx = tid & 15;   // outputs a = ty*8 .. +7, c = tx*4 .. +3
-  double acc[8][4];
+  // staging: V element (row x, reflector t) with x = tid / 8 .. (4 rows apart? no: one row),
+  // t = (tid % 8) * 16 + u; Z element (row x, column cc) with x = tid / 8, cc = (tid % 8) * 8 + u
+  const int sx = tid >> 3, st16 = (tid & 7) * 16, sc8 = (tid & 7) * 8;
+  double gv[16], gz[8];
+  auto load = [&](int rb) {
+    const int r = min(rb + sx, n - 1);
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
+    for (int u = 0; u < 16; ++u) gv[u] = A[int64_t(r) * lda + min(g0 + st16 + u, nref - 1)];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[a][q] = 0.0;
+    for (int u = 0; u < 8; ++u) gz[u] = Z[int64_t(r) * ncols + min(c0 + sc8 + u, ncols - 1)];
+  };
+  auto store = [&](int rb) {
+    const int r = rb + sx;
+    const bool okr = r < rend;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int t = st16 + u;
+      sv[sx][t] = (okr && g0 + t < nref && r > g0 + t) ? gv[u] : 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sz[sx][sc8 + u] = (okr && c0 + sc8 + u < ncols) ? gz[u] : 0.0;
+  };
+  f64x4 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+  load(rbase);
   for (int rb = rbase; rb < rend; rb += 32) {
     __syncthreads();
-    for (int q = tid; q < 32 * BW; q += 256) {
-      const int x = q / BW, t = q % BW;
-      const int r = rb + x;
-      sv[x][t] = r < rend ? refl(A, lda, nref, g0, r, t) : 0.0;
-    }
-    for (int q = tid; q < 32 * 64; q += 256) {
-      const int x = q / 64, cc = q % 64;
-      const int r = rb + x;
-      sz[x][cc] = (r < rend && c0 + cc < ncols) ? Z[int64_t(r) * ncols + c0 + cc] : 0.0;
-    }
+    store(rb);
     __syncthreads();
-    for (int x = 0; x < 32; ++x) {
-      double a8[8], z4[4];
+    if (rb + 32 < rend) load(rb + 32);
 #pragma unroll
-      for (int a = 0; a < 8; ++a) a8[a] = sv[x][ty * 8 + a];
+    for (int kk = 0; kk < 32; kk += 4) {
+      double a[2], b[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) z4[q] = sz[x][tx * 4 + q];
+      for (int i = 0; i < 2; ++i) a[i] = sv[kk + lq][wave * 32 + i * 16 + l16];
 #pragma unroll
-      for (int a = 0; a < 8; ++a)
+      for (int j = 0; j < 4; ++j) b[j] = sz[kk + lq][j * 16 + l16];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[a][q] += a8[a] * z4[q];
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
     }
   }
+  // fp64 16 x 16 output: lane l, element e -> row l / 16 + 4 e, column l % 16
   double* out = Yp + int64_t(ch) * BW * ncols;
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int cc = c0 + tx * 4 + q;
-      if (cc < ncols) out[int64_t(ty * 8 + a) * ncols + cc] = acc[a][q];
-    }
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int a = wave * 32 + i * 16 + lq + 4 * e, cc = c0 + j * 16 + l16;
+        if (cc < ncols) out[int64_t(a) * ncols + cc] = acc[i][j][e];
+      }
 }
 
 // Y[a][c] = sum_ch Yp[ch][a][c]  (one element per thread, partials in order)
@@ -1047,54 +1072,86 @@ __global__ __launch_bounds__(256) void bt_ty_kernel(const double* __restrict__ Y
   }
 }
 
-// Z[r][c] -= sum_a V[r][a] Y2[a][c]   (64 x 64 tile of rows g0+1.. per workgroup)
+// Z[r][c] -= sum_a V[r][a] Y2[a][c]   (64 x 64 tile of rows g0+1.. per workgroup) on fp64
+// MFMA: four waves of 32 x 32, reflectors staged 32 at a time; the tile's old Z values are
+// loaded at the start
+constexpr int BUP = 32 + 1;   // LDS pitch of the staged V rows (odd: column reads spread over banks)
+
 __global__ __launch_bounds__(256) void bt_update_kernel(const double* __restrict__ A, int64_t lda, int n, int nref,
                                                         int g0, const double* __restrict__ Y2, int ncols,
                                                         double* __restrict__ Z) {
-  __shared__ double sv[64][32 + 1];
-  __shared__ double sy[32][64 + 1];
-  const int tid = threadIdx.x;
+  __shared__ double sv[64][BUP];
+  __shared__ double sy[32][BZP];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave >> 1, wc = wave & 1;
+  const int l16 = lane & 15, lq = lane >> 4;
   const int r0 = g0 + 1 + blockIdx.x * 64, c0 = blockIdx.y * 64;
-  const int ty = tid >> 4, tx = tid & 15;   // rows ty*4.., cols tx*4..
-  double acc[4][4];
+  double old[2][2][4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[a][q] = 0.0;
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = min(r0 + wr * 32 + i * 16 + lq + 4 * e, n - 1);
+        const int cc = min(c0 + wc * 32 + j * 16 + l16, ncols - 1);
+        old[i][j][e] = Z[int64_t(r) * ncols + cc];
+      }
+  // staging: V (row x = tid / 4, reflectors k0 + (tid % 4) * 8 + u), Y2 (reflector row
+  // t = tid / 8, columns (tid % 8) * 8 + u)
+  const int vx = tid >> 2, vt = (tid & 3) * 8, yt = tid >> 3, yc = (tid & 7) * 8;
+  double gv[8], gy[8];
+  auto load = [&](int k0) {
+    const int r = min(r0 + vx, n - 1);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) gv[u] = A[int64_t(r) * lda + min(g0 + k0 + vt + u, nref - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) gy[u] = Y2[int64_t(k0 + yt) * ncols + min(c0 + yc + u, ncols - 1)];
+  };
+  auto store = [&](int k0) {
+    const int r = r0 + vx;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int t = k0 + vt + u;
+      sv[vx][vt + u] = (r < n && g0 + t < nref && r > g0 + t) ? gv[u] : 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sy[yt][yc + u] = c0 + yc + u < ncols ? gy[u] : 0.0;
+  };
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+  load(0);
   for (int k0 = 0; k0 < BW; k0 += 32) {
     __syncthreads();
-    for (int q = tid; q < 64 * 32; q += 256) {
-      const int x = q / 32, t = q % 32;
-      const int r = r0 + x;
-      sv[x][t] = r < n ? refl(A, lda, nref, g0, r, k0 + t) : 0.0;
-    }
-    for (int q = tid; q < 32 * 64; q += 256) {
-      const int t = q / 64, cc = q % 64;
-      sy[t][cc] = c0 + cc < ncols ? Y2[int64_t(k0 + t) * ncols + c0 + cc] : 0.0;
-    }
+    store(k0);
     __syncthreads();
-    for (int t = 0; t < 32; ++t) {
-      double v4[4], y4[4];
+    if (k0 + 32 < BW) load(k0 + 32);
 #pragma unroll
-      for (int a = 0; a < 4; ++a) v4[a] = sv[ty * 4 + a][t];
+    for (int kk = 0; kk < 32; kk += 4) {
+      double a[2], b[2];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) y4[q] = sy[t][tx * 4 + q];
+      for (int i = 0; i < 2; ++i) a[i] = sv[wr * 32 + i * 16 + l16][kk + lq];
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int j = 0; j < 2; ++j) b[j] = sy[kk + lq][wc * 32 + j * 16 + l16];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[a][q] += v4[a] * y4[q];
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
     }
   }
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int r = r0 + ty * 4 + a;
-    if (r >= n) continue;
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int cc = c0 + tx * 4 + q;
-      if (cc < ncols) Z[int64_t(r) * ncols + cc] -= acc[a][q];
-    }
-  }
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = r0 + wr * 32 + i * 16 + lq + 4 * e, cc = c0 + wc * 32 + j * 16 + l16;
+        if (r < n && cc < ncols) Z[int64_t(r) * ncols + cc] = old[i][j][e] - acc[i][j][e];
+      }
 }
 
 // ---- outputs: sigma (all k, descending) and Qt rows = eigenvectors, sign-fixed, fp32
