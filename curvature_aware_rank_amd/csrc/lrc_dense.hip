@@ -9,13 +9,17 @@ namespace {
 
 // ---------------------------------------------------------------------------------
 // fp32 GEMM: 64 x 64 output tile per workgroup, 4 waves in 2 x 2, each wave a 32 x 32
-// block as 2 x 2 v_mfma_f32_16x16x4f32 blocks.  Operands are staged k-major in LDS so
-// a lane reads its fragment element with one conflict-free 4-byte read.
+// block as 2 x 2 v_mfma_f32_16x16x4f32 blocks.  Operands are staged k-major in LDS in
+// chunks of GK (a lane reads its fragment element with one 4-byte read); the next
+// chunk's global loads (clamped addresses, masked when stored) are in flight while the
+// current chunk's MFMAs run.
 // Fragment layout (16x16x4): A[row = l%16][k = l/16], B[k = l/16][col = l%16],
 // D element r of lane l = D[4*(l/16) + r][l%16].
 // ---------------------------------------------------------------------------------
 constexpr int GT = 64;
-constexpr int GK = 16;
+constexpr int GK = 32;
+constexpr int GPE = (GT * GK) / 256;   // staged elements per thread per operand
+constexpr int WT = GT / 32;            // 16 x 16 blocks per wave side
 
 __global__ __launch_bounds__(256) void gemm_f32_kernel(unsigned flags, int m, int n, int k, float alpha,
                                                        const float* __restrict__ A, int64_t lda, int64_t sA,
@@ -35,51 +39,71 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(unsigned flags, int m, in
   if (flags & GEMM_K_TO_ROW) ke = min(ke, row0 + GT);
   kb = (kb / GK) * GK;
   const bool ta = flags & GEMM_TA, tb = flags & GEMM_TB;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave >> 1, wc = wave & 1;
-  f32x4 acc[2][2];
+  f32x4 acc[WT][WT];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < WT; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int k0 = kb; k0 < ke; k0 += GK) {
+    for (int j = 0; j < WT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // staged element e = tid + 256 it: (row r, kk) of A and (kk, column c) of B, with the
+  // index order that makes consecutive threads read consecutive addresses
+  auto a_rk = [&](int e, int& r, int& kk) {
+    if (ta) { kk = e / GT; r = e % GT; } else { r = e / GK; kk = e % GK; }
+  };
+  auto b_kc = [&](int e, int& kk, int& c) {
+    if (tb) { c = e / GK; kk = e % GK; } else { kk = e / GT; c = e % GT; }
+  };
+  float ga[GPE], gb[GPE];
+  auto load = [&](int k0) {
 #pragma unroll
-    for (int it = 0; it < (GT * GK) / 256; ++it) {
+    for (int it = 0; it < GPE; ++it) {
       const int e = tid + it * 256;
-      int r, kk;
-      if (ta) { kk = e / GT; r = e % GT; } else { r = e / GK; kk = e % GK; }
-      const int gr = row0 + r, gk = k0 + kk;
-      float v = 0.f;
-      if (gr < m && gk < ke) v = ta ? A[int64_t(gk) * lda + gr] : A[int64_t(gr) * lda + gk];
-      As[kk][r] = v;
-      int c;
-      if (tb) { c = e / GK; kk = e % GK; } else { kk = e / GT; c = e % GT; }
-      const int gc = col0 + c, gk2 = k0 + kk;
-      float w = 0.f;
-      if (gc < n && gk2 < ke) w = tb ? B[int64_t(gc) * ldb + gk2] : B[int64_t(gk2) * ldb + gc];
-      Bs[kk][c] = w;
+      int r, kk, c, kk2;
+      a_rk(e, r, kk);
+      b_kc(e, kk2, c);
+      const int gr = min(row0 + r, m - 1), gk = min(k0 + kk, k - 1);
+      const int gc = min(col0 + c, n - 1), gk2 = min(k0 + kk2, k - 1);
+      ga[it] = ta ? A[int64_t(gk) * lda + gr] : A[int64_t(gr) * lda + gk];
+      gb[it] = tb ? B[int64_t(gc) * ldb + gk2] : B[int64_t(gk2) * ldb + gc];
     }
+  };
+  auto store = [&](int k0) {
+#pragma unroll
+    for (int it = 0; it < GPE; ++it) {
+      const int e = tid + it * 256;
+      int r, kk, c, kk2;
+      a_rk(e, r, kk);
+      b_kc(e, kk2, c);
+      As[kk][r] = (row0 + r < m && k0 + kk < ke) ? ga[it] : 0.f;
+      Bs[kk2][c] = (col0 + c < n && k0 + kk2 < ke) ? gb[it] : 0.f;
+    }
+  };
+  if (kb < ke) load(kb);
+  for (int k0 = kb; k0 < ke; k0 += GK) {
     __syncthreads();
+    store(k0);
+    __syncthreads();
+    if (k0 + GK < ke) load(k0 + GK);
 #pragma unroll
     for (int kq = 0; kq < GK; kq += 4) {
-      float a[2], b[2];
+      float a[WT], b[WT];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = As[kq + (lane >> 4)][wr * 32 + i * 16 + (lane & 15)];
+      for (int i = 0; i < WT; ++i) a[i] = As[kq + (lane >> 4)][wr * 32 + i * 16 + (lane & 15)];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = Bs[kq + (lane >> 4)][wc * 32 + j * 16 + (lane & 15)];
+      for (int j = 0; j < WT; ++j) b[j] = Bs[kq + (lane >> 4)][wc * 32 + j * 16 + (lane & 15)];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < WT; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < WT; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    __syncthreads();
   }
   const bool lower = flags & GEMM_LOWER, mirror = flags & GEMM_MIRROR;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < WT; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < WT; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = row0 + wr * 32 + i * 16 + 4 * (lane >> 4) + r;
