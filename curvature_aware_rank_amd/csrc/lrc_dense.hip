@@ -251,7 +251,7 @@ __global__ __launch_bounds__(64) void potf2_kernel(float* __restrict__ L, int64_
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     if (j < b && fail == 0) {
-      const float piv = __shfl(a[j], j);
+      const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[j]), j));
       if (!(piv > 0.f) || !isfinite(piv)) {
         fail = j + 1;
       } else {
