@@ -236,7 +236,6 @@ constexpr int NB = 64;  // Cholesky / triangular-solve block size
 // LDS to every lane, and each lane updates its own row.
 __global__ __launch_bounds__(64) void potf2_kernel(float* __restrict__ L, int64_t ldl, int64_t n, int64_t k0,
                                                    int* __restrict__ info) {
-  __shared__ float col[NB];
   const int lane = threadIdx.x;
   const int b = int(min<int64_t>(NB, n - k0));
   if (*info != 0) return;
@@ -246,8 +245,10 @@ __global__ __launch_bounds__(64) void potf2_kernel(float* __restrict__ L, int64_
   for (int c = 0; c < NB; ++c) a[c] = L[(k0 + rr) * ldl + k0 + min(c, b - 1)];
 #pragma unroll
   for (int c = 0; c < NB; ++c) a[c] = (c <= lane && lane < b && c < b) ? a[c] : 0.f;
-  int fail = 0;   // uniform: the pivot is broadcast from lane j
-  // fully unrolled (static register indices); finished or failed columns are skipped
+  int fail = 0;   // uniform: the pivot is read from lane j into a scalar register
+  // fully unrolled (static register indices); finished or failed columns are skipped.
+  // Column j's multipliers l_c (lane c's a[j]) reach the other lanes by readlane, so no
+  // LDS round trip or barrier separates consecutive columns.
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     if (j < b && fail == 0) {
@@ -258,12 +259,12 @@ __global__ __launch_bounds__(64) void potf2_kernel(float* __restrict__ L, int64_
         const float djj = sqrtf(piv);
         const float inv = 1.0f / djj;
         a[j] = lane == j ? djj : (lane > j ? a[j] * inv : a[j]);
-        col[lane] = a[j];
-        __syncthreads();
         const float lij = a[j];
 #pragma unroll
-        for (int c = j + 1; c < NB; ++c) a[c] = (c <= lane) ? fmaf(-lij, col[c], a[c]) : a[c];
-        __syncthreads();
+        for (int c = j + 1; c < NB; ++c) {
+          const float lc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[j]), c));
+          a[c] = (c <= lane) ? fmaf(-lij, lc, a[c]) : a[c];
+        }
       }
     }
   }

@@ -925,32 +925,40 @@ __global__ __launch_bounds__(256) void bt_gram_kernel(const double* __restrict__
 }
 
 // T of block g (upper triangular): T[j][j] = tau_j, T[0:j, j] = -tau_j T[0:j,0:j] G[0:j, j];
-// thread i owns row i of T (it alone writes and reads it)
+// thread i owns row i of T, kept in LDS.  G = V^T V is symmetric, so its column j is
+// row j (one coalesced load per column, the next column's load in flight).
 __global__ __launch_bounds__(BW) void bt_t_kernel(const double* __restrict__ Gp, int ngc, int nref,
                                                   const double* __restrict__ tau, double* __restrict__ Tm) {
-  __shared__ double G[BW][BW + 1];
+  __shared__ double Ts[BW][BW + 1];
+  __shared__ double gcol[2][BW];
   const int tid = threadIdx.x;
   const int g = blockIdx.x, g0 = g * BW;
-  for (int q = tid; q < BW * BW; q += BW) {
+  // column j of G (entries 0..j-1 used), summed over the row chunks in chunk order
+  auto load_col = [&](int j) {
     double s = 0.0;
-    for (int ch = 0; ch < ngc; ++ch) s += Gp[(int64_t(g) * ngc + ch) * BW * BW + q];
-    G[q / BW][q % BW] = s;
-  }
-  __syncthreads();
-  double* T = Tm + int64_t(g) * BW * BW;
+    for (int ch = 0; ch < ngc; ++ch) s += Gp[(int64_t(g) * ngc + ch) * BW * BW + int64_t(j) * BW + tid];
+    return s;
+  };
   const int i = tid;
+  double nxt = load_col(0);
   for (int jcol = 0; jcol < BW; ++jcol) {
+    gcol[jcol & 1][tid] = nxt;
+    __syncthreads();
+    if (jcol + 1 < BW) nxt = load_col(jcol + 1);
     const double tj = g0 + jcol < nref ? tau[g0 + jcol] : 0.0;
     double v = 0.0;
     if (i < jcol) {
       double s = 0.0;
-      for (int l = i; l < jcol; ++l) s += T[i * BW + l] * G[l][jcol];
+      for (int l = i; l < jcol; ++l) s += Ts[i][l] * gcol[jcol & 1][l];
       v = -tj * s;
     } else if (i == jcol) {
       v = tj;
     }
-    T[i * BW + jcol] = v;
+    Ts[i][jcol] = v;
   }
+  __syncthreads();
+  double* T = Tm + int64_t(g) * BW * BW;
+  for (int q = tid; q < BW * BW; q += BW) T[q] = Ts[q / BW][q % BW];
 }
 
 // Yp[ch][a][c] = sum over the chunk's rows of V[r][a] Z[r][c]   (64 columns per workgroup)
