@@ -70,6 +70,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs)
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {

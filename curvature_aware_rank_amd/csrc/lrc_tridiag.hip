@@ -14,10 +14,12 @@
 //      The reflector of column i (v[i+1] = 1) is stored in column i below the diagonal.
 //   2. All eigenvalues of T by Sturm-count multisection (16 points per step, 14 steps).
 //   3. Eigenvectors of the wanted (largest) eigenvalues by inverse iteration on T with
-//      partial pivoting (two solves), one thread per vector; eigenvalues closer than 1e-7 ||T|| form a
-//      cluster whose vectors one thread computes in turn, orthogonalised against each
-//      other (modified Gram-Schmidt).  Clusters larger than 32 are reported to the caller,
-//      which then uses the Jacobi solver.
+//      partial pivoting, two solves (the eigenvalues are accurate to ~eps ||T||): the
+//      factorisation and first solve of every vector in parallel, then per cluster of
+//      eigenvalues closer than 1e-7 ||T|| (a lone one is a cluster of one) the second
+//      solves in turn, each iterate orthogonalised against the cluster's finished vectors
+//      (modified Gram-Schmidt).  Clusters larger than 32 are reported to the caller, which
+//      then uses the Jacobi solver.
 //   4. Back-transformation Z <- Q Z in blocks of 128 reflectors, I - V T V^T (T from the
 //      forward columnwise recurrence on V^T V).
 // Every reduction has a fixed order, so equal inputs give equal bits.
@@ -42,7 +44,6 @@ constexpr int BIS_ITERS = 14;   // 17^14 > 2^57: the interval shrinks below fp64
 constexpr int BIS_STAGE = 2048; // d, e^2 staged through LDS in chunks of this many
 constexpr int CL_MAX = 32;      // largest cluster inverse iteration handles
 constexpr double CL_TOL = 1e-7; // eigenvalues closer than CL_TOL ||T|| share a cluster
-constexpr int INV_ITERS = 2;    // inverse-iteration solves per vector (eigenvalues are accurate to ~eps ||T||)
 constexpr double EPS = 2.220446049250313e-16;
 
 __device__ __forceinline__ void tile_of(int t, int& b, int& c) {
@@ -674,205 +675,353 @@ __device__ __forceinline__ double start_value(int j, int k) {
   return double(h) * (2.0 / 4294967296.0) - 1.0;
 }
 
-// one thread per cluster: LU (partial pivoting) of T - lambda I, INV_ITERS solves, MGS
-// within the cluster; Z[k][j] (n x ncols) receives eigenvector j of T.  Per-thread arrays
-// live at [k][j] (coalesced across the wave); every pass runs in unguarded batches of IB
-// elements (all loads of a batch in flight together) followed by a guarded tail.
-constexpr int IB = 16;
+// Inverse iteration on T for the wanted eigenvalues, in two kernels:
+//  A) one wave per vector: LU with partial pivoting of T - lambda I (the lambda of a
+//     cluster member is lowered to stay at least 10 eps ||T|| below the previous
+//     member's), with the first solve's forward elimination of a pseudo-random start
+//     vector done in the same pass, then the back-substitution;
+//  B) one wave per cluster (a lone eigenvalue is a cluster of one), members in order:
+//     orthogonalise the first iterate against the cluster's finished vectors (modified
+//     Gram-Schmidt), normalise, second solve, orthogonalise again, normalise.
+// The recurrences are sequential, so lane 0 runs them out of LDS while the whole wave
+// streams their inputs and outputs in chunks of CH steps (the next chunk's loads in
+// flight during the current chunk's recurrence).  The per-vector arrays are vector
+// major: LU records {1/pivot, u1, u2, multiplier} (32 B) and row-interchange flags, and
+// the iterates Zw (one row of n per vector); a transpose writes Z (n x ncols) at the end.
+// The orthogonalisation and scaling passes use all lanes (sums per lane in row order,
+// then a fixed butterfly).
+constexpr int CH = 256;   // recurrence steps per staged chunk
+constexpr int CPL = CH / 64;
 
-__global__ __launch_bounds__(64) void tri_inviter_kernel(const double* __restrict__ d, const double* __restrict__ e,
-                                                         int n, const double* __restrict__ lam, int ncols,
-                                                         const double* __restrict__ bounds,
-                                                         const int* __restrict__ clen, const int* __restrict__ flag,
-                                                         double* __restrict__ U, uint8_t* __restrict__ piv,
-                                                         double* __restrict__ Z) {
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= ncols || *flag) return;
-  const int len = clen[j];
-  if (len == 0) return;
+// max over the 64 lanes (exact in any order)
+__device__ __forceinline__ double wave_max(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
+  return v;
+}
+
+// back-substitution z <- U^-1 z on vector j (records R, iterate z), chunks from the end;
+// returns ||z||^2 (to every lane)
+__device__ double inv_usolve(const double* __restrict__ R, double* __restrict__ z, int n, double (*s_in)[CH][4],
+                             double (*s_z)[CH], double* s_out, double* s_sc) {
+  const int lane = threadIdx.x;
+  const int nch = (n + CH - 1) / CH;
+  double gr[CPL][4], gz[CPL];
+  auto load = [&](int c) {
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      const int k = min(c * CH + lane + 64 * u, n - 1);
+      const f64x2 a = *reinterpret_cast<const f64x2*>(R + int64_t(k) * 4);
+      const f64x2 b = *reinterpret_cast<const f64x2*>(R + int64_t(k) * 4 + 2);
+      gr[u][0] = a[0];
+      gr[u][1] = a[1];
+      gr[u][2] = b[0];
+      gr[u][3] = b[1];
+      gz[u] = z[k];
+    }
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      const int i = lane + 64 * u;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) s_in[buf][i][t] = gr[u][t];
+      s_z[buf][i] = gz[u];
+    }
+  };
+  double x1 = 0.0, x2 = 0.0, nrm2 = 0.0;
+  load(nch - 1);
+  stage((nch - 1) & 1);
+  for (int c = nch - 1; c >= 0; --c) {
+    const int buf = c & 1;
+    if (c > 0) load(c - 1);
+    __syncthreads();
+    const int cnt = min(CH, n - c * CH);
+    if (lane == 0) {
+      #pragma unroll 8
+      for (int i = cnt - 1; i >= 0; --i) {
+        const double xk = (s_z[buf][i] - s_in[buf][i][1] * x1 - s_in[buf][i][2] * x2) * s_in[buf][i][0];
+        s_out[i] = xk;
+        nrm2 += xk * xk;
+        x2 = x1;
+        x1 = xk;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      const int i = lane + 64 * u;
+      if (i < cnt) z[c * CH + i] = s_out[i];
+    }
+    if (c > 0) stage(buf ^ 1);
+  }
+  if (lane == 0) s_sc[0] = nrm2;
+  __syncthreads();
+  return s_sc[0];
+}
+
+__global__ __launch_bounds__(64) void tri_inviter_a_kernel(const double* __restrict__ d, const double* __restrict__ e,
+                                                           int n, const double* __restrict__ lam, int ncols,
+                                                           const double* __restrict__ bounds,
+                                                           const int* __restrict__ clen, const int* __restrict__ flag,
+                                                           double* __restrict__ Rall, uint8_t* __restrict__ Pall,
+                                                           double* __restrict__ Zw) {
+  __shared__ double s_in[2][CH][4];
+  __shared__ double s_z[2][CH];
+  __shared__ double s_out[CH];
+  __shared__ double s_rec[CH][4];
+  __shared__ uint8_t s_piv[CH];
+  __shared__ double s_sc[1];
+  const int jv = blockIdx.x;
+  if (*flag) return;
+  const int lane = threadIdx.x;
+  int s = jv;   // the cluster's first member (clen is > 0 there, 0 at the others)
+  while (s > 0 && clen[s] == 0) --s;
   const double tnorm = bounds[3];
   const double tiny = EPS * tnorm;
-  const int64_t nc = ncols;
-  double* __restrict__ r0 = U;                       // 1 / pivot (tiny pivots replaced by +-tiny)
-  double* __restrict__ u1 = U + int64_t(n) * nc;     // first superdiagonal of U
-  double* __restrict__ u2 = U + 2 * int64_t(n) * nc; // second superdiagonal (fill from pivoting)
-  double* __restrict__ ml = U + 3 * int64_t(n) * nc; // multipliers
+  double lmb = lam[n - 1 - s];
+  for (int p = s + 1; p <= jv; ++p) lmb = fmin(lam[n - 1 - p], lmb - 10.0 * EPS * tnorm);
+  double* R = Rall + int64_t(jv) * n * 4;
+  uint8_t* PV = Pall + int64_t(jv) * n;
+  double* z = Zw + int64_t(jv) * n;
   const int nm1 = n - 1;
-  double lprev = 0.0;
-  for (int q = 0; q < len; ++q) {
-    const int jv = j + q;
-    double lmb = lam[n - 1 - jv];
-    if (q > 0) lmb = fmin(lmb, lprev - 10.0 * EPS * tnorm);
-    lprev = lmb;
-    // ---- factor T - lmb I = P L U
-    double cd = d[0] - lmb, cs = n > 1 ? e[0] : 0.0;
-    auto fstep = [&](int k, double sub, double nd, double ns) {
-      const int64_t o = int64_t(k) * nc + j;
-      double piv_u0;
-      if (fabs(cd) >= fabs(sub)) {
-        const double dd = cd == 0.0 ? tiny : cd;
-        const double l = sub / dd;
-        piv_u0 = dd;
-        u1[o] = cs;
-        u2[o] = 0.0;
-        ml[o] = l;
-        piv[o] = 0;
-        cd = nd - l * cs;
-        cs = ns;
-      } else {
-        const double l = cd / sub;
-        piv_u0 = sub;
-        u1[o] = nd;
-        u2[o] = ns;
-        ml[o] = l;
-        piv[o] = 1;
-        cd = cs - l * nd;
-        cs = -l * ns;
-      }
-      if (fabs(piv_u0) < tiny) piv_u0 = piv_u0 < 0.0 ? -tiny : tiny;
-      r0[o] = 1.0 / piv_u0;
-    };
-    int k0 = 0;
-    for (; k0 + IB < nm1; k0 += IB) {   // e[k0 .. k0+IB] and d[k0+1 .. k0+IB] all valid
-      double eb[IB + 1], db[IB];
+  // ---- factor T - lmb I = P L U (steps k = 0 .. n-2, then the last pivot) and, in the
+  //      same pass, y = L^-1 P z0 for the start vector z0 (generated on the fly)
+  // inputs of step k: e[k], d[k+1], e[k+1]; chunk c stages d[cCH+1 ..], e[cCH ..] (CH + 1)
+  double (*s_d)[CH] = s_z;   // the factor pass uses the z staging buffers for d
+  double gd[CPL], ge[CPL], ge_last = 0.0;
+  auto load_de = [&](int c) {
 #pragma unroll
-      for (int u = 0; u <= IB; ++u) eb[u] = e[k0 + u];
-#pragma unroll
-      for (int u = 0; u < IB; ++u) db[u] = d[k0 + u + 1];
-#pragma unroll
-      for (int u = 0; u < IB; ++u) fstep(k0 + u, eb[u], db[u] - lmb, eb[u + 1]);
+    for (int u = 0; u < CPL; ++u) {
+      const int k = c * CH + lane + 64 * u;
+      gd[u] = d[min(k + 1, n - 1)];
+      ge[u] = e[min(k, max(n - 2, 0))];
     }
-    for (int k = k0; k < nm1; ++k) fstep(k, e[k], d[k + 1] - lmb, k + 1 < nm1 ? e[k + 1] : 0.0);
-    {
-      double p0 = cd;
-      if (fabs(p0) < tiny) p0 = p0 < 0.0 ? -tiny : tiny;
-      const int64_t o = int64_t(nm1) * nc + j;
-      r0[o] = 1.0 / p0;
-      u1[o] = 0.0;
-      u2[o] = 0.0;
+    ge_last = e[min(c * CH + CH, max(n - 2, 0))];
+  };
+  auto stage_de = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      const int i = lane + 64 * u;
+      s_d[buf][i] = gd[u];
+      s_in[buf][i][0] = ge[u];
     }
-    double* __restrict__ z = Z + jv;
-    double sc = 1.0;   // scale of the stored vector (applied on the fly)
-    for (int it = 0; it < INV_ITERS; ++it) {
-      // ---- apply P and L^-1 to sc * z (the running element stays in a register); the
-      // first solve starts from the pseudo-random vector, generated on the fly
-      const bool first = it == 0;
-      auto zin = [&](int k) { return first ? start_value(jv, k) : z[int64_t(k) * nc] * sc; };
-      double ycur = zin(0);
-      auto lstep = [&](int k, double ynext, double l, int pv) {
+    if (lane == 0) s_in[buf][0][1] = ge_last;   // e at the chunk's end, for its last step
+  };
+  double cd = d[0] - lmb, cs = n > 1 ? e[0] : 0.0;
+  double ycur = start_value(jv, 0);
+  const int nchf = (nm1 + CH - 1) / CH;
+  if (nchf > 0) {
+    load_de(0);
+    stage_de(0);
+  }
+  for (int c = 0; c < nchf; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nchf) load_de(c + 1);
+    __syncthreads();
+    const int cnt = min(CH, nm1 - c * CH);
+    if (lane == 0) {
+      #pragma unroll 8
+      for (int i = 0; i < cnt; ++i) {
+        const int k = c * CH + i;
+        const double sub = s_in[buf][i][0];
+        const double nd = s_d[buf][i] - lmb;
+        const double ns = k + 1 < nm1 ? (i + 1 < CH ? s_in[buf][i + 1][0] : s_in[buf][0][1]) : 0.0;
+        double piv_u0, u1, u2, l;
+        int pv;
+        if (fabs(cd) >= fabs(sub)) {
+          const double dd = cd == 0.0 ? tiny : cd;
+          l = sub / dd;
+          piv_u0 = dd;
+          u1 = cs;
+          u2 = 0.0;
+          pv = 0;
+          cd = nd - l * cs;
+          cs = ns;
+        } else {
+          l = cd / sub;
+          piv_u0 = sub;
+          u1 = nd;
+          u2 = ns;
+          pv = 1;
+          cd = cs - l * nd;
+          cs = -l * ns;
+        }
+        if (fabs(piv_u0) < tiny) piv_u0 = piv_u0 < 0.0 ? -tiny : tiny;
+        s_rec[i][0] = 1.0 / piv_u0;
+        s_rec[i][1] = u1;
+        s_rec[i][2] = u2;
+        s_rec[i][3] = l;
+        s_piv[i] = uint8_t(pv);
+        // forward elimination of the start vector with this step's multiplier
+        double ynext = start_value(jv, k + 1);
         double yk = ycur;
         if (pv) {
           yk = ynext;
           ynext = ycur;
         }
-        z[int64_t(k) * nc] = yk;
+        s_out[i] = yk;
         ycur = ynext - l * yk;
-      };
-      int k = 0;
-      for (; k + IB <= nm1; k += IB) {
-        double zn[IB], lm[IB];
-        int pv[IB];
-#pragma unroll
-        for (int u = 0; u < IB; ++u) {
-          zn[u] = zin(k + u + 1);
-          lm[u] = ml[int64_t(k + u) * nc + j];
-          pv[u] = piv[int64_t(k + u) * nc + j];
-        }
-#pragma unroll
-        for (int u = 0; u < IB; ++u) lstep(k + u, zn[u], lm[u], pv[u]);
-      }
-      for (; k < nm1; ++k) lstep(k, zin(k + 1), ml[int64_t(k) * nc + j], piv[int64_t(k) * nc + j]);
-      z[int64_t(nm1) * nc] = ycur;
-      // ---- back-substitution with U, squared norm on the way
-      double x1 = 0.0, x2 = 0.0, nrm2 = 0.0;
-      auto ustep = [&](int kk, double zk, double rp, double a1, double a2) {
-        const double xk = (zk - a1 * x1 - a2 * x2) * rp;
-        z[int64_t(kk) * nc] = xk;
-        nrm2 += xk * xk;
-        x2 = x1;
-        x1 = xk;
-      };
-      int k1 = nm1;
-      for (; k1 - IB + 1 >= 0; k1 -= IB) {
-        double zz[IB], a0[IB], a1[IB], a2[IB];
-#pragma unroll
-        for (int u = 0; u < IB; ++u) {
-          const int64_t o = int64_t(k1 - u) * nc + j;
-          zz[u] = z[int64_t(k1 - u) * nc];
-          a0[u] = r0[o];
-          a1[u] = u1[o];
-          a2[u] = u2[o];
-        }
-#pragma unroll
-        for (int u = 0; u < IB; ++u) ustep(k1 - u, zz[u], a0[u], a1[u], a2[u]);
-      }
-      for (; k1 >= 0; --k1) {
-        const int64_t o = int64_t(k1) * nc + j;
-        ustep(k1, z[int64_t(k1) * nc], r0[o], u1[o], u2[o]);
-      }
-      // ---- orthogonalise against the cluster's earlier (unit) vectors
-      // (loads in batches of IB, all in flight together; sums in element order)
-      for (int p = 0; p < q; ++p) {
-        const double* zp = Z + (j + p);
-        double dot = 0.0;
-        int kb = 0;
-        for (; kb + IB <= n; kb += IB) {
-          double ta[IB], tb[IB];
-#pragma unroll
-          for (int u = 0; u < IB; ++u) {
-            ta[u] = zp[int64_t(kb + u) * nc];
-            tb[u] = z[int64_t(kb + u) * nc];
-          }
-#pragma unroll
-          for (int u = 0; u < IB; ++u) dot += ta[u] * tb[u];
-        }
-        for (; kb < n; ++kb) dot += zp[int64_t(kb) * nc] * z[int64_t(kb) * nc];
-        nrm2 = 0.0;
-        kb = 0;
-        for (; kb + IB <= n; kb += IB) {
-          double ta[IB], tb[IB];
-#pragma unroll
-          for (int u = 0; u < IB; ++u) {
-            ta[u] = zp[int64_t(kb + u) * nc];
-            tb[u] = z[int64_t(kb + u) * nc];
-          }
-#pragma unroll
-          for (int u = 0; u < IB; ++u) {
-            const double zk = tb[u] - dot * ta[u];
-            z[int64_t(kb + u) * nc] = zk;
-            nrm2 += zk * zk;
-          }
-        }
-        for (; kb < n; ++kb) {
-          const double zk = z[int64_t(kb) * nc] - dot * zp[int64_t(kb) * nc];
-          z[int64_t(kb) * nc] = zk;
-          nrm2 += zk * zk;
-        }
-      }
-      // the solve's growth is at most ~1/tiny: squares stay finite for sane scalings
-      sc = nrm2 > 0.0 && nrm2 < 1e300 ? 1.0 / sqrt(nrm2) : 0.0;
-      if (sc == 0.0) {
-        // badly scaled input: scale by the largest entry first
-        double mx = 0.0;
-        for (int kk = 0; kk < n; ++kk) mx = fmax(mx, fabs(z[int64_t(kk) * nc]));
-        const double inv_mx = mx > 0.0 && mx < 1e308 ? 1.0 / mx : 1.0;
-        nrm2 = 0.0;
-        for (int kk = 0; kk < n; ++kk) {
-          const double zk = z[int64_t(kk) * nc] * inv_mx;
-          nrm2 += zk * zk;
-        }
-        sc = nrm2 > 0.0 ? inv_mx / sqrt(nrm2) : 1.0;
       }
     }
-    int kk = 0;
-    for (; kk + IB <= n; kk += IB) {
-      double t[IB];
+    __syncthreads();
 #pragma unroll
-      for (int u = 0; u < IB; ++u) t[u] = z[int64_t(kk + u) * nc];
-#pragma unroll
-      for (int u = 0; u < IB; ++u) z[int64_t(kk + u) * nc] = t[u] * sc;
+    for (int u = 0; u < CPL; ++u) {
+      const int i = lane + 64 * u;
+      if (i < cnt) {
+        const int k = c * CH + i;
+        *reinterpret_cast<f64x2*>(R + int64_t(k) * 4) = f64x2{s_rec[i][0], s_rec[i][1]};
+        *reinterpret_cast<f64x2*>(R + int64_t(k) * 4 + 2) = f64x2{s_rec[i][2], s_rec[i][3]};
+        PV[k] = s_piv[i];
+        z[k] = s_out[i];
+      }
     }
-    for (; kk < n; ++kk) z[int64_t(kk) * nc] *= sc;
+    if (c + 1 < nchf) stage_de(buf ^ 1);
+  }
+  if (lane == 0) {
+    double p0 = cd;
+    if (fabs(p0) < tiny) p0 = p0 < 0.0 ? -tiny : tiny;
+    *reinterpret_cast<f64x2*>(R + int64_t(nm1) * 4) = f64x2{1.0 / p0, 0.0};
+    *reinterpret_cast<f64x2*>(R + int64_t(nm1) * 4 + 2) = f64x2{0.0, 0.0};
+    PV[nm1] = 0;
+    z[nm1] = ycur;
+  }
+  __syncthreads();   // the records and y written above are read back below
+  inv_usolve(R, z, n, s_in, s_z, s_out, s_sc);
+}
+
+__global__ __launch_bounds__(64) void tri_inviter_b_kernel(int n, int ncols, const int* __restrict__ clen,
+                                                           const int* __restrict__ flag,
+                                                           const double* __restrict__ Rall,
+                                                           const uint8_t* __restrict__ Pall,
+                                                           double* __restrict__ Zw) {
+  __shared__ double s_in[2][CH][4];
+  __shared__ double s_z[2][CH];
+  __shared__ double s_out[CH];
+  __shared__ uint8_t s_piv[2][CH];
+  __shared__ double s_zx[2];
+  __shared__ double s_sc[1];
+  const int j = blockIdx.x;
+  if (*flag) return;
+  const int len = clen[j];
+  if (len == 0) return;
+  const int lane = threadIdx.x;
+  // orthogonalise iterate jv against the finished vectors j .. jv-1; returns ||z||^2
+  auto orth = [&](int jv) {
+    double* z = Zw + int64_t(jv) * n;
+    for (int p = j; p < jv; ++p) {
+      const double* zp = Zw + int64_t(p) * n;
+      double dot = 0.0;
+      for (int k = lane; k < n; k += 64) dot += zp[k] * z[k];
+      dot = wave_sum(dot);
+      for (int k = lane; k < n; k += 64) z[k] -= dot * zp[k];
+    }
+    double s2 = 0.0;
+    for (int k = lane; k < n; k += 64) s2 += z[k] * z[k];
+    return wave_sum(s2);
+  };
+  // 1 / ||z||, or for a badly scaled z 1 / ||z|| taken after scaling by its largest entry
+  auto unit_scale = [&](int jv, double nrm2) {
+    if (nrm2 > 0.0 && nrm2 < 1e300) return 1.0 / sqrt(nrm2);
+    const double* z = Zw + int64_t(jv) * n;
+    double mx = 0.0;
+    for (int k = lane; k < n; k += 64) mx = fmax(mx, fabs(z[k]));
+    mx = wave_max(mx);
+    const double inv_mx = mx > 0.0 && mx < 1e308 ? 1.0 / mx : 1.0;
+    double s2 = 0.0;
+    for (int k = lane; k < n; k += 64) {
+      const double v = z[k] * inv_mx;
+      s2 += v * v;
+    }
+    s2 = wave_sum(s2);
+    return s2 > 0.0 ? inv_mx / sqrt(s2) : 1.0;
+  };
+  const int nm1 = n - 1;
+  const int nch = (n + CH - 1) / CH;
+  for (int q = 0; q < len; ++q) {
+    const int jv = j + q;
+    const double* R = Rall + int64_t(jv) * n * 4;
+    const uint8_t* PV = Pall + int64_t(jv) * n;
+    double* z = Zw + int64_t(jv) * n;
+    const double sc = unit_scale(jv, orth(jv));
+    __syncthreads();
+    // ---- y = L^-1 P (sc z): chunk c stages z[cCH .. cCH+CH] (one past, for the
+    //      interchange), the multipliers and the flags
+    double gz[CPL], gl[CPL], gx = 0.0;
+    uint8_t gp[CPL];
+    auto load = [&](int c) {
+#pragma unroll
+      for (int u = 0; u < CPL; ++u) {
+        const int k = min(c * CH + lane + 64 * u, n - 1);
+        gz[u] = z[k] * sc;
+        gl[u] = R[int64_t(k) * 4 + 3];
+        gp[u] = PV[k];
+      }
+      gx = z[min(c * CH + CH, n - 1)] * sc;
+    };
+    auto stage = [&](int buf) {
+#pragma unroll
+      for (int u = 0; u < CPL; ++u) {
+        const int i = lane + 64 * u;
+        s_z[buf][i] = gz[u];
+        s_in[buf][i][3] = gl[u];
+        s_piv[buf][i] = gp[u];
+      }
+      if (lane == 0) s_zx[buf] = gx;
+    };
+    load(0);
+    stage(0);
+    double ycur = z[0] * sc;
+    for (int c = 0; c < nch; ++c) {
+      const int buf = c & 1;
+      if (c + 1 < nch) load(c + 1);
+      __syncthreads();
+      const int cnt = min(CH, nm1 - c * CH);   // elimination steps in this chunk
+      if (lane == 0) {
+        #pragma unroll 8
+        for (int i = 0; i < cnt; ++i) {
+          double ynext = i + 1 < CH ? s_z[buf][i + 1] : s_zx[buf];
+          double yk = ycur;
+          if (s_piv[buf][i]) {
+            yk = ynext;
+            ynext = ycur;
+          }
+          s_out[i] = yk;
+          ycur = ynext - s_in[buf][i][3] * yk;
+        }
+        if (c == nch - 1) s_out[max(cnt, 0)] = ycur;   // the last element
+      }
+      __syncthreads();
+      const int nw = min(CH, n - c * CH);   // elements written by this chunk
+#pragma unroll
+      for (int u = 0; u < CPL; ++u) {
+        const int i = lane + 64 * u;
+        if (i < nw) z[c * CH + i] = s_out[i];
+      }
+      if (c + 1 < nch) stage(buf ^ 1);
+    }
+    __syncthreads();
+    inv_usolve(R, z, n, s_in, s_z, s_out, s_sc);
+    const double sc2 = unit_scale(jv, orth(jv));
+    for (int k = lane; k < n; k += 64) z[k] *= sc2;
+    __syncthreads();
+  }
+}
+
+// Z (n x ncols) = Zw^T (Zw: ncols x n)
+__global__ __launch_bounds__(256) void inv_transpose_kernel(const double* __restrict__ Zw, int n, int ncols,
+                                                            double* __restrict__ Z) {
+  __shared__ double t[64][65];
+  const int k0 = blockIdx.x * 64, j0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int jv = j0 + i, k = k0 + tx;
+    t[i][tx] = (jv < ncols && k < n) ? Zw[int64_t(jv) * n + k] : 0.0;
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int k = k0 + i, jv = j0 + tx;
+    if (k < n && jv < ncols) Z[int64_t(k) * ncols + jv] = t[tx][i];
   }
 }
 
@@ -1201,7 +1350,7 @@ __global__ __launch_bounds__(256) void tri_out_kernel(const double* __restrict__
 }
 
 struct TWs {
-  double *P, *S, *SV, *SW, *npart, *x0, *d, *e, *tau, *Wp, *lam, *bounds, *U, *Z, *Gp, *T, *Yp, *Yr, *Y2;
+  double *P, *S, *SV, *SW, *npart, *x0, *d, *e, *tau, *Wp, *lam, *bounds, *U, *Z, *Zw, *Gp, *T, *Yp, *Yr, *Y2;
   int *clen, *flag;
   uint8_t* piv;
 };
@@ -1228,6 +1377,7 @@ TWs carve_tri(Carve& cv, int64_t n, int64_t ncols) {
   w.U = cv.take<double>(size_t(4 * n * ncols));
   w.piv = cv.take<uint8_t>(size_t(n * ncols));
   w.Z = cv.take<double>(size_t(n * ncols));
+  w.Zw = cv.take<double>(size_t(n * ncols));
   w.Gp = cv.take<double>(size_t(ngroups * ngc * BW * BW));
   w.T = cv.take<double>(size_t(ngroups * BW * BW));
   w.Yp = cv.take<double>(size_t(nbc * BW * ncols));
@@ -1332,8 +1482,13 @@ lrc_status tridiag_eig(hipStream_t st, double* A, int64_t k, int64_t lda, int64_
   }
   {
     ProfScope scope("tri_inviter_kernel", st, 0.0, 0.0);
-    tri_inviter_kernel<<<unsigned(cdiv(ncols, 64)), 64, 0, st>>>(w.d, w.e, n, w.lam, ncols, w.bounds, w.clen, w.flag,
-                                                                 w.U, w.piv, w.Z);
+    tri_inviter_a_kernel<<<unsigned(ncols), 64, 0, st>>>(w.d, w.e, n, w.lam, ncols, w.bounds, w.clen, w.flag, w.U,
+                                                         w.piv, w.Zw);
+    LRC_LAUNCHED();
+    tri_inviter_b_kernel<<<unsigned(ncols), 64, 0, st>>>(n, ncols, w.clen, w.flag, w.U, w.piv, w.Zw);
+    LRC_LAUNCHED();
+    inv_transpose_kernel<<<dim3(unsigned(cdiv(n, 64)), unsigned(cdiv(ncols, 64))), 256, 0, st>>>(w.Zw, n, ncols,
+                                                                                                 w.Z);
     LRC_LAUNCHED();
   }
 
