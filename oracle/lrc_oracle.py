@@ -5,7 +5,9 @@ baseline leg import this module; the library never does, and this module imports
 nothing from the library.  It is written to be read against the pages, not to be
 fast: numpy/scipy (LAPACK) in fp64, one step per function, in the pages' order.
 
-Pages (gist.science explainers):
+Pages (gist.science explainers; the alternative scorers at the end also cite UniRank
+2.1 "Local Structural Significance" / "Global Functional Importance" and Swift-SVD
+section B "Dynamic Rank Allocation Strategy", item "Hybrid Scoring"):
   * LASER: Loss-Aware Singular-value Decomposition and Rank Allocation for Efficient
     Low-Precision Vision-Language Models (technical summary, Methodology 1 "loss-aware
     SVD" with the items K-FAC surrogate / Transformation / QAW, Methodology 2
@@ -36,6 +38,7 @@ __all__ = [
     "qaw_fake_quant", "covariance_sum", "covariance", "cholesky_lower", "whiten",
     "truncated_svd", "canonical_signs", "back_map", "whiten_decompose",
     "fisher_scores", "kfac_scores", "allocation_keys", "allocate", "kfac_loss",
+    "unirank_scores", "swift_layer_scores",
 ]
 
 
@@ -286,3 +289,37 @@ def kfac_loss(dw, x, g):
     v = dwp.reshape(-1, order="F")
     k = np.kron(np.asarray(g, dtype=np.float64), np.asarray(x, dtype=np.float64))
     return 0.5 * float(v @ k @ v)
+
+
+# ---------------------------------------------------------------------------
+# alternative component scores for the same allocator
+# ---------------------------------------------------------------------------
+def unirank_scores(sigmas_per_matrix, importance):
+    """UniRank (2.1 Sorting-and-Truncation, "Aggregation and Truncation"): the score of
+    singular triplet i of matrix l is the layer's global functional importance I_l times
+    the triplet's local structural significance, its share of the squared singular-value
+    energy sigma_{l,i}^2 / ||Sigma_l||_F^2.  I_l is supplied by the caller (the pages
+    measure it as one minus the mean input/output cosine similarity of the layer on
+    calibration data).  A matrix whose singular values are all zero scores 0.
+    Returns one fp64 array per matrix."""
+    out = []
+    for sig, il in zip(sigmas_per_matrix, importance):
+        s2 = np.asarray(sig, dtype=np.float64) ** 2
+        total = float(np.sum(s2))
+        out.append(float(il) * s2 / total if total > 0.0 else np.zeros_like(s2))
+    return out
+
+
+def swift_layer_scores(sigmas_per_matrix, beta, alpha):
+    """Swift-SVD (section B, Hybrid Scoring): the compressibility score of layer l at
+    rank k is beta_l^alpha * log(e + eps*_{k,l})^(1 - alpha), where beta_l is the
+    caller's layer importance and eps*_{k,l} the theoretical loss of the closed-form
+    rank-k solution, i.e. the energy of the discarded singular values,
+    sum_{j > k} sigma_{l,j}^2.  Entry k - 1 of matrix l's array is the score at rank k
+    (k = 1 .. number of singular values).  Returns one fp64 array per matrix."""
+    out = []
+    for sig, b in zip(sigmas_per_matrix, beta):
+        s2 = np.asarray(sig, dtype=np.float64) ** 2
+        eps = np.array([float(np.sum(s2[k:])) for k in range(1, len(s2) + 1)], dtype=np.float64)
+        out.append(float(b) ** alpha * np.log(np.e + eps) ** (1.0 - alpha))
+    return out

@@ -291,3 +291,58 @@ def test_allocate_equal_costs_is_optimal_subset():
 def test_allocate_rejects_nan():
     with pytest.raises(ValueError):
         oracle.allocate([np.array([1.0, np.nan], np.float32)], [3], 10)
+
+
+# ----------------------------------------------------------------------------- alternative scorers
+def _rank_score_fixture():
+    rows = []
+    for ln in read_golden("rank_scores.txt"):
+        head, sig, want = (part.split() for part in ln.split("|"))
+        rows.append((head[0], [float(x) for x in head[1:]], np.array(sig, float), np.array(want, float)))
+    return rows
+
+
+def test_rank_scores_golden():
+    """Hand-worked values (tests/golden/rank_scores.txt, 7 significant digits)."""
+    for kind, par, sig, want in _rank_score_fixture():
+        if kind == "unirank":
+            got = oracle.unirank_scores([sig], [par[0]])[0]
+        else:
+            got = oracle.swift_layer_scores([sig], [par[0]], par[1])[0]
+        np.testing.assert_allclose(got, want, rtol=1e-6)
+
+
+def test_unirank_scores_sum_to_importance():
+    """Energy shares sum to one, so a matrix's scores sum to its importance I_l; they are
+    proportional to sigma^2; I_l = 0 or an all-zero spectrum scores zero."""
+    sig = [np.sort(RNG.random(n))[::-1] for n in (5, 1, 12)]
+    imp = [0.3, 2.0, 0.0]
+    out = oracle.unirank_scores(sig, imp)
+    for s, i, o in zip(sig, imp, out):
+        np.testing.assert_allclose(o.sum(), i, rtol=1e-14, atol=1e-300)
+        if i > 0:
+            np.testing.assert_allclose(o / o[0], s ** 2 / s[0] ** 2, rtol=1e-14)
+    assert np.all(oracle.unirank_scores([np.zeros(4)], [1.0])[0] == 0.0)
+
+
+def test_swift_discarded_energy_is_the_truncation_residual():
+    """eps*_k of the score is the theoretical loss of the rank-k optimum: by
+    Eckart-Young-Mirsky it equals ||M - M_k||_F^2 for the truncated SVD M_k, computed
+    here by reconstruction from numpy's SVD.  With alpha = 0 the score is log(e + eps*)."""
+    m = RNG.standard_normal((9, 6))
+    u, sv, vt = np.linalg.svd(m, full_matrices=False)
+    got = oracle.swift_layer_scores([sv], [1.7], 0.0)[0]
+    for k in range(1, len(sv) + 1):
+        resid = m - (u[:, :k] * sv[:k]) @ vt[:k]
+        np.testing.assert_allclose(got[k - 1], np.log(np.e + np.sum(resid ** 2)), rtol=1e-12)
+
+
+def test_swift_limits_and_monotone():
+    """alpha = 1 gives beta at every rank; at full rank nothing is discarded, so the score
+    is beta^alpha; the score never grows with the rank (less is discarded)."""
+    sv = np.sort(RNG.random(7) * 3)[::-1]
+    np.testing.assert_allclose(oracle.swift_layer_scores([sv], [2.5], 1.0)[0], 2.5, rtol=1e-15)
+    for a in (0.0, 0.3, 0.8):
+        s = oracle.swift_layer_scores([sv], [2.5], a)[0]
+        np.testing.assert_allclose(s[-1], 2.5 ** a, rtol=1e-15)
+        assert np.all(np.diff(s) <= 0)
