@@ -134,6 +134,18 @@ def secondary(lrc, torch, dev):
                             "TFLOP/s": round(flops / t / 1e12, 2),
                             "mfma_bf16_frac": round(flops / t / 1e12 / PEAK_TFLOPS["bf16"], 4)}
     del a, b, left, right
+    # alternative scores from the singular values (224 matrices x 4096 components)
+    n_mat, per = 224, 4096
+    sig = torch.sort(torch.rand(n_mat, per, generator=g, device=dev), dim=1, descending=True)[0].reshape(-1)
+    offs = torch.arange(0, n_mat * per + 1, per, dtype=torch.int64, device=dev)
+    wgt = torch.rand(n_mat, generator=g, device=dev) + 0.5
+    for mode in ("unirank", "swift"):
+        lrc.lrc_rank_scores(sig, offs, wgt, mode=mode)
+        t = _time(lambda: lrc.lrc_rank_scores(sig, offs, wgt, mode=mode), torch, 5)
+        byt = 8.0 * n_mat * per   # sigma in, score out
+        out[f"rank_scores_{mode}"] = {"workload": f"{n_mat * per} components ({n_mat} matrices)",
+                                      "ms": round(t * 1e3, 3), "GB/s": round(byt / t / 1e9, 1)}
+    del sig, offs, wgt
     for m_items, label in ((917504, "decoder stack: 224 matrices"), (64 * 1024 * 1024, "scaled pool")):
         n_mat = 224 if m_items == 917504 else 16384
         per = m_items // n_mat

@@ -17,8 +17,9 @@ import torch
 __all__ = [
     "LRC_OK", "LRC_EINVAL", "LRC_EDTYPE", "LRC_EWORKSPACE", "LRC_EHIP", "LRC_ENOTPD",
     "LRC_ENOCONV", "LRC_ENONFINITE", "LRC_F32", "LRC_BF16", "LRC_COV_QUANT_INT8_TOKEN",
-    "LRC_SCORE_FISHER", "LRC_SCORE_KFAC", "LrcError", "lib", "library_path",
-    "lrc_accumulate_cov", "lrc_whiten_decompose", "lrc_score_components", "lrc_allocate_ranks",
+    "LRC_SCORE_FISHER", "LRC_SCORE_KFAC", "LRC_RANKSCORE_UNIRANK", "LRC_RANKSCORE_SWIFT", "LrcError", "lib",
+    "library_path", "lrc_accumulate_cov", "lrc_whiten_decompose", "lrc_score_components", "lrc_allocate_ranks",
+    "lrc_rank_scores",
     "lrc_status_string", "lrc_profile_start", "lrc_profile_stop", "lrc_profile_kernels",
 ]
 
@@ -27,6 +28,8 @@ LRC_F32, LRC_BF16 = 0, 1
 LRC_COV_QUANT_INT8_TOKEN = 0x1
 LRC_SCORE_FISHER = 0x1
 LRC_SCORE_KFAC = 0x2
+LRC_RANKSCORE_UNIRANK = 0x1
+LRC_RANKSCORE_SWIFT = 0x2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "liblrc.so")
@@ -44,6 +47,7 @@ _SIGS = {
     "lrc_score_components_workspace": (_sz, [_i64, _i64, _i64, _i64, _u32]),
     "lrc_allocate_ranks": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "lrc_allocate_ranks_workspace": (_sz, [_i64, _i64]),
+    "lrc_rank_scores": (_i32, [_vp, _vp, _i64, _i64, _vp, ctypes.c_float, _u32, _vp, _vp, _vp]),
     "lrc_status_string": (ctypes.c_char_p, [_i32]),
     "lrc_last_hip_error": (_i32, []),
     "lrc_profile_start": (_i32, []),
@@ -238,6 +242,30 @@ def lrc_allocate_ranks(scores: torch.Tensor, offsets: torch.Tensor, cost: torch.
                                   n_mat, M, int(budget), _ptr(order), _ptr(n_kept), _ptr(ranks), _ptr(kept),
                                   _ptr(info), _ptr(ws), ws.numel(), _stream()), "lrc_allocate_ranks")
     return order, n_kept, ranks, kept, info
+
+
+def lrc_rank_scores(sigma: torch.Tensor, offsets: torch.Tensor, weight: torch.Tensor, mode: str = "unirank",
+                    alpha: float = 0.5):
+    """Alternative component scores from singular values.  sigma: (M,) fp32, matrices
+    concatenated per offsets ((n_mat+1,) int64); weight: (n_mat,) fp32 -- the layer
+    importance I_l (mode "unirank") or beta_l (mode "swift", with alpha).
+
+    Returns (scores fp32 (M,), info int32 (1,))."""
+    for t, nm in ((sigma, "sigma"), (offsets, "offsets"), (weight, "weight")):
+        _dev(t, nm)
+    if sigma.dtype != torch.float32 or offsets.dtype != torch.int64 or weight.dtype != torch.float32:
+        raise ValueError("sigma and weight fp32, offsets int64")
+    n_mat = weight.numel()
+    if offsets.numel() != n_mat + 1:
+        raise ValueError("offsets must have n_mat + 1 entries")
+    flag = {"unirank": LRC_RANKSCORE_UNIRANK, "swift": LRC_RANKSCORE_SWIFT}[mode]
+    M = sigma.numel()
+    scores = torch.empty(M, dtype=torch.float32, device=sigma.device)
+    info = torch.empty(1, dtype=torch.int32, device=sigma.device)
+    _check(lib.lrc_rank_scores(_ptr(sigma.contiguous()), _ptr(offsets.contiguous()), n_mat, M,
+                               _ptr(weight.contiguous()), float(alpha), flag, _ptr(scores), _ptr(info), _stream()),
+           "lrc_rank_scores")
+    return scores, info
 
 
 def lrc_profile_start() -> None:

@@ -59,6 +59,10 @@ typedef enum { LRC_F32 = 0, LRC_BF16 = 1 } lrc_dtype;
 #define LRC_SCORE_FISHER 0x1u          /* empirical-Fisher score, needs A and B */
 #define LRC_SCORE_KFAC 0x2u            /* 1/2 sigma^2, needs sigma only */
 
+/* lrc_rank_scores modes (exactly one) */
+#define LRC_RANKSCORE_UNIRANK 0x1u     /* I_l sigma^2 / ||Sigma_l||_F^2 per component */
+#define LRC_RANKSCORE_SWIFT 0x2u       /* beta_l^alpha log(e + eps*_k)^(1-alpha) per rank k */
+
 /*
  * lrc_accumulate_cov -- covariance streaming.
  * LASER Methodology 1 (K-FAC surrogate): X and G are the activation and gradient
@@ -175,6 +179,31 @@ lrc_status lrc_allocate_ranks(const float* scores, const int64_t* offsets, const
                               int64_t* n_kept, int32_t* ranks, uint8_t* kept_mask, int32_t* info,
                               void* ws, size_t ws_bytes, void* stream);
 size_t lrc_allocate_ranks_workspace(int64_t n_mat, int64_t n_items);
+
+/*
+ * lrc_rank_scores -- alternative scores over the same component layout as
+ * lrc_allocate_ranks, from the singular values alone.
+ *   UNIRANK (UniRank 2.1, "Aggregation and Truncation"): scores[j] = weight[m] *
+ *     sigma_j^2 / sum over matrix m of sigma^2 -- the layer's global functional
+ *     importance I_l (weight, >= 0, supplied by the caller) times the component's share
+ *     of the singular-value energy; an all-zero spectrum scores 0.  These feed
+ *     lrc_allocate_ranks directly.
+ *   SWIFT (Swift-SVD section B, "Hybrid Scoring"): for the component at position p of
+ *     matrix m, scores[j] = weight[m]^alpha * log(e + eps)^(1 - alpha) with eps = the sum
+ *     of sigma^2 over positions > p: the layer's compressibility score if its rank were
+ *     p + 1 (weight = the layer importance beta_l > 0, 0 <= alpha <= 1).  The pages choose
+ *     ranks from these by a search on validation data, which is not part of the library.
+ * sigma: M = offsets[n_mat] fp32 singular values, matrix m owning sigma[offsets[m] ..
+ *   offsets[m+1]) in descending order (as lrc_whiten_decompose writes them).
+ * offsets: int64[n_mat + 1] (device, offsets[0] = 0, non-decreasing, offsets[n_mat] =
+ *   n_items).  weight: float[n_mat] (device).  scores: float[M] (device, output).
+ * info (device int32): 0 ok, LRC_EINVAL for inconsistent offsets or a weight out of range,
+ *   LRC_ENONFINITE for a NaN/Inf sigma or weight (the offending matrices' scores are not
+ *   written).  Sums are fp64 in a fixed order; identical inputs give identical bits.
+ */
+lrc_status lrc_rank_scores(const float* sigma, const int64_t* offsets, int64_t n_mat, int64_t n_items,
+                           const float* weight, float alpha, uint32_t mode, float* scores, int32_t* info,
+                           void* stream);
 
 /*
  * Measurement support (benchmarks and profilers; not needed for results).

@@ -101,6 +101,18 @@ def test_allocate_ranks_validation(lib):
     assert f(FAKE, FAKE, FAKE, 2, 10, 5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == EWORKSPACE
 
 
+def test_rank_scores_validation(lib):
+    f = lib.lrc_rank_scores
+    assert f(FAKE, FAKE, 2, 10, FAKE, 0.5, 0x3, FAKE, FAKE, None) == EDTYPE     # two modes
+    assert f(FAKE, FAKE, 2, 10, FAKE, 0.5, 0x0, FAKE, FAKE, None) == EDTYPE     # no mode
+    assert f(FAKE, FAKE, 0, 10, FAKE, 0.5, 0x1, FAKE, FAKE, None) == EINVAL     # n_mat 0
+    assert f(FAKE, FAKE, 2, -1, FAKE, 0.5, 0x1, FAKE, FAKE, None) == EINVAL     # n_items < 0
+    assert f(FAKE, None, 2, 10, FAKE, 0.5, 0x1, FAKE, FAKE, None) == EINVAL     # offsets null
+    assert f(FAKE, FAKE, 2, 10, FAKE, 1.5, 0x2, FAKE, FAKE, None) == EINVAL     # alpha > 1
+    assert f(FAKE, FAKE, 2, 10, FAKE, -0.1, 0x2, FAKE, FAKE, None) == EINVAL    # alpha < 0
+    assert f(None, FAKE, 2, 10, FAKE, 0.5, 0x1, FAKE, FAKE, None) == EINVAL     # sigma null
+
+
 def test_profile_session_without_work(lib):
     # no kernel launched: the session records nothing and out-of-range queries fail
     assert lib.lrc_profile_start() == 0

@@ -478,3 +478,68 @@ def test_allocate_rejects_nan_and_bad_cost(lrc):
     flat = torch.tensor([1.0, 2.0, 2.0], device=dev())
     _, _, _, _, info = lrc.lrc_allocate_ranks(flat, offs, torch.tensor([0], dtype=torch.int64, device=dev()), 10)
     assert int(info[0]) == lrc.LRC_EINVAL
+
+
+# ----------------------------------------------------------------------------- alternative scorers
+def _rank_score_case(lrc, sizes, mode, alpha, seed, zero_matrix=None):
+    rng = np.random.default_rng(seed)
+    sig = []
+    for m, z in enumerate(sizes):
+        s = np.sort(rng.gamma(0.7, 2.0, z))[::-1].astype(np.float32)
+        if m == zero_matrix:
+            s[:] = 0
+        sig.append(s)
+    weight = rng.uniform(0.2, 3.0, len(sizes)).astype(np.float32)
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    flat = np.concatenate(sig) if sig else np.zeros(0, np.float32)
+    got, info = lrc.lrc_rank_scores(torch.tensor(flat, device=dev()), torch.tensor(offs, device=dev()),
+                                    torch.tensor(weight, device=dev()), mode=mode, alpha=alpha)
+    if mode == "unirank":
+        ref = oracle.unirank_scores(sig, weight.astype(np.float64))
+    else:
+        ref = oracle.swift_layer_scores(sig, weight.astype(np.float64), float(np.float32(alpha)))
+    ref = np.concatenate(ref) if ref else np.zeros(0)
+    return to_np(got), ref, int(to_np(info)[0]), sig, weight, offs
+
+
+@pytest.mark.parametrize("mode,alpha", [("unirank", 0.0), ("swift", 0.5), ("swift", 0.0), ("swift", 1.0)])
+def test_rank_scores_match_oracle(lrc, mode, alpha):
+    """fp64 sums on the device, fp32 outputs: within 2 fp32 ulps of the fp64 oracle.  Sizes
+    cover empty and one-element matrices, segments shorter than a workgroup and a matrix
+    longer than a workgroup's 256 threads (several elements per thread)."""
+    got, ref, info, *_ = _rank_score_case(lrc, [5, 0, 1, 300, 4096, 17, 11008], mode, alpha, 3, zero_matrix=5)
+    assert info == 0
+    np.testing.assert_allclose(got, ref, rtol=2.5e-7, atol=1e-37)
+
+
+def test_rank_scores_unirank_feed_the_allocator(lrc):
+    """UniRank scores go straight into the global sort-and-truncate: the allocation of the
+    GPU's fp32 scores matches the oracle allocator on the same scores bit for bit."""
+    sizes = [64, 128, 96, 200]
+    got, ref, info, sig, weight, offs = _rank_score_case(lrc, sizes, "unirank", 0.0, 8)
+    assert info == 0
+    costs = [256, 384, 300, 520]
+    lst = [got[offs[m]:offs[m + 1]] for m in range(len(sizes))]
+    order, n_kept, ranks, kept, ainfo = lrc.lrc_allocate_ranks(
+        torch.tensor(got, device=dev()), torch.tensor(offs, device=dev()),
+        torch.tensor(np.asarray(costs, np.int64), device=dev()), 40000)
+    o = oracle.allocate(lst, costs, 40000)
+    assert int(to_np(ainfo)[0]) == 0
+    assert to_np(order).tolist() == o[0].tolist() and int(to_np(n_kept)[0]) == o[1]
+    assert to_np(ranks).tolist() == o[2].tolist()
+
+
+def test_rank_scores_reject_bad_inputs(lrc):
+    sig = torch.tensor([2.0, float("nan"), 1.0], device=dev())
+    offs = torch.tensor([0, 3], dtype=torch.int64, device=dev())
+    _, info = lrc.lrc_rank_scores(sig, offs, torch.tensor([1.0], device=dev()))
+    assert int(info[0]) == lrc.LRC_ENONFINITE
+    sig = torch.tensor([2.0, 1.0, 1.0], device=dev())
+    _, info = lrc.lrc_rank_scores(sig, offs, torch.tensor([-1.0], device=dev()))
+    assert int(info[0]) == lrc.LRC_EINVAL
+    _, info = lrc.lrc_rank_scores(sig, offs, torch.tensor([0.0], device=dev()), mode="swift")
+    assert int(info[0]) == lrc.LRC_EINVAL
+    _, info = lrc.lrc_rank_scores(sig, torch.tensor([0, 2], dtype=torch.int64, device=dev()),
+                                  torch.tensor([1.0], device=dev()))
+    assert int(info[0]) == lrc.LRC_EINVAL
+
