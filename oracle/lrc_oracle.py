@@ -7,7 +7,8 @@ fast: numpy/scipy (LAPACK) in fp64, one step per function, in the pages' order.
 
 Pages (gist.science explainers; the alternative scorers at the end also cite UniRank
 2.1 "Local Structural Significance" / "Global Functional Importance" and Swift-SVD
-section B "Dynamic Rank Allocation Strategy", item "Hybrid Scoring"):
+section B "Dynamic Rank Allocation Strategy", item "Hybrid Scoring"; the factor codec
+cites LASER section 3 "Hybrid SVD-Quantization for FFNs", item "Quantization"):
   * LASER: Loss-Aware Singular-value Decomposition and Rank Allocation for Efficient
     Low-Precision Vision-Language Models (technical summary, Methodology 1 "loss-aware
     SVD" with the items K-FAC surrogate / Transformation / QAW, Methodology 2
@@ -38,7 +39,7 @@ __all__ = [
     "qaw_fake_quant", "covariance_sum", "covariance", "cholesky_lower", "whiten",
     "truncated_svd", "canonical_signs", "back_map", "whiten_decompose",
     "fisher_scores", "kfac_scores", "allocation_keys", "allocate", "kfac_loss",
-    "unirank_scores", "swift_layer_scores",
+    "unirank_scores", "swift_layer_scores", "hadamard_rotation", "rotate_factors", "rtn_rows",
 ]
 
 
@@ -323,3 +324,36 @@ def swift_layer_scores(sigmas_per_matrix, beta, alpha):
         eps = np.array([float(np.sum(s2[k:])) for k in range(1, len(s2) + 1)], dtype=np.float64)
         out.append(float(b) ** alpha * np.log(np.e + eps) ** (1.0 - alpha))
     return out
+
+
+# ---------------------------------------------------------------------------
+# factor codec (LASER, 3. Hybrid SVD-Quantization for FFNs, item Quantization)
+# ---------------------------------------------------------------------------
+def hadamard_rotation(r, signs):
+    """The orthogonal rotation inserted between the low-rank factors to smooth outliers.
+    The pages do not fix it; the reading used here is a sign-randomised Hadamard matrix
+    R = H_r diag(signs) / sqrt(r), with H_r the Sylvester Hadamard matrix (r a power of
+    two) and signs a caller-supplied vector of +-1."""
+    h = scipy.linalg.hadamard(int(r)).astype(np.float64)
+    return h * np.asarray(signs, dtype=np.float64)[None, :] / np.sqrt(float(r))
+
+
+def rotate_factors(left, right, signs):
+    """left' = left R and right' = R^T right, so left' right' = left right (R orthogonal).
+    left: d_out x r, right: r x d_in.  The products are taken in fp64 and rounded once to
+    fp32 (the values the quantiser then sees)."""
+    rot = hadamard_rotation(np.asarray(left).shape[1], signs)
+    lr = np.asarray(left, dtype=np.float64) @ rot
+    rr = rot.T @ np.asarray(right, dtype=np.float64)
+    return lr.astype(np.float32), rr.astype(np.float32)
+
+
+def rtn_rows(x):
+    """Round-to-nearest int8 quantisation of each row (one output channel per row) of an
+    fp32 matrix.  The pages name RTN without its parameters; the reading used here is the
+    same symmetric quantiser as qaw_fake_quant, per row: scale = fl32(max|row| / 127),
+    q = clamp(round_half_even(fl32(x / scale)), -127, 127), an all-zero row gives zeros
+    with scale 0.  Returns (q int8, scale float32)."""
+    q, s, _ = qaw_fake_quant(np.asarray(x, dtype=np.float32))
+    return q, s
+

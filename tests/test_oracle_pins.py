@@ -346,3 +346,50 @@ def test_swift_limits_and_monotone():
         s = oracle.swift_layer_scores([sv], [2.5], a)[0]
         np.testing.assert_allclose(s[-1], 2.5 ** a, rtol=1e-15)
         assert np.all(np.diff(s) <= 0)
+
+
+# ----------------------------------------------------------------------------- factor codec
+def test_rotation_golden():
+    g = {ln.split(":")[0]: np.array(ln.split(":", 1)[1].split(), float) for ln in read_golden("hadamard_rotation.txt")}
+    lr, rr = oracle.rotate_factors(np.array([[1.0, 2.0]], np.float32), np.array([[1.0], [2.0]], np.float32), [1, -1])
+    np.testing.assert_allclose(lr[0], g["left"], rtol=1e-7)
+    np.testing.assert_allclose(rr[:, 0], g["right"], rtol=1e-7)
+
+
+def test_rotation_is_orthogonal_and_keeps_the_product():
+    """R R^T = I; left' right' = left right up to the fp32 rounding of the factors."""
+    r = 64
+    signs = RNG.choice([-1.0, 1.0], r)
+    rot = oracle.hadamard_rotation(r, signs)
+    np.testing.assert_allclose(rot @ rot.T, np.eye(r), atol=1e-14)
+    left = RNG.standard_normal((10, r)).astype(np.float32)
+    right = RNG.standard_normal((r, 7)).astype(np.float32)
+    lr, rr = oracle.rotate_factors(left, right, signs)
+    prod = left.astype(np.float64) @ right.astype(np.float64)
+    np.testing.assert_allclose(lr.astype(np.float64) @ rr.astype(np.float64), prod,
+                               atol=64 * 2 ** -23 * np.abs(prod).max())
+
+
+def test_rotation_spreads_an_outlier():
+    """A row with one spike of size M (the outlier channels the rotation smooths) becomes
+    a row whose every entry has magnitude M / sqrt(r): its max drops by sqrt(r)."""
+    r = 256
+    x = np.zeros((1, r), np.float32)
+    x[0, 37] = 50.0
+    lr, _ = oracle.rotate_factors(x, np.zeros((r, 1), np.float32), RNG.choice([-1.0, 1.0], r))
+    np.testing.assert_allclose(np.abs(lr[0]), 50.0 / 16.0, rtol=1e-7)
+
+
+def test_rtn_rows_is_the_token_quantiser_per_row():
+    """Per-row RTN equals the QAW quantiser applied to rows: codes within +-127, each
+    non-zero row reaches 127, reconstruction error within half a step."""
+    x = RNG.standard_normal((6, 33)).astype(np.float32) * np.float32(3.0)
+    x[2] = 0
+    q, s = oracle.rtn_rows(x)
+    assert q.dtype == np.int8 and np.all(np.abs(q.astype(int)) <= 127)
+    for i in range(6):
+        if i == 2:
+            assert s[i] == 0 and np.all(q[i] == 0)
+        else:
+            assert np.abs(q[i].astype(int)).max() == 127
+            assert np.all(np.abs(q[i].astype(np.float32) * s[i] - x[i]) <= s[i] / 2 * (1 + 1e-6))
