@@ -146,6 +146,16 @@ def secondary(lrc, torch, dev):
         out[f"rank_scores_{mode}"] = {"workload": f"{n_mat * per} components ({n_mat} matrices)",
                                       "ms": round(t * 1e3, 3), "GB/s": round(byt / t / 1e9, 1)}
     del sig, offs, wgt
+    # factor codec at the attention projection's rank-1024 factors
+    left = torch.randn(d, 1024, generator=g, device=dev)
+    right = torch.randn(1024, d, generator=g, device=dev)
+    signs = torch.randint(0, 2, (1024,), generator=g, device=dev).float() * 2 - 1
+    lrc.lrc_rotate_quantize(left, right, signs)
+    t = _time(lambda: lrc.lrc_rotate_quantize(left, right, signs), torch, 5)
+    byt = 5.0 * 2 * d * 1024   # fp32 factors in, int8 codes out
+    out["rotate_quantize"] = {"workload": f"left {d}x1024, right 1024x{d} fp32 -> int8", "ms": round(t * 1e3, 3),
+                              "GB/s": round(byt / t / 1e9, 1), "hbm_frac": round(byt / t / 1e9 / HBM_PEAK_GBS, 4)}
+    del left, right, signs
     for m_items, label in ((917504, "decoder stack: 224 matrices"), (64 * 1024 * 1024, "scaled pool")):
         n_mat = 224 if m_items == 917504 else 16384
         per = m_items // n_mat

@@ -19,7 +19,7 @@ __all__ = [
     "LRC_ENOCONV", "LRC_ENONFINITE", "LRC_F32", "LRC_BF16", "LRC_COV_QUANT_INT8_TOKEN",
     "LRC_SCORE_FISHER", "LRC_SCORE_KFAC", "LRC_RANKSCORE_UNIRANK", "LRC_RANKSCORE_SWIFT", "LrcError", "lib",
     "library_path", "lrc_accumulate_cov", "lrc_whiten_decompose", "lrc_score_components", "lrc_allocate_ranks",
-    "lrc_rank_scores",
+    "lrc_rank_scores", "lrc_rotate_quantize", "lrc_quantize_rows",
     "lrc_status_string", "lrc_profile_start", "lrc_profile_stop", "lrc_profile_kernels",
 ]
 
@@ -48,6 +48,9 @@ _SIGS = {
     "lrc_allocate_ranks": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "lrc_allocate_ranks_workspace": (_sz, [_i64, _i64]),
     "lrc_rank_scores": (_i32, [_vp, _vp, _i64, _i64, _vp, ctypes.c_float, _u32, _vp, _vp, _vp]),
+    "lrc_rotate_quantize": (_i32, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "lrc_rotate_quantize_workspace": (_sz, [_i64, _i64, _i64]),
+    "lrc_quantize_rows": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "lrc_status_string": (ctypes.c_char_p, [_i32]),
     "lrc_last_hip_error": (_i32, []),
     "lrc_profile_start": (_i32, []),
@@ -266,6 +269,48 @@ def lrc_rank_scores(sigma: torch.Tensor, offsets: torch.Tensor, weight: torch.Te
                                _ptr(weight.contiguous()), float(alpha), flag, _ptr(scores), _ptr(info), _stream()),
            "lrc_rank_scores")
     return scores, info
+
+
+def lrc_rotate_quantize(left: torch.Tensor, right: torch.Tensor, signs: torch.Tensor, keep_rotated: bool = False):
+    """Rotate the factors by a sign-randomised Hadamard matrix and quantise each row to
+    int8.  left: (d_out, r) fp32, right: (r, d_in) fp32, signs: (r,) fp32 of +-1.
+
+    Returns (q_left int8, s_left fp32, q_right int8, s_right fp32) and, with
+    keep_rotated, the rotated fp32 factors as two more entries."""
+    for t, nm in ((left, "left"), (right, "right"), (signs, "signs")):
+        _dev(t, nm)
+        if t.dtype != torch.float32:
+            raise ValueError(f"{nm} must be fp32")
+    d_out, r = left.shape
+    if right.shape[0] != r or signs.numel() != r:
+        raise ValueError("left (d_out, r), right (r, d_in), signs (r,)")
+    d_in = right.shape[1]
+    dev = left.device
+    ql = torch.empty(d_out, r, dtype=torch.int8, device=dev)
+    sl = torch.empty(d_out, dtype=torch.float32, device=dev)
+    qr = torch.empty(r, d_in, dtype=torch.int8, device=dev)
+    sr = torch.empty(r, dtype=torch.float32, device=dev)
+    lrot = torch.empty(d_out, r, dtype=torch.float32, device=dev) if keep_rotated else None
+    rrot = torch.empty(r, d_in, dtype=torch.float32, device=dev) if keep_rotated else None
+    ws = _workspace(lib.lrc_rotate_quantize_workspace(d_out, r, d_in), dev)
+    _check(lib.lrc_rotate_quantize(_ptr(left.contiguous()), _ptr(right.contiguous()), d_out, r, d_in,
+                                   _ptr(signs.contiguous()), _ptr(ql), _ptr(sl), _ptr(qr), _ptr(sr),
+                                   _ptr(lrot) if keep_rotated else None, _ptr(rrot) if keep_rotated else None,
+                                   _ptr(ws), ws.numel(), _stream()), "lrc_rotate_quantize")
+    return (ql, sl, qr, sr, lrot, rrot) if keep_rotated else (ql, sl, qr, sr)
+
+
+def lrc_quantize_rows(x: torch.Tensor):
+    """Per-row int8 RTN of an fp32 matrix (rows, cols).  Returns (q int8, scale fp32 (rows,))."""
+    _dev(x, "x")
+    if x.dtype != torch.float32 or x.dim() != 2:
+        raise ValueError("x must be a 2-D fp32 tensor")
+    x = x.contiguous()
+    rows, cols = x.shape
+    q = torch.empty(rows, cols, dtype=torch.int8, device=x.device)
+    s = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _check(lib.lrc_quantize_rows(_ptr(x), rows, cols, cols, _ptr(q), _ptr(s), _stream()), "lrc_quantize_rows")
+    return q, s
 
 
 def lrc_profile_start() -> None:

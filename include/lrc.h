@@ -206,6 +206,36 @@ lrc_status lrc_rank_scores(const float* sigma, const int64_t* offsets, int64_t n
                            void* stream);
 
 /*
+ * lrc_rotate_quantize -- factor codec after the back-map.
+ * LASER section 3 (Hybrid SVD-Quantization for FFNs), item Quantization: an orthogonal
+ * rotation between the low-rank factors smooths outliers, then both factors are quantised
+ * round-to-nearest.  With R = H_r diag(signs) / sqrt(r) (H_r the Sylvester Hadamard
+ * matrix; r a power of two, r <= 8192; signs: r floats, each +1 or -1, chosen by the
+ * caller), left' = left R (d_out x r) and right' = R^T right (r x d_in), so their product
+ * is unchanged.  The rotation runs in fp64 and is rounded once to fp32; each row of left'
+ * and of right' is then quantised with its own scale:
+ *   scale = fl32(max|row| / 127), q = clamp(round_half_even(fl32(x / scale)), -127, 127)
+ *   (an all-zero row gives codes 0 and scale 0).
+ * left: d_out x r (leading dim r), right: r x d_in (leading dim d_in), fp32 (as written by
+ *   lrc_whiten_decompose).  Outputs (device): q_left int8 d_out x r, s_left float[d_out],
+ *   q_right int8 r x d_in, s_right float[r]; left_rot / right_rot (fp32, same shapes) may be
+ *   NULL or receive the rotated factors.
+ */
+lrc_status lrc_rotate_quantize(const float* left, const float* right, int64_t d_out, int64_t r, int64_t d_in,
+                               const float* signs, int8_t* q_left, float* s_left, int8_t* q_right,
+                               float* s_right, float* left_rot, float* right_rot, void* ws, size_t ws_bytes,
+                               void* stream);
+size_t lrc_rotate_quantize_workspace(int64_t d_out, int64_t r, int64_t d_in);
+
+/*
+ * lrc_quantize_rows -- the same per-row int8 RTN for a dense branch (LASER section 3: the
+ * channels kept dense are quantised as well).  X: rows x cols fp32 (leading dim ldx);
+ * q: int8 rows x cols (leading dim cols); scale: float[rows].
+ */
+lrc_status lrc_quantize_rows(const float* X, int64_t rows, int64_t cols, int64_t ldx, int8_t* q, float* scale,
+                             void* stream);
+
+/*
  * Measurement support (benchmarks and profilers; not needed for results).
  * Between lrc_profile_start and lrc_profile_stop every launch of an instrumented kernel
  * is bracketed by two HIP events recorded on the stream it runs on, and the work it

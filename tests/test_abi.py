@@ -113,6 +113,31 @@ def test_rank_scores_validation(lib):
     assert f(None, FAKE, 2, 10, FAKE, 0.5, 0x1, FAKE, FAKE, None) == EINVAL     # sigma null
 
 
+def test_rotate_quantize_validation(lib):
+    f = lib.lrc_rotate_quantize
+    args = [FAKE, FAKE, 8, 4, 6, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 30, None]
+
+    def call(**over):
+        a = list(args)
+        for i, v in over.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    assert call(a3=6) == EINVAL          # r not a power of two
+    assert call(a3=0) == EINVAL
+    assert call(a3=16384) == EINVAL      # r above the LDS row
+    assert call(a2=0) == EINVAL          # d_out
+    assert call(a4=-1) == EINVAL         # d_in
+    assert call(a5=None) == EINVAL       # signs
+    assert call(a6=None) == EINVAL       # q_left
+    need = lib.lrc_rotate_quantize_workspace(8, 4, 6)
+    assert need > 0 and call(a13=need - 1) == EWORKSPACE
+    g = lib.lrc_quantize_rows
+    assert g(FAKE, 4, 8, 7, FAKE, FAKE, None) == EINVAL   # ldx < cols
+    assert g(FAKE, 0, 8, 8, FAKE, FAKE, None) == EINVAL
+    assert g(None, 4, 8, 8, FAKE, FAKE, None) == EINVAL
+
+
 def test_profile_session_without_work(lib):
     # no kernel launched: the session records nothing and out-of-range queries fail
     assert lib.lrc_profile_start() == 0

@@ -543,3 +543,41 @@ def test_rank_scores_reject_bad_inputs(lrc):
                                   torch.tensor([1.0], device=dev()))
     assert int(info[0]) == lrc.LRC_EINVAL
 
+
+# ----------------------------------------------------------------------------- factor codec
+@pytest.mark.parametrize("d_out,r,d_in", [(96, 64, 40), (300, 1024, 257), (5, 1, 3), (64, 2048, 128)])
+def test_rotate_quantize(lrc, d_out, r, d_in):
+    """The rotated factors are the fp64 products rounded once to fp32: they match the
+    oracle's within one fp32 rounding (the two sides sum in different orders).  The int8
+    codes and scales are a decision taken in fp32 on those values, so they are checked bit
+    for bit against the oracle's quantiser applied to the GPU's own rotated factors.
+    The shapes include an outlier channel, r = 1 and ragged d_out / d_in."""
+    g = torch.Generator().manual_seed(r + d_in)
+    left = torch.randn(d_out, r, generator=g)
+    left[:, r // 3] *= 40.0      # an outlier channel, the case the rotation is for
+    right = torch.randn(r, d_in, generator=g)
+    signs = (torch.randint(0, 2, (r,), generator=g) * 2 - 1).float()
+    ql, sl, qr, sr, lrot, rrot = lrc.lrc_rotate_quantize(left.to(dev()), right.to(dev()), signs.to(dev()),
+                                                          keep_rotated=True)
+    ref_l, ref_r = oracle.rotate_factors(left.numpy(), right.numpy(), signs.numpy())
+    np.testing.assert_allclose(to_np(lrot), ref_l, rtol=2.4e-7, atol=1e-30)
+    np.testing.assert_allclose(to_np(rrot), ref_r, rtol=2.4e-7, atol=1e-30)
+    for q, s, rot in ((ql, sl, lrot), (qr, sr, rrot)):
+        oq, os_ = oracle.rtn_rows(to_np(rot))
+        assert np.array_equal(to_np(q), oq) and np.array_equal(to_np(s), os_)
+    # the rotation spreads the outlier: left's largest magnitude falls
+    if r > 1:
+        assert np.abs(to_np(lrot)).max() < np.abs(left.numpy()).max()
+
+
+def test_quantize_rows_bit_exact(lrc):
+    """Dense branch: per-row RTN of the input itself, bit for bit with the oracle (ties
+    to even and an all-zero row included)."""
+    x = torch.randn(70, 333, generator=torch.Generator().manual_seed(5)) * 3
+    x[4] = 0
+    x[7, :4] = torch.tensor([127.0, 0.5, 1.5, -2.5])   # scale 1: exact halves round to even
+    x[7, 4:] = 0
+    q, s = lrc.lrc_quantize_rows(x.to(dev()))
+    oq, os_ = oracle.rtn_rows(x.numpy())
+    assert np.array_equal(to_np(q), oq) and np.array_equal(to_np(s), os_)
+
