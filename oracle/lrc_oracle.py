@@ -8,7 +8,8 @@ fast: numpy/scipy (LAPACK) in fp64, one step per function, in the pages' order.
 Pages (gist.science explainers; the alternative scorers at the end also cite UniRank
 2.1 "Local Structural Significance" / "Global Functional Importance" and Swift-SVD
 section B "Dynamic Rank Allocation Strategy", item "Hybrid Scoring"; the factor codec
-cites LASER section 3 "Hybrid SVD-Quantization for FFNs", item "Quantization"):
+cites LASER section 3 "Hybrid SVD-Quantization for FFNs", item "Quantization", and the
+low-rank FFN forward cites LASER section 4 "System Implementation"):
   * LASER: Loss-Aware Singular-value Decomposition and Rank Allocation for Efficient
     Low-Precision Vision-Language Models (technical summary, Methodology 1 "loss-aware
     SVD" with the items K-FAC surrogate / Transformation / QAW, Methodology 2
@@ -40,6 +41,7 @@ __all__ = [
     "truncated_svd", "canonical_signs", "back_map", "whiten_decompose",
     "fisher_scores", "kfac_scores", "allocation_keys", "allocate", "kfac_loss",
     "unirank_scores", "swift_layer_scores", "hadamard_rotation", "rotate_factors", "rtn_rows",
+    "silu", "lowrank_ffn",
 ]
 
 
@@ -356,4 +358,34 @@ def rtn_rows(x):
     with scale 0.  Returns (q int8, scale float32)."""
     q, s, _ = qaw_fake_quant(np.asarray(x, dtype=np.float32))
     return q, s
+
+
+# ---------------------------------------------------------------------------
+# low-rank FFN forward (LASER, 4. System Implementation)
+# ---------------------------------------------------------------------------
+def silu(z):
+    """SiLU(z) = z / (1 + exp(-z)), the gate nonlinearity of the SwiGLU FFN."""
+    z = np.asarray(z, dtype=np.float64)
+    return z / (1.0 + np.exp(-z))
+
+
+def lowrank_ffn(x, gate, up, down):
+    """Forward pass of a SwiGLU FFN whose three weights are replaced by their low-rank
+    factors, as the pages' fused decode kernels run it: the input projection to the
+    latent space, the latent-to-hidden expansion, SwiGLU, and the down projection,
+    with the int8 factors dequantised on the fly.  The reading: y = W_down (SiLU(W_gate x)
+    * (W_up x)) with W ~ L R for each of gate, up, down; every factor is int8 with one
+    scale per row, L = q_L * s_L[:, None], R = q_R * s_R[:, None].
+    x: n_tok x d.  gate, up: (q_R (r x d), s_R, q_L (d_ff x r), s_L); down: (q_R
+    (r_d x d_ff), s_R, q_L (d x r_d), s_L).  Returns y: n_tok x d in fp64."""
+    def deq(q, sc):
+        return np.asarray(q, dtype=np.float64) * np.asarray(sc, dtype=np.float64)[:, None]
+
+    def apply(f, v):
+        q_r, s_r, q_l, s_l = f
+        return (v @ deq(q_r, s_r).T) @ deq(q_l, s_l).T
+
+    xv = np.asarray(x, dtype=np.float64)
+    h = silu(apply(gate, xv)) * apply(up, xv)
+    return apply(down, h)
 

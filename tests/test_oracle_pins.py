@@ -5,6 +5,7 @@ construction or a hand-derived fixture (tests/golden/), chosen so that a plausib
 slip (a transposed factor, a dropped 1/2, a wrong vec order, a wrong tie-break) fails.
 """
 import itertools
+import math
 
 import numpy as np
 import pytest
@@ -393,3 +394,44 @@ def test_rtn_rows_is_the_token_quantiser_per_row():
         else:
             assert np.abs(q[i].astype(int)).max() == 127
             assert np.all(np.abs(q[i].astype(np.float32) * s[i] - x[i]) <= s[i] / 2 * (1 + 1e-6))
+
+
+# ----------------------------------------------------------------------------- low-rank FFN
+def _int8_factor(rng, rows, cols):
+    return rng.integers(-127, 128, (rows, cols)).astype(np.int8), rng.uniform(0.001, 0.02, rows).astype(np.float32)
+
+
+def test_lowrank_ffn_golden():
+    y = np.array(read_golden("lowrank_ffn.txt")[0].split(":")[1].split(), float)
+    half = np.array([0.5], np.float32)
+    gate = (np.array([[2, 4]], np.int8), half, np.array([[2], [0]], np.int8), np.array([0.5, 0.5], np.float32))
+    up = (np.array([[2, 0]], np.int8), half, np.array([[2], [2]], np.int8), np.array([0.5, 0.5], np.float32))
+    down = (np.array([[2, 2]], np.int8), half, np.array([[2], [4]], np.int8), np.array([0.5, 0.5], np.float32))
+    np.testing.assert_allclose(oracle.lowrank_ffn(np.ones((1, 2)), gate, up, down)[0], y, rtol=1e-12)
+
+
+def test_lowrank_ffn_equals_the_dense_ffn_of_the_product():
+    """With each weight built explicitly as L R, the factored forward equals the dense
+    SwiGLU FFN y = W_down (SiLU(W_gate x) * W_up x), evaluated here elementwise."""
+    rng = np.random.default_rng(4)
+    d, dff, r = 12, 20, 5
+    g = (*_int8_factor(rng, r, d), *_int8_factor(rng, dff, r))
+    u = (*_int8_factor(rng, r, d), *_int8_factor(rng, dff, r))
+    dn = (*_int8_factor(rng, r, dff), *_int8_factor(rng, d, r))
+
+    def dense(f):
+        return (f[2].astype(np.float64) * f[3][:, None]) @ (f[0].astype(np.float64) * f[1][:, None])
+
+    wg, wu, wd = dense(g), dense(u), dense(dn)
+    x = rng.standard_normal((3, d))
+    want = np.zeros((3, d))
+    for t in range(3):
+        zg, zu = wg @ x[t], wu @ x[t]
+        h = np.array([z / (1.0 + math.exp(-z)) * v for z, v in zip(zg, zu)])
+        want[t] = wd @ h
+    np.testing.assert_allclose(oracle.lowrank_ffn(x, g, u, dn), want, rtol=1e-12, atol=1e-12)
+
+
+def test_silu_values():
+    np.testing.assert_allclose(oracle.silu([0.0, 1.0, -1.0, 30.0]),
+                               [0.0, 0.7310585786300049, -0.2689414213699951, 30.0], rtol=1e-12)
