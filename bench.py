@@ -156,6 +156,26 @@ def secondary(lrc, torch, dev):
     out["rotate_quantize"] = {"workload": f"left {d}x1024, right 1024x{d} fp32 -> int8", "ms": round(t * 1e3, 3),
                               "GB/s": round(byt / t / 1e9, 1), "hbm_frac": round(byt / t / 1e9 / HBM_PEAK_GBS, 4)}
     del left, right, signs
+    # decode-time low-rank FFN (hidden 4096, FFN 11008, every rank 2048, int8 factors)
+    dff, rk = 11008, 2048
+
+    def fac(rows, cols):
+        return (torch.randint(-127, 128, (rows, cols), generator=g, device=dev, dtype=torch.int8),
+                torch.rand(rows, generator=g, device=dev) * 0.004 + 0.001)
+
+    gate = (*fac(rk, d), *fac(dff, rk))
+    up = (*fac(rk, d), *fac(dff, rk))
+    down = (*fac(dff, rk), *fac(d, rk))   # R_down stored transposed (d_ff x r)
+    fbytes = 2.0 * rk * d + 2.0 * dff * rk + dff * rk + d * rk
+    for nt in (1, 8):
+        xin = torch.randn(nt, d, generator=g, device=dev)
+        lrc.lrc_lowrank_ffn(xin, gate, up, down)
+        t = _time(lambda: lrc.lrc_lowrank_ffn(xin, gate, up, down), torch, 10)
+        out[f"lowrank_ffn_decode_{nt}tok"] = {"workload": f"{nt} tokens, 4096 -> 11008 -> 4096, ranks 2048, int8",
+                                             "us": round(t * 1e6, 1), "tokens_per_s": round(nt / t, 1),
+                                             "GB/s": round(fbytes / t / 1e9, 1),
+                                             "hbm_frac": round(fbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+    del gate, up, down
     for m_items, label in ((917504, "decoder stack: 224 matrices"), (64 * 1024 * 1024, "scaled pool")):
         n_mat = 224 if m_items == 917504 else 16384
         per = m_items // n_mat

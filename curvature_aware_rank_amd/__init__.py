@@ -19,7 +19,7 @@ __all__ = [
     "LRC_ENOCONV", "LRC_ENONFINITE", "LRC_F32", "LRC_BF16", "LRC_COV_QUANT_INT8_TOKEN",
     "LRC_SCORE_FISHER", "LRC_SCORE_KFAC", "LRC_RANKSCORE_UNIRANK", "LRC_RANKSCORE_SWIFT", "LrcError", "lib",
     "library_path", "lrc_accumulate_cov", "lrc_whiten_decompose", "lrc_score_components", "lrc_allocate_ranks",
-    "lrc_rank_scores", "lrc_rotate_quantize", "lrc_quantize_rows",
+    "lrc_rank_scores", "lrc_rotate_quantize", "lrc_quantize_rows", "lrc_lowrank_ffn",
     "lrc_status_string", "lrc_profile_start", "lrc_profile_stop", "lrc_profile_kernels",
 ]
 
@@ -51,6 +51,9 @@ _SIGS = {
     "lrc_rotate_quantize": (_i32, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "lrc_rotate_quantize_workspace": (_sz, [_i64, _i64, _i64]),
     "lrc_quantize_rows": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "lrc_lowrank_ffn": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i64,
+                               _vp, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
+    "lrc_lowrank_ffn_workspace": (_sz, [_i64, _i64, _i64, _i64, _i64]),
     "lrc_status_string": (ctypes.c_char_p, [_i32]),
     "lrc_last_hip_error": (_i32, []),
     "lrc_profile_start": (_i32, []),
@@ -311,6 +314,31 @@ def lrc_quantize_rows(x: torch.Tensor):
     s = torch.empty(rows, dtype=torch.float32, device=x.device)
     _check(lib.lrc_quantize_rows(_ptr(x), rows, cols, cols, _ptr(q), _ptr(s), _stream()), "lrc_quantize_rows")
     return q, s
+
+
+def lrc_lowrank_ffn(x: torch.Tensor, gate, up, down):
+    """Low-rank SwiGLU FFN forward with int8 factors.  x: (n_tok, d) fp32.
+    gate, up: (q_R (r, d) int8, s_R (r,), q_L (d_ff, r) int8, s_L (d_ff,)).
+    down: (q_Rt (d_ff, r_d) int8 -- R_down transposed, s_R (r_d,), q_L (d, r_d) int8, s_L (d,)).
+    Returns y (n_tok, d) fp32."""
+    tens = [x, *gate, *up, *down]
+    for t in tens:
+        _dev(t, "ffn operand")
+    n_tok, d = x.shape
+    d_ff, rg = gate[2].shape
+    ru = up[2].shape[1]
+    rd = down[2].shape[1]
+    x = x.contiguous()
+    gate = [t.contiguous() for t in gate]
+    up = [t.contiguous() for t in up]
+    down = [t.contiguous() for t in down]
+    y = torch.empty(n_tok, d, dtype=torch.float32, device=x.device)
+    ws = _workspace(lib.lrc_lowrank_ffn_workspace(n_tok, d_ff, rg, ru, rd), x.device)
+    _check(lib.lrc_lowrank_ffn(_ptr(x), n_tok, d, d_ff, _ptr(gate[0]), _ptr(gate[1]), _ptr(gate[2]), _ptr(gate[3]), rg,
+                               _ptr(up[0]), _ptr(up[1]), _ptr(up[2]), _ptr(up[3]), ru, _ptr(down[0]), _ptr(down[1]),
+                               _ptr(down[2]), _ptr(down[3]), rd, _ptr(y), _ptr(ws), ws.numel(), _stream()),
+           "lrc_lowrank_ffn")
+    return y
 
 
 def lrc_profile_start() -> None:

@@ -121,6 +121,9 @@ extern "C" lrc_status lrc_rotate_quantize(const float* left, const float* right,
   float* rr = right_rot != nullptr ? right_rot : cv.take<float>(size_t(r * d_in));
   ProfScope scope("rot_rows_kernel", st, 0.0, 4.0 * double(d_out + d_in) * double(r) * 2.0);
   const size_t lds = size_t(r) * sizeof(double);
+  if (lds > 48 * 1024)
+    LRC_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&rot_rows_kernel),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)));
   rot_rows_kernel<<<unsigned(d_out), CT, lds, st>>>(left, r, int(r), signs, left_rot, q_left, s_left);
   LRC_LAUNCHED();
   LRC_TRY(transpose_f32(st, right, d_in, rt, r, r, d_in));

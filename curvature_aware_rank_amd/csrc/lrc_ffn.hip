@@ -1,0 +1,307 @@
+// Decode-time low-rank SwiGLU FFN with int8 factors.
+//
+// LASER technical summary, 4 (System Implementation): the low-rank FFN runs as fused
+// kernels covering the input projection, the latent activations, SwiGLU and the
+// quantisation/dequantisation steps, to cut memory movement and launches.  Reading:
+// y = W_down (SiLU(W_gate x) * (W_up x)) with every W replaced by its factors L R, each an
+// int8 matrix with one fp32 scale per row (as lrc_rotate_quantize writes them; a rotation
+// between the factors leaves the product unchanged).  Activations and sums are fp32.
+//
+// Four launches per call, each reading its int8 factors once, in 16-byte rows pieces:
+//   1. latent_g = R_gate x, latent_u = R_up x         (one wave per latent row)
+//   2. for a chunk of hidden channels: expand both latents (rows of L_gate, L_up),
+//      h = SiLU(gate) * up in LDS, and its share of R_down h (rows of R_down^T), written
+//      as per-chunk partial latents
+//   3. latent_d = sum of the partials in chunk order, times R_down's row scales
+//   4. y = L_down latent_d                              (one wave per output row)
+// Tokens are handled TG at a time so every weight piece is dequantised once per group.
+#include "lrc_internal.h"
+
+namespace lrc {
+namespace {
+
+constexpr int FT = 256;      // threads per workgroup
+constexpr int TG = 4;        // tokens per group
+constexpr int HC = 256;      // hidden-channel chunks (workgroups of the expansion kernel)
+
+__device__ __forceinline__ float wave_sumf(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ void unpack16(uint4 w, float (&f)[16]) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) f[i] = float(int8_t(uint8_t(u[i >> 2] >> (8 * (i & 3)))));
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// out[t][row] = scale[row] * (q[row] . v[t]) for the rows of one or two int8 matrices
+// (rows0 rows of q0, then rows1 rows of q1; each row n int8, n % 16 == 0); one wave per row
+__global__ __launch_bounds__(FT) void rows_gemv_kernel(const int8_t* __restrict__ q0, const float* __restrict__ s0,
+                                                       int rows0, const int8_t* __restrict__ q1,
+                                                       const float* __restrict__ s1, int rows1, int n,
+                                                       const float* __restrict__ v, int n_tok,
+                                                       float* __restrict__ out0, float* __restrict__ out1) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * (FT / 64) + (threadIdx.x >> 6);
+  if (row >= rows0 + rows1) return;
+  const bool first = row < rows0;
+  const int r = first ? row : row - rows0;
+  const int8_t* q = (first ? q0 : q1) + int64_t(r) * n;
+  const float sc = first ? s0[r] : s1[r];
+  float* out = first ? out0 : out1;
+  const int ld_out = first ? rows0 : rows1;
+  for (int t0 = 0; t0 < n_tok; t0 += TG) {
+    float acc[TG] = {0.f, 0.f, 0.f, 0.f};
+    for (int j0 = lane * 16; j0 < n; j0 += 64 * 16) {
+      float w[16];
+      unpack16(*reinterpret_cast<const uint4*>(q + j0), w);
+#pragma unroll
+      for (int t = 0; t < TG; ++t) {
+        if (t0 + t < n_tok) {
+          const float4* x = reinterpret_cast<const float4*>(v + int64_t(t0 + t) * n + j0);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float4 xv = x[c];
+            acc[t] += w[4 * c] * xv.x + w[4 * c + 1] * xv.y + w[4 * c + 2] * xv.z + w[4 * c + 3] * xv.w;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < TG; ++t) {
+      const float a = wave_sumf(acc[t]);
+      if (lane == 0 && t0 + t < n_tok) out[int64_t(t0 + t) * ld_out + r] = sc * a;
+    }
+  }
+}
+
+// Hidden channels [b J, b J + J): gate/up expansion, SwiGLU, and the chunk's partial of
+// R_down h: pd[b][t][k] = sum_j q_rdt[j][k] h[t][j] (R_down's row scales come later).
+__global__ __launch_bounds__(FT) void swiglu_down_kernel(const int8_t* __restrict__ qlg, const float* __restrict__ slg,
+                                                         const int8_t* __restrict__ qlu, const float* __restrict__ slu,
+                                                         int rg, int ru, const float* __restrict__ latg,
+                                                         const float* __restrict__ latu,
+                                                         const int8_t* __restrict__ qrdt, int rd, int d_ff, int J,
+                                                         int n_tok, float* __restrict__ pd) {
+  extern __shared__ float sh[];
+  float* lg = sh;                 // [TG][rg]
+  float* lu = lg + TG * rg;       // [TG][ru]
+  float* hh = lu + TG * ru;       // [TG][J]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j0 = blockIdx.x * J;
+  const int jn = min(J, d_ff - j0);
+  for (int t0 = 0; t0 < n_tok; t0 += TG) {
+    const int nt = min(TG, n_tok - t0);
+    __syncthreads();
+    for (int i = tid; i < TG * rg; i += FT) {
+      const int t = i / rg, k = i % rg;
+      lg[i] = t < nt ? latg[int64_t(t0 + t) * rg + k] : 0.f;
+    }
+    for (int i = tid; i < TG * ru; i += FT) {
+      const int t = i / ru, k = i % ru;
+      lu[i] = t < nt ? latu[int64_t(t0 + t) * ru + k] : 0.f;
+    }
+    __syncthreads();
+    // expansion: a wave takes four hidden rows at a time, 16 lanes per row (lanes split
+    // the latent index), every weight load of the four rows issued before any use
+    const int sub = lane >> 4, sl = lane & 15;
+    for (int jb = wave * 4; jb < jn; jb += FT / 16) {
+      const int jj = jb + sub;
+      const int j = j0 + min(jj, jn - 1);
+      float g[TG] = {0.f, 0.f, 0.f, 0.f}, u[TG] = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = sl * 16; k0 < rg; k0 += 16 * 16 * 4) {
+        uint4 wq[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int k = min(k0 + c * 256, rg - 16);
+          wq[c] = *reinterpret_cast<const uint4*>(qlg + int64_t(j) * rg + k);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int k = k0 + c * 256;
+          if (k < rg) {
+            float w[16];
+            unpack16(wq[c], w);
+#pragma unroll
+            for (int t = 0; t < TG; ++t)
+              if (t < nt)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) g[t] += w[e] * lg[t * rg + k + e];
+          }
+        }
+      }
+      for (int k0 = sl * 16; k0 < ru; k0 += 16 * 16 * 4) {
+        uint4 wq[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int k = min(k0 + c * 256, ru - 16);
+          wq[c] = *reinterpret_cast<const uint4*>(qlu + int64_t(j) * ru + k);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int k = k0 + c * 256;
+          if (k < ru) {
+            float w[16];
+            unpack16(wq[c], w);
+#pragma unroll
+            for (int t = 0; t < TG; ++t)
+              if (t < nt)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) u[t] += w[e] * lu[t * ru + k + e];
+          }
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < TG; ++t) {
+        float gs = g[t], us = u[t];
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) {   // sum over the row's 16 lanes
+          gs += __shfl_xor(gs, o);
+          us += __shfl_xor(us, o);
+        }
+        if (sl == 0 && jj < jn) hh[t * J + jj] = silu(slg[j] * gs) * (slu[j] * us);
+      }
+    }
+    __syncthreads();
+    for (int kb = tid * 8; kb < rd; kb += FT * 8) {
+      float acc[TG][8];
+#pragma unroll
+      for (int t = 0; t < TG; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[t][e] = 0.f;
+      for (int jb = 0; jb < jn; jb += 8) {
+        uint2 w8[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          w8[c] = *reinterpret_cast<const uint2*>(qrdt + int64_t(j0 + min(jb + c, jn - 1)) * rd + kb);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          if (jb + c < jn) {
+            const uint32_t wu[2] = {w8[c].x, w8[c].y};
+            float w[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w[e] = float(int8_t(uint8_t(wu[e >> 2] >> (8 * (e & 3)))));
+#pragma unroll
+            for (int t = 0; t < TG; ++t) {
+              if (t < nt) {
+                const float hv = hh[t * J + jb + c];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[t][e] += w[e] * hv;
+              }
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < TG; ++t) {
+        if (t < nt) {
+          float4* dst = reinterpret_cast<float4*>(pd + (int64_t(blockIdx.x) * n_tok + t0 + t) * rd + kb);
+          dst[0] = make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+          dst[1] = make_float4(acc[t][4], acc[t][5], acc[t][6], acc[t][7]);
+        }
+      }
+    }
+  }
+}
+
+// latent_d[t][k] = s_rd[k] * sum over chunks b of pd[b][t][k]: four threads per output,
+// each summing a quarter of the chunks in order (16 loads in flight), quarters added in
+// order
+__global__ __launch_bounds__(FT) void latent_reduce_kernel(const float* __restrict__ pd, int nb, int n_tok, int rd,
+                                                           const float* __restrict__ srd, float* __restrict__ latd) {
+  __shared__ float part[4][FT / 4];
+  const int qtr = threadIdx.x >> 6, o = threadIdx.x & 63;
+  const int64_t i = int64_t(blockIdx.x) * (FT / 4) + o;
+  const int64_t tot = int64_t(n_tok) * rd;
+  const int64_t ic = min(i, tot - 1);
+  const int per = (nb + 3) / 4, b0 = qtr * per, b1 = min(nb, b0 + per);
+  float s = 0.f;
+  for (int b = b0; b < b1; b += 16) {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = pd[int64_t(min(b + u, b1 - 1)) * tot + ic];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) s += b + u < b1 ? v[u] : 0.f;
+  }
+  part[qtr][o] = s;
+  __syncthreads();
+  if (qtr == 0 && i < tot) latd[i] = srd[int(i % rd)] * (((part[0][o] + part[1][o]) + part[2][o]) + part[3][o]);
+}
+
+}  // namespace
+}  // namespace lrc
+
+using namespace lrc;
+
+namespace {
+struct FfnWs {
+  float *latg, *latu, *pd, *latd;
+};
+FfnWs carve_ffn(Carve& cv, int64_t n_tok, int64_t rg, int64_t ru, int64_t rd, int64_t nb) {
+  FfnWs w;
+  w.latg = cv.take<float>(size_t(n_tok * rg));
+  w.latu = cv.take<float>(size_t(n_tok * ru));
+  w.pd = cv.take<float>(size_t(nb * n_tok * rd));
+  w.latd = cv.take<float>(size_t(n_tok * rd));
+  return w;
+}
+int64_t ffn_chunk(int64_t d_ff) { return cdiv(d_ff, HC); }
+}  // namespace
+
+extern "C" size_t lrc_lowrank_ffn_workspace(int64_t n_tok, int64_t d_ff, int64_t rg, int64_t ru, int64_t rd) {
+  if (n_tok <= 0 || d_ff <= 0 || rg <= 0 || ru <= 0 || rd <= 0) return 0;
+  Carve cv(nullptr);
+  carve_ffn(cv, n_tok, rg, ru, rd, cdiv(d_ff, ffn_chunk(d_ff)));
+  return cv.bytes();
+}
+
+extern "C" lrc_status lrc_lowrank_ffn(const float* x, int64_t n_tok, int64_t d, int64_t d_ff, const int8_t* q_rg,
+                                      const float* s_rg, const int8_t* q_lg, const float* s_lg, int64_t rg,
+                                      const int8_t* q_ru, const float* s_ru, const int8_t* q_lu, const float* s_lu,
+                                      int64_t ru, const int8_t* q_rdt, const float* s_rd, const int8_t* q_ld,
+                                      const float* s_ld, int64_t rd, float* y, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  const void* ptrs[] = {x, q_rg, s_rg, q_lg, s_lg, q_ru, s_ru, q_lu, s_lu, q_rdt, s_rd, q_ld, s_ld, y};
+  for (const void* p : ptrs)
+    if (p == nullptr) return LRC_EINVAL;
+  // 16-byte pieces of every int8 row and of the activations
+  for (const void* p : {(const void*)x, (const void*)q_rg, (const void*)q_lg, (const void*)q_ru, (const void*)q_lu,
+                        (const void*)q_ld})
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return LRC_EINVAL;
+  if (reinterpret_cast<uintptr_t>(q_rdt) % 8 != 0) return LRC_EINVAL;
+  if (n_tok <= 0 || d <= 0 || d_ff <= 0 || rg <= 0 || ru <= 0 || rd <= 0) return LRC_EINVAL;
+  if (d % 16 || rg % 16 || ru % 16 || rd % 16) return LRC_EINVAL;
+  if (n_tok > (int64_t(1) << 20) || d > (int64_t(1) << 24) || d_ff > (int64_t(1) << 24)) return LRC_EINVAL;
+  const int64_t J = ffn_chunk(d_ff), nb = cdiv(d_ff, J);
+  const size_t lds = sizeof(float) * size_t(TG * (rg + ru) + TG * J);
+  if (lds > 160 * 1024) return LRC_EINVAL;   // both latents of a token group must fit in LDS
+  const size_t need = lrc_lowrank_ffn_workspace(n_tok, d_ff, rg, ru, rd);
+  if (ws == nullptr || ws_bytes < need) return LRC_EWORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // the expansion kernel's LDS (both latents of a token group) may exceed the default cap
+  if (lds > 64 * 1024)
+    LRC_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&swiglu_down_kernel),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)));
+  Carve cv(ws);
+  const FfnWs w = carve_ffn(cv, n_tok, rg, ru, rd, nb);
+  // bytes: every int8 factor once, the activations, the outputs
+  const double fb = double(rg + ru) * d + double(d_ff) * (rg + ru) + double(d_ff) * rd + double(d) * rd;
+  ProfScope scope("lowrank_ffn", st, 0.0, fb + 4.0 * double(n_tok) * 2 * d);
+  rows_gemv_kernel<<<unsigned(cdiv(rg + ru, FT / 64)), FT, 0, st>>>(q_rg, s_rg, int(rg), q_ru, s_ru, int(ru), int(d), x,
+                                                                   int(n_tok), w.latg, w.latu);
+  LRC_LAUNCHED();
+  swiglu_down_kernel<<<unsigned(nb), FT, lds, st>>>(q_lg, s_lg, q_lu, s_lu, int(rg), int(ru), w.latg, w.latu, q_rdt,
+                                                    int(rd), int(d_ff), int(J), int(n_tok), w.pd);
+  LRC_LAUNCHED();
+  latent_reduce_kernel<<<unsigned(cdiv(n_tok * rd, FT / 4)), FT, 0, st>>>(w.pd, int(nb), int(n_tok), int(rd), s_rd,
+                                                                          w.latd);
+  LRC_LAUNCHED();
+  rows_gemv_kernel<<<unsigned(cdiv(d, FT / 64)), FT, 0, st>>>(q_ld, s_ld, int(d), nullptr, nullptr, 0, int(rd), w.latd,
+                                                             int(n_tok), y, nullptr);
+  LRC_LAUNCHED();
+  return LRC_OK;
+}

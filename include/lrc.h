@@ -236,6 +236,28 @@ lrc_status lrc_quantize_rows(const float* X, int64_t rows, int64_t cols, int64_t
                              void* stream);
 
 /*
+ * lrc_lowrank_ffn -- decode-time forward of a SwiGLU FFN whose weights are replaced by
+ * int8 low-rank factors.
+ * LASER section 4 (System Implementation): the low-rank FFN runs as fused kernels for the
+ * input projection, the latent activations, SwiGLU and the dequantisation.  Computes
+ *   y = W_down (SiLU(W_gate x) * (W_up x)),  W = (q_L * s_L[:,None]) (q_R * s_R[:,None])
+ * for gate, up and down (one fp32 scale per factor row, as lrc_rotate_quantize writes).
+ * x: n_tok x d fp32 (16-byte aligned); y: n_tok x d fp32.
+ * gate: q_rg (rg x d int8), s_rg[rg], q_lg (d_ff x rg int8), s_lg[d_ff]; up likewise with ru.
+ * down: q_rdt = R_down^T (d_ff x rd int8: row j holds hidden channel j's latent weights),
+ *   s_rd[rd] (R_down's row scales), q_ld (d x rd int8), s_ld[d].
+ * d, rg, ru, rd multiples of 16; the int8 matrices 16-byte aligned (q_rdt 8-byte);
+ * 4 (rg + ru) floats of one token group must fit in LDS (rg + ru <= 8192).
+ * Activations and sums are fp32; the reduction order is fixed.
+ */
+lrc_status lrc_lowrank_ffn(const float* x, int64_t n_tok, int64_t d, int64_t d_ff, const int8_t* q_rg,
+                           const float* s_rg, const int8_t* q_lg, const float* s_lg, int64_t rg, const int8_t* q_ru,
+                           const float* s_ru, const int8_t* q_lu, const float* s_lu, int64_t ru, const int8_t* q_rdt,
+                           const float* s_rd, const int8_t* q_ld, const float* s_ld, int64_t rd, float* y, void* ws,
+                           size_t ws_bytes, void* stream);
+size_t lrc_lowrank_ffn_workspace(int64_t n_tok, int64_t d_ff, int64_t rg, int64_t ru, int64_t rd);
+
+/*
  * Measurement support (benchmarks and profilers; not needed for results).
  * Between lrc_profile_start and lrc_profile_stop every launch of an instrumented kernel
  * is bracketed by two HIP events recorded on the stream it runs on, and the work it

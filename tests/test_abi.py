@@ -138,6 +138,28 @@ def test_rotate_quantize_validation(lib):
     assert g(None, 4, 8, 8, FAKE, FAKE, None) == EINVAL
 
 
+def test_lowrank_ffn_validation(lib):
+    f = lib.lrc_lowrank_ffn
+    ok = [FAKE, 1, 64, 96, FAKE, FAKE, FAKE, FAKE, 32, FAKE, FAKE, FAKE, FAKE, 32, FAKE, FAKE, FAKE, FAKE, 32, FAKE,
+          FAKE, 1 << 30, None]
+
+    def call(**over):
+        a = list(ok)
+        for i, v in over.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    assert call(a0=None) == EINVAL          # x
+    assert call(a2=60) == EINVAL            # d not a multiple of 16
+    assert call(a8=20) == EINVAL            # rg not a multiple of 16
+    assert call(a18=0) == EINVAL            # rd
+    assert call(a1=0) == EINVAL             # n_tok
+    assert call(a8=8192, a13=8192) == EINVAL   # latents too large for LDS
+    assert call(a4=ctypes.c_void_p(0x1008)) == EINVAL   # q_rg not 16-byte aligned
+    need = lib.lrc_lowrank_ffn_workspace(1, 96, 32, 32, 32)
+    assert need > 0 and call(a21=need - 1) == EWORKSPACE
+
+
 def test_profile_session_without_work(lib):
     # no kernel launched: the session records nothing and out-of-range queries fail
     assert lib.lrc_profile_start() == 0

@@ -581,3 +581,32 @@ def test_quantize_rows_bit_exact(lrc):
     oq, os_ = oracle.rtn_rows(x.numpy())
     assert np.array_equal(to_np(q), oq) and np.array_equal(to_np(s), os_)
 
+
+# ----------------------------------------------------------------------------- low-rank FFN
+def _ffn_factor(g, rows, cols):
+    q = torch.randint(-127, 128, (rows, cols), generator=g, dtype=torch.int8)
+    s = (torch.rand(rows, generator=g) * 0.004 + 0.001).float()
+    return q, s
+
+
+@pytest.mark.parametrize("n_tok,d,d_ff,rg,ru,rd", [(1, 256, 688, 64, 48, 32), (5, 128, 300, 32, 32, 16),
+                                                   (9, 4096, 11008, 2048, 2048, 2048)])
+def test_lowrank_ffn(lrc, n_tok, d, d_ff, rg, ru, rd):
+    """fp32 products and sums against the fp64 oracle.  Each output is a chain of four
+    dot products of at most 11008 terms; the per-lane partial sums (<= 172 terms) and the
+    fixed trees keep the rounding error near 200 u of the summed magnitudes, and for these
+    random factors the summed magnitudes stay within ~30x of the outputs' largest, so the
+    bound is 200 * 2^-24 * 30 ~ 4e-4 of max|y|; the observed error is far below it."""
+    g = torch.Generator().manual_seed(d_ff + n_tok)
+    gate = (*_ffn_factor(g, rg, d), *_ffn_factor(g, d_ff, rg))
+    up = (*_ffn_factor(g, ru, d), *_ffn_factor(g, d_ff, ru))
+    qrd, srd = _ffn_factor(g, rd, d_ff)
+    qld, sld = _ffn_factor(g, d, rd)
+    x = torch.randn(n_tok, d, generator=g) * 4
+    y = lrc.lrc_lowrank_ffn(x.to(dev()), [t.to(dev()) for t in gate], [t.to(dev()) for t in up],
+                            [qrd.t().contiguous().to(dev()), srd.to(dev()), qld.to(dev()), sld.to(dev())])
+    ref = oracle.lowrank_ffn(x.numpy(), [t.numpy() for t in gate], [t.numpy() for t in up],
+                             (qrd.numpy(), srd.numpy(), qld.numpy(), sld.numpy()))
+    err = np.abs(to_np(y) - ref).max() / np.abs(ref).max()
+    assert err < 4e-4, err
+
