@@ -81,6 +81,9 @@ __global__ __launch_bounds__(FT) void rows_gemv_kernel(const int8_t* __restrict_
 
 // Hidden channels [b J, b J + J): gate/up expansion, SwiGLU, and the chunk's partial of
 // R_down h: pd[b][t][k] = sum_j q_rdt[j][k] h[t][j] (R_down's row scales come later).
+// NG tokens per group (1 or TG); with TG the latents sit in LDS token-interleaved
+// ([k][t]), so one 16-byte read serves the four tokens of a weight element.
+template <int NG>
 __global__ __launch_bounds__(FT) void swiglu_down_kernel(const int8_t* __restrict__ qlg, const float* __restrict__ slg,
                                                          const int8_t* __restrict__ qlu, const float* __restrict__ slu,
                                                          int rg, int ru, const float* __restrict__ latg,
@@ -88,22 +91,22 @@ __global__ __launch_bounds__(FT) void swiglu_down_kernel(const int8_t* __restric
                                                          const int8_t* __restrict__ qrdt, int rd, int d_ff, int J,
                                                          int n_tok, float* __restrict__ pd) {
   extern __shared__ float sh[];
-  float* lg = sh;                 // [TG][rg]
-  float* lu = lg + TG * rg;       // [TG][ru]
-  float* hh = lu + TG * ru;       // [TG][J]
+  float* lg = sh;                 // [k][NG]
+  float* lu = lg + NG * rg;       // [k][NG]
+  float* hh = lu + NG * ru;       // [NG][J]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j0 = blockIdx.x * J;
   const int jn = min(J, d_ff - j0);
-  for (int t0 = 0; t0 < n_tok; t0 += TG) {
-    const int nt = min(TG, n_tok - t0);
+  for (int t0 = 0; t0 < n_tok; t0 += NG) {
+    const int nt = min(NG, n_tok - t0);
     __syncthreads();
-    for (int i = tid; i < TG * rg; i += FT) {
+    for (int i = tid; i < NG * rg; i += FT) {
       const int t = i / rg, k = i % rg;
-      lg[i] = t < nt ? latg[int64_t(t0 + t) * rg + k] : 0.f;
+      lg[k * NG + t] = t < nt ? latg[int64_t(t0 + t) * rg + k] : 0.f;
     }
-    for (int i = tid; i < TG * ru; i += FT) {
+    for (int i = tid; i < NG * ru; i += FT) {
       const int t = i / ru, k = i % ru;
-      lu[i] = t < nt ? latu[int64_t(t0 + t) * ru + k] : 0.f;
+      lu[k * NG + t] = t < nt ? latu[int64_t(t0 + t) * ru + k] : 0.f;
     }
     __syncthreads();
     // expansion: a wave takes four hidden rows at a time, 16 lanes per row (lanes split
@@ -126,11 +129,19 @@ __global__ __launch_bounds__(FT) void swiglu_down_kernel(const int8_t* __restric
           if (k < rg) {
             float w[16];
             unpack16(wq[c], w);
+            if constexpr (NG == 1) {
 #pragma unroll
-            for (int t = 0; t < TG; ++t)
-              if (t < nt)
+              for (int e = 0; e < 16; ++e) g[0] += w[e] * lg[k + e];
+            } else {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) g[t] += w[e] * lg[t * rg + k + e];
+              for (int e = 0; e < 16; ++e) {
+                const float4 lv = *reinterpret_cast<const float4*>(lg + (k + e) * NG);
+                g[0] += w[e] * lv.x;
+                g[1] += w[e] * lv.y;
+                g[2] += w[e] * lv.z;
+                g[3] += w[e] * lv.w;
+              }
+            }
           }
         }
       }
@@ -147,16 +158,24 @@ __global__ __launch_bounds__(FT) void swiglu_down_kernel(const int8_t* __restric
           if (k < ru) {
             float w[16];
             unpack16(wq[c], w);
+            if constexpr (NG == 1) {
 #pragma unroll
-            for (int t = 0; t < TG; ++t)
-              if (t < nt)
+              for (int e = 0; e < 16; ++e) u[0] += w[e] * lu[k + e];
+            } else {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) u[t] += w[e] * lu[t * ru + k + e];
+              for (int e = 0; e < 16; ++e) {
+                const float4 lv = *reinterpret_cast<const float4*>(lu + (k + e) * NG);
+                u[0] += w[e] * lv.x;
+                u[1] += w[e] * lv.y;
+                u[2] += w[e] * lv.z;
+                u[3] += w[e] * lv.w;
+              }
+            }
           }
         }
       }
 #pragma unroll
-      for (int t = 0; t < TG; ++t) {
+      for (int t = 0; t < NG; ++t) {
         float gs = g[t], us = u[t];
 #pragma unroll
         for (int o = 8; o > 0; o >>= 1) {   // sum over the row's 16 lanes
@@ -168,9 +187,9 @@ __global__ __launch_bounds__(FT) void swiglu_down_kernel(const int8_t* __restric
     }
     __syncthreads();
     for (int kb = tid * 8; kb < rd; kb += FT * 8) {
-      float acc[TG][8];
+      float acc[NG][8];
 #pragma unroll
-      for (int t = 0; t < TG; ++t)
+      for (int t = 0; t < NG; ++t)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[t][e] = 0.f;
       for (int jb = 0; jb < jn; jb += 8) {
@@ -186,7 +205,7 @@ __global__ __launch_bounds__(FT) void swiglu_down_kernel(const int8_t* __restric
 #pragma unroll
             for (int e = 0; e < 8; ++e) w[e] = float(int8_t(uint8_t(wu[e >> 2] >> (8 * (e & 3)))));
 #pragma unroll
-            for (int t = 0; t < TG; ++t) {
+            for (int t = 0; t < NG; ++t) {
               if (t < nt) {
                 const float hv = hh[t * J + jb + c];
 #pragma unroll
@@ -197,7 +216,7 @@ __global__ __launch_bounds__(FT) void swiglu_down_kernel(const int8_t* __restric
         }
       }
 #pragma unroll
-      for (int t = 0; t < TG; ++t) {
+      for (int t = 0; t < NG; ++t) {
         if (t < nt) {
           float4* dst = reinterpret_cast<float4*>(pd + (int64_t(blockIdx.x) * n_tok + t0 + t) * rd + kb);
           dst[0] = make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
@@ -283,9 +302,12 @@ extern "C" lrc_status lrc_lowrank_ffn(const float* x, int64_t n_tok, int64_t d, 
   if (ws == nullptr || ws_bytes < need) return LRC_EWORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   // the expansion kernel's LDS (both latents of a token group) may exceed the default cap
-  if (lds > 64 * 1024)
-    LRC_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&swiglu_down_kernel),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)));
+  const int ng = n_tok == 1 ? 1 : TG;
+  const size_t lds_used = sizeof(float) * size_t(ng * (rg + ru) + ng * J);
+  if (lds_used > 64 * 1024)
+    LRC_HIP(hipFuncSetAttribute(ng == 1 ? reinterpret_cast<const void*>(&swiglu_down_kernel<1>)
+                                        : reinterpret_cast<const void*>(&swiglu_down_kernel<TG>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds_used)));
   Carve cv(ws);
   const FfnWs w = carve_ffn(cv, n_tok, rg, ru, rd, nb);
   // bytes: every int8 factor once, the activations, the outputs
@@ -294,8 +316,13 @@ extern "C" lrc_status lrc_lowrank_ffn(const float* x, int64_t n_tok, int64_t d, 
   rows_gemv_kernel<<<unsigned(cdiv(rg + ru, FT / 64)), FT, 0, st>>>(q_rg, s_rg, int(rg), q_ru, s_ru, int(ru), int(d), x,
                                                                    int(n_tok), w.latg, w.latu);
   LRC_LAUNCHED();
-  swiglu_down_kernel<<<unsigned(nb), FT, lds, st>>>(q_lg, s_lg, q_lu, s_lu, int(rg), int(ru), w.latg, w.latu, q_rdt,
-                                                    int(rd), int(d_ff), int(J), int(n_tok), w.pd);
+  if (ng == 1)
+    swiglu_down_kernel<1><<<unsigned(nb), FT, lds_used, st>>>(q_lg, s_lg, q_lu, s_lu, int(rg), int(ru), w.latg, w.latu,
+                                                              q_rdt, int(rd), int(d_ff), int(J), int(n_tok), w.pd);
+  else
+    swiglu_down_kernel<TG><<<unsigned(nb), FT, lds_used, st>>>(q_lg, s_lg, q_lu, s_lu, int(rg), int(ru), w.latg,
+                                                               w.latu, q_rdt, int(rd), int(d_ff), int(J), int(n_tok),
+                                                               w.pd);
   LRC_LAUNCHED();
   latent_reduce_kernel<<<unsigned(cdiv(n_tok * rd, FT / 4)), FT, 0, st>>>(w.pd, int(nb), int(n_tok), int(rd), s_rd,
                                                                           w.latd);
