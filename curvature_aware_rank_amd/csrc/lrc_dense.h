@@ -32,6 +32,8 @@ lrc_status jacobi_eig(hipStream_t st, double* A, int64_t k, int64_t batch, int64
 // eigenvalues, inverse iteration for the ncols largest, blocked back-transformation.
 // Same outputs as jacobi_eig (batch 1).  When the wanted eigenvalues contain a cluster
 // too large for inverse iteration, *clustered is set and nothing past sigma is written.
+// A must be 16-byte aligned with an even lda, and lda > k when k is odd (LRC_EINVAL
+// otherwise).
 size_t tridiag_workspace(int64_t k, int64_t ncols);
 lrc_status tridiag_eig(hipStream_t st, double* A, int64_t k, int64_t lda, int64_t ncols, float* sigma, float* Qt,
                        void* ws, bool* clustered);

@@ -55,14 +55,6 @@ __device__ __forceinline__ void tile_of(int t, int& b, int& c) {
   c = t - bb * (bb + 1) / 2;
 }
 
-// sum of the squared-norm partials of a column, strided over 256 threads then a fixed
-// tree (the symv and w kernels call this with the same arguments and get the same bits)
-__device__ __forceinline__ double npart_sum_part(const double* __restrict__ npart, int np) {
-  double s = 0.0;
-  for (int b = threadIdx.x; b < np; b += 256) s += npart[b];
-  return s;
-}
-
 __device__ __forceinline__ void house_from_sum(double xn2, double x0, double& tau, double& beta, double& scale) {
   if (xn2 == 0.0) {
     tau = 0.0;
@@ -108,21 +100,6 @@ __device__ __forceinline__ double wave_sum(double v) {
   return (lane_val(0) + lane_val(16)) + (lane_val(32) + lane_val(48));
 }
 
-// block-wide sums (256 threads) of two values: wave butterflies, then the four wave
-// results in order; results to all threads
-__device__ __forceinline__ void block_sum2_fast(double& v0, double& v1, double (*red)[4]) {
-  const int tid = threadIdx.x;
-  v0 = wave_sum(v0);
-  v1 = wave_sum(v1);
-  if ((tid & 63) == 0) {
-    red[0][tid >> 6] = v0;
-    red[1][tid >> 6] = v1;
-  }
-  __syncthreads();
-  v0 = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
-  v1 = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
-}
-
 // block-wide sum of one value per thread (256 threads), fixed tree; result to all
 __device__ __forceinline__ double block_sum256(double v, double* red) {
   const int tid = threadIdx.x;
@@ -137,7 +114,8 @@ __device__ __forceinline__ double block_sum256(double v, double* red) {
   return r;
 }
 
-// ---- 1a. first column of a panel: d[i], x0, squared-norm partials (no deferred updates)
+// ---- 1a. first column of a panel: d[i], x0, squared-norm partials (no deferred updates;
+// four partials per 64-row block, as the w kernel writes them: the block's sum, then zeros)
 __global__ __launch_bounds__(256) void tri_colstart_kernel(const double* __restrict__ A, int64_t lda, int n, int i,
                                                            double* __restrict__ npart, double* __restrict__ x0,
                                                            double* __restrict__ d) {
@@ -152,7 +130,7 @@ __global__ __launch_bounds__(256) void tri_colstart_kernel(const double* __restr
     if (r >= i + 2) sq = val * val;
   }
   const double s = block_sum256(sq, red);
-  if (tid == 0) npart[blockIdx.x] = s;
+  if (tid < 4) npart[4 * blockIdx.x + tid] = tid == 0 ? s : 0.0;
 }
 
 // ---- 1b. symv over the trailing matrix (rows/cols i+1 .. n-1) with the raw column
@@ -160,12 +138,20 @@ __global__ __launch_bounds__(256) void tri_colstart_kernel(const double* __restr
 // applies that), one 64 x 64 lower tile per workgroup.  Outputs: P[x][y][*], the
 // contribution to y-block x from the tile pairing x and y; S[t] = tile part of x^T C x;
 // on diagonal tiles the panel products V^T x, W^T x over the block's rows.
+// Each thread holds a 4 x 4 patch of the tile in registers (rows 4 rb .., columns 4 cb ..,
+// rb = tid / 16, cb = tid % 16), loaded as 16-byte pairs (EVEN: the tile's first column is
+// even; otherwise three pairs per row, of which the middle four values are used).  Row
+// sums reduce over the 16 lanes of a DPP row by a transposing butterfly; column partials
+// go through a 16 x 64 LDS table and are added in row-band order.
+constexpr int DPP_ROW_ROR8 = 0x128;   // row_ror:8, lane i <-> i + 8 within 16 lanes
+
+template <bool EVEN>
 __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict__ A, int64_t lda, int n, int i, int i0,
                                                        int jj, const double* __restrict__ Wp,
                                                        double* __restrict__ P, double* __restrict__ S,
                                                        double* __restrict__ SV, double* __restrict__ SW) {
-  __shared__ double T[TS][TS + 1];
-  __shared__ double vb[TS], vc[TS], rs[TS], cs[TS];
+  __shared__ double vb[TS], vc[TS], rsum[TS];
+  __shared__ double cpart[16][TS + 1];
   __shared__ double red[8][2][NB];
   const int tid = threadIdx.x;
   const int s0 = i + 1;
@@ -175,15 +161,46 @@ __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict_
   tile_of(blockIdx.x, b, c);
   const int R0 = s0 + b * TS, C0 = s0 + c * TS;
   const bool diag = b == c;
-  // every load below is unconditional from a clamped (valid) address and masked after,
-  // so that all of them are in flight together
-  double tv[16];
-  const int lc = tid & 63, cc = C0 + lc, ccc = min(cc, n - 1);
+  const int rb = tid >> 4, cb = tid & 15;
+  const int c4 = C0 + 4 * cb;
+  // every load is unconditional from a clamped address and masked at use: pairs start at
+  // even columns, at most at pe, the last even column; for odd n the pair (n - 1, n) reads
+  // one element of the row padding (the pitch is even and exceeds n)
+  const int pe = (n - 1) & ~1;
+  double tv[4][4];
+  if (EVEN) {
+    const int p0 = min(c4, pe), p1 = min(c4 + 2, pe);
+    double2 u[4][2];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int lr = (tid >> 6) + 4 * j;
-    const int r = R0 + lr;
-    tv[j] = A[int64_t(min(r, n - 1)) * lda + ccc];
+    for (int k = 0; k < 4; ++k) {
+      const int r = min(R0 + 4 * rb + k, n - 1);
+      u[k][0] = *reinterpret_cast<const double2*>(A + int64_t(r) * lda + p0);
+      u[k][1] = *reinterpret_cast<const double2*>(A + int64_t(r) * lda + p1);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      tv[k][0] = u[k][0].x;
+      tv[k][1] = u[k][0].y;
+      tv[k][2] = u[k][1].x;
+      tv[k][3] = u[k][1].y;
+    }
+  } else {
+    const int p0 = min(c4 - 1, pe), p1 = min(c4 + 1, pe), p2 = min(c4 + 3, pe);
+    double2 u[4][3];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int r = min(R0 + 4 * rb + k, n - 1);
+      u[k][0] = *reinterpret_cast<const double2*>(A + int64_t(r) * lda + p0);
+      u[k][1] = *reinterpret_cast<const double2*>(A + int64_t(r) * lda + p1);
+      u[k][2] = *reinterpret_cast<const double2*>(A + int64_t(r) * lda + p2);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      tv[k][0] = u[k][0].y;
+      tv[k][1] = u[k][1].x;
+      tv[k][2] = u[k][1].y;
+      tv[k][3] = u[k][2].x;
+    }
   }
   double colv;
   {
@@ -210,34 +227,44 @@ __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict_
       wa[q] = ok ? wa[q] : 0.0;
     }
   }
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int lr = (tid >> 6) + 4 * j;
-    const bool ok = R0 + lr < n && cc < n && (!diag || lr >= lc);
-    tv[j] = ok ? tv[j] : 0.0;
-  }
   if (tid < TS) vb[tid] = colv;
   else if (tid < 2 * TS) vc[tid - TS] = colv;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) T[(tid >> 6) + 4 * j][lc] = tv[j];
   __syncthreads();
-  {
-    const int x = tid >> 2, part = tid & 3;
-    double srow = 0.0, scol = 0.0;
+  double vcl[4], vbl[4];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int q = part * 16 + j;
-      srow += T[x][q] * vc[q];
-      // column sums: strictly lower rows in a diagonal tile
-      const double t = (diag && q == x) ? 0.0 : T[q][x];
-      scol += t * vb[q];
+  for (int e = 0; e < 4; ++e) {
+    vcl[e] = vc[4 * cb + e];
+    vbl[e] = vb[4 * rb + e];
+  }
+  // row sums over the tile's lower part incl. the diagonal; column sums strictly below it
+  double rp[4] = {0.0, 0.0, 0.0, 0.0}, cp[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int row = 4 * rb + k;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int col = 4 * cb + e;
+      const bool in = R0 + row < n && C0 + col < n;
+      const bool okr = in && (!diag || col <= row);
+      const bool okc = in && (!diag || col < row);
+      rp[k] += okr ? tv[k][e] * vcl[e] : 0.0;
+      cp[e] += okc ? tv[k][e] * vbl[k] : 0.0;
     }
-    srow = quad_sum(srow);
-    scol = quad_sum(scol);
-    if (part == 0) {
-      rs[x] = srow;
-      cs[x] = scol;
-    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) cpart[rb][4 * cb + e] = cp[e];
+  {
+    // four row values over 16 lanes: exchange halves with the lane 8 away, then with the
+    // mirrored lane of the 8-lane half, then sum the quad; row 4 rb + 2 b3 + b2 results
+    const bool h = cb & 8;
+    const double s0v = h ? rp[0] : rp[2], s1v = h ? rp[1] : rp[3];
+    const double k0v = h ? rp[2] : rp[0], k1v = h ? rp[3] : rp[1];
+    const double a0 = k0v + dpp_mov<DPP_ROW_ROR8>(s0v);
+    const double a1 = k1v + dpp_mov<DPP_ROW_ROR8>(s1v);
+    const bool h2 = cb & 4;
+    const double sv = h2 ? a0 : a1, kv = h2 ? a1 : a0;
+    const double r = quad_sum(kv + dpp_mov<DPP_HALF_MIRROR>(sv));
+    if ((cb & 3) == 0) rsum[4 * rb + 2 * ((cb >> 3) & 1) + ((cb >> 2) & 1)] = r;
   }
   if (pan) {
     double sv = 0.0, sw = 0.0;
@@ -251,7 +278,10 @@ __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict_
   }
   __syncthreads();
   if (tid < TS) {
-    const double r_ = rs[tid], c_ = cs[tid];
+    double c_ = 0.0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) c_ += cpart[q][tid];
+    const double r_ = rsum[tid];
     if (diag) {
       P[(int64_t(b) * nbt + b) * TS + tid] = r_ + c_;
     } else {
@@ -280,11 +310,12 @@ __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict_
 // v = scale x + c e_{s0} (c = 1 - scale x0), C v = scale (C x) + c C e_{s0},
 // w = tau (C v - W V^T v - V W^T v) + alpha v with alpha = -tau^2/2 (v^T C v - 2 (V^T v).(W^T v));
 // store v (column i) and w (column jj of W); then bring column s0 up to date with the
-// panel's reflectors 0..jj (if it is in the panel) and write its squared-norm partials.
-// Every global load of the kernel is issued in one phase (clamped addresses, masked
-// after), so the kernel makes one round trip to memory before its stores.
-constexpr int WB = 64;   // row blocks (and tile partials per row) covered by the single load phase
-
+// panel's reflectors 0..jj (if it is in the panel) and write its squared-norm partials
+// (one per wave: rows 16 wv .. 16 wv + 15 of the block).
+// Every global load is issued in one phase, from clamped addresses and masked after: the
+// block's row of symv partials, the panel partials and the block's panel rows as 16-byte
+// pairs along contiguous rows, columns i and s0 once per row (one pair when i is even).
+template <bool EVEN>
 __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int64_t lda, int n, int i, int i0, int jj,
                                                     int do_next, double* __restrict__ Wp,
                                                     const double* __restrict__ npart, const double* __restrict__ x0p,
@@ -294,108 +325,146 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
                                                     double* __restrict__ d, double* __restrict__ e,
                                                     double* __restrict__ tau_out) {
   __shared__ double Vs[TS][NB + 1], Ws[TS][NB + 1];
-  __shared__ double vn[NB], wn[NB];
-  __shared__ double sv[NB], sw[NB];
-  __shared__ double red8[8][2][NB];
-  __shared__ double red4[2][4];
+  __shared__ double yp[8][TS];
+  __shared__ double svq[16][NB], swq[16][NB];
+  __shared__ double vn[NB], wn[NB], sv[NB], sw[NB];
+  __shared__ double colI[TS], colS[TS];
+  __shared__ double red[3][4];
   __shared__ double sc[2];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int s0 = i + 1;
   const int m = n - s0;
   const int nbt = (m + TS - 1) / TS;
   const int ntile = nbt * (nbt + 1) / 2;
-  const int np = (n - i + TS - 1) / TS;
+  const int np4 = 4 * ((n - i + TS - 1) / TS);
   const int b = blockIdx.x;
   const int R0 = s0 + b * TS;
-  const int jc = max(jj - 1, 0);
-  const int c32 = tid & 31, g8 = tid >> 5, c32c = min(c32, jc);
-  const int x = tid >> 2, part = tid & 3;
-  const int r = R0 + x, rc = min(r, n - 1);
+  const int xp = tid & 31, cg = tid >> 5;   // symv partials: row pair 2 xp, column blocks cg + 8 u
+  const int cq = tid & 15, qg = tid >> 4;   // panel: column pair 2 cq, row (block) group qg + 16 u
+  // panel column pair start, never past column i0 + jj = i
+  const int pcs = max(min(2 * cq, (jj - 1) & ~1), 0);
 
   // ---- load phase
-  double pvv[8], pww[8], tsv[8], tsw[8], tp[16], tp0[16], ts[9];
+  double2 pp[8], svl[4], swl[4], pv[4], pw[4];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int rr = min(R0 + g8 + 8 * u, n - 1);
-    pvv[u] = A[int64_t(rr) * lda + i0 + c32c];
-    pww[u] = Wp[int64_t(rr) * NB + c32c];
-  }
-  const double vnl = A[int64_t(s0) * lda + i0 + c32c];
-  const double wnl = Wp[int64_t(s0) * NB + c32c];
-  double coli = A[int64_t(rc) * lda + i];
-  double cols0 = A[int64_t(rc) * lda + s0];
-  const double x0v = *x0p;
-  const double a00 = A[int64_t(s0) * lda + s0];
+  for (int u = 0; u < 8; ++u)
+    pp[u] = *reinterpret_cast<const double2*>(P + (int64_t(b) * nbt + min(cg + 8 * u, nbt - 1)) * TS + 2 * xp);
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int q = min(g8 + 8 * u, nbt - 1);
-    tsv[u] = SV[q * NB + c32c];
-    tsw[u] = SW[q * NB + c32c];
+  for (int u = 0; u < 4; ++u) {
+    const int q = min(qg + 16 * u, nbt - 1);
+    svl[u] = *reinterpret_cast<const double2*>(SV + q * NB + pcs);
+    swl[u] = *reinterpret_cast<const double2*>(SW + q * NB + pcs);
+    const int r = min(R0 + qg + 16 * u, n - 1);
+    pv[u] = *reinterpret_cast<const double2*>(A + int64_t(r) * lda + i0 + pcs);
+    pw[u] = *reinterpret_cast<const double2*>(Wp + int64_t(r) * NB + pcs);
   }
-#pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int c = min(part + 4 * u, nbt - 1);
-    tp[u] = P[(int64_t(b) * nbt + c) * TS + x];
-    tp0[u] = P[int64_t(c) * TS];   // row s0 = block 0, local 0
+  double2 vnl = make_double2(0.0, 0.0), wnl = make_double2(0.0, 0.0);
+  if (tid < 16) {
+    vnl = *reinterpret_cast<const double2*>(A + int64_t(s0) * lda + i0 + pcs);
+    wnl = *reinterpret_cast<const double2*>(Wp + int64_t(s0) * NB + pcs);
   }
-  const double tnp = npart[min(tid, np - 1)];
+  double ci = 0.0, cs0 = 0.0;
+  if (tid < TS) {
+    const int r = min(R0 + tid, n - 1);
+    if (EVEN) {
+      const double2 t2 = *reinterpret_cast<const double2*>(A + int64_t(r) * lda + i);
+      ci = t2.x;
+      cs0 = t2.y;
+    } else {
+      ci = A[int64_t(r) * lda + i];
+      cs0 = A[int64_t(r) * lda + s0];
+    }
+  }
+  double ts[9];
 #pragma unroll
   for (int u = 0; u < 9; ++u) ts[u] = S[min(tid + 256 * u, ntile - 1)];
+  const double tnp = npart[min(tid, np4 - 1)];
+  const double tp0 = P[int64_t(min(tid, nbt - 1)) * TS];   // row s0 = block 0, local 0
+  const double x0v = *x0p;
+  const double a00 = A[int64_t(s0) * lda + s0];
 
-  // ---- reductions (fixed order: sequential within a lane, then butterflies)
-  double yraw = 0.0, y0raw = 0.0;
-#pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const bool ok = part + 4 * u < nbt;
-    yraw += ok ? tp[u] : 0.0;
-    y0raw += ok ? tp0[u] : 0.0;
-  }
-  for (int c0 = part + 4 * 16; c0 < nbt; c0 += 4) {   // more than 64 row blocks
-    yraw += P[(int64_t(b) * nbt + c0) * TS + x];
-    y0raw += P[int64_t(c0) * TS];
-  }
-  yraw = quad_sum(yraw);
-  y0raw = quad_sum(y0raw);
-  double a0 = 0.0, a1 = 0.0;
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const bool ok = c32 < jj && g8 + 8 * u < nbt;
-    a0 += ok ? tsv[u] : 0.0;
-    a1 += ok ? tsw[u] : 0.0;
-  }
-  if (c32 < jj)
-    for (int q = g8 + 64; q < nbt; q += 8) {
-      a0 += SV[q * NB + c32];
-      a1 += SW[q * NB + c32];
-    }
-  red8[g8][0][c32] = a0;
-  red8[g8][1][c32] = a1;
-  double v0 = tid < np ? tnp : 0.0;
-  for (int t = tid + 256; t < np; t += 256) v0 += npart[t];
-  double v1 = 0.0;
-#pragma unroll
-  for (int u = 0; u < 9; ++u) v1 += tid + 256 * u < ntile ? ts[u] : 0.0;
-  for (int t = tid + 256 * 9; t < ntile; t += 256) v1 += S[t];
+  // ---- partial sums to LDS (fixed order: sequential within a lane), block sums by wave
   {
+    double ya = 0.0, yb = 0.0;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int xr = g8 + 8 * u;
-      const bool ok = c32 < jj && R0 + xr < n;
-      Vs[xr][c32] = ok ? pvv[u] : 0.0;
-      Ws[xr][c32] = ok ? pww[u] : 0.0;
+      const bool ok = cg + 8 * u < nbt;
+      ya += ok ? pp[u].x : 0.0;
+      yb += ok ? pp[u].y : 0.0;
+    }
+    for (int c = cg + 64; c < nbt; c += 8) {   // more than 64 row blocks
+      const double2 t2 = *reinterpret_cast<const double2*>(P + (int64_t(b) * nbt + c) * TS + 2 * xp);
+      ya += t2.x;
+      yb += t2.y;
+    }
+    yp[cg][2 * xp] = ya;
+    yp[cg][2 * xp + 1] = yb;
+  }
+  {
+    double a0 = 0.0, a1 = 0.0, b0 = 0.0, b1 = 0.0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool ok = qg + 16 * u < nbt;
+      a0 += ok ? svl[u].x : 0.0;
+      a1 += ok ? svl[u].y : 0.0;
+      b0 += ok ? swl[u].x : 0.0;
+      b1 += ok ? swl[u].y : 0.0;
+    }
+    for (int q = qg + 64; q < nbt; q += 16) {
+      const double2 t1 = *reinterpret_cast<const double2*>(SV + q * NB + pcs);
+      const double2 t2 = *reinterpret_cast<const double2*>(SW + q * NB + pcs);
+      a0 += t1.x;
+      a1 += t1.y;
+      b0 += t2.x;
+      b1 += t2.y;
+    }
+    svq[qg][2 * cq] = a0;
+    svq[qg][2 * cq + 1] = a1;
+    swq[qg][2 * cq] = b0;
+    swq[qg][2 * cq + 1] = b1;
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int rr = qg + 16 * u;
+    const bool okr = R0 + rr < n;
+    Vs[rr][2 * cq] = okr && 2 * cq < jj ? pv[u].x : 0.0;
+    Vs[rr][2 * cq + 1] = okr && 2 * cq + 1 < jj ? pv[u].y : 0.0;
+    Ws[rr][2 * cq] = okr && 2 * cq < jj ? pw[u].x : 0.0;
+    Ws[rr][2 * cq + 1] = okr && 2 * cq + 1 < jj ? pw[u].y : 0.0;
+  }
+  if (tid < 16) {
+    vn[2 * tid] = 2 * tid < jj ? vnl.x : 0.0;
+    vn[2 * tid + 1] = 2 * tid + 1 < jj ? vnl.y : 0.0;
+    wn[2 * tid] = 2 * tid < jj ? wnl.x : 0.0;
+    wn[2 * tid + 1] = 2 * tid + 1 < jj ? wnl.y : 0.0;
+  }
+  if (tid < TS) {
+    const bool ok = R0 + tid < n;
+    colI[tid] = ok ? ci : 0.0;
+    colS[tid] = ok ? cs0 : 0.0;
+  }
+  {
+    double v0 = tid < np4 ? tnp : 0.0;
+    for (int t = tid + 256; t < np4; t += 256) v0 += npart[t];
+    double v1 = 0.0;
+#pragma unroll
+    for (int u = 0; u < 9; ++u) v1 += tid + 256 * u < ntile ? ts[u] : 0.0;
+    for (int t = tid + 256 * 9; t < ntile; t += 256) v1 += S[t];
+    double y0 = tid < nbt ? tp0 : 0.0;
+    for (int c = tid + 256; c < nbt; c += 256) y0 += P[int64_t(c) * TS];
+    v0 = wave_sum(v0);
+    v1 = wave_sum(v1);
+    y0 = wave_sum(y0);
+    if (lane == 0) {
+      red[0][wv] = v0;
+      red[1][wv] = v1;
+      red[2][wv] = y0;
     }
   }
-  if (tid < NB) {
-    vn[tid] = tid < jj ? vnl : 0.0;
-    wn[tid] = tid < jj ? wnl : 0.0;
-  }
-  if (r >= n) {
-    coli = 0.0;
-    cols0 = 0.0;
-  }
-  block_sum2_fast(v0, v1, red4);   // barrier: also publishes Vs, Ws, vn, wn, red8
+  __syncthreads();
+  const double xn2 = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
   double tau, beta, scale;
-  house_from_sum(v0, x0v, tau, beta, scale);
+  house_from_sum(xn2, x0v, tau, beta, scale);
   const double cfac = 1.0 - scale * x0v;
   if (b == 0 && tid == 0) {
     e[i] = beta;
@@ -407,9 +476,9 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
     if (tid < jj) {
       double b0 = 0.0, b1 = 0.0;
 #pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        b0 += red8[g][0][tid];
-        b1 += red8[g][1][tid];
+      for (int g = 0; g < 16; ++g) {
+        b0 += svq[g][tid];
+        b1 += swq[g][tid];
       }
       svc = scale * b0 + cfac * vn[tid];
       swc = scale * b1 + cfac * wn[tid];
@@ -419,6 +488,8 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
     const double dsw = wave_sum(svc * swc);
     const double corr0 = wave_sum(tid < jj ? wn[tid] * svc + vn[tid] * swc : 0.0);
     if (tid == 0) {
+      const double v1 = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+      const double y0raw = (red[2][0] + red[2][1]) + (red[2][2] + red[2][3]);
       const double y0 = scale * y0raw + cfac * a00;
       const double vav = scale * scale * v1 + 2.0 * scale * cfac * y0raw + cfac * cfac * a00;
       const double alpha = -0.5 * tau * tau * (vav - 2.0 * dsw);
@@ -428,19 +499,25 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
   }
   __syncthreads();
   const double alpha = sc[0], w0 = sc[1];
-  // rows: corrections split over the quad's 4 lanes (c = part, part + 4, ...)
+  // rows x = tid / 4: the quad splits the panel columns (c = part, part + 4, ...) and the
+  // row-sum groups (2 part, 2 part + 1)
+  const int x = tid >> 2, part = tid & 3;
+  const int r = R0 + x;
   double corr = 0.0, c2 = 0.0;
   for (int c = part; c < jj; c += 4) {
     const double vr = Vs[x][c], wr = Ws[x][c];
     corr += wr * sv[c] + vr * sw[c];
     c2 += vr * wn[c] + wr * vn[c];
   }
+  double yr = yp[2 * part][x] + yp[2 * part + 1][x];
   corr = quad_sum(corr);
   c2 = quad_sum(c2);
+  yr = quad_sum(yr);
   double v = 0.0, w = 0.0;
+  const double cs0x = colS[x];
   if (r < n) {
-    const double y = scale * yraw + cfac * cols0 - corr;
-    v = r == s0 ? 1.0 : coli * scale;
+    const double y = scale * yr + cfac * cs0x - corr;
+    v = r == s0 ? 1.0 : colI[x] * scale;
     w = r == s0 ? w0 : tau * y + alpha * v;   // row s0: the value every block uses
     if (part == 0) {
       Wp[int64_t(r) * NB + jj] = w;
@@ -451,15 +528,14 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
   // column s0: rows s0.., C[r][s0] -= sum_c V[r][c] W[s0][c] + W[r][c] V[s0][c], c = 0..jj
   double sq = 0.0;
   if (r < n && part == 0) {
-    const double val = cols0 - (c2 + (v * w0 + w));
+    const double val = cs0x - (c2 + (v * w0 + w));
     A[int64_t(r) * lda + s0] = val;
     if (r == s0) d[s0] = val;
     if (r == s0 + 1) *x0_next = val;
     if (r >= s0 + 2) sq = val * val;
   }
-  double dummy = 0.0;
-  block_sum2_fast(sq, dummy, red4);
-  if (tid == 0) npart_next[b] = sq;
+  sq = wave_sum(sq);
+  if (lane == 0) npart_next[4 * b + wv] = sq;
 }
 
 // ---- 1d. trailing rank-2 panel update, lower tiles of rows/cols j1 .. n-1:
@@ -1366,7 +1442,7 @@ TWs carve_tri(Carve& cv, int64_t n, int64_t ncols) {
   w.S = cv.take<double>(size_t(nbt * (nbt + 1) / 2));
   w.SV = cv.take<double>(size_t(nbt * NB));
   w.SW = cv.take<double>(size_t(nbt * NB));
-  w.npart = cv.take<double>(size_t(2 * nbt));
+  w.npart = cv.take<double>(size_t(2 * 4 * nbt));   // two columns' partials, four per row block
   w.x0 = cv.take<double>(2);
   w.d = cv.take<double>(size_t(n));
   w.e = cv.take<double>(size_t(n));
@@ -1404,6 +1480,9 @@ size_t tridiag_workspace(int64_t k, int64_t ncols) {
 lrc_status tridiag_eig(hipStream_t st, double* A, int64_t k, int64_t lda, int64_t ncols_in, float* sigma, float* Qt,
                        void* ws, bool* clustered) {
   *clustered = false;
+  // the symv kernel reads 16-byte column pairs: even pitch, 16-byte base, padding after
+  // an odd last column
+  if (lda % 2 != 0 || (k % 2 != 0 && lda < k + 1) || reinterpret_cast<uintptr_t>(A) % 16 != 0) return LRC_EINVAL;
   const int n = int(k);
   const int ncols = int(std::max<int64_t>(ncols_in, 1));
   Carve cv(ws);
@@ -1414,7 +1493,8 @@ lrc_status tridiag_eig(hipStream_t st, double* A, int64_t k, int64_t lda, int64_
     const int pb = std::min(NB, n - 1 - i0);
     {
       const unsigned g = unsigned(cdiv(n - i0, TS));
-      tri_colstart_kernel<<<g, 256, 0, st>>>(A, lda, n, i0, w.npart + (i0 & 1) * cdiv(n, TS), w.x0 + (i0 & 1), w.d);
+      tri_colstart_kernel<<<g, 256, 0, st>>>(A, lda, n, i0, w.npart + (i0 & 1) * 4 * cdiv(n, TS), w.x0 + (i0 & 1),
+                                             w.d);
       LRC_LAUNCHED();
     }
     for (int jj = 0; jj < pb; ++jj) {
@@ -1422,13 +1502,19 @@ lrc_status tridiag_eig(hipStream_t st, double* A, int64_t k, int64_t lda, int64_
       const int m = n - i - 1;
       const int nbt = int(cdiv(m, TS));
       const int par = i & 1, npar = (i + 1) & 1;
-      double* np_cur = w.npart + par * cdiv(n, TS);
-      double* np_next = w.npart + npar * cdiv(n, TS);
+      double* np_cur = w.npart + par * 4 * cdiv(n, TS);
+      double* np_next = w.npart + npar * 4 * cdiv(n, TS);
       {
         ProfScope scope("tri_symv_kernel", st, 2.0 * double(m) * double(m),
                         8.0 * double(m) * double(m + 1) / 2);
-        tri_symv_kernel<<<unsigned(nbt * (nbt + 1) / 2), 256, 0, st>>>(A, lda, n, i, i0, jj, w.Wp, w.P, w.S,
-                                                                        w.SV, w.SW);
+        // 16-byte pairs need an even matrix pitch and base; the tile's first column parity
+        // picks the pair alignment
+        if ((i + 1) % 2 == 0)
+          tri_symv_kernel<true><<<unsigned(nbt * (nbt + 1) / 2), 256, 0, st>>>(A, lda, n, i, i0, jj, w.Wp, w.P,
+                                                                                w.S, w.SV, w.SW);
+        else
+          tri_symv_kernel<false><<<unsigned(nbt * (nbt + 1) / 2), 256, 0, st>>>(A, lda, n, i, i0, jj, w.Wp, w.P,
+                                                                                 w.S, w.SV, w.SW);
         LRC_LAUNCHED();
       }
       {
@@ -1436,9 +1522,14 @@ lrc_status tridiag_eig(hipStream_t st, double* A, int64_t k, int64_t lda, int64_
         // written, the new column of W
         ProfScope scope("tri_w_kernel", st, 4.0 * double(m) * (jj + 1),
                         8.0 * (double(nbt) * nbt * TS + 2.0 * double(m) * jj + 5.0 * double(m)));
-        tri_w_kernel<<<unsigned(nbt), 256, 0, st>>>(A, lda, n, i, i0, jj, jj + 1 < pb ? 1 : 0, w.Wp, np_cur,
-                                                    w.x0 + par, w.P, w.S, w.SV, w.SW, np_next, w.x0 + npar, w.d,
-                                                    w.e, w.tau);
+        if (i % 2 == 0)   // columns i, i + 1 form an aligned pair
+          tri_w_kernel<true><<<unsigned(nbt), 256, 0, st>>>(A, lda, n, i, i0, jj, jj + 1 < pb ? 1 : 0, w.Wp, np_cur,
+                                                            w.x0 + par, w.P, w.S, w.SV, w.SW, np_next, w.x0 + npar,
+                                                            w.d, w.e, w.tau);
+        else
+          tri_w_kernel<false><<<unsigned(nbt), 256, 0, st>>>(A, lda, n, i, i0, jj, jj + 1 < pb ? 1 : 0, w.Wp, np_cur,
+                                                             w.x0 + par, w.P, w.S, w.SV, w.SW, np_next, w.x0 + npar,
+                                                             w.d, w.e, w.tau);
         LRC_LAUNCHED();
       }
     }
@@ -1453,7 +1544,7 @@ lrc_status tridiag_eig(hipStream_t st, double* A, int64_t k, int64_t lda, int64_
   {
     // last diagonal entry (and the whole job when n == 1)
     const int i = n - 1;
-    tri_colstart_kernel<<<1, 256, 0, st>>>(A, lda, n, i, w.npart + (i & 1) * cdiv(n, TS), w.x0 + (i & 1), w.d);
+    tri_colstart_kernel<<<1, 256, 0, st>>>(A, lda, n, i, w.npart + (i & 1) * 4 * cdiv(n, TS), w.x0 + (i & 1), w.d);
     LRC_LAUNCHED();
   }
 

@@ -226,7 +226,7 @@ def test_decompose_two_sided_fp32_config0_shape(lrc, solver):
 
 
 @pytest.mark.parametrize("d_out,d_in,rank", [(100, 150, 30), (150, 100, 40), (64, 64, 64), (300, 200, 7),
-                                             (33, 1, 1)])
+                                             (33, 1, 1), (257, 301, 40)])
 def test_decompose_ragged_shapes(lrc, solver, d_out, d_in, rank):
     case = _decompose_case(lrc, d_out, d_in, 2000, rank, True, 23 + d_out)
     _check_decomposition(case, rank)
