@@ -116,15 +116,17 @@ __device__ __forceinline__ double block_sum256(double v, double* red) {
 
 // ---- 1a. first column of a panel: d[i], x0, squared-norm partials (no deferred updates;
 // four partials per 64-row block, as the w kernel writes them: the block's sum, then zeros)
+// and the column as a contiguous vector xv[r] (rows i .. n - 1) for the symv kernel
 __global__ __launch_bounds__(256) void tri_colstart_kernel(const double* __restrict__ A, int64_t lda, int n, int i,
                                                            double* __restrict__ npart, double* __restrict__ x0,
-                                                           double* __restrict__ d) {
+                                                           double* __restrict__ d, double* __restrict__ xv) {
   __shared__ double red[256];
   const int tid = threadIdx.x;
   const int r = i + blockIdx.x * TS + tid;
   double sq = 0.0;
   if (tid < TS && r < n) {
     const double val = A[int64_t(r) * lda + i];
+    xv[r] = val;
     if (r == i) d[i] = val;
     if (r == i + 1) *x0 = val;
     if (r >= i + 2) sq = val * val;
@@ -137,7 +139,8 @@ __global__ __launch_bounds__(256) void tri_colstart_kernel(const double* __restr
 // x = C[i+1:, i] (the reflector is v = scale x + (1 - scale x0) e_{i+1}; the w kernel
 // applies that), one 64 x 64 lower tile per workgroup.  Outputs: P[x][y][*], the
 // contribution to y-block x from the tile pairing x and y; S[t] = tile part of x^T C x;
-// on diagonal tiles the panel products V^T x, W^T x over the block's rows.
+// on diagonal tiles the panel products V^T x, W^T x over the block's rows.  x is read from
+// the contiguous copy xv of column i (rows i + 1 ..) that the previous kernel wrote.
 // Each thread holds a 4 x 4 patch of the tile in registers (rows 4 rb .., columns 4 cb ..,
 // rb = tid / 16, cb = tid % 16), loaded as 16-byte pairs (EVEN: the tile's first column is
 // even; otherwise three pairs per row, of which the middle four values are used).  Row
@@ -148,9 +151,10 @@ constexpr int DPP_ROW_ROR8 = 0x128;   // row_ror:8, lane i <-> i + 8 within 16 l
 template <bool EVEN>
 __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict__ A, int64_t lda, int n, int i, int i0,
                                                        int jj, const double* __restrict__ Wp,
-                                                       double* __restrict__ P, double* __restrict__ S,
-                                                       double* __restrict__ SV, double* __restrict__ SW) {
-  __shared__ double vb[TS], vc[TS], rsum[TS];
+                                                       const double* __restrict__ xv, double* __restrict__ P,
+                                                       double* __restrict__ S, double* __restrict__ SV,
+                                                       double* __restrict__ SW) {
+  __shared__ double rsum[TS];
   __shared__ double cpart[16][TS + 1];
   __shared__ double red[8][2][NB];
   const int tid = threadIdx.x;
@@ -202,15 +206,17 @@ __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict_
       tv[k][3] = u[k][2].x;
     }
   }
-  double colv;
-  {
-    const int r = tid < TS ? R0 + tid : C0 + (tid & 63);
-    colv = A[int64_t(min(r, n - 1)) * lda + i];
-    if (r >= n) colv = 0.0;
+  // x on the patch's columns (vcl) and rows (vbl), masked with the tile below
+  double vcl[4], vbl[4];
+  const int rr4 = R0 + 4 * rb;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    vcl[e] = xv[min(c4 + e, n - 1)];
+    vbl[e] = xv[min(rr4 + e, n - 1)];
   }
   // panel rows for V^T x, W^T x (diagonal tiles): 32 columns x 8 groups of 8 rows
   const int pc = tid & 31, pg = tid >> 5;
-  double va[8], wa[8];
+  double va[8], wa[8], xa[8];
   const bool pan = diag && jj > 0;
   if (pan) {
     const int pcc = min(pc, jj - 1);
@@ -219,23 +225,11 @@ __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict_
       const int r = min(R0 + pg * 8 + q, n - 1);
       va[q] = A[int64_t(r) * lda + i0 + pcc];
       wa[q] = Wp[int64_t(r) * NB + pcc];
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const bool ok = pc < jj && R0 + pg * 8 + q < n;
-      va[q] = ok ? va[q] : 0.0;
-      wa[q] = ok ? wa[q] : 0.0;
+      xa[q] = xv[r];
     }
   }
-  if (tid < TS) vb[tid] = colv;
-  else if (tid < 2 * TS) vc[tid - TS] = colv;
-  __syncthreads();
-  double vcl[4], vbl[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    vcl[e] = vc[4 * cb + e];
-    vbl[e] = vb[4 * rb + e];
-  }
+  double xe = 0.0;   // x on row R0 + tid (x^T C x epilogue)
+  if (tid < TS) xe = xv[min(R0 + tid, n - 1)];
   // row sums over the tile's lower part incl. the diagonal; column sums strictly below it
   double rp[4] = {0.0, 0.0, 0.0, 0.0}, cp[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
@@ -270,8 +264,9 @@ __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict_
     double sv = 0.0, sw = 0.0;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      sv += va[q] * vb[pg * 8 + q];
-      sw += wa[q] * vb[pg * 8 + q];
+      const bool ok = pc < jj && R0 + pg * 8 + q < n;
+      sv += ok ? va[q] * xa[q] : 0.0;
+      sw += ok ? wa[q] * xa[q] : 0.0;
     }
     red[pg][0][pc] = sv;
     red[pg][1][pc] = sw;
@@ -282,6 +277,7 @@ __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict_
 #pragma unroll
     for (int q = 0; q < 16; ++q) c_ += cpart[q][tid];
     const double r_ = rsum[tid];
+    const double xb = R0 + tid < n ? xe : 0.0;
     if (diag) {
       P[(int64_t(b) * nbt + b) * TS + tid] = r_ + c_;
     } else {
@@ -289,7 +285,7 @@ __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict_
       P[(int64_t(c) * nbt + b) * TS + tid] = c_;
     }
     // x_b^T (tile contribution), fixed butterfly over the first wave
-    const double sacc = wave_sum(diag ? vb[tid] * (r_ + c_) : 2.0 * (vb[tid] * r_));
+    const double sacc = wave_sum(diag ? xb * (r_ + c_) : 2.0 * (xb * r_));
     if (tid == 0) S[blockIdx.x] = sacc;
   } else if (pan && tid < TS + NB) {
     const int cc = tid - TS;
@@ -323,14 +319,14 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
                                                     const double* __restrict__ SV, const double* __restrict__ SW,
                                                     double* __restrict__ npart_next, double* __restrict__ x0_next,
                                                     double* __restrict__ d, double* __restrict__ e,
-                                                    double* __restrict__ tau_out) {
+                                                    double* __restrict__ tau_out, double* __restrict__ xv_next) {
   __shared__ double Vs[TS][NB + 1], Ws[TS][NB + 1];
   __shared__ double yp[8][TS];
   __shared__ double svq[16][NB], swq[16][NB];
-  __shared__ double vn[NB], wn[NB], sv[NB], sw[NB];
+  __shared__ double vn[NB], wn[NB];
+  __shared__ double svw[4][NB], sww[4][NB];   // per-wave copies of V^T v, W^T v
   __shared__ double colI[TS], colS[TS];
   __shared__ double red[3][4];
-  __shared__ double sc[2];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int s0 = i + 1;
   const int m = n - s0;
@@ -470,43 +466,46 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
     e[i] = beta;
     tau_out[i] = tau;
   }
-  if (tid < 64) {
-    // lanes c < jj: V^T v, W^T v; then (V^T v).(W^T v) and row s0's correction by butterflies
-    double svc = 0.0, swc = 0.0;
-    if (tid < jj) {
-      double b0 = 0.0, b1 = 0.0;
+  // every wave derives the scalars itself (no second block barrier): lanes c < jj form
+  // V^T v and W^T v, the wave's own LDS copy serves its rows below; then (V^T v).(W^T v)
+  // and row s0's correction by butterflies
+  double svc = 0.0, swc = 0.0;
+  if (lane < jj) {
+    double b0 = 0.0, b1 = 0.0;
 #pragma unroll
-      for (int g = 0; g < 16; ++g) {
-        b0 += svq[g][tid];
-        b1 += swq[g][tid];
-      }
-      svc = scale * b0 + cfac * vn[tid];
-      swc = scale * b1 + cfac * wn[tid];
-      sv[tid] = svc;
-      sw[tid] = swc;
+    for (int g = 0; g < 16; ++g) {
+      b0 += svq[g][lane];
+      b1 += swq[g][lane];
     }
-    const double dsw = wave_sum(svc * swc);
-    const double corr0 = wave_sum(tid < jj ? wn[tid] * svc + vn[tid] * swc : 0.0);
-    if (tid == 0) {
-      const double v1 = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
-      const double y0raw = (red[2][0] + red[2][1]) + (red[2][2] + red[2][3]);
-      const double y0 = scale * y0raw + cfac * a00;
-      const double vav = scale * scale * v1 + 2.0 * scale * cfac * y0raw + cfac * cfac * a00;
-      const double alpha = -0.5 * tau * tau * (vav - 2.0 * dsw);
-      sc[0] = alpha;
-      sc[1] = tau * (y0 - corr0) + alpha;   // w of row s0 (v = 1 there)
-    }
+    svc = scale * b0 + cfac * vn[lane];
+    swc = scale * b1 + cfac * wn[lane];
   }
-  __syncthreads();
-  const double alpha = sc[0], w0 = sc[1];
-  // rows x = tid / 4: the quad splits the panel columns (c = part, part + 4, ...) and the
-  // row-sum groups (2 part, 2 part + 1)
+  if (lane < NB) {
+    svw[wv][lane] = svc;
+    sww[wv][lane] = swc;
+  }
+  const double dsw = wave_sum(svc * swc);
+  const double corr0 = wave_sum(lane < jj ? wn[lane] * svc + vn[lane] * swc : 0.0);
+  const double v1 = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+  const double y0raw = (red[2][0] + red[2][1]) + (red[2][2] + red[2][3]);
+  const double y0 = scale * y0raw + cfac * a00;
+  const double vav = scale * scale * v1 + 2.0 * scale * cfac * y0raw + cfac * cfac * a00;
+  const double alpha = -0.5 * tau * tau * (vav - 2.0 * dsw);
+  const double w0 = tau * (y0 - corr0) + alpha;   // w of row s0 (v = 1 there)
+  // the wave's LDS copy is read by other lanes of the same wave only
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // rows x = tid / 4 (a wave's rows only): the quad splits the panel columns
+  // (c = part + 4 k) and the row-sum groups (2 part, 2 part + 1)
   const int x = tid >> 2, part = tid & 3;
   const int r = R0 + x;
   double corr = 0.0, c2 = 0.0;
-  for (int c = part; c < jj; c += 4) {
+#pragma unroll
+  for (int k = 0; k < NB / 4; ++k) {   // columns c >= jj hold zeros in every operand
+    const int c = part + 4 * k;
     const double vr = Vs[x][c], wr = Ws[x][c];
-    corr += wr * sv[c] + vr * sw[c];
+    corr += wr * svw[wv][c] + vr * sww[wv][c];
     c2 += vr * wn[c] + wr * vn[c];
   }
   double yr = yp[2 * part][x] + yp[2 * part + 1][x];
@@ -530,6 +529,7 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
   if (r < n && part == 0) {
     const double val = cs0x - (c2 + (v * w0 + w));
     A[int64_t(r) * lda + s0] = val;
+    xv_next[r] = val;
     if (r == s0) d[s0] = val;
     if (r == s0 + 1) *x0_next = val;
     if (r >= s0 + 2) sq = val * val;
@@ -1426,7 +1426,7 @@ __global__ __launch_bounds__(256) void tri_out_kernel(const double* __restrict__
 }
 
 struct TWs {
-  double *P, *S, *SV, *SW, *npart, *x0, *d, *e, *tau, *Wp, *lam, *bounds, *U, *Z, *Zw, *Gp, *T, *Yp, *Yr, *Y2;
+  double *P, *S, *SV, *SW, *npart, *x0, *xv, *d, *e, *tau, *Wp, *lam, *bounds, *U, *Z, *Zw, *Gp, *T, *Yp, *Yr, *Y2;
   int *clen, *flag;
   uint8_t* piv;
 };
@@ -1444,6 +1444,7 @@ TWs carve_tri(Carve& cv, int64_t n, int64_t ncols) {
   w.SW = cv.take<double>(size_t(nbt * NB));
   w.npart = cv.take<double>(size_t(2 * 4 * nbt));   // two columns' partials, four per row block
   w.x0 = cv.take<double>(2);
+  w.xv = cv.take<double>(size_t(2 * n));   // two columns as contiguous vectors
   w.d = cv.take<double>(size_t(n));
   w.e = cv.take<double>(size_t(n));
   w.tau = cv.take<double>(size_t(n));
@@ -1469,6 +1470,73 @@ __global__ void zero_int_kernel(int* p, int n) {
   if (i < n) p[i] = 0;
 }
 
+// Householder tridiagonalisation of the lower triangle of A (n x n, pitch lda) in place:
+// d, e, tau and the reflectors (below the subdiagonal) land in w and A.
+lrc_status tri_reduce(hipStream_t st, double* A, int n, int64_t lda, const TWs& w) {
+  for (int i0 = 0; i0 < n - 1; i0 += NB) {
+    const int pb = std::min(NB, n - 1 - i0);
+    {
+      const unsigned g = unsigned(cdiv(n - i0, TS));
+      tri_colstart_kernel<<<g, 256, 0, st>>>(A, lda, n, i0, w.npart + (i0 & 1) * 4 * cdiv(n, TS), w.x0 + (i0 & 1),
+                                             w.d, w.xv + (i0 & 1) * n);
+      LRC_LAUNCHED();
+    }
+    for (int jj = 0; jj < pb; ++jj) {
+      const int i = i0 + jj;
+      const int m = n - i - 1;
+      const int nbt = int(cdiv(m, TS));
+      const int par = i & 1, npar = (i + 1) & 1;
+      double* np_cur = w.npart + par * 4 * cdiv(n, TS);
+      double* np_next = w.npart + npar * 4 * cdiv(n, TS);
+      {
+        ProfScope scope("tri_symv_kernel", st, 2.0 * double(m) * double(m),
+                        8.0 * double(m) * double(m + 1) / 2);
+        // 16-byte pairs need an even matrix pitch and base; the tile's first column parity
+        // picks the pair alignment
+        const double* xv = w.xv + par * n;
+        if ((i + 1) % 2 == 0)
+          tri_symv_kernel<true><<<unsigned(nbt * (nbt + 1) / 2), 256, 0, st>>>(A, lda, n, i, i0, jj, w.Wp, xv, w.P,
+                                                                                w.S, w.SV, w.SW);
+        else
+          tri_symv_kernel<false><<<unsigned(nbt * (nbt + 1) / 2), 256, 0, st>>>(A, lda, n, i, i0, jj, w.Wp, xv, w.P,
+                                                                                 w.S, w.SV, w.SW);
+        LRC_LAUNCHED();
+      }
+      {
+        // bytes: the symv partials, the panel rows of V and W, column i (and i+1) read and
+        // written, the new column of W
+        ProfScope scope("tri_w_kernel", st, 4.0 * double(m) * (jj + 1),
+                        8.0 * (double(nbt) * nbt * TS + 2.0 * double(m) * jj + 5.0 * double(m)));
+        if (i % 2 == 0)   // columns i, i + 1 form an aligned pair
+          tri_w_kernel<true><<<unsigned(nbt), 256, 0, st>>>(A, lda, n, i, i0, jj, jj + 1 < pb ? 1 : 0, w.Wp, np_cur,
+                                                            w.x0 + par, w.P, w.S, w.SV, w.SW, np_next, w.x0 + npar,
+                                                            w.d, w.e, w.tau, w.xv + npar * n);
+        else
+          tri_w_kernel<false><<<unsigned(nbt), 256, 0, st>>>(A, lda, n, i, i0, jj, jj + 1 < pb ? 1 : 0, w.Wp, np_cur,
+                                                             w.x0 + par, w.P, w.S, w.SV, w.SW, np_next, w.x0 + npar,
+                                                             w.d, w.e, w.tau, w.xv + npar * n);
+        LRC_LAUNCHED();
+      }
+    }
+    const int j1 = i0 + pb;
+    if (j1 < n) {
+      const int nt = int(cdiv(n - j1, TS));
+      ProfScope scope("tri_syr2k_kernel", st, 2.0 * double(n - j1) * double(n - j1 + 1) * pb, 0.0);
+      tri_syr2k_kernel<<<unsigned(nt * (nt + 1) / 2), 256, 0, st>>>(A, lda, n, i0, pb, j1, w.Wp);
+      LRC_LAUNCHED();
+    }
+  }
+  {
+    // last diagonal entry (and the whole job when n == 1)
+    const int i = n - 1;
+    tri_colstart_kernel<<<1, 256, 0, st>>>(A, lda, n, i, w.npart + (i & 1) * 4 * cdiv(n, TS), w.x0 + (i & 1), w.d,
+                                           w.xv + (i & 1) * n);
+    LRC_LAUNCHED();
+  }
+
+  return LRC_OK;
+}
+
 }  // namespace
 
 size_t tridiag_workspace(int64_t k, int64_t ncols) {
@@ -1489,64 +1557,7 @@ lrc_status tridiag_eig(hipStream_t st, double* A, int64_t k, int64_t lda, int64_
   TWs w = carve_tri(cv, n, ncols);
 
   // 1. tridiagonalisation
-  for (int i0 = 0; i0 < n - 1; i0 += NB) {
-    const int pb = std::min(NB, n - 1 - i0);
-    {
-      const unsigned g = unsigned(cdiv(n - i0, TS));
-      tri_colstart_kernel<<<g, 256, 0, st>>>(A, lda, n, i0, w.npart + (i0 & 1) * 4 * cdiv(n, TS), w.x0 + (i0 & 1),
-                                             w.d);
-      LRC_LAUNCHED();
-    }
-    for (int jj = 0; jj < pb; ++jj) {
-      const int i = i0 + jj;
-      const int m = n - i - 1;
-      const int nbt = int(cdiv(m, TS));
-      const int par = i & 1, npar = (i + 1) & 1;
-      double* np_cur = w.npart + par * 4 * cdiv(n, TS);
-      double* np_next = w.npart + npar * 4 * cdiv(n, TS);
-      {
-        ProfScope scope("tri_symv_kernel", st, 2.0 * double(m) * double(m),
-                        8.0 * double(m) * double(m + 1) / 2);
-        // 16-byte pairs need an even matrix pitch and base; the tile's first column parity
-        // picks the pair alignment
-        if ((i + 1) % 2 == 0)
-          tri_symv_kernel<true><<<unsigned(nbt * (nbt + 1) / 2), 256, 0, st>>>(A, lda, n, i, i0, jj, w.Wp, w.P,
-                                                                                w.S, w.SV, w.SW);
-        else
-          tri_symv_kernel<false><<<unsigned(nbt * (nbt + 1) / 2), 256, 0, st>>>(A, lda, n, i, i0, jj, w.Wp, w.P,
-                                                                                 w.S, w.SV, w.SW);
-        LRC_LAUNCHED();
-      }
-      {
-        // bytes: the symv partials, the panel rows of V and W, column i (and i+1) read and
-        // written, the new column of W
-        ProfScope scope("tri_w_kernel", st, 4.0 * double(m) * (jj + 1),
-                        8.0 * (double(nbt) * nbt * TS + 2.0 * double(m) * jj + 5.0 * double(m)));
-        if (i % 2 == 0)   // columns i, i + 1 form an aligned pair
-          tri_w_kernel<true><<<unsigned(nbt), 256, 0, st>>>(A, lda, n, i, i0, jj, jj + 1 < pb ? 1 : 0, w.Wp, np_cur,
-                                                            w.x0 + par, w.P, w.S, w.SV, w.SW, np_next, w.x0 + npar,
-                                                            w.d, w.e, w.tau);
-        else
-          tri_w_kernel<false><<<unsigned(nbt), 256, 0, st>>>(A, lda, n, i, i0, jj, jj + 1 < pb ? 1 : 0, w.Wp, np_cur,
-                                                             w.x0 + par, w.P, w.S, w.SV, w.SW, np_next, w.x0 + npar,
-                                                             w.d, w.e, w.tau);
-        LRC_LAUNCHED();
-      }
-    }
-    const int j1 = i0 + pb;
-    if (j1 < n) {
-      const int nt = int(cdiv(n - j1, TS));
-      ProfScope scope("tri_syr2k_kernel", st, 2.0 * double(n - j1) * double(n - j1 + 1) * pb, 0.0);
-      tri_syr2k_kernel<<<unsigned(nt * (nt + 1) / 2), 256, 0, st>>>(A, lda, n, i0, pb, j1, w.Wp);
-      LRC_LAUNCHED();
-    }
-  }
-  {
-    // last diagonal entry (and the whole job when n == 1)
-    const int i = n - 1;
-    tri_colstart_kernel<<<1, 256, 0, st>>>(A, lda, n, i, w.npart + (i & 1) * 4 * cdiv(n, TS), w.x0 + (i & 1), w.d);
-    LRC_LAUNCHED();
-  }
+  LRC_TRY(tri_reduce(st, A, n, lda, w));
 
   // 2. eigenvalues
   tri_bounds_kernel<<<1, 256, 0, st>>>(w.d, w.e, n, w.bounds);
