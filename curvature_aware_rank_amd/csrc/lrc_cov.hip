@@ -220,6 +220,210 @@ __global__ __launch_bounds__(NTH, 1) void syrk_bf16_kernel(
       }
 }
 
+
+// ---- bf16 SYRK with direct global -> LDS loads (channel count a multiple of 8, 16-byte
+// aligned rows).  The same tiles, waves and MFMAs as above; the operands travel as
+// buffer loads straight into LDS (16 bytes per lane, no staging registers), four LDS
+// stages of 32 tokens, three of them in flight while one is computed.  A buffer resource
+// per operand spans exactly the split's tokens, so rows past the split (and channels
+// past d, by an out-of-range offset) read as zeros without any masking code.  Token rows
+// sit unpadded (512 bytes) with their 16-byte granules XOR-swizzled by the token index
+// (granule g of token t at slot g ^ 4 (t % 4)), so the transposing fragment reads of four
+// consecutive tokens fall on four different bank groups.
+constexpr int KS2 = 32;                  // tokens per stage
+constexpr int NSTG = 4;                  // LDS stages
+constexpr int ROWB = TB * 2;             // bytes per token row of one operand
+constexpr int OPB = KS2 * ROWB;          // 16 KB: one operand, one stage
+constexpr int STB = 2 * OPB;             // 32 KB: one stage
+constexpr int LDPW = OPB / 1024 / 4;     // 1 KB loads per wave per operand per stage (4)
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Stage barrier: wait until at most N vector memory operations of this wave are
+// outstanding and all its LDS reads have returned (a buffer may be refilled by any wave
+// once everyone has passed the barrier), then synchronise the workgroup.  Written out
+// because the fence of __syncthreads would also wait for the direct loads still in flight.
+#define LRC_VMCNT_BARRIER(N) asm volatile("s_waitcnt vmcnt(" #N ") lgkmcnt(0)\n\ts_barrier" ::: "memory")
+
+__device__ __forceinline__ bf16x8 frag_sw(const uint8_t* base, int off) {
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base + off));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base + off + 4 * ROWB));
+  const short tmp[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  bf16x8 f;
+  __builtin_memcpy(&f, tmp, sizeof(f));
+  return f;
+}
+
+// byte offset in a stage operand of lane `lane`'s first transposed read for the 32-channel
+// block starting at channel ch0 (token 0 of the stage; later 16-token steps add 16 rows)
+__device__ __forceinline__ int frag_off(int ch0, int lane) {
+  const int g = lane >> 4, sl = lane & 15;
+  const int ch = ch0 + 16 * (g & 1) + 4 * (sl & 3);
+  const int tk = 8 * (g >> 1) + (sl >> 2);
+  return tk * ROWB + (((ch >> 3) ^ (4 * (tk & 3))) << 4) + (ch & 7) * 2;
+}
+
+__global__ __launch_bounds__(NTH, 1) void syrk_bf16_dl_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ Y, int64_t ldx, int64_t n, int d, int n1,
+    int n_tiles, int tiles_per_xcd, int splits, int64_t tok_per_split, float* __restrict__ partial) {
+  // one LDS object per stage: the compiler tracks the direct loads per object, so a read
+  // of one stage waits only for that stage's loads (with a shared array it would wait for
+  // all of them)
+  __shared__ __attribute__((aligned(1024))) uint8_t sb0[STB], sb1[STB], sb2[STB], sb3[STB];
+
+  const int b = blockIdx.x;
+  const int xcd = b % NXCD;
+  const int local = b / NXCD;
+  const int split = local / tiles_per_xcd;
+  const int tile = xcd * tiles_per_xcd + local % tiles_per_xcd;
+  if (tile >= n_tiles || split >= splits) return;
+  const TileRC tc = tile_of(tile, n1);
+  const int ti = tc.ti, tj = tc.tj;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave >> 1, wc = wave & 1;
+  const bool wave_dead = (ti == tj) && (wr < wc);
+
+  const int64_t tok_begin = int64_t(split) * tok_per_split;
+  const int64_t tok_end = min<int64_t>(n, tok_begin + tok_per_split);
+  const int nsteps = tok_end > tok_begin ? int((tok_end - tok_begin + KS2 - 1) / KS2) : 0;
+  // buffer resources over the split's token rows (the launch keeps them below 2^31 bytes);
+  // every field is workgroup-uniform, which readfirstlane makes explicit (scalar registers)
+  const int nrec = __builtin_amdgcn_readfirstlane(int((tok_end - tok_begin) * ldx * 2));
+  auto uniform_ptr = [](const uint16_t* p) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(a));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32));
+    return reinterpret_cast<void*>((uint64_t(hi) << 32) | lo);
+  };
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(X + tok_begin * ldx), 0, nrec, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ry =
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(Y + tok_begin * ldx), 0, nrec, 0x00020000);
+
+  // lane byte offsets of its loads: operand op, load j covers token rows 2 q, 2 q + 1
+  // (q = LDPW wave + j) of the stage, lane -> row 2 q + lane / 32, LDS slot lane % 32
+  unsigned voff[2][LDPW];
+#pragma unroll
+  for (int op = 0; op < 2; ++op)
+#pragma unroll
+    for (int j = 0; j < LDPW; ++j) {
+      const int q = LDPW * wave + j;
+      const int t = 2 * q + (lane >> 5);
+      const int gch = (lane & 31) ^ (4 * (t & 3));
+      const int chan = (op ? tj : ti) * TB + 8 * gch;
+      voff[op][j] = chan < d ? unsigned((int64_t(t) * ldx + chan) * 2) : 0x80000000u;
+    }
+  auto issue = [&](uint8_t* dst, int st) {
+    const int soff = int(int64_t(st) * KS2 * ldx * 2);
+#pragma unroll
+    for (int j = 0; j < LDPW; ++j) {
+      const int q = LDPW * wave + j;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(dst + q * 1024), 16, voff[0][j], soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (lds_void_t*)(dst + OPB + q * 1024), 16, voff[1][j], soff, 0,
+                                               0);
+    }
+  };
+
+  int offa[4], offb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    offa[i] = frag_off(wr * 128 + i * 32, lane);
+    offb[i] = frag_off(wc * 128 + i * 32, lane);
+  }
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  auto compute = [&](const uint8_t* xa) {
+    const uint8_t* yb = xa + OPB;
+#pragma unroll
+    for (int kk = 0; kk < KS2 / 16; ++kk) {
+      bf16x8 fa[4], fb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[i] = frag_sw(xa + kk * 16 * ROWB, offa[i]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[j] = frag_sw(yb + kk * 16 * ROWB, offb[j]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // Steady state: before stage s, this wave's loads of stage s are the oldest of three
+  // stages outstanding (2 LDPW each), so vmcnt(16) leaves exactly the two newer ones in
+  // flight; after the barrier every wave's stage-s data is in LDS and every wave has
+  // finished stage s - 1, whose buffer then takes stage s + 3.  The loop is unrolled over
+  // the four stage buffers so that every access names its buffer; the last stages select
+  // buffers at run time and wait for everything.  A wave whose block lies above the
+  // diagonal of a diagonal tile only loads and synchronises.
+  auto buf = [&](int st) -> uint8_t* {
+    const int k = st & 3;
+    return k == 0 ? sb0 : k == 1 ? sb1 : k == 2 ? sb2 : sb3;
+  };
+  // the first three stages unconditionally: stages past the split read zeros
+  issue(sb0, 0);
+  issue(sb1, 1);
+  issue(sb2, 2);
+  int s = 0;
+  if (!wave_dead) {
+    for (; s + 6 < nsteps; s += 4) {
+      LRC_VMCNT_BARRIER(16);
+      issue(sb3, s + 3);
+      compute(sb0);
+      LRC_VMCNT_BARRIER(16);
+      issue(sb0, s + 4);
+      compute(sb1);
+      LRC_VMCNT_BARRIER(16);
+      issue(sb1, s + 5);
+      compute(sb2);
+      LRC_VMCNT_BARRIER(16);
+      issue(sb2, s + 6);
+      compute(sb3);
+    }
+    for (; s < nsteps; ++s) {
+      if (s + 3 < nsteps) {
+        LRC_VMCNT_BARRIER(16);
+        issue(buf(s + 3), s + 3);
+      } else {
+        LRC_VMCNT_BARRIER(0);
+      }
+      compute(buf(s));
+    }
+  } else {
+    for (; s < nsteps; ++s) {
+      if (s + 3 < nsteps) {
+        LRC_VMCNT_BARRIER(16);
+        issue(buf(s + 3), s + 3);
+      } else {
+        LRC_VMCNT_BARRIER(0);
+      }
+    }
+  }
+
+  const int r_base = wr * 128, c_base = wc * 128;
+  float* part = partial + (int64_t(split) * n_tiles + tile) * (TB * TB);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int lr = r_base + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int lc = c_base + j * 32 + (lane & 31);
+        part[lr * TB + lc] = acc[i][j][e];
+      }
+}
+
 // C[lower] += sum over splits of the partial tiles, in split order (bit-reproducible).
 // Block (tile, q) handles 256 consecutive float4 of the tile; loads are batched 8 splits
 // at a time from clamped addresses, then masked.
@@ -383,7 +587,13 @@ lrc_status launch_syrk_bf16(hipStream_t st, const uint16_t* X, const uint16_t* Y
   const double tri = double(d) * double(d + 1) / 2;
   ProfScope scope("syrk_bf16_kernel", st, 2.0 * double(n) * tri,
                   double(n) * double(d) * 2.0 * (X == Y ? 1 : 2) + 8.0 * tri);
-  if (vec)
+  const int64_t tok_per_split = int64_t(p.steps_per_split) * KS;
+  // direct-load kernel: buffer offsets of a split (rows of ldx bf16, plus the three
+  // stages the pipeline may fetch past its end) must stay below 2^31
+  if (vec && (tok_per_split + 3 * KS2) * ldx * 2 < (int64_t(1) << 31))
+    syrk_bf16_dl_kernel<<<grid, NTH, 0, st>>>(X, Y, ldx, n, int(d), p.n1, p.n_tiles, p.tiles_per_xcd, p.splits,
+                                              tok_per_split, partial);
+  else if (vec)
     syrk_bf16_kernel<true><<<grid, NTH, 0, st>>>(X, Y, ldx, n, int(d), p.n1, p.n_tiles, p.tiles_per_xcd,
                                                  p.splits, p.steps_per_split, partial);
   else
