@@ -260,10 +260,13 @@ __global__ __launch_bounds__(64) void potf2_kernel(float* __restrict__ L, int64_
         const float inv = 1.0f / djj;
         a[j] = lane == j ? djj : (lane > j ? a[j] * inv : a[j]);
         const float lij = a[j];
+        // every lane updates its whole row: entries above the diagonal (c > lane) are never
+        // read as pivots or multipliers (those come from lanes c > j, column j) and stay
+        // finite; the store writes zeros there
 #pragma unroll
         for (int c = j + 1; c < NB; ++c) {
           const float lc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[j]), c));
-          a[c] = (c <= lane) ? fmaf(-lij, lc, a[c]) : a[c];
+          a[c] = fmaf(-lij, lc, a[c]);
         }
       }
     }

@@ -37,7 +37,7 @@ namespace {
 constexpr int NB = 32;          // tridiagonalisation panel width
 constexpr int TS = 64;          // tile and row-block size of the symv / w kernels
 constexpr int BW = 128;         // reflectors per back-transformation block
-constexpr int BT_CHUNK = 256;   // rows per partial of V^T Z
+constexpr int BT_CHUNK = 128;   // rows per partial of V^T Z
 constexpr int G_CHUNK = 1024;   // rows per partial of V^T V
 constexpr int BIS_PTS = 16;     // Sturm points per eigenvalue per multisection step
 constexpr int BIS_ITERS = 14;   // 17^14 > 2^57: the interval shrinks below fp64 resolution
@@ -1285,11 +1285,24 @@ __global__ __launch_bounds__(256) void bt_ty_kernel(const double* __restrict__ Y
   __shared__ double st[16][BW + 1];
   const int tid = threadIdx.x;
   const int c0 = blockIdx.x * 64, a0 = blockIdx.y * 16;
-  for (int q = tid; q < BW * 64; q += 256) {
-    const int l = q >> 6, cc = q & 63;
-    sy[l][cc] = c0 + cc < ncols ? Y[int64_t(l) * ncols + c0 + cc] : 0.0;
+  // every load first (clamped addresses), then the LDS stores with the masks
+  constexpr int NY = BW * 64 / 256, NT = 16 * BW / 256;
+  double gy[NY], gt[NT];
+  const int ccy = tid & 63, ccl = min(c0 + ccy, ncols - 1);
+#pragma unroll
+  for (int u = 0; u < NY; ++u) gy[u] = Y[int64_t((tid >> 6) + 4 * u) * ncols + ccl];
+#pragma unroll
+  for (int u = 0; u < NT; ++u) {
+    const int q = tid + 256 * u;
+    gt[u] = T[(a0 + q / BW) * BW + q % BW];
   }
-  for (int q = tid; q < 16 * BW; q += 256) st[q / BW][q % BW] = T[(a0 + q / BW) * BW + q % BW];
+#pragma unroll
+  for (int u = 0; u < NY; ++u) sy[(tid >> 6) + 4 * u][ccy] = c0 + ccy < ncols ? gy[u] : 0.0;
+#pragma unroll
+  for (int u = 0; u < NT; ++u) {
+    const int q = tid + 256 * u;
+    st[q / BW][q % BW] = gt[u];
+  }
   __syncthreads();
   const int ar = tid >> 4, cq = (tid & 15) * 4;
   double acc[4] = {0.0, 0.0, 0.0, 0.0};
