@@ -21,6 +21,11 @@ constexpr int GK = 32;
 constexpr int GPE = (GT * GK) / 256;   // staged elements per thread per operand
 constexpr int WT = GT / 32;            // 16 x 16 blocks per wave side
 
+// VEC: m, n, k, lda, ldb multiples of 4 and A, B 16-byte aligned.  The staged element
+// order makes elements e .. e + 3 (e a multiple of 4) contiguous in memory for every
+// layout, so each thread stages its operands as 16-byte groups, each wholly inside or
+// wholly outside the matrix (groups are clamped as a whole and masked at the LDS store).
+template <bool VEC>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(unsigned flags, int m, int n, int k, float alpha,
                                                        const float* __restrict__ A, int64_t lda, int64_t sA,
                                                        const float* __restrict__ B, int64_t ldb, int64_t sB,
@@ -57,22 +62,48 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(unsigned flags, int m, in
   };
   float ga[GPE], gb[GPE];
   auto load = [&](int k0) {
+    if (VEC) {
 #pragma unroll
-    for (int it = 0; it < GPE; ++it) {
-      const int e = tid + it * 256;
-      int r, kk, c, kk2;
-      a_rk(e, r, kk);
-      b_kc(e, kk2, c);
-      const int gr = min(row0 + r, m - 1), gk = min(k0 + kk, k - 1);
-      const int gc = min(col0 + c, n - 1), gk2 = min(k0 + kk2, k - 1);
-      ga[it] = ta ? A[int64_t(gk) * lda + gr] : A[int64_t(gr) * lda + gk];
-      gb[it] = tb ? B[int64_t(gc) * ldb + gk2] : B[int64_t(gk2) * ldb + gc];
+      for (int g = 0; g < GPE / 4; ++g) {
+        const int e = 4 * (tid + g * 256);
+        int r, kk, c, kk2;
+        a_rk(e, r, kk);
+        b_kc(e, kk2, c);
+        // the group runs along kk (A) / c (B) when not transposed, along r / kk2 otherwise
+        const int gr = ta ? min(row0 + r, m - 4) : min(row0 + r, m - 1);
+        const int gk = ta ? min(k0 + kk, k - 1) : min(k0 + kk, k - 4);
+        const int gc = tb ? min(col0 + c, n - 1) : min(col0 + c, n - 4);
+        const int gk2 = tb ? min(k0 + kk2, k - 4) : min(k0 + kk2, k - 1);
+        const float4 va = *reinterpret_cast<const float4*>(ta ? A + int64_t(gk) * lda + gr : A + int64_t(gr) * lda + gk);
+        const float4 vb = *reinterpret_cast<const float4*>(tb ? B + int64_t(gc) * ldb + gk2 : B + int64_t(gk2) * ldb + gc);
+        ga[4 * g] = va.x;
+        ga[4 * g + 1] = va.y;
+        ga[4 * g + 2] = va.z;
+        ga[4 * g + 3] = va.w;
+        gb[4 * g] = vb.x;
+        gb[4 * g + 1] = vb.y;
+        gb[4 * g + 2] = vb.z;
+        gb[4 * g + 3] = vb.w;
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < GPE; ++it) {
+        const int e = tid + it * 256;
+        int r, kk, c, kk2;
+        a_rk(e, r, kk);
+        b_kc(e, kk2, c);
+        const int gr = min(row0 + r, m - 1), gk = min(k0 + kk, k - 1);
+        const int gc = min(col0 + c, n - 1), gk2 = min(k0 + kk2, k - 1);
+        ga[it] = ta ? A[int64_t(gk) * lda + gr] : A[int64_t(gr) * lda + gk];
+        gb[it] = tb ? B[int64_t(gc) * ldb + gk2] : B[int64_t(gk2) * ldb + gc];
+      }
     }
   };
   auto store = [&](int k0) {
 #pragma unroll
     for (int it = 0; it < GPE; ++it) {
-      const int e = tid + it * 256;
+      // VEC: group g = it / 4 holds elements 4 (tid + 256 g) + it % 4
+      const int e = VEC ? 4 * (tid + (it / 4) * 256) + (it % 4) : tid + it * 256;
       int r, kk, c, kk2;
       a_rk(e, r, kk);
       b_kc(e, kk2, c);
@@ -371,7 +402,14 @@ lrc_status gemm_f32(hipStream_t st, unsigned flags, int64_t m, int64_t n, int64_
   if (flags & (GEMM_K_FROM_COL | GEMM_K_FROM_ROW | GEMM_K_TO_ROW)) fl *= 0.5;
   if (flags & GEMM_LOWER) fl *= 0.5;
   ProfScope scope("gemm_f32_kernel", st, fl, 4.0 * double(batch) * (double(m) * k + double(k) * n + 2.0 * double(m) * n));
-  gemm_f32_kernel<<<grid, 256, 0, st>>>(flags, int(m), int(n), int(k), alpha, A, lda, sA, B, ldb, sB, beta, C, ldc, sC);
+  const bool vec = m % 4 == 0 && n % 4 == 0 && k % 4 == 0 && lda % 4 == 0 && ldb % 4 == 0 && sA % 4 == 0 &&
+                   sB % 4 == 0 && reinterpret_cast<uintptr_t>(A) % 16 == 0 && reinterpret_cast<uintptr_t>(B) % 16 == 0;
+  if (vec)
+    gemm_f32_kernel<true><<<grid, 256, 0, st>>>(flags, int(m), int(n), int(k), alpha, A, lda, sA, B, ldb, sB, beta, C,
+                                                ldc, sC);
+  else
+    gemm_f32_kernel<false><<<grid, 256, 0, st>>>(flags, int(m), int(n), int(k), alpha, A, lda, sA, B, ldb, sB, beta,
+                                                 C, ldc, sC);
   LRC_LAUNCHED();
   return LRC_OK;
 }
