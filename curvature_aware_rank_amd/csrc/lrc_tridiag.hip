@@ -546,7 +546,9 @@ constexpr int SYP = 64 + 2;   // LDS pitch (doubles) of an operand k row
 
 __global__ __launch_bounds__(256) void tri_syr2k_kernel(double* __restrict__ A, int64_t lda, int n, int i0, int pb,
                                                         int j1, const double* __restrict__ Wp) {
-  __shared__ double opa[2 * NB][SYP], opb[2 * NB][SYP];
+  // the K = 64 product in two halves through one LDS pair (V_r W_c^T, then W_r V_c^T), so
+  // that four workgroups fit on a CU
+  __shared__ double opa[NB][SYP], opb[NB][SYP];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave >> 1, wc = wave & 1;
@@ -567,49 +569,58 @@ __global__ __launch_bounds__(256) void tri_syr2k_kernel(double* __restrict__ A, 
         const int cc = min(C0 + wc * 32 + j * 16 + l16, n - 1);
         old[i][j][e] = A[int64_t(r) * lda + cc];
       }
-  // operands: thread takes row x = tid / 4 and panel columns (tid % 4) * 8 .. + 7
+  // operands: thread takes row x = tid / 4 and panel columns (tid % 4) * 8 .. + 7 as four
+  // 16-byte pairs (the panel starts at an even column; pairs past pb are masked below)
   const int x = tid >> 2, t0 = (tid & 3) * 8;
-  double vr[8], wr8[8], vc[8], wc8[8];
+  double2 vr[4], wr8[4], vc[4], wc8[4];
   {
     const int r = min(R0 + x, n - 1), cc = min(C0 + x, n - 1);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int tc = min(t0 + u, pb - 1);   // panel columns past pb are masked below
-      vr[u] = A[int64_t(r) * lda + i0 + tc];
-      wr8[u] = Wp[int64_t(r) * NB + tc];
-      vc[u] = A[int64_t(cc) * lda + i0 + tc];
-      wc8[u] = Wp[int64_t(cc) * NB + tc];
+    for (int u = 0; u < 4; ++u) {
+      const int tc = min(t0 + 2 * u, (pb - 1) & ~1);
+      vr[u] = *reinterpret_cast<const double2*>(A + int64_t(r) * lda + i0 + tc);
+      wr8[u] = *reinterpret_cast<const double2*>(Wp + int64_t(r) * NB + tc);
+      vc[u] = *reinterpret_cast<const double2*>(A + int64_t(cc) * lda + i0 + tc);
+      wc8[u] = *reinterpret_cast<const double2*>(Wp + int64_t(cc) * NB + tc);
     }
   }
-  {
-    const bool okr = R0 + x < n, okc = C0 + x < n;
+  const bool okr = R0 + x < n, okc = C0 + x < n;
+  auto stage = [&](const double2 (&ra)[4], bool oka, const double2 (&rb)[4], bool okb) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const bool okt = t0 + u < pb;
-      opa[t0 + u][x] = okr && okt ? vr[u] : 0.0;        // k < NB: V_r
-      opa[NB + t0 + u][x] = okr && okt ? wr8[u] : 0.0;  // k >= NB: W_r
-      opb[t0 + u][x] = okc && okt ? wc8[u] : 0.0;       // k < NB: W_c
-      opb[NB + t0 + u][x] = okc && okt ? vc[u] : 0.0;   // k >= NB: V_c
+    for (int u = 0; u < 4; ++u) {
+      const bool ok0 = t0 + 2 * u < pb, ok1 = t0 + 2 * u + 1 < pb;
+      opa[t0 + 2 * u][x] = oka && ok0 ? ra[u].x : 0.0;
+      opa[t0 + 2 * u + 1][x] = oka && ok1 ? ra[u].y : 0.0;
+      opb[t0 + 2 * u][x] = okb && ok0 ? rb[u].x : 0.0;
+      opb[t0 + 2 * u + 1][x] = okb && ok1 ? rb[u].y : 0.0;
     }
-  }
-  __syncthreads();
+  };
   f64x4 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+  auto mma = [&]() {
 #pragma unroll
-  for (int kk = 0; kk < 2 * NB; kk += 4) {
-    double a[2], bb[2];
+    for (int kk = 0; kk < NB; kk += 4) {
+      double a[2], bb[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) a[i] = opa[kk + lq][wr * 32 + i * 16 + l16];
+      for (int i = 0; i < 2; ++i) a[i] = opa[kk + lq][wr * 32 + i * 16 + l16];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) bb[j] = opb[kk + lq][wc * 32 + j * 16 + l16];
+      for (int j = 0; j < 2; ++j) bb[j] = opb[kk + lq][wc * 32 + j * 16 + l16];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], bb[j], acc[i][j], 0, 0, 0);
-  }
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], bb[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  stage(vr, okr, wc8, okc);   // V_r W_c^T
+  __syncthreads();
+  mma();
+  __syncthreads();
+  stage(wr8, okr, vc, okc);   // W_r V_c^T
+  __syncthreads();
+  mma();
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
