@@ -157,13 +157,15 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(unsigned flags, int m, in
 // fp32 values are exact in fp64, sums are fp64.  The reduction runs in chunks of GRK
 // staged through LDS as doubles; the next chunk's loads are in flight during the MFMAs.
 constexpr int GRK = 32;
-constexpr int GRP = 64 + 2;   // LDS pitch (doubles) of a k row
+constexpr int GRP = 64 + 4;   // LDS pitch (floats) of a k row
 
+template <bool VEC>
 __global__ __launch_bounds__(256) void gram_f64_kernel(bool rows, int p, int q, const float* __restrict__ M,
                                                        int64_t ldm, int64_t sM, double* __restrict__ G,
                                                        int64_t ldg, int64_t sG) {
-  __shared__ double xs[GRK][GRP];
-  __shared__ double ys[GRK][GRP];
+  // operands stay fp32 in LDS and are widened (exactly) as the MFMA fragments are read
+  __shared__ float xs[GRK][GRP];
+  __shared__ float ys[GRK][GRP];
   M += blockIdx.z * sM;
   G += blockIdx.z * sG;
   int lin = blockIdx.x, ti = 0;
@@ -175,35 +177,60 @@ __global__ __launch_bounds__(256) void gram_f64_kernel(bool rows, int p, int q, 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave >> 1, wc = wave & 1;
-  // staging: 8 elements per thread per operand.  rows: element (c, kk) at M[c * ldm + k];
-  // thread takes c = tid / 4 (0..63), kk = (tid % 4) * 8 + u.  cols: element at
-  // M[k * ldm + c]; thread takes kk = tid / 64 + 4 u, c = tid % 64.
-  float gx[8], gy[8];
+  // staging: 8 elements per thread per operand, as two groups of 4 consecutive elements in
+  // memory.  rows: element (c, kk) at M[c * ldm + k]; thread takes c = tid / 4,
+  // kk = (tid % 4) * 8 + 4 g + u.  cols: element at M[k * ldm + c]; thread takes
+  // kk = tid / 16 + 16 g, c = (tid % 16) * 4 + u.  VEC (dim, red, ldm multiples of 4, 16-byte
+  // base): each group is one 16-byte load, wholly in or out of range.
+  auto elem = [&](int g, int u, int& c, int& kk) {
+    if (rows) { c = tid >> 2; kk = (tid & 3) * 8 + 4 * g + u; } else { kk = (tid >> 4) + 16 * g; c = (tid & 15) * 4 + u; }
+  };
+  float gx[2][4], gy[2][4];
   auto load = [&](int k0) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      int c, kk;
-      if (rows) { c = tid >> 2; kk = (tid & 3) * 8 + u; } else { kk = (tid >> 6) + 4 * u; c = tid & 63; }
-      const int gk = min(k0 + kk, red - 1);
-      const int ci = min(ti * 64 + c, dim - 1), cj = min(tj * 64 + c, dim - 1);
-      if (rows) {
-        gx[u] = M[int64_t(ci) * ldm + gk];
-        gy[u] = M[int64_t(cj) * ldm + gk];
+    for (int g = 0; g < 2; ++g) {
+      if (VEC) {
+        int c, kk;
+        elem(g, 0, c, kk);
+        if (rows) {
+          const int gk = min(k0 + kk, red - 4);
+          const int ci = min(ti * 64 + c, dim - 1), cj = min(tj * 64 + c, dim - 1);
+          const float4 vx = *reinterpret_cast<const float4*>(M + int64_t(ci) * ldm + gk);
+          const float4 vy = *reinterpret_cast<const float4*>(M + int64_t(cj) * ldm + gk);
+          gx[g][0] = vx.x; gx[g][1] = vx.y; gx[g][2] = vx.z; gx[g][3] = vx.w;
+          gy[g][0] = vy.x; gy[g][1] = vy.y; gy[g][2] = vy.z; gy[g][3] = vy.w;
+        } else {
+          const int gk = min(k0 + kk, red - 1);
+          const int ci = min(ti * 64 + c, dim - 4), cj = min(tj * 64 + c, dim - 4);
+          const float4 vx = *reinterpret_cast<const float4*>(M + int64_t(gk) * ldm + ci);
+          const float4 vy = *reinterpret_cast<const float4*>(M + int64_t(gk) * ldm + cj);
+          gx[g][0] = vx.x; gx[g][1] = vx.y; gx[g][2] = vx.z; gx[g][3] = vx.w;
+          gy[g][0] = vy.x; gy[g][1] = vy.y; gy[g][2] = vy.z; gy[g][3] = vy.w;
+        }
       } else {
-        gx[u] = M[int64_t(gk) * ldm + ci];
-        gy[u] = M[int64_t(gk) * ldm + cj];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          int c, kk;
+          elem(g, u, c, kk);
+          const int gk = min(k0 + kk, red - 1);
+          const int ci = min(ti * 64 + c, dim - 1), cj = min(tj * 64 + c, dim - 1);
+          gx[g][u] = rows ? M[int64_t(ci) * ldm + gk] : M[int64_t(gk) * ldm + ci];
+          gy[g][u] = rows ? M[int64_t(cj) * ldm + gk] : M[int64_t(gk) * ldm + cj];
+        }
       }
     }
   };
   auto store = [&](int k0) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      int c, kk;
-      if (rows) { c = tid >> 2; kk = (tid & 3) * 8 + u; } else { kk = (tid >> 6) + 4 * u; c = tid & 63; }
-      const bool okk = k0 + kk < red;
-      xs[kk][c] = (okk && ti * 64 + c < dim) ? double(gx[u]) : 0.0;
-      ys[kk][c] = (okk && tj * 64 + c < dim) ? double(gy[u]) : 0.0;
-    }
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        int c, kk;
+        elem(g, u, c, kk);
+        const bool okk = k0 + kk < red;
+        xs[kk][c] = (okk && ti * 64 + c < dim) ? gx[g][u] : 0.f;
+        ys[kk][c] = (okk && tj * 64 + c < dim) ? gy[g][u] : 0.f;
+      }
   };
   f64x4 acc[2][2];
 #pragma unroll
@@ -221,9 +248,9 @@ __global__ __launch_bounds__(256) void gram_f64_kernel(bool rows, int p, int q, 
     for (int kk = 0; kk < GRK; kk += 4) {
       double a[2], b[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = xs[kk + lq][wr * 32 + i * 16 + l16];
+      for (int i = 0; i < 2; ++i) a[i] = double(xs[kk + lq][wr * 32 + i * 16 + l16]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = ys[kk + lq][wc * 32 + j * 16 + l16];
+      for (int j = 0; j < 2; ++j) b[j] = double(ys[kk + lq][wc * 32 + j * 16 + l16]);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -422,7 +449,12 @@ lrc_status gram_f64(hipStream_t st, bool rows, int64_t p, int64_t q, const float
   const double other = rows ? double(q) : double(p);
   ProfScope scope("gram_f64_kernel", st, double(batch) * double(dim) * double(dim + 1) * other,
                   double(batch) * (4.0 * double(p) * double(q) + 4.0 * double(dim) * double(dim + 1)));
-  gram_f64_kernel<<<grid, 256, 0, st>>>(rows, int(p), int(q), M, ldm, sM, G, ldg, sG);
+  const bool vec = dim % 4 == 0 && (rows ? q : p) % 4 == 0 && ldm % 4 == 0 && sM % 4 == 0 &&
+                   reinterpret_cast<uintptr_t>(M) % 16 == 0;
+  if (vec)
+    gram_f64_kernel<true><<<grid, 256, 0, st>>>(rows, int(p), int(q), M, ldm, sM, G, ldg, sG);
+  else
+    gram_f64_kernel<false><<<grid, 256, 0, st>>>(rows, int(p), int(q), M, ldm, sM, G, ldg, sG);
   LRC_LAUNCHED();
   return LRC_OK;
 }
