@@ -770,15 +770,35 @@ __device__ __forceinline__ double start_value(int j, int k) {
 //  B) one wave per cluster (a lone eigenvalue is a cluster of one), members in order:
 //     orthogonalise the first iterate against the cluster's finished vectors (modified
 //     Gram-Schmidt), normalise, second solve, orthogonalise again, normalise.
-// The recurrences are sequential, so lane 0 runs them out of LDS while the whole wave
-// streams their inputs and outputs in chunks of CH steps (the next chunk's loads in
-// flight during the current chunk's recurrence).  The per-vector arrays are vector
-// major: LU records {1/pivot, u1, u2, multiplier} (32 B) and row-interchange flags, and
-// the iterates Zw (one row of n per vector); a transpose writes Z (n x ncols) at the end.
-// The orthogonalisation and scaling passes use all lanes (sums per lane in row order,
-// then a fixed butterfly).
-constexpr int CH = 256;   // recurrence steps per staged chunk
-constexpr int CPL = CH / 64;
+// The recurrences are sequential.  They run in chunks of 64 steps whose inputs sit in
+// registers, step i's in lane i (the next chunk's loads in flight meanwhile); the wave
+// evaluates every step uniformly with the operands taken by readlane, so no memory
+// latency enters the dependence chain, and lane 0 drops each step's results into LDS,
+// from where the whole wave writes them out after the chunk.  Divisions are a hardware
+// reciprocal refined by a Newton step, the quotient then corrected by its residual.
+// The per-vector arrays are vector major: LU records {1/pivot, u1, u2, multiplier}
+// (32 B) and row-interchange flags, and the iterates Zw (one row of n per vector); a
+// transpose writes Z (n x ncols) at the end.  The orthogonalisation and scaling passes
+// use all lanes (sums per lane in row order, then a fixed butterfly).
+constexpr int CH = 64;   // recurrence steps per chunk (one per lane)
+
+// lane l's value of a double (l a compile-time constant after unrolling)
+__device__ __forceinline__ double lane_of(double v, int l) {
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
+                          __builtin_amdgcn_readlane(__double2loint(v), l));
+}
+
+// 1 / b: hardware reciprocal refined by one Newton step
+__device__ __forceinline__ double recip(double b) {
+  double r = __builtin_amdgcn_rcp(b);
+  return fma(r, fma(-b, r, 1.0), r);
+}
+
+// a / b from r ~ 1 / b, corrected by the residual of the product
+__device__ __forceinline__ double quot(double a, double b, double r) {
+  const double q = a * r;
+  return fma(r, fma(-q, b, a), q);
+}
 
 // max over the 64 lanes (exact in any order)
 __device__ __forceinline__ double wave_max(double v) {
@@ -789,62 +809,46 @@ __device__ __forceinline__ double wave_max(double v) {
 
 // back-substitution z <- U^-1 z on vector j (records R, iterate z), chunks from the end;
 // returns ||z||^2 (to every lane)
-__device__ double inv_usolve(const double* __restrict__ R, double* __restrict__ z, int n, double (*s_in)[CH][4],
-                             double (*s_z)[CH], double* s_out, double* s_sc) {
+__device__ double inv_usolve(const double* __restrict__ R, double* __restrict__ z, int n,
+                             double* __restrict__ s_out) {
   const int lane = threadIdx.x;
   const int nch = (n + CH - 1) / CH;
-  double gr[CPL][4], gz[CPL];
-  auto load = [&](int c) {
-#pragma unroll
-    for (int u = 0; u < CPL; ++u) {
-      const int k = min(c * CH + lane + 64 * u, n - 1);
-      const f64x2 a = *reinterpret_cast<const f64x2*>(R + int64_t(k) * 4);
-      const f64x2 b = *reinterpret_cast<const f64x2*>(R + int64_t(k) * 4 + 2);
-      gr[u][0] = a[0];
-      gr[u][1] = a[1];
-      gr[u][2] = b[0];
-      gr[u][3] = b[1];
-      gz[u] = z[k];
-    }
-  };
-  auto stage = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < CPL; ++u) {
-      const int i = lane + 64 * u;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) s_in[buf][i][t] = gr[u][t];
-      s_z[buf][i] = gz[u];
-    }
+  double r0, r1, r2, zz;   // this lane's step of the current chunk
+  double n0, n1, n2, nz;   // the next (lower) chunk, in flight
+  auto load = [&](int c, double& a0, double& a1, double& a2, double& az) {
+    const int k = min(c * CH + lane, n - 1);
+    const f64x2 u = *reinterpret_cast<const f64x2*>(R + int64_t(k) * 4);
+    const f64x2 v = *reinterpret_cast<const f64x2*>(R + int64_t(k) * 4 + 2);
+    a0 = u[0];
+    a1 = u[1];
+    a2 = v[0];
+    az = z[k];
   };
   double x1 = 0.0, x2 = 0.0, nrm2 = 0.0;
-  load(nch - 1);
-  stage((nch - 1) & 1);
+  load(nch - 1, r0, r1, r2, zz);
   for (int c = nch - 1; c >= 0; --c) {
-    const int buf = c & 1;
-    if (c > 0) load(c - 1);
-    __syncthreads();
+    if (c > 0) load(c - 1, n0, n1, n2, nz);
     const int cnt = min(CH, n - c * CH);
-    if (lane == 0) {
-      #pragma unroll 8
-      for (int i = cnt - 1; i >= 0; --i) {
-        const double xk = (s_z[buf][i] - s_in[buf][i][1] * x1 - s_in[buf][i][2] * x2) * s_in[buf][i][0];
-        s_out[i] = xk;
+#pragma unroll
+    for (int i = CH - 1; i >= 0; --i) {
+      if (i < cnt) {   // uniform
+        const double xk = (lane_of(zz, i) - lane_of(r1, i) * x1 - lane_of(r2, i) * x2) * lane_of(r0, i);
+        if (lane == 0) s_out[i] = xk;
         nrm2 += xk * xk;
         x2 = x1;
         x1 = xk;
       }
     }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < CPL; ++u) {
-      const int i = lane + 64 * u;
-      if (i < cnt) z[c * CH + i] = s_out[i];
-    }
-    if (c > 0) stage(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): lane 0's stores, read by every lane
+    __builtin_amdgcn_wave_barrier();
+    if (lane < cnt) z[c * CH + lane] = s_out[lane];
+    __builtin_amdgcn_wave_barrier();
+    r0 = n0;
+    r1 = n1;
+    r2 = n2;
+    zz = nz;
   }
-  if (lane == 0) s_sc[0] = nrm2;
-  __syncthreads();
-  return s_sc[0];
+  return nrm2;   // uniform: every lane ran the same recurrence
 }
 
 __global__ __launch_bounds__(64) void tri_inviter_a_kernel(const double* __restrict__ d, const double* __restrict__ e,
@@ -853,12 +857,9 @@ __global__ __launch_bounds__(64) void tri_inviter_a_kernel(const double* __restr
                                                            const int* __restrict__ clen, const int* __restrict__ flag,
                                                            double* __restrict__ Rall, uint8_t* __restrict__ Pall,
                                                            double* __restrict__ Zw) {
-  __shared__ double s_in[2][CH][4];
-  __shared__ double s_z[2][CH];
   __shared__ double s_out[CH];
   __shared__ double s_rec[CH][4];
   __shared__ uint8_t s_piv[CH];
-  __shared__ double s_sc[1];
   const int jv = blockIdx.x;
   if (*flag) return;
   const int lane = threadIdx.x;
@@ -873,61 +874,45 @@ __global__ __launch_bounds__(64) void tri_inviter_a_kernel(const double* __restr
   double* z = Zw + int64_t(jv) * n;
   const int nm1 = n - 1;
   // ---- factor T - lmb I = P L U (steps k = 0 .. n-2, then the last pivot) and, in the
-  //      same pass, y = L^-1 P z0 for the start vector z0 (generated on the fly)
-  // inputs of step k: e[k], d[k+1], e[k+1]; chunk c stages d[cCH+1 ..], e[cCH ..] (CH + 1)
-  double (*s_d)[CH] = s_z;   // the factor pass uses the z staging buffers for d
-  double gd[CPL], ge[CPL], ge_last = 0.0;
-  auto load_de = [&](int c) {
-#pragma unroll
-    for (int u = 0; u < CPL; ++u) {
-      const int k = c * CH + lane + 64 * u;
-      gd[u] = d[min(k + 1, n - 1)];
-      ge[u] = e[min(k, max(n - 2, 0))];
-    }
-    ge_last = e[min(c * CH + CH, max(n - 2, 0))];
-  };
-  auto stage_de = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < CPL; ++u) {
-      const int i = lane + 64 * u;
-      s_d[buf][i] = gd[u];
-      s_in[buf][i][0] = ge[u];
-    }
-    if (lane == 0) s_in[buf][0][1] = ge_last;   // e at the chunk's end, for its last step
+  //      same pass, y = L^-1 P z0 for the start vector z0 (generated on the fly).
+  // Step k reads e[k], d[k+1], e[k+1]; lane i of chunk c holds e[cCH+i] and d[cCH+i+1],
+  // e[k+1] of the chunk's last step is e[cCH+CH] (held by every lane).
+  double ge, gd, gx, ne, nd_, nx;
+  auto load_de = [&](int c, double& a_e, double& a_d, double& a_x) {
+    const int k = c * CH + lane;
+    a_e = e[min(k, max(n - 2, 0))];
+    a_d = d[min(k + 1, n - 1)];
+    a_x = e[min(c * CH + CH, max(n - 2, 0))];
   };
   double cd = d[0] - lmb, cs = n > 1 ? e[0] : 0.0;
   double ycur = start_value(jv, 0);
   const int nchf = (nm1 + CH - 1) / CH;
-  if (nchf > 0) {
-    load_de(0);
-    stage_de(0);
-  }
+  if (nchf > 0) load_de(0, ge, gd, gx);
   for (int c = 0; c < nchf; ++c) {
-    const int buf = c & 1;
-    if (c + 1 < nchf) load_de(c + 1);
-    __syncthreads();
+    if (c + 1 < nchf) load_de(c + 1, ne, nd_, nx);
     const int cnt = min(CH, nm1 - c * CH);
-    if (lane == 0) {
-      #pragma unroll 8
-      for (int i = 0; i < cnt; ++i) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      if (i < cnt) {   // uniform
         const int k = c * CH + i;
-        const double sub = s_in[buf][i][0];
-        const double nd = s_d[buf][i] - lmb;
-        const double ns = k + 1 < nm1 ? (i + 1 < CH ? s_in[buf][i + 1][0] : s_in[buf][0][1]) : 0.0;
+        const double sub = lane_of(ge, i);
+        const double nd = lane_of(gd, i) - lmb;
+        const double ns = k + 1 < nm1 ? (i + 1 < CH ? lane_of(ge, i + 1) : gx) : 0.0;
         double piv_u0, u1, u2, l;
         int pv;
         if (fabs(cd) >= fabs(sub)) {
-          const double dd = cd == 0.0 ? tiny : cd;
-          l = sub / dd;
-          piv_u0 = dd;
+          piv_u0 = cd == 0.0 ? tiny : cd;
+          const double rp = recip(piv_u0);
+          l = quot(sub, piv_u0, rp);
           u1 = cs;
           u2 = 0.0;
           pv = 0;
           cd = nd - l * cs;
           cs = ns;
         } else {
-          l = cd / sub;
           piv_u0 = sub;
+          const double rp = recip(piv_u0);
+          l = quot(cd, piv_u0, rp);
           u1 = nd;
           u2 = ns;
           pv = 1;
@@ -935,11 +920,6 @@ __global__ __launch_bounds__(64) void tri_inviter_a_kernel(const double* __restr
           cs = -l * ns;
         }
         if (fabs(piv_u0) < tiny) piv_u0 = piv_u0 < 0.0 ? -tiny : tiny;
-        s_rec[i][0] = 1.0 / piv_u0;
-        s_rec[i][1] = u1;
-        s_rec[i][2] = u2;
-        s_rec[i][3] = l;
-        s_piv[i] = uint8_t(pv);
         // forward elimination of the start vector with this step's multiplier
         double ynext = start_value(jv, k + 1);
         double yk = ycur;
@@ -947,34 +927,41 @@ __global__ __launch_bounds__(64) void tri_inviter_a_kernel(const double* __restr
           yk = ynext;
           ynext = ycur;
         }
-        s_out[i] = yk;
+        if (lane == 0) {
+          s_rec[i][0] = recip(piv_u0);
+          s_rec[i][1] = u1;
+          s_rec[i][2] = u2;
+          s_rec[i][3] = l;
+          s_piv[i] = uint8_t(pv);
+          s_out[i] = yk;
+        }
         ycur = ynext - l * yk;
       }
     }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < CPL; ++u) {
-      const int i = lane + 64 * u;
-      if (i < cnt) {
-        const int k = c * CH + i;
-        *reinterpret_cast<f64x2*>(R + int64_t(k) * 4) = f64x2{s_rec[i][0], s_rec[i][1]};
-        *reinterpret_cast<f64x2*>(R + int64_t(k) * 4 + 2) = f64x2{s_rec[i][2], s_rec[i][3]};
-        PV[k] = s_piv[i];
-        z[k] = s_out[i];
-      }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): lane 0's stores, read by every lane
+    __builtin_amdgcn_wave_barrier();
+    if (lane < cnt) {
+      const int k = c * CH + lane;
+      *reinterpret_cast<f64x2*>(R + int64_t(k) * 4) = f64x2{s_rec[lane][0], s_rec[lane][1]};
+      *reinterpret_cast<f64x2*>(R + int64_t(k) * 4 + 2) = f64x2{s_rec[lane][2], s_rec[lane][3]};
+      PV[k] = s_piv[lane];
+      z[k] = s_out[lane];
     }
-    if (c + 1 < nchf) stage_de(buf ^ 1);
+    __builtin_amdgcn_wave_barrier();
+    ge = ne;
+    gd = nd_;
+    gx = nx;
   }
   if (lane == 0) {
     double p0 = cd;
     if (fabs(p0) < tiny) p0 = p0 < 0.0 ? -tiny : tiny;
-    *reinterpret_cast<f64x2*>(R + int64_t(nm1) * 4) = f64x2{1.0 / p0, 0.0};
+    *reinterpret_cast<f64x2*>(R + int64_t(nm1) * 4) = f64x2{recip(p0), 0.0};
     *reinterpret_cast<f64x2*>(R + int64_t(nm1) * 4 + 2) = f64x2{0.0, 0.0};
     PV[nm1] = 0;
     z[nm1] = ycur;
   }
   __syncthreads();   // the records and y written above are read back below
-  inv_usolve(R, z, n, s_in, s_z, s_out, s_sc);
+  inv_usolve(R, z, n, s_out);
 }
 
 __global__ __launch_bounds__(64) void tri_inviter_b_kernel(int n, int ncols, const int* __restrict__ clen,
@@ -982,12 +969,7 @@ __global__ __launch_bounds__(64) void tri_inviter_b_kernel(int n, int ncols, con
                                                            const double* __restrict__ Rall,
                                                            const uint8_t* __restrict__ Pall,
                                                            double* __restrict__ Zw) {
-  __shared__ double s_in[2][CH][4];
-  __shared__ double s_z[2][CH];
   __shared__ double s_out[CH];
-  __shared__ uint8_t s_piv[2][CH];
-  __shared__ double s_zx[2];
-  __shared__ double s_sc[1];
   const int j = blockIdx.x;
   if (*flag) return;
   const int len = clen[j];
@@ -1032,63 +1014,51 @@ __global__ __launch_bounds__(64) void tri_inviter_b_kernel(int n, int ncols, con
     double* z = Zw + int64_t(jv) * n;
     const double sc = unit_scale(jv, orth(jv));
     __syncthreads();
-    // ---- y = L^-1 P (sc z): chunk c stages z[cCH .. cCH+CH] (one past, for the
-    //      interchange), the multipliers and the flags
-    double gz[CPL], gl[CPL], gx = 0.0;
-    uint8_t gp[CPL];
-    auto load = [&](int c) {
-#pragma unroll
-      for (int u = 0; u < CPL; ++u) {
-        const int k = min(c * CH + lane + 64 * u, n - 1);
-        gz[u] = z[k] * sc;
-        gl[u] = R[int64_t(k) * 4 + 3];
-        gp[u] = PV[k];
-      }
-      gx = z[min(c * CH + CH, n - 1)] * sc;
+    // ---- y = L^-1 P (sc z): lane i of chunk c holds z[cCH+i], the multiplier and the
+    //      flag of step cCH+i; z[cCH+CH] (for the last step's interchange) is held by every lane
+    double gz, gl, gx, nz, nl, nx;
+    int gp, np_;
+    auto load = [&](int c, double& a_z, double& a_l, int& a_p, double& a_x) {
+      const int k = min(c * CH + lane, n - 1);
+      a_z = z[k] * sc;
+      a_l = R[int64_t(k) * 4 + 3];
+      a_p = PV[k];
+      a_x = z[min(c * CH + CH, n - 1)] * sc;
     };
-    auto stage = [&](int buf) {
-#pragma unroll
-      for (int u = 0; u < CPL; ++u) {
-        const int i = lane + 64 * u;
-        s_z[buf][i] = gz[u];
-        s_in[buf][i][3] = gl[u];
-        s_piv[buf][i] = gp[u];
-      }
-      if (lane == 0) s_zx[buf] = gx;
-    };
-    load(0);
-    stage(0);
+    load(0, gz, gl, gp, gx);
     double ycur = z[0] * sc;
+    __syncthreads();   // every lane has read the iterate before it is overwritten below
     for (int c = 0; c < nch; ++c) {
-      const int buf = c & 1;
-      if (c + 1 < nch) load(c + 1);
-      __syncthreads();
+      if (c + 1 < nch) load(c + 1, nz, nl, np_, nx);
       const int cnt = min(CH, nm1 - c * CH);   // elimination steps in this chunk
-      if (lane == 0) {
-        #pragma unroll 8
-        for (int i = 0; i < cnt; ++i) {
-          double ynext = i + 1 < CH ? s_z[buf][i + 1] : s_zx[buf];
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        if (i < cnt) {   // uniform
+          double ynext = i + 1 < CH ? lane_of(gz, i + 1) : gx;
           double yk = ycur;
-          if (s_piv[buf][i]) {
+          if (__builtin_amdgcn_readlane(gp, i)) {
             yk = ynext;
             ynext = ycur;
           }
-          s_out[i] = yk;
-          ycur = ynext - s_in[buf][i][3] * yk;
+          if (lane == 0) s_out[i] = yk;
+          ycur = ynext - lane_of(gl, i) * yk;
         }
-        if (c == nch - 1) s_out[max(cnt, 0)] = ycur;   // the last element
       }
-      __syncthreads();
+      if (c == nch - 1 && lane == 0) s_out[max(cnt, 0)] = ycur;   // the last element
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): lane 0's stores, read by every lane
+      __builtin_amdgcn_wave_barrier();
       const int nw = min(CH, n - c * CH);   // elements written by this chunk
-#pragma unroll
-      for (int u = 0; u < CPL; ++u) {
-        const int i = lane + 64 * u;
-        if (i < nw) z[c * CH + i] = s_out[i];
-      }
-      if (c + 1 < nch) stage(buf ^ 1);
+      // the next chunk's inputs were loaded before this chunk's outputs overwrite z
+      if (lane < nw) z[c * CH + lane] = s_out[lane];
+      __builtin_amdgcn_wave_barrier();
+      gz = nz;
+      gl = nl;
+      gp = np_;
+      gx = nx;
     }
     __syncthreads();
-    inv_usolve(R, z, n, s_in, s_z, s_out, s_sc);
+    inv_usolve(R, z, n, s_out);
+    __syncthreads();
     const double sc2 = unit_scale(jv, orth(jv));
     for (int k = lane; k < n; k += 64) z[k] *= sc2;
     __syncthreads();
