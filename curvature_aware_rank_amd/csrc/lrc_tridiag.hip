@@ -851,6 +851,70 @@ __device__ double inv_usolve(const double* __restrict__ R, double* __restrict__ 
   return nrm2;   // uniform: every lane ran the same recurrence
 }
 
+constexpr int CHL = 256;   // steps per LDS-staged chunk of the second solve
+constexpr int CPLL = CHL / 64;
+
+// back-substitution z <- U^-1 z as in inv_usolve, lane 0 running the recurrence out of LDS chunks of
+// CHL steps staged by the whole wave (the form the second solve uses);
+// returns ||z||^2 (to every lane)
+__device__ double inv_usolve_lds(const double* __restrict__ R, double* __restrict__ z, int n, double (*s_in)[CHL][4],
+                             double (*s_z)[CHL], double* s_out, double* s_sc) {
+  const int lane = threadIdx.x;
+  const int nch = (n + CHL - 1) / CHL;
+  double gr[CPLL][4], gz[CPLL];
+  auto load = [&](int c) {
+#pragma unroll
+    for (int u = 0; u < CPLL; ++u) {
+      const int k = min(c * CHL + lane + 64 * u, n - 1);
+      const f64x2 a = *reinterpret_cast<const f64x2*>(R + int64_t(k) * 4);
+      const f64x2 b = *reinterpret_cast<const f64x2*>(R + int64_t(k) * 4 + 2);
+      gr[u][0] = a[0];
+      gr[u][1] = a[1];
+      gr[u][2] = b[0];
+      gr[u][3] = b[1];
+      gz[u] = z[k];
+    }
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < CPLL; ++u) {
+      const int i = lane + 64 * u;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) s_in[buf][i][t] = gr[u][t];
+      s_z[buf][i] = gz[u];
+    }
+  };
+  double x1 = 0.0, x2 = 0.0, nrm2 = 0.0;
+  load(nch - 1);
+  stage((nch - 1) & 1);
+  for (int c = nch - 1; c >= 0; --c) {
+    const int buf = c & 1;
+    if (c > 0) load(c - 1);
+    __syncthreads();
+    const int cnt = min(CHL, n - c * CHL);
+    if (lane == 0) {
+      #pragma unroll 8
+      for (int i = cnt - 1; i >= 0; --i) {
+        const double xk = (s_z[buf][i] - s_in[buf][i][1] * x1 - s_in[buf][i][2] * x2) * s_in[buf][i][0];
+        s_out[i] = xk;
+        nrm2 += xk * xk;
+        x2 = x1;
+        x1 = xk;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < CPLL; ++u) {
+      const int i = lane + 64 * u;
+      if (i < cnt) z[c * CHL + i] = s_out[i];
+    }
+    if (c > 0) stage(buf ^ 1);
+  }
+  if (lane == 0) s_sc[0] = nrm2;
+  __syncthreads();
+  return s_sc[0];
+}
+
 __global__ __launch_bounds__(64) void tri_inviter_a_kernel(const double* __restrict__ d, const double* __restrict__ e,
                                                            int n, const double* __restrict__ lam, int ncols,
                                                            const double* __restrict__ bounds,
@@ -877,19 +941,21 @@ __global__ __launch_bounds__(64) void tri_inviter_a_kernel(const double* __restr
   //      same pass, y = L^-1 P z0 for the start vector z0 (generated on the fly).
   // Step k reads e[k], d[k+1], e[k+1]; lane i of chunk c holds e[cCH+i] and d[cCH+i+1],
   // e[k+1] of the chunk's last step is e[cCH+CH] (held by every lane).
-  double ge, gd, gx, ne, nd_, nx;
-  auto load_de = [&](int c, double& a_e, double& a_d, double& a_x) {
+  // lane i also holds the start vector's entry k + 1 of its step (gy)
+  double ge, gd, gx, gy, ne, nd_, nx, ny;
+  auto load_de = [&](int c, double& a_e, double& a_d, double& a_x, double& a_y) {
     const int k = c * CH + lane;
     a_e = e[min(k, max(n - 2, 0))];
     a_d = d[min(k + 1, n - 1)];
     a_x = e[min(c * CH + CH, max(n - 2, 0))];
+    a_y = start_value(jv, k + 1);
   };
   double cd = d[0] - lmb, cs = n > 1 ? e[0] : 0.0;
   double ycur = start_value(jv, 0);
   const int nchf = (nm1 + CH - 1) / CH;
-  if (nchf > 0) load_de(0, ge, gd, gx);
+  if (nchf > 0) load_de(0, ge, gd, gx, gy);
   for (int c = 0; c < nchf; ++c) {
-    if (c + 1 < nchf) load_de(c + 1, ne, nd_, nx);
+    if (c + 1 < nchf) load_de(c + 1, ne, nd_, nx, ny);
     const int cnt = min(CH, nm1 - c * CH);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
@@ -898,35 +964,21 @@ __global__ __launch_bounds__(64) void tri_inviter_a_kernel(const double* __restr
         const double sub = lane_of(ge, i);
         const double nd = lane_of(gd, i) - lmb;
         const double ns = k + 1 < nm1 ? (i + 1 < CH ? lane_of(ge, i + 1) : gx) : 0.0;
-        double piv_u0, u1, u2, l;
-        int pv;
-        if (fabs(cd) >= fabs(sub)) {
-          piv_u0 = cd == 0.0 ? tiny : cd;
-          const double rp = recip(piv_u0);
-          l = quot(sub, piv_u0, rp);
-          u1 = cs;
-          u2 = 0.0;
-          pv = 0;
-          cd = nd - l * cs;
-          cs = ns;
-        } else {
-          piv_u0 = sub;
-          const double rp = recip(piv_u0);
-          l = quot(cd, piv_u0, rp);
-          u1 = nd;
-          u2 = ns;
-          pv = 1;
-          cd = cs - l * nd;
-          cs = -l * ns;
-        }
+        // partial pivoting, branch-free: keep row k (pv = 0) or interchange with row k + 1
+        const bool pv = !(fabs(cd) >= fabs(sub));
+        double piv_u0 = pv ? sub : (cd == 0.0 ? tiny : cd);
+        const double num = pv ? cd : sub;
+        const double l = quot(num, piv_u0, recip(piv_u0));
+        const double u1 = pv ? nd : cs;
+        const double u2 = pv ? ns : 0.0;
+        const double ncd = pv ? cs - l * nd : nd - l * cs;
+        cs = pv ? -l * ns : ns;
+        cd = ncd;
         if (fabs(piv_u0) < tiny) piv_u0 = piv_u0 < 0.0 ? -tiny : tiny;
         // forward elimination of the start vector with this step's multiplier
-        double ynext = start_value(jv, k + 1);
-        double yk = ycur;
-        if (pv) {
-          yk = ynext;
-          ynext = ycur;
-        }
+        const double yn = lane_of(gy, i);
+        const double yk = pv ? yn : ycur;
+        const double ynext = pv ? ycur : yn;
         if (lane == 0) {
           s_rec[i][0] = recip(piv_u0);
           s_rec[i][1] = u1;
@@ -951,6 +1003,7 @@ __global__ __launch_bounds__(64) void tri_inviter_a_kernel(const double* __restr
     ge = ne;
     gd = nd_;
     gx = nx;
+    gy = ny;
   }
   if (lane == 0) {
     double p0 = cd;
@@ -969,7 +1022,12 @@ __global__ __launch_bounds__(64) void tri_inviter_b_kernel(int n, int ncols, con
                                                            const double* __restrict__ Rall,
                                                            const uint8_t* __restrict__ Pall,
                                                            double* __restrict__ Zw) {
-  __shared__ double s_out[CH];
+  __shared__ double s_in[2][CHL][4];
+  __shared__ double s_z[2][CHL];
+  __shared__ double s_out[CHL];
+  __shared__ uint8_t s_piv[2][CHL];
+  __shared__ double s_zx[2];
+  __shared__ double s_sc[1];
   const int j = blockIdx.x;
   if (*flag) return;
   const int len = clen[j];
@@ -1006,7 +1064,7 @@ __global__ __launch_bounds__(64) void tri_inviter_b_kernel(int n, int ncols, con
     return s2 > 0.0 ? inv_mx / sqrt(s2) : 1.0;
   };
   const int nm1 = n - 1;
-  const int nch = (n + CH - 1) / CH;
+  const int nch = (n + CHL - 1) / CHL;
   for (int q = 0; q < len; ++q) {
     const int jv = j + q;
     const double* R = Rall + int64_t(jv) * n * 4;
@@ -1014,51 +1072,63 @@ __global__ __launch_bounds__(64) void tri_inviter_b_kernel(int n, int ncols, con
     double* z = Zw + int64_t(jv) * n;
     const double sc = unit_scale(jv, orth(jv));
     __syncthreads();
-    // ---- y = L^-1 P (sc z): lane i of chunk c holds z[cCH+i], the multiplier and the
-    //      flag of step cCH+i; z[cCH+CH] (for the last step's interchange) is held by every lane
-    double gz, gl, gx, nz, nl, nx;
-    int gp, np_;
-    auto load = [&](int c, double& a_z, double& a_l, int& a_p, double& a_x) {
-      const int k = min(c * CH + lane, n - 1);
-      a_z = z[k] * sc;
-      a_l = R[int64_t(k) * 4 + 3];
-      a_p = PV[k];
-      a_x = z[min(c * CH + CH, n - 1)] * sc;
-    };
-    load(0, gz, gl, gp, gx);
-    double ycur = z[0] * sc;
-    __syncthreads();   // every lane has read the iterate before it is overwritten below
-    for (int c = 0; c < nch; ++c) {
-      if (c + 1 < nch) load(c + 1, nz, nl, np_, nx);
-      const int cnt = min(CH, nm1 - c * CH);   // elimination steps in this chunk
+    // ---- y = L^-1 P (sc z): chunk c stages z[c CHL .. c CHL + CHL] (one past, for the
+    //      interchange), the multipliers and the flags
+    double gz[CPLL], gl[CPLL], gx = 0.0;
+    uint8_t gp[CPLL];
+    auto load = [&](int c) {
 #pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        if (i < cnt) {   // uniform
-          double ynext = i + 1 < CH ? lane_of(gz, i + 1) : gx;
+      for (int u = 0; u < CPLL; ++u) {
+        const int k = min(c * CHL + lane + 64 * u, n - 1);
+        gz[u] = z[k] * sc;
+        gl[u] = R[int64_t(k) * 4 + 3];
+        gp[u] = PV[k];
+      }
+      gx = z[min(c * CHL + CHL, n - 1)] * sc;
+    };
+    auto stage = [&](int buf) {
+#pragma unroll
+      for (int u = 0; u < CPLL; ++u) {
+        const int i = lane + 64 * u;
+        s_z[buf][i] = gz[u];
+        s_in[buf][i][3] = gl[u];
+        s_piv[buf][i] = gp[u];
+      }
+      if (lane == 0) s_zx[buf] = gx;
+    };
+    load(0);
+    stage(0);
+    double ycur = z[0] * sc;
+    for (int c = 0; c < nch; ++c) {
+      const int buf = c & 1;
+      if (c + 1 < nch) load(c + 1);
+      __syncthreads();
+      const int cnt = min(CHL, nm1 - c * CHL);   // elimination steps in this chunk
+      if (lane == 0) {
+        #pragma unroll 8
+        for (int i = 0; i < cnt; ++i) {
+          double ynext = i + 1 < CHL ? s_z[buf][i + 1] : s_zx[buf];
           double yk = ycur;
-          if (__builtin_amdgcn_readlane(gp, i)) {
+          if (s_piv[buf][i]) {
             yk = ynext;
             ynext = ycur;
           }
-          if (lane == 0) s_out[i] = yk;
-          ycur = ynext - lane_of(gl, i) * yk;
+          s_out[i] = yk;
+          ycur = ynext - s_in[buf][i][3] * yk;
         }
+        if (c == nch - 1) s_out[max(cnt, 0)] = ycur;   // the last element
       }
-      if (c == nch - 1 && lane == 0) s_out[max(cnt, 0)] = ycur;   // the last element
-      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): lane 0's stores, read by every lane
-      __builtin_amdgcn_wave_barrier();
-      const int nw = min(CH, n - c * CH);   // elements written by this chunk
-      // the next chunk's inputs were loaded before this chunk's outputs overwrite z
-      if (lane < nw) z[c * CH + lane] = s_out[lane];
-      __builtin_amdgcn_wave_barrier();
-      gz = nz;
-      gl = nl;
-      gp = np_;
-      gx = nx;
+      __syncthreads();
+      const int nw = min(CHL, n - c * CHL);   // elements written by this chunk
+#pragma unroll
+      for (int u = 0; u < CPLL; ++u) {
+        const int i = lane + 64 * u;
+        if (i < nw) z[c * CHL + i] = s_out[i];
+      }
+      if (c + 1 < nch) stage(buf ^ 1);
     }
     __syncthreads();
-    inv_usolve(R, z, n, s_out);
-    __syncthreads();
+    inv_usolve_lds(R, z, n, s_in, s_z, s_out, s_sc);
     const double sc2 = unit_scale(jv, orth(jv));
     for (int k = lane; k < n; k += 64) z[k] *= sc2;
     __syncthreads();
