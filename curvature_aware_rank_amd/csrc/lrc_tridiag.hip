@@ -770,12 +770,14 @@ __device__ __forceinline__ double start_value(int j, int k) {
 //  B) one wave per cluster (a lone eigenvalue is a cluster of one), members in order:
 //     orthogonalise the first iterate against the cluster's finished vectors (modified
 //     Gram-Schmidt), normalise, second solve, orthogonalise again, normalise.
-// The recurrences are sequential.  They run in chunks of 64 steps whose inputs sit in
-// registers, step i's in lane i (the next chunk's loads in flight meanwhile); the wave
-// evaluates every step uniformly with the operands taken by readlane, so no memory
-// latency enters the dependence chain, and lane 0 drops each step's results into LDS,
-// from where the whole wave writes them out after the chunk.  Divisions are a hardware
-// reciprocal refined by a Newton step, the quotient then corrected by its residual.
+// The recurrences are sequential.  The factorisation runs in chunks of 64 steps whose
+// inputs sit in registers, step i's in lane i (the next chunk's loads in flight
+// meanwhile); the wave evaluates every step uniformly with the operands taken by
+// readlane, so no memory latency enters its dependence chain, and lane 0 drops each
+// step's results into LDS, from where the whole wave writes them out after the chunk.
+// Its divisions are a hardware reciprocal refined by a Newton step, the quotient then
+// corrected by its residual.  The solves (lighter steps) run on lane 0 out of LDS chunks
+// of CHL steps that the whole wave stages.
 // The per-vector arrays are vector major: LU records {1/pivot, u1, u2, multiplier}
 // (32 B) and row-interchange flags, and the iterates Zw (one row of n per vector); a
 // transpose writes Z (n x ncols) at the end.  The orthogonalisation and scaling passes
@@ -807,55 +809,12 @@ __device__ __forceinline__ double wave_max(double v) {
   return v;
 }
 
-// back-substitution z <- U^-1 z on vector j (records R, iterate z), chunks from the end;
-// returns ||z||^2 (to every lane)
-__device__ double inv_usolve(const double* __restrict__ R, double* __restrict__ z, int n,
-                             double* __restrict__ s_out) {
-  const int lane = threadIdx.x;
-  const int nch = (n + CH - 1) / CH;
-  double r0, r1, r2, zz;   // this lane's step of the current chunk
-  double n0, n1, n2, nz;   // the next (lower) chunk, in flight
-  auto load = [&](int c, double& a0, double& a1, double& a2, double& az) {
-    const int k = min(c * CH + lane, n - 1);
-    const f64x2 u = *reinterpret_cast<const f64x2*>(R + int64_t(k) * 4);
-    const f64x2 v = *reinterpret_cast<const f64x2*>(R + int64_t(k) * 4 + 2);
-    a0 = u[0];
-    a1 = u[1];
-    a2 = v[0];
-    az = z[k];
-  };
-  double x1 = 0.0, x2 = 0.0, nrm2 = 0.0;
-  load(nch - 1, r0, r1, r2, zz);
-  for (int c = nch - 1; c >= 0; --c) {
-    if (c > 0) load(c - 1, n0, n1, n2, nz);
-    const int cnt = min(CH, n - c * CH);
-#pragma unroll
-    for (int i = CH - 1; i >= 0; --i) {
-      if (i < cnt) {   // uniform
-        const double xk = (lane_of(zz, i) - lane_of(r1, i) * x1 - lane_of(r2, i) * x2) * lane_of(r0, i);
-        if (lane == 0) s_out[i] = xk;
-        nrm2 += xk * xk;
-        x2 = x1;
-        x1 = xk;
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): lane 0's stores, read by every lane
-    __builtin_amdgcn_wave_barrier();
-    if (lane < cnt) z[c * CH + lane] = s_out[lane];
-    __builtin_amdgcn_wave_barrier();
-    r0 = n0;
-    r1 = n1;
-    r2 = n2;
-    zz = nz;
-  }
-  return nrm2;   // uniform: every lane ran the same recurrence
-}
-
-constexpr int CHL = 256;   // steps per LDS-staged chunk of the second solve
+constexpr int CHL = 256;   // steps per LDS-staged chunk of the solves
 constexpr int CPLL = CHL / 64;
 
-// back-substitution z <- U^-1 z as in inv_usolve, lane 0 running the recurrence out of LDS chunks of
-// CHL steps staged by the whole wave (the form the second solve uses);
+// back-substitution z <- U^-1 z on vector j (records R, iterate z), chunks from the end:
+// lane 0 runs the recurrence out of LDS chunks of CHL steps staged by the whole wave (the
+// next chunk's loads in flight), which measured faster here than register-resident chunks;
 // returns ||z||^2 (to every lane)
 __device__ double inv_usolve_lds(const double* __restrict__ R, double* __restrict__ z, int n, double (*s_in)[CHL][4],
                              double (*s_z)[CHL], double* s_out, double* s_sc) {
@@ -921,9 +880,13 @@ __global__ __launch_bounds__(64) void tri_inviter_a_kernel(const double* __restr
                                                            const int* __restrict__ clen, const int* __restrict__ flag,
                                                            double* __restrict__ Rall, uint8_t* __restrict__ Pall,
                                                            double* __restrict__ Zw) {
-  __shared__ double s_out[CH];
+  __shared__ double s_out[CH];   // factorisation outputs of a 64-step chunk
   __shared__ double s_rec[CH][4];
   __shared__ uint8_t s_piv[CH];
+  __shared__ double s_in[2][CHL][4];   // staging of the back-substitution
+  __shared__ double s_z[2][CHL];
+  __shared__ double s_outl[CHL];
+  __shared__ double s_sc[1];
   const int jv = blockIdx.x;
   if (*flag) return;
   const int lane = threadIdx.x;
@@ -1014,7 +977,7 @@ __global__ __launch_bounds__(64) void tri_inviter_a_kernel(const double* __restr
     z[nm1] = ycur;
   }
   __syncthreads();   // the records and y written above are read back below
-  inv_usolve(R, z, n, s_out);
+  inv_usolve_lds(R, z, n, s_in, s_z, s_outl, s_sc);
 }
 
 __global__ __launch_bounds__(64) void tri_inviter_b_kernel(int n, int ncols, const int* __restrict__ clen,
