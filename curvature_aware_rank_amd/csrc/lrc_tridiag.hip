@@ -633,6 +633,96 @@ __global__ __launch_bounds__(256) void tri_syr2k_kernel(double* __restrict__ A, 
       }
 }
 
+
+// ---- 1e. the last columns (trailing matrix of at most TT rows, already fully updated at
+// a panel boundary) in one workgroup: the whole trailing matrix lives in LDS (full
+// symmetric storage), and each column is reduced unblocked, H A H = A - v w^T - w v^T with
+// w = tau A v - tau^2/2 (v^T A v) v.  Writes the same d, e, tau and reflectors (column i
+// below the diagonal, v[i+1] = 1) as the panel path; one launch instead of two per column.
+constexpr int TT = 128;          // rows of the trailing matrix handled this way
+constexpr int TTP = TT + 1;      // LDS pitch (doubles)
+
+__device__ __forceinline__ double block_sum4w(double v, double* red) {
+  // sum over 256 threads: wave butterflies, then the four wave results in order
+  v = wave_sum(v);
+  __syncthreads();   // red may still be read from the previous call
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+__global__ __launch_bounds__(256) void tri_tail_kernel(double* __restrict__ A, int64_t lda, int n, int t0,
+                                                       double* __restrict__ d, double* __restrict__ e,
+                                                       double* __restrict__ tau_out) {
+  __shared__ double T[TT][TTP];
+  __shared__ double vv[TT], yy[TT];
+  __shared__ double red[4];
+  const int tid = threadIdx.x;
+  const int nt = n - t0;   // <= TT
+  // load the lower triangle of the trailing matrix and mirror it
+  for (int q = tid; q < nt * nt; q += 256) {
+    const int r = q / nt, c = q % nt;
+    if (c <= r) {
+      const double val = A[int64_t(t0 + r) * lda + t0 + c];
+      T[r][c] = val;
+      T[c][r] = val;
+    }
+  }
+  __syncthreads();
+  for (int li = 0; li < nt - 1; ++li) {
+    const int i = t0 + li;
+    const int m = nt - 1 - li;   // length of the column below the diagonal
+    const int b0 = li + 1;       // first trailing row / column
+    // reflector of column li: x = T[b0.., li]
+    const double x0 = T[b0][li];
+    double sq = 0.0;
+    for (int r = tid + 1; r < m; r += 256) sq += T[b0 + r][li] * T[b0 + r][li];
+    const double xn2 = block_sum4w(sq, red);
+    double tau, beta, scale;
+    house_from_sum(xn2, x0, tau, beta, scale);
+    if (tid == 0) {
+      d[i] = T[li][li];
+      e[i] = beta;
+      tau_out[i] = tau;
+    }
+    for (int r = tid; r < m; r += 256) {
+      const double v = r == 0 ? 1.0 : T[b0 + r][li] * scale;
+      vv[r] = v;
+      A[int64_t(b0 + t0 + r) * lda + i] = v;
+    }
+    __syncthreads();
+    // y = T_trailing v (four threads per row, the quad adding in a fixed order)
+    double vy_part = 0.0;
+    {
+      const int part = tid & 3;
+      for (int r0 = tid >> 2; r0 < m; r0 += 64) {
+        double acc = 0.0;
+        for (int c = part; c < m; c += 4) acc += T[b0 + r0][b0 + c] * vv[c];
+        acc = quad_sum(acc);
+        if (part == 0) {
+          yy[r0] = acc;
+          vy_part += acc * vv[r0];
+        }
+      }
+    }
+    const double vy = block_sum4w(vy_part, red);   // barrier: also publishes yy
+    const double alpha = -0.5 * tau * tau * vy;
+    // T_trailing -= v w^T + w v^T, w = tau y + alpha v (16 x 16 threads, strided)
+    {
+      const int tr = tid >> 4, tc = tid & 15;
+      for (int r = tr; r < m; r += 16) {
+        const double vr = vv[r], wr = tau * yy[r] + alpha * vr;
+        for (int c = tc; c < m; c += 16) {
+          const double vc = vv[c], wc = tau * yy[c] + alpha * vc;
+          T[b0 + r][b0 + c] -= vr * wc + wr * vc;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (tid == 0) d[n - 1] = T[nt - 1][nt - 1];
+}
+
 // ---- 2. eigenvalues of T
 // bounds: [0] gl, [1] gu, [2] pivmin, [3] ||T|| (max |Gershgorin end|)
 __global__ __launch_bounds__(256) void tri_bounds_kernel(const double* __restrict__ d, const double* __restrict__ e,
@@ -1500,7 +1590,9 @@ __global__ void zero_int_kernel(int* p, int n) {
 // Householder tridiagonalisation of the lower triangle of A (n x n, pitch lda) in place:
 // d, e, tau and the reflectors (below the subdiagonal) land in w and A.
 lrc_status tri_reduce(hipStream_t st, double* A, int n, int64_t lda, const TWs& w) {
-  for (int i0 = 0; i0 < n - 1; i0 += NB) {
+  // panels up to t0 (a multiple of NB), then the last n - t0 <= TT columns in one workgroup
+  const int t0 = n <= TT ? 0 : int(cdiv(n - TT, NB) * NB);
+  for (int i0 = 0; i0 < t0; i0 += NB) {
     const int pb = std::min(NB, n - 1 - i0);
     {
       const unsigned g = unsigned(cdiv(n - i0, TS));
@@ -1553,14 +1645,8 @@ lrc_status tri_reduce(hipStream_t st, double* A, int n, int64_t lda, const TWs& 
       LRC_LAUNCHED();
     }
   }
-  {
-    // last diagonal entry (and the whole job when n == 1)
-    const int i = n - 1;
-    tri_colstart_kernel<<<1, 256, 0, st>>>(A, lda, n, i, w.npart + (i & 1) * 4 * cdiv(n, TS), w.x0 + (i & 1), w.d,
-                                           w.xv + (i & 1) * n);
-    LRC_LAUNCHED();
-  }
-
+  tri_tail_kernel<<<1, 256, 0, st>>>(A, lda, n, t0, w.d, w.e, w.tau);
+  LRC_LAUNCHED();
   return LRC_OK;
 }
 
