@@ -65,6 +65,13 @@ __device__ __forceinline__ int matrix_of_item(const int64_t* __restrict__ offs, 
   return lo;
 }
 
+// an id read back from the sorted order, kept inside [0, M) so that a lookup can never
+// leave the tables (the sort writes a permutation; this only guards the reads)
+__device__ __forceinline__ int32_t order_id(const int32_t* __restrict__ order, int64_t p, int M) {
+  const int32_t id = order[p];
+  return id < 0 ? 0 : (id >= M ? M - 1 : id);
+}
+
 // Tables of the item -> matrix -> cost lookup
 struct CostLookup {
   const int64_t* offs;
@@ -317,7 +324,7 @@ __global__ __launch_bounds__(256) void cost_bsum_kernel(const int32_t* __restric
 #pragma unroll
   for (int i = 0; i < SC; ++i) {
     const int64_t p = min<int64_t>(base + i * 256 + int(threadIdx.x), M - 1);
-    id[i] = order[p];
+    id[i] = order_id(order, p, M);
   }
   int64_t c[SC];
 #pragma unroll
@@ -399,7 +406,7 @@ __global__ __launch_bounds__(256) void cost_cut_kernel(const int32_t* __restrict
 #pragma unroll
   for (int i = 0; i < SC; ++i) {
     const int64_t p = base + i;
-    c[i] = p < M ? cl(order[p]) : 0;
+    c[i] = p < M ? cl(order_id(order, p, M)) : 0;
     s += c[i];
   }
   int64_t inc = s;
@@ -429,7 +436,7 @@ __global__ void set_i64_kernel(int64_t* __restrict__ p, int64_t v) { *p = v; }
 
 // key and id of the last kept position (or an empty marker) for the mask
 __global__ void cut_key_kernel(const float* __restrict__ scores, CostLookup cl,
-                               const int32_t* __restrict__ order, const int64_t* __restrict__ n_kept,
+                               const int32_t* __restrict__ order, int M, const int64_t* __restrict__ n_kept,
                                const int32_t* __restrict__ info, uint64_t* __restrict__ cutkey) {
   const int64_t nk = *n_kept;
   if (nk <= 0) {
@@ -437,7 +444,7 @@ __global__ void cut_key_kernel(const float* __restrict__ scores, CostLookup cl,
     return;
   }
   bool nf;
-  const int32_t id = order[nk - 1];
+  const int32_t id = order_id(order, nk - 1, M);
   cutkey[0] = item_key(scores, cl, id, *info == int32_t(LRC_EINVAL), nf);
   cutkey[1] = uint64_t(id);
 }
@@ -587,7 +594,7 @@ extern "C" lrc_status lrc_allocate_ranks(const float* scores, const int64_t* off
     LRC_LAUNCHED();
     cost_cut_kernel<<<1, 256, 0, st>>>(order, cl, M, budget, w.cut, n_kept);
     LRC_LAUNCHED();
-    cut_key_kernel<<<1, 1, 0, st>>>(scores, cl, order, n_kept, info, w.cutkey);
+    cut_key_kernel<<<1, 1, 0, st>>>(scores, cl, order, M, n_kept, info, w.cutkey);
     LRC_LAUNCHED();
     mask_kernel<<<unsigned(cdiv(M, MASK_PER)), 256, 0, st>>>(scores, cl, M, w.cutkey, info, kept_mask);
     LRC_LAUNCHED();
