@@ -235,7 +235,6 @@ constexpr int NSTG = 4;                  // LDS stages
 constexpr int ROWB = TB * 2;             // bytes per token row of one operand
 constexpr int OPB = KS2 * ROWB;          // 16 KB: one operand, one stage
 constexpr int STB = 2 * OPB;             // 32 KB: one stage
-constexpr int LDPW = OPB / 1024 / 4;     // 1 KB loads per wave per operand per stage (4)
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -263,9 +262,15 @@ __device__ __forceinline__ int frag_off(int ch0, int lane) {
   return tk * ROWB + (((ch >> 3) ^ (4 * (tk & 3))) << 4) + (ch & 7) * 2;
 }
 
-__global__ __launch_bounds__(NTH, 1) void syrk_bf16_dl_kernel(
+// DL_NW waves per workgroup (4 or 8): wave (wr, wc) owns rows wr RB .. + RB of the tile
+// (RB = 512 / DL_NW) and columns wc 128 .. + 128, i.e. (RB / 32) x 4 blocks of 32 x 32
+constexpr int DL_NW = 8;
+__global__ __launch_bounds__(64 * DL_NW, 1) void syrk_bf16_dl_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Y, int64_t ldx, int64_t n, int d, int n1,
     int n_tiles, int tiles_per_xcd, int splits, int64_t tok_per_split, float* __restrict__ partial) {
+  constexpr int LDPW = OPB / 1024 / DL_NW;  // 1 KB loads per wave per operand per stage
+  constexpr int RB = TB / (DL_NW / 2);      // rows of a wave's block
+  constexpr int NI = RB / 32;
   // one LDS object per stage: the compiler tracks the direct loads per object, so a read
   // of one stage waits only for that stage's loads (with a shared array it would wait for
   // all of them)
@@ -284,7 +289,8 @@ __global__ __launch_bounds__(NTH, 1) void syrk_bf16_dl_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave >> 1, wc = wave & 1;
-  const bool wave_dead = (ti == tj) && (wr < wc);
+  // on a diagonal tile a block wholly above the diagonal is skipped
+  const bool wave_dead = (ti == tj) && (wr * RB + RB - 1 < wc * 128);
 
   const int64_t tok_begin = int64_t(split) * tok_per_split;
   const int64_t tok_end = min<int64_t>(n, tok_begin + tok_per_split);
@@ -327,16 +333,15 @@ __global__ __launch_bounds__(NTH, 1) void syrk_bf16_dl_kernel(
     }
   };
 
-  int offa[4], offb[4];
+  int offa[NI], offb[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    offa[i] = frag_off(wr * 128 + i * 32, lane);
-    offb[i] = frag_off(wc * 128 + i * 32, lane);
-  }
+  for (int i = 0; i < NI; ++i) offa[i] = frag_off(wr * RB + i * 32, lane);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) offb[j] = frag_off(wc * 128 + j * 32, lane);
 
-  f32x16 acc[4][4];
+  f32x16 acc[NI][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -346,13 +351,13 @@ __global__ __launch_bounds__(NTH, 1) void syrk_bf16_dl_kernel(
     const uint8_t* yb = xa + OPB;
 #pragma unroll
     for (int kk = 0; kk < KS2 / 16; ++kk) {
-      bf16x8 fa[4], fb[4];
+      bf16x8 fa[NI], fb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = frag_sw(xa + kk * 16 * ROWB, offa[i]);
+      for (int i = 0; i < NI; ++i) fa[i] = frag_sw(xa + kk * 16 * ROWB, offa[i]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) fb[j] = frag_sw(yb + kk * 16 * ROWB, offb[j]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
@@ -360,12 +365,20 @@ __global__ __launch_bounds__(NTH, 1) void syrk_bf16_dl_kernel(
   };
 
   // Steady state: before stage s, this wave's loads of stage s are the oldest of three
-  // stages outstanding (2 LDPW each), so vmcnt(16) leaves exactly the two newer ones in
-  // flight; after the barrier every wave's stage-s data is in LDS and every wave has
+  // stages outstanding (2 LDPW each), so vmcnt(4 LDPW) leaves exactly the two newer ones
+  // in flight; after the barrier every wave's stage-s data is in LDS and every wave has
   // finished stage s - 1, whose buffer then takes stage s + 3.  The loop is unrolled over
   // the four stage buffers so that every access names its buffer; the last stages select
   // buffers at run time and wait for everything.  A wave whose block lies above the
   // diagonal of a diagonal tile only loads and synchronises.
+  auto stage_barrier = [&]() {
+    if constexpr (LDPW == 4) {
+      LRC_VMCNT_BARRIER(16);
+    } else {
+      static_assert(LDPW == 2, "four or eight waves");
+      LRC_VMCNT_BARRIER(8);
+    }
+  };
   auto buf = [&](int st) -> uint8_t* {
     const int k = st & 3;
     return k == 0 ? sb0 : k == 1 ? sb1 : k == 2 ? sb2 : sb3;
@@ -377,22 +390,22 @@ __global__ __launch_bounds__(NTH, 1) void syrk_bf16_dl_kernel(
   int s = 0;
   if (!wave_dead) {
     for (; s + 6 < nsteps; s += 4) {
-      LRC_VMCNT_BARRIER(16);
+      stage_barrier();
       issue(sb3, s + 3);
       compute(sb0);
-      LRC_VMCNT_BARRIER(16);
+      stage_barrier();
       issue(sb0, s + 4);
       compute(sb1);
-      LRC_VMCNT_BARRIER(16);
+      stage_barrier();
       issue(sb1, s + 5);
       compute(sb2);
-      LRC_VMCNT_BARRIER(16);
+      stage_barrier();
       issue(sb2, s + 6);
       compute(sb3);
     }
     for (; s < nsteps; ++s) {
       if (s + 3 < nsteps) {
-        LRC_VMCNT_BARRIER(16);
+        stage_barrier();
         issue(buf(s + 3), s + 3);
       } else {
         LRC_VMCNT_BARRIER(0);
@@ -402,7 +415,7 @@ __global__ __launch_bounds__(NTH, 1) void syrk_bf16_dl_kernel(
   } else {
     for (; s < nsteps; ++s) {
       if (s + 3 < nsteps) {
-        LRC_VMCNT_BARRIER(16);
+        stage_barrier();
         issue(buf(s + 3), s + 3);
       } else {
         LRC_VMCNT_BARRIER(0);
@@ -410,10 +423,10 @@ __global__ __launch_bounds__(NTH, 1) void syrk_bf16_dl_kernel(
     }
   }
 
-  const int r_base = wr * 128, c_base = wc * 128;
+  const int r_base = wr * RB, c_base = wc * 128;
   float* part = partial + (int64_t(split) * n_tiles + tile) * (TB * TB);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -591,8 +604,8 @@ lrc_status launch_syrk_bf16(hipStream_t st, const uint16_t* X, const uint16_t* Y
   // direct-load kernel: buffer offsets of a split (rows of ldx bf16, plus the three
   // stages the pipeline may fetch past its end) must stay below 2^31
   if (vec && (tok_per_split + 3 * KS2) * ldx * 2 < (int64_t(1) << 31))
-    syrk_bf16_dl_kernel<<<grid, NTH, 0, st>>>(X, Y, ldx, n, int(d), p.n1, p.n_tiles, p.tiles_per_xcd, p.splits,
-                                              tok_per_split, partial);
+    syrk_bf16_dl_kernel<<<grid, 64 * DL_NW, 0, st>>>(X, Y, ldx, n, int(d), p.n1, p.n_tiles, p.tiles_per_xcd, p.splits,
+                                                 tok_per_split, partial);
   else if (vec)
     syrk_bf16_kernel<true><<<grid, NTH, 0, st>>>(X, Y, ldx, n, int(d), p.n1, p.n_tiles, p.tiles_per_xcd,
                                                  p.splits, p.steps_per_split, partial);
