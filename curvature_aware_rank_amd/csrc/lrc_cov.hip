@@ -347,28 +347,34 @@ __global__ __launch_bounds__(64 * DL_NW, 1) void syrk_bf16_dl_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  auto compute = [&](const uint8_t* xa) {
+  // A stage is two 16-token halves.  Fragment sets: F0 holds a stage's first half, F1
+  // its second half.
+  static_assert(KS2 == 32, "two 16-token halves per stage");
+  bf16x8 fa0[NI], fb0[4], fa1[NI], fb1[4];
+  auto read_half = [&](const uint8_t* xa, int half, bf16x8* fa, bf16x8* fb) {
     const uint8_t* yb = xa + OPB;
 #pragma unroll
-    for (int kk = 0; kk < KS2 / 16; ++kk) {
-      bf16x8 fa[NI], fb[4];
+    for (int i = 0; i < NI; ++i) fa[i] = frag_sw(xa + half * 16 * ROWB, offa[i]);
 #pragma unroll
-      for (int i = 0; i < NI; ++i) fa[i] = frag_sw(xa + kk * 16 * ROWB, offa[i]);
+    for (int j = 0; j < 4; ++j) fb[j] = frag_sw(yb + half * 16 * ROWB, offb[j]);
+  };
+  auto mma = [&](const bf16x8* fa, const bf16x8* fb) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) fb[j] = frag_sw(yb + kk * 16 * ROWB, offb[j]);
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
   };
 
-  // Steady state: before stage s, this wave's loads of stage s are the oldest of three
-  // stages outstanding (2 LDPW each), so vmcnt(4 LDPW) leaves exactly the two newer ones
-  // in flight; after the barrier every wave's stage-s data is in LDS and every wave has
-  // finished stage s - 1, whose buffer then takes stage s + 3.  The loop is unrolled over
-  // the four stage buffers so that every access names its buffer; the last stages select
+  // Schedule (four stage buffers, stage s in buffer s mod 4).  Iteration s: read the
+  // second half of stage s, run the MFMAs of its first half, then a barrier that waits
+  // for stage s + 1.  At that barrier this wave's loads of s + 1 are the oldest of three
+  // stages outstanding (2 LDPW loads each), so vmcnt(4 LDPW) leaves the two newer ones in
+  // flight; afterwards stage s + 1 is in LDS and every wave has read all of stage s
+  // (lgkmcnt(0) before the barrier), so buffer s mod 4 takes stage s + 4.  Then read the
+  // first half of stage s + 1 and run the MFMAs of the second half of stage s: the MFMA
+  // pipe never waits on a fragment read across the barrier.  The steady loop is unrolled
+  // over the four buffers so that every access names its buffer; the last stages select
   // buffers at run time and wait for everything.  A wave whose block lies above the
   // diagonal of a diagonal tile only loads and synchronises.
   auto stage_barrier = [&]() {
@@ -379,49 +385,68 @@ __global__ __launch_bounds__(64 * DL_NW, 1) void syrk_bf16_dl_kernel(
       LRC_VMCNT_BARRIER(8);
     }
   };
+  auto first_barrier = [&]() {  // stage 0 of four outstanding
+    if constexpr (LDPW == 4) {
+      LRC_VMCNT_BARRIER(24);
+    } else {
+      LRC_VMCNT_BARRIER(12);
+    }
+  };
   auto buf = [&](int st) -> uint8_t* {
     const int k = st & 3;
     return k == 0 ? sb0 : k == 1 ? sb1 : k == 2 ? sb2 : sb3;
   };
-  // the first three stages unconditionally: stages past the split read zeros
+  // the first four stages unconditionally (every split has at least one): stages past
+  // the split read zeros
   issue(sb0, 0);
   issue(sb1, 1);
   issue(sb2, 2);
+  issue(sb3, 3);
+  first_barrier();
   int s = 0;
   if (!wave_dead) {
-    for (; s + 6 < nsteps; s += 4) {
-      stage_barrier();
-      issue(sb3, s + 3);
-      compute(sb0);
-      stage_barrier();
-      issue(sb0, s + 4);
-      compute(sb1);
-      stage_barrier();
-      issue(sb1, s + 5);
-      compute(sb2);
-      stage_barrier();
-      issue(sb2, s + 6);
-      compute(sb3);
+    read_half(sb0, 0, fa0, fb0);
+#define LRC_DL_STEP(CUR, NXT, NEXT_ISSUE) \
+  read_half(CUR, 1, fa1, fb1);            \
+  mma(fa0, fb0);                          \
+  stage_barrier();                        \
+  issue(CUR, NEXT_ISSUE);                 \
+  __builtin_amdgcn_sched_barrier(0);      \
+  read_half(NXT, 0, fa0, fb0);            \
+  mma(fa1, fb1);
+    for (; s + 7 < nsteps; s += 4) {
+      LRC_DL_STEP(sb0, sb1, s + 4)
+      LRC_DL_STEP(sb1, sb2, s + 5)
+      LRC_DL_STEP(sb2, sb3, s + 6)
+      LRC_DL_STEP(sb3, sb0, s + 7)
     }
+#undef LRC_DL_STEP
     for (; s < nsteps; ++s) {
-      if (s + 3 < nsteps) {
-        stage_barrier();
-        issue(buf(s + 3), s + 3);
-      } else {
-        LRC_VMCNT_BARRIER(0);
+      read_half(buf(s), 1, fa1, fb1);
+      mma(fa0, fb0);
+      if (s + 1 < nsteps) {
+        if (s + 4 < nsteps) {  // stages s + 2 and s + 3 are outstanding
+          stage_barrier();
+          issue(buf(s), s + 4);
+        } else {
+          LRC_VMCNT_BARRIER(0);
+        }
+        read_half(buf(s + 1), 0, fa0, fb0);
       }
-      compute(buf(s));
+      mma(fa1, fb1);
     }
   } else {
-    for (; s < nsteps; ++s) {
-      if (s + 3 < nsteps) {
+    for (; s + 1 < nsteps; ++s) {
+      if (s + 4 < nsteps) {
         stage_barrier();
-        issue(buf(s + 3), s + 3);
+        issue(buf(s), s + 4);
       } else {
         LRC_VMCNT_BARRIER(0);
       }
     }
   }
+  // prologue loads of stages past a short split may still be in flight
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   const int r_base = wr * RB, c_base = wc * 128;
   float* part = partial + (int64_t(split) * n_tiles + tile) * (TB * TB);
@@ -601,9 +626,9 @@ lrc_status launch_syrk_bf16(hipStream_t st, const uint16_t* X, const uint16_t* Y
   ProfScope scope("syrk_bf16_kernel", st, 2.0 * double(n) * tri,
                   double(n) * double(d) * 2.0 * (X == Y ? 1 : 2) + 8.0 * tri);
   const int64_t tok_per_split = int64_t(p.steps_per_split) * KS;
-  // direct-load kernel: buffer offsets of a split (rows of ldx bf16, plus the three
+  // direct-load kernel: buffer offsets of a split (rows of ldx bf16, plus the four
   // stages the pipeline may fetch past its end) must stay below 2^31
-  if (vec && (tok_per_split + 3 * KS2) * ldx * 2 < (int64_t(1) << 31))
+  if (vec && (tok_per_split + 4 * KS2) * ldx * 2 < (int64_t(1) << 31))
     syrk_bf16_dl_kernel<<<grid, 64 * DL_NW, 0, st>>>(X, Y, ldx, n, int(d), p.n1, p.n_tiles, p.tiles_per_xcd, p.splits,
                                                  tok_per_split, partial);
   else if (vec)
