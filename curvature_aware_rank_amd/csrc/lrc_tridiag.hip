@@ -161,6 +161,44 @@ __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict_
   const int s0 = i + 1;
   const int m = n - s0;
   const int nbt = (m + TS - 1) / TS;
+  const int ntile = nbt * (nbt + 1) / 2;
+  if (int(blockIdx.x) >= ntile) {
+    // panel workgroup for row block pb: V^T x and W^T x over the block's 64 rows, 32
+    // columns x 8 groups of 8 rows, summed over the groups in order
+    const int pb = blockIdx.x - ntile;
+    const int R0 = s0 + pb * TS;
+    const int pc = tid & 31, pg = tid >> 5;
+    const int pcc = min(pc, jj - 1);
+    double va[8], wa[8], xa[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int r = min(R0 + pg * 8 + q, n - 1);
+      va[q] = A[int64_t(r) * lda + i0 + pcc];
+      wa[q] = Wp[int64_t(r) * NB + pcc];
+      xa[q] = xv[r];
+    }
+    double sv = 0.0, sw = 0.0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const bool ok = pc < jj && R0 + pg * 8 + q < n;
+      sv += ok ? va[q] * xa[q] : 0.0;
+      sw += ok ? wa[q] * xa[q] : 0.0;
+    }
+    red[pg][0][pc] = sv;
+    red[pg][1][pc] = sw;
+    __syncthreads();
+    if (tid < jj) {
+      double a0 = 0.0, a1 = 0.0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        a0 += red[q][0][tid];
+        a1 += red[q][1][tid];
+      }
+      SV[pb * NB + tid] = a0;
+      SW[pb * NB + tid] = a1;
+    }
+    return;
+  }
   int b, c;
   tile_of(blockIdx.x, b, c);
   const int R0 = s0 + b * TS, C0 = s0 + c * TS;
@@ -214,20 +252,6 @@ __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict_
     vcl[e] = xv[min(c4 + e, n - 1)];
     vbl[e] = xv[min(rr4 + e, n - 1)];
   }
-  // panel rows for V^T x, W^T x (diagonal tiles): 32 columns x 8 groups of 8 rows
-  const int pc = tid & 31, pg = tid >> 5;
-  double va[8], wa[8], xa[8];
-  const bool pan = diag && jj > 0;
-  if (pan) {
-    const int pcc = min(pc, jj - 1);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int r = min(R0 + pg * 8 + q, n - 1);
-      va[q] = A[int64_t(r) * lda + i0 + pcc];
-      wa[q] = Wp[int64_t(r) * NB + pcc];
-      xa[q] = xv[r];
-    }
-  }
   double xe = 0.0;   // x on row R0 + tid (x^T C x epilogue)
   if (tid < TS) xe = xv[min(R0 + tid, n - 1)];
   // row sums over the tile's lower part incl. the diagonal; column sums strictly below it
@@ -260,17 +284,6 @@ __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict_
     const double r = quad_sum(kv + dpp_mov<DPP_HALF_MIRROR>(sv));
     if ((cb & 3) == 0) rsum[4 * rb + 2 * ((cb >> 3) & 1) + ((cb >> 2) & 1)] = r;
   }
-  if (pan) {
-    double sv = 0.0, sw = 0.0;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const bool ok = pc < jj && R0 + pg * 8 + q < n;
-      sv += ok ? va[q] * xa[q] : 0.0;
-      sw += ok ? wa[q] * xa[q] : 0.0;
-    }
-    red[pg][0][pc] = sv;
-    red[pg][1][pc] = sw;
-  }
   __syncthreads();
   if (tid < TS) {
     double c_ = 0.0;
@@ -287,18 +300,6 @@ __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict_
     // x_b^T (tile contribution), fixed butterfly over the first wave
     const double sacc = wave_sum(diag ? xb * (r_ + c_) : 2.0 * (xb * r_));
     if (tid == 0) S[blockIdx.x] = sacc;
-  } else if (pan && tid < TS + NB) {
-    const int cc = tid - TS;
-    if (cc < jj) {
-      double a0 = 0.0, a1 = 0.0;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        a0 += red[q][0][cc];
-        a1 += red[q][1][cc];
-      }
-      SV[b * NB + cc] = a0;
-      SW[b * NB + cc] = a1;
-    }
   }
 }
 
@@ -1613,12 +1614,12 @@ lrc_status tri_reduce(hipStream_t st, double* A, int n, int64_t lda, const TWs& 
         // 16-byte pairs need an even matrix pitch and base; the tile's first column parity
         // picks the pair alignment
         const double* xv = w.xv + par * n;
+        // the tiles, then (inside the panel) one workgroup per row block for V^T x, W^T x
+        const unsigned grid = unsigned(nbt * (nbt + 1) / 2 + (jj > 0 ? nbt : 0));
         if ((i + 1) % 2 == 0)
-          tri_symv_kernel<true><<<unsigned(nbt * (nbt + 1) / 2), 256, 0, st>>>(A, lda, n, i, i0, jj, w.Wp, xv, w.P,
-                                                                                w.S, w.SV, w.SW);
+          tri_symv_kernel<true><<<grid, 256, 0, st>>>(A, lda, n, i, i0, jj, w.Wp, xv, w.P, w.S, w.SV, w.SW);
         else
-          tri_symv_kernel<false><<<unsigned(nbt * (nbt + 1) / 2), 256, 0, st>>>(A, lda, n, i, i0, jj, w.Wp, xv, w.P,
-                                                                                 w.S, w.SV, w.SW);
+          tri_symv_kernel<false><<<grid, 256, 0, st>>>(A, lda, n, i, i0, jj, w.Wp, xv, w.P, w.S, w.SV, w.SW);
         LRC_LAUNCHED();
       }
       {
