@@ -92,6 +92,28 @@ ProfScope::~ProfScope() {
   t.bytes += bytes;
 }
 
+ProfKernel::ProfKernel(const char* n, double f, double b) : name(n), flops(f), bytes(b) {
+  if (!g_prof_on) return;
+  start = acquire_event();
+  stop = acquire_event();
+  if (!start || !stop) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (start) g_prof_pool.push_back(start);
+    if (stop) g_prof_pool.push_back(stop);
+    start = stop = nullptr;
+  }
+}
+
+ProfKernel::~ProfKernel() {
+  if (!start) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_events.push_back(ProfEvent{name, start, stop});
+  ProfTotal& t = total_for(name);
+  t.launches += 1;
+  t.flops += flops;
+  t.bytes += bytes;
+}
+
 }  // namespace lrc
 
 extern "C" lrc_status lrc_profile_start(void) {

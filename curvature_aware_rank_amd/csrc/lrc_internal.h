@@ -63,6 +63,18 @@ struct ProfScope {
   ~ProfScope();
 };
 
+// One kernel launched through hipExtLaunchKernelGGL with start/stop: the two events then
+// carry the kernel's own begin and end (no marker packets of their own in the stream, so
+// a short kernel reads as long as in a kernel trace).  Both are null when the session is
+// off, which makes the launch an ordinary one.
+struct ProfKernel {
+  const char* name;
+  double flops, bytes;
+  hipEvent_t start = nullptr, stop = nullptr;
+  ProfKernel(const char* n, double f, double b);
+  ~ProfKernel();
+};
+
 // ---------------------------------------------------------------------------------
 // device-side types and conversions
 // ---------------------------------------------------------------------------------

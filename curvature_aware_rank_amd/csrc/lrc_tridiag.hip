@@ -29,6 +29,8 @@
 #include <algorithm>
 #include <vector>
 
+#include <hip/hip_ext.h>
+
 #include "lrc_dense.h"
 
 namespace lrc {
@@ -1609,32 +1611,32 @@ lrc_status tri_reduce(hipStream_t st, double* A, int n, int64_t lda, const TWs& 
       double* np_cur = w.npart + par * 4 * cdiv(n, TS);
       double* np_next = w.npart + npar * 4 * cdiv(n, TS);
       {
-        ProfScope scope("tri_symv_kernel", st, 2.0 * double(m) * double(m),
-                        8.0 * double(m) * double(m + 1) / 2);
+        ProfKernel pk("tri_symv_kernel", 2.0 * double(m) * double(m), 8.0 * double(m) * double(m + 1) / 2);
         // 16-byte pairs need an even matrix pitch and base; the tile's first column parity
         // picks the pair alignment
         const double* xv = w.xv + par * n;
         // the tiles, then (inside the panel) one workgroup per row block for V^T x, W^T x
-        const unsigned grid = unsigned(nbt * (nbt + 1) / 2 + (jj > 0 ? nbt : 0));
+        const dim3 grid(unsigned(nbt * (nbt + 1) / 2 + (jj > 0 ? nbt : 0)));
         if ((i + 1) % 2 == 0)
-          tri_symv_kernel<true><<<grid, 256, 0, st>>>(A, lda, n, i, i0, jj, w.Wp, xv, w.P, w.S, w.SV, w.SW);
+          hipExtLaunchKernelGGL(tri_symv_kernel<true>, grid, dim3(256), 0, st, pk.start, pk.stop, 0, (const double*)A,
+                                lda, n, i, i0, jj, (const double*)w.Wp, xv, w.P, w.S, w.SV, w.SW);
         else
-          tri_symv_kernel<false><<<grid, 256, 0, st>>>(A, lda, n, i, i0, jj, w.Wp, xv, w.P, w.S, w.SV, w.SW);
+          hipExtLaunchKernelGGL(tri_symv_kernel<false>, grid, dim3(256), 0, st, pk.start, pk.stop, 0, (const double*)A,
+                                lda, n, i, i0, jj, (const double*)w.Wp, xv, w.P, w.S, w.SV, w.SW);
         LRC_LAUNCHED();
       }
       {
         // bytes: the symv partials, the panel rows of V and W, column i (and i+1) read and
         // written, the new column of W
-        ProfScope scope("tri_w_kernel", st, 4.0 * double(m) * (jj + 1),
-                        8.0 * (double(nbt) * nbt * TS + 2.0 * double(m) * jj + 5.0 * double(m)));
-        if (i % 2 == 0)   // columns i, i + 1 form an aligned pair
-          tri_w_kernel<true><<<unsigned(nbt), 256, 0, st>>>(A, lda, n, i, i0, jj, jj + 1 < pb ? 1 : 0, w.Wp, np_cur,
-                                                            w.x0 + par, w.P, w.S, w.SV, w.SW, np_next, w.x0 + npar,
-                                                            w.d, w.e, w.tau, w.xv + npar * n);
-        else
-          tri_w_kernel<false><<<unsigned(nbt), 256, 0, st>>>(A, lda, n, i, i0, jj, jj + 1 < pb ? 1 : 0, w.Wp, np_cur,
-                                                             w.x0 + par, w.P, w.S, w.SV, w.SW, np_next, w.x0 + npar,
-                                                             w.d, w.e, w.tau, w.xv + npar * n);
+        ProfKernel pk("tri_w_kernel", 4.0 * double(m) * (jj + 1),
+                      8.0 * (double(nbt) * nbt * TS + 2.0 * double(m) * jj + 5.0 * double(m)));
+        const int do_next = jj + 1 < pb ? 1 : 0;
+        // columns i, i + 1 form an aligned pair when i is even
+        hipExtLaunchKernelGGL(i % 2 == 0 ? tri_w_kernel<true> : tri_w_kernel<false>, dim3(unsigned(nbt)), dim3(256), 0,
+                              st, pk.start, pk.stop, 0, A, lda, n, i, i0, jj, do_next, w.Wp, (const double*)np_cur,
+                              (const double*)(w.x0 + par), (const double*)w.P, (const double*)w.S,
+                              (const double*)w.SV, (const double*)w.SW, np_next, w.x0 + npar, w.d, w.e, w.tau,
+                              w.xv + npar * n);
         LRC_LAUNCHED();
       }
     }
