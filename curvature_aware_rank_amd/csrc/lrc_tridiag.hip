@@ -41,6 +41,8 @@ constexpr int TS = 64;          // tile and row-block size of the symv / w kerne
 constexpr int BW = 128;         // reflectors per back-transformation block
 constexpr int BT_CHUNK = 128;   // rows per partial of V^T Z
 constexpr int G_CHUNK = 1024;   // rows per partial of V^T V
+constexpr int WR = 32;          // rows per workgroup of the w kernel (half a 64-row block)
+constexpr int NPB = 8;          // squared-norm partials per 64-row block (one per w wave)
 constexpr int BIS_PTS = 16;     // Sturm points per eigenvalue per multisection step
 constexpr int BIS_ITERS = 14;   // 17^14 > 2^57: the interval shrinks below fp64 resolution
 constexpr int BIS_STAGE = 2048; // d, e^2 staged through LDS in chunks of this many
@@ -117,7 +119,7 @@ __device__ __forceinline__ double block_sum256(double v, double* red) {
 }
 
 // ---- 1a. first column of a panel: d[i], x0, squared-norm partials (no deferred updates;
-// four partials per 64-row block, as the w kernel writes them: the block's sum, then zeros)
+// NPB partials per 64-row block, as the w kernel writes them: the block's sum, then zeros)
 // and the column as a contiguous vector xv[r] (rows i .. n - 1) for the symv kernel
 __global__ __launch_bounds__(256) void tri_colstart_kernel(const double* __restrict__ A, int64_t lda, int n, int i,
                                                            double* __restrict__ npart, double* __restrict__ x0,
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(256) void tri_colstart_kernel(const double* __restr
     if (r >= i + 2) sq = val * val;
   }
   const double s = block_sum256(sq, red);
-  if (tid < 4) npart[4 * blockIdx.x + tid] = tid == 0 ? s : 0.0;
+  if (tid < NPB) npart[NPB * blockIdx.x + tid] = tid == 0 ? s : 0.0;
 }
 
 // ---- 1b. symv over the trailing matrix (rows/cols i+1 .. n-1) with the raw column
@@ -305,15 +307,24 @@ __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict_
   }
 }
 
-// ---- 1c. for one 64-row block of the trailing rows: the Householder scalars of column i,
-// v = scale x + c e_{s0} (c = 1 - scale x0), C v = scale (C x) + c C e_{s0},
+// ---- 1c. for 32 rows of the trailing rows (two workgroups per 64-row block): the
+// Householder scalars of column i, v = scale x + c e_{s0} (c = 1 - scale x0),
+// C v = scale (C x) + c C e_{s0},
 // w = tau (C v - W V^T v - V W^T v) + alpha v with alpha = -tau^2/2 (v^T C v - 2 (V^T v).(W^T v));
 // store v (column i) and w (column jj of W); then bring column s0 up to date with the
 // panel's reflectors 0..jj (if it is in the panel) and write its squared-norm partials
-// (one per wave: rows 16 wv .. 16 wv + 15 of the block).
+// (one per wave: 8 rows each, NPB per 64-row block).
 // Every global load is issued in one phase, from clamped addresses and masked after: the
-// block's row of symv partials, the panel partials and the block's panel rows as 16-byte
-// pairs along contiguous rows, columns i and s0 once per row (one pair when i is even).
+// rows' symv partials, the panel partials and the rows' panel entries as 16-byte pairs
+// along contiguous rows, columns i and s0 once per row (one pair when i is even).  Half a
+// block per workgroup halves the per-workgroup bytes that are not shared by all of them
+// (the load phase is bound by what one CU can fetch) and the per-row work per thread.
+// sum over the 8 lanes of an aligned octet (every lane of the octet gets the same bits)
+__device__ __forceinline__ double oct_sum(double v) {
+  v = quad_sum(v);
+  return v + dpp_mov<DPP_HALF_MIRROR>(v);
+}
+
 template <bool EVEN>
 __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int64_t lda, int n, int i, int i0, int jj,
                                                     int do_next, double* __restrict__ Wp,
@@ -323,36 +334,40 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
                                                     double* __restrict__ npart_next, double* __restrict__ x0_next,
                                                     double* __restrict__ d, double* __restrict__ e,
                                                     double* __restrict__ tau_out, double* __restrict__ xv_next) {
-  __shared__ double Vs[TS][NB + 1], Ws[TS][NB + 1];
-  __shared__ double yp[8][TS];
+  __shared__ double Vs[WR][NB + 1], Ws[WR][NB + 1];
+  __shared__ double yp[16][WR];
   __shared__ double svq[16][NB], swq[16][NB];
   __shared__ double vn[NB], wn[NB];
   __shared__ double svw[4][NB], sww[4][NB];   // per-wave copies of V^T v, W^T v
-  __shared__ double colI[TS], colS[TS];
+  __shared__ double colI[WR], colS[WR];
   __shared__ double red[3][4];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int s0 = i + 1;
   const int m = n - s0;
   const int nbt = (m + TS - 1) / TS;
   const int ntile = nbt * (nbt + 1) / 2;
-  const int np4 = 4 * ((n - i + TS - 1) / TS);
-  const int b = blockIdx.x;
-  const int R0 = s0 + b * TS;
-  const int xp = tid & 31, cg = tid >> 5;   // symv partials: row pair 2 xp, column blocks cg + 8 u
+  const int npp = NPB * ((n - i + TS - 1) / TS);   // partials written for column i
+  const int b = blockIdx.x >> 1, h = blockIdx.x & 1;
+  const int lr0 = h * WR;        // first row of this workgroup within its 64-row block
+  const int R0 = s0 + b * TS + lr0;
+  const int xp = tid & 15, cg = tid >> 4;   // symv partials: row pair 2 xp, column blocks cg + 16 u
   const int cq = tid & 15, qg = tid >> 4;   // panel: column pair 2 cq, row (block) group qg + 16 u
   // panel column pair start, never past column i0 + jj = i
   const int pcs = max(min(2 * cq, (jj - 1) & ~1), 0);
 
   // ---- load phase
-  double2 pp[8], svl[4], swl[4], pv[4], pw[4];
+  double2 pp[4], svl[4], swl[4], pv[2], pw[2];
 #pragma unroll
-  for (int u = 0; u < 8; ++u)
-    pp[u] = *reinterpret_cast<const double2*>(P + (int64_t(b) * nbt + min(cg + 8 * u, nbt - 1)) * TS + 2 * xp);
+  for (int u = 0; u < 4; ++u)
+    pp[u] = *reinterpret_cast<const double2*>(P + (int64_t(b) * nbt + min(cg + 16 * u, nbt - 1)) * TS + lr0 + 2 * xp);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int q = min(qg + 16 * u, nbt - 1);
     svl[u] = *reinterpret_cast<const double2*>(SV + q * NB + pcs);
     swl[u] = *reinterpret_cast<const double2*>(SW + q * NB + pcs);
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
     const int r = min(R0 + qg + 16 * u, n - 1);
     pv[u] = *reinterpret_cast<const double2*>(A + int64_t(r) * lda + i0 + pcs);
     pw[u] = *reinterpret_cast<const double2*>(Wp + int64_t(r) * NB + pcs);
@@ -363,7 +378,7 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
     wnl = *reinterpret_cast<const double2*>(Wp + int64_t(s0) * NB + pcs);
   }
   double ci = 0.0, cs0 = 0.0;
-  if (tid < TS) {
+  if (tid < WR) {
     const int r = min(R0 + tid, n - 1);
     if (EVEN) {
       const double2 t2 = *reinterpret_cast<const double2*>(A + int64_t(r) * lda + i);
@@ -377,7 +392,8 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
   double ts[9];
 #pragma unroll
   for (int u = 0; u < 9; ++u) ts[u] = S[min(tid + 256 * u, ntile - 1)];
-  const double tnp = npart[min(tid, np4 - 1)];
+  const double tnp0 = npart[min(tid, npp - 1)];
+  const double tnp1 = npart[min(tid + 256, npp - 1)];
   const double tp0 = P[int64_t(min(tid, nbt - 1)) * TS];   // row s0 = block 0, local 0
   const double x0v = *x0p;
   const double a00 = A[int64_t(s0) * lda + s0];
@@ -386,13 +402,13 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
   {
     double ya = 0.0, yb = 0.0;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const bool ok = cg + 8 * u < nbt;
+    for (int u = 0; u < 4; ++u) {
+      const bool ok = cg + 16 * u < nbt;
       ya += ok ? pp[u].x : 0.0;
       yb += ok ? pp[u].y : 0.0;
     }
-    for (int c = cg + 64; c < nbt; c += 8) {   // more than 64 row blocks
-      const double2 t2 = *reinterpret_cast<const double2*>(P + (int64_t(b) * nbt + c) * TS + 2 * xp);
+    for (int c = cg + 64; c < nbt; c += 16) {   // more than 64 row blocks
+      const double2 t2 = *reinterpret_cast<const double2*>(P + (int64_t(b) * nbt + c) * TS + lr0 + 2 * xp);
       ya += t2.x;
       yb += t2.y;
     }
@@ -423,7 +439,7 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
     swq[qg][2 * cq + 1] = b1;
   }
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < 2; ++u) {
     const int rr = qg + 16 * u;
     const bool okr = R0 + rr < n;
     Vs[rr][2 * cq] = okr && 2 * cq < jj ? pv[u].x : 0.0;
@@ -437,14 +453,14 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
     wn[2 * tid] = 2 * tid < jj ? wnl.x : 0.0;
     wn[2 * tid + 1] = 2 * tid + 1 < jj ? wnl.y : 0.0;
   }
-  if (tid < TS) {
+  if (tid < WR) {
     const bool ok = R0 + tid < n;
     colI[tid] = ok ? ci : 0.0;
     colS[tid] = ok ? cs0 : 0.0;
   }
   {
-    double v0 = tid < np4 ? tnp : 0.0;
-    for (int t = tid + 256; t < np4; t += 256) v0 += npart[t];
+    double v0 = (tid < npp ? tnp0 : 0.0) + (tid + 256 < npp ? tnp1 : 0.0);
+    for (int t = tid + 512; t < npp; t += 256) v0 += npart[t];
     double v1 = 0.0;
 #pragma unroll
     for (int u = 0; u < 9; ++u) v1 += tid + 256 * u < ntile ? ts[u] : 0.0;
@@ -465,7 +481,7 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
   double tau, beta, scale;
   house_from_sum(xn2, x0v, tau, beta, scale);
   const double cfac = 1.0 - scale * x0v;
-  if (b == 0 && tid == 0) {
+  if (blockIdx.x == 0 && tid == 0) {
     e[i] = beta;
     tau_out[i] = tau;
   }
@@ -499,22 +515,22 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // rows x = tid / 4 (a wave's rows only): the quad splits the panel columns
-  // (c = part + 4 k) and the row-sum groups (2 part, 2 part + 1)
-  const int x = tid >> 2, part = tid & 3;
+  // rows x = tid / 8 (a wave's rows only): the octet splits the panel columns
+  // (c = part + 8 k) and the row-sum groups (2 part, 2 part + 1)
+  const int x = tid >> 3, part = tid & 7;
   const int r = R0 + x;
   double corr = 0.0, c2 = 0.0;
 #pragma unroll
-  for (int k = 0; k < NB / 4; ++k) {   // columns c >= jj hold zeros in every operand
-    const int c = part + 4 * k;
+  for (int k = 0; k < NB / 8; ++k) {   // columns c >= jj hold zeros in every operand
+    const int c = part + 8 * k;
     const double vr = Vs[x][c], wr = Ws[x][c];
     corr += wr * svw[wv][c] + vr * sww[wv][c];
     c2 += vr * wn[c] + wr * vn[c];
   }
   double yr = yp[2 * part][x] + yp[2 * part + 1][x];
-  corr = quad_sum(corr);
-  c2 = quad_sum(c2);
-  yr = quad_sum(yr);
+  corr = oct_sum(corr);
+  c2 = oct_sum(c2);
+  yr = oct_sum(yr);
   double v = 0.0, w = 0.0;
   const double cs0x = colS[x];
   if (r < n) {
@@ -538,7 +554,7 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
     if (r >= s0 + 2) sq = val * val;
   }
   sq = wave_sum(sq);
-  if (lane == 0) npart_next[4 * b + wv] = sq;
+  if (lane == 0) npart_next[NPB * b + 4 * h + wv] = sq;
 }
 
 // ---- 1d. trailing rank-2 panel update, lower tiles of rows/cols j1 .. n-1:
@@ -1562,7 +1578,7 @@ TWs carve_tri(Carve& cv, int64_t n, int64_t ncols) {
   w.S = cv.take<double>(size_t(nbt * (nbt + 1) / 2));
   w.SV = cv.take<double>(size_t(nbt * NB));
   w.SW = cv.take<double>(size_t(nbt * NB));
-  w.npart = cv.take<double>(size_t(2 * 4 * nbt));   // two columns' partials, four per row block
+  w.npart = cv.take<double>(size_t(2 * NPB * nbt));   // two columns' partials, NPB per row block
   w.x0 = cv.take<double>(2);
   w.xv = cv.take<double>(size_t(2 * n));   // two columns as contiguous vectors
   w.d = cv.take<double>(size_t(n));
@@ -1599,7 +1615,7 @@ lrc_status tri_reduce(hipStream_t st, double* A, int n, int64_t lda, const TWs& 
     const int pb = std::min(NB, n - 1 - i0);
     {
       const unsigned g = unsigned(cdiv(n - i0, TS));
-      tri_colstart_kernel<<<g, 256, 0, st>>>(A, lda, n, i0, w.npart + (i0 & 1) * 4 * cdiv(n, TS), w.x0 + (i0 & 1),
+      tri_colstart_kernel<<<g, 256, 0, st>>>(A, lda, n, i0, w.npart + (i0 & 1) * NPB * cdiv(n, TS), w.x0 + (i0 & 1),
                                              w.d, w.xv + (i0 & 1) * n);
       LRC_LAUNCHED();
     }
@@ -1608,8 +1624,8 @@ lrc_status tri_reduce(hipStream_t st, double* A, int n, int64_t lda, const TWs& 
       const int m = n - i - 1;
       const int nbt = int(cdiv(m, TS));
       const int par = i & 1, npar = (i + 1) & 1;
-      double* np_cur = w.npart + par * 4 * cdiv(n, TS);
-      double* np_next = w.npart + npar * 4 * cdiv(n, TS);
+      double* np_cur = w.npart + par * NPB * cdiv(n, TS);
+      double* np_next = w.npart + npar * NPB * cdiv(n, TS);
       {
         ProfKernel pk("tri_symv_kernel", 2.0 * double(m) * double(m), 8.0 * double(m) * double(m + 1) / 2);
         // 16-byte pairs need an even matrix pitch and base; the tile's first column parity
@@ -1632,7 +1648,7 @@ lrc_status tri_reduce(hipStream_t st, double* A, int n, int64_t lda, const TWs& 
                       8.0 * (double(nbt) * nbt * TS + 2.0 * double(m) * jj + 5.0 * double(m)));
         const int do_next = jj + 1 < pb ? 1 : 0;
         // columns i, i + 1 form an aligned pair when i is even
-        hipExtLaunchKernelGGL(i % 2 == 0 ? tri_w_kernel<true> : tri_w_kernel<false>, dim3(unsigned(nbt)), dim3(256), 0,
+        hipExtLaunchKernelGGL(i % 2 == 0 ? tri_w_kernel<true> : tri_w_kernel<false>, dim3(unsigned(2 * nbt)), dim3(256), 0,
                               st, pk.start, pk.stop, 0, A, lda, n, i, i0, jj, do_next, w.Wp, (const double*)np_cur,
                               (const double*)(w.x0 + par), (const double*)w.P, (const double*)w.S,
                               (const double*)w.SV, (const double*)w.SW, np_next, w.x0 + npar, w.d, w.e, w.tau,
