@@ -41,8 +41,9 @@ constexpr int TS = 64;          // tile and row-block size of the symv / w kerne
 constexpr int BW = 128;         // reflectors per back-transformation block
 constexpr int BT_CHUNK = 128;   // rows per partial of V^T Z
 constexpr int G_CHUNK = 1024;   // rows per partial of V^T V
-constexpr int WR = 32;          // rows per workgroup of the w kernel (half a 64-row block)
-constexpr int NPB = 8;          // squared-norm partials per 64-row block (one per w wave)
+constexpr int WR = 32;          // rows per workgroup of the w kernel (16 or 32; 16 measured no faster)
+constexpr int WPB = TS / WR;    // w workgroups per 64-row block
+constexpr int NPB = 4 * WPB;    // squared-norm partials per 64-row block (one per w wave)
 constexpr int BIS_PTS = 16;     // Sturm points per eigenvalue per multisection step
 constexpr int BIS_ITERS = 14;   // 17^14 > 2^57: the interval shrinks below fp64 resolution
 constexpr int BIS_STAGE = 2048; // d, e^2 staged through LDS in chunks of this many
@@ -307,22 +308,30 @@ __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict_
   }
 }
 
-// ---- 1c. for 32 rows of the trailing rows (two workgroups per 64-row block): the
+// ---- 1c. for WR rows of the trailing rows (TS / WR workgroups per 64-row block): the
 // Householder scalars of column i, v = scale x + c e_{s0} (c = 1 - scale x0),
 // C v = scale (C x) + c C e_{s0},
 // w = tau (C v - W V^T v - V W^T v) + alpha v with alpha = -tau^2/2 (v^T C v - 2 (V^T v).(W^T v));
 // store v (column i) and w (column jj of W); then bring column s0 up to date with the
 // panel's reflectors 0..jj (if it is in the panel) and write its squared-norm partials
-// (one per wave: 8 rows each, NPB per 64-row block).
+// (one per wave: WR / 4 rows each, NPB per 64-row block).
 // Every global load is issued in one phase, from clamped addresses and masked after: the
 // rows' symv partials, the panel partials and the rows' panel entries as 16-byte pairs
 // along contiguous rows, columns i and s0 once per row (one pair when i is even).  Half a
 // block per workgroup halves the per-workgroup bytes that are not shared by all of them
-// (the load phase is bound by what one CU can fetch) and the per-row work per thread.
+// (the load phase is bound by what one CU can fetch) and the per-row work per thread;
+// a quarter block measured no faster (the bytes every workgroup needs then dominate).
 // sum over the 8 lanes of an aligned octet (every lane of the octet gets the same bits)
 __device__ __forceinline__ double oct_sum(double v) {
   v = quad_sum(v);
   return v + dpp_mov<DPP_HALF_MIRROR>(v);
+}
+// sum over the TPR (8 or 16) lanes of an aligned group
+template <int TPR>
+__device__ __forceinline__ double group_sum(double v) {
+  v = oct_sum(v);
+  if constexpr (TPR == 16) v += dpp_mov<DPP_MIRROR>(v);
+  return v;
 }
 
 template <bool EVEN>
@@ -334,8 +343,14 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
                                                     double* __restrict__ npart_next, double* __restrict__ x0_next,
                                                     double* __restrict__ d, double* __restrict__ e,
                                                     double* __restrict__ tau_out, double* __restrict__ xv_next) {
+  constexpr int RPAIRS = WR / 2;       // row pairs of the symv partials
+  constexpr int NCG = 256 / RPAIRS;    // column-block groups (16 or 32)
+  constexpr int NPU = TS / NCG;        // column blocks per group below 64 blocks
+  constexpr int TPR = 256 / WR;        // threads per row in the row stage (8 or 16)
+  constexpr int NRU = WR / 16;         // panel row groups of 16
+  static_assert(WR == 16 || WR == 32, "16 or 32 rows per workgroup");
   __shared__ double Vs[WR][NB + 1], Ws[WR][NB + 1];
-  __shared__ double yp[16][WR];
+  __shared__ double yp[NCG][WR];
   __shared__ double svq[16][NB], swq[16][NB];
   __shared__ double vn[NB], wn[NB];
   __shared__ double svw[4][NB], sww[4][NB];   // per-wave copies of V^T v, W^T v
@@ -347,19 +362,19 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
   const int nbt = (m + TS - 1) / TS;
   const int ntile = nbt * (nbt + 1) / 2;
   const int npp = NPB * ((n - i + TS - 1) / TS);   // partials written for column i
-  const int b = blockIdx.x >> 1, h = blockIdx.x & 1;
+  const int b = blockIdx.x / WPB, h = blockIdx.x % WPB;
   const int lr0 = h * WR;        // first row of this workgroup within its 64-row block
   const int R0 = s0 + b * TS + lr0;
-  const int xp = tid & 15, cg = tid >> 4;   // symv partials: row pair 2 xp, column blocks cg + 16 u
+  const int xp = tid % RPAIRS, cg = tid / RPAIRS;   // symv partials: row pair 2 xp, column blocks cg + NCG u
   const int cq = tid & 15, qg = tid >> 4;   // panel: column pair 2 cq, row (block) group qg + 16 u
   // panel column pair start, never past column i0 + jj = i
   const int pcs = max(min(2 * cq, (jj - 1) & ~1), 0);
 
   // ---- load phase
-  double2 pp[4], svl[4], swl[4], pv[2], pw[2];
+  double2 pp[NPU], svl[4], swl[4], pv[NRU], pw[NRU];
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
-    pp[u] = *reinterpret_cast<const double2*>(P + (int64_t(b) * nbt + min(cg + 16 * u, nbt - 1)) * TS + lr0 + 2 * xp);
+  for (int u = 0; u < NPU; ++u)
+    pp[u] = *reinterpret_cast<const double2*>(P + (int64_t(b) * nbt + min(cg + NCG * u, nbt - 1)) * TS + lr0 + 2 * xp);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int q = min(qg + 16 * u, nbt - 1);
@@ -367,7 +382,7 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
     swl[u] = *reinterpret_cast<const double2*>(SW + q * NB + pcs);
   }
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < NRU; ++u) {
     const int r = min(R0 + qg + 16 * u, n - 1);
     pv[u] = *reinterpret_cast<const double2*>(A + int64_t(r) * lda + i0 + pcs);
     pw[u] = *reinterpret_cast<const double2*>(Wp + int64_t(r) * NB + pcs);
@@ -402,12 +417,12 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
   {
     double ya = 0.0, yb = 0.0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const bool ok = cg + 16 * u < nbt;
+    for (int u = 0; u < NPU; ++u) {
+      const bool ok = cg + NCG * u < nbt;
       ya += ok ? pp[u].x : 0.0;
       yb += ok ? pp[u].y : 0.0;
     }
-    for (int c = cg + 64; c < nbt; c += 16) {   // more than 64 row blocks
+    for (int c = cg + 64; c < nbt; c += NCG) {   // more than 64 row blocks
       const double2 t2 = *reinterpret_cast<const double2*>(P + (int64_t(b) * nbt + c) * TS + lr0 + 2 * xp);
       ya += t2.x;
       yb += t2.y;
@@ -439,7 +454,7 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
     swq[qg][2 * cq + 1] = b1;
   }
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < NRU; ++u) {
     const int rr = qg + 16 * u;
     const bool okr = R0 + rr < n;
     Vs[rr][2 * cq] = okr && 2 * cq < jj ? pv[u].x : 0.0;
@@ -515,22 +530,22 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // rows x = tid / 8 (a wave's rows only): the octet splits the panel columns
-  // (c = part + 8 k) and the row-sum groups (2 part, 2 part + 1)
-  const int x = tid >> 3, part = tid & 7;
+  // rows x = tid / TPR (a wave's rows only): the row's TPR lanes split the panel columns
+  // (c = part + TPR k) and the row-sum groups (2 part, 2 part + 1)
+  const int x = tid / TPR, part = tid % TPR;
   const int r = R0 + x;
   double corr = 0.0, c2 = 0.0;
 #pragma unroll
-  for (int k = 0; k < NB / 8; ++k) {   // columns c >= jj hold zeros in every operand
-    const int c = part + 8 * k;
+  for (int k = 0; k < NB / TPR; ++k) {   // columns c >= jj hold zeros in every operand
+    const int c = part + TPR * k;
     const double vr = Vs[x][c], wr = Ws[x][c];
     corr += wr * svw[wv][c] + vr * sww[wv][c];
     c2 += vr * wn[c] + wr * vn[c];
   }
   double yr = yp[2 * part][x] + yp[2 * part + 1][x];
-  corr = oct_sum(corr);
-  c2 = oct_sum(c2);
-  yr = oct_sum(yr);
+  corr = group_sum<TPR>(corr);
+  c2 = group_sum<TPR>(c2);
+  yr = group_sum<TPR>(yr);
   double v = 0.0, w = 0.0;
   const double cs0x = colS[x];
   if (r < n) {
@@ -778,7 +793,16 @@ __global__ __launch_bounds__(256) void tri_bounds_kernel(const double* __restric
   }
 }
 
-// 16 eigenvalues per workgroup, 16 Sturm points each; lam ascending
+// 16 eigenvalues per workgroup, 16 Sturm points each; lam ascending.
+// The Sturm count at x is the number of negative ratios q_k = p_k / p_{k-1} of the leading
+// principal minors p_k of T - x I.  The minors follow p_{k+1} = (d_k - x) p_k - e_{k-1}^2
+// p_{k-1} with no division (the ratio form needs one per step, whose latency bound the
+// recurrence); a sign change between p_{k-1} and p_k is a negative q_k.  T is scaled by a
+// power of two to norm in [1, 2) (exact), a |q_k| below 2^-60 is replaced by -2^-60 (a
+// perturbation of d_k far below the n eps ||T|| accuracy of any count), and the pair
+// (p_{k-1}, p_k) is rescaled by a power of two every 8 steps, which keeps both inside the
+// fp64 range (each step changes max(|p_k|, |p_{k-1}|) by at most a factor 8 up or 2^-60
+// down).
 __global__ __launch_bounds__(256) void tri_bisect_kernel(const double* __restrict__ d, const double* __restrict__ e,
                                                          int n, const double* __restrict__ bounds,
                                                          double* __restrict__ lam) {
@@ -786,37 +810,41 @@ __global__ __launch_bounds__(256) void tri_bisect_kernel(const double* __restric
   const int tid = threadIdx.x;
   const int grp = tid >> 4, pt = tid & 15;
   const int mi = blockIdx.x * 16 + grp;   // ascending index
-  const double pivmin = bounds[2];
   double lo = bounds[0], hi = bounds[1];
+  // 2^-ex with ||T|| = bounds[3] in [2^(ex-1), 2^ex)
+  int ex;
+  (void)frexp(bounds[3], &ex);
+  const double sc = ldexp(1.0, -ex);
   for (int it = 0; it < BIS_ITERS; ++it) {
     const double x = lo + (hi - lo) * (double(pt + 1) / double(BIS_PTS + 1));
+    const double xs = x * sc;
     int cnt = 0;
-    double q = 1.0;
+    double pa = 0.0, pb = 1.0;   // p_{k-1}, p_k (p_{-1} = 0, p_0 = 1)
+    auto step = [&](double dk, double e2k) {
+      double p = fma(dk - xs, pb, -(e2k * pa));
+      const double fl = ldexp(fabs(pb), -60);
+      p = fabs(p) < fl ? -ldexp(pb, -60) : p;
+      cnt += (__double2hiint(p) ^ __double2hiint(pb)) < 0;
+      pa = pb;
+      pb = p;
+    };
+    auto rescale = [&]() {
+      int eb;
+      (void)frexp(pb, &eb);
+      pa = ldexp(pa, -eb);
+      pb = ldexp(pb, -eb);
+    };
     for (int k0 = 0; k0 < n; k0 += BIS_STAGE) {
       const int kn = min(BIS_STAGE, n - k0);
       __syncthreads();
       for (int k = tid; k < kn; k += 256) {
-        sd[k] = d[k0 + k];
-        se2[k] = (k0 + k > 0) ? e[k0 + k - 1] * e[k0 + k - 1] : 0.0;
+        sd[k] = d[k0 + k] * sc;
+        const double es = (k0 + k > 0) ? e[k0 + k - 1] * sc : 0.0;
+        se2[k] = es * es;
       }
       __syncthreads();
       int k = 0;
-      if (k0 == 0) {
-        q = sd[0] - x;
-        if (fabs(q) < pivmin) q = -pivmin;
-        cnt += q < 0.0;
-        k = 1;
-      }
-      // e^2 / q via the hardware reciprocal refined by one Newton step (which squares its
-      // relative error): a count is insensitive to last-bit differences.  LDS operands are
-      // read 8 steps at a time, off the recurrence's critical path.
-      auto step = [&](double dk, double e2k) {
-        double rq = __builtin_amdgcn_rcp(q);
-        rq = fma(rq, fma(-q, rq, 1.0), rq);
-        q = fma(-e2k, rq, dk - x);
-        if (fabs(q) < pivmin) q = -pivmin;
-        cnt += q < 0.0;
-      };
+      // LDS operands are read 8 steps at a time, off the recurrence's critical path
       for (; k + 8 <= kn; k += 8) {
         double dk[8], ek[8];
 #pragma unroll
@@ -826,8 +854,10 @@ __global__ __launch_bounds__(256) void tri_bisect_kernel(const double* __restric
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) step(dk[u], ek[u]);
+        rescale();
       }
       for (; k < kn; ++k) step(sd[k], se2[k]);
+      rescale();
     }
     // smallest point whose count exceeds mi bounds the eigenvalue from above
     const unsigned long long bal = __ballot(cnt > mi);
@@ -1648,7 +1678,7 @@ lrc_status tri_reduce(hipStream_t st, double* A, int n, int64_t lda, const TWs& 
                       8.0 * (double(nbt) * nbt * TS + 2.0 * double(m) * jj + 5.0 * double(m)));
         const int do_next = jj + 1 < pb ? 1 : 0;
         // columns i, i + 1 form an aligned pair when i is even
-        hipExtLaunchKernelGGL(i % 2 == 0 ? tri_w_kernel<true> : tri_w_kernel<false>, dim3(unsigned(2 * nbt)), dim3(256), 0,
+        hipExtLaunchKernelGGL(i % 2 == 0 ? tri_w_kernel<true> : tri_w_kernel<false>, dim3(unsigned(WPB * nbt)), dim3(256), 0,
                               st, pk.start, pk.stop, 0, A, lda, n, i, i0, jj, do_next, w.Wp, (const double*)np_cur,
                               (const double*)(w.x0 + par), (const double*)w.P, (const double*)w.S,
                               (const double*)w.SV, (const double*)w.SW, np_next, w.x0 + npar, w.d, w.e, w.tau,
