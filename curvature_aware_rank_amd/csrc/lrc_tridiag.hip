@@ -902,32 +902,26 @@ __device__ __forceinline__ double start_value(int j, int k) {
 }
 
 // Inverse iteration on T for the wanted eigenvalues, in two kernels:
-//  A) one wave per vector: LU with partial pivoting of T - lambda I (the lambda of a
-//     cluster member is lowered to stay at least 10 eps ||T|| below the previous
-//     member's), with the first solve's forward elimination of a pseudo-random start
-//     vector done in the same pass, then the back-substitution;
+//  A) one lane per vector (64 vectors per wave): LU with partial pivoting of T - lambda I
+//     (the lambda of a cluster member is lowered to stay at least 10 eps ||T|| below the
+//     previous member's), with the first solve's forward elimination of a pseudo-random
+//     start vector done in the same pass.  Every lane runs its own vector's recurrence,
+//     so a step costs one wave instruction per operation with no cross-lane traffic; d
+//     and e are wave-uniform operands, loaded a batch of steps ahead, and the results are
+//     only stored, so no memory latency enters the recurrence;
 //  B) one wave per cluster (a lone eigenvalue is a cluster of one), members in order:
-//     orthogonalise the first iterate against the cluster's finished vectors (modified
-//     Gram-Schmidt), normalise, second solve, orthogonalise again, normalise.
-// The recurrences are sequential.  The factorisation runs in chunks of 64 steps whose
-// inputs sit in registers, step i's in lane i (the next chunk's loads in flight
-// meanwhile); the wave evaluates every step uniformly with the operands taken by
-// readlane, so no memory latency enters its dependence chain, and lane 0 drops each
-// step's results into LDS, from where the whole wave writes them out after the chunk.
-// Its divisions are a hardware reciprocal refined by a Newton step, the quotient then
-// corrected by its residual.  The solves (lighter steps) run on lane 0 out of LDS chunks
-// of CHL steps that the whole wave stages.
-// The per-vector arrays are vector major: LU records {1/pivot, u1, u2, multiplier}
-// (32 B) and row-interchange flags, and the iterates Zw (one row of n per vector); a
-// transpose writes Z (n x ncols) at the end.  The orthogonalisation and scaling passes
-// use all lanes (sums per lane in row order, then a fixed butterfly).
-constexpr int CH = 64;   // recurrence steps per chunk (one per lane)
-
-// lane l's value of a double (l a compile-time constant after unrolling)
-__device__ __forceinline__ double lane_of(double v, int l) {
-  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
-                          __builtin_amdgcn_readlane(__double2loint(v), l));
-}
+//     the first solve's back-substitution, orthogonalise the iterate against the
+//     cluster's finished vectors (modified Gram-Schmidt), normalise, second solve,
+//     orthogonalise again, normalise.  These recurrences read back what A stored; with
+//     one wave per vector there are enough waves in flight to cover that latency
+//     (one lane per vector measured latency-bound: 4.5 ms against 2.8 ms).
+// The divisions are a hardware reciprocal refined by a Newton step, the quotient then
+// corrected by its residual.  The arrays are step major, one column per vector: LU
+// records Rt[k][j] = {1/pivot, u1, u2, multiplier} (32 B), row-interchange flags
+// PVt[k][j] and the iterates in Z[k][j] (n x ncols, the layout the back-transformation
+// reads), so the lanes of a wave touch consecutive addresses at every step.  Kernel B's
+// orthogonalisation and scaling passes use all lanes (sums per lane in row order, then a
+// fixed butterfly); its solves run on lane 0 out of LDS chunks the whole wave stages.
 
 // 1 / b: hardware reciprocal refined by one Newton step
 __device__ __forceinline__ double recip(double b) {
@@ -948,15 +942,118 @@ __device__ __forceinline__ double wave_max(double v) {
   return v;
 }
 
-constexpr int CHL = 256;   // steps per LDS-staged chunk of the solves
+constexpr int FCH = 256;   // steps per LDS-staged chunk of d, e in kernel A
+constexpr int CHL = 256;   // steps per LDS-staged chunk of kernel B's solves
 constexpr int CPLL = CHL / 64;
 
-// back-substitution z <- U^-1 z on vector j (records R, iterate z), chunks from the end:
-// lane 0 runs the recurrence out of LDS chunks of CHL steps staged by the whole wave (the
-// next chunk's loads in flight), which measured faster here than register-resident chunks;
-// returns ||z||^2 (to every lane)
-__device__ double inv_usolve_lds(const double* __restrict__ R, double* __restrict__ z, int n, double (*s_in)[CHL][4],
-                             double (*s_z)[CHL], double* s_out, double* s_sc) {
+__global__ __launch_bounds__(64) void tri_inviter_a_kernel(const double* __restrict__ d, const double* __restrict__ e,
+                                                           int n, const double* __restrict__ lam, int ncols,
+                                                           const double* __restrict__ bounds,
+                                                           const int* __restrict__ clen, const int* __restrict__ flag,
+                                                           double* __restrict__ Rt, uint8_t* __restrict__ PVt,
+                                                           double* __restrict__ Z) {
+  if (*flag) return;
+  const int lane = threadIdx.x;
+  const int jr = blockIdx.x * 64 + lane;
+  const int jv = min(jr, ncols - 1);   // lanes past the last vector repeat it
+  int s = jv;   // the cluster's first member (clen is > 0 there, 0 at the others)
+  while (s > 0 && clen[s] == 0) --s;
+  const double tnorm = bounds[3];
+  const double tiny = EPS * tnorm;
+  double lmb = lam[n - 1 - s];
+  for (int p = s + 1; p <= jv; ++p) lmb = fmin(lam[n - 1 - p], lmb - 10.0 * EPS * tnorm);
+  const int nm1 = n - 1;
+  double* Rj = Rt + int64_t(jv) * 4;   // record k at Rj + k * rs
+  const int64_t rs = int64_t(ncols) * 4;
+  uint8_t* Pj = PVt + jv;              // flag k at Pj + k * ncols
+  double* zj = Z + jv;                 // entry k at zj + k * ncols
+
+  // ---- factor T - lmb I = P L U (steps k = 0 .. n-2, then the last pivot) and, in the
+  //      same pass, y = L^-1 P z0 for the start vector z0 (generated on the fly).
+  //      Step k reads e[k], d[k+1], e[k+1], staged through LDS in chunks of FCH steps
+  //      (every lane reads the same address: a broadcast), the next chunk's global loads
+  //      in flight meanwhile.  Lanes past the last vector compute and store exactly what
+  //      that vector's lane does (same bits).
+  __shared__ double s_e[2][FCH + 1], s_d[2][FCH];
+  double ge[FCH / 64 + 1], gd[FCH / 64];
+  auto load_c = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < FCH / 64; ++u) {
+      ge[u] = e[min(k0 + lane + 64 * u, max(n - 2, 0))];
+      gd[u] = d[min(k0 + 1 + lane + 64 * u, n - 1)];
+    }
+    ge[FCH / 64] = e[min(k0 + FCH, max(n - 2, 0))];
+  };
+  auto stage_c = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < FCH / 64; ++u) {
+      s_e[buf][lane + 64 * u] = ge[u];
+      s_d[buf][lane + 64 * u] = gd[u];
+    }
+    if (lane == 0) s_e[buf][FCH] = ge[FCH / 64];
+  };
+  double cd = d[0] - lmb, cs = n > 1 ? e[0] : 0.0;
+  double ycur = start_value(jv, 0);
+  const int nchf = (nm1 + FCH - 1) / FCH;
+  if (nchf > 0) {
+    load_c(0);
+    stage_c(0);
+  }
+  for (int c = 0; c < nchf; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nchf) load_c((c + 1) * FCH);
+    __syncthreads();   // one wave: the chunk's LDS stores are visible
+    const int k0 = c * FCH;
+    const int cnt = min(FCH, nm1 - k0);
+#pragma unroll 8
+    for (int u = 0; u < cnt; ++u) {
+      const int k = k0 + u;
+      const double sub = s_e[buf][u];
+      const double ndk = s_d[buf][u] - lmb;
+      const double ns = k + 1 < nm1 ? s_e[buf][u + 1] : 0.0;
+      // partial pivoting, branch-free: keep row k (pv = 0) or interchange with row k + 1
+      const bool pv = !(fabs(cd) >= fabs(sub));
+      double piv_u0 = pv ? sub : (cd == 0.0 ? tiny : cd);
+      const double num = pv ? cd : sub;
+      double rp = recip(piv_u0);
+      const double l = quot(num, piv_u0, rp);
+      const double u1 = pv ? ndk : cs;
+      const double u2 = pv ? ns : 0.0;
+      const double ncd = pv ? cs - l * ndk : ndk - l * cs;
+      cs = pv ? -l * ns : ns;
+      cd = ncd;
+      if (fabs(piv_u0) < tiny) {   // rare: the recorded pivot is clamped to +-tiny
+        piv_u0 = piv_u0 < 0.0 ? -tiny : tiny;
+        rp = recip(piv_u0);
+      }
+      // forward elimination of the start vector with this step's multiplier
+      const double yn = start_value(jv, k + 1);
+      const double yk = pv ? yn : ycur;
+      const double ynext = pv ? ycur : yn;
+      *reinterpret_cast<f64x2*>(Rj + k * rs) = f64x2{rp, u1};
+      *reinterpret_cast<f64x2*>(Rj + k * rs + 2) = f64x2{u2, l};
+      Pj[int64_t(k) * ncols] = uint8_t(pv);
+      zj[int64_t(k) * ncols] = yk;
+      ycur = ynext - l * yk;
+    }
+    if (c + 1 < nchf) stage_c(buf ^ 1);
+  }
+  {
+    double p0 = cd;
+    if (fabs(p0) < tiny) p0 = p0 < 0.0 ? -tiny : tiny;
+    *reinterpret_cast<f64x2*>(Rj + nm1 * rs) = f64x2{recip(p0), 0.0};
+    *reinterpret_cast<f64x2*>(Rj + nm1 * rs + 2) = f64x2{0.0, 0.0};
+    Pj[int64_t(nm1) * ncols] = 0;
+    zj[int64_t(nm1) * ncols] = ycur;
+  }
+}
+
+// back-substitution z <- U^-1 z on one vector (records R[k * rs], iterate z[k * zs]),
+// chunks from the end: lane 0 runs the recurrence out of LDS chunks of CHL steps staged by
+// the whole wave (the next chunk's loads in flight); returns ||z||^2 (to every lane)
+__device__ double inv_usolve_lds(const double* __restrict__ R, int64_t rs, double* __restrict__ z, int64_t zs, int n,
+                                 double (*__restrict__ s_in)[CHL][4], double (*__restrict__ s_z)[CHL],
+                                 double* __restrict__ s_out, double* __restrict__ s_sc) {
   const int lane = threadIdx.x;
   const int nch = (n + CHL - 1) / CHL;
   double gr[CPLL][4], gz[CPLL];
@@ -964,13 +1061,13 @@ __device__ double inv_usolve_lds(const double* __restrict__ R, double* __restric
 #pragma unroll
     for (int u = 0; u < CPLL; ++u) {
       const int k = min(c * CHL + lane + 64 * u, n - 1);
-      const f64x2 a = *reinterpret_cast<const f64x2*>(R + int64_t(k) * 4);
-      const f64x2 b = *reinterpret_cast<const f64x2*>(R + int64_t(k) * 4 + 2);
+      const f64x2 a = *reinterpret_cast<const f64x2*>(R + int64_t(k) * rs);
+      const f64x2 b = *reinterpret_cast<const f64x2*>(R + int64_t(k) * rs + 2);
       gr[u][0] = a[0];
       gr[u][1] = a[1];
       gr[u][2] = b[0];
       gr[u][3] = b[1];
-      gz[u] = z[k];
+      gz[u] = z[int64_t(k) * zs];
     }
   };
   auto stage = [&](int buf) {
@@ -993,7 +1090,9 @@ __device__ double inv_usolve_lds(const double* __restrict__ R, double* __restric
     if (lane == 0) {
       #pragma unroll 8
       for (int i = cnt - 1; i >= 0; --i) {
-        const double xk = (s_z[buf][i] - s_in[buf][i][1] * x1 - s_in[buf][i][2] * x2) * s_in[buf][i][0];
+        // the older x2 term first: only one fma and the scaling wait for x1
+        const double t = fma(-s_in[buf][i][2], x2, s_z[buf][i]);
+        const double xk = fma(-s_in[buf][i][1], x1, t) * s_in[buf][i][0];
         s_out[i] = xk;
         nrm2 += xk * xk;
         x2 = x1;
@@ -1004,7 +1103,7 @@ __device__ double inv_usolve_lds(const double* __restrict__ R, double* __restric
 #pragma unroll
     for (int u = 0; u < CPLL; ++u) {
       const int i = lane + 64 * u;
-      if (i < cnt) z[c * CHL + i] = s_out[i];
+      if (i < cnt) z[int64_t(c * CHL + i) * zs] = s_out[i];
     }
     if (c > 0) stage(buf ^ 1);
   }
@@ -1013,245 +1112,173 @@ __device__ double inv_usolve_lds(const double* __restrict__ R, double* __restric
   return s_sc[0];
 }
 
-__global__ __launch_bounds__(64) void tri_inviter_a_kernel(const double* __restrict__ d, const double* __restrict__ e,
-                                                           int n, const double* __restrict__ lam, int ncols,
-                                                           const double* __restrict__ bounds,
-                                                           const int* __restrict__ clen, const int* __restrict__ flag,
-                                                           double* __restrict__ Rall, uint8_t* __restrict__ Pall,
-                                                           double* __restrict__ Zw) {
-  __shared__ double s_out[CH];   // factorisation outputs of a 64-step chunk
-  __shared__ double s_rec[CH][4];
-  __shared__ uint8_t s_piv[CH];
-  __shared__ double s_in[2][CHL][4];   // staging of the back-substitution
-  __shared__ double s_z[2][CHL];
-  __shared__ double s_outl[CHL];
-  __shared__ double s_sc[1];
-  const int jv = blockIdx.x;
-  if (*flag) return;
+// Helpers of the per-vector and per-cluster kernels (one wave each); vector p's entry k
+// is Z[k * ncols + p].
+// 1 / ||z||, or for a badly scaled z 1 / ||z|| taken after scaling by its largest entry
+__device__ double inv_unit_scale(const double* __restrict__ z, int64_t zs, int n, double nrm2) {
+  if (nrm2 > 0.0 && nrm2 < 1e300) return 1.0 / sqrt(nrm2);
   const int lane = threadIdx.x;
-  int s = jv;   // the cluster's first member (clen is > 0 there, 0 at the others)
-  while (s > 0 && clen[s] == 0) --s;
-  const double tnorm = bounds[3];
-  const double tiny = EPS * tnorm;
-  double lmb = lam[n - 1 - s];
-  for (int p = s + 1; p <= jv; ++p) lmb = fmin(lam[n - 1 - p], lmb - 10.0 * EPS * tnorm);
-  double* R = Rall + int64_t(jv) * n * 4;
-  uint8_t* PV = Pall + int64_t(jv) * n;
-  double* z = Zw + int64_t(jv) * n;
-  const int nm1 = n - 1;
-  // ---- factor T - lmb I = P L U (steps k = 0 .. n-2, then the last pivot) and, in the
-  //      same pass, y = L^-1 P z0 for the start vector z0 (generated on the fly).
-  // Step k reads e[k], d[k+1], e[k+1]; lane i of chunk c holds e[cCH+i] and d[cCH+i+1],
-  // e[k+1] of the chunk's last step is e[cCH+CH] (held by every lane).
-  // lane i also holds the start vector's entry k + 1 of its step (gy)
-  double ge, gd, gx, gy, ne, nd_, nx, ny;
-  auto load_de = [&](int c, double& a_e, double& a_d, double& a_x, double& a_y) {
-    const int k = c * CH + lane;
-    a_e = e[min(k, max(n - 2, 0))];
-    a_d = d[min(k + 1, n - 1)];
-    a_x = e[min(c * CH + CH, max(n - 2, 0))];
-    a_y = start_value(jv, k + 1);
-  };
-  double cd = d[0] - lmb, cs = n > 1 ? e[0] : 0.0;
-  double ycur = start_value(jv, 0);
-  const int nchf = (nm1 + CH - 1) / CH;
-  if (nchf > 0) load_de(0, ge, gd, gx, gy);
-  for (int c = 0; c < nchf; ++c) {
-    if (c + 1 < nchf) load_de(c + 1, ne, nd_, nx, ny);
-    const int cnt = min(CH, nm1 - c * CH);
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      if (i < cnt) {   // uniform
-        const int k = c * CH + i;
-        const double sub = lane_of(ge, i);
-        const double nd = lane_of(gd, i) - lmb;
-        const double ns = k + 1 < nm1 ? (i + 1 < CH ? lane_of(ge, i + 1) : gx) : 0.0;
-        // partial pivoting, branch-free: keep row k (pv = 0) or interchange with row k + 1
-        const bool pv = !(fabs(cd) >= fabs(sub));
-        double piv_u0 = pv ? sub : (cd == 0.0 ? tiny : cd);
-        const double num = pv ? cd : sub;
-        const double l = quot(num, piv_u0, recip(piv_u0));
-        const double u1 = pv ? nd : cs;
-        const double u2 = pv ? ns : 0.0;
-        const double ncd = pv ? cs - l * nd : nd - l * cs;
-        cs = pv ? -l * ns : ns;
-        cd = ncd;
-        if (fabs(piv_u0) < tiny) piv_u0 = piv_u0 < 0.0 ? -tiny : tiny;
-        // forward elimination of the start vector with this step's multiplier
-        const double yn = lane_of(gy, i);
-        const double yk = pv ? yn : ycur;
-        const double ynext = pv ? ycur : yn;
-        if (lane == 0) {
-          s_rec[i][0] = recip(piv_u0);
-          s_rec[i][1] = u1;
-          s_rec[i][2] = u2;
-          s_rec[i][3] = l;
-          s_piv[i] = uint8_t(pv);
-          s_out[i] = yk;
-        }
-        ycur = ynext - l * yk;
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): lane 0's stores, read by every lane
-    __builtin_amdgcn_wave_barrier();
-    if (lane < cnt) {
-      const int k = c * CH + lane;
-      *reinterpret_cast<f64x2*>(R + int64_t(k) * 4) = f64x2{s_rec[lane][0], s_rec[lane][1]};
-      *reinterpret_cast<f64x2*>(R + int64_t(k) * 4 + 2) = f64x2{s_rec[lane][2], s_rec[lane][3]};
-      PV[k] = s_piv[lane];
-      z[k] = s_out[lane];
-    }
-    __builtin_amdgcn_wave_barrier();
-    ge = ne;
-    gd = nd_;
-    gx = nx;
-    gy = ny;
+  double mx = 0.0;
+  for (int k = lane; k < n; k += 64) mx = fmax(mx, fabs(z[int64_t(k) * zs]));
+  mx = wave_max(mx);
+  const double inv_mx = mx > 0.0 && mx < 1e308 ? 1.0 / mx : 1.0;
+  double s2 = 0.0;
+  for (int k = lane; k < n; k += 64) {
+    const double v = z[int64_t(k) * zs] * inv_mx;
+    s2 += v * v;
   }
-  if (lane == 0) {
-    double p0 = cd;
-    if (fabs(p0) < tiny) p0 = p0 < 0.0 ? -tiny : tiny;
-    *reinterpret_cast<f64x2*>(R + int64_t(nm1) * 4) = f64x2{recip(p0), 0.0};
-    *reinterpret_cast<f64x2*>(R + int64_t(nm1) * 4 + 2) = f64x2{0.0, 0.0};
-    PV[nm1] = 0;
-    z[nm1] = ycur;
-  }
-  __syncthreads();   // the records and y written above are read back below
-  inv_usolve_lds(R, z, n, s_in, s_z, s_outl, s_sc);
+  s2 = wave_sum(s2);
+  return s2 > 0.0 ? inv_mx / sqrt(s2) : 1.0;
 }
 
-__global__ __launch_bounds__(64) void tri_inviter_b_kernel(int n, int ncols, const int* __restrict__ clen,
+// z *= sc, in batches of 8 entries per lane (loads first, so their latencies overlap)
+__device__ void inv_scale(double* __restrict__ z, int64_t zs, int n, double sc) {
+  const int lane = threadIdx.x;
+  for (int k0 = lane; k0 < n; k0 += 64 * 8) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = k0 + 64 * u;
+      v[u] = k < n ? z[int64_t(k) * zs] : 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = k0 + 64 * u;
+      if (k < n) z[int64_t(k) * zs] = v[u] * sc;
+    }
+  }
+}
+
+// first solve's back-substitution, one wave per vector; its squared norm to nrm[j]
+__global__ __launch_bounds__(64) void tri_inviter_u_kernel(int n, int ncols, const int* __restrict__ flag,
+                                                           const double* __restrict__ Rt, double* __restrict__ Z,
+                                                           double* __restrict__ nrm) {
+  __shared__ double s_in[2][CHL][4];
+  __shared__ double s_z[2][CHL];
+  __shared__ double s_out[CHL];
+  __shared__ double s_sc[1];
+  if (*flag) return;
+  const int jv = blockIdx.x;
+  const double n1 = inv_usolve_lds(Rt + int64_t(jv) * 4, int64_t(ncols) * 4, Z + jv, ncols, n, s_in, s_z, s_out, s_sc);
+  if (threadIdx.x == 0) nrm[jv] = n1;
+}
+
+// one wave per cluster of two or more (final = 0) or per cluster of any size (final = 1):
+// members in order, orthogonalise against the cluster's earlier members (modified
+// Gram-Schmidt, those already normalised) and normalise.  A lone vector is only
+// normalised, with the squared norm its solve recorded.
+__global__ __launch_bounds__(64) void tri_inviter_o_kernel(int n, int ncols, int final, const int* __restrict__ clen,
+                                                           const int* __restrict__ flag, double* __restrict__ Z,
+                                                           const double* __restrict__ nrm) {
+  if (*flag) return;
+  const int j = blockIdx.x;
+  const int len = clen[j];
+  if (len == 0 || (len == 1 && !final)) return;
+  const int lane = threadIdx.x;
+  for (int q = 0; q < len; ++q) {
+    const int jv = j + q;
+    double* z = Z + jv;
+    double s2 = nrm[jv];
+    if (q > 0) {
+      for (int p = j; p < jv; ++p) {
+        const double* zp = Z + p;
+        double dot = 0.0;
+#pragma unroll 8
+        for (int k = lane; k < n; k += 64) dot += zp[int64_t(k) * ncols] * z[int64_t(k) * ncols];
+        dot = wave_sum(dot);
+        for (int k = lane; k < n; k += 64) z[int64_t(k) * ncols] -= dot * zp[int64_t(k) * ncols];
+      }
+      s2 = 0.0;
+#pragma unroll 8
+      for (int k = lane; k < n; k += 64) s2 += z[int64_t(k) * ncols] * z[int64_t(k) * ncols];
+      s2 = wave_sum(s2);
+    }
+    inv_scale(z, ncols, n, inv_unit_scale(z, ncols, n, s2));
+    __syncthreads();   // the normalised member is read by the next members' passes
+  }
+}
+
+// second solve, one wave per vector: y = L^-1 P (sc z), then U^-1 y; its squared norm to
+// nrm[j].  A lone vector's iterate is normalised on the fly (sc from its recorded norm);
+// cluster members were normalised by the cluster kernel (sc = 1).
+__global__ __launch_bounds__(64) void tri_inviter_s_kernel(int n, int ncols, const int* __restrict__ clen,
                                                            const int* __restrict__ flag,
-                                                           const double* __restrict__ Rall,
-                                                           const uint8_t* __restrict__ Pall,
-                                                           double* __restrict__ Zw) {
+                                                           const double* __restrict__ Rt,
+                                                           const uint8_t* __restrict__ PVt,
+                                                           double* __restrict__ Z, double* __restrict__ nrm) {
   __shared__ double s_in[2][CHL][4];
   __shared__ double s_z[2][CHL];
   __shared__ double s_out[CHL];
   __shared__ uint8_t s_piv[2][CHL];
   __shared__ double s_zx[2];
   __shared__ double s_sc[1];
-  const int j = blockIdx.x;
   if (*flag) return;
-  const int len = clen[j];
-  if (len == 0) return;
+  const int jv = blockIdx.x;
   const int lane = threadIdx.x;
-  // orthogonalise iterate jv against the finished vectors j .. jv-1; returns ||z||^2
-  auto orth = [&](int jv) {
-    double* z = Zw + int64_t(jv) * n;
-    for (int p = j; p < jv; ++p) {
-      const double* zp = Zw + int64_t(p) * n;
-      double dot = 0.0;
-      for (int k = lane; k < n; k += 64) dot += zp[k] * z[k];
-      dot = wave_sum(dot);
-      for (int k = lane; k < n; k += 64) z[k] -= dot * zp[k];
-    }
-    double s2 = 0.0;
-    for (int k = lane; k < n; k += 64) s2 += z[k] * z[k];
-    return wave_sum(s2);
-  };
-  // 1 / ||z||, or for a badly scaled z 1 / ||z|| taken after scaling by its largest entry
-  auto unit_scale = [&](int jv, double nrm2) {
-    if (nrm2 > 0.0 && nrm2 < 1e300) return 1.0 / sqrt(nrm2);
-    const double* z = Zw + int64_t(jv) * n;
-    double mx = 0.0;
-    for (int k = lane; k < n; k += 64) mx = fmax(mx, fabs(z[k]));
-    mx = wave_max(mx);
-    const double inv_mx = mx > 0.0 && mx < 1e308 ? 1.0 / mx : 1.0;
-    double s2 = 0.0;
-    for (int k = lane; k < n; k += 64) {
-      const double v = z[k] * inv_mx;
-      s2 += v * v;
-    }
-    s2 = wave_sum(s2);
-    return s2 > 0.0 ? inv_mx / sqrt(s2) : 1.0;
-  };
   const int nm1 = n - 1;
   const int nch = (n + CHL - 1) / CHL;
-  for (int q = 0; q < len; ++q) {
-    const int jv = j + q;
-    const double* R = Rall + int64_t(jv) * n * 4;
-    const uint8_t* PV = Pall + int64_t(jv) * n;
-    double* z = Zw + int64_t(jv) * n;
-    const double sc = unit_scale(jv, orth(jv));
+  const double* R = Rt + int64_t(jv) * 4;   // record k at R + k * rs
+  const int64_t rs = int64_t(ncols) * 4;
+  const uint8_t* PV = PVt + jv;               // flag k at PV + k * ncols
+  double* z = Z + jv;                         // entry k at z + k * ncols
+  const bool lone = clen[jv] == 1;
+  const double sc = lone ? inv_unit_scale(z, ncols, n, nrm[jv]) : 1.0;
+  // ---- y = L^-1 P (sc z): chunk c stages z[c CHL .. c CHL + CHL] (one past, for the
+  //      interchange), the multipliers and the flags
+  double gz[CPLL], gl[CPLL], gx = 0.0;
+  uint8_t gp[CPLL];
+  auto load = [&](int c) {
+#pragma unroll
+    for (int u = 0; u < CPLL; ++u) {
+      const int k = min(c * CHL + lane + 64 * u, n - 1);
+      gz[u] = z[int64_t(k) * ncols] * sc;
+      gl[u] = R[int64_t(k) * rs + 3];
+      gp[u] = PV[int64_t(k) * ncols];
+    }
+    gx = z[int64_t(min(c * CHL + CHL, n - 1)) * ncols] * sc;
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < CPLL; ++u) {
+      const int i = lane + 64 * u;
+      s_z[buf][i] = gz[u];
+      s_in[buf][i][3] = gl[u];
+      s_piv[buf][i] = gp[u];
+    }
+    if (lane == 0) s_zx[buf] = gx;
+  };
+  load(0);
+  stage(0);
+  double ycur = z[0] * sc;
+  for (int c = 0; c < nch; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nch) load(c + 1);
     __syncthreads();
-    // ---- y = L^-1 P (sc z): chunk c stages z[c CHL .. c CHL + CHL] (one past, for the
-    //      interchange), the multipliers and the flags
-    double gz[CPLL], gl[CPLL], gx = 0.0;
-    uint8_t gp[CPLL];
-    auto load = [&](int c) {
-#pragma unroll
-      for (int u = 0; u < CPLL; ++u) {
-        const int k = min(c * CHL + lane + 64 * u, n - 1);
-        gz[u] = z[k] * sc;
-        gl[u] = R[int64_t(k) * 4 + 3];
-        gp[u] = PV[k];
+    const int cnt = min(CHL, nm1 - c * CHL);   // elimination steps in this chunk
+    if (lane == 0) {
+      #pragma unroll 8
+      for (int i = 0; i < cnt; ++i) {
+        const double yn = i + 1 < CHL ? s_z[buf][i + 1] : s_zx[buf];
+        const bool sw = s_piv[buf][i];
+        const double yk = sw ? yn : ycur;
+        const double ynext = sw ? ycur : yn;
+        s_out[i] = yk;
+        ycur = fma(-s_in[buf][i][3], yk, ynext);
       }
-      gx = z[min(c * CHL + CHL, n - 1)] * sc;
-    };
-    auto stage = [&](int buf) {
-#pragma unroll
-      for (int u = 0; u < CPLL; ++u) {
-        const int i = lane + 64 * u;
-        s_z[buf][i] = gz[u];
-        s_in[buf][i][3] = gl[u];
-        s_piv[buf][i] = gp[u];
-      }
-      if (lane == 0) s_zx[buf] = gx;
-    };
-    load(0);
-    stage(0);
-    double ycur = z[0] * sc;
-    for (int c = 0; c < nch; ++c) {
-      const int buf = c & 1;
-      if (c + 1 < nch) load(c + 1);
-      __syncthreads();
-      const int cnt = min(CHL, nm1 - c * CHL);   // elimination steps in this chunk
-      if (lane == 0) {
-        #pragma unroll 8
-        for (int i = 0; i < cnt; ++i) {
-          double ynext = i + 1 < CHL ? s_z[buf][i + 1] : s_zx[buf];
-          double yk = ycur;
-          if (s_piv[buf][i]) {
-            yk = ynext;
-            ynext = ycur;
-          }
-          s_out[i] = yk;
-          ycur = ynext - s_in[buf][i][3] * yk;
-        }
-        if (c == nch - 1) s_out[max(cnt, 0)] = ycur;   // the last element
-      }
-      __syncthreads();
-      const int nw = min(CHL, n - c * CHL);   // elements written by this chunk
-#pragma unroll
-      for (int u = 0; u < CPLL; ++u) {
-        const int i = lane + 64 * u;
-        if (i < nw) z[c * CHL + i] = s_out[i];
-      }
-      if (c + 1 < nch) stage(buf ^ 1);
+      if (c == nch - 1) s_out[max(cnt, 0)] = ycur;   // the last element
     }
     __syncthreads();
-    inv_usolve_lds(R, z, n, s_in, s_z, s_out, s_sc);
-    const double sc2 = unit_scale(jv, orth(jv));
-    for (int k = lane; k < n; k += 64) z[k] *= sc2;
-    __syncthreads();
-  }
-}
-
-// Z (n x ncols) = Zw^T (Zw: ncols x n)
-__global__ __launch_bounds__(256) void inv_transpose_kernel(const double* __restrict__ Zw, int n, int ncols,
-                                                            double* __restrict__ Z) {
-  __shared__ double t[64][65];
-  const int k0 = blockIdx.x * 64, j0 = blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int jv = j0 + i, k = k0 + tx;
-    t[i][tx] = (jv < ncols && k < n) ? Zw[int64_t(jv) * n + k] : 0.0;
+    const int nw = min(CHL, n - c * CHL);   // elements written by this chunk
+#pragma unroll
+    for (int u = 0; u < CPLL; ++u) {
+      const int i = lane + 64 * u;
+      if (i < nw) z[int64_t(c * CHL + i) * ncols] = s_out[i];
+    }
+    if (c + 1 < nch) stage(buf ^ 1);
   }
   __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int k = k0 + i, jv = j0 + tx;
-    if (k < n && jv < ncols) Z[int64_t(k) * ncols + jv] = t[tx][i];
-  }
+  const double n2 = inv_usolve_lds(R, rs, z, ncols, n, s_in, s_z, s_out, s_sc);
+  if (lane == 0) nrm[jv] = n2;
 }
 
 // ---- 4. back-transformation.  Block g holds reflectors g*BW .. g*BW+BW-1; reflector t
@@ -1592,7 +1619,7 @@ __global__ __launch_bounds__(256) void tri_out_kernel(const double* __restrict__
 }
 
 struct TWs {
-  double *P, *S, *SV, *SW, *npart, *x0, *xv, *d, *e, *tau, *Wp, *lam, *bounds, *U, *Z, *Zw, *Gp, *T, *Yp, *Yr, *Y2;
+  double *P, *S, *SV, *SW, *npart, *x0, *xv, *d, *e, *tau, *Wp, *lam, *bounds, *U, *Z, *nrm, *Gp, *T, *Yp, *Yr, *Y2;
   int *clen, *flag;
   uint8_t* piv;
 };
@@ -1620,12 +1647,12 @@ TWs carve_tri(Carve& cv, int64_t n, int64_t ncols) {
   w.U = cv.take<double>(size_t(4 * n * ncols));
   w.piv = cv.take<uint8_t>(size_t(n * ncols));
   w.Z = cv.take<double>(size_t(n * ncols));
-  w.Zw = cv.take<double>(size_t(n * ncols));
   w.Gp = cv.take<double>(size_t(ngroups * ngc * BW * BW));
   w.T = cv.take<double>(size_t(ngroups * BW * BW));
   w.Yp = cv.take<double>(size_t(nbc * BW * ncols));
   w.Yr = cv.take<double>(size_t(BW * ncols));
   w.Y2 = cv.take<double>(size_t(BW * ncols));
+  w.nrm = cv.take<double>(size_t(ncols));
   w.clen = cv.take<int>(size_t(ncols));
   w.flag = cv.take<int>(1);
   return w;
@@ -1745,14 +1772,20 @@ lrc_status tridiag_eig(hipStream_t st, double* A, int64_t k, int64_t lda, int64_
     return LRC_OK;
   }
   {
-    ProfScope scope("tri_inviter_kernel", st, 0.0, 0.0);
-    tri_inviter_a_kernel<<<unsigned(ncols), 64, 0, st>>>(w.d, w.e, n, w.lam, ncols, w.bounds, w.clen, w.flag, w.U,
-                                                         w.piv, w.Zw);
+    ProfScope scope("tri_inviter_a_kernel", st, 0.0, 0.0);
+    tri_inviter_a_kernel<<<unsigned(cdiv(ncols, 64)), 64, 0, st>>>(w.d, w.e, n, w.lam, ncols, w.bounds, w.clen,
+                                                                    w.flag, w.U, w.piv, w.Z);
     LRC_LAUNCHED();
-    tri_inviter_b_kernel<<<unsigned(ncols), 64, 0, st>>>(n, ncols, w.clen, w.flag, w.U, w.piv, w.Zw);
+  }
+  {
+    ProfScope scope("tri_inviter_b_kernel", st, 0.0, 0.0);
+    tri_inviter_u_kernel<<<unsigned(ncols), 64, 0, st>>>(n, ncols, w.flag, w.U, w.Z, w.nrm);
     LRC_LAUNCHED();
-    inv_transpose_kernel<<<dim3(unsigned(cdiv(n, 64)), unsigned(cdiv(ncols, 64))), 256, 0, st>>>(w.Zw, n, ncols,
-                                                                                                 w.Z);
+    tri_inviter_o_kernel<<<unsigned(ncols), 64, 0, st>>>(n, ncols, 0, w.clen, w.flag, w.Z, w.nrm);
+    LRC_LAUNCHED();
+    tri_inviter_s_kernel<<<unsigned(ncols), 64, 0, st>>>(n, ncols, w.clen, w.flag, w.U, w.piv, w.Z, w.nrm);
+    LRC_LAUNCHED();
+    tri_inviter_o_kernel<<<unsigned(ncols), 64, 0, st>>>(n, ncols, 1, w.clen, w.flag, w.Z, w.nrm);
     LRC_LAUNCHED();
   }
 
