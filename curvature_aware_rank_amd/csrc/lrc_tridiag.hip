@@ -40,7 +40,7 @@ constexpr int NB = 32;          // tridiagonalisation panel width
 constexpr int TS = 64;          // tile and row-block size of the symv / w kernels
 constexpr int BW = 128;         // reflectors per back-transformation block
 constexpr int BT_CHUNK = 128;   // rows per partial of V^T Z
-constexpr int G_CHUNK = 1024;   // rows per partial of V^T V
+constexpr int G_CHUNK = 256;    // rows per partial of V^T V
 constexpr int WR = 32;          // rows per workgroup of the w kernel (16 or 32; 16 measured no faster)
 constexpr int WPB = TS / WR;    // w workgroups per 64-row block
 constexpr int NPB = 4 * WPB;    // squared-norm partials per 64-row block (one per w wave)
@@ -1165,16 +1165,28 @@ __global__ __launch_bounds__(64) void tri_inviter_u_kernel(int n, int ncols, con
 
 // one wave per cluster of two or more (final = 0) or per cluster of any size (final = 1):
 // members in order, orthogonalise against the cluster's earlier members (modified
-// Gram-Schmidt, those already normalised) and normalise.  A lone vector is only
-// normalised, with the squared norm its solve recorded.
+// Gram-Schmidt, those already normalised) and normalise (scl = 1).  A lone vector's final
+// normalisation is left to the output kernel: scl = 1 / ||z|| from the squared norm its
+// solve recorded (scaling commutes with the back-transformation); only a norm outside
+// [1e-100, 1e100] is applied here.
 __global__ __launch_bounds__(64) void tri_inviter_o_kernel(int n, int ncols, int final, const int* __restrict__ clen,
                                                            const int* __restrict__ flag, double* __restrict__ Z,
-                                                           const double* __restrict__ nrm) {
+                                                           const double* __restrict__ nrm, double* __restrict__ scl) {
   if (*flag) return;
   const int j = blockIdx.x;
   const int len = clen[j];
   if (len == 0 || (len == 1 && !final)) return;
   const int lane = threadIdx.x;
+  if (len == 1) {
+    const double s2 = nrm[j];
+    double sv = 1.0;
+    if (s2 > 1e-200 && s2 < 1e200)
+      sv = 1.0 / sqrt(s2);
+    else
+      inv_scale(Z + j, ncols, n, inv_unit_scale(Z + j, ncols, n, s2));
+    if (lane == 0) scl[j] = sv;
+    return;
+  }
   for (int q = 0; q < len; ++q) {
     const int jv = j + q;
     double* z = Z + jv;
@@ -1194,6 +1206,7 @@ __global__ __launch_bounds__(64) void tri_inviter_o_kernel(int n, int ncols, int
       s2 = wave_sum(s2);
     }
     inv_scale(z, ncols, n, inv_unit_scale(z, ncols, n, s2));
+    if (lane == 0 && final) scl[jv] = 1.0;
     __syncthreads();   // the normalised member is read by the next members' passes
   }
 }
@@ -1329,19 +1342,30 @@ __global__ __launch_bounds__(256) void bt_gram_kernel(const double* __restrict__
     for (int q = 0; q < 8; ++q) out[(ty * 8 + a) * BW + tx * 8 + q] = acc[a][q];
 }
 
+// the row-chunk partials of each group's V^T V summed in chunk order into its first partial
+__global__ __launch_bounds__(256) void bt_gsum_kernel(double* __restrict__ Gp, int ngc) {
+  const int g = blockIdx.y;
+  const int q = blockIdx.x * 256 + threadIdx.x;   // < BW * BW
+  double* base = Gp + int64_t(g) * ngc * BW * BW + q;
+  double s = 0.0;
+  for (int ch = 0; ch < ngc; ++ch) s += base[int64_t(ch) * BW * BW];
+  base[0] = s;
+}
+
 // T of block g (upper triangular): T[j][j] = tau_j, T[0:j, j] = -tau_j T[0:j,0:j] G[0:j, j];
 // thread i owns row i of T, kept in LDS.  G = V^T V is symmetric, so its column j is
 // row j (one coalesced load per column, the next column's load in flight).
-__global__ __launch_bounds__(BW) void bt_t_kernel(const double* __restrict__ Gp, int ngc, int nref,
+__global__ __launch_bounds__(BW) void bt_t_kernel(const double* __restrict__ Gp, int ngc, int nsum, int nref,
                                                   const double* __restrict__ tau, double* __restrict__ Tm) {
   __shared__ double Ts[BW][BW + 1];
   __shared__ double gcol[2][BW];
   const int tid = threadIdx.x;
   const int g = blockIdx.x, g0 = g * BW;
-  // column j of G (entries 0..j-1 used), summed over the row chunks in chunk order
+  // column j of G (entries 0..j-1 used), summed over the first nsum row-chunk partials in
+  // chunk order (ngc partials per group in the layout)
   auto load_col = [&](int j) {
     double s = 0.0;
-    for (int ch = 0; ch < ngc; ++ch) s += Gp[(int64_t(g) * ngc + ch) * BW * BW + int64_t(j) * BW + tid];
+    for (int ch = 0; ch < nsum; ++ch) s += Gp[(int64_t(g) * ngc + ch) * BW * BW + int64_t(j) * BW + tid];
     return s;
   };
   const int i = tid;
@@ -1586,8 +1610,8 @@ __global__ void tri_sigma_kernel(const double* __restrict__ lam, int n, float* _
   if (m < n) sigma[m] = float(sqrt(fmax(lam[n - 1 - m], 0.0)));
 }
 
-__global__ __launch_bounds__(256) void tri_out_kernel(const double* __restrict__ Z, int n, int ncols,
-                                                      float* __restrict__ Qt) {
+__global__ __launch_bounds__(256) void tri_out_kernel(const double* __restrict__ Z, const double* __restrict__ scl,
+                                                      int n, int ncols, float* __restrict__ Qt) {
   __shared__ double bv[256];
   __shared__ int bi[256];
   const int j = blockIdx.x, tid = threadIdx.x;
@@ -1614,12 +1638,13 @@ __global__ __launch_bounds__(256) void tri_out_kernel(const double* __restrict__
     }
     __syncthreads();
   }
-  const double sgn = Z[int64_t(bi[0]) * ncols + j] < 0.0 ? -1.0 : 1.0;
+  // the vector's pending normalisation (positive: the sign choice is unaffected)
+  const double sgn = (Z[int64_t(bi[0]) * ncols + j] < 0.0 ? -1.0 : 1.0) * scl[j];
   for (int k = tid; k < n; k += 256) Qt[int64_t(j) * n + k] = float(sgn * Z[int64_t(k) * ncols + j]);
 }
 
 struct TWs {
-  double *P, *S, *SV, *SW, *npart, *x0, *xv, *d, *e, *tau, *Wp, *lam, *bounds, *U, *Z, *nrm, *Gp, *T, *Yp, *Yr, *Y2;
+  double *P, *S, *SV, *SW, *npart, *x0, *xv, *d, *e, *tau, *Wp, *lam, *bounds, *U, *Z, *nrm, *scl, *Gp, *T, *Yp, *Yr, *Y2;
   int *clen, *flag;
   uint8_t* piv;
 };
@@ -1653,6 +1678,7 @@ TWs carve_tri(Carve& cv, int64_t n, int64_t ncols) {
   w.Yr = cv.take<double>(size_t(BW * ncols));
   w.Y2 = cv.take<double>(size_t(BW * ncols));
   w.nrm = cv.take<double>(size_t(ncols));
+  w.scl = cv.take<double>(size_t(ncols));
   w.clen = cv.take<int>(size_t(ncols));
   w.flag = cv.take<int>(1);
   return w;
@@ -1781,11 +1807,11 @@ lrc_status tridiag_eig(hipStream_t st, double* A, int64_t k, int64_t lda, int64_
     ProfScope scope("tri_inviter_b_kernel", st, 0.0, 0.0);
     tri_inviter_u_kernel<<<unsigned(ncols), 64, 0, st>>>(n, ncols, w.flag, w.U, w.Z, w.nrm);
     LRC_LAUNCHED();
-    tri_inviter_o_kernel<<<unsigned(ncols), 64, 0, st>>>(n, ncols, 0, w.clen, w.flag, w.Z, w.nrm);
+    tri_inviter_o_kernel<<<unsigned(ncols), 64, 0, st>>>(n, ncols, 0, w.clen, w.flag, w.Z, w.nrm, w.scl);
     LRC_LAUNCHED();
     tri_inviter_s_kernel<<<unsigned(ncols), 64, 0, st>>>(n, ncols, w.clen, w.flag, w.U, w.piv, w.Z, w.nrm);
     LRC_LAUNCHED();
-    tri_inviter_o_kernel<<<unsigned(ncols), 64, 0, st>>>(n, ncols, 1, w.clen, w.flag, w.Z, w.nrm);
+    tri_inviter_o_kernel<<<unsigned(ncols), 64, 0, st>>>(n, ncols, 1, w.clen, w.flag, w.Z, w.nrm, w.scl);
     LRC_LAUNCHED();
   }
 
@@ -1796,7 +1822,9 @@ lrc_status tridiag_eig(hipStream_t st, double* A, int64_t k, int64_t lda, int64_
     const int ngc = int(cdiv(n, G_CHUNK));
     bt_gram_kernel<<<dim3(unsigned(ngroups), unsigned(ngc)), 256, 0, st>>>(A, lda, n, nref, ngc, w.Gp);
     LRC_LAUNCHED();
-    bt_t_kernel<<<unsigned(ngroups), BW, 0, st>>>(w.Gp, ngc, nref, w.tau, w.T);
+    bt_gsum_kernel<<<dim3(unsigned(BW * BW / 256), unsigned(ngroups)), 256, 0, st>>>(w.Gp, ngc);
+    LRC_LAUNCHED();
+    bt_t_kernel<<<unsigned(ngroups), BW, 0, st>>>(w.Gp, ngc, 1, nref, w.tau, w.T);
     LRC_LAUNCHED();
     const unsigned ctiles = unsigned(cdiv(ncols, 64));
     for (int g = ngroups - 1; g >= 0; --g) {
@@ -1821,7 +1849,7 @@ lrc_status tridiag_eig(hipStream_t st, double* A, int64_t k, int64_t lda, int64_
       }
     }
   }
-  tri_out_kernel<<<unsigned(ncols), 256, 0, st>>>(w.Z, n, ncols, Qt);
+  tri_out_kernel<<<unsigned(ncols), 256, 0, st>>>(w.Z, w.scl, n, ncols, Qt);
   LRC_LAUNCHED();
   return LRC_OK;
 }
