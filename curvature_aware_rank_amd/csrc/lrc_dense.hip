@@ -291,9 +291,11 @@ constexpr int NB = 64;  // Cholesky / triangular-solve block size
 // unblocked factorisation of the diagonal block at k0 (one workgroup)
 // Unblocked Cholesky of one diagonal block (b <= 64), a single wave: lane i keeps row i
 // in registers; per column j the pivot comes from lane j, the scaled column goes through
-// LDS to every lane, and each lane updates its own row.
+// LDS to every lane (one store per lane, then broadcast reads that the wave's in-order
+// LDS queue serves after the store), and each lane updates its own row.
 __global__ __launch_bounds__(64) void potf2_kernel(float* __restrict__ L, int64_t ldl, int64_t n, int64_t k0,
                                                    int* __restrict__ info) {
+  __shared__ float colv[NB];
   const int lane = threadIdx.x;
   const int b = int(min<int64_t>(NB, n - k0));
   if (*info != 0) return;
@@ -305,8 +307,6 @@ __global__ __launch_bounds__(64) void potf2_kernel(float* __restrict__ L, int64_
   for (int c = 0; c < NB; ++c) a[c] = (c <= lane && lane < b && c < b) ? a[c] : 0.f;
   int fail = 0;   // uniform: the pivot is read from lane j into a scalar register
   // fully unrolled (static register indices); finished or failed columns are skipped.
-  // Column j's multipliers l_c (lane c's a[j]) reach the other lanes by readlane, so no
-  // LDS round trip or barrier separates consecutive columns.
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     if (j < b && fail == 0) {
@@ -314,18 +314,18 @@ __global__ __launch_bounds__(64) void potf2_kernel(float* __restrict__ L, int64_
       if (!(piv > 0.f) || !isfinite(piv)) {
         fail = j + 1;
       } else {
+        // correctly rounded square root and reciprocal: the smallest singular values of
+        // an ill-conditioned whitening are sensitive to the last bits of these pivots
         const float djj = sqrtf(piv);
         const float inv = 1.0f / djj;
         a[j] = lane == j ? djj : (lane > j ? a[j] * inv : a[j]);
         const float lij = a[j];
+        colv[lane] = lij;
         // every lane updates its whole row: entries above the diagonal (c > lane) are never
         // read as pivots or multipliers (those come from lanes c > j, column j) and stay
         // finite; the store writes zeros there
 #pragma unroll
-        for (int c = j + 1; c < NB; ++c) {
-          const float lc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[j]), c));
-          a[c] = fmaf(-lij, lc, a[c]);
-        }
+        for (int c = j + 1; c < NB; ++c) a[c] = fmaf(-lij, colv[c], a[c]);
       }
     }
   }
