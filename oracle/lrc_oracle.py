@@ -8,7 +8,8 @@ fast: numpy/scipy (LAPACK) in fp64, one step per function, in the pages' order.
 Pages (gist.science explainers; the alternative scorers at the end also cite UniRank
 2.1 "Local Structural Significance" / "Global Functional Importance" and Swift-SVD
 section B "Dynamic Rank Allocation Strategy", item "Hybrid Scoring"; the factor codec
-cites LASER section 3 "Hybrid SVD-Quantization for FFNs", item "Quantization", and the
+cites LASER section 3 "Hybrid SVD-Quantization for FFNs", item "Quantization", the FFN
+channel selection its items "Channel selection" and "Hybrid architecture", and the
 low-rank FFN forward cites LASER section 4 "System Implementation"):
   * LASER: Loss-Aware Singular-value Decomposition and Rank Allocation for Efficient
     Low-Precision Vision-Language Models (technical summary, Methodology 1 "loss-aware
@@ -41,7 +42,7 @@ __all__ = [
     "truncated_svd", "canonical_signs", "back_map", "whiten_decompose",
     "fisher_scores", "kfac_scores", "allocation_keys", "allocate", "kfac_loss",
     "unirank_scores", "swift_layer_scores", "hadamard_rotation", "rotate_factors", "rtn_rows",
-    "silu", "lowrank_ffn",
+    "silu", "lowrank_ffn", "ffn_channel_errors", "select_channels",
 ]
 
 
@@ -389,3 +390,40 @@ def lowrank_ffn(x, gate, up, down):
     h = silu(apply(gate, xv)) * apply(up, xv)
     return apply(down, h)
 
+
+# ---------------------------------------------------------------------------
+# FFN hybrid channel selection (LASER, 3. Hybrid SVD-Quantization for FFNs, items
+# "Channel selection" and "Hybrid architecture")
+# ---------------------------------------------------------------------------
+def ffn_channel_errors(w_gate, w_up, gate_factors, up_factors, xsum, n_x, damping=0.0):
+    """Reconstruction error of every hidden channel under the temporary low-rank form of
+    the gate and up projections.  The pages call the channels with a low reconstruction
+    error "SVD-friendly"; the reading here measures a channel's error the way the
+    method measures loss, in the activation-weighted space: the expected squared error
+    of the channel's two pre-activations under the calibration distribution,
+        err[h] = sum over P in (gate, up) of dW_P[h] X dW_P[h]^T,  dW_P = W_P - Left_P Right_P,
+    with X = Xsum / n_x + damping I (the covariance the decompositions used).
+    w_gate, w_up: d_ff x d; *_factors: (Left d_ff x r, Right r x d) or None (r = 0).
+    Returns err (d_ff,) in fp64."""
+    x = np.asarray(xsum, dtype=np.float64)
+    x = np.tril(x) + np.tril(x, -1).T
+    x = x / float(n_x) + damping * np.eye(x.shape[0])
+    err = 0.0
+    for w, fac in ((w_gate, gate_factors), (w_up, up_factors)):
+        dw = np.asarray(w, dtype=np.float64)
+        if fac is not None:
+            dw = dw - np.asarray(fac[0], dtype=np.float64) @ np.asarray(fac[1], dtype=np.float64)
+        err = err + np.einsum("hi,ij,hj->h", dw, x, dw)
+    return err
+
+
+def select_channels(err, n_lowrank):
+    """The n_lowrank channels with the smallest error take the low-rank branch, the rest
+    stay dense (the pages: the SVD-friendly channels are compressed).  Ties go to the
+    lower channel index.  Returns (order: channels by ascending error, lowrank: 0/1 mask)."""
+    err = [float(v) for v in err]
+    order = sorted(range(len(err)), key=lambda h: (err[h], h))
+    lowrank = np.zeros(len(err), dtype=np.uint8)
+    for h in order[:n_lowrank]:
+        lowrank[h] = 1
+    return np.array(order, dtype=np.int64), lowrank

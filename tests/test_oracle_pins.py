@@ -435,3 +435,74 @@ def test_lowrank_ffn_equals_the_dense_ffn_of_the_product():
 def test_silu_values():
     np.testing.assert_allclose(oracle.silu([0.0, 1.0, -1.0, 30.0]),
                                [0.0, 0.7310585786300049, -0.2689414213699951, 30.0], rtol=1e-12)
+
+
+# --------------------------------------------------------------------------- FFN channel selection
+@pytest.mark.parametrize("d_ff,d,r", [(7, 4, 2), (9, 5, 0), (6, 6, 3)])
+def test_ffn_channel_error_is_the_mean_squared_preactivation_error(d_ff, d, r):
+    """LASER 3, item Channel selection: a hidden channel's reconstruction error (reading:
+    the expected squared error of its gate and up pre-activations over the calibration
+    tokens) equals, token by token, the mean of (dW_gate a_t)_h^2 + (dW_up a_t)_h^2."""
+    n = 200
+    a = _spd_stream(n, d, 1.0, RNG)
+    wg, wu = RNG.standard_normal((d_ff, d)), RNG.standard_normal((d_ff, d))
+    xs = oracle.covariance_sum(a)
+    fg = fu = None
+    if r:
+        rg = oracle.whiten_decompose(wg, xs, n, rank=r)
+        ru = oracle.whiten_decompose(wu, xs, n, rank=r)
+        fg, fu = (rg["left"], rg["right"]), (ru["left"], ru["right"])
+    err = oracle.ffn_channel_errors(wg, wu, fg, fu, xs, n)
+    dg = wg - (fg[0] @ fg[1] if r else 0.0)
+    du = wu - (fu[0] @ fu[1] if r else 0.0)
+    brute = np.zeros(d_ff)
+    for t in range(n):
+        brute += (dg @ a[t]) ** 2 + (du @ a[t]) ** 2
+    np.testing.assert_allclose(err, brute / n, rtol=1e-10)
+    # damping adds damping * ||dW[h]||^2 per projection
+    errd = oracle.ffn_channel_errors(wg, wu, fg, fu, xs, n, damping=0.25)
+    np.testing.assert_allclose(errd, err + 0.25 * (np.sum(dg ** 2, axis=1) + np.sum(du ** 2, axis=1)),
+                               rtol=1e-10)
+
+
+def test_ffn_channel_errors_sum_to_the_discarded_whitened_energy():
+    """Summed over the channels, one projection's errors are its whitened truncation
+    error (Eckart-Young in the whitened space): sum of the discarded sigma_tilde^2; at
+    full rank every error vanishes."""
+    n, d_ff, d, r = 300, 12, 8, 3
+    a = _spd_stream(n, d, 1.2, RNG)
+    xs = oracle.covariance_sum(a)
+    wg, wu = RNG.standard_normal((d_ff, d)), RNG.standard_normal((d_ff, d))
+    rg = oracle.whiten_decompose(wg, xs, n, rank=r)
+    ru = oracle.whiten_decompose(wu, xs, n, rank=r)
+    zero = np.zeros_like(wu)
+    eg = oracle.ffn_channel_errors(wg, zero, (rg["left"], rg["right"]), None, xs, n)
+    eu = oracle.ffn_channel_errors(zero, wu, None, (ru["left"], ru["right"]), xs, n)
+    np.testing.assert_allclose(eg.sum(), np.sum(rg["sigma"][r:] ** 2), rtol=1e-10)
+    np.testing.assert_allclose(eu.sum(), np.sum(ru["sigma"][r:] ** 2), rtol=1e-10)
+    both = oracle.ffn_channel_errors(wg, wu, (rg["left"], rg["right"]), (ru["left"], ru["right"]), xs, n)
+    np.testing.assert_allclose(both, eg + eu, rtol=1e-12)
+    full_g = oracle.whiten_decompose(wg, xs, n, rank=d)
+    full_u = oracle.whiten_decompose(wu, xs, n, rank=d)
+    e0 = oracle.ffn_channel_errors(wg, wu, (full_g["left"], full_g["right"]), (full_u["left"], full_u["right"]), xs, n)
+    assert np.max(np.abs(e0)) <= 1e-20 * np.max(oracle.ffn_channel_errors(wg, wu, None, None, xs, n))
+
+
+def test_select_channels_rule():
+    """The n smallest errors take the low-rank branch; equal errors go by channel index.
+    Hand-derived: errors (0.5, 0.25, 0.5, 0, 0.25) order as 3, 1, 4, 0, 2."""
+    order, low = oracle.select_channels([0.5, 0.25, 0.5, 0.0, 0.25], 3)
+    assert order.tolist() == [3, 1, 4, 0, 2]
+    assert low.tolist() == [0, 1, 0, 1, 1]
+    order, low = oracle.select_channels([0.5, 0.25, 0.5, 0.0, 0.25], 0)
+    assert low.sum() == 0
+    order, low = oracle.select_channels([0.5, 0.25, 0.5, 0.0, 0.25], 5)
+    assert low.sum() == 5
+    err = RNG.random(50)
+    err[10:20] = err[5]                          # ties
+    order, low = oracle.select_channels(err, 17)
+    assert sorted(order.tolist()) == list(range(50))
+    assert low.sum() == 17
+    assert np.max(err[low == 1]) <= np.min(err[low == 0])
+    keys = [(err[h], h) for h in order]
+    assert keys == sorted(keys)
