@@ -176,6 +176,25 @@ def secondary(lrc, torch, dev):
                                              "GB/s": round(fbytes / t / 1e9, 1),
                                              "hbm_frac": round(fbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
     del gate, up, down
+    # FFN hybrid channel selection: gate and up 11008 x 4096 at rank 2048 (the factors'
+    # values do not change the work), covariance of a 4096-wide stream
+    wg = torch.randn(dff, d, generator=g, device=dev) / d ** 0.5
+    wu = torch.randn(dff, d, generator=g, device=dev) / d ** 0.5
+    fg = (torch.randn(dff, rk, generator=g, device=dev) / rk ** 0.5, torch.randn(rk, d, generator=g, device=dev))
+    fu = (torch.randn(dff, rk, generator=g, device=dev) / rk ** 0.5, torch.randn(rk, d, generator=g, device=dev))
+    xa = synth.activation_stream(8192, d, 1.0, 44, dtype=torch.bfloat16, device=dev)
+    xsum = torch.zeros(d, d, device=dev)
+    lrc.lrc_accumulate_cov(xa, xsum)
+    del xa
+    lrc.lrc_ffn_select_channels(wg, wu, fg, fu, xsum, 8192, dff // 2, 1e-3)
+    t = _time(lambda: lrc.lrc_ffn_select_channels(wg, wu, fg, fu, xsum, 8192, dff // 2, 1e-3), torch, 3)
+    # per projection: D = W - Left Right (2 d_ff r d) and E = D L_x (d_ff d (d + 1)), plus
+    # the Cholesky of X (d^3 / 3)
+    flops = 2 * (2.0 * dff * rk * d + dff * d * (d + 1.0)) + d ** 3 / 3.0
+    out["ffn_channel_selection"] = {"workload": f"gate and up {dff}x{d}, rank {rk}, select {dff // 2} channels",
+                                    "ms": round(t * 1e3, 3), "TFLOP/s": round(flops / t / 1e12, 2),
+                                    "mfma_fp32_frac": round(flops / t / 1e12 / PEAK_TFLOPS["f32"], 4)}
+    del wg, wu, fg, fu, xsum
     for m_items, label in ((917504, "decoder stack: 224 matrices"), (64 * 1024 * 1024, "scaled pool")):
         n_mat = 224 if m_items == 917504 else 16384
         per = m_items // n_mat

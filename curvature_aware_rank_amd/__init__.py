@@ -19,7 +19,7 @@ __all__ = [
     "LRC_ENOCONV", "LRC_ENONFINITE", "LRC_F32", "LRC_BF16", "LRC_COV_QUANT_INT8_TOKEN",
     "LRC_SCORE_FISHER", "LRC_SCORE_KFAC", "LRC_RANKSCORE_UNIRANK", "LRC_RANKSCORE_SWIFT", "LrcError", "lib",
     "library_path", "lrc_accumulate_cov", "lrc_whiten_decompose", "lrc_score_components", "lrc_allocate_ranks",
-    "lrc_rank_scores", "lrc_rotate_quantize", "lrc_quantize_rows", "lrc_lowrank_ffn",
+    "lrc_rank_scores", "lrc_rotate_quantize", "lrc_quantize_rows", "lrc_lowrank_ffn", "lrc_ffn_select_channels",
     "lrc_status_string", "lrc_profile_start", "lrc_profile_stop", "lrc_profile_kernels",
 ]
 
@@ -54,6 +54,9 @@ _SIGS = {
     "lrc_lowrank_ffn": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i64,
                                _vp, _vp, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
     "lrc_lowrank_ffn_workspace": (_sz, [_i64, _i64, _i64, _i64, _i64]),
+    "lrc_ffn_select_channels": (_i32, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _i64,
+                                       ctypes.c_float, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "lrc_ffn_select_channels_workspace": (_sz, [_i64, _i64]),
     "lrc_status_string": (ctypes.c_char_p, [_i32]),
     "lrc_last_hip_error": (_i32, []),
     "lrc_profile_start": (_i32, []),
@@ -314,6 +317,52 @@ def lrc_quantize_rows(x: torch.Tensor):
     s = torch.empty(rows, dtype=torch.float32, device=x.device)
     _check(lib.lrc_quantize_rows(_ptr(x), rows, cols, cols, _ptr(q), _ptr(s), _stream()), "lrc_quantize_rows")
     return q, s
+
+
+def lrc_ffn_select_channels(w_gate: torch.Tensor, w_up: torch.Tensor, gate_factors, up_factors,
+                            Xsum: torch.Tensor, n_x: int, n_lowrank: int, damping: float = 0.0):
+    """Hidden-channel selection of an FFN's hybrid low-rank form.  w_gate, w_up: (d_ff, d)
+    fp32; gate_factors, up_factors: (left (d_ff, r), right (r, d)) fp32 from
+    lrc_whiten_decompose with the same Xsum (or None for r = 0); Xsum: (d, d) fp32 sum.
+
+    Returns (err fp64 (d_ff,), order int32 (d_ff,), lowrank uint8 (d_ff,), info int32 (1,))."""
+    for t, nm in ((w_gate, "w_gate"), (w_up, "w_up"), (Xsum, "Xsum")):
+        _dev(t, nm)
+        if t.dtype != torch.float32:
+            raise ValueError(f"{nm} must be fp32")
+    if w_gate.shape != w_up.shape or w_gate.dim() != 2:
+        raise ValueError("w_gate and w_up must both be (d_ff, d)")
+    d_ff, d = w_gate.shape
+    if tuple(Xsum.shape) != (d, d):
+        raise ValueError("Xsum must be (d, d)")
+    wg, wu = w_gate.contiguous(), w_up.contiguous()
+    r = 0
+    fac = []
+    if gate_factors is not None or up_factors is not None:
+        for pair, nm in ((gate_factors, "gate"), (up_factors, "up")):
+            if pair is None:
+                raise ValueError("give the factors of both gate and up, or of neither")
+            left, right = pair
+            _dev(left, f"{nm} left")
+            _dev(right, f"{nm} right")
+            if left.dtype != torch.float32 or right.dtype != torch.float32:
+                raise ValueError(f"{nm} factors must be fp32")
+            fac += [left.contiguous(), right.contiguous()]
+        r = fac[0].shape[1]
+        if any(tuple(f.shape) != shp for f, shp in zip(fac, [(d_ff, r), (r, d)] * 2)):
+            raise ValueError("factors must be left (d_ff, r) and right (r, d) for both")
+    dev = w_gate.device
+    err = torch.empty(d_ff, dtype=torch.float64, device=dev)
+    order = torch.empty(d_ff, dtype=torch.int32, device=dev)
+    lowrank = torch.empty(d_ff, dtype=torch.uint8, device=dev)
+    info = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = _workspace(lib.lrc_ffn_select_channels_workspace(d_ff, d), dev)
+    ptrs = [_ptr(f) for f in fac] if r > 0 else [None] * 4
+    _check(lib.lrc_ffn_select_channels(_ptr(wg), _ptr(wu), d_ff, d, d, ptrs[0], ptrs[1], ptrs[2], ptrs[3], r,
+                                       _ptr(Xsum), _rowmajor_ld(Xsum, "Xsum"), int(n_x), float(damping),
+                                       int(n_lowrank), _ptr(err), _ptr(order), _ptr(lowrank), _ptr(info), _ptr(ws),
+                                       ws.numel(), _stream()), "lrc_ffn_select_channels")
+    return err, order, lowrank, info
 
 
 def lrc_lowrank_ffn(x: torch.Tensor, gate, up, down):

@@ -236,6 +236,33 @@ lrc_status lrc_quantize_rows(const float* X, int64_t rows, int64_t cols, int64_t
                              void* stream);
 
 /*
+ * lrc_ffn_select_channels -- which hidden channels of an FFN take the low-rank branch.
+ * LASER section 3 (Hybrid SVD-Quantization for FFNs), items Channel selection and Hybrid
+ * architecture: a temporary SVD of the gate and up projections finds the hidden channels
+ * the low-rank form reconstructs well ("SVD-friendly"); those are compressed, the rest stay
+ * dense.  A channel's error is the expected squared error of its two pre-activations under
+ * the calibration distribution:
+ *   err[h] = sum over P in {gate, up} of dW_P[h] X dW_P[h]^T,  dW_P = W_P - left_P right_P,
+ * X = Xsum/n_x + damping*I, evaluated as the squared row norm of dW_P L_x (X = L_x L_x^T,
+ * fp32 products, fp64 row sums in a fixed order).
+ * w_gate, w_up: d_ff x d fp32, leading dim ldw >= d.  left_*: d_ff x r (leading dim r),
+ *   right_*: r x d (leading dim d): the factors lrc_whiten_decompose wrote for gate and up
+ *   with this Xsum, no Gsum and rank r (0 <= r <= min(d_ff, d); r = 0 needs no factors).
+ * Xsum: d x d fp32 (lower triangle read), leading dim ldx >= d; n_x > 0; damping >= 0.
+ * Outputs (device): err double[d_ff]; order int32[d_ff]: the channels by ascending err,
+ *   ties by channel index; lowrank uint8[d_ff]: 1 for the first n_lowrank channels of
+ *   `order` (0 <= n_lowrank <= d_ff), else 0.
+ * info (device int32[1]): 0, or p when pivot p of X is not positive (then LRC_ENOTPD and
+ *   the outputs are not written).  Blocks the host on `stream` once (after the Cholesky).
+ */
+lrc_status lrc_ffn_select_channels(const float* w_gate, const float* w_up, int64_t d_ff, int64_t d, int64_t ldw,
+                                   const float* left_gate, const float* right_gate, const float* left_up,
+                                   const float* right_up, int64_t r, const float* Xsum, int64_t ldx, int64_t n_x,
+                                   float damping, int64_t n_lowrank, double* err, int32_t* order, uint8_t* lowrank,
+                                   int32_t* info, void* ws, size_t ws_bytes, void* stream);
+size_t lrc_ffn_select_channels_workspace(int64_t d_ff, int64_t d);
+
+/*
  * lrc_lowrank_ffn -- decode-time forward of a SwiGLU FFN whose weights are replaced by
  * int8 low-rank factors.
  * LASER section 4 (System Implementation): the low-rank FFN runs as fused kernels for the

@@ -160,6 +160,32 @@ def test_lowrank_ffn_validation(lib):
     assert need > 0 and call(a21=need - 1) == EWORKSPACE
 
 
+def test_ffn_select_channels_validation(lib):
+    f = lib.lrc_ffn_select_channels
+    ok = [FAKE, FAKE, 40, 16, 16, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 16, 100, 0.0, 10, FAKE, FAKE, FAKE, FAKE,
+          FAKE, 1 << 30, None]
+
+    def call(**over):
+        a = list(ok)
+        for i, v in over.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    assert call(a0=None) == EINVAL          # w_gate
+    assert call(a10=None) == EINVAL         # Xsum
+    assert call(a4=15) == EINVAL            # ldw < d
+    assert call(a11=15) == EINVAL           # ldx < d
+    assert call(a12=0) == EINVAL            # n_x
+    assert call(a9=17) == EINVAL            # r > min(d_ff, d)
+    assert call(a9=-1) == EINVAL
+    assert call(a14=41) == EINVAL           # n_lowrank > d_ff
+    assert call(a13=-1.0) == EINVAL         # damping
+    assert call(a5=None) == EINVAL          # factors needed for r > 0
+    assert call(a9=0, a5=None, a6=None, a7=None, a8=None, a20=0, a19=None) == EWORKSPACE   # r = 0: no factors
+    need = lib.lrc_ffn_select_channels_workspace(40, 16)
+    assert need > 0 and call(a20=need - 1) == EWORKSPACE
+
+
 def test_profile_session_without_work(lib):
     # no kernel launched: the session records nothing and out-of-range queries fail
     assert lib.lrc_profile_start() == 0

@@ -268,3 +268,45 @@ def test_decoder_layers_fisher_allocation(lrc):
     iso = [i for i in range(1, 511) if min(s_ref[i - 1] - s_ref[i], s_ref[i] - s_ref[i + 1]) > 1e-3 * s_ref[0]]
     assert len(iso) > 0
     np.testing.assert_allclose(keep["s"][iso], f_ref[iso], rtol=1e-3)
+
+
+def test_ffn_channel_selection_full(lrc):
+    """FFN pair width: gate and up 11008 x 4096 at rank 2048 (the pages' rank ratio 0.5),
+    the covariance of a power-law 4096-wide stream.  Sampled channels' errors against the
+    oracle's quadratic form dW[h] X dW[h]^T (fp64, one channel at a time); the order and
+    selection bit-exact against the oracle's rule on the GPU's errors.  The factors are
+    seeded fp32 matrices (the selection step takes any factors; their optimality is the
+    decomposition's business)."""
+    d_ff, d, r, n = 11008, 4096, 2048, 16384
+    rng = np.random.default_rng(11)
+    step("inputs")
+    a = synth.activation_stream(n, d, 1.0, 51, dtype=torch.bfloat16, device=dev())
+    xs = torch.zeros(d, d, device=dev())
+    lrc.lrc_accumulate_cov(a, xs)
+    xs_np = xs.cpu().numpy()
+    del a
+    wg = rng.standard_normal((d_ff, d), dtype=np.float32) / np.float32(64.0)
+    wu = rng.standard_normal((d_ff, d), dtype=np.float32) / np.float32(64.0)
+    fac = [(rng.standard_normal((d_ff, r), dtype=np.float32) / np.float32(64.0),
+            rng.standard_normal((r, d), dtype=np.float32) / np.float32(64.0)) for _ in range(2)]
+    t = lambda x: torch.from_numpy(x).to(dev())
+    step("select on the GPU")
+    err, order, low, info = lrc.lrc_ffn_select_channels(t(wg), t(wu), (t(fac[0][0]), t(fac[0][1])),
+                                                        (t(fac[1][0]), t(fac[1][1])), xs, n, d_ff // 2, 1e-3)
+    assert int(info.item()) == 0
+    e = err.cpu().numpy()
+    step("oracle on sampled channels")
+    hs = rng.choice(d_ff, 24, replace=False)
+    x = np.tril(xs_np.astype(np.float64))
+    x = x + np.tril(x, -1).T
+    x = x / n + 1e-3 * np.eye(d)
+    for h in hs:
+        tot = 0.0
+        for w, (lf, rf) in zip((wg, wu), fac):
+            dw = w[h].astype(np.float64) - lf[h].astype(np.float64) @ rf.astype(np.float64)
+            tot += dw @ x @ dw
+        np.testing.assert_allclose(e[h], tot, rtol=5e-5)
+    o_ord, o_low = oracle.select_channels(e, d_ff // 2)
+    assert np.array_equal(order.cpu().numpy().astype(np.int64), o_ord)
+    assert np.array_equal(low.cpu().numpy(), o_low)
+    step("done")

@@ -610,3 +610,74 @@ def test_lowrank_ffn(lrc, n_tok, d, d_ff, rg, ru, rd):
     err = np.abs(to_np(y) - ref).max() / np.abs(ref).max()
     assert err < 4e-4, err
 
+
+
+# ----------------------------------------------------------------------------- FFN channel selection
+def _ffn_sel_inputs(d_ff, d, r, n, seed, dup=False):
+    """Seeded gate/up weights, a power-law calibration stream and the oracle's own rank-r
+    factors (fp32) as the inputs both sides receive."""
+    rng = np.random.default_rng(seed)
+    q, rr = np.linalg.qr(rng.standard_normal((d, d)))
+    q = q * np.sign(np.diag(rr))
+    lam = np.arange(1, d + 1, dtype=np.float64) ** -1.0
+    a = ((rng.standard_normal((n, d)) * np.sqrt(lam)) @ q.T).astype(np.float32)
+    wg = (rng.standard_normal((d_ff, d)) / math.sqrt(d)).astype(np.float32)
+    wu = (rng.standard_normal((d_ff, d)) / math.sqrt(d)).astype(np.float32)
+    if dup:   # repeated channels: equal errors, ordered by index
+        wg[7::11] = wg[3]
+        wu[7::11] = wu[3]
+    xs = oracle.covariance_sum(a).astype(np.float32)
+    fac = []
+    for w in (wg, wu):
+        if r == 0:
+            fac.append(None)
+            continue
+        res = oracle.whiten_decompose(w, xs.astype(np.float64), n, rank=r, damping=1e-3)
+        left = res["left"].astype(np.float32)
+        if dup:
+            left[7::11] = left[3]
+        fac.append((left, res["right"].astype(np.float32)))
+    return wg, wu, fac, xs
+
+
+@pytest.mark.parametrize("d_ff,d,r,n_low", [(300, 96, 24, 120), (257, 64, 0, 100), (1100, 256, 128, 550),
+                                            (130, 80, 60, 0), (130, 80, 40, 130)])
+def test_ffn_select_channels(lrc, d_ff, d, r, n_low):
+    """Per-channel errors against the fp64 oracle (its quadratic form dW X dW^T, not the
+    library's ||dW L_x||^2).  The GPU forms D = W - Left Right and E = D L_x in fp32
+    (MFMA, sums of <= 256 products: relative error of an entry ~ sqrt(k) u = 16 u against
+    the summed magnitudes, which stay within a few times |E| for these inputs) and sums
+    E^2 in fp64, so err is within ~1e-5 relative; the bound is 5e-5.  The order and the
+    selection are a decision in fp64 on the GPU's errors: bit-exact against the oracle's
+    rule applied to them."""
+    n, damping = 2000, 1e-3
+    wg, wu, fac, xs = _ffn_sel_inputs(d_ff, d, r, n, seed=d_ff + r)
+    t = lambda x: torch.from_numpy(x).to(dev())
+    err, order, low, info = lrc.lrc_ffn_select_channels(
+        t(wg), t(wu), None if r == 0 else (t(fac[0][0]), t(fac[0][1])), None if r == 0 else (t(fac[1][0]), t(fac[1][1])),
+        t(xs), n, n_low, damping)
+    assert int(info.item()) == 0
+    ref = oracle.ffn_channel_errors(wg, wu, fac[0], fac[1], xs, n, damping)
+    np.testing.assert_allclose(to_np(err), ref, rtol=5e-5)
+    o_ord, o_low = oracle.select_channels(to_np(err), n_low)
+    assert np.array_equal(to_np(order).astype(np.int64), o_ord)
+    assert np.array_equal(to_np(low), o_low)
+
+
+def test_ffn_select_channels_ties_and_failure(lrc):
+    """Repeated channels give bit-equal errors (row-independent arithmetic) and are
+    ordered by index; a covariance that is not positive definite is reported (info =
+    the failing pivot), not patched."""
+    d_ff, d, r, n = 140, 64, 16, 1000
+    wg, wu, fac, xs = _ffn_sel_inputs(d_ff, d, r, n, seed=7, dup=True)
+    t = lambda x: torch.from_numpy(x).to(dev())
+    err, order, low, info = lrc.lrc_ffn_select_channels(t(wg), t(wu), (t(fac[0][0]), t(fac[0][1])),
+                                                        (t(fac[1][0]), t(fac[1][1])), t(xs), n, 60, 1e-3)
+    e = to_np(err)
+    assert np.all(e[7::11] == e[3])
+    o_ord, o_low = oracle.select_channels(e, 60)
+    assert np.array_equal(to_np(order).astype(np.int64), o_ord) and np.array_equal(to_np(low), o_low)
+    bad = np.zeros((d, d), dtype=np.float32)
+    with pytest.raises(lrc.LrcError) as ex:
+        lrc.lrc_ffn_select_channels(t(wg), t(wu), None, None, t(bad), n, 10, 0.0)
+    assert ex.value.status == lrc.LRC_ENOTPD
