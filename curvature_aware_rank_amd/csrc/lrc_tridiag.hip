@@ -45,7 +45,7 @@ constexpr int WR = 32;          // rows per workgroup of the w kernel (16 or 32;
 constexpr int WPB = TS / WR;    // w workgroups per 64-row block
 constexpr int NPB = 4 * WPB;    // squared-norm partials per 64-row block (one per w wave)
 constexpr int BIS_PTS = 16;     // Sturm points per eigenvalue per multisection step
-constexpr int BIS_ITERS = 14;   // 17^14 > 2^57: the interval shrinks below fp64 resolution
+constexpr int BIS_ITERS = 12;   // 17^12 > 2^49: width below 2^-48 of the bounds, under a count's own n eps accuracy
 constexpr int BIS_STAGE = 2048; // d, e^2 staged through LDS in chunks of this many
 constexpr int CL_MAX = 32;      // largest cluster inverse iteration handles
 constexpr double CL_TOL = 1e-7; // eigenvalues closer than CL_TOL ||T|| share a cluster
