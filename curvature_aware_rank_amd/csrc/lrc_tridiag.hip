@@ -579,10 +579,13 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
 constexpr int SYP = 64 + 2;   // LDS pitch (doubles) of an operand k row
 
 __global__ __launch_bounds__(256) void tri_syr2k_kernel(double* __restrict__ A, int64_t lda, int n, int i0, int pb,
-                                                        int j1, const double* __restrict__ Wp) {
+                                                        int j1, const double* __restrict__ Wp,
+                                                        double* __restrict__ npart, double* __restrict__ x0,
+                                                        double* __restrict__ d, double* __restrict__ xv) {
   // the K = 64 product in two halves through one LDS pair (V_r W_c^T, then W_r V_c^T), so
   // that four workgroups fit on a CU
   __shared__ double opa[NB][SYP], opb[NB][SYP];
+  __shared__ double sqp[8];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave >> 1, wc = wave & 1;
@@ -655,6 +658,12 @@ __global__ __launch_bounds__(256) void tri_syr2k_kernel(double* __restrict__ A, 
   stage(wr8, okr, vc, okc);   // W_r V_c^T
   __syncthreads();
   mma();
+  // Tiles of the first column block also start the next panel (what the column-start
+  // kernel does for the first panel): column j1, now up to date, as the contiguous vector
+  // xv, d[j1], x0 = A[j1 + 1][j1] and the block's squared-norm partial over rows >= j1 + 2
+  // (NPB partials per 64-row block: the sum, then zeros).  Its values sit in lanes
+  // l16 = 0 of the waves with wc = 0 (j = 0), rows wr 32 + i 16 + lq + 4 e.
+  double sq = 0.0;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -663,8 +672,23 @@ __global__ __launch_bounds__(256) void tri_syr2k_kernel(double* __restrict__ A, 
       for (int e = 0; e < 4; ++e) {
         const int lr = wr * 32 + i * 16 + lq + 4 * e, lc = wc * 32 + j * 16 + l16;
         const int r = R0 + lr, cc = C0 + lc;
-        if (r < n && cc < n && (b != c || lr >= lc)) A[int64_t(r) * lda + cc] = old[i][j][e] - acc[i][j][e];
+        const double val = old[i][j][e] - acc[i][j][e];
+        if (r < n && cc < n && (b != c || lr >= lc)) A[int64_t(r) * lda + cc] = val;
+        if (c == 0 && lc == 0 && r < n) {
+          xv[r] = val;
+          if (r == j1) d[j1] = val;
+          if (r == j1 + 1) *x0 = val;
+          if (r >= j1 + 2) sq += val * val;
+        }
       }
+  if (c == 0) {
+    // lanes 0, 16, 32, 48 of waves 0 and 2 hold partial sums; fixed-order total
+    if (wc == 0 && l16 == 0) sqp[wr * 4 + lq] = sq;
+    __syncthreads();
+    if (tid < NPB) npart[NPB * b + tid] = tid == 0 ? ((sqp[0] + sqp[1]) + (sqp[2] + sqp[3])) +
+                                                        ((sqp[4] + sqp[5]) + (sqp[6] + sqp[7]))
+                                                  : 0.0;
+  }
 }
 
 
@@ -1696,7 +1720,7 @@ lrc_status tri_reduce(hipStream_t st, double* A, int n, int64_t lda, const TWs& 
   const int t0 = n <= TT ? 0 : int(cdiv(n - TT, NB) * NB);
   for (int i0 = 0; i0 < t0; i0 += NB) {
     const int pb = std::min(NB, n - 1 - i0);
-    {
+    if (i0 == 0) {   // later panels are started by the previous panel's rank-2 update
       const unsigned g = unsigned(cdiv(n - i0, TS));
       tri_colstart_kernel<<<g, 256, 0, st>>>(A, lda, n, i0, w.npart + (i0 & 1) * NPB * cdiv(n, TS), w.x0 + (i0 & 1),
                                              w.d, w.xv + (i0 & 1) * n);
@@ -1743,7 +1767,11 @@ lrc_status tri_reduce(hipStream_t st, double* A, int n, int64_t lda, const TWs& 
     if (j1 < n) {
       const int nt = int(cdiv(n - j1, TS));
       ProfScope scope("tri_syr2k_kernel", st, 2.0 * double(n - j1) * double(n - j1 + 1) * pb, 0.0);
-      tri_syr2k_kernel<<<unsigned(nt * (nt + 1) / 2), 256, 0, st>>>(A, lda, n, i0, pb, j1, w.Wp);
+      // j1 is the next panel's first column (i0 + NB): its start-of-panel state goes to the
+      // buffers of its parity
+      tri_syr2k_kernel<<<unsigned(nt * (nt + 1) / 2), 256, 0, st>>>(
+          A, lda, n, i0, pb, j1, w.Wp, w.npart + (j1 & 1) * NPB * cdiv(n, TS), w.x0 + (j1 & 1), w.d,
+          w.xv + (j1 & 1) * n);
       LRC_LAUNCHED();
     }
   }
