@@ -51,6 +51,10 @@ constexpr int CL_MAX = 32;      // largest cluster inverse iteration handles
 constexpr double CL_TOL = 1e-7; // eigenvalues closer than CL_TOL ||T|| share a cluster
 constexpr double EPS = 2.220446049250313e-16;
 
+// first row / column of the 64-row blocks of the trailing matrix that starts at s0: the
+// 16-column boundary at or below s0, so that every tile row starts on a 128-byte line
+__host__ __device__ __forceinline__ int blk_origin(int s0) { return s0 & ~15; }
+
 __device__ __forceinline__ void tile_of(int t, int& b, int& c) {
   // t = b (b + 1) / 2 + c, 0 <= c <= b
   int bb = int((sqrt(8.0 * double(t) + 1.0) - 1.0) * 0.5);
@@ -153,7 +157,6 @@ __global__ __launch_bounds__(256) void tri_colstart_kernel(const double* __restr
 // go through a 16 x 64 LDS table and are added in row-band order.
 constexpr int DPP_ROW_ROR8 = 0x128;   // row_ror:8, lane i <-> i + 8 within 16 lanes
 
-template <bool EVEN>
 __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict__ A, int64_t lda, int n, int i, int i0,
                                                        int jj, const double* __restrict__ Wp,
                                                        const double* __restrict__ xv, double* __restrict__ P,
@@ -164,14 +167,14 @@ __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict_
   __shared__ double red[8][2][NB];
   const int tid = threadIdx.x;
   const int s0 = i + 1;
-  const int m = n - s0;
-  const int nbt = (m + TS - 1) / TS;
+  const int so = blk_origin(s0);   // blocks start at a 16-column boundary
+  const int nbt = (n - so + TS - 1) / TS;
   const int ntile = nbt * (nbt + 1) / 2;
   if (int(blockIdx.x) >= ntile) {
     // panel workgroup for row block pb: V^T x and W^T x over the block's 64 rows, 32
     // columns x 8 groups of 8 rows, summed over the groups in order
     const int pb = blockIdx.x - ntile;
-    const int R0 = s0 + pb * TS;
+    const int R0 = so + pb * TS;
     const int pc = tid & 31, pg = tid >> 5;
     const int pcc = min(pc, jj - 1);
     double va[8], wa[8], xa[8];
@@ -185,7 +188,8 @@ __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict_
     double sv = 0.0, sw = 0.0;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const bool ok = pc < jj && R0 + pg * 8 + q < n;
+      const int r = R0 + pg * 8 + q;
+      const bool ok = pc < jj && r >= s0 && r < n;
       sv += ok ? va[q] * xa[q] : 0.0;
       sw += ok ? wa[q] * xa[q] : 0.0;
     }
@@ -206,16 +210,18 @@ __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict_
   }
   int b, c;
   tile_of(blockIdx.x, b, c);
-  const int R0 = s0 + b * TS, C0 = s0 + c * TS;
+  const int R0 = so + b * TS, C0 = so + c * TS;
   const bool diag = b == c;
   const int rb = tid >> 4, cb = tid & 15;
   const int c4 = C0 + 4 * cb;
-  // every load is unconditional from a clamped address and masked at use: pairs start at
-  // even columns, at most at pe, the last even column; for odd n the pair (n - 1, n) reads
-  // one element of the row padding (the pitch is even and exceeds n)
+  // every load is unconditional from a clamped address and masked at use: the tile's
+  // columns start at a 16-column boundary, so every 4-column patch row is two 16-byte
+  // pairs at even columns, at most at pe, the last even column; for odd n the pair
+  // (n - 1, n) reads one element of the row padding (the pitch is even and exceeds n).
+  // Entries left of s0 (and above it) are read and masked.
   const int pe = (n - 1) & ~1;
   double tv[4][4];
-  if (EVEN) {
+  {
     const int p0 = min(c4, pe), p1 = min(c4 + 2, pe);
     double2 u[4][2];
 #pragma unroll
@@ -230,23 +236,6 @@ __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict_
       tv[k][1] = u[k][0].y;
       tv[k][2] = u[k][1].x;
       tv[k][3] = u[k][1].y;
-    }
-  } else {
-    const int p0 = min(c4 - 1, pe), p1 = min(c4 + 1, pe), p2 = min(c4 + 3, pe);
-    double2 u[4][3];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int r = min(R0 + 4 * rb + k, n - 1);
-      u[k][0] = *reinterpret_cast<const double2*>(A + int64_t(r) * lda + p0);
-      u[k][1] = *reinterpret_cast<const double2*>(A + int64_t(r) * lda + p1);
-      u[k][2] = *reinterpret_cast<const double2*>(A + int64_t(r) * lda + p2);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      tv[k][0] = u[k][0].y;
-      tv[k][1] = u[k][1].x;
-      tv[k][2] = u[k][1].y;
-      tv[k][3] = u[k][2].x;
     }
   }
   // x on the patch's columns (vcl) and rows (vbl), masked with the tile below
@@ -267,7 +256,7 @@ __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict_
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int col = 4 * cb + e;
-      const bool in = R0 + row < n && C0 + col < n;
+      const bool in = R0 + row >= s0 && R0 + row < n && C0 + col >= s0 && C0 + col < n;
       const bool okr = in && (!diag || col <= row);
       const bool okc = in && (!diag || col < row);
       rp[k] += okr ? tv[k][e] * vcl[e] : 0.0;
@@ -295,7 +284,7 @@ __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict_
 #pragma unroll
     for (int q = 0; q < 16; ++q) c_ += cpart[q][tid];
     const double r_ = rsum[tid];
-    const double xb = R0 + tid < n ? xe : 0.0;
+    const double xb = R0 + tid >= s0 && R0 + tid < n ? xe : 0.0;
     if (diag) {
       P[(int64_t(b) * nbt + b) * TS + tid] = r_ + c_;
     } else {
@@ -358,13 +347,13 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
   __shared__ double red[3][4];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int s0 = i + 1;
-  const int m = n - s0;
-  const int nbt = (m + TS - 1) / TS;
+  const int so = blk_origin(s0);   // the symv's block origin
+  const int nbt = (n - so + TS - 1) / TS;
   const int ntile = nbt * (nbt + 1) / 2;
-  const int npp = NPB * ((n - i + TS - 1) / TS);   // partials written for column i
+  const int npp = NPB * ((n - blk_origin(i) + TS - 1) / TS);   // partials written for column i
   const int b = blockIdx.x / WPB, h = blockIdx.x % WPB;
   const int lr0 = h * WR;        // first row of this workgroup within its 64-row block
-  const int R0 = s0 + b * TS + lr0;
+  const int R0 = so + b * TS + lr0;
   const int xp = tid % RPAIRS, cg = tid / RPAIRS;   // symv partials: row pair 2 xp, column blocks cg + NCG u
   const int cq = tid & 15, qg = tid >> 4;   // panel: column pair 2 cq, row (block) group qg + 16 u
   // panel column pair start, never past column i0 + jj = i
@@ -409,7 +398,7 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
   for (int u = 0; u < 9; ++u) ts[u] = S[min(tid + 256 * u, ntile - 1)];
   const double tnp0 = npart[min(tid, npp - 1)];
   const double tnp1 = npart[min(tid + 256, npp - 1)];
-  const double tp0 = P[int64_t(min(tid, nbt - 1)) * TS];   // row s0 = block 0, local 0
+  const double tp0 = P[int64_t(min(tid, nbt - 1)) * TS + (s0 - so)];   // row s0: block 0, local s0 - so
   const double x0v = *x0p;
   const double a00 = A[int64_t(s0) * lda + s0];
 
@@ -456,7 +445,7 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
 #pragma unroll
   for (int u = 0; u < NRU; ++u) {
     const int rr = qg + 16 * u;
-    const bool okr = R0 + rr < n;
+    const bool okr = R0 + rr >= s0 && R0 + rr < n;
     Vs[rr][2 * cq] = okr && 2 * cq < jj ? pv[u].x : 0.0;
     Vs[rr][2 * cq + 1] = okr && 2 * cq + 1 < jj ? pv[u].y : 0.0;
     Ws[rr][2 * cq] = okr && 2 * cq < jj ? pw[u].x : 0.0;
@@ -469,7 +458,7 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
     wn[2 * tid + 1] = 2 * tid + 1 < jj ? wnl.y : 0.0;
   }
   if (tid < WR) {
-    const bool ok = R0 + tid < n;
+    const bool ok = R0 + tid >= s0 && R0 + tid < n;
     colI[tid] = ok ? ci : 0.0;
     colS[tid] = ok ? cs0 : 0.0;
   }
@@ -481,7 +470,7 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
     for (int u = 0; u < 9; ++u) v1 += tid + 256 * u < ntile ? ts[u] : 0.0;
     for (int t = tid + 256 * 9; t < ntile; t += 256) v1 += S[t];
     double y0 = tid < nbt ? tp0 : 0.0;
-    for (int c = tid + 256; c < nbt; c += 256) y0 += P[int64_t(c) * TS];
+    for (int c = tid + 256; c < nbt; c += 256) y0 += P[int64_t(c) * TS + (s0 - so)];
     v0 = wave_sum(v0);
     v1 = wave_sum(v1);
     y0 = wave_sum(y0);
@@ -548,7 +537,7 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
   yr = group_sum<TPR>(yr);
   double v = 0.0, w = 0.0;
   const double cs0x = colS[x];
-  if (r < n) {
+  if (r >= s0 && r < n) {
     const double y = scale * yr + cfac * cs0x - corr;
     v = r == s0 ? 1.0 : colI[x] * scale;
     w = r == s0 ? w0 : tau * y + alpha * v;   // row s0: the value every block uses
@@ -560,7 +549,7 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
   if (!do_next) return;
   // column s0: rows s0.., C[r][s0] -= sum_c V[r][c] W[s0][c] + W[r][c] V[s0][c], c = 0..jj
   double sq = 0.0;
-  if (r < n && part == 0) {
+  if (r >= s0 && r < n && part == 0) {
     const double val = cs0x - (c2 + (v * w0 + w));
     A[int64_t(r) * lda + s0] = val;
     xv_next[r] = val;
@@ -1729,23 +1718,19 @@ lrc_status tri_reduce(hipStream_t st, double* A, int n, int64_t lda, const TWs& 
     for (int jj = 0; jj < pb; ++jj) {
       const int i = i0 + jj;
       const int m = n - i - 1;
-      const int nbt = int(cdiv(m, TS));
+      const int nbt = int(cdiv(n - blk_origin(i + 1), TS));   // blocks from the aligned origin
       const int par = i & 1, npar = (i + 1) & 1;
       double* np_cur = w.npart + par * NPB * cdiv(n, TS);
       double* np_next = w.npart + npar * NPB * cdiv(n, TS);
       {
         ProfKernel pk("tri_symv_kernel", 2.0 * double(m) * double(m), 8.0 * double(m) * double(m + 1) / 2);
-        // 16-byte pairs need an even matrix pitch and base; the tile's first column parity
-        // picks the pair alignment
+        // 16-byte pairs need an even matrix pitch and base; tiles start at 16-column
+        // boundaries (rows and columns before s0 are masked)
         const double* xv = w.xv + par * n;
         // the tiles, then (inside the panel) one workgroup per row block for V^T x, W^T x
         const dim3 grid(unsigned(nbt * (nbt + 1) / 2 + (jj > 0 ? nbt : 0)));
-        if ((i + 1) % 2 == 0)
-          hipExtLaunchKernelGGL(tri_symv_kernel<true>, grid, dim3(256), 0, st, pk.start, pk.stop, 0, (const double*)A,
-                                lda, n, i, i0, jj, (const double*)w.Wp, xv, w.P, w.S, w.SV, w.SW);
-        else
-          hipExtLaunchKernelGGL(tri_symv_kernel<false>, grid, dim3(256), 0, st, pk.start, pk.stop, 0, (const double*)A,
-                                lda, n, i, i0, jj, (const double*)w.Wp, xv, w.P, w.S, w.SV, w.SW);
+        hipExtLaunchKernelGGL(tri_symv_kernel, grid, dim3(256), 0, st, pk.start, pk.stop, 0, (const double*)A, lda, n, i,
+                              i0, jj, (const double*)w.Wp, xv, w.P, w.S, w.SV, w.SW);
         LRC_LAUNCHED();
       }
       {
