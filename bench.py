@@ -48,9 +48,9 @@ ROOFLINE = {
 
 # HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE on this
 # workload, scaled by the copy-kernel calibration (profiles/counters_tri_symv_attnproj_4096.md:
-# fetch 29.88 MB x 1 + write 0.77 MB, the average over the 3968 launches of a 4096-wide
+# fetch 24.43 MB + write 0.77 MB, the average over the 3968 launches of a 4096-wide
 # tridiagonalisation); absent (None) for a kernel whose counters were not taken
-TRAFFIC = {"tri_symv_kernel": 30.65e6}
+TRAFFIC = {"tri_symv_kernel": 25.20e6}
 
 
 def parse():
