@@ -220,8 +220,8 @@ def secondary(lrc, torch, dev):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this path has no multi-GPU mode (see DESIGN.md for how it "
-              "would shard).", file=sys.stderr)
+        print("bench.py runs on one GPU only: this path has no multi-GPU mode (covariance sums would be "
+              "all-reduced and matrices dealt out to GPUs; that layer is not built).", file=sys.stderr)
         sys.exit(2)
     import torch
 

@@ -70,7 +70,7 @@ _SIGS = {
 
 def _load():
     if not os.path.exists(library_path):
-        raise ImportError(f"liblrc.so not built at {library_path}; run __graft_entry__.build()")
+        raise ImportError(f"liblrc.so not built at {library_path}; run python curvature_aware_rank_amd/build.py")
     so = ctypes.CDLL(library_path)
     for name, (res, args) in _SIGS.items():
         fn = getattr(so, name)

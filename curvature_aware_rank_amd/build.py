@@ -1,6 +1,6 @@
 """Build liblrc.so (all HIP sources, gfx950) in-tree with hipcc.
 
-    python curvature_aware_rank_amd/build.py      (or __graft_entry__.build())
+    python curvature_aware_rank_amd/build.py
 """
 from __future__ import annotations
 
