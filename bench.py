@@ -178,6 +178,22 @@ def secondary(lrc, torch, dev):
                                              "GB/s": round(fbytes / t / 1e9, 1),
                                              "hbm_frac": round(fbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
     del gate, up, down
+    # hybrid decode: half the hidden channels low-rank (rank 2048), the other half dense int8
+    nl = nd = dff // 2
+    gate = (*fac(rk, d), *fac(nl, rk))
+    up = (*fac(rk, d), *fac(nl, rk))
+    down = (*fac(nl, rk), *fac(d, rk))
+    dense = (*fac(nd, d), *fac(nd, d), *fac(d, nd))
+    hbytes = 2.0 * rk * d + 2.0 * nl * rk + nl * rk + d * rk + 3.0 * nd * d
+    for nt in (1, 8):
+        xin = torch.randn(nt, d, generator=g, device=dev)
+        lrc.lrc_hybrid_ffn(xin, gate, up, down, dense)
+        t = _time(lambda: lrc.lrc_hybrid_ffn(xin, gate, up, down, dense), torch, 10)
+        out[f"hybrid_ffn_decode_{nt}tok"] = {
+            "workload": f"{nt} tokens, 4096 -> 11008 -> 4096, {nl} channels low-rank (ranks 2048), {nd} dense, int8",
+            "us": round(t * 1e6, 1), "tokens_per_s": round(nt / t, 1), "GB/s": round(hbytes / t / 1e9, 1),
+            "hbm_frac": round(hbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+    del gate, up, down, dense
     # FFN hybrid channel selection: gate and up 11008 x 4096 at rank 2048 (the factors'
     # values do not change the work), covariance of a 4096-wide stream
     wg = torch.randn(dff, d, generator=g, device=dev) / d ** 0.5

@@ -20,6 +20,7 @@ __all__ = [
     "LRC_SCORE_FISHER", "LRC_SCORE_KFAC", "LRC_RANKSCORE_UNIRANK", "LRC_RANKSCORE_SWIFT", "LrcError", "lib",
     "library_path", "lrc_accumulate_cov", "lrc_whiten_decompose", "lrc_score_components", "lrc_allocate_ranks",
     "lrc_rank_scores", "lrc_rotate_quantize", "lrc_quantize_rows", "lrc_lowrank_ffn", "lrc_ffn_select_channels",
+    "lrc_hybrid_ffn",
     "lrc_status_string", "lrc_profile_start", "lrc_profile_stop", "lrc_profile_kernels",
 ]
 
@@ -57,6 +58,9 @@ _SIGS = {
     "lrc_ffn_select_channels": (_i32, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _i64,
                                        ctypes.c_float, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "lrc_ffn_select_channels_workspace": (_sz, [_i64, _i64]),
+    "lrc_hybrid_ffn": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp,
+                              _vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "lrc_hybrid_ffn_workspace": (_sz, [_i64, _i64, _i64, _i64, _i64, _i64]),
     "lrc_status_string": (ctypes.c_char_p, [_i32]),
     "lrc_last_hip_error": (_i32, []),
     "lrc_profile_start": (_i32, []),
@@ -363,6 +367,47 @@ def lrc_ffn_select_channels(w_gate: torch.Tensor, w_up: torch.Tensor, gate_facto
                                        int(n_lowrank), _ptr(err), _ptr(order), _ptr(lowrank), _ptr(info), _ptr(ws),
                                        ws.numel(), _stream()), "lrc_ffn_select_channels")
     return err, order, lowrank, info
+
+
+def lrc_hybrid_ffn(x: torch.Tensor, gate=None, up=None, down=None, dense=None):
+    """Hybrid FFN forward: hidden channels [0, n_lr) low-rank (gate, up, down as for
+    lrc_lowrank_ffn, or all None when n_lr = 0), the next n_dense dense:
+    dense = (q_gd (n_dense, d) int8, s_gd (n_dense,), q_ud, s_ud, q_dd (d, n_dense) int8 --
+    W_down's dense columns as rows, s_dd (d,)), or None when n_dense = 0.
+    Returns y (n_tok, d) fp32."""
+    _dev(x, "x")
+    n_tok, d = x.shape
+    x = x.contiguous()
+    lr = gate is not None
+    if lr != (up is not None) or lr != (down is not None):
+        raise ValueError("give gate, up and down together, or none of them")
+    if lr:
+        for t in [*gate, *up, *down]:
+            _dev(t, "ffn factor")
+        g = [t.contiguous() for t in gate]
+        u = [t.contiguous() for t in up]
+        dn = [t.contiguous() for t in down]
+        rg, ru, rd = g[0].shape[0], u[0].shape[0], dn[0].shape[1]
+        n_lr = g[2].shape[0]
+    else:
+        g = u = dn = [None] * 4
+        rg = ru = rd = n_lr = 0
+    if dense is not None:
+        for t in dense:
+            _dev(t, "dense FFN operand")
+        dd = [t.contiguous() for t in dense]
+        n_dense = dd[0].shape[0]
+    else:
+        dd = [None] * 6
+        n_dense = 0
+    y = torch.empty(n_tok, d, dtype=torch.float32, device=x.device)
+    ws = _workspace(lib.lrc_hybrid_ffn_workspace(n_tok, n_lr, rg, ru, rd, n_dense), x.device)
+    p = lambda t: None if t is None else _ptr(t)
+    _check(lib.lrc_hybrid_ffn(_ptr(x), n_tok, d, n_lr, p(g[0]), p(g[1]), p(g[2]), p(g[3]), rg, p(u[0]), p(u[1]),
+                              p(u[2]), p(u[3]), ru, p(dn[0]), p(dn[1]), p(dn[2]), p(dn[3]), rd, n_dense, p(dd[0]),
+                              p(dd[1]), p(dd[2]), p(dd[3]), p(dd[4]), p(dd[5]), _ptr(y), _ptr(ws), ws.numel(),
+                              _stream()), "lrc_hybrid_ffn")
+    return y
 
 
 def lrc_lowrank_ffn(x: torch.Tensor, gate, up, down):

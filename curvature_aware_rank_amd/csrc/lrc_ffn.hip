@@ -44,7 +44,8 @@ __global__ __launch_bounds__(FT) void rows_gemv_kernel(const int8_t* __restrict_
                                                        int rows0, const int8_t* __restrict__ q1,
                                                        const float* __restrict__ s1, int rows1, int n,
                                                        const float* __restrict__ v, int n_tok,
-                                                       float* __restrict__ out0, float* __restrict__ out1) {
+                                                       float* __restrict__ out0, float* __restrict__ out1,
+                                                       int accumulate = 0) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * (FT / 64) + (threadIdx.x >> 6);
   if (row >= rows0 + rows1) return;
@@ -74,7 +75,10 @@ __global__ __launch_bounds__(FT) void rows_gemv_kernel(const int8_t* __restrict_
 #pragma unroll
     for (int t = 0; t < TG; ++t) {
       const float a = wave_sumf(acc[t]);
-      if (lane == 0 && t0 + t < n_tok) out[int64_t(t0 + t) * ld_out + r] = sc * a;
+      if (lane == 0 && t0 + t < n_tok) {
+        float* o = out + int64_t(t0 + t) * ld_out + r;
+        *o = accumulate ? *o + sc * a : sc * a;
+      }
     }
   }
 }
@@ -227,6 +231,13 @@ __global__ __launch_bounds__(FT) void swiglu_down_kernel(const int8_t* __restric
   }
 }
 
+// dense hidden channels: g[i] <- SiLU(g[i]) * u[i] (n_tok x n_dense, in place)
+__global__ __launch_bounds__(FT) void swiglu_dense_kernel(float* __restrict__ g, const float* __restrict__ u,
+                                                          int64_t cnt) {
+  const int64_t i = int64_t(blockIdx.x) * FT + threadIdx.x;
+  if (i < cnt) g[i] = silu(g[i]) * u[i];
+}
+
 // latent_d[t][k] = s_rd[k] * sum over chunks b of pd[b][t][k]: four threads per output,
 // each summing a quarter of the chunks in order (16 loads in flight), quarters added in
 // order
@@ -330,5 +341,84 @@ extern "C" lrc_status lrc_lowrank_ffn(const float* x, int64_t n_tok, int64_t d, 
   rows_gemv_kernel<<<unsigned(cdiv(d, FT / 64)), FT, 0, st>>>(q_ld, s_ld, int(d), nullptr, nullptr, 0, int(rd), w.latd,
                                                              int(n_tok), y, nullptr);
   LRC_LAUNCHED();
+  return LRC_OK;
+}
+
+// Hybrid FFN (LASER 3, item Hybrid architecture): hidden channels [0, n_lr) take the
+// low-rank branch (the kernels above), channels [n_lr, n_lr + n_dense) stay dense (int8
+// rows with per-row scales): their gate and up pre-activations are one row GEMV each, the
+// SwiGLU runs in place, and W_down's dense columns (passed as d rows of n_dense int8) add
+// their share to y.
+namespace {
+struct HybWs {
+  FfnWs lr;
+  float *gd, *ud;
+};
+HybWs carve_hyb(Carve& cv, int64_t n_tok, int64_t n_lr, int64_t rg, int64_t ru, int64_t rd, int64_t n_dense) {
+  HybWs w{};
+  if (n_lr > 0) w.lr = carve_ffn(cv, n_tok, rg, ru, rd, cdiv(n_lr, ffn_chunk(n_lr)));
+  if (n_dense > 0) {
+    w.gd = cv.take<float>(size_t(n_tok * n_dense));
+    w.ud = cv.take<float>(size_t(n_tok * n_dense));
+  }
+  return w;
+}
+}  // namespace
+
+extern "C" size_t lrc_hybrid_ffn_workspace(int64_t n_tok, int64_t n_lr, int64_t rg, int64_t ru, int64_t rd,
+                                           int64_t n_dense) {
+  if (n_tok <= 0 || n_lr < 0 || n_dense < 0 || n_lr + n_dense <= 0) return 0;
+  if (n_lr > 0 && (rg <= 0 || ru <= 0 || rd <= 0)) return 0;
+  Carve cv(nullptr);
+  carve_hyb(cv, n_tok, n_lr, rg, ru, rd, n_dense);
+  return cv.bytes();
+}
+
+extern "C" lrc_status lrc_hybrid_ffn(const float* x, int64_t n_tok, int64_t d, int64_t n_lr, const int8_t* q_rg,
+                                     const float* s_rg, const int8_t* q_lg, const float* s_lg, int64_t rg,
+                                     const int8_t* q_ru, const float* s_ru, const int8_t* q_lu, const float* s_lu,
+                                     int64_t ru, const int8_t* q_rdt, const float* s_rd, const int8_t* q_ld,
+                                     const float* s_ld, int64_t rd, int64_t n_dense, const int8_t* q_gd,
+                                     const float* s_gd, const int8_t* q_ud, const float* s_ud, const int8_t* q_dd,
+                                     const float* s_dd, float* y, void* ws, size_t ws_bytes, void* stream) {
+  if (x == nullptr || y == nullptr || n_tok <= 0 || d <= 0 || n_lr < 0 || n_dense < 0 || n_lr + n_dense <= 0)
+    return LRC_EINVAL;
+  if (d % 16 || n_dense % 16 || reinterpret_cast<uintptr_t>(x) % 16 != 0) return LRC_EINVAL;
+  if (n_dense > 0) {
+    const void* ptrs[] = {q_gd, s_gd, q_ud, s_ud, q_dd, s_dd};
+    for (const void* p : ptrs)
+      if (p == nullptr) return LRC_EINVAL;
+    for (const void* p : {(const void*)q_gd, (const void*)q_ud, (const void*)q_dd})
+      if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return LRC_EINVAL;
+    if (n_tok > (int64_t(1) << 20) || n_dense > (int64_t(1) << 24) || d > (int64_t(1) << 24) ||
+        n_tok * n_dense > (int64_t(1) << 31))
+      return LRC_EINVAL;
+  }
+  const size_t need = lrc_hybrid_ffn_workspace(n_tok, n_lr, rg, ru, rd, n_dense);
+  if (n_lr > 0 && need == 0) return LRC_EINVAL;
+  if (ws == nullptr || ws_bytes < need) return LRC_EWORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Carve cv(ws);
+  const HybWs w = carve_hyb(cv, n_tok, n_lr, rg, ru, rd, n_dense);
+  if (n_lr > 0) {
+    // the low-rank channels write y; the dense ones add to it
+    const lrc_status s2 = lrc_lowrank_ffn(x, n_tok, d, n_lr, q_rg, s_rg, q_lg, s_lg, rg, q_ru, s_ru, q_lu, s_lu, ru,
+                                          q_rdt, s_rd, q_ld, s_ld, rd, y, static_cast<void*>(w.lr.latg),
+                                          lrc_lowrank_ffn_workspace(n_tok, n_lr, rg, ru, rd), stream);
+    if (s2 != LRC_OK) return s2;
+  }
+  if (n_dense > 0) {
+    ProfScope scope("hybrid_ffn_dense", st, 0.0, 3.0 * double(n_dense) * double(d) + 4.0 * double(n_tok) * 2 * d);
+    rows_gemv_kernel<<<unsigned(cdiv(2 * n_dense, FT / 64)), FT, 0, st>>>(q_gd, s_gd, int(n_dense), q_ud, s_ud,
+                                                                          int(n_dense), int(d), x, int(n_tok), w.gd,
+                                                                          w.ud);
+    LRC_LAUNCHED();
+    swiglu_dense_kernel<<<unsigned(cdiv(n_tok * n_dense, FT)), FT, 0, st>>>(w.gd, w.ud, n_tok * n_dense);
+    LRC_LAUNCHED();
+    rows_gemv_kernel<<<unsigned(cdiv(d, FT / 64)), FT, 0, st>>>(q_dd, s_dd, int(d), nullptr, nullptr, 0,
+                                                               int(n_dense), w.gd, int(n_tok), y, nullptr,
+                                                               n_lr > 0 ? 1 : 0);
+    LRC_LAUNCHED();
+  }
   return LRC_OK;
 }

@@ -285,6 +285,29 @@ lrc_status lrc_lowrank_ffn(const float* x, int64_t n_tok, int64_t d, int64_t d_f
 size_t lrc_lowrank_ffn_workspace(int64_t n_tok, int64_t d_ff, int64_t rg, int64_t ru, int64_t rd);
 
 /*
+ * lrc_hybrid_ffn -- the same forward for an FFN in LASER's hybrid form (section 3, item
+ * Hybrid architecture: the selected hidden channels compressed, the others dense).  The
+ * hidden channels are ordered so that [0, n_lr) take the low-rank branch and the next
+ * n_dense stay dense (the order lrc_ffn_select_channels returns, applied by the caller to
+ * the rows of W_gate, W_up and the columns of W_down; a permutation of the hidden channels
+ * leaves the FFN unchanged):
+ *   y = sum over low-rank channels (as lrc_lowrank_ffn, with d_ff = n_lr)
+ *     + Wd_dense (SiLU(Wg_dense x) * (Wu_dense x)),
+ * every dense matrix int8 with one fp32 scale per row: q_gd, q_ud: n_dense x d (scales
+ * s_gd, s_ud [n_dense]); q_dd: d x n_dense, W_down's dense columns as rows (scales s_dd[d]).
+ * n_lr = 0 (no factors needed) or n_dense = 0 (no dense matrices needed) are allowed,
+ * not both.  d and n_dense multiples of 16; x and the dense int8 matrices 16-byte aligned;
+ * the low-rank arguments as lrc_lowrank_ffn requires.  Sums fp32, order fixed.
+ */
+lrc_status lrc_hybrid_ffn(const float* x, int64_t n_tok, int64_t d, int64_t n_lr, const int8_t* q_rg,
+                          const float* s_rg, const int8_t* q_lg, const float* s_lg, int64_t rg, const int8_t* q_ru,
+                          const float* s_ru, const int8_t* q_lu, const float* s_lu, int64_t ru, const int8_t* q_rdt,
+                          const float* s_rd, const int8_t* q_ld, const float* s_ld, int64_t rd, int64_t n_dense,
+                          const int8_t* q_gd, const float* s_gd, const int8_t* q_ud, const float* s_ud,
+                          const int8_t* q_dd, const float* s_dd, float* y, void* ws, size_t ws_bytes, void* stream);
+size_t lrc_hybrid_ffn_workspace(int64_t n_tok, int64_t n_lr, int64_t rg, int64_t ru, int64_t rd, int64_t n_dense);
+
+/*
  * Measurement support (benchmarks and profilers; not needed for results).
  * Between lrc_profile_start and lrc_profile_stop every launch of an instrumented kernel
  * is bracketed by two HIP events recorded on the stream it runs on, and the work it

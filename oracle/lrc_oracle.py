@@ -42,7 +42,7 @@ __all__ = [
     "truncated_svd", "canonical_signs", "back_map", "whiten_decompose",
     "fisher_scores", "kfac_scores", "allocation_keys", "allocate", "kfac_loss",
     "unirank_scores", "swift_layer_scores", "hadamard_rotation", "rotate_factors", "rtn_rows",
-    "silu", "lowrank_ffn", "ffn_channel_errors", "select_channels",
+    "silu", "lowrank_ffn", "hybrid_ffn", "ffn_channel_errors", "select_channels",
 ]
 
 
@@ -389,6 +389,26 @@ def lowrank_ffn(x, gate, up, down):
     xv = np.asarray(x, dtype=np.float64)
     h = silu(apply(gate, xv)) * apply(up, xv)
     return apply(down, h)
+
+
+def hybrid_ffn(x, gate=None, up=None, down=None, dense=None):
+    """Forward pass of an FFN in the hybrid form (LASER, 3. Hybrid SVD-Quantization for
+    FFNs, item "Hybrid architecture"): the selected hidden channels go through the
+    low-rank factors, the rest keep dense (int8, per-row scale) rows.  Reading: the
+    channels are ordered low-rank first; the FFN is the sum of the two channel groups'
+    contributions, y = lowrank_ffn(x, gate, up, down) + Wd_dense (SiLU(Wg_dense x) *
+    (Wu_dense x)).  dense = (q_gd (n_dense x d), s_gd, q_ud, s_ud, q_dd (d x n_dense), s_dd)
+    with each matrix = q * s[:, None]; either group may be absent (None).
+    Returns y: n_tok x d in fp64."""
+    xv = np.asarray(x, dtype=np.float64)
+    y = np.zeros_like(xv)
+    if gate is not None:
+        y = y + lowrank_ffn(xv, gate, up, down)
+    if dense is not None:
+        wg, wu, wd = (np.asarray(dense[i], np.float64) * np.asarray(dense[i + 1], np.float64)[:, None]
+                      for i in (0, 2, 4))
+        y = y + (silu(xv @ wg.T) * (xv @ wu.T)) @ wd.T
+    return y
 
 
 # ---------------------------------------------------------------------------

@@ -160,6 +160,34 @@ def test_lowrank_ffn_validation(lib):
     assert need > 0 and call(a21=need - 1) == EWORKSPACE
 
 
+def test_hybrid_ffn_validation(lib):
+    f = lib.lrc_hybrid_ffn
+    ok = [FAKE, 1, 64, 96, FAKE, FAKE, FAKE, FAKE, 32, FAKE, FAKE, FAKE, FAKE, 32, FAKE, FAKE, FAKE, FAKE, 32, 48,
+          FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None]
+
+    def call(**over):
+        a = list(ok)
+        for i, v in over.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    assert call(a0=None) == EINVAL          # x
+    assert call(a26=None) == EINVAL         # y
+    assert call(a3=0, a19=0) == EINVAL      # no channels at all
+    assert call(a19=40) == EINVAL           # n_dense not a multiple of 16
+    assert call(a2=60) == EINVAL            # d not a multiple of 16
+    assert call(a20=None) == EINVAL         # q_gd with dense channels
+    assert call(a24=ctypes.c_void_p(0x1008)) == EINVAL   # q_dd not 16-byte aligned
+    assert call(a8=20) == EINVAL            # rg not a multiple of 16 (low-rank part)
+    assert call(a1=1 << 20, a19=1 << 12) == EINVAL       # n_tok * n_dense too large
+    need = lib.lrc_hybrid_ffn_workspace(1, 96, 32, 32, 32, 48)
+    assert need > lib.lrc_lowrank_ffn_workspace(1, 96, 32, 32, 32)
+    assert call(a28=need - 1) == EWORKSPACE
+    # dense only: the factor pointers may be null
+    assert lib.lrc_hybrid_ffn_workspace(1, 0, 0, 0, 0, 48) > 0
+    assert call(a3=0, a4=None, a5=None, a6=None, a7=None, a8=0, a28=0) == EWORKSPACE
+
+
 def test_ffn_select_channels_validation(lib):
     f = lib.lrc_ffn_select_channels
     ok = [FAKE, FAKE, 40, 16, 16, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 16, 100, 0.0, 10, FAKE, FAKE, FAKE, FAKE,

@@ -612,6 +612,40 @@ def test_lowrank_ffn(lrc, n_tok, d, d_ff, rg, ru, rd):
 
 
 
+
+@pytest.mark.parametrize("n_tok,d,n_lr,n_dense,r", [(1, 256, 344, 336, 64), (5, 128, 160, 144, 32),
+                                                    (3, 128, 0, 96, 0), (2, 128, 300, 0, 32),
+                                                    (9, 4096, 5504, 5504, 2048)])
+def test_hybrid_ffn(lrc, n_tok, d, n_lr, n_dense, r):
+    """Hybrid FFN (low-rank channels first, then dense ones) against the fp64 oracle, at
+    the low-rank FFN's bound (4e-4 of max|y|: the dense channels add one more dot product
+    of d terms and one of n_dense terms per output, each with a fixed-order fp32 sum);
+    either group may be empty."""
+    g = torch.Generator().manual_seed(n_lr + 7 * n_dense + n_tok)
+    lr = dn = None
+    if n_lr:
+        gate = (*_ffn_factor(g, r, d), *_ffn_factor(g, n_lr, r))
+        up = (*_ffn_factor(g, r, d), *_ffn_factor(g, n_lr, r))
+        qrd, srd = _ffn_factor(g, r, n_lr)
+        qld, sld = _ffn_factor(g, d, r)
+        lr = (gate, up, (qrd, srd, qld, sld))
+    if n_dense:
+        dn = (*_ffn_factor(g, n_dense, d), *_ffn_factor(g, n_dense, d), *_ffn_factor(g, d, n_dense))
+    x = torch.randn(n_tok, d, generator=g) * 4
+    to = lambda ts: [t.to(dev()) for t in ts]
+    if lr:
+        gate, up, (qrd, srd, qld, sld) = lr
+        args = (to(gate), to(up), [qrd.t().contiguous().to(dev()), srd.to(dev()), qld.to(dev()), sld.to(dev())])
+    else:
+        args = (None, None, None)
+    y = lrc.lrc_hybrid_ffn(x.to(dev()), *args, dense=to(dn) if dn else None)
+    npy = lambda ts: [t.numpy() for t in ts]
+    ref = oracle.hybrid_ffn(x.numpy(), *(npy(f) for f in lr) if lr else (None, None, None),
+                            dense=npy(dn) if dn else None)
+    err = np.abs(to_np(y) - ref).max() / np.abs(ref).max()
+    assert err < 4e-4, err
+
+
 # ----------------------------------------------------------------------------- FFN channel selection
 def _ffn_sel_inputs(d_ff, d, r, n, seed, dup=False):
     """Seeded gate/up weights, a power-law calibration stream and the oracle's own rank-r

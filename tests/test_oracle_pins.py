@@ -432,6 +432,41 @@ def test_lowrank_ffn_equals_the_dense_ffn_of_the_product():
     np.testing.assert_allclose(oracle.lowrank_ffn(x, g, u, dn), want, rtol=1e-12, atol=1e-12)
 
 
+def test_hybrid_ffn_equals_the_dense_ffn_of_the_assembled_weights():
+    """Hybrid form: the full weights are assembled channel by channel (rows of W_gate and
+    W_up, columns of W_down: low-rank channels from L R, dense ones from q * s), and the
+    plain dense SwiGLU FFN of those weights, token by token, must equal the hybrid
+    forward; with either group empty it reduces to the other one alone."""
+    rng = np.random.default_rng(6)
+    d, n_lr, n_dn, r = 10, 7, 5, 3
+    g = (*_int8_factor(rng, r, d), *_int8_factor(rng, n_lr, r))
+    u = (*_int8_factor(rng, r, d), *_int8_factor(rng, n_lr, r))
+    dn = (*_int8_factor(rng, r, n_lr), *_int8_factor(rng, d, r))
+    dense = (*_int8_factor(rng, n_dn, d), *_int8_factor(rng, n_dn, d), *_int8_factor(rng, d, n_dn))
+
+    def lr(f):
+        return (f[2].astype(np.float64) * f[3][:, None]) @ (f[0].astype(np.float64) * f[1][:, None])
+
+    def rows(q, s):
+        return q.astype(np.float64) * s.astype(np.float64)[:, None]
+
+    wg = np.vstack([lr(g), rows(dense[0], dense[1])])
+    wu = np.vstack([lr(u), rows(dense[2], dense[3])])
+    wd = np.hstack([lr(dn), rows(dense[4], dense[5])])
+    x = rng.standard_normal((4, d))
+    want = np.zeros((4, d))
+    for t in range(4):
+        zg, zu = wg @ x[t], wu @ x[t]
+        want[t] = wd @ np.array([z / (1.0 + math.exp(-z)) * v for z, v in zip(zg, zu)])
+    np.testing.assert_allclose(oracle.hybrid_ffn(x, g, u, dn, dense), want, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(oracle.hybrid_ffn(x, g, u, dn, None), oracle.lowrank_ffn(x, g, u, dn), rtol=1e-14)
+    only_dense = np.zeros((4, d))
+    for t in range(4):
+        zg, zu = rows(dense[0], dense[1]) @ x[t], rows(dense[2], dense[3]) @ x[t]
+        only_dense[t] = rows(dense[4], dense[5]) @ (zg / (1.0 + np.exp(-zg)) * zu)
+    np.testing.assert_allclose(oracle.hybrid_ffn(x, dense=dense), only_dense, rtol=1e-12, atol=1e-12)
+
+
 def test_silu_values():
     np.testing.assert_allclose(oracle.silu([0.0, 1.0, -1.0, 30.0]),
                                [0.0, 0.7310585786300049, -0.2689414213699951, 30.0], rtol=1e-12)
