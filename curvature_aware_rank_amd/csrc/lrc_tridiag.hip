@@ -1817,7 +1817,7 @@ lrc_status tridiag_eig(hipStream_t st, double* A, int64_t k, int64_t lda, int64_
     LRC_LAUNCHED();
   }
   {
-    ProfScope scope("tri_inviter_b_kernel", st, 0.0, 0.0);
+    ProfScope scope("tri_inviter_u_o_s_kernels", st, 0.0, 0.0);  // the four solve and orthogonalisation launches together
     tri_inviter_u_kernel<<<unsigned(ncols), 64, 0, st>>>(n, ncols, w.flag, w.U, w.Z, w.nrm);
     LRC_LAUNCHED();
     tri_inviter_o_kernel<<<unsigned(ncols), 64, 0, st>>>(n, ncols, 0, w.clen, w.flag, w.Z, w.nrm, w.scl);
