@@ -12,7 +12,7 @@
 //   2. for a chunk of hidden channels: expand both latents (rows of L_gate, L_up),
 //      h = SiLU(gate) * up in LDS, and its share of R_down h (rows of R_down^T), written
 //      as per-chunk partial latents
-//   3. latent_d = sum of the partials in chunk order, times R_down's row scales
+//   3. latent_d = sum of the partials in a fixed order, times R_down's row scales
 //   4. y = L_down latent_d                              (one wave per output row)
 // Tokens are handled TG at a time so every weight piece is dequantised once per group.
 #include "lrc_internal.h"
@@ -22,7 +22,11 @@ namespace {
 
 constexpr int FT = 256;      // threads per workgroup
 constexpr int TG = 4;        // tokens per group
-constexpr int HC = 256;      // hidden-channel chunks (workgroups of the expansion kernel)
+// hidden-channel chunks (workgroups of the expansion kernel): several workgroups per CU so
+// that enough weight loads are in flight; each chunk writes an n_tok x r_down partial, so
+// fewer chunks when several tokens share the pass
+constexpr int HC1 = 1024;    // one token
+constexpr int HCN = 512;     // token groups
 
 __device__ __forceinline__ float wave_sumf(float v) {
 #pragma unroll
@@ -57,17 +61,26 @@ __global__ __launch_bounds__(FT) void rows_gemv_kernel(const int8_t* __restrict_
   const int ld_out = first ? rows0 : rows1;
   for (int t0 = 0; t0 < n_tok; t0 += TG) {
     float acc[TG] = {0.f, 0.f, 0.f, 0.f};
-    for (int j0 = lane * 16; j0 < n; j0 += 64 * 16) {
-      float w[16];
-      unpack16(*reinterpret_cast<const uint4*>(q + j0), w);
+    for (int jb = lane * 16; jb < n; jb += 4 * 64 * 16) {
+      uint4 wq[4];   // the lane's next four 16-byte pieces, all in flight before any use
 #pragma unroll
-      for (int t = 0; t < TG; ++t) {
-        if (t0 + t < n_tok) {
-          const float4* x = reinterpret_cast<const float4*>(v + int64_t(t0 + t) * n + j0);
+      for (int p = 0; p < 4; ++p) wq[p] = *reinterpret_cast<const uint4*>(q + min(jb + p * 1024, n - 16));
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const float4 xv = x[c];
-            acc[t] += w[4 * c] * xv.x + w[4 * c + 1] * xv.y + w[4 * c + 2] * xv.z + w[4 * c + 3] * xv.w;
+      for (int p = 0; p < 4; ++p) {
+        const int j0 = jb + p * 1024;
+        if (j0 < n) {
+          float w[16];
+          unpack16(wq[p], w);
+#pragma unroll
+          for (int t = 0; t < TG; ++t) {
+            if (t0 + t < n_tok) {
+              const float4* x = reinterpret_cast<const float4*>(v + int64_t(t0 + t) * n + j0);
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                const float4 xv = x[c];
+                acc[t] += w[4 * c] * xv.x + w[4 * c + 1] * xv.y + w[4 * c + 2] * xv.z + w[4 * c + 3] * xv.w;
+              }
+            }
           }
         }
       }
@@ -83,6 +96,11 @@ __global__ __launch_bounds__(FT) void rows_gemv_kernel(const int8_t* __restrict_
   }
 }
 
+// LDS slot of latent index k: one spare slot after every 16, so the 16 lanes of a row,
+// which start 16 indices apart, fall in distinct banks (unpadded, the four-token layout
+// puts all 16 on one bank group)
+__host__ __device__ __forceinline__ int64_t pslot(int64_t k) { return k + (k >> 4); }
+
 // Hidden channels [b J, b J + J): gate/up expansion, SwiGLU, and the chunk's partial of
 // R_down h: pd[b][t][k] = sum_j q_rdt[j][k] h[t][j] (R_down's row scales come later).
 // NG tokens per group (1 or TG); with TG the latents sit in LDS token-interleaved
@@ -96,8 +114,8 @@ __global__ __launch_bounds__(FT) void swiglu_down_kernel(const int8_t* __restric
                                                          int n_tok, float* __restrict__ pd) {
   extern __shared__ float sh[];
   float* lg = sh;                 // [k][NG]
-  float* lu = lg + NG * rg;       // [k][NG]
-  float* hh = lu + NG * ru;       // [NG][J]
+  float* lu = lg + NG * pslot(rg);   // [slot(k)][NG]
+  float* hh = lu + NG * pslot(ru);   // [NG][J]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j0 = blockIdx.x * J;
   const int jn = min(J, d_ff - j0);
@@ -106,11 +124,11 @@ __global__ __launch_bounds__(FT) void swiglu_down_kernel(const int8_t* __restric
     __syncthreads();
     for (int i = tid; i < NG * rg; i += FT) {
       const int t = i / rg, k = i % rg;
-      lg[k * NG + t] = t < nt ? latg[int64_t(t0 + t) * rg + k] : 0.f;
+      lg[pslot(k) * NG + t] = t < nt ? latg[int64_t(t0 + t) * rg + k] : 0.f;
     }
     for (int i = tid; i < NG * ru; i += FT) {
       const int t = i / ru, k = i % ru;
-      lu[k * NG + t] = t < nt ? latu[int64_t(t0 + t) * ru + k] : 0.f;
+      lu[pslot(k) * NG + t] = t < nt ? latu[int64_t(t0 + t) * ru + k] : 0.f;
     }
     __syncthreads();
     // expansion: a wave takes four hidden rows at a time, 16 lanes per row (lanes split
@@ -135,11 +153,11 @@ __global__ __launch_bounds__(FT) void swiglu_down_kernel(const int8_t* __restric
             unpack16(wq[c], w);
             if constexpr (NG == 1) {
 #pragma unroll
-              for (int e = 0; e < 16; ++e) g[0] += w[e] * lg[k + e];
+              for (int e = 0; e < 16; ++e) g[0] += w[e] * lg[pslot(k) + e];
             } else {
 #pragma unroll
               for (int e = 0; e < 16; ++e) {
-                const float4 lv = *reinterpret_cast<const float4*>(lg + (k + e) * NG);
+                const float4 lv = *reinterpret_cast<const float4*>(lg + (pslot(k) + e) * NG);
                 g[0] += w[e] * lv.x;
                 g[1] += w[e] * lv.y;
                 g[2] += w[e] * lv.z;
@@ -164,11 +182,11 @@ __global__ __launch_bounds__(FT) void swiglu_down_kernel(const int8_t* __restric
             unpack16(wq[c], w);
             if constexpr (NG == 1) {
 #pragma unroll
-              for (int e = 0; e < 16; ++e) u[0] += w[e] * lu[k + e];
+              for (int e = 0; e < 16; ++e) u[0] += w[e] * lu[pslot(k) + e];
             } else {
 #pragma unroll
               for (int e = 0; e < 16; ++e) {
-                const float4 lv = *reinterpret_cast<const float4*>(lu + (k + e) * NG);
+                const float4 lv = *reinterpret_cast<const float4*>(lu + (pslot(k) + e) * NG);
                 u[0] += w[e] * lv.x;
                 u[1] += w[e] * lv.y;
                 u[2] += w[e] * lv.z;
@@ -238,17 +256,18 @@ __global__ __launch_bounds__(FT) void swiglu_dense_kernel(float* __restrict__ g,
   if (i < cnt) g[i] = silu(g[i]) * u[i];
 }
 
-// latent_d[t][k] = s_rd[k] * sum over chunks b of pd[b][t][k]: four threads per output,
-// each summing a quarter of the chunks in order (16 loads in flight), quarters added in
-// order
+// latent_d[t][k] = s_rd[k] * sum over chunks b of pd[b][t][k]: a workgroup takes RO
+// consecutive outputs and RS slices of the chunks, each thread summing its slice in chunk
+// order (16 loads in flight), the slices then added in slice order
+constexpr int RO = 16, RS = FT / RO;
 __global__ __launch_bounds__(FT) void latent_reduce_kernel(const float* __restrict__ pd, int nb, int n_tok, int rd,
                                                            const float* __restrict__ srd, float* __restrict__ latd) {
-  __shared__ float part[4][FT / 4];
-  const int qtr = threadIdx.x >> 6, o = threadIdx.x & 63;
-  const int64_t i = int64_t(blockIdx.x) * (FT / 4) + o;
+  __shared__ float part[RS][RO];
+  const int sl = threadIdx.x / RO, o = threadIdx.x % RO;
+  const int64_t i = int64_t(blockIdx.x) * RO + o;
   const int64_t tot = int64_t(n_tok) * rd;
   const int64_t ic = min(i, tot - 1);
-  const int per = (nb + 3) / 4, b0 = qtr * per, b1 = min(nb, b0 + per);
+  const int per = (nb + RS - 1) / RS, b0 = min(nb, sl * per), b1 = min(nb, b0 + per);
   float s = 0.f;
   for (int b = b0; b < b1; b += 16) {
     float v[16];
@@ -257,9 +276,13 @@ __global__ __launch_bounds__(FT) void latent_reduce_kernel(const float* __restri
 #pragma unroll
     for (int u = 0; u < 16; ++u) s += b + u < b1 ? v[u] : 0.f;
   }
-  part[qtr][o] = s;
+  part[sl][o] = s;
   __syncthreads();
-  if (qtr == 0 && i < tot) latd[i] = srd[int(i % rd)] * (((part[0][o] + part[1][o]) + part[2][o]) + part[3][o]);
+  if (sl == 0 && i < tot) {
+    float t = part[0][o];
+    for (int q = 1; q < RS; ++q) t += part[q][o];
+    latd[i] = srd[int(i % rd)] * t;
+  }
 }
 
 }  // namespace
@@ -279,13 +302,13 @@ FfnWs carve_ffn(Carve& cv, int64_t n_tok, int64_t rg, int64_t ru, int64_t rd, in
   w.latd = cv.take<float>(size_t(n_tok * rd));
   return w;
 }
-int64_t ffn_chunk(int64_t d_ff) { return cdiv(d_ff, HC); }
+int64_t ffn_chunk(int64_t d_ff, int64_t n_tok) { return cdiv(d_ff, n_tok == 1 ? HC1 : HCN); }
 }  // namespace
 
 extern "C" size_t lrc_lowrank_ffn_workspace(int64_t n_tok, int64_t d_ff, int64_t rg, int64_t ru, int64_t rd) {
   if (n_tok <= 0 || d_ff <= 0 || rg <= 0 || ru <= 0 || rd <= 0) return 0;
   Carve cv(nullptr);
-  carve_ffn(cv, n_tok, rg, ru, rd, cdiv(d_ff, ffn_chunk(d_ff)));
+  carve_ffn(cv, n_tok, rg, ru, rd, cdiv(d_ff, ffn_chunk(d_ff, n_tok)));
   return cv.bytes();
 }
 
@@ -306,15 +329,15 @@ extern "C" lrc_status lrc_lowrank_ffn(const float* x, int64_t n_tok, int64_t d, 
   if (n_tok <= 0 || d <= 0 || d_ff <= 0 || rg <= 0 || ru <= 0 || rd <= 0) return LRC_EINVAL;
   if (d % 16 || rg % 16 || ru % 16 || rd % 16) return LRC_EINVAL;
   if (n_tok > (int64_t(1) << 20) || d > (int64_t(1) << 24) || d_ff > (int64_t(1) << 24)) return LRC_EINVAL;
-  const int64_t J = ffn_chunk(d_ff), nb = cdiv(d_ff, J);
-  const size_t lds = sizeof(float) * size_t(TG * (rg + ru) + TG * J);
+  const int64_t J = ffn_chunk(d_ff, n_tok), nb = cdiv(d_ff, J);
+  const size_t lds = sizeof(float) * size_t(TG * (pslot(rg) + pslot(ru)) + TG * J);
   if (lds > 160 * 1024) return LRC_EINVAL;   // both latents of a token group must fit in LDS
   const size_t need = lrc_lowrank_ffn_workspace(n_tok, d_ff, rg, ru, rd);
   if (ws == nullptr || ws_bytes < need) return LRC_EWORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   // the expansion kernel's LDS (both latents of a token group) may exceed the default cap
   const int ng = n_tok == 1 ? 1 : TG;
-  const size_t lds_used = sizeof(float) * size_t(ng * (rg + ru) + ng * J);
+  const size_t lds_used = sizeof(float) * size_t(ng * (pslot(rg) + pslot(ru)) + ng * J);
   if (lds_used > 64 * 1024)
     LRC_HIP(hipFuncSetAttribute(ng == 1 ? reinterpret_cast<const void*>(&swiglu_down_kernel<1>)
                                         : reinterpret_cast<const void*>(&swiglu_down_kernel<TG>),
@@ -335,7 +358,7 @@ extern "C" lrc_status lrc_lowrank_ffn(const float* x, int64_t n_tok, int64_t d, 
                                                                w.latu, q_rdt, int(rd), int(d_ff), int(J), int(n_tok),
                                                                w.pd);
   LRC_LAUNCHED();
-  latent_reduce_kernel<<<unsigned(cdiv(n_tok * rd, FT / 4)), FT, 0, st>>>(w.pd, int(nb), int(n_tok), int(rd), s_rd,
+  latent_reduce_kernel<<<unsigned(cdiv(n_tok * rd, RO)), FT, 0, st>>>(w.pd, int(nb), int(n_tok), int(rd), s_rd,
                                                                           w.latd);
   LRC_LAUNCHED();
   rows_gemv_kernel<<<unsigned(cdiv(d, FT / 64)), FT, 0, st>>>(q_ld, s_ld, int(d), nullptr, nullptr, 0, int(rd), w.latd,
@@ -356,7 +379,7 @@ struct HybWs {
 };
 HybWs carve_hyb(Carve& cv, int64_t n_tok, int64_t n_lr, int64_t rg, int64_t ru, int64_t rd, int64_t n_dense) {
   HybWs w{};
-  if (n_lr > 0) w.lr = carve_ffn(cv, n_tok, rg, ru, rd, cdiv(n_lr, ffn_chunk(n_lr)));
+  if (n_lr > 0) w.lr = carve_ffn(cv, n_tok, rg, ru, rd, cdiv(n_lr, ffn_chunk(n_lr, n_tok)));
   if (n_dense > 0) {
     w.gd = cv.take<float>(size_t(n_tok * n_dense));
     w.ud = cv.take<float>(size_t(n_tok * n_dense));
