@@ -22,11 +22,10 @@ namespace {
 
 constexpr int FT = 256;      // threads per workgroup
 constexpr int TG = 4;        // tokens per group
-// hidden-channel chunks (workgroups of the expansion kernel): several workgroups per CU so
-// that enough weight loads are in flight; each chunk writes an n_tok x r_down partial, so
-// fewer chunks when several tokens share the pass
-constexpr int HC1 = 1024;    // one token
-constexpr int HCN = 512;     // token groups
+// hidden-channel chunks (workgroups of the expansion kernel): two workgroups of 8 waves per
+// CU keep enough weight loads in flight, while each chunk's n_tok x r_down partial stays a
+// small share of the traffic
+constexpr int HC = 512;
 
 __device__ __forceinline__ float wave_sumf(float v) {
 #pragma unroll
@@ -105,92 +104,65 @@ __host__ __device__ __forceinline__ int64_t pslot(int64_t k) { return k + (k >> 
 // R_down h: pd[b][t][k] = sum_j q_rdt[j][k] h[t][j] (R_down's row scales come later).
 // NG tokens per group (1 or TG); with TG the latents sit in LDS token-interleaved
 // ([k][t]), so one 16-byte read serves the four tokens of a weight element.
+constexpr int FE = 512;      // threads per workgroup of the expansion kernel
+constexpr int DK = FE / 2 * 8;   // down-projection outputs per pass (8 per thread of a half)
+
 template <int NG>
-__global__ __launch_bounds__(FT) void swiglu_down_kernel(const int8_t* __restrict__ qlg, const float* __restrict__ slg,
+__global__ __launch_bounds__(FE) void swiglu_down_kernel(const int8_t* __restrict__ qlg, const float* __restrict__ slg,
                                                          const int8_t* __restrict__ qlu, const float* __restrict__ slu,
                                                          int rg, int ru, const float* __restrict__ latg,
                                                          const float* __restrict__ latu,
                                                          const int8_t* __restrict__ qrdt, int rd, int d_ff, int J,
                                                          int n_tok, float* __restrict__ pd) {
   extern __shared__ float sh[];
-  float* lg = sh;                 // [k][NG]
-  float* lu = lg + NG * pslot(rg);   // [slot(k)][NG]
-  float* hh = lu + NG * pslot(ru);   // [NG][J]
+  // one latent at a time in LDS ([slot(k)][NG]): the gate pass, then the up pass over the
+  // same region, so the footprint is one latent and several workgroups fit on a CU
+  float* lat = sh;                             // also the down pass's exchange buffer [NG][DK]
+  float* gg = lat + NG * max(int(pslot(max(rg, ru))), DK);   // [NG][J] scaled gate pre-activations
+  float* hh = gg + NG * J;                     // [NG][J]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j0 = blockIdx.x * J;
   const int jn = min(J, d_ff - j0);
-  for (int t0 = 0; t0 < n_tok; t0 += NG) {
-    const int nt = min(NG, n_tok - t0);
+  const int sub = lane >> 4, sl = lane & 15;
+  // one expansion pass: for the chunk's rows j, out(j, t) = row j of q (r int8) . latent t,
+  // a wave taking four rows at a time with 16 lanes per row (lanes split the latent index),
+  // every weight load of the four rows issued before any use; fin(jj, t, sum) stores it
+  auto expand = [&](const int8_t* __restrict__ q, int r, const float* __restrict__ src, int nt, int t0,
+                    auto fin) {
     __syncthreads();
-    for (int i = tid; i < NG * rg; i += FT) {
-      const int t = i / rg, k = i % rg;
-      lg[pslot(k) * NG + t] = t < nt ? latg[int64_t(t0 + t) * rg + k] : 0.f;
-    }
-    for (int i = tid; i < NG * ru; i += FT) {
-      const int t = i / ru, k = i % ru;
-      lu[pslot(k) * NG + t] = t < nt ? latu[int64_t(t0 + t) * ru + k] : 0.f;
+    for (int i = tid; i < NG * r; i += FE) {
+      const int t = i / r, k = i % r;
+      lat[pslot(k) * NG + t] = t < nt ? src[int64_t(t0 + t) * r + k] : 0.f;
     }
     __syncthreads();
-    // expansion: a wave takes four hidden rows at a time, 16 lanes per row (lanes split
-    // the latent index), every weight load of the four rows issued before any use
-    const int sub = lane >> 4, sl = lane & 15;
-    for (int jb = wave * 4; jb < jn; jb += FT / 16) {
+    for (int jb = wave * 4; jb < jn; jb += FE / 16) {
       const int jj = jb + sub;
       const int j = j0 + min(jj, jn - 1);
-      float g[TG] = {0.f, 0.f, 0.f, 0.f}, u[TG] = {0.f, 0.f, 0.f, 0.f};
-      for (int k0 = sl * 16; k0 < rg; k0 += 16 * 16 * 4) {
+      float a[TG] = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = sl * 16; k0 < r; k0 += 16 * 16 * 4) {
         uint4 wq[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const int k = min(k0 + c * 256, rg - 16);
-          wq[c] = *reinterpret_cast<const uint4*>(qlg + int64_t(j) * rg + k);
+          const int k = min(k0 + c * 256, r - 16);
+          wq[c] = *reinterpret_cast<const uint4*>(q + int64_t(j) * r + k);
         }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int k = k0 + c * 256;
-          if (k < rg) {
+          if (k < r) {
             float w[16];
             unpack16(wq[c], w);
             if constexpr (NG == 1) {
 #pragma unroll
-              for (int e = 0; e < 16; ++e) g[0] += w[e] * lg[pslot(k) + e];
+              for (int e = 0; e < 16; ++e) a[0] += w[e] * lat[pslot(k) + e];
             } else {
 #pragma unroll
               for (int e = 0; e < 16; ++e) {
-                const float4 lv = *reinterpret_cast<const float4*>(lg + (pslot(k) + e) * NG);
-                g[0] += w[e] * lv.x;
-                g[1] += w[e] * lv.y;
-                g[2] += w[e] * lv.z;
-                g[3] += w[e] * lv.w;
-              }
-            }
-          }
-        }
-      }
-      for (int k0 = sl * 16; k0 < ru; k0 += 16 * 16 * 4) {
-        uint4 wq[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int k = min(k0 + c * 256, ru - 16);
-          wq[c] = *reinterpret_cast<const uint4*>(qlu + int64_t(j) * ru + k);
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int k = k0 + c * 256;
-          if (k < ru) {
-            float w[16];
-            unpack16(wq[c], w);
-            if constexpr (NG == 1) {
-#pragma unroll
-              for (int e = 0; e < 16; ++e) u[0] += w[e] * lu[pslot(k) + e];
-            } else {
-#pragma unroll
-              for (int e = 0; e < 16; ++e) {
-                const float4 lv = *reinterpret_cast<const float4*>(lu + (pslot(k) + e) * NG);
-                u[0] += w[e] * lv.x;
-                u[1] += w[e] * lv.y;
-                u[2] += w[e] * lv.z;
-                u[3] += w[e] * lv.w;
+                const float4 lv = *reinterpret_cast<const float4*>(lat + (pslot(k) + e) * NG);
+                a[0] += w[e] * lv.x;
+                a[1] += w[e] * lv.y;
+                a[2] += w[e] * lv.z;
+                a[3] += w[e] * lv.w;
               }
             }
           }
@@ -198,30 +170,40 @@ __global__ __launch_bounds__(FT) void swiglu_down_kernel(const int8_t* __restric
       }
 #pragma unroll
       for (int t = 0; t < NG; ++t) {
-        float gs = g[t], us = u[t];
+        float s = a[t];
 #pragma unroll
-        for (int o = 8; o > 0; o >>= 1) {   // sum over the row's 16 lanes
-          gs += __shfl_xor(gs, o);
-          us += __shfl_xor(us, o);
-        }
-        if (sl == 0 && jj < jn) hh[t * J + jj] = silu(slg[j] * gs) * (slu[j] * us);
+        for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o);   // sum over the row's 16 lanes
+        if (sl == 0 && jj < jn) fin(jj, j, t, s);
       }
     }
+  };
+  for (int t0 = 0; t0 < n_tok; t0 += NG) {
+    const int nt = min(NG, n_tok - t0);
+    expand(qlg, rg, latg, nt, t0, [&](int jj, int j, int t, float s) { gg[t * J + jj] = slg[j] * s; });
+    expand(qlu, ru, latu, nt, t0,
+           [&](int jj, int j, int t, float s) { hh[t * J + jj] = silu(gg[t * J + jj]) * (slu[j] * s); });
     __syncthreads();
-    for (int kb = tid * 8; kb < rd; kb += FT * 8) {
+    // R_down's share: the two halves of the workgroup take the two halves of the chunk's
+    // channels for the same 8 outputs per thread; the upper half's sums pass through LDS
+    // and are added to the lower half's
+    const int half = tid / (FE / 2), ht = tid % (FE / 2);
+    const int jh = (jn + 1) / 2, r0 = half ? jh : 0, r1 = half ? jn : jh;
+    for (int kp = 0; kp < rd; kp += DK) {
+      const int kb = kp + ht * 8;
+      const bool act = kb < rd;
       float acc[NG][8];
 #pragma unroll
       for (int t = 0; t < NG; ++t)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[t][e] = 0.f;
-      for (int jb = 0; jb < jn; jb += 8) {
+      for (int jb = r0; act && jb < r1; jb += 8) {
         uint2 w8[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c)
-          w8[c] = *reinterpret_cast<const uint2*>(qrdt + int64_t(j0 + min(jb + c, jn - 1)) * rd + kb);
+          w8[c] = *reinterpret_cast<const uint2*>(qrdt + int64_t(j0 + min(jb + c, r1 - 1)) * rd + kb);
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          if (jb + c < jn) {
+          if (jb + c < r1) {
             const uint32_t wu[2] = {w8[c].x, w8[c].y};
             float w[8];
 #pragma unroll
@@ -237,14 +219,27 @@ __global__ __launch_bounds__(FT) void swiglu_down_kernel(const int8_t* __restric
           }
         }
       }
+      if (half == 1 && act) {
 #pragma unroll
-      for (int t = 0; t < NG; ++t) {
-        if (t < nt) {
-          float4* dst = reinterpret_cast<float4*>(pd + (int64_t(blockIdx.x) * n_tok + t0 + t) * rd + kb);
-          dst[0] = make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
-          dst[1] = make_float4(acc[t][4], acc[t][5], acc[t][6], acc[t][7]);
+        for (int t = 0; t < NG; ++t)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) lat[t * DK + ht * 8 + e] = acc[t][e];
+      }
+      __syncthreads();
+      if (half == 0 && act) {
+#pragma unroll
+        for (int t = 0; t < NG; ++t) {
+          if (t < nt) {
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = acc[t][e] + lat[t * DK + ht * 8 + e];
+            float4* dst = reinterpret_cast<float4*>(pd + (int64_t(blockIdx.x) * n_tok + t0 + t) * rd + kb);
+            dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+            dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+          }
         }
       }
+      __syncthreads();
     }
   }
 }
@@ -302,13 +297,13 @@ FfnWs carve_ffn(Carve& cv, int64_t n_tok, int64_t rg, int64_t ru, int64_t rd, in
   w.latd = cv.take<float>(size_t(n_tok * rd));
   return w;
 }
-int64_t ffn_chunk(int64_t d_ff, int64_t n_tok) { return cdiv(d_ff, n_tok == 1 ? HC1 : HCN); }
+int64_t ffn_chunk(int64_t d_ff) { return cdiv(d_ff, HC); }
 }  // namespace
 
 extern "C" size_t lrc_lowrank_ffn_workspace(int64_t n_tok, int64_t d_ff, int64_t rg, int64_t ru, int64_t rd) {
   if (n_tok <= 0 || d_ff <= 0 || rg <= 0 || ru <= 0 || rd <= 0) return 0;
   Carve cv(nullptr);
-  carve_ffn(cv, n_tok, rg, ru, rd, cdiv(d_ff, ffn_chunk(d_ff, n_tok)));
+  carve_ffn(cv, n_tok, rg, ru, rd, cdiv(d_ff, ffn_chunk(d_ff)));
   return cv.bytes();
 }
 
@@ -329,15 +324,15 @@ extern "C" lrc_status lrc_lowrank_ffn(const float* x, int64_t n_tok, int64_t d, 
   if (n_tok <= 0 || d <= 0 || d_ff <= 0 || rg <= 0 || ru <= 0 || rd <= 0) return LRC_EINVAL;
   if (d % 16 || rg % 16 || ru % 16 || rd % 16) return LRC_EINVAL;
   if (n_tok > (int64_t(1) << 20) || d > (int64_t(1) << 24) || d_ff > (int64_t(1) << 24)) return LRC_EINVAL;
-  const int64_t J = ffn_chunk(d_ff, n_tok), nb = cdiv(d_ff, J);
-  const size_t lds = sizeof(float) * size_t(TG * (pslot(rg) + pslot(ru)) + TG * J);
+  const int64_t J = ffn_chunk(d_ff), nb = cdiv(d_ff, J);
+  const size_t lds = sizeof(float) * size_t(TG * std::max(pslot(std::max(rg, ru)), int64_t(DK)) + 2 * TG * J);
   if (lds > 160 * 1024) return LRC_EINVAL;   // both latents of a token group must fit in LDS
   const size_t need = lrc_lowrank_ffn_workspace(n_tok, d_ff, rg, ru, rd);
   if (ws == nullptr || ws_bytes < need) return LRC_EWORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   // the expansion kernel's LDS (both latents of a token group) may exceed the default cap
   const int ng = n_tok == 1 ? 1 : TG;
-  const size_t lds_used = sizeof(float) * size_t(ng * (pslot(rg) + pslot(ru)) + ng * J);
+  const size_t lds_used = sizeof(float) * size_t(ng * std::max(pslot(std::max(rg, ru)), int64_t(DK)) + 2 * ng * J);
   if (lds_used > 64 * 1024)
     LRC_HIP(hipFuncSetAttribute(ng == 1 ? reinterpret_cast<const void*>(&swiglu_down_kernel<1>)
                                         : reinterpret_cast<const void*>(&swiglu_down_kernel<TG>),
@@ -351,10 +346,10 @@ extern "C" lrc_status lrc_lowrank_ffn(const float* x, int64_t n_tok, int64_t d, 
                                                                    int(n_tok), w.latg, w.latu);
   LRC_LAUNCHED();
   if (ng == 1)
-    swiglu_down_kernel<1><<<unsigned(nb), FT, lds_used, st>>>(q_lg, s_lg, q_lu, s_lu, int(rg), int(ru), w.latg, w.latu,
+    swiglu_down_kernel<1><<<unsigned(nb), FE, lds_used, st>>>(q_lg, s_lg, q_lu, s_lu, int(rg), int(ru), w.latg, w.latu,
                                                               q_rdt, int(rd), int(d_ff), int(J), int(n_tok), w.pd);
   else
-    swiglu_down_kernel<TG><<<unsigned(nb), FT, lds_used, st>>>(q_lg, s_lg, q_lu, s_lu, int(rg), int(ru), w.latg,
+    swiglu_down_kernel<TG><<<unsigned(nb), FE, lds_used, st>>>(q_lg, s_lg, q_lu, s_lu, int(rg), int(ru), w.latg,
                                                                w.latu, q_rdt, int(rd), int(d_ff), int(J), int(n_tok),
                                                                w.pd);
   LRC_LAUNCHED();
@@ -379,7 +374,7 @@ struct HybWs {
 };
 HybWs carve_hyb(Carve& cv, int64_t n_tok, int64_t n_lr, int64_t rg, int64_t ru, int64_t rd, int64_t n_dense) {
   HybWs w{};
-  if (n_lr > 0) w.lr = carve_ffn(cv, n_tok, rg, ru, rd, cdiv(n_lr, ffn_chunk(n_lr, n_tok)));
+  if (n_lr > 0) w.lr = carve_ffn(cv, n_tok, rg, ru, rd, cdiv(n_lr, ffn_chunk(n_lr)));
   if (n_dense > 0) {
     w.gd = cv.take<float>(size_t(n_tok * n_dense));
     w.ud = cv.take<float>(size_t(n_tok * n_dense));
