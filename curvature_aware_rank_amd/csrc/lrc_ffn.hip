@@ -42,8 +42,77 @@ __device__ __forceinline__ void unpack16(uint4 w, float (&f)[16]) {
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // out[t][row] = scale[row] * (q[row] . v[t]) for the rows of one or two int8 matrices
-// (rows0 rows of q0, then rows1 rows of q1; each row n int8, n % 16 == 0); one wave per row
-__global__ __launch_bounds__(FT) void rows_gemv_kernel(const int8_t* __restrict__ q0, const float* __restrict__ s0,
+// (rows0 rows of q0, then rows1 rows of q1; each row n int8, n % 16 == 0).  One wave per
+// row, GW / 64 rows per workgroup; the activations of a token group pass through LDS in
+// XC-column chunks, so each is read from L2 once per workgroup rather than once per row.
+// A lane takes 4-byte weight pieces 256 columns apart, eight in flight, and the matching
+// float4 of each token from LDS (consecutive lanes, consecutive 16 bytes: no bank conflicts).
+constexpr int GW = 1024;
+constexpr int XC = 2048;
+__global__ __launch_bounds__(GW) void rows_gemv_kernel(const int8_t* __restrict__ q0, const float* __restrict__ s0,
+                                                       int rows0, const int8_t* __restrict__ q1,
+                                                       const float* __restrict__ s1, int rows1, int n,
+                                                       const float* __restrict__ v, int n_tok,
+                                                       float* __restrict__ out0, float* __restrict__ out1,
+                                                       int accumulate = 0) {
+  __shared__ float4 xs[TG][XC / 4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int row = blockIdx.x * (GW / 64) + (tid >> 6);
+  const bool live = row < rows0 + rows1;   // waves past the last row still join the staging
+  const int rw = live ? row : rows0 + rows1 - 1;
+  const bool first = rw < rows0;
+  const int r = first ? rw : rw - rows0;
+  const int8_t* q = (first ? q0 : q1) + int64_t(r) * n;
+  const float sc = first ? s0[r] : s1[r];
+  float* out = first ? out0 : out1;
+  const int ld_out = first ? rows0 : rows1;
+  for (int t0 = 0; t0 < n_tok; t0 += TG) {
+    float acc[TG] = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < n; c0 += XC) {
+      const int nc4 = min(XC, n - c0) / 4;
+      __syncthreads();
+      for (int i = tid; i < TG * nc4; i += GW) {
+        const int t = i / nc4, k4 = i % nc4;
+        xs[t][k4] = t0 + t < n_tok ? reinterpret_cast<const float4*>(v + int64_t(t0 + t) * n + c0)[k4]
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      __syncthreads();
+      if (live) {
+        uint32_t wq[8];
+#pragma unroll
+        for (int p = 0; p < 8; ++p)
+          wq[p] = *reinterpret_cast<const uint32_t*>(q + c0 + 4 * min(lane + 64 * p, nc4 - 1));
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          const int k4 = lane + 64 * p;
+          if (k4 < nc4) {
+            float w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = float(int8_t(uint8_t(wq[p] >> (8 * e))));
+#pragma unroll
+            for (int t = 0; t < TG; ++t) {
+              const float4 xv = xs[t][k4];
+              acc[t] += w[0] * xv.x + w[1] * xv.y + w[2] * xv.z + w[3] * xv.w;
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < TG; ++t) {
+      const float a = wave_sumf(acc[t]);
+      if (live && lane == 0 && t0 + t < n_tok) {
+        float* o = out + int64_t(t0 + t) * ld_out + r;
+        *o = accumulate ? *o + sc * a : sc * a;
+      }
+    }
+  }
+}
+
+// The same product for a single token: one wave per row, a lane's four 16-byte weight
+// pieces in flight together and the activation read straight from L2 (at one token the
+// re-reads cost less than the loads in flight that LDS staging gives up)
+__global__ __launch_bounds__(FT) void rows_gemv1_kernel(const int8_t* __restrict__ q0, const float* __restrict__ s0,
                                                        int rows0, const int8_t* __restrict__ q1,
                                                        const float* __restrict__ s1, int rows1, int n,
                                                        const float* __restrict__ v, int n_tok,
@@ -93,6 +162,19 @@ __global__ __launch_bounds__(FT) void rows_gemv_kernel(const int8_t* __restrict_
       }
     }
   }
+}
+
+
+// row GEMV launch: the single-token kernel at n_tok == 1, the LDS-staged one otherwise
+void launch_rows_gemv(hipStream_t st, const int8_t* q0, const float* s0, int rows0, const int8_t* q1, const float* s1,
+                      int rows1, int n, const float* v, int n_tok, float* out0, float* out1, int accumulate) {
+  const int rows = rows0 + rows1;
+  if (n_tok == 1)
+    rows_gemv1_kernel<<<unsigned(cdiv(rows, FT / 64)), FT, 0, st>>>(q0, s0, rows0, q1, s1, rows1, n, v, n_tok, out0,
+                                                                     out1, accumulate);
+  else
+    rows_gemv_kernel<<<unsigned(cdiv(rows, GW / 64)), GW, 0, st>>>(q0, s0, rows0, q1, s1, rows1, n, v, n_tok, out0,
+                                                                    out1, accumulate);
 }
 
 // LDS slot of latent index k: one spare slot after every 16, so the 16 lanes of a row,
@@ -342,8 +424,7 @@ extern "C" lrc_status lrc_lowrank_ffn(const float* x, int64_t n_tok, int64_t d, 
   // bytes: every int8 factor once, the activations, the outputs
   const double fb = double(rg + ru) * d + double(d_ff) * (rg + ru) + double(d_ff) * rd + double(d) * rd;
   ProfScope scope("lowrank_ffn", st, 0.0, fb + 4.0 * double(n_tok) * 2 * d);
-  rows_gemv_kernel<<<unsigned(cdiv(rg + ru, FT / 64)), FT, 0, st>>>(q_rg, s_rg, int(rg), q_ru, s_ru, int(ru), int(d), x,
-                                                                   int(n_tok), w.latg, w.latu);
+  launch_rows_gemv(st, q_rg, s_rg, int(rg), q_ru, s_ru, int(ru), int(d), x, int(n_tok), w.latg, w.latu, 0);
   LRC_LAUNCHED();
   if (ng == 1)
     swiglu_down_kernel<1><<<unsigned(nb), FE, lds_used, st>>>(q_lg, s_lg, q_lu, s_lu, int(rg), int(ru), w.latg, w.latu,
@@ -356,8 +437,7 @@ extern "C" lrc_status lrc_lowrank_ffn(const float* x, int64_t n_tok, int64_t d, 
   latent_reduce_kernel<<<unsigned(cdiv(n_tok * rd, RO)), FT, 0, st>>>(w.pd, int(nb), int(n_tok), int(rd), s_rd,
                                                                           w.latd);
   LRC_LAUNCHED();
-  rows_gemv_kernel<<<unsigned(cdiv(d, FT / 64)), FT, 0, st>>>(q_ld, s_ld, int(d), nullptr, nullptr, 0, int(rd), w.latd,
-                                                             int(n_tok), y, nullptr);
+  launch_rows_gemv(st, q_ld, s_ld, int(d), nullptr, nullptr, 0, int(rd), w.latd, int(n_tok), y, nullptr, 0);
   LRC_LAUNCHED();
   return LRC_OK;
 }
@@ -427,15 +507,12 @@ extern "C" lrc_status lrc_hybrid_ffn(const float* x, int64_t n_tok, int64_t d, i
   }
   if (n_dense > 0) {
     ProfScope scope("hybrid_ffn_dense", st, 0.0, 3.0 * double(n_dense) * double(d) + 4.0 * double(n_tok) * 2 * d);
-    rows_gemv_kernel<<<unsigned(cdiv(2 * n_dense, FT / 64)), FT, 0, st>>>(q_gd, s_gd, int(n_dense), q_ud, s_ud,
-                                                                          int(n_dense), int(d), x, int(n_tok), w.gd,
-                                                                          w.ud);
+    launch_rows_gemv(st, q_gd, s_gd, int(n_dense), q_ud, s_ud, int(n_dense), int(d), x, int(n_tok), w.gd, w.ud, 0);
     LRC_LAUNCHED();
     swiglu_dense_kernel<<<unsigned(cdiv(n_tok * n_dense, FT)), FT, 0, st>>>(w.gd, w.ud, n_tok * n_dense);
     LRC_LAUNCHED();
-    rows_gemv_kernel<<<unsigned(cdiv(d, FT / 64)), FT, 0, st>>>(q_dd, s_dd, int(d), nullptr, nullptr, 0,
-                                                               int(n_dense), w.gd, int(n_tok), y, nullptr,
-                                                               n_lr > 0 ? 1 : 0);
+    launch_rows_gemv(st, q_dd, s_dd, int(d), nullptr, nullptr, 0, int(n_dense), w.gd, int(n_tok), y, nullptr,
+                     n_lr > 0 ? 1 : 0);
     LRC_LAUNCHED();
   }
   return LRC_OK;
