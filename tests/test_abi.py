@@ -154,7 +154,7 @@ def test_lowrank_ffn_validation(lib):
     assert call(a8=20) == EINVAL            # rg not a multiple of 16
     assert call(a18=0) == EINVAL            # rd
     assert call(a1=0) == EINVAL             # n_tok
-    assert call(a8=8192, a13=8192) == EINVAL   # latents too large for LDS
+    assert call(a8=10240, a13=10240) == EINVAL   # a latent too large for LDS
     assert call(a4=ctypes.c_void_p(0x1008)) == EINVAL   # q_rg not 16-byte aligned
     need = lib.lrc_lowrank_ffn_workspace(1, 96, 32, 32, 32)
     assert need > 0 and call(a21=need - 1) == EWORKSPACE
