@@ -408,11 +408,11 @@ extern "C" lrc_status lrc_lowrank_ffn(const float* x, int64_t n_tok, int64_t d, 
   if (n_tok > (int64_t(1) << 20) || d > (int64_t(1) << 24) || d_ff > (int64_t(1) << 24)) return LRC_EINVAL;
   const int64_t J = ffn_chunk(d_ff), nb = cdiv(d_ff, J);
   const size_t lds = sizeof(float) * size_t(TG * std::max(pslot(std::max(rg, ru)), int64_t(DK)) + 2 * TG * J);
-  if (lds > 160 * 1024) return LRC_EINVAL;   // both latents of a token group must fit in LDS
+  if (lds > 160 * 1024) return LRC_EINVAL;   // the larger latent of a token group must fit in LDS
   const size_t need = lrc_lowrank_ffn_workspace(n_tok, d_ff, rg, ru, rd);
   if (ws == nullptr || ws_bytes < need) return LRC_EWORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // the expansion kernel's LDS (both latents of a token group) may exceed the default cap
+  // the expansion kernel's LDS (one latent of a token group at a time) may exceed the default cap
   const int ng = n_tok == 1 ? 1 : TG;
   const size_t lds_used = sizeof(float) * size_t(ng * std::max(pslot(std::max(rg, ru)), int64_t(DK)) + 2 * ng * J);
   if (lds_used > 64 * 1024)

@@ -274,7 +274,8 @@ size_t lrc_ffn_select_channels_workspace(int64_t d_ff, int64_t d);
  * down: q_rdt = R_down^T (d_ff x rd int8: row j holds hidden channel j's latent weights),
  *   s_rd[rd] (R_down's row scales), q_ld (d x rd int8), s_ld[d].
  * d, rg, ru, rd multiples of 16; the int8 matrices 16-byte aligned (q_rdt 8-byte);
- * 4 (rg + ru) floats of one token group must fit in LDS (rg + ru <= 8192).
+ * the larger latent of a token group must fit in LDS: 4 * (17/16) * max(rg, ru) + 8 * ceil(d_ff / 512)
+ * floats within 160 KiB (max(rg, ru) up to about 9500).
  * Activations and sums are fp32; the reduction order is fixed.
  */
 lrc_status lrc_lowrank_ffn(const float* x, int64_t n_tok, int64_t d, int64_t d_ff, const int8_t* q_rg,
