@@ -264,7 +264,7 @@ def main():
         cov.zero_()
         lrc.lrc_accumulate_cov(a, cov)
         sig, left, right, info = lrc.lrc_whiten_decompose(w, r, cov, n)
-        scores = lrc.lrc_score_components(sigma=sig, mode="kfac")
+        scores, _ = lrc.lrc_score_components(sigma=sig, mode="kfac")
         return lrc.lrc_allocate_ranks(scores, offs, cost, budget)
 
     for _ in range(args.warmup):

@@ -1,9 +1,15 @@
 """Python binding of liblrc (argument marshalling only).
 
 Every computation runs in the HIP kernels of liblrc.so; this module checks tensor
-shapes and dtypes, allocates device workspace with torch, passes raw device pointers
-and torch's current HIP stream, and turns status codes into exceptions.  There is no
-fallback: if liblrc.so is missing or no GPU is present the calls raise.
+shapes, dtypes and devices, allocates device workspace with torch, passes raw device
+pointers and torch's current HIP stream, and turns status codes into exceptions.  There
+is no fallback: if liblrc.so is missing or no GPU is present the calls raise.
+
+Like the library, the binding never waits for the GPU: failures the kernels find are
+reported in the returned device `info` tensors, which the caller reads after its own
+synchronisation.  Every tensor whose pointer is passed (contiguous copies included) is
+held in a local variable until the C call has returned, so the caching allocator cannot
+hand its memory to another tensor while the enqueued kernels may still read it.
 
 Names match the C ABI in include/lrc.h.
 """
@@ -38,13 +44,13 @@ library_path = os.path.join(_HERE, "liblrc.so")
 _i64, _u32, _sz, _vp, _i32 = ctypes.c_int64, ctypes.c_uint32, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int
 
 _SIGS = {
-    "lrc_accumulate_cov": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _i64, _u32, _vp, _sz, _vp]),
+    "lrc_accumulate_cov": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _i64, _u32, _vp, _vp, _sz, _vp]),
     "lrc_accumulate_cov_workspace": (_sz, [_i32, _i64, _i64, _u32]),
     "lrc_whiten_decompose": (_i32, [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
                                     _i64, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "lrc_whiten_decompose_workspace": (_sz, [_i64, _i64, _i64, _i64, _i32, _i32]),
     "lrc_score_components": (_i32, [_vp, _vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _u32, _i32, _i32,
-                                    _i64, _vp, _vp, _sz, _vp]),
+                                    _i64, _vp, _vp, _vp, _sz, _vp]),
     "lrc_score_components_workspace": (_sz, [_i64, _i64, _i64, _i64, _u32]),
     "lrc_allocate_ranks": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "lrc_allocate_ranks_workspace": (_sz, [_i64, _i64]),
@@ -117,6 +123,25 @@ def _dev(t, name):
         raise ValueError(f"{name} must be a GPU tensor")
 
 
+def _tensor(t, name, dtype, shape, device=None):
+    """Check a GPU tensor's dtype, shape (None entries are free) and device; return it."""
+    _dev(t, name)
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if len(shape) != t.dim() or any(want is not None and want != got for want, got in zip(shape, t.shape)):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    return t
+
+
+def _info(info, device):
+    """An optional caller-given int32 (1,) flag on `device`, or a fresh one set to 0."""
+    if info is None:
+        return torch.zeros(1, dtype=torch.int32, device=device)
+    return _tensor(info, "info", torch.int32, (1,), device)
+
+
 def _workspace(nbytes: int, device):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
@@ -135,30 +160,36 @@ def _rowmajor_ld(t, name):
     return t.stride(0)
 
 
-def lrc_accumulate_cov(A: torch.Tensor, C: torch.Tensor, quant: bool = False) -> None:
-    """C[lower] += sum_t a_t^T a_t over the rows of A (fake-quantised per token if quant)."""
+def lrc_accumulate_cov(A: torch.Tensor, C: torch.Tensor, quant: bool = False, info=None):
+    """C[lower] += sum_t a_t^T a_t over the rows of A (fake-quantised per token if quant).
+
+    info: optional int32 (1,) device flag (sticky LRC_ENONFINITE); a fresh zeroed one is
+    made otherwise.  Returns the flag (read it after synchronising)."""
     _dev(A, "A")
-    _dev(C, "C")
-    if C.dtype != torch.float32:
-        raise ValueError("C must be fp32")
+    if A.dim() != 2:
+        raise ValueError("A must be (n_tokens, d)")
     n, d = A.shape
+    _tensor(C, "C", torch.float32, (d, d), A.device)
     lda = _rowmajor_ld(A, "A")
     ldc = _rowmajor_ld(C, "C")
-    if C.shape != (d, d):
-        raise ValueError("C must be d x d")
     dt = _dtype_code(A)
+    info = _info(info, A.device)
     flags = LRC_COV_QUANT_INT8_TOKEN if quant else 0
     ws = _workspace(lib.lrc_accumulate_cov_workspace(dt, n, d, flags), A.device)
-    _check(lib.lrc_accumulate_cov(_ptr(A), dt, n, d, lda, _ptr(C), ldc, flags, _ptr(ws), ws.numel(), _stream()),
-           "lrc_accumulate_cov")
+    _check(lib.lrc_accumulate_cov(_ptr(A), dt, n, d, lda, _ptr(C), ldc, flags, _ptr(info), _ptr(ws), ws.numel(),
+                                  _stream()), "lrc_accumulate_cov")
+    return info
 
 
 def lrc_whiten_decompose(W: torch.Tensor, rank: int, Xsum=None, n_x: int = 0, Gsum=None, n_g: int = 0,
-                         damping: float = 0.0, check: bool = True):
-    """Whitened truncated decomposition.  W: (d_out, d_in) or (batch, d_out, d_in) fp32.
+                         damping: float = 0.0):
+    """Whitened truncated decomposition.  W: (d_out, d_in) or (batch, d_out, d_in) fp32;
+    Xsum (d_in, d_in) and Gsum (d_out, d_out) fp32 sums, or None for identity.
 
     Returns (sigma, left, right, info): sigma (batch, k), left (batch, d_out, r),
-    right (batch, r, d_in), info (batch,) int32 -- batch dim dropped for 2-D W."""
+    right (batch, r, d_in), info (batch,) int32 -- batch dim dropped for 2-D W.  A
+    covariance that is not positive definite or an eigensolver at its sweep cap is
+    reported in info only (the call does not wait for the GPU)."""
     _dev(W, "W")
     if W.dtype != torch.float32:
         raise ValueError("W must be fp32")
@@ -176,84 +207,97 @@ def lrc_whiten_decompose(W: torch.Tensor, rank: int, Xsum=None, n_x: int = 0, Gs
     info = torch.empty(batch, dtype=torch.int32, device=dev)
     ldx = ldg = 0
     if Xsum is not None:
-        _dev(Xsum, "Xsum")
+        _tensor(Xsum, "Xsum", torch.float32, (d_in, d_in), dev)
         ldx = _rowmajor_ld(Xsum, "Xsum")
     if Gsum is not None:
-        _dev(Gsum, "Gsum")
+        _tensor(Gsum, "Gsum", torch.float32, (d_out, d_out), dev)
         ldg = _rowmajor_ld(Gsum, "Gsum")
     nb = lib.lrc_whiten_decompose_workspace(d_out, d_in, batch, rank, Xsum is not None, Gsum is not None)
     ws = _workspace(nb, dev)
     st = lib.lrc_whiten_decompose(_ptr(W3), d_out, d_in, ldw, batch, sw, _ptr(Xsum), ldx, int(n_x), _ptr(Gsum), ldg,
                                   int(n_g), int(rank), float(damping), _ptr(sigma), _ptr(left), _ptr(right),
                                   _ptr(info), _ptr(ws), ws.numel(), _stream())
-    if check:
-        _check(st, "lrc_whiten_decompose")
+    _check(st, "lrc_whiten_decompose")
     if squeeze:
         return sigma[0], left[0], right[0], info
     return sigma, left, right, info
 
 
 def lrc_score_components(left=None, right=None, sigma=None, A=None, B=None, mode: str = "fisher",
-                         scores=None, accumulate: bool = False, finalize: bool = True, n_total=None):
-    """Per-component scores; returns the scores tensor (k,) fp32.
+                         scores=None, accumulate: bool = False, finalize: bool = True, n_total=None, info=None):
+    """Per-component scores; returns (scores (k,) fp32, info int32 (1,)).
 
-    mode="fisher": needs left (d_out, k), right (k, d_in), A (n, d_in), B (n, d_out).
-    mode="kfac":   needs sigma (k,) only."""
+    mode="fisher": needs left (d_out, k), right (k, d_in) fp32, A (n, d_in), B (n, d_out)
+    (both bf16 or both fp32).  mode="kfac": needs sigma (k,) fp32 only.  info: optional
+    int32 (1,) device flag that receives LRC_ENONFINITE when a score is NaN/Inf (sticky
+    over a chunked stream); a fresh zeroed one is made otherwise."""
     if mode == "kfac":
         _dev(sigma, "sigma")
-        k = sigma.numel()
+        if sigma.dtype != torch.float32 or sigma.dim() != 1:
+            raise ValueError("sigma must be a 1-D fp32 tensor")
+        sig = sigma.contiguous()
+        k = sig.numel()
+        dev = sig.device
         if scores is None:
-            scores = torch.empty(k, dtype=torch.float32, device=sigma.device)
-        _check(lib.lrc_score_components(None, None, LRC_F32, 0, 1, 1, None, None, _ptr(sigma), k,
-                                        LRC_SCORE_KFAC, 0, 1, 1, _ptr(scores), None, 0, _stream()),
+            scores = torch.empty(k, dtype=torch.float32, device=dev)
+        _tensor(scores, "scores", torch.float32, (k,), dev)
+        info = _info(info, dev)
+        _check(lib.lrc_score_components(None, None, LRC_F32, 0, 1, 1, None, None, _ptr(sig), k,
+                                        LRC_SCORE_KFAC, 0, 1, 1, _ptr(scores), _ptr(info), None, 0, _stream()),
                "lrc_score_components")
-        return scores
+        return scores, info
     if mode != "fisher":
         raise ValueError("mode is 'fisher' or 'kfac'")
     _dev(left, "left")
+    if left.dim() != 2:
+        raise ValueError("left must be (d_out, k)")
     d_out, k = left.shape
-    kk, d_in = right.shape
-    if kk != k:
-        raise ValueError("left and right disagree on k")
-    if scores is None:
-        scores = torch.empty(k, dtype=torch.float32, device=left.device)
+    dev = left.device
+    _tensor(left, "left", torch.float32, (d_out, k), dev)
+    _tensor(right, "right", torch.float32, (k, None), dev)
+    d_in = right.shape[1]
     _dev(A, "A")
     _dev(B, "B")
+    if A.dim() != 2:
+        raise ValueError("A must be (n, d_in)")
     n = A.shape[0]
-    if A.shape != (n, d_in) or B.shape != (n, d_out) or A.dtype != B.dtype:
-        raise ValueError("A must be (n, d_in) and B (n, d_out), same dtype")
-    if not (A.is_contiguous() and B.is_contiguous() and left.is_contiguous() and right.is_contiguous()):
-        raise ValueError("contiguous tensors required")
+    _tensor(A, "A", A.dtype, (n, d_in), dev)
+    _tensor(B, "B", A.dtype, (n, d_out), dev)
     dt = _dtype_code(A)
-    ws = _workspace(lib.lrc_score_components_workspace(n, d_in, d_out, k, LRC_SCORE_FISHER), A.device)
-    _check(lib.lrc_score_components(_ptr(A), _ptr(B), dt, n, d_in, d_out, _ptr(left), _ptr(right), None, k,
+    if scores is None:
+        scores = torch.empty(k, dtype=torch.float32, device=dev)
+    _tensor(scores, "scores", torch.float32, (k,), dev)
+    info = _info(info, dev)
+    # contiguous copies (if any) stay referenced until the call has returned
+    a, b, lf, rt = A.contiguous(), B.contiguous(), left.contiguous(), right.contiguous()
+    ws = _workspace(lib.lrc_score_components_workspace(n, d_in, d_out, k, LRC_SCORE_FISHER), dev)
+    _check(lib.lrc_score_components(_ptr(a), _ptr(b), dt, n, d_in, d_out, _ptr(lf), _ptr(rt), None, k,
                                     LRC_SCORE_FISHER, int(accumulate), int(finalize), int(n_total or n),
-                                    _ptr(scores), _ptr(ws), ws.numel(), _stream()), "lrc_score_components")
-    return scores
+                                    _ptr(scores), _ptr(info), _ptr(ws), ws.numel(), _stream()), "lrc_score_components")
+    return scores, info
 
 
 def lrc_allocate_ranks(scores: torch.Tensor, offsets: torch.Tensor, cost: torch.Tensor, budget: int):
     """Global sort-and-truncate.  scores: (M,) fp32; offsets: (n_mat+1,) int64; cost: (n_mat,) int64.
 
     Returns (order int32 (M,), n_kept int64 (1,), ranks int32 (n_mat,), kept_mask uint8 (M,), info int32 (1,))."""
-    for t, nm in ((scores, "scores"), (offsets, "offsets"), (cost, "cost")):
-        _dev(t, nm)
-    if scores.dtype != torch.float32 or offsets.dtype != torch.int64 or cost.dtype != torch.int64:
-        raise ValueError("scores fp32, offsets and cost int64")
-    n_mat = cost.numel()
-    if offsets.numel() != n_mat + 1:
-        raise ValueError("offsets must have n_mat + 1 entries")
-    M = scores.numel()
+    _dev(scores, "scores")
     dev = scores.device
+    n_mat = cost.numel() if isinstance(cost, torch.Tensor) else 0
+    _tensor(scores, "scores", torch.float32, (None,), dev)
+    _tensor(offsets, "offsets", torch.int64, (n_mat + 1,), dev)
+    _tensor(cost, "cost", torch.int64, (n_mat,), dev)
+    M = scores.numel()
+    sc, offs, cst = scores.contiguous(), offsets.contiguous(), cost.contiguous()
     order = torch.empty(M, dtype=torch.int32, device=dev)
     n_kept = torch.empty(1, dtype=torch.int64, device=dev)
     ranks = torch.empty(n_mat, dtype=torch.int32, device=dev)
     kept = torch.empty(M, dtype=torch.uint8, device=dev)
     info = torch.empty(1, dtype=torch.int32, device=dev)
     ws = _workspace(lib.lrc_allocate_ranks_workspace(n_mat, M), dev)
-    _check(lib.lrc_allocate_ranks(_ptr(scores.contiguous()), _ptr(offsets.contiguous()), _ptr(cost.contiguous()),
-                                  n_mat, M, int(budget), _ptr(order), _ptr(n_kept), _ptr(ranks), _ptr(kept),
-                                  _ptr(info), _ptr(ws), ws.numel(), _stream()), "lrc_allocate_ranks")
+    _check(lib.lrc_allocate_ranks(_ptr(sc), _ptr(offs), _ptr(cst), n_mat, M, int(budget), _ptr(order), _ptr(n_kept),
+                                  _ptr(ranks), _ptr(kept), _ptr(info), _ptr(ws), ws.numel(), _stream()),
+           "lrc_allocate_ranks")
     return order, n_kept, ranks, kept, info
 
 
@@ -264,20 +308,19 @@ def lrc_rank_scores(sigma: torch.Tensor, offsets: torch.Tensor, weight: torch.Te
     importance I_l (mode "unirank") or beta_l (mode "swift", with alpha).
 
     Returns (scores fp32 (M,), info int32 (1,))."""
-    for t, nm in ((sigma, "sigma"), (offsets, "offsets"), (weight, "weight")):
-        _dev(t, nm)
-    if sigma.dtype != torch.float32 or offsets.dtype != torch.int64 or weight.dtype != torch.float32:
-        raise ValueError("sigma and weight fp32, offsets int64")
-    n_mat = weight.numel()
-    if offsets.numel() != n_mat + 1:
-        raise ValueError("offsets must have n_mat + 1 entries")
+    _dev(sigma, "sigma")
+    dev = sigma.device
+    n_mat = weight.numel() if isinstance(weight, torch.Tensor) else 0
+    _tensor(sigma, "sigma", torch.float32, (None,), dev)
+    _tensor(offsets, "offsets", torch.int64, (n_mat + 1,), dev)
+    _tensor(weight, "weight", torch.float32, (n_mat,), dev)
     flag = {"unirank": LRC_RANKSCORE_UNIRANK, "swift": LRC_RANKSCORE_SWIFT}[mode]
     M = sigma.numel()
-    scores = torch.empty(M, dtype=torch.float32, device=sigma.device)
-    info = torch.empty(1, dtype=torch.int32, device=sigma.device)
-    _check(lib.lrc_rank_scores(_ptr(sigma.contiguous()), _ptr(offsets.contiguous()), n_mat, M,
-                               _ptr(weight.contiguous()), float(alpha), flag, _ptr(scores), _ptr(info), _stream()),
-           "lrc_rank_scores")
+    sig, offs, wgt = sigma.contiguous(), offsets.contiguous(), weight.contiguous()
+    scores = torch.empty(M, dtype=torch.float32, device=dev)
+    info = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(lib.lrc_rank_scores(_ptr(sig), _ptr(offs), n_mat, M, _ptr(wgt), float(alpha), flag, _ptr(scores),
+                               _ptr(info), _stream()), "lrc_rank_scores")
     return scores, info
 
 
@@ -287,15 +330,16 @@ def lrc_rotate_quantize(left: torch.Tensor, right: torch.Tensor, signs: torch.Te
 
     Returns (q_left int8, s_left fp32, q_right int8, s_right fp32) and, with
     keep_rotated, the rotated fp32 factors as two more entries."""
-    for t, nm in ((left, "left"), (right, "right"), (signs, "signs")):
-        _dev(t, nm)
-        if t.dtype != torch.float32:
-            raise ValueError(f"{nm} must be fp32")
+    _dev(left, "left")
+    if left.dim() != 2:
+        raise ValueError("left must be (d_out, r)")
     d_out, r = left.shape
-    if right.shape[0] != r or signs.numel() != r:
-        raise ValueError("left (d_out, r), right (r, d_in), signs (r,)")
-    d_in = right.shape[1]
     dev = left.device
+    _tensor(left, "left", torch.float32, (d_out, r), dev)
+    _tensor(right, "right", torch.float32, (r, None), dev)
+    _tensor(signs, "signs", torch.float32, (r,), dev)
+    d_in = right.shape[1]
+    lf, rt, sg = left.contiguous(), right.contiguous(), signs.contiguous()
     ql = torch.empty(d_out, r, dtype=torch.int8, device=dev)
     sl = torch.empty(d_out, dtype=torch.float32, device=dev)
     qr = torch.empty(r, d_in, dtype=torch.int8, device=dev)
@@ -303,8 +347,7 @@ def lrc_rotate_quantize(left: torch.Tensor, right: torch.Tensor, signs: torch.Te
     lrot = torch.empty(d_out, r, dtype=torch.float32, device=dev) if keep_rotated else None
     rrot = torch.empty(r, d_in, dtype=torch.float32, device=dev) if keep_rotated else None
     ws = _workspace(lib.lrc_rotate_quantize_workspace(d_out, r, d_in), dev)
-    _check(lib.lrc_rotate_quantize(_ptr(left.contiguous()), _ptr(right.contiguous()), d_out, r, d_in,
-                                   _ptr(signs.contiguous()), _ptr(ql), _ptr(sl), _ptr(qr), _ptr(sr),
+    _check(lib.lrc_rotate_quantize(_ptr(lf), _ptr(rt), d_out, r, d_in, _ptr(sg), _ptr(ql), _ptr(sl), _ptr(qr), _ptr(sr),
                                    _ptr(lrot) if keep_rotated else None, _ptr(rrot) if keep_rotated else None,
                                    _ptr(ws), ws.numel(), _stream()), "lrc_rotate_quantize")
     return (ql, sl, qr, sr, lrot, rrot) if keep_rotated else (ql, sl, qr, sr)
@@ -330,15 +373,14 @@ def lrc_ffn_select_channels(w_gate: torch.Tensor, w_up: torch.Tensor, gate_facto
     lrc_whiten_decompose with the same Xsum (or None for r = 0); Xsum: (d, d) fp32 sum.
 
     Returns (err fp64 (d_ff,), order int32 (d_ff,), lowrank uint8 (d_ff,), info int32 (1,))."""
-    for t, nm in ((w_gate, "w_gate"), (w_up, "w_up"), (Xsum, "Xsum")):
-        _dev(t, nm)
-        if t.dtype != torch.float32:
-            raise ValueError(f"{nm} must be fp32")
-    if w_gate.shape != w_up.shape or w_gate.dim() != 2:
-        raise ValueError("w_gate and w_up must both be (d_ff, d)")
+    _dev(w_gate, "w_gate")
+    if w_gate.dim() != 2:
+        raise ValueError("w_gate must be (d_ff, d)")
     d_ff, d = w_gate.shape
-    if tuple(Xsum.shape) != (d, d):
-        raise ValueError("Xsum must be (d, d)")
+    dev = w_gate.device
+    _tensor(w_gate, "w_gate", torch.float32, (d_ff, d), dev)
+    _tensor(w_up, "w_up", torch.float32, (d_ff, d), dev)
+    _tensor(Xsum, "Xsum", torch.float32, (d, d), dev)
     wg, wu = w_gate.contiguous(), w_up.contiguous()
     r = 0
     fac = []
@@ -347,15 +389,12 @@ def lrc_ffn_select_channels(w_gate: torch.Tensor, w_up: torch.Tensor, gate_facto
             if pair is None:
                 raise ValueError("give the factors of both gate and up, or of neither")
             left, right = pair
-            _dev(left, f"{nm} left")
-            _dev(right, f"{nm} right")
-            if left.dtype != torch.float32 or right.dtype != torch.float32:
-                raise ValueError(f"{nm} factors must be fp32")
+            _tensor(left, f"{nm} left", torch.float32, (d_ff, None), dev)
+            _tensor(right, f"{nm} right", torch.float32, (None, d), dev)
             fac += [left.contiguous(), right.contiguous()]
         r = fac[0].shape[1]
         if any(tuple(f.shape) != shp for f, shp in zip(fac, [(d_ff, r), (r, d)] * 2)):
             raise ValueError("factors must be left (d_ff, r) and right (r, d) for both")
-    dev = w_gate.device
     err = torch.empty(d_ff, dtype=torch.float64, device=dev)
     order = torch.empty(d_ff, dtype=torch.int32, device=dev)
     lowrank = torch.empty(d_ff, dtype=torch.uint8, device=dev)
@@ -369,6 +408,30 @@ def lrc_ffn_select_channels(w_gate: torch.Tensor, w_up: torch.Tensor, gate_facto
     return err, order, lowrank, info
 
 
+def _lowrank_factors(gate, up, down, d, dev):
+    """Check the int8 factor sets of a low-rank FFN (shapes, dtypes, device) and return
+    contiguous copies plus (d_ff, rg, ru, rd)."""
+    i8, f32 = torch.int8, torch.float32
+    for t in [*gate, *up, *down]:
+        _dev(t, "ffn factor")
+    if len(gate) != 4 or len(up) != 4 or len(down) != 4:
+        raise ValueError("gate, up and down are 4-tuples (q_R, s_R, q_L, s_L)")
+    rg, ru = gate[0].shape[0], up[0].shape[0]
+    d_ff = gate[2].shape[0]
+    rd = down[0].shape[1]
+    for (q_r, s_r, q_l, s_l), r, nm in ((gate, rg, "gate"), (up, ru, "up")):
+        _tensor(q_r, f"{nm} q_R", i8, (r, d), dev)
+        _tensor(s_r, f"{nm} s_R", f32, (r,), dev)
+        _tensor(q_l, f"{nm} q_L", i8, (d_ff, r), dev)
+        _tensor(s_l, f"{nm} s_L", f32, (d_ff,), dev)
+    _tensor(down[0], "down q_Rt", i8, (d_ff, rd), dev)
+    _tensor(down[1], "down s_R", f32, (rd,), dev)
+    _tensor(down[2], "down q_L", i8, (d, rd), dev)
+    _tensor(down[3], "down s_L", f32, (d,), dev)
+    return ([t.contiguous() for t in gate], [t.contiguous() for t in up], [t.contiguous() for t in down],
+            d_ff, rg, ru, rd)
+
+
 def lrc_hybrid_ffn(x: torch.Tensor, gate=None, up=None, down=None, dense=None):
     """Hybrid FFN forward: hidden channels [0, n_lr) low-rank (gate, up, down as for
     lrc_lowrank_ffn, or all None when n_lr = 0), the next n_dense dense:
@@ -376,34 +439,36 @@ def lrc_hybrid_ffn(x: torch.Tensor, gate=None, up=None, down=None, dense=None):
     W_down's dense columns as rows, s_dd (d,)), or None when n_dense = 0.
     Returns y (n_tok, d) fp32."""
     _dev(x, "x")
+    if x.dtype != torch.float32 or x.dim() != 2:
+        raise ValueError("x must be (n_tok, d) fp32")
     n_tok, d = x.shape
-    x = x.contiguous()
+    dev = x.device
+    xc = x.contiguous()
     lr = gate is not None
     if lr != (up is not None) or lr != (down is not None):
         raise ValueError("give gate, up and down together, or none of them")
     if lr:
-        for t in [*gate, *up, *down]:
-            _dev(t, "ffn factor")
-        g = [t.contiguous() for t in gate]
-        u = [t.contiguous() for t in up]
-        dn = [t.contiguous() for t in down]
-        rg, ru, rd = g[0].shape[0], u[0].shape[0], dn[0].shape[1]
-        n_lr = g[2].shape[0]
+        g, u, dn, n_lr, rg, ru, rd = _lowrank_factors(gate, up, down, d, dev)
     else:
         g = u = dn = [None] * 4
         rg = ru = rd = n_lr = 0
     if dense is not None:
-        for t in dense:
-            _dev(t, "dense FFN operand")
+        if len(dense) != 6:
+            raise ValueError("dense is a 6-tuple (q_gd, s_gd, q_ud, s_ud, q_dd, s_dd)")
+        _dev(dense[0], "q_gd")
+        n_dense = dense[0].shape[0]
+        for t, nm, dt, shp in zip(dense, ("q_gd", "s_gd", "q_ud", "s_ud", "q_dd", "s_dd"),
+                                  (torch.int8, torch.float32) * 3,
+                                  ((n_dense, d), (n_dense,), (n_dense, d), (n_dense,), (d, n_dense), (d,))):
+            _tensor(t, nm, dt, shp, dev)
         dd = [t.contiguous() for t in dense]
-        n_dense = dd[0].shape[0]
     else:
         dd = [None] * 6
         n_dense = 0
-    y = torch.empty(n_tok, d, dtype=torch.float32, device=x.device)
-    ws = _workspace(lib.lrc_hybrid_ffn_workspace(n_tok, n_lr, rg, ru, rd, n_dense), x.device)
+    y = torch.empty(n_tok, d, dtype=torch.float32, device=dev)
+    ws = _workspace(lib.lrc_hybrid_ffn_workspace(n_tok, n_lr, rg, ru, rd, n_dense), dev)
     p = lambda t: None if t is None else _ptr(t)
-    _check(lib.lrc_hybrid_ffn(_ptr(x), n_tok, d, n_lr, p(g[0]), p(g[1]), p(g[2]), p(g[3]), rg, p(u[0]), p(u[1]),
+    _check(lib.lrc_hybrid_ffn(_ptr(xc), n_tok, d, n_lr, p(g[0]), p(g[1]), p(g[2]), p(g[3]), rg, p(u[0]), p(u[1]),
                               p(u[2]), p(u[3]), ru, p(dn[0]), p(dn[1]), p(dn[2]), p(dn[3]), rd, n_dense, p(dd[0]),
                               p(dd[1]), p(dd[2]), p(dd[3]), p(dd[4]), p(dd[5]), _ptr(y), _ptr(ws), ws.numel(),
                               _stream()), "lrc_hybrid_ffn")
@@ -415,22 +480,18 @@ def lrc_lowrank_ffn(x: torch.Tensor, gate, up, down):
     gate, up: (q_R (r, d) int8, s_R (r,), q_L (d_ff, r) int8, s_L (d_ff,)).
     down: (q_Rt (d_ff, r_d) int8 -- R_down transposed, s_R (r_d,), q_L (d, r_d) int8, s_L (d,)).
     Returns y (n_tok, d) fp32."""
-    tens = [x, *gate, *up, *down]
-    for t in tens:
-        _dev(t, "ffn operand")
+    _dev(x, "x")
+    if x.dtype != torch.float32 or x.dim() != 2:
+        raise ValueError("x must be (n_tok, d) fp32")
     n_tok, d = x.shape
-    d_ff, rg = gate[2].shape
-    ru = up[2].shape[1]
-    rd = down[2].shape[1]
-    x = x.contiguous()
-    gate = [t.contiguous() for t in gate]
-    up = [t.contiguous() for t in up]
-    down = [t.contiguous() for t in down]
-    y = torch.empty(n_tok, d, dtype=torch.float32, device=x.device)
-    ws = _workspace(lib.lrc_lowrank_ffn_workspace(n_tok, d_ff, rg, ru, rd), x.device)
-    _check(lib.lrc_lowrank_ffn(_ptr(x), n_tok, d, d_ff, _ptr(gate[0]), _ptr(gate[1]), _ptr(gate[2]), _ptr(gate[3]), rg,
-                               _ptr(up[0]), _ptr(up[1]), _ptr(up[2]), _ptr(up[3]), ru, _ptr(down[0]), _ptr(down[1]),
-                               _ptr(down[2]), _ptr(down[3]), rd, _ptr(y), _ptr(ws), ws.numel(), _stream()),
+    dev = x.device
+    xc = x.contiguous()
+    g, u, dn, d_ff, rg, ru, rd = _lowrank_factors(gate, up, down, d, dev)
+    y = torch.empty(n_tok, d, dtype=torch.float32, device=dev)
+    ws = _workspace(lib.lrc_lowrank_ffn_workspace(n_tok, d_ff, rg, ru, rd), dev)
+    _check(lib.lrc_lowrank_ffn(_ptr(xc), n_tok, d, d_ff, _ptr(g[0]), _ptr(g[1]), _ptr(g[2]), _ptr(g[3]), rg,
+                               _ptr(u[0]), _ptr(u[1]), _ptr(u[2]), _ptr(u[3]), ru, _ptr(dn[0]), _ptr(dn[1]),
+                               _ptr(dn[2]), _ptr(dn[3]), rd, _ptr(y), _ptr(ws), ws.numel(), _stream()),
            "lrc_lowrank_ffn")
     return y
 

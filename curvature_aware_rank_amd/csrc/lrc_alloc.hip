@@ -85,7 +85,7 @@ struct CostLookup {
 };
 
 // sort key of item j: ~bits(fp64(score) / fp64(cost)); 0 (first in the order) for a
-// rejected item, whose call reports an error
+// rejected item, whose call reports an error and keeps nothing
 __device__ __forceinline__ uint64_t item_key(const float* __restrict__ scores, const CostLookup& cl, int64_t j,
                                              bool inputs_bad, bool& nonfinite) {
   nonfinite = false;
@@ -434,10 +434,13 @@ __global__ __launch_bounds__(256) void cost_cut_kernel(const int32_t* __restrict
 
 __global__ void set_i64_kernel(int64_t* __restrict__ p, int64_t v) { *p = v; }
 
-// key and id of the last kept position (or an empty marker) for the mask
+// key and id of the last kept position (or an empty marker) for the mask.  A call whose
+// inputs were rejected (info != 0: a score NaN, infinite or negative, or inconsistent
+// offsets or costs) keeps nothing: n_kept = 0, and the mask and ranks come out zero.
 __global__ void cut_key_kernel(const float* __restrict__ scores, CostLookup cl,
-                               const int32_t* __restrict__ order, int M, const int64_t* __restrict__ n_kept,
+                               const int32_t* __restrict__ order, int M, int64_t* __restrict__ n_kept,
                                const int32_t* __restrict__ info, uint64_t* __restrict__ cutkey) {
+  if (*info != 0) *n_kept = 0;
   const int64_t nk = *n_kept;
   if (nk <= 0) {
     cutkey[1] = ~uint64_t(0);   // no id is <= this as a signed int64: nothing kept

@@ -131,15 +131,25 @@ extern "C" lrc_status lrc_profile_start(void) {
 extern "C" lrc_status lrc_profile_stop(void) {
   std::lock_guard<std::mutex> lk(lrc::g_prof_mu);
   lrc::g_prof_on = false;
+  // every recorded pair goes back to the pool exactly once and the list is cleared, also
+  // when an event reports an error (the first error is returned; later pairs still count)
+  hipError_t first = hipSuccess;
   for (auto& e : lrc::g_prof_events) {
-    LRC_HIP(hipEventSynchronize(e.e1));
+    hipError_t r = hipEventSynchronize(e.e1);
     float ms = 0.f;
-    LRC_HIP(hipEventElapsedTime(&ms, e.e0, e.e1));
-    lrc::total_for(e.name).ms += ms;
+    if (r == hipSuccess) r = hipEventElapsedTime(&ms, e.e0, e.e1);
+    if (r == hipSuccess)
+      lrc::total_for(e.name).ms += ms;
+    else if (first == hipSuccess)
+      first = r;
     lrc::g_prof_pool.push_back(e.e0);
     lrc::g_prof_pool.push_back(e.e1);
   }
   lrc::g_prof_events.clear();
+  if (first != hipSuccess) {
+    lrc::set_last_hip_error(first);
+    return LRC_EHIP;
+  }
   return LRC_OK;
 }
 

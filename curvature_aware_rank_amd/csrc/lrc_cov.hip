@@ -464,10 +464,12 @@ __global__ __launch_bounds__(64 * DL_NW, 1) void syrk_bf16_dl_kernel(
 
 // C[lower] += sum over splits of the partial tiles, in split order (bit-reproducible).
 // Block (tile, q) handles 256 consecutive float4 of the tile; loads are batched 8 splits
-// at a time from clamped addresses, then masked.
+// at a time from clamped addresses, then masked.  A diagonal entry of C is a sum of
+// squares, so a NaN or Inf anywhere in column i of the tokens (or an overflow) makes
+// C[i][i] non-finite; the thread holding it then sets *info (when given).
 __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restrict__ partial, int splits, int n_tiles,
                                                           int n1, int d, float* __restrict__ C, int64_t ldc,
-                                                          int vec4) {
+                                                          int vec4, int32_t* __restrict__ info) {
   const int tile = blockIdx.x;
   const TileRC tc = tile_of(tile, n1);
   const int idx = blockIdx.y * 256 + threadIdx.x;   // float4 index within the tile
@@ -491,13 +493,19 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restric
   float* c = C + int64_t(row) * ldc + col0;
   if (vec4 && col0 + 3 < d && (tc.ti != tc.tj || col0 + 3 <= row)) {
     f32x4 cv = *reinterpret_cast<const f32x4*>(c);
-    *reinterpret_cast<f32x4*>(c) = cv + sum;
+    cv += sum;
+    *reinterpret_cast<f32x4*>(c) = cv;
+    if (info && row == col0 + 3 && !isfinite(cv[3])) *info = LRC_ENONFINITE;
     return;
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int col = col0 + e;
-    if (col < d && (tc.ti != tc.tj || col <= row)) c[e] += sum[e];
+    if (col < d && (tc.ti != tc.tj || col <= row)) {
+      const float v = c[e] + sum[e];
+      c[e] = v;
+      if (info && col == row && !isfinite(v)) *info = LRC_ENONFINITE;
+    }
   }
 }
 
@@ -540,7 +548,8 @@ __global__ __launch_bounds__(256) void qaw_prepass_kernel(const T* __restrict__ 
 
 // ---- fp32 input: plain LDS-tiled SYRK, 64 x 64 lower tiles, no split (deterministic)
 __global__ __launch_bounds__(256) void syrk_f32_kernel(const float* __restrict__ A, int64_t lda, int64_t n,
-                                                       int d, float* __restrict__ C, int64_t ldc) {
+                                                       int d, float* __restrict__ C, int64_t ldc,
+                                                       int32_t* __restrict__ info) {
   __shared__ float xs[16][65];
   __shared__ float ys[16][65];
   int lin = blockIdx.x, ti = 0;
@@ -574,7 +583,13 @@ __global__ __launch_bounds__(256) void syrk_f32_kernel(const float* __restrict__
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = ti * 64 + ty * 4 + i, col = tj * 64 + tx * 4 + j;
-      if (row < d && col < d && row >= col) C[int64_t(row) * ldc + col] += acc[i][j];
+      if (row < d && col < d && row >= col) {
+        const float v = C[int64_t(row) * ldc + col] + acc[i][j];
+        C[int64_t(row) * ldc + col] = v;
+        // a diagonal entry is a sum of squares: non-finite iff a token entry of this
+        // column is (or the sum overflowed)
+        if (info && row == col && !isfinite(v)) *info = LRC_ENONFINITE;
+      }
     }
 }
 
@@ -613,7 +628,7 @@ size_t syrk_partial_floats(const SyrkPlan& p) { return size_t(p.splits) * p.n_ti
 
 // bf16 SYRK launch over a token block, partial/counter space from the carve
 lrc_status launch_syrk_bf16(hipStream_t st, const uint16_t* X, const uint16_t* Y, int64_t ldx, int64_t n,
-                            int64_t d, float* C, int64_t ldc, float* partial, int split_cap) {
+                            int64_t d, float* C, int64_t ldc, float* partial, int split_cap, int32_t* info) {
   if (n <= 0) return LRC_OK;
   const SyrkPlan p = plan_syrk(n, d, split_cap);  // never more splits than the partial buffer holds
   const bool vec = (d % 8 == 0) && (ldx % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0) &&
@@ -640,7 +655,7 @@ lrc_status launch_syrk_bf16(hipStream_t st, const uint16_t* X, const uint16_t* Y
   LRC_LAUNCHED();
   const int vec4 = (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & 15) == 0);
   syrk_reduce_kernel<<<dim3(unsigned(p.n_tiles), unsigned(TB * TB / 4 / 256)), 256, 0, st>>>(
-      partial, p.splits, p.n_tiles, p.n1, int(d), C, ldc, vec4);
+      partial, p.splits, p.n_tiles, p.n1, int(d), C, ldc, vec4, info);
   LRC_LAUNCHED();
   return LRC_OK;
 }
@@ -688,8 +703,8 @@ extern "C" size_t lrc_accumulate_cov_workspace(lrc_dtype dt, int64_t n_tokens, i
 }
 
 extern "C" lrc_status lrc_accumulate_cov(const void* A, lrc_dtype dt, int64_t n_tokens, int64_t d, int64_t lda,
-                                         float* C, int64_t ldc, uint32_t flags, void* ws, size_t ws_bytes,
-                                         void* stream) {
+                                         float* C, int64_t ldc, uint32_t flags, int32_t* info, void* ws,
+                                         size_t ws_bytes, void* stream) {
   if (dt != LRC_F32 && dt != LRC_BF16) return LRC_EDTYPE;
   if (flags & ~uint32_t(LRC_COV_QUANT_INT8_TOKEN)) return LRC_EDTYPE;
   if (n_tokens < 0 || d <= 0 || d > (int64_t(1) << 30) || lda < d || ldc < d) return LRC_EINVAL;
@@ -711,13 +726,13 @@ extern "C" lrc_status lrc_accumulate_cov(const void* A, lrc_dtype dt, int64_t n_
     const int tiles = int(cdiv(d, 64) * (cdiv(d, 64) + 1) / 2);
     const double tri = double(d) * double(d + 1) / 2;
     ProfScope scope("syrk_f32_kernel", st, 2.0 * double(n_tokens) * tri, double(n_tokens) * double(d) * 4.0 + 8.0 * tri);
-    syrk_f32_kernel<<<tiles, 256, 0, st>>>(static_cast<const float*>(A), lda, n_tokens, int(d), C, ldc);
+    syrk_f32_kernel<<<tiles, 256, 0, st>>>(static_cast<const float*>(A), lda, n_tokens, int(d), C, ldc, info);
     LRC_LAUNCHED();
     return LRC_OK;
   }
   if (!quant) {
     const uint16_t* a = static_cast<const uint16_t*>(A);
-    return launch_syrk_bf16(st, a, a, lda, n_tokens, d, C, ldc, partial, cap);
+    return launch_syrk_bf16(st, a, a, lda, n_tokens, d, C, ldc, partial, cap, info);
   }
   for (int64_t t0 = 0; t0 < n_tokens; t0 += chunk) {
     const int64_t nb = std::min(chunk, n_tokens - t0);
@@ -731,8 +746,8 @@ extern "C" lrc_status lrc_accumulate_cov(const void* A, lrc_dtype dt, int64_t n_
                                                               int(d), q, h, l, d);
     LRC_LAUNCHED();
     }
-    LRC_TRY(launch_syrk_bf16(st, q, h, d, nb, d, C, ldc, partial, cap));
-    LRC_TRY(launch_syrk_bf16(st, q, l, d, nb, d, C, ldc, partial, cap));
+    LRC_TRY(launch_syrk_bf16(st, q, h, d, nb, d, C, ldc, partial, cap, info));
+    LRC_TRY(launch_syrk_bf16(st, q, l, d, nb, d, C, ldc, partial, cap, info));
   }
   return LRC_OK;
 }

@@ -35,6 +35,25 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
   if (i < n) p[i] = v;
 }
 
+// After a failed Cholesky (a pivot of X or G not positive) the whitened weight holds
+// non-finite values.  Every item's info gets the failing pivot (p for X, d_in + p for G)
+// and its Gram is replaced by diag(k, k-1, ..., 1): distinct, well separated eigenvalues,
+// so the eigensolver's fixed work runs on benign data.  Nothing is read by the host; the
+// outputs of such a call are undefined.
+__global__ void chol_guard_kernel(const int* __restrict__ chol_info, int d_in, double* __restrict__ G, int64_t ldg,
+                                  int64_t sG, int k, int32_t* __restrict__ info) {
+  const int cx = chol_info[0], cg = chol_info[1];
+  if (cx == 0 && cg == 0) return;
+  const int b = blockIdx.y;
+  double* g = G + b * sG;
+  const int64_t kk = int64_t(k) * k;
+  for (int64_t e = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; e < kk; e += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t i = e / k, c = e % k;
+    g[i * ldg + c] = i == c ? double(k - i) : 0.0;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) info[b] = cx != 0 ? cx : d_in + cg;
+}
+
 // out[i][c] = in[i][c] * g(sigma[c]);  g = sqrt (mode 0) or 1/sqrt (mode 1, 0 where sigma == 0)
 __global__ void scale_cols_kernel(const float* __restrict__ in, int64_t ldi, float* __restrict__ out, int64_t ldo,
                                   int64_t rows, int cols, const float* __restrict__ sigma, int mode) {
@@ -78,11 +97,9 @@ DWs carve_decomp(Carve& cv, int64_t d_out, int64_t d_in, int64_t batch, int64_t 
   w.qt = cv.take<float>(size_t(batch * std::max<int64_t>(rank, 1) * k));
   w.u = cv.take<float>(size_t(k * std::max<int64_t>(rank, 1)));
   w.p = cv.take<float>(size_t(big * std::max<int64_t>(rank, 1)));
-  // the two eigensolvers run one after the other at most (a clustered spectrum falls back
-  // from the tridiagonal route to Jacobi), so they share one region
-  size_t jb = jacobi_workspace(k, batch);
-  if (use_tridiag(k, batch)) jb = std::max(jb, tridiag_workspace(k, std::max<int64_t>(rank, 1)));
-  w.jac = cv.take<char>(jb);
+  // one eigensolver runs per call
+  w.jac = cv.take<char>(use_tridiag(k, batch) ? tridiag_workspace(k, std::max<int64_t>(rank, 1))
+                                              : jacobi_workspace(k, batch));
   return w;
 }
 
@@ -128,20 +145,10 @@ extern "C" lrc_status lrc_whiten_decompose(const float* W, int64_t d_out, int64_
   fill_i32_kernel<<<1, 64, 0, st>>>(w.chol_info, 2, 0);
   LRC_LAUNCHED();
 
-  // a2: Cholesky factors of the covariances
+  // a2: Cholesky factors of the covariances (a failed pivot is recorded in chol_info and
+  // acted on after the Gram, on the device)
   if (hx) LRC_TRY(cholesky_f32(st, Xsum, ldx, d_in, n_x, damping, w.lx, w.chol_info));
   if (hg) LRC_TRY(cholesky_f32(st, Gsum, ldg, d_out, n_g, damping, w.lg, w.chol_info + 1));
-  if (hx || hg) {
-    int ci[2] = {0, 0};
-    LRC_HIP(hipMemcpyAsync(ci, w.chol_info, sizeof(ci), hipMemcpyDeviceToHost, st));
-    LRC_HIP(hipStreamSynchronize(st));
-    if (ci[0] != 0 || ci[1] != 0) {
-      const int32_t v = ci[0] != 0 ? ci[0] : int32_t(d_in + ci[1]);
-      fill_i32_kernel<<<unsigned(cdiv(batch, 256)), 256, 0, st>>>(info, batch, v);
-      LRC_LAUNCHED();
-      return LRC_ENOTPD;
-    }
-  }
 
   // a3: whitening  W~ = L_g^T W L_x
   const float* cur = W;
@@ -165,19 +172,16 @@ extern "C" lrc_status lrc_whiten_decompose(const float* W, int64_t d_out, int64_
   // a4: fp64 Gram of the smaller side and its eigendecomposition
   const bool left_side = d_out <= d_in;
   LRC_TRY(gram_f64(st, left_side, d_out, d_in, cur, ldc, scur, w.gram, kp, kp * kp, batch));
+  if (hx || hg) {
+    const dim3 g(unsigned(std::min<int64_t>(cdiv(k * k, 256), 64)), unsigned(batch));
+    chol_guard_kernel<<<g, 256, 0, st>>>(w.chol_info, int(d_in), w.gram, kp, kp * kp, int(k), info);
+    LRC_LAUNCHED();
+  }
   const int64_t ncols = std::max<int64_t>(rank, 1);
-  bool jacobi = true;
-  if (use_tridiag(k, batch)) {
-    bool clustered = false;
-    LRC_TRY(tridiag_eig(st, w.gram, k, kp, ncols, sigma, w.qt, w.jac, &clustered));
-    jacobi = clustered;
-    // the tridiagonalisation consumed the Gram: form it again for the Jacobi solver
-    if (clustered) LRC_TRY(gram_f64(st, left_side, d_out, d_in, cur, ldc, scur, w.gram, kp, kp * kp, batch));
-  }
-  if (jacobi) {
-    const lrc_status es = jacobi_eig(st, w.gram, k, batch, ncols, sigma, w.qt, info, w.jac);
-    if (es != LRC_OK) return es;
-  }
+  if (use_tridiag(k, batch))
+    LRC_TRY(tridiag_eig(st, w.gram, k, kp, ncols, sigma, w.qt, w.jac));
+  else
+    LRC_TRY(jacobi_eig(st, w.gram, k, batch, ncols, sigma, w.qt, info, w.jac));
   if (rank == 0) return LRC_OK;
 
   // a5: back-map to weight space

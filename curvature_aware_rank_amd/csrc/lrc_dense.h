@@ -21,7 +21,9 @@ lrc_status transpose_f32(hipStream_t st, const float* S, int64_t lds_, float* D,
 // Outputs: lam (batch x k, descending, fp64 -> float sigma = sqrt(max(lam,0))) and
 // Qt (batch x ncols x k, fp32): row c = eigenvector c, sign fixed so that its
 // largest-magnitude entry (lowest index on ties) is positive.
-// Returns LRC_ENOCONV (and sets info[b] = -1 for unconverged items) at the sweep cap.
+// Enqueues a fixed number of sweeps (items that converge skip the rest on the device);
+// an item still rotating after the last sweep gets info[b] = -1 (written on the device,
+// unless info[b] already holds a nonzero code).
 int64_t jacobi_padded(int64_t k);
 size_t jacobi_workspace(int64_t k, int64_t batch);
 lrc_status jacobi_eig(hipStream_t st, double* A, int64_t k, int64_t batch, int64_t ncols, float* sigma,
@@ -30,12 +32,11 @@ lrc_status jacobi_eig(hipStream_t st, double* A, int64_t k, int64_t batch, int64
 // Symmetric eigendecomposition of one fp64 k x k Gram (lower triangle of A, leading
 // dimension lda; destroyed): Householder tridiagonalisation, Sturm multisection for all
 // eigenvalues, inverse iteration for the ncols largest, blocked back-transformation.
-// Same outputs as jacobi_eig (batch 1).  When the wanted eigenvalues contain a cluster
-// too large for inverse iteration, *clustered is set and nothing past sigma is written.
+// Same outputs as jacobi_eig (batch 1); enqueues a fixed amount of work and never waits.
 // A must be 16-byte aligned with an even lda, and lda > k when k is odd (LRC_EINVAL
 // otherwise).
 size_t tridiag_workspace(int64_t k, int64_t ncols);
 lrc_status tridiag_eig(hipStream_t st, double* A, int64_t k, int64_t lda, int64_t ncols, float* sigma, float* Qt,
-                       void* ws, bool* clustered);
+                       void* ws);
 
 }  // namespace lrc

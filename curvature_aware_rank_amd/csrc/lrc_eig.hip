@@ -14,9 +14,12 @@
 //   * C <- J^T C J and V <- V J are applied tile by tile with fp64 MFMA
 //     (v_mfma_f64_16x16x4f64); diagonal pair tiles take the pair solver's result, and
 //     a pair that needed nothing contributes the identity.
-// A sweep in which no pair needed a rotation ends the iteration; the host reads one
-// counter per sweep.  Rotations are skipped when |a_pq| <= max(tol_r sqrt|a_pp a_qq|,
-// floor_rel * trace), which bounds what is left off the diagonal.
+// A sweep in which no pair needed a rotation ends the iteration: a per-item flag set on
+// the device at the end of that sweep turns every later launch for the item into an
+// immediate return, so the host enqueues a fixed number of sweeps and never waits.  An
+// item still rotating after the last sweep gets info = -1.  Rotations are skipped when
+// |a_pq| <= max(tol_r sqrt|a_pp a_qq|, floor_rel * trace), which bounds what is left off
+// the diagonal.
 #include <stdio.h>
 #include <stdlib.h>
 
@@ -32,7 +35,7 @@ constexpr int PD = 2 * JB;   // pair dimension
 constexpr int PP = PD + 1;   // LDS row pitch in doubles
 constexpr double TOL_R_DEFAULT = 1e-10;
 constexpr double FLOOR_REL_DEFAULT = 1e-12;
-constexpr int MAX_SWEEPS = 40;
+constexpr int MAX_SWEEPS = 40;   // sweeps enqueued per call (LRC_JACOBI_MAX_SWEEPS overrides, for tests)
 
 // work counters, filled only while measurement is on (see lrc_profile_start)
 enum : int { PROF_ROTATIONS, PROF_PAIRS_ACTIVE, PROF_V_TILES, PROF_C_TILES, PROF_C_PRODUCTS, PROF_C_DIAG, PROF_N };
@@ -88,6 +91,21 @@ __global__ void jacobi_init_kernel(double* __restrict__ A, double* __restrict__ 
 __global__ void zero_i32_kernel(int* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0;
+}
+
+// end of a sweep: an item whose sweep rotated nothing is done; the counters restart
+__global__ void jacobi_sweep_end_kernel(int* __restrict__ count, int* __restrict__ done, int batch) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= batch) return;
+  if (count[b] == 0) done[b] = 1;
+  count[b] = 0;
+}
+
+// after the last sweep: an item that never finished reports -1 (a Cholesky failure code
+// already in info is kept)
+__global__ void jacobi_info_kernel(const int* __restrict__ done, int32_t* __restrict__ info, int batch) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < batch && !done[b] && info[b] == 0) info[b] = -1;
 }
 
 // D(64x64) = op(X) * Y with X, Y in LDS (pitch PP).  transX: X element (i,k) read as X[k][i].
@@ -351,12 +369,14 @@ __global__ __launch_bounds__(256) void jacobi_pairs_v_kernel(
     const double* __restrict__ Ad, double* __restrict__ Vd, int kp, int64_t sA, int nb, int npair_wg, int round,
     double* __restrict__ Jcur, double* __restrict__ Scur, int* __restrict__ chcur, int prev_round,
     const double* __restrict__ Jprev, const int* __restrict__ chprev, int* __restrict__ sweep_count,
-    const double* __restrict__ floors, double tol_r, int max_inner, unsigned long long* __restrict__ prof) {
+    const int* __restrict__ done, const double* __restrict__ floors, double tol_r, int max_inner,
+    unsigned long long* __restrict__ prof) {
   __shared__ double L0[PD][PP];
   __shared__ double L1[PD][PP];
   __shared__ PairScratch ps;
   const int npairs = nb / 2, bt = blockIdx.y;
   const int t = blockIdx.x;
+  if (done[bt]) return;   // converged in an earlier sweep: nothing rotates, nothing is pending
   if (t < npair_wg) {
     pair_solve(L0, L1, ps, Ad, kp, sA, nb, round, t, Jcur, Scur, chcur, sweep_count, floors, tol_r, max_inner,
                prof);
@@ -375,10 +395,12 @@ __global__ __launch_bounds__(256) void jacobi_apply_c_kernel(double* __restrict_
                                                              int round, const double* __restrict__ Jbuf,
                                                              const double* __restrict__ Sbuf,
                                                              const int* __restrict__ changed,
+                                                             const int* __restrict__ done,
                                                              unsigned long long* __restrict__ prof) {
   __shared__ double T0[PD][PP];
   __shared__ double T1[PD][PP];
   const int bt = blockIdx.y, tid = threadIdx.x;
+  if (done[bt]) return;
   const int npairs = nb / 2;
   double* A = Ad + bt * sA;
   const int64_t jbase = int64_t(bt) * npairs * (PD * PD);
@@ -490,14 +512,15 @@ __global__ __launch_bounds__(256) void gather_sign_kernel(const double* __restri
     }
     __syncthreads();
   }
-  const double sgn = (v[bi[0]] < 0.0) ? -1.0 : 1.0;
+  // no entry compares above -1 only when every entry is NaN: the index stays in range
+  const double sgn = (v[min(bi[0], k - 1)] < 0.0) ? -1.0 : 1.0;
   float* out = Qt + (int64_t(bt) * ncols + c) * k;
   for (int j = threadIdx.x; j < k; j += 256) out[j] = float(sgn * v[j]);
 }
 
 struct JWs {
   double *V, *J, *S, *pad, *floor_v, *dvec;
-  int *changed, *count, *perm;
+  int *changed, *count, *done, *perm;
   unsigned long long* prof;
 };
 
@@ -513,6 +536,7 @@ JWs carve_jacobi(Carve& cv, int64_t k, int64_t batch) {
   w.dvec = cv.take<double>(size_t(batch * kp));
   w.changed = cv.take<int>(size_t(2 * batch * npairs));
   w.count = cv.take<int>(size_t(batch));
+  w.done = cv.take<int>(size_t(batch));
   w.perm = cv.take<int>(size_t(batch * k));
   w.prof = cv.take<unsigned long long>(PROF_N);
   return w;
@@ -523,6 +547,12 @@ double env_double(const char* name, double dflt) {
   const char* e = getenv(name);
   const double v = e ? atof(e) : 0.0;
   return v > 0.0 ? v : dflt;
+}
+
+int max_sweeps() {
+  const char* e = getenv("LRC_JACOBI_MAX_SWEEPS");
+  const int v = e ? atoi(e) : 0;
+  return v > 0 ? v : MAX_SWEEPS;
 }
 
 int inner_sweeps() {
@@ -554,7 +584,7 @@ lrc_status jacobi_eig(hipStream_t st, double* A, int64_t k, int64_t batch, int64
   const int max_inner = inner_sweeps();
   const double tol_r = env_double("LRC_JACOBI_TOL", TOL_R_DEFAULT);
   const double floor_rel = env_double("LRC_JACOBI_FLOOR", FLOOR_REL_DEFAULT);
-  const bool debug = getenv("LRC_DEBUG") != nullptr;
+  const int n_sweeps = max_sweeps();
 
   const bool prof_on = prof_enabled();
   unsigned long long* prof = prof_on ? w.prof : nullptr;
@@ -567,9 +597,11 @@ lrc_status jacobi_eig(hipStream_t st, double* A, int64_t k, int64_t batch, int64
   LRC_LAUNCHED();
   jacobi_init_kernel<<<dim3(unsigned(kp), unsigned(batch)), 256, 0, st>>>(A, w.V, int(k), int(kp), sA, w.pad);
   LRC_LAUNCHED();
+  zero_i32_kernel<<<unsigned(cdiv(batch, 256)), 256, 0, st>>>(w.count, int(batch));
+  LRC_LAUNCHED();
+  zero_i32_kernel<<<unsigned(cdiv(batch, 256)), 256, 0, st>>>(w.done, int(batch));
+  LRC_LAUNCHED();
 
-  std::vector<int> counts(size_t(batch), 0);
-  bool converged = false;
   const size_t jslot = size_t(batch) * npairs * PD * PD;
   const size_t cslot = size_t(batch) * npairs;
   int64_t g = 0;            // rounds launched so far, over all sweeps
@@ -581,34 +613,29 @@ lrc_status jacobi_eig(hipStream_t st, double* A, int64_t k, int64_t batch, int64
     ProfScope scope("jacobi_pairs_v_kernel", st, 0.0, 0.0);  // work is counted on the device
     jacobi_pairs_v_kernel<<<dim3(unsigned(npair_wg + nv), unsigned(batch)), 256, 0, st>>>(
         A, w.V, int(kp), sA, nb, npair_wg, round, w.J + cur * jslot, w.S + cur * jslot, w.changed + cur * cslot,
-        prev_round, w.J + prv * jslot, w.changed + prv * cslot, w.count, w.floor_v, tol_r, max_inner, prof);
+        prev_round, w.J + prv * jslot, w.changed + prv * cslot, w.count, w.done, w.floor_v, tol_r, max_inner, prof);
     LRC_LAUNCHED();
     pair_wgs += int64_t(npair_wg) * batch;
     return LRC_OK;
   };
-  for (int sweep = 0; sweep < MAX_SWEEPS && !converged; ++sweep) {
-    zero_i32_kernel<<<unsigned(cdiv(batch, 256)), 256, 0, st>>>(w.count, int(batch));
-    LRC_LAUNCHED();
+  // a fixed number of sweeps; items that finish early skip the rest on the device
+  for (int sweep = 0; sweep < n_sweeps; ++sweep) {
     for (int r = 0; r < nb - 1; ++r) {
       LRC_TRY(launch_pairs_v(npairs, r));
       const int cur = int(g & 1);
       {
         ProfScope scope("jacobi_apply_c_kernel", st, 0.0, 0.0);
         jacobi_apply_c_kernel<<<dim3(unsigned(n_ctiles), unsigned(batch)), 256, 0, st>>>(
-            A, int(kp), sA, nb, r, w.J + cur * jslot, w.S + cur * jslot, w.changed + cur * cslot, prof);
+            A, int(kp), sA, nb, r, w.J + cur * jslot, w.S + cur * jslot, w.changed + cur * cslot, w.done, prof);
         LRC_LAUNCHED();
       }
       prev_round = r;
       ++g;
     }
-    LRC_HIP(hipMemcpyAsync(counts.data(), w.count, sizeof(int) * size_t(batch), hipMemcpyDeviceToHost, st));
-    LRC_HIP(hipStreamSynchronize(st));
-    bool any = false;
-    for (int c : counts) any |= (c != 0);
-    if (debug) fprintf(stderr, "lrc jacobi k=%lld sweep %d: pairs rotated %d (item 0)\n", (long long)k, sweep, counts[0]);
-    converged = !any;
+    jacobi_sweep_end_kernel<<<unsigned(cdiv(batch, 256)), 256, 0, st>>>(w.count, w.done, int(batch));
+    LRC_LAUNCHED();
   }
-  // the last round's rotations still have to reach V
+  // an item still rotating at the end has its last round's rotations pending for V
   LRC_TRY(launch_pairs_v(0, 0));
 
   diag_kernel<<<dim3(unsigned(cdiv(kp, 256)), unsigned(batch)), 256, 0, st>>>(A, int(kp), sA, w.dvec);
@@ -623,7 +650,10 @@ lrc_status jacobi_eig(hipStream_t st, double* A, int64_t k, int64_t batch, int64
   gather_sign_kernel<<<dim3(unsigned(ncols), unsigned(batch)), 256, 0, st>>>(A, int(k), int(kp), sA, w.perm, Qt,
                                                                              int(ncols));
   LRC_LAUNCHED();
+  jacobi_info_kernel<<<unsigned(cdiv(batch, 256)), 256, 0, st>>>(w.done, info, int(batch));
+  LRC_LAUNCHED();
   if (prof_on) {
+    // the measurement session only: the device-side work counters are read back
     unsigned long long c[PROF_N];
     LRC_HIP(hipMemcpyAsync(c, w.prof, sizeof(c), hipMemcpyDeviceToHost, st));
     LRC_HIP(hipStreamSynchronize(st));
@@ -638,14 +668,6 @@ lrc_status jacobi_eig(hipStream_t st, double* A, int64_t k, int64_t batch, int64
     prof_add_work("jacobi_apply_c_kernel", double(c[PROF_C_PRODUCTS]) * FLOPS_PER_TILE_PRODUCT,
                   double(c[PROF_C_TILES]) * 2 * TILE_BYTES + double(c[PROF_C_PRODUCTS]) * TILE_BYTES +
                       double(c[PROF_C_DIAG]) * 2 * lower_bytes);
-  }
-  if (!converged) {
-    // mark every item that still rotated in the last sweep
-    std::vector<int32_t> inf(size_t(batch), 0);
-    for (int64_t b = 0; b < batch; ++b) inf[size_t(b)] = counts[size_t(b)] ? -1 : 0;
-    LRC_HIP(hipMemcpyAsync(info, inf.data(), sizeof(int32_t) * size_t(batch), hipMemcpyHostToDevice, st));
-    LRC_HIP(hipStreamSynchronize(st));
-    return LRC_ENOCONV;
   }
   return LRC_OK;
 }

@@ -56,10 +56,18 @@ __global__ __launch_bounds__(ST) void fsel_row_sq_kernel(const float* __restrict
 // channels g with err[g] < err[h], or err[g] == err[h] and g < h.  The keys are the
 // errors' bit patterns as unsigned integers (for the non-negative values here, and +inf,
 // the same order as the values; a NaN sorts after them), so the order is total and every
-// rank is distinct.  order[rank] = h; lowrank[h] = rank < n_lowrank.
+// rank is distinct.  order[rank] = h; lowrank[h] = rank < n_lowrank.  After a failed
+// Cholesky of X (chol_info != 0) the errors are meaningless: info gets the pivot and
+// nothing is written.
 __global__ __launch_bounds__(ST) void fsel_rank_kernel(const double* __restrict__ err, int n, int n_lowrank,
+                                                       const int* __restrict__ chol_info, int32_t* __restrict__ info,
                                                        int32_t* __restrict__ order, uint8_t* __restrict__ lowrank) {
   __shared__ uint64_t keys[KCH];
+  const int ci = *chol_info;
+  if (ci != 0) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) *info = ci;
+    return;
+  }
   const int h = blockIdx.x * ST + threadIdx.x;
   const uint64_t mine = h < n ? uint64_t(__double_as_longlong(err[h])) : 0;
   int rank = 0;
@@ -134,17 +142,8 @@ extern "C" lrc_status lrc_ffn_select_channels(const float* w_gate, const float* 
   LRC_LAUNCHED();
   fsel_fill_i32_kernel<<<1, 64, 0, st>>>(info, 1, 0);
   LRC_LAUNCHED();
+  // a failed pivot is acted on by the rank kernel, on the device
   LRC_TRY(cholesky_f32(st, Xsum, ldx, d, n_x, damping, w.lx, w.info));
-  {
-    int ci = 0;
-    LRC_HIP(hipMemcpyAsync(&ci, w.info, sizeof(ci), hipMemcpyDeviceToHost, st));
-    LRC_HIP(hipStreamSynchronize(st));
-    if (ci != 0) {
-      fsel_fill_i32_kernel<<<1, 64, 0, st>>>(info, 1, ci);
-      LRC_LAUNCHED();
-      return LRC_ENOTPD;
-    }
-  }
   const float* Ws[2] = {w_gate, w_up};
   const float* Ls[2] = {left_gate, left_up};
   const float* Rs[2] = {right_gate, right_up};
@@ -160,7 +159,8 @@ extern "C" lrc_status lrc_ffn_select_channels(const float* w_gate, const float* 
     fsel_row_sq_kernel<<<unsigned(d_ff), ST, 0, st>>>(w.E, d, int(d), p, err);
     LRC_LAUNCHED();
   }
-  fsel_rank_kernel<<<unsigned(cdiv(d_ff, ST)), ST, 0, st>>>(err, int(d_ff), int(n_lowrank), order, lowrank);
+  fsel_rank_kernel<<<unsigned(cdiv(d_ff, ST)), ST, 0, st>>>(err, int(d_ff), int(n_lowrank), w.info, info, order,
+                                                           lowrank);
   LRC_LAUNCHED();
   return LRC_OK;
 }

@@ -298,19 +298,27 @@ __global__ __launch_bounds__(256) void fisher_mfma_kernel(const uint16_t* __rest
     partial[int64_t(tt) * k + c0 + tid] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
 }
 
+// A score is a sum of non-negative terms over the tokens: a NaN or Inf in the tokens or
+// the factors (or an overflow) leaves it non-finite, which sets *info (when given).
 __global__ void fisher_final_kernel(const float* __restrict__ partial, int ntb, int k, int accumulate, int finalize,
-                                    double inv2n, float* __restrict__ scores) {
+                                    double inv2n, float* __restrict__ scores, int32_t* __restrict__ info) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= k) return;
   double s = accumulate ? double(scores[i]) : 0.0;
   for (int b = 0; b < ntb; ++b) s += double(partial[int64_t(b) * k + i]);
   if (finalize) s *= inv2n;
-  scores[i] = float(s);
+  const float f = float(s);
+  scores[i] = f;
+  if (info && !isfinite(f)) *info = LRC_ENONFINITE;
 }
 
-__global__ void kfac_kernel(const float* __restrict__ sigma, int k, float* __restrict__ scores) {
+__global__ void kfac_kernel(const float* __restrict__ sigma, int k, float* __restrict__ scores,
+                            int32_t* __restrict__ info) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < k) scores[i] = 0.5f * sigma[i] * sigma[i];
+  if (i >= k) return;
+  const float f = 0.5f * sigma[i] * sigma[i];
+  scores[i] = f;
+  if (info && !isfinite(f)) *info = LRC_ENONFINITE;
 }
 
 }  // namespace
@@ -356,13 +364,13 @@ extern "C" size_t lrc_score_components_workspace(int64_t n_tokens, int64_t d_in,
 extern "C" lrc_status lrc_score_components(const void* A, const void* B, lrc_dtype dt, int64_t n_tokens, int64_t d_in,
                                            int64_t d_out, const float* left, const float* right, const float* sigma,
                                            int64_t k, uint32_t flags, int accumulate, int finalize, int64_t n_total,
-                                           float* scores, void* ws, size_t ws_bytes, void* stream) {
+                                           float* scores, int32_t* info, void* ws, size_t ws_bytes, void* stream) {
   if (flags != LRC_SCORE_FISHER && flags != LRC_SCORE_KFAC) return LRC_EDTYPE;
   if (scores == nullptr || k <= 0 || k > (int64_t(1) << 30)) return LRC_EINVAL;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (flags == LRC_SCORE_KFAC) {
     if (sigma == nullptr) return LRC_EINVAL;
-    kfac_kernel<<<unsigned(cdiv(k, 256)), 256, 0, st>>>(sigma, int(k), scores);
+    kfac_kernel<<<unsigned(cdiv(k, 256)), 256, 0, st>>>(sigma, int(k), scores, info);
     LRC_LAUNCHED();
     return LRC_OK;
   }
@@ -405,7 +413,7 @@ extern "C" lrc_status lrc_score_components(const void* A, const void* B, lrc_dty
       LRC_LAUNCHED();
     }
     fisher_final_kernel<<<unsigned(cdiv(k, 256)), 256, 0, st>>>(w.partial, n_tt, int(k), accumulate, finalize, inv2n,
-                                                                 scores);
+                                                                 scores, info);
     LRC_LAUNCHED();
     return LRC_OK;
   }
@@ -431,7 +439,7 @@ extern "C" lrc_status lrc_score_components(const void* A, const void* B, lrc_dty
     LRC_LAUNCHED();
   }
   fisher_final_kernel<<<unsigned(cdiv(k, 256)), 256, 0, st>>>(partial, ntb, int(k), accumulate, finalize, inv2n,
-                                                               scores);
+                                                               scores, info);
   LRC_LAUNCHED();
   return LRC_OK;
 }

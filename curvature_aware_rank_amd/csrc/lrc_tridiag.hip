@@ -12,14 +12,15 @@
 //          with alpha = -tau/2 (w^T v), stores v and w, and brings the next column up to
 //          date with the panel so far (its squared norm goes to per-block partials).
 //      The reflector of column i (v[i+1] = 1) is stored in column i below the diagonal.
-//   2. All eigenvalues of T by Sturm-count multisection (16 points per step, 14 steps).
+//   2. All eigenvalues of T by Sturm-count multisection (16 points per step, 12 steps).
 //   3. Eigenvectors of the wanted (largest) eigenvalues by inverse iteration on T with
 //      partial pivoting, two solves (the eigenvalues are accurate to ~eps ||T||): the
-//      factorisation and first solve of every vector in parallel, then per cluster of
-//      eigenvalues closer than 1e-7 ||T|| (a lone one is a cluster of one) the second
-//      solves in turn, each iterate orthogonalised against the cluster's finished vectors
-//      (modified Gram-Schmidt).  Clusters larger than 32 are reported to the caller, which
-//      then uses the Jacobi solver.
+//      factorisation and both solves of every vector in parallel; after each solve, per
+//      cluster of eigenvalues closer than 1e-7 ||T|| (a lone one is a cluster of one),
+//      each iterate is orthogonalised against the cluster's earlier vectors and
+//      normalised (one wave per cluster of up to 32 members, modified Gram-Schmidt; a
+//      workgroup per longer cluster, block Gram-Schmidt applied twice).  Nothing is read
+//      back to the host: the whole solve is enqueued at once.
 //   4. Back-transformation Z <- Q Z in blocks of 128 reflectors, I - V T V^T (T from the
 //      forward columnwise recurrence on V^T V).
 // Every reduction has a fixed order, so equal inputs give equal bits.
@@ -47,7 +48,7 @@ constexpr int NPB = 4 * WPB;    // squared-norm partials per 64-row block (one p
 constexpr int BIS_PTS = 16;     // Sturm points per eigenvalue per multisection step
 constexpr int BIS_ITERS = 12;   // 17^12 > 2^49: width below 2^-48 of the bounds, under a count's own n eps accuracy
 constexpr int BIS_STAGE = 2048; // d, e^2 staged through LDS in chunks of this many
-constexpr int CL_MAX = 32;      // largest cluster inverse iteration handles
+constexpr int CL_MAX = 32;      // larger clusters are orthogonalised by a whole workgroup
 constexpr double CL_TOL = 1e-7; // eigenvalues closer than CL_TOL ||T|| share a cluster
 constexpr double EPS = 2.220446049250313e-16;
 
@@ -885,10 +886,12 @@ __global__ __launch_bounds__(256) void tri_bisect_kernel(const double* __restric
   if (pt == 0 && mi < n) lam[mi] = 0.5 * (lo + hi);
 }
 
-// ---- 3. clusters among the wanted eigenvalues (descending order j = 0 .. ncols-1)
+// ---- 3. clusters among the wanted eigenvalues (descending order j = 0 .. ncols-1): the
+// length at each cluster's first member (0 at the others), and the first members of the
+// clusters longer than CL_MAX in a list (in any order: each is processed on its own)
 __global__ void tri_cluster_kernel(const double* __restrict__ lam, int n, int ncols,
                                    const double* __restrict__ bounds, int* __restrict__ clen,
-                                   int* __restrict__ flag) {
+                                   int* __restrict__ nbig, int* __restrict__ big) {
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= ncols) return;
   const double ctol = CL_TOL * bounds[3];
@@ -900,7 +903,7 @@ __global__ void tri_cluster_kernel(const double* __restrict__ lam, int n, int nc
   int len = 1;
   while (j + len < ncols && !(lam[n - j - len] - lam[n - 1 - j - len] > ctol)) ++len;
   clen[j] = len;
-  if (len > CL_MAX) atomicMax(flag, len);
+  if (len > CL_MAX) big[atomicAdd(nbig, 1)] = j;
 }
 
 __device__ __forceinline__ double start_value(int j, int k) {
@@ -962,10 +965,9 @@ constexpr int CPLL = CHL / 64;
 __global__ __launch_bounds__(64) void tri_inviter_a_kernel(const double* __restrict__ d, const double* __restrict__ e,
                                                            int n, const double* __restrict__ lam, int ncols,
                                                            const double* __restrict__ bounds,
-                                                           const int* __restrict__ clen, const int* __restrict__ flag,
+                                                           const int* __restrict__ clen,
                                                            double* __restrict__ Rt, uint8_t* __restrict__ PVt,
                                                            double* __restrict__ Z) {
-  if (*flag) return;
   const int lane = threadIdx.x;
   const int jr = blockIdx.x * 64 + lane;
   const int jv = min(jr, ncols - 1);   // lanes past the last vector repeat it
@@ -1163,32 +1165,29 @@ __device__ void inv_scale(double* __restrict__ z, int64_t zs, int n, double sc) 
 }
 
 // first solve's back-substitution, one wave per vector; its squared norm to nrm[j]
-__global__ __launch_bounds__(64) void tri_inviter_u_kernel(int n, int ncols, const int* __restrict__ flag,
-                                                           const double* __restrict__ Rt, double* __restrict__ Z,
-                                                           double* __restrict__ nrm) {
+__global__ __launch_bounds__(64) void tri_inviter_u_kernel(int n, int ncols, const double* __restrict__ Rt,
+                                                           double* __restrict__ Z, double* __restrict__ nrm) {
   __shared__ double s_in[2][CHL][4];
   __shared__ double s_z[2][CHL];
   __shared__ double s_out[CHL];
   __shared__ double s_sc[1];
-  if (*flag) return;
   const int jv = blockIdx.x;
   const double n1 = inv_usolve_lds(Rt + int64_t(jv) * 4, int64_t(ncols) * 4, Z + jv, ncols, n, s_in, s_z, s_out, s_sc);
   if (threadIdx.x == 0) nrm[jv] = n1;
 }
 
-// one wave per cluster of two or more (final = 0) or per cluster of any size (final = 1):
-// members in order, orthogonalise against the cluster's earlier members (modified
-// Gram-Schmidt, those already normalised) and normalise (scl = 1).  A lone vector's final
-// normalisation is left to the output kernel: scl = 1 / ||z|| from the squared norm its
-// solve recorded (scaling commutes with the back-transformation); only a norm outside
-// [1e-100, 1e100] is applied here.
+// one wave per cluster of two to CL_MAX members (final = 0) or of at most CL_MAX members
+// (final = 1): members in order, orthogonalise against the cluster's earlier members
+// (modified Gram-Schmidt, those already normalised) and normalise (scl = 1).  A lone
+// vector's final normalisation is left to the output kernel: scl = 1 / ||z|| from the
+// squared norm its solve recorded (scaling commutes with the back-transformation); only a
+// norm outside [1e-100, 1e100] is applied here.  Longer clusters: tri_inviter_obig_kernel.
 __global__ __launch_bounds__(64) void tri_inviter_o_kernel(int n, int ncols, int final, const int* __restrict__ clen,
-                                                           const int* __restrict__ flag, double* __restrict__ Z,
-                                                           const double* __restrict__ nrm, double* __restrict__ scl) {
-  if (*flag) return;
+                                                           double* __restrict__ Z, const double* __restrict__ nrm,
+                                                           double* __restrict__ scl) {
   const int j = blockIdx.x;
   const int len = clen[j];
-  if (len == 0 || (len == 1 && !final)) return;
+  if (len == 0 || len > CL_MAX || (len == 1 && !final)) return;
   const int lane = threadIdx.x;
   if (len == 1) {
     const double s2 = nrm[j];
@@ -1224,11 +1223,114 @@ __global__ __launch_bounds__(64) void tri_inviter_o_kernel(int n, int ncols, int
   }
 }
 
+constexpr int OB_T = 1024;          // threads per long cluster (16 waves)
+constexpr int OB_W = OB_T / 64;
+constexpr int OB_CH = 256;          // earlier members per chunk of a Gram-Schmidt pass
+constexpr int OB_U = OB_CH / 64;
+
+// sum (op 0) or max (op 1) over the workgroup, the same value to every thread; waves'
+// results combined in wave order
+__device__ double ob_reduce(double v, int op, double* __restrict__ red) {
+  v = op == 0 ? wave_sum(v) : wave_max(v);
+  __syncthreads();   // red is free
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double r = red[0];
+  for (int w = 1; w < OB_W; ++w) r = op == 0 ? r + red[w] : fmax(r, red[w]);
+  return r;
+}
+
+// one workgroup per cluster of more than CL_MAX members (first members listed in big[]):
+// members in order, each orthogonalised against the cluster's earlier, already normalised
+// members by two block Gram-Schmidt passes (chunks of OB_CH earlier members: all the
+// chunk's projections from one set of dot products, chunks in order), then normalised
+// (scl = 1 when final).  The cluster occupies contiguous columns of Z, so a wave reading
+// the chunk's entries of one row reads consecutive addresses.  Dot products: wave w sums
+// rows w, w + 16, ..., the 16 wave partials are added in wave order.
+__global__ __launch_bounds__(OB_T) void tri_inviter_obig_kernel(int n, int ncols, int final,
+                                                               const int* __restrict__ clen,
+                                                               const int* __restrict__ nbig,
+                                                               const int* __restrict__ big, double* __restrict__ Z,
+                                                               double* __restrict__ scl) {
+  __shared__ double part[OB_W][OB_CH];
+  __shared__ double dots[OB_CH];
+  __shared__ double red[OB_W];
+  if (int(blockIdx.x) >= *nbig) return;
+  const int j = big[blockIdx.x];
+  const int len = clen[j];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int q = 0; q < len; ++q) {
+    const int jq = j + q;
+    for (int pass = 0; pass < 2 && q > 0; ++pass) {
+      for (int p0 = 0; p0 < q; p0 += OB_CH) {
+        const int pc = min(OB_CH, q - p0);
+        double acc[OB_U];
+#pragma unroll
+        for (int u = 0; u < OB_U; ++u) acc[u] = 0.0;
+        for (int k = wv; k < n; k += OB_W) {
+          const double* row = Z + int64_t(k) * ncols + j + p0;
+          const double zk = Z[int64_t(k) * ncols + jq];
+#pragma unroll
+          for (int u = 0; u < OB_U; ++u) {
+            const int p = lane + 64 * u;
+            if (p < pc) acc[u] = fma(row[p], zk, acc[u]);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < OB_U; ++u) part[wv][lane + 64 * u] = acc[u];
+        __syncthreads();
+        if (tid < pc) {
+          double t = part[0][tid];
+          for (int w = 1; w < OB_W; ++w) t += part[w][tid];
+          dots[tid] = t;
+        }
+        __syncthreads();
+        for (int k = wv; k < n; k += OB_W) {
+          const double* row = Z + int64_t(k) * ncols + j + p0;
+          double t = 0.0;
+#pragma unroll
+          for (int u = 0; u < OB_U; ++u) {
+            const int p = lane + 64 * u;
+            if (p < pc) t = fma(dots[p], row[p], t);
+          }
+          t = wave_sum(t);
+          if (lane == 0) Z[int64_t(k) * ncols + jq] -= t;
+        }
+        __syncthreads();   // the updated member is read by the next chunk or pass
+      }
+    }
+    double s2 = 0.0;
+    for (int k = tid; k < n; k += OB_T) {
+      const double v = Z[int64_t(k) * ncols + jq];
+      s2 = fma(v, v, s2);
+    }
+    s2 = ob_reduce(s2, 0, red);
+    double sc;
+    if (s2 > 0.0 && s2 < 1e300) {
+      sc = 1.0 / sqrt(s2);
+    } else {   // badly scaled: the norm after scaling by the largest entry
+      double mx = 0.0;
+      for (int k = tid; k < n; k += OB_T) mx = fmax(mx, fabs(Z[int64_t(k) * ncols + jq]));
+      mx = ob_reduce(mx, 1, red);
+      const double inv_mx = mx > 0.0 && mx < 1e308 ? 1.0 / mx : 1.0;
+      double t2 = 0.0;
+      for (int k = tid; k < n; k += OB_T) {
+        const double v = Z[int64_t(k) * ncols + jq] * inv_mx;
+        t2 = fma(v, v, t2);
+      }
+      t2 = ob_reduce(t2, 0, red);
+      sc = t2 > 0.0 ? inv_mx / sqrt(t2) : 1.0;
+    }
+    for (int k = tid; k < n; k += OB_T) Z[int64_t(k) * ncols + jq] *= sc;
+    if (tid == 0 && final) scl[jq] = 1.0;
+    __syncthreads();   // the normalised member is read by the next members' passes
+  }
+}
+
 // second solve, one wave per vector: y = L^-1 P (sc z), then U^-1 y; its squared norm to
 // nrm[j].  A lone vector's iterate is normalised on the fly (sc from its recorded norm);
 // cluster members were normalised by the cluster kernel (sc = 1).
 __global__ __launch_bounds__(64) void tri_inviter_s_kernel(int n, int ncols, const int* __restrict__ clen,
-                                                           const int* __restrict__ flag,
                                                            const double* __restrict__ Rt,
                                                            const uint8_t* __restrict__ PVt,
                                                            double* __restrict__ Z, double* __restrict__ nrm) {
@@ -1238,7 +1340,6 @@ __global__ __launch_bounds__(64) void tri_inviter_s_kernel(int n, int ncols, con
   __shared__ uint8_t s_piv[2][CHL];
   __shared__ double s_zx[2];
   __shared__ double s_sc[1];
-  if (*flag) return;
   const int jv = blockIdx.x;
   const int lane = threadIdx.x;
   const int nm1 = n - 1;
@@ -1658,7 +1759,7 @@ __global__ __launch_bounds__(256) void tri_out_kernel(const double* __restrict__
 
 struct TWs {
   double *P, *S, *SV, *SW, *npart, *x0, *xv, *d, *e, *tau, *Wp, *lam, *bounds, *U, *Z, *nrm, *scl, *Gp, *T, *Yp, *Yr, *Y2;
-  int *clen, *flag;
+  int *clen, *nbig, *big;
   uint8_t* piv;
 };
 
@@ -1693,7 +1794,8 @@ TWs carve_tri(Carve& cv, int64_t n, int64_t ncols) {
   w.nrm = cv.take<double>(size_t(ncols));
   w.scl = cv.take<double>(size_t(ncols));
   w.clen = cv.take<int>(size_t(ncols));
-  w.flag = cv.take<int>(1);
+  w.nbig = cv.take<int>(1);
+  w.big = cv.take<int>(size_t(ncols));
   return w;
 }
 
@@ -1774,8 +1876,7 @@ size_t tridiag_workspace(int64_t k, int64_t ncols) {
 }
 
 lrc_status tridiag_eig(hipStream_t st, double* A, int64_t k, int64_t lda, int64_t ncols_in, float* sigma, float* Qt,
-                       void* ws, bool* clustered) {
-  *clustered = false;
+                       void* ws) {
   // the symv kernel reads 16-byte column pairs: even pitch, 16-byte base, padding after
   // an odd last column
   if (lda % 2 != 0 || (k % 2 != 0 && lda < k + 1) || reinterpret_cast<uintptr_t>(A) % 16 != 0) return LRC_EINVAL;
@@ -1799,33 +1900,36 @@ lrc_status tridiag_eig(hipStream_t st, double* A, int64_t k, int64_t lda, int64_
   LRC_LAUNCHED();
 
   // 3. clusters and inverse iteration
-  zero_int_kernel<<<1, 64, 0, st>>>(w.flag, 1);
+  zero_int_kernel<<<1, 64, 0, st>>>(w.nbig, 1);
   LRC_LAUNCHED();
-  tri_cluster_kernel<<<unsigned(cdiv(ncols, 256)), 256, 0, st>>>(w.lam, n, ncols, w.bounds, w.clen, w.flag);
+  tri_cluster_kernel<<<unsigned(cdiv(ncols, 256)), 256, 0, st>>>(w.lam, n, ncols, w.bounds, w.clen, w.nbig, w.big);
   LRC_LAUNCHED();
-  int flag = 0;
-  LRC_HIP(hipMemcpyAsync(&flag, w.flag, sizeof(int), hipMemcpyDeviceToHost, st));
-  LRC_HIP(hipStreamSynchronize(st));
-  if (flag) {
-    *clustered = true;
-    return LRC_OK;
-  }
   {
     ProfScope scope("tri_inviter_a_kernel", st, 0.0, 0.0);
-    tri_inviter_a_kernel<<<unsigned(cdiv(ncols, 64)), 64, 0, st>>>(w.d, w.e, n, w.lam, ncols, w.bounds, w.clen,
-                                                                    w.flag, w.U, w.piv, w.Z);
+    tri_inviter_a_kernel<<<unsigned(cdiv(ncols, 64)), 64, 0, st>>>(w.d, w.e, n, w.lam, ncols, w.bounds, w.clen, w.U,
+                                                                    w.piv, w.Z);
     LRC_LAUNCHED();
   }
   {
-    ProfScope scope("tri_inviter_u_o_s_kernels", st, 0.0, 0.0);  // the four solve and orthogonalisation launches together
-    tri_inviter_u_kernel<<<unsigned(ncols), 64, 0, st>>>(n, ncols, w.flag, w.U, w.Z, w.nrm);
+    // the solve and orthogonalisation launches together; clusters longer than CL_MAX
+    // (at most ncols / (CL_MAX + 1) of them) get a workgroup each
+    ProfScope scope("tri_inviter_u_o_s_kernels", st, 0.0, 0.0);
+    const int max_big = ncols / (CL_MAX + 1);
+    tri_inviter_u_kernel<<<unsigned(ncols), 64, 0, st>>>(n, ncols, w.U, w.Z, w.nrm);
     LRC_LAUNCHED();
-    tri_inviter_o_kernel<<<unsigned(ncols), 64, 0, st>>>(n, ncols, 0, w.clen, w.flag, w.Z, w.nrm, w.scl);
-    LRC_LAUNCHED();
-    tri_inviter_s_kernel<<<unsigned(ncols), 64, 0, st>>>(n, ncols, w.clen, w.flag, w.U, w.piv, w.Z, w.nrm);
-    LRC_LAUNCHED();
-    tri_inviter_o_kernel<<<unsigned(ncols), 64, 0, st>>>(n, ncols, 1, w.clen, w.flag, w.Z, w.nrm, w.scl);
-    LRC_LAUNCHED();
+    for (int fin = 0; fin < 2; ++fin) {
+      if (fin == 1) {
+        tri_inviter_s_kernel<<<unsigned(ncols), 64, 0, st>>>(n, ncols, w.clen, w.U, w.piv, w.Z, w.nrm);
+        LRC_LAUNCHED();
+      }
+      tri_inviter_o_kernel<<<unsigned(ncols), 64, 0, st>>>(n, ncols, fin, w.clen, w.Z, w.nrm, w.scl);
+      LRC_LAUNCHED();
+      if (max_big > 0) {
+        tri_inviter_obig_kernel<<<unsigned(max_big), OB_T, 0, st>>>(n, ncols, fin, w.clen, w.nbig, w.big, w.Z,
+                                                                     w.scl);
+        LRC_LAUNCHED();
+      }
+    }
   }
 
   // 4. back-transformation

@@ -23,11 +23,15 @@
  *     from the caller's workspace `ws` of at least the size the matching *_workspace
  *     query returns (256-byte aligned, contents need not be initialised).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Kernels are enqueued on
- *     it.  lrc_accumulate_cov, lrc_score_components and lrc_allocate_ranks do not block
- *     the host.  lrc_whiten_decompose blocks the host on `stream` (it reads device
- *     convergence flags between eigensolver sweeps), see below.
+ *     it and no entry point waits for them: every call returns as soon as its work is
+ *     enqueued (only lrc_profile_stop, a measurement call, waits for its events).
  *   - Return value: LRC_OK, or an error found before or while enqueueing work.
  *     Argument errors are detected on the host before any HIP call is made.
+ *   - Failures found by the kernels themselves (a covariance that is not positive
+ *     definite, an eigensolver that hit its sweep cap, a NaN or Inf in the data) are
+ *     written to a device `info` argument; the caller reads it after its own
+ *     synchronisation.  The outputs of a call whose info reports a failure are undefined
+ *     unless the entry point says otherwise.
  */
 #ifndef LRC_H
 #define LRC_H
@@ -83,11 +87,16 @@ typedef enum { LRC_F32 = 0, LRC_BF16 = 1 } lrc_dtype;
  *    formed as q_i * (s_t^2 q_j) with s_t^2 q_j split into two bf16 terms (error ~2^-17).
  * Accumulation is fp32 with bf16 x bf16 products exact; the split of the token range
  * over workgroups and its reduction order are fixed, so equal inputs give equal bits.
+ * info: device int32, or NULL for no check.  Set to LRC_ENONFINITE when a diagonal entry
+ *    of C comes out NaN or Inf after this call (a diagonal entry is a sum of squares, so
+ *    that happens exactly when a token entry of its column is NaN/Inf, when the sum
+ *    overflows, or when C held a non-finite diagonal already); never cleared, so a stream
+ *    of chunks can share one flag initialised to 0 by the caller.
  * n_tokens == 0 is a no-op (A may be NULL).
  */
 lrc_status lrc_accumulate_cov(const void* A, lrc_dtype dt, int64_t n_tokens, int64_t d,
                               int64_t lda, float* C, int64_t ldc, uint32_t flags,
-                              void* ws, size_t ws_bytes, void* stream);
+                              int32_t* info, void* ws, size_t ws_bytes, void* stream);
 size_t lrc_accumulate_cov_workspace(lrc_dtype dt, int64_t n_tokens, int64_t d, uint32_t flags);
 
 /*
@@ -115,10 +124,13 @@ size_t lrc_accumulate_cov_workspace(lrc_dtype dt, int64_t n_tokens, int64_t d, u
  *    NULL.  Gsum: d_out x d_out (lower read), leading dim ldg, or NULL.  n_x, n_g > 0
  *    when the matching sum is given.  rank: 0 <= r <= k.  damping >= 0.
  * Outputs (packed, fp32): sigma[batch][k], left[batch][d_out][r], right[batch][r][d_in].
- * info (device int32[batch]): 0 ok; p in 1..d_in: pivot p of X not positive;
- *    d_in + p: pivot p of G not positive; -1: eigensolver hit its sweep cap.
- * Returns LRC_ENOTPD / LRC_ENOCONV when any info entry reports that (the outputs of the
- * affected slices are then undefined).  Blocks the host on `stream`.
+ * info (device int32[batch], written by the call): 0 ok; p in 1..d_in: pivot p of X not
+ *    positive (LRC_ENOTPD condition; every slice reports it); d_in + p: pivot p of G not
+ *    positive; -1: the Jacobi solver (batches, and k < 512) still rotated after its last
+ *    sweep (LRC_ENOCONV condition).  The outputs of a slice with nonzero info are
+ *    undefined.  These conditions are found on the device: the call itself returns LRC_OK
+ *    once everything is enqueued (the solver's work is fixed in advance, so nothing is
+ *    read back to the host).
  */
 lrc_status lrc_whiten_decompose(const float* W, int64_t d_out, int64_t d_in, int64_t ldw,
                                 int64_t batch, int64_t stride_w,
@@ -145,12 +157,16 @@ size_t lrc_whiten_decompose_workspace(int64_t d_out, int64_t d_in, int64_t batch
  * (scores are overwritten by this chunk's sum), later calls accumulate=1; the call with
  * finalize=1 scales the running sum by 1/(2*n_total).  KFAC ignores A, B, accumulate.
  * The per-token products are formed on fp32 values; the reduction order is fixed.
+ * info: device int32, or NULL for no check.  Set to LRC_ENONFINITE when a score written
+ *    by this call is NaN or Inf (each is a sum of non-negative terms, so a NaN/Inf in A,
+ *    B or the factors, or an overflow, shows up there); never cleared by the library.
  */
 lrc_status lrc_score_components(const void* A, const void* B, lrc_dtype dt, int64_t n_tokens,
                                 int64_t d_in, int64_t d_out, const float* left,
                                 const float* right, const float* sigma, int64_t k,
                                 uint32_t flags, int accumulate, int finalize, int64_t n_total,
-                                float* scores, void* ws, size_t ws_bytes, void* stream);
+                                float* scores, int32_t* info, void* ws, size_t ws_bytes,
+                                void* stream);
 size_t lrc_score_components_workspace(int64_t n_tokens, int64_t d_in, int64_t d_out, int64_t k,
                                       uint32_t flags);
 
@@ -171,7 +187,9 @@ size_t lrc_score_components_workspace(int64_t n_tokens, int64_t d_in, int64_t d_
  * Outputs (device): order[M] (int32 item ids in sorted order), n_kept (one int64),
  *   ranks[n_mat] (int32 kept count per matrix), kept_mask[M] (uint8 0/1),
  *   info (one int32: 0 ok, LRC_ENONFINITE if a score is NaN/Inf or negative,
- *   LRC_EINVAL if a cost is <= 0 or offsets are inconsistent).
+ *   LRC_EINVAL if a cost is <= 0 or offsets are inconsistent).  A call with nonzero info
+ *   keeps nothing: n_kept = 0, kept_mask and ranks all zero (order is still a
+ *   permutation, with no meaning).
  * Identical inputs give identical outputs bit for bit.  M must be < 2^31.
  */
 lrc_status lrc_allocate_ranks(const float* scores, const int64_t* offsets, const int64_t* cost,
@@ -252,8 +270,9 @@ lrc_status lrc_quantize_rows(const float* X, int64_t rows, int64_t cols, int64_t
  * Outputs (device): err double[d_ff]; order int32[d_ff]: the channels by ascending err,
  *   ties by channel index; lowrank uint8[d_ff]: 1 for the first n_lowrank channels of
  *   `order` (0 <= n_lowrank <= d_ff), else 0.
- * info (device int32[1]): 0, or p when pivot p of X is not positive (then LRC_ENOTPD and
- *   the outputs are not written).  Blocks the host on `stream` once (after the Cholesky).
+ * info (device int32[1], written by the call): 0, or p when pivot p of X is not positive
+ *   (the LRC_ENOTPD condition; order and lowrank are then not written and err holds no
+ *   meaningful values).  Found on the device: the call returns LRC_OK once enqueued.
  */
 lrc_status lrc_ffn_select_channels(const float* w_gate, const float* w_up, int64_t d_ff, int64_t d, int64_t ldw,
                                    const float* left_gate, const float* right_gate, const float* left_up,

@@ -255,13 +255,17 @@ def allocate(scores_per_matrix, costs, budget):
     rank is the number of its kept components.
 
     scores_per_matrix: list of 1-D float32 arrays; costs: list of ints; budget: int.
-    Returns (order, n_kept, ranks, kept_mask) with order a list of global item ids."""
+    Returns (order, n_kept, ranks, kept_mask) with order a list of global item ids.
+    A score is an importance (a sum of squares, or half a squared singular value), so
+    NaN, infinite and negative scores are rejected, as are costs that are not positive."""
     mat, idx, sc, cst = [], [], [], []
     for m, s in enumerate(scores_per_matrix):
+        if int(costs[m]) <= 0:
+            raise ValueError("cost must be positive")
         s = np.asarray(s, dtype=np.float32)
         for i, v in enumerate(s.tolist()):
-            if v != v:
-                raise ValueError("NaN score")
+            if v != v or v in (float("inf"), float("-inf")) or v < 0.0:
+                raise ValueError("score must be finite and non-negative")
             mat.append(m)
             idx.append(i)
             sc.append(v)

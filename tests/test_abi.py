@@ -41,17 +41,18 @@ def test_status_strings(lib):
 
 def test_accumulate_cov_validation(lib):
     f = lib.lrc_accumulate_cov
-    assert f(FAKE, 7, 10, 4, 4, FAKE, 4, 0, FAKE, 1 << 30, None) == EDTYPE          # dtype
-    assert f(FAKE, 1, 10, 4, 4, FAKE, 4, 0x8, FAKE, 1 << 30, None) == EDTYPE        # flags
-    assert f(None, 1, 10, 4, 4, FAKE, 4, 0, FAKE, 1 << 30, None) == EINVAL          # A null
-    assert f(FAKE, 1, 10, 4, 4, None, 4, 0, FAKE, 1 << 30, None) == EINVAL          # C null
-    assert f(FAKE, 1, 10, 4, 3, FAKE, 4, 0, FAKE, 1 << 30, None) == EINVAL          # lda < d
-    assert f(FAKE, 1, 10, 4, 4, FAKE, 3, 0, FAKE, 1 << 30, None) == EINVAL          # ldc < d
-    assert f(FAKE, 1, -1, 4, 4, FAKE, 4, 0, FAKE, 1 << 30, None) == EINVAL          # n < 0
-    assert f(None, 1, 0, 4, 4, FAKE, 4, 0, None, 0, None) == 0                      # empty: no-op
+    # (A, dt, n, d, lda, C, ldc, flags, info, ws, ws_bytes, stream)
+    assert f(FAKE, 7, 10, 4, 4, FAKE, 4, 0, None, FAKE, 1 << 30, None) == EDTYPE          # dtype
+    assert f(FAKE, 1, 10, 4, 4, FAKE, 4, 0x8, None, FAKE, 1 << 30, None) == EDTYPE        # flags
+    assert f(None, 1, 10, 4, 4, FAKE, 4, 0, None, FAKE, 1 << 30, None) == EINVAL          # A null
+    assert f(FAKE, 1, 10, 4, 4, None, 4, 0, None, FAKE, 1 << 30, None) == EINVAL          # C null
+    assert f(FAKE, 1, 10, 4, 3, FAKE, 4, 0, FAKE, FAKE, 1 << 30, None) == EINVAL          # lda < d
+    assert f(FAKE, 1, 10, 4, 4, FAKE, 3, 0, FAKE, FAKE, 1 << 30, None) == EINVAL          # ldc < d
+    assert f(FAKE, 1, -1, 4, 4, FAKE, 4, 0, None, FAKE, 1 << 30, None) == EINVAL          # n < 0
+    assert f(None, 1, 0, 4, 4, FAKE, 4, 0, None, None, 0, None) == 0                      # empty: no-op
     need = lib.lrc_accumulate_cov_workspace(1, 4096, 256, 0)
     assert need > 0
-    assert f(FAKE, 1, 4096, 256, 256, FAKE, 256, 0, FAKE, need - 1, None) == EWORKSPACE
+    assert f(FAKE, 1, 4096, 256, 256, FAKE, 256, 0, FAKE, FAKE, need - 1, None) == EWORKSPACE
     # QAW needs more scratch than plain accumulation
     assert lib.lrc_accumulate_cov_workspace(1, 4096, 256, 1) > need
 
@@ -84,12 +85,15 @@ def test_whiten_decompose_validation(lib):
 
 def test_score_components_validation(lib):
     f = lib.lrc_score_components
-    assert f(FAKE, FAKE, 1, 10, 4, 4, FAKE, FAKE, None, 4, 0x3, 0, 1, 10, FAKE, FAKE, 1 << 30, None) == EDTYPE
-    assert f(FAKE, FAKE, 1, 10, 4, 4, FAKE, FAKE, None, 0, 0x1, 0, 1, 10, FAKE, FAKE, 1 << 30, None) == EINVAL
-    assert f(None, None, 0, 0, 4, 4, FAKE, FAKE, None, 4, 0x2, 0, 1, 1, FAKE, None, 0, None) == EINVAL  # KFAC no sigma
-    assert f(FAKE, FAKE, 1, 10, 4, 4, FAKE, FAKE, None, 4, 0x1, 0, 1, 0, FAKE, FAKE, 1 << 30, None) == EINVAL
+    # (A, B, dt, n, d_in, d_out, left, right, sigma, k, flags, accumulate, finalize, n_total, scores, info,
+    #  ws, ws_bytes, stream)
+    assert f(FAKE, FAKE, 1, 10, 4, 4, FAKE, FAKE, None, 4, 0x3, 0, 1, 10, FAKE, None, FAKE, 1 << 30, None) == EDTYPE
+    assert f(FAKE, FAKE, 1, 10, 4, 4, FAKE, FAKE, None, 0, 0x1, 0, 1, 10, FAKE, None, FAKE, 1 << 30, None) == EINVAL
+    assert f(None, None, 0, 0, 4, 4, FAKE, FAKE, None, 4, 0x2, 0, 1, 1, FAKE, FAKE, None, 0, None) == EINVAL  # no sigma
+    assert f(FAKE, FAKE, 1, 10, 4, 4, FAKE, FAKE, None, 4, 0x1, 0, 1, 0, FAKE, FAKE, FAKE, 1 << 30, None) == EINVAL
     need = lib.lrc_score_components_workspace(1000, 4, 4, 4, 0x1)
-    assert f(FAKE, FAKE, 1, 1000, 4, 4, FAKE, FAKE, None, 4, 0x1, 0, 1, 1000, FAKE, FAKE, need - 1, None) == EWORKSPACE
+    assert f(FAKE, FAKE, 1, 1000, 4, 4, FAKE, FAKE, None, 4, 0x1, 0, 1, 1000, FAKE, None, FAKE, need - 1,
+             None) == EWORKSPACE
 
 
 def test_allocate_ranks_validation(lib):

@@ -289,9 +289,19 @@ def test_allocate_equal_costs_is_optimal_subset():
         np.testing.assert_allclose(flat.sum() - flat[kept.astype(bool)].sum(), best, rtol=1e-12)
 
 
-def test_allocate_rejects_nan():
+@pytest.mark.parametrize("bad", [np.nan, np.inf, -np.inf, -0.5])
+def test_allocate_rejects_invalid_scores(bad):
+    """Importance scores are non-negative finite numbers (sums of squares, or half a
+    squared singular value): anything else is rejected rather than sorted."""
     with pytest.raises(ValueError):
-        oracle.allocate([np.array([1.0, np.nan], np.float32)], [3], 10)
+        oracle.allocate([np.array([1.0, bad], np.float32)], [3], 10)
+
+
+def test_allocate_accepts_negative_zero_and_rejects_bad_cost():
+    order, n_kept, _, _ = oracle.allocate([np.array([-0.0, 1.0], np.float32)], [3], 10)
+    assert order.tolist() == [1, 0] and n_kept == 2
+    with pytest.raises(ValueError):
+        oracle.allocate([np.array([1.0], np.float32)], [0], 10)
 
 
 # ----------------------------------------------------------------------------- alternative scorers
