@@ -54,6 +54,8 @@ _SIGS = {
     "lrc_score_components_workspace": (_sz, [_i64, _i64, _i64, _i64, _u32]),
     "lrc_allocate_ranks": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "lrc_allocate_ranks_workspace": (_sz, [_i64, _i64]),
+    "lrc_allocate_ranks_noalloc": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "lrc_allocate_ranks_noalloc_max_items": (_i64, []),
     "lrc_rank_scores": (_i32, [_vp, _vp, _i64, _i64, _vp, ctypes.c_float, _u32, _vp, _vp, _vp]),
     "lrc_rotate_quantize": (_i32, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "lrc_rotate_quantize_workspace": (_sz, [_i64, _i64, _i64]),

@@ -16,7 +16,17 @@
 // running total first exceeds the budget, and resolves the position inside it; the mask
 // is then written in item order by comparing each item's (key, id) with the last kept
 // item's.  Matrix costs are looked up per 4096-item bucket.
+#include <mutex>
+
 #include "lrc_internal.h"
+
+// ---- scratch of the allocation-free variant (lrc_allocate_ranks_noalloc): one array per
+// GPU, held until the process ends.  carve_alloc at NOALLOC_MAX_ITEMS needs 24 B per item
+// (two key and two id buffers) plus at most ~1.1 MB of histogram, lookup and cut tables;
+// the entry point checks the carve against the array's size at run time.
+constexpr int64_t NOALLOC_MAX_ITEMS = int64_t(1) << 21;
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(24) * NOALLOC_MAX_ITEMS + (size_t(2) << 20);
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
 
 namespace lrc {
 namespace {
@@ -546,18 +556,24 @@ extern "C" size_t lrc_allocate_ranks_workspace(int64_t n_mat, int64_t n_items) {
   return cv.bytes();
 }
 
-extern "C" lrc_status lrc_allocate_ranks(const float* scores, const int64_t* offsets, const int64_t* cost,
-                                         int64_t n_mat, int64_t n_items, int64_t budget, int32_t* order,
-                                         int64_t* n_kept, int32_t* ranks, uint8_t* kept_mask, int32_t* info,
-                                         void* ws, size_t ws_bytes, void* stream) {
+namespace {
+
+// argument checks shared by both entry points (host only, before any HIP call)
+lrc_status alloc_check_args(const float* scores, const int64_t* offsets, const int64_t* cost, int64_t n_mat,
+                            int64_t n_items, int64_t budget, int32_t* order, int64_t* n_kept, int32_t* ranks,
+                            uint8_t* kept_mask, int32_t* info) {
   if (offsets == nullptr || cost == nullptr || n_kept == nullptr || ranks == nullptr || info == nullptr)
     return LRC_EINVAL;
   if (n_mat <= 0 || n_mat > (int64_t(1) << 30) || n_items < 0 || n_items >= (int64_t(1) << 31) || budget < 0)
     return LRC_EINVAL;
   if (n_items > 0 && (scores == nullptr || order == nullptr || kept_mask == nullptr)) return LRC_EINVAL;
-  const size_t need = lrc_allocate_ranks_workspace(n_mat, n_items);
-  if (ws == nullptr || ws_bytes < need) return LRC_EWORKSPACE;
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  return LRC_OK;
+}
+
+// the whole allocation on `st`, scratch at ws (laid out by carve_alloc for n_items)
+lrc_status allocate_impl(const float* scores, const int64_t* offsets, const int64_t* cost, int64_t n_mat,
+                         int64_t n_items, int64_t budget, int32_t* order, int64_t* n_kept, int32_t* ranks,
+                         uint8_t* kept_mask, int32_t* info, void* ws, hipStream_t st) {
   Carve cv(ws);
   AWs w = carve_alloc(cv, n_items);
   const int M = int(n_items);
@@ -608,4 +624,53 @@ extern "C" lrc_status lrc_allocate_ranks(const float* scores, const int64_t* off
   ranks_kernel<<<unsigned(nm), 256, 0, st>>>(kept_mask, offsets, n_items, info, ranks);
   LRC_LAUNCHED();
   return LRC_OK;
+}
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// the device address of `scratch` on the current device, looked up once per device (the
+// array's host-side name is only a stand-in and must never reach a kernel)
+lrc_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  LRC_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= MAX_DEVICES) return LRC_EINVAL;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    LRC_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (p == nullptr) return LRC_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LRC_OK;
+}
+
+}  // namespace
+
+extern "C" lrc_status lrc_allocate_ranks(const float* scores, const int64_t* offsets, const int64_t* cost,
+                                         int64_t n_mat, int64_t n_items, int64_t budget, int32_t* order,
+                                         int64_t* n_kept, int32_t* ranks, uint8_t* kept_mask, int32_t* info,
+                                         void* ws, size_t ws_bytes, void* stream) {
+  LRC_TRY(alloc_check_args(scores, offsets, cost, n_mat, n_items, budget, order, n_kept, ranks, kept_mask, info));
+  const size_t need = lrc_allocate_ranks_workspace(n_mat, n_items);
+  if (ws == nullptr || ws_bytes < need) return LRC_EWORKSPACE;
+  return allocate_impl(scores, offsets, cost, n_mat, n_items, budget, order, n_kept, ranks, kept_mask, info, ws,
+                       static_cast<hipStream_t>(stream));
+}
+
+extern "C" int64_t lrc_allocate_ranks_noalloc_max_items(void) { return NOALLOC_MAX_ITEMS; }
+
+extern "C" lrc_status lrc_allocate_ranks_noalloc(const float* scores, const int64_t* offsets, const int64_t* cost,
+                                                 int64_t n_mat, int64_t n_items, int64_t budget, int32_t* order,
+                                                 int64_t* n_kept, int32_t* ranks, uint8_t* kept_mask, int32_t* info,
+                                                 void* stream) {
+  LRC_TRY(alloc_check_args(scores, offsets, cost, n_mat, n_items, budget, order, n_kept, ranks, kept_mask, info));
+  if (n_items > NOALLOC_MAX_ITEMS) return LRC_EWORKSPACE;
+  if (lrc_allocate_ranks_workspace(n_mat, n_items) > NOALLOC_SCRATCH_BYTES) return LRC_EWORKSPACE;
+  void* ws = nullptr;
+  LRC_TRY(scratch_for_current_device(&ws));
+  return allocate_impl(scores, offsets, cost, n_mat, n_items, budget, order, n_kept, ranks, kept_mask, info, ws,
+                       static_cast<hipStream_t>(stream));
 }

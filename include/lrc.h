@@ -199,6 +199,24 @@ lrc_status lrc_allocate_ranks(const float* scores, const int64_t* offsets, const
 size_t lrc_allocate_ranks_workspace(int64_t n_mat, int64_t n_items);
 
 /*
+ * lrc_allocate_ranks_noalloc -- lrc_allocate_ranks for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, outputs and kernels, minus the workspace.  Its scratch
+ * is a device array inside the library (about 52 MB, one per GPU the library runs on,
+ * held until the process ends), so no memory is allocated by the call.
+ * n_items may be at most lrc_allocate_ranks_noalloc_max_items() (2^21 = 2,097,152);
+ * larger pools get LRC_EWORKSPACE (use lrc_allocate_ranks).  Every call on one GPU uses
+ * that GPU's single array: calls that overlap on one GPU (two streams, two host threads)
+ * race and must be serialised by the caller.  The array needs no initialisation; it
+ * keeps the last call's contents.
+ */
+lrc_status lrc_allocate_ranks_noalloc(const float* scores, const int64_t* offsets, const int64_t* cost,
+                                      int64_t n_mat, int64_t n_items, int64_t budget, int32_t* order,
+                                      int64_t* n_kept, int32_t* ranks, uint8_t* kept_mask, int32_t* info,
+                                      void* stream);
+int64_t lrc_allocate_ranks_noalloc_max_items(void);
+
+/*
  * lrc_rank_scores -- alternative scores over the same component layout as
  * lrc_allocate_ranks, from the singular values alone.
  *   UNIRANK (UniRank 2.1, "Aggregation and Truncation"): scores[j] = weight[m] *
