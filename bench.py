@@ -7,13 +7,18 @@ per-component K-FAC scores (this workload has no gradients) and the global
 sort-and-truncate at the budget of rank 1024.  Inputs are resident in HBM before the
 timed region.  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-secondary]
+    python bench.py --only syrk|tridiag|ffn-decode [--copy-probe-mib M]
+
+The --only modes run one part of the path a few times (and, with --copy-probe-mib, a
+plain device copy of known size first): they are the programs the rocprofv3 summaries
+under profiles/ were taken from.  They never start the library's own event timing, so a
+counter profiler sees ordinary kernel launches.
 """
 from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -26,8 +31,8 @@ HBM_PEAK_GBS = 8000.0
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "f64": 78.6}
 
 # roofline class of each instrumented kernel: MFMA contractions against the dense peak of
-# their input type, the fp64 Jacobi kernels against the fp64 peak (vector and matrix fp64
-# peaks are equal on MI355X), streaming passes against HBM
+# their input type, the fp64 kernels against the fp64 peak (vector and matrix fp64 peaks
+# are equal on MI355X), streaming passes against HBM
 ROOFLINE = {
     "syrk_bf16_kernel": {"bound": "mfma", "dtype": "bf16", "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s"},
     "syrk_f32_kernel": {"bound": "mfma", "dtype": "f32", "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s"},
@@ -40,17 +45,30 @@ ROOFLINE = {
     "qaw_prepass_kernel": {"bound": "hbm", "dtype": "bf16", "peak": HBM_PEAK_GBS, "unit": "GB/s"},
     "tri_symv_kernel": {"bound": "hbm", "dtype": "f64", "peak": HBM_PEAK_GBS, "unit": "GB/s"},
     "tri_w_kernel": {"bound": "hbm", "dtype": "f64", "peak": HBM_PEAK_GBS, "unit": "GB/s"},
-    "tri_fused_kernel": {"bound": "hbm", "dtype": "f64", "peak": HBM_PEAK_GBS, "unit": "GB/s"},
     "tri_syr2k_kernel": {"bound": "alu", "dtype": "f64", "peak": PEAK_TFLOPS["f64"], "unit": "TFLOP/s"},
     "bt_vtz_kernel": {"bound": "alu", "dtype": "f64", "peak": PEAK_TFLOPS["f64"], "unit": "TFLOP/s"},
     "bt_update_kernel": {"bound": "alu", "dtype": "f64", "peak": PEAK_TFLOPS["f64"], "unit": "TFLOP/s"},
 }
 
 # HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE on this
-# workload, scaled by the copy-kernel calibration (profiles/counters_tri_symv_attnproj_4096.md:
-# fetch 24.43 MB + write 0.77 MB, the average over the 3968 launches of a 4096-wide
-# tridiagonalisation); absent (None) for a kernel whose counters were not taken
-TRAFFIC = {"tri_symv_kernel": 25.20e6}
+# workload, scaled by the copy-kernel calibration, with the commit of the kernel source the
+# counters were taken on (profiles/counters_tri_symv_attnproj_4096.md: fetch 24.43 MB +
+# write 0.77 MB, the average over the 3968 launches of a 4096-wide tridiagonalisation).
+# A kernel without an entry reports traffic null.
+TRAFFIC = {"tri_symv_kernel": {"bytes": 25.20e6, "kernel_source_commit": "6524d8f"}}
+
+
+def layer_flops(d, r):
+    """Algorithmic flops of one decomposition of a d x d weight at rank r with G = I:
+    Cholesky d^3/3, whitening d^3, Gram d^3, tridiagonalisation 4d^3/3, back-transformation
+    and back-map 2 d^2 r each, triangular solve d^2 r."""
+    return d ** 3 / 3 + d ** 3 + d ** 3 + 4 * d ** 3 / 3 + 4.0 * d * d * r + d * d * r
+
+
+def layer_bytes(d):
+    """Bytes the BLAS-2 half of a one-stage tridiagonalisation reads: the fp64 lower
+    trailing matrix once per column, 8 B x d^3 / 6."""
+    return 4.0 * d ** 3 / 3
 
 
 def parse():
@@ -62,45 +80,133 @@ def parse():
     p.add_argument("--d", type=int, default=4096)
     p.add_argument("--rank", type=int, default=1024)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--no-secondary", action="store_true", help="skip the scoring / allocation measurements")
+    p.add_argument("--no-secondary", action="store_true", help="skip the other workloads and passes")
+    p.add_argument("--only", choices=["syrk", "tridiag", "ffn-decode"], default=None,
+                   help="run one part of the path (for rocprofv3) instead of the benchmark")
     p.add_argument("--copy-probe-mib", type=int, default=0,
-                   help="before the steps, run a plain elementwise copy (neg) of this many MiB three times: "
-                        "the known-size kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
+                   help="first run a plain elementwise copy (neg) of this many MiB three times: the "
+                        "known-size kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
     return p.parse_args()
 
 
+def blas_info():
+    """(vendor string, thread count) of the host BLAS numpy uses."""
+    import numpy  # noqa: F401  (loads the BLAS)
+    try:
+        from threadpoolctl import threadpool_info
+        infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if infos:
+            i = infos[0]
+            return f"{i.get('internal_api')} {i.get('version')} ({i.get('architecture')})", int(i["num_threads"])
+    except Exception:
+        pass
+    return "unknown", len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(d, n, rank):
-    """The fp64 oracle on host cores, on a bounded sample of the same workload: the
-    covariance of 16384 of the n tokens (scaled by n / 16384), then the full-size
-    Cholesky, whitening, SVD, back-map, K-FAC scores and allocation of the layer."""
+    """The fp64 oracle on host cores: config 1 whole (covariance over all n tokens, then
+    Cholesky, whitening, SVD, back-map, K-FAC scores and allocation of the layer), plus
+    bounded-sample estimates of the other workloads (each labelled with its sample)."""
     import numpy as np
     import torch
 
     import oracle
     import synth
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
-    ns = min(16384, n)
-    a = synth.activation_stream(ns, d, 1.0, 31, outlier_frac=0.01, dtype=torch.bfloat16).float().numpy()
+    vendor, threads = blas_info()
+    a = synth.activation_stream(n, d, 1.0, 31, outlier_frac=0.01, dtype=torch.bfloat16).float().numpy()
     t0 = time.perf_counter()
     xs = oracle.covariance_sum(a)
-    t_cov_meas = time.perf_counter() - t0
+    t_cov = time.perf_counter() - t0
     del a
     w = synth.weight(d, d, 35).numpy()
     t0 = time.perf_counter()
-    res = oracle.whiten_decompose(w, xs, ns, rank=rank)
+    res = oracle.whiten_decompose(w, xs, n, rank=rank)
     sc = oracle.kfac_scores(res["sigma"])
     oracle.allocate([sc.astype(np.float32)], [2 * d], rank * 2 * d)
     t_dec = time.perf_counter() - t0
-    t_cov = t_cov_meas * (n / ns)
-    return {"value": 1.0 / (t_cov + t_dec), "unit": "layers/s", "cores": threads, "kind": "oracle",
-            "sample": f"fp64 covariance of {ns} of {n} tokens (time x{n / ns:g}) + full {d}x{d} "
+    cov_rate = n / t_cov                                  # tokens/s into a d-wide covariance
+    per_cfg = {"attention_projection_4096": {"s": round(t_cov + t_dec, 2), "sample": "whole workload"}}
+    spent = t_cov + t_dec
+
+    # single linear layer 256 x 256, 4096 fp32 tokens, two-sided, rank 64: whole
+    cs0 = synth.config_spec(0)
+    a0 = synth.stream(cs0, "a").numpy()
+    b0 = synth.stream(cs0, "b").numpy()
+    w0 = synth.weight(256, 256, 3).numpy()
+    t1 = time.perf_counter()
+    oracle.whiten_decompose(w0, oracle.covariance_sum(a0), cs0.n_tokens, oracle.covariance_sum(b0), cs0.n_tokens,
+                            rank=64)
+    t0 = time.perf_counter() - t1
+    per_cfg["single_layer_256"] = {"s": round(t0, 3), "sample": "whole workload"}
+    spent += t0
+
+    # FFN pair: covariances per token measured on 2048 tokens of each stream of the up
+    # projection (x 131072 / 2048, twice for the pair), the up projection's two-sided
+    # decomposition at full size (the down projection's taken as equal)
+    cs2 = synth.config_spec(2, n_tokens=2048)
+    t_tok = 0.0
+    covs = {}
+    for key in ("a_up", "b_up"):
+        s = synth.stream(cs2, key).float().numpy()
+        if key.startswith("a"):
+            s = oracle.qaw_fake_quant(s)[2]
+        t1 = time.perf_counter()
+        covs[key] = oracle.covariance_sum(s)
+        t_tok += time.perf_counter() - t1
+    t_cov2 = 2 * t_tok * (131072 / 2048)
+    wu = synth.weight(11008, 4096, 45).numpy()
+    t1 = time.perf_counter()
+    oracle.whiten_decompose(wu, covs["a_up"], 2048, covs["b_up"], 2048, rank=2048)
+    t_dec2 = time.perf_counter() - t1
+    per_cfg["ffn_pair_11008x4096"] = {
+        "s": round(t_cov2 + 2 * t_dec2, 1),
+        "sample": "covariances of 2048 tokens per stream (x64, x2) + the up projection's decomposition (x2)"}
+    spent += t_tok + t_dec2
+
+    # decoder stack: one 4096 x 4096 decomposition with every component and its Fisher
+    # scores on 1024 tokens (x32 to the 32768 tokens), both x224; covariances at the
+    # measured per-token rate (scaled by width squared); the 917,504-component allocation
+    # whole
+    cs3 = synth.config_spec(3, n_tokens=1024)
+    a3 = synth.stream(cs3, "attn_in").float().numpy()
+    b3 = synth.stream(cs3, "g_q").float().numpy()
+    w3 = synth.weight(4096, 4096, 1000).numpy()
+    t1 = time.perf_counter()
+    r3 = oracle.whiten_decompose(w3, xs, n, rank=4096)
+    t_dec3 = time.perf_counter() - t1
+    t1 = time.perf_counter()
+    f3 = oracle.fisher_scores(a3, b3, r3["left"], r3["right"])
+    t_fis = time.perf_counter() - t1
+    pool = [f3.astype(np.float32)] * 224
+    t1 = time.perf_counter()
+    oracle.allocate(pool, [8192] * 224, 3885603225)
+    t_alloc3 = time.perf_counter() - t1
+    cov3 = 32 * 32768 / cov_rate * (3 + (11008 / 4096) ** 2)
+    per_cfg["decoder_stack_32_layers"] = {
+        "s": round(224 * (t_dec3 + 32 * t_fis) + cov3 + t_alloc3, 0),
+        "sample": "one 4096x4096 decomposition (x224), its Fisher scores on 1024 tokens (x32, x224), covariances "
+                  "at the measured per-token rate, the 917504-component allocation whole"}
+    spent += t_dec3 + t_fis + t_alloc3
+
+    # per-head K/V: the shared covariance at the measured per-token rate, 64 head
+    # decompositions whole
+    lx, _ = oracle.cholesky_lower(xs / n)
+    t1 = time.perf_counter()
+    for h in range(64):
+        wh = w[(h % 32) * 128:(h % 32 + 1) * 128]
+        oracle.truncated_svd(oracle.whiten(wh, lx))
+    t_heads = time.perf_counter() - t1
+    per_cfg["kv_heads_64x128x4096"] = {"s": round(65536 / cov_rate + t_heads, 2),
+                                       "sample": "covariance at the measured per-token rate, 64 head SVDs whole"}
+    spent += t_heads
+
+    return {"value": 1.0 / (t_cov + t_dec), "unit": "layers/s", "cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle",
+            "sample": f"the whole attention-projection layer: fp64 covariance of all {n} tokens + {d}x{d} "
                       f"Cholesky/whitening/SVD/back-map/K-FAC scores/allocation at rank {rank}",
-            "cov_tokens_per_s": round(n / t_cov, 1), "seconds_measured": round(t_cov_meas + t_dec, 2)}
+            "blas": vendor, "blas_threads": threads, "cov_tokens_per_s": round(cov_rate, 1),
+            "seconds_measured": round(spent, 1), "per_config_s": per_cfg}
 
 
 def _time(fn, torch, reps):
@@ -115,11 +221,136 @@ def _time(fn, torch, reps):
     return sorted(ts)[len(ts) // 2]
 
 
-def secondary(lrc, torch, dev):
+def workloads(lrc, torch, dev):
+    """End-to-end GPU times of the other workloads (inputs resident, generation excluded)."""
+    import synth
+    out = {}
+    # single linear layer: 256 x 256, 4096 fp32 tokens, two-sided, rank 64
+    cs = synth.config_spec(0)
+    a = synth.stream(cs, "a", device=dev)
+    b = synth.stream(cs, "b", device=dev)
+    w = synth.weight(256, 256, 3, device=dev)
+    xs = torch.empty(256, 256, device=dev)
+    gs = torch.empty(256, 256, device=dev)
+
+    def cfg0():
+        xs.zero_()
+        gs.zero_()
+        lrc.lrc_accumulate_cov(a, xs)
+        lrc.lrc_accumulate_cov(b, gs)
+        return lrc.lrc_whiten_decompose(w, 64, xs, 4096, gs, 4096)
+
+    cfg0()
+    t = _time(cfg0, torch, 5)
+    out["single_layer_256"] = {"workload": "256x256 fp32, 4096 fp32 tokens, two-sided, rank 64",
+                               "ms": round(t * 1e3, 3)}
+    del a, b, w, xs, gs
+
+    # FFN pair: 131072 bf16 tokens per stream, QAW on the activations, two-sided, rank 2048
+    cs = synth.config_spec(2)
+    st = {k: synth.stream(cs, k, device=dev) for k in cs.streams}
+    ws = [synth.weight(m.d_out, m.d_in, 45 + i, device=dev) for i, m in enumerate(cs.matrices)]
+    covs = {k: torch.empty(v.shape[1], v.shape[1], device=dev) for k, v in st.items()}
+
+    def cfg2():
+        for k, c in covs.items():
+            c.zero_()
+            lrc.lrc_accumulate_cov(st[k], c, quant=k.startswith("a"))
+        for m, wm in zip(cs.matrices, ws):
+            lrc.lrc_whiten_decompose(wm, 2048, covs[m.a_stream], cs.n_tokens, covs[m.b_stream], cs.n_tokens)
+
+    cfg2()
+    t = _time(cfg2, torch, 2)
+    out["ffn_pair_11008x4096"] = {"workload": "up 11008x4096 + down 4096x11008, 131072 bf16 tokens per stream, "
+                                              "int8 QAW, two-sided, rank 2048", "ms": round(t * 1e3, 1)}
+    # the QAW pre-pass alone, measured on the library's events (bf16 read, int8 codes and
+    # the two bf16 terms written)
+    lrc.lrc_profile_start()
+    c = covs["a_down"]
+    c.zero_()
+    lrc.lrc_accumulate_cov(st["a_down"], c, quant=True)
+    torch.cuda.synchronize()
+    lrc.lrc_profile_stop()
+    q = lrc.lrc_profile_kernels().get("qaw_prepass_kernel")
+    if q and q["total_ms"] > 0:
+        gbs = q["bytes"] / (q["total_ms"] * 1e-3) / 1e9
+        out["qaw_prepass"] = {"workload": "131072 bf16 tokens x 11008", "ms": round(q["total_ms"], 3),
+                              "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    del st, ws, covs, c
+
+    # decoder stack: 32 layers x (4 covariances + 7 decompositions with every component +
+    # 7 empirical-Fisher score passes) and one allocation over the 917,504 components; one
+    # layer's streams and weights are generated once and reused by every layer (the work
+    # does not depend on the values)
+    cs = synth.config_spec(3)
+    n = cs.n_tokens
+    st = {k: synth.stream(cs, k, device=dev) for k in cs.streams}
+    ws = [synth.weight(m.d_out, m.d_in, 1000 + i, device=dev) for i, m in enumerate(cs.matrices)]
+    covs = {k: torch.empty(st[k].shape[1], st[k].shape[1], device=dev) for k in ("attn_in", "o_in", "mlp_in",
+                                                                               "down_in")}
+    scores = torch.empty(224 * 4096, device=dev)
+    offs = torch.arange(0, 224 * 4096 + 1, 4096, dtype=torch.int64, device=dev)
+    cost = torch.tensor([m.d_out + m.d_in for m in cs.matrices] * 32, dtype=torch.int64, device=dev)
+    budget = int(0.6 * 32 * sum(m.d_out * m.d_in for m in cs.matrices))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for layer in range(32):
+        for k, c in covs.items():
+            c.zero_()
+            lrc.lrc_accumulate_cov(st[k], c)
+        for mi, (m, wm) in enumerate(zip(cs.matrices, ws)):
+            _, left, right, _ = lrc.lrc_whiten_decompose(wm, 4096, covs[m.a_stream], n)
+            j = (layer * 7 + mi) * 4096
+            lrc.lrc_score_components(left, right, A=st[m.a_stream], B=st[m.b_stream], scores=scores[j:j + 4096])
+            del left, right
+    lrc.lrc_allocate_ranks(scores, offs, cost, budget)
+    torch.cuda.synchronize()
+    t = time.perf_counter() - t0
+    out["decoder_stack_32_layers"] = {
+        "workload": "32 layers x (q,k,v,o 4096x4096, gate/up 11008x4096, down 4096x11008), 32768 bf16 tokens per "
+                    "stream, every component decomposed and Fisher-scored, allocation of 917504 components at 60%",
+        "s": round(t, 2), "matrices_per_s": round(224 / t, 2)}
+    del st, ws, covs, scores
+
+    # per-head K/V: 65536 bf16 tokens, 64 head slices of 128 x 4096, K-FAC scores, 40% budget
+    cs = synth.config_spec(4)
+    a = synth.stream(cs, "a", device=dev)
+    w3 = torch.cat([synth.weight(4096, 4096, 137, device=dev), synth.weight(4096, 4096, 139, device=dev)]).view(
+        64, 128, 4096)
+    cov = torch.empty(4096, 4096, device=dev)
+    offs = torch.arange(0, 64 * 128 + 1, 128, dtype=torch.int64, device=dev)
+    cost = torch.full((64,), 128 + 4096, dtype=torch.int64, device=dev)
+
+    def cfg4():
+        cov.zero_()
+        lrc.lrc_accumulate_cov(a, cov)
+        sig, _, _, _ = lrc.lrc_whiten_decompose(w3, 128, cov, 65536)
+        sc, _ = lrc.lrc_score_components(sigma=sig.reshape(-1), mode="kfac")
+        return lrc.lrc_allocate_ranks(sc, offs, cost, int(0.4 * 2 * 4096 * 4096))
+
+    cfg4()
+    t = _time(cfg4, torch, 3)
+    out["kv_heads_64x128x4096"] = {"workload": "64 heads of 128x4096 sharing one covariance of 65536 bf16 tokens, "
+                                               "K-FAC scores, allocation at 40%", "ms": round(t * 1e3, 2)}
+    return out
+
+
+def _fac(torch, g, dev, rows, cols):
+    return (torch.randint(-127, 128, (rows, cols), generator=g, device=dev, dtype=torch.int8),
+            torch.rand(rows, generator=g, device=dev) * 0.004 + 0.001)
+
+
+def _ffn_factors(torch, g, dev, d, d_ff, rk):
+    """int8 factor sets of a low-rank SwiGLU FFN (R_down stored transposed, d_ff x rk)."""
+    gate = (*_fac(torch, g, dev, rk, d), *_fac(torch, g, dev, d_ff, rk))
+    up = (*_fac(torch, g, dev, rk, d), *_fac(torch, g, dev, d_ff, rk))
+    down = (*_fac(torch, g, dev, d_ff, rk), *_fac(torch, g, dev, d, rk))
+    return gate, up, down
+
+
+def passes(lrc, torch, dev):
     """Throughput of the scoring and allocation passes at the decoder-stack workload's
-    shapes (synthetic inputs): empirical-Fisher scores of one 4096 x 4096 matrix over
-    32768 tokens with all 4096 components, and the global sort-and-truncate over the
-    stack's 917,504 components and over a scaled 64M-component pool."""
+    shapes (synthetic inputs), and of the follow-on kernels."""
     import synth
     out = {}
     n, d, k = 32768, 4096, 4096
@@ -160,14 +391,7 @@ def secondary(lrc, torch, dev):
     del left, right, signs
     # decode-time low-rank FFN (hidden 4096, FFN 11008, every rank 2048, int8 factors)
     dff, rk = 11008, 2048
-
-    def fac(rows, cols):
-        return (torch.randint(-127, 128, (rows, cols), generator=g, device=dev, dtype=torch.int8),
-                torch.rand(rows, generator=g, device=dev) * 0.004 + 0.001)
-
-    gate = (*fac(rk, d), *fac(dff, rk))
-    up = (*fac(rk, d), *fac(dff, rk))
-    down = (*fac(dff, rk), *fac(d, rk))   # R_down stored transposed (d_ff x r)
+    gate, up, down = _ffn_factors(torch, g, dev, d, dff, rk)
     fbytes = 2.0 * rk * d + 2.0 * dff * rk + dff * rk + d * rk
     for nt in (1, 8):
         xin = torch.randn(nt, d, generator=g, device=dev)
@@ -180,10 +404,8 @@ def secondary(lrc, torch, dev):
     del gate, up, down
     # hybrid decode: half the hidden channels low-rank (rank 2048), the other half dense int8
     nl = nd = dff // 2
-    gate = (*fac(rk, d), *fac(nl, rk))
-    up = (*fac(rk, d), *fac(nl, rk))
-    down = (*fac(nl, rk), *fac(d, rk))
-    dense = (*fac(nd, d), *fac(nd, d), *fac(d, nd))
+    gate, up, down = _ffn_factors(torch, g, dev, d, nl, rk)
+    dense = (*_fac(torch, g, dev, nd, d), *_fac(torch, g, dev, nd, d), *_fac(torch, g, dev, d, nd))
     hbytes = 2.0 * rk * d + 2.0 * nl * rk + nl * rk + d * rk + 3.0 * nd * d
     for nt in (1, 8):
         xin = torch.randn(nt, d, generator=g, device=dev)
@@ -233,6 +455,80 @@ def secondary(lrc, torch, dev):
     return out
 
 
+def copy_probe(torch, dev, mib):
+    """A plain elementwise copy (torch.neg) of mib MiB, three times: a kernel of known
+    size whose FETCH_SIZE / WRITE_SIZE readings calibrate the counters."""
+    src = torch.ones(mib << 18, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
+def only(args, lrc, torch, dev):
+    """The --only modes (programs for rocprofv3; no library event timing)."""
+    import synth
+    if args.copy_probe_mib:
+        copy_probe(torch, dev, args.copy_probe_mib)
+    res = {"mode": args.only}
+    if args.only == "syrk":
+        # three accumulations of the attention projection's token block
+        a = synth.activation_stream(args.tokens, args.d, 1.0, 31, outlier_frac=0.01, dtype=torch.bfloat16,
+                                    device=dev)
+        cov = torch.zeros(args.d, args.d, device=dev)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(3):
+            cov.zero_()
+            lrc.lrc_accumulate_cov(a, cov)
+        e.record()
+        torch.cuda.synchronize()
+        res["ms_per_accumulation"] = round(s.elapsed_time(e) / 3, 4)
+    elif args.only == "tridiag":
+        # one covariance and one whitened decomposition of the attention projection
+        a = synth.activation_stream(args.tokens, args.d, 1.0, 31, outlier_frac=0.01, dtype=torch.bfloat16,
+                                    device=dev)
+        w = synth.weight(args.d, args.d, 35, device=dev)
+        cov = torch.zeros(args.d, args.d, device=dev)
+        lrc.lrc_accumulate_cov(a, cov)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        _, _, _, info = lrc.lrc_whiten_decompose(w, args.rank, cov, args.tokens)
+        torch.cuda.synchronize()
+        res["decomposition_ms"] = round((time.perf_counter() - t0) * 1e3, 2)
+        res["info"] = int(info[0])
+    else:
+        # decode-time FFN: low-rank and hybrid forms at 1 and 8 tokens, 20 untimed + 50 timed calls
+        g = torch.Generator(device=dev)
+        g.manual_seed(1)
+        d, dff, rk = 4096, 11008, 2048
+        nl = nd = dff // 2
+        dense = (*_fac(torch, g, dev, nd, d), *_fac(torch, g, dev, nd, d), *_fac(torch, g, dev, d, nd))
+        cases = [("lowrank", _ffn_factors(torch, g, dev, d, dff, rk), None),
+                 ("hybrid", _ffn_factors(torch, g, dev, d, nl, rk), dense)]
+        for name, (gate, up, down), dn in cases:
+            for nt in (1, 8):
+                x = torch.randn(nt, d, generator=g, device=dev)
+                if dn is None:
+                    def fn():
+                        lrc.lrc_lowrank_ffn(x, gate, up, down)
+                else:
+                    def fn():
+                        lrc.lrc_hybrid_ffn(x, gate, up, down, dn)
+                for _ in range(20):
+                    fn()
+                torch.cuda.synchronize()
+                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s.record()
+                for _ in range(50):
+                    fn()
+                e.record()
+                torch.cuda.synchronize()
+                res[f"{name}_{nt}tok_us"] = round(s.elapsed_time(e) / 50 * 1e3, 1)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -245,6 +541,9 @@ def main():
     import synth
 
     dev = torch.device("cuda:0")
+    if args.only:
+        only(args, lrc, torch, dev)
+        return
     d, n, r = args.d, args.tokens, args.rank
     a = synth.activation_stream(n, d, 1.0, 31, outlier_frac=0.01, dtype=torch.bfloat16, device=dev)
     w = synth.weight(d, d, 35, device=dev)
@@ -253,11 +552,7 @@ def main():
     cost = torch.tensor([2 * d], dtype=torch.int64, device=dev)
     budget = r * 2 * d
     if args.copy_probe_mib:
-        src = torch.ones(args.copy_probe_mib << 18, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.neg(src, out=dst)
-        del src, dst
+        copy_probe(torch, dev, args.copy_probe_mib)
     torch.cuda.synchronize()
 
     def step():
@@ -265,7 +560,7 @@ def main():
         lrc.lrc_accumulate_cov(a, cov)
         sig, left, right, info = lrc.lrc_whiten_decompose(w, r, cov, n)
         scores, _ = lrc.lrc_score_components(sigma=sig, mode="kfac")
-        return lrc.lrc_allocate_ranks(scores, offs, cost, budget)
+        return lrc.lrc_allocate_ranks(scores, offs, cost, budget), info
 
     for _ in range(args.warmup):
         step()
@@ -273,11 +568,20 @@ def main():
     # timed region: K whole steps, nothing else on the stream
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        out = step()
+        out, info = step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    assert int(info[0]) == 0 and int(out[4][0]) == 0
     n_kept = int(out[1][0])
     ms = 1e3 * elapsed / args.steps
+    # the covariance alone: K accumulations back to back, timed with events around the loop
+    s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s_ev.record()
+    for _ in range(args.steps):
+        lrc.lrc_accumulate_cov(a, cov)
+    e_ev.record()
+    torch.cuda.synchronize()
+    cov_ms = s_ev.elapsed_time(e_ev) / args.steps
     # the same K steps again with the library's measurement on: every instrumented launch
     # is bracketed by HIP events on the stream it is enqueued on, and the work each launch
     # performed is counted.  The events add host and GPU time per launch, so this pass is
@@ -309,9 +613,8 @@ def main():
     avg_s = dk["total_ms"] / dk["launches"] * 1e-3
     work = (dk["flops"] if roof["unit"] == "TFLOP/s" else dk["bytes"]) / dk["launches"]
     achieved = work / avg_s / (1e12 if roof["unit"] == "TFLOP/s" else 1e9)
-
-    syrk = prof["syrk_bf16_kernel"]
-    syrk_s = syrk["total_ms"] * 1e-3 / args.steps        # one launch per step here
+    tr = TRAFFIC.get(dom)
+    dec_ms = ms - cov_ms
     res = {
         "metric": METRIC,
         "value": round(1e3 / ms, 4),
@@ -328,19 +631,27 @@ def main():
         "config": {"workload": f"attention projection W {d}x{d} fp32, {n} bf16 calibration tokens "
                                f"(power-law spectrum, 1% outlier channels x20), activation-only whitening, rank {r}",
                    "tokens_per_layer": n, "d": d, "rank": r},
-        "cov_tokens_per_s": round(n / syrk_s, 1),
+        "cov_tokens_per_s": round(n / (cov_ms * 1e-3), 1),
+        "cov_ms": round(cov_ms, 4),
+        "cov_mfma_bf16_frac": round(n * d * (d + 1.0) / (cov_ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
         "step_tokens_per_s": round(n * 1e3 / ms, 1),
         "n_kept": n_kept,
+        "layer": {"decomposition_ms": round(dec_ms, 3), "algorithmic_flops": layer_flops(d, r),
+                  "mfma_f32_frac": round(layer_flops(d, r) / (dec_ms * 1e-3) / 1e12 / PEAK_TFLOPS["f32"], 4),
+                  "one_stage_tridiag_bytes": layer_bytes(d),
+                  "hbm_frac": round(layer_bytes(d) / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "profiled_ms_per_step": round(prof_ms, 3),
         "roofline": {"bound": roof["bound"], "kernel": dom, "dtype": roof["dtype"],
                      "achieved": round(achieved, 3), "peak": roof["peak"], "unit": roof["unit"],
-                     "frac": round(achieved / roof["peak"], 4), "traffic": TRAFFIC.get(dom),
+                     "frac": round(achieved / roof["peak"], 4), "traffic": tr["bytes"] if tr else None,
+                     "traffic_kernel_source_commit": tr["kernel_source_commit"] if tr else None,
                      "avg_launch_ms": round(dk["total_ms"] / dk["launches"], 5),
                      "launches_per_step": dk["launches"] / args.steps},
         "kernels": kernels,
     }
     if not args.no_secondary:
-        res["secondary"] = secondary(lrc, torch, dev)
+        res["secondary"] = passes(lrc, torch, dev)
+        res["workloads"] = workloads(lrc, torch, dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(d, n, r)
     print(json.dumps(res), flush=True)
