@@ -341,10 +341,12 @@ def _fac(torch, g, dev, rows, cols):
 
 
 def _ffn_factors(torch, g, dev, d, d_ff, rk):
-    """int8 factor sets of a low-rank SwiGLU FFN (R_down stored transposed, d_ff x rk)."""
+    """int8 factor sets of a low-rank SwiGLU FFN: gate and up (R rk x d, L d_ff x rk), down
+    with R_down (rk x d_ff) stored transposed (d_ff x rk) beside its rk row scales."""
     gate = (*_fac(torch, g, dev, rk, d), *_fac(torch, g, dev, d_ff, rk))
     up = (*_fac(torch, g, dev, rk, d), *_fac(torch, g, dev, d_ff, rk))
-    down = (*_fac(torch, g, dev, d_ff, rk), *_fac(torch, g, dev, d, rk))
+    q_rd, s_rd = _fac(torch, g, dev, rk, d_ff)
+    down = (q_rd.t().contiguous(), s_rd, *_fac(torch, g, dev, d, rk))
     return gate, up, down
 
 
