@@ -89,6 +89,14 @@ def parse():
     return p.parse_args()
 
 
+_T_START = time.perf_counter()
+
+
+def progress(msg):
+    """One line per finished part on stderr (the JSON result is the only stdout line)."""
+    print(f"[bench {time.perf_counter() - _T_START:7.1f}s] {msg}", file=sys.stderr, flush=True)
+
+
 def blas_info():
     """(vendor string, thread count) of the host BLAS numpy uses."""
     import numpy  # noqa: F401  (loads the BLAS)
@@ -128,6 +136,7 @@ def cpu_baseline(d, n, rank):
     cov_rate = n / t_cov                                  # tokens/s into a d-wide covariance
     per_cfg = {"attention_projection_4096": {"s": round(t_cov + t_dec, 2), "sample": "whole workload"}}
     spent = t_cov + t_dec
+    progress(f"oracle: attention projection {t_cov + t_dec:.1f} s")
 
     # single linear layer 256 x 256, 4096 fp32 tokens, two-sided, rank 64: whole
     cs0 = synth.config_spec(0)
@@ -140,6 +149,7 @@ def cpu_baseline(d, n, rank):
     t0 = time.perf_counter() - t1
     per_cfg["single_layer_256"] = {"s": round(t0, 3), "sample": "whole workload"}
     spent += t0
+    progress("oracle: single layer")
 
     # FFN pair: covariances per token measured on 2048 tokens of each stream of the up
     # projection (x 131072 / 2048, twice for the pair), the up projection's two-sided
@@ -163,6 +173,7 @@ def cpu_baseline(d, n, rank):
         "s": round(t_cov2 + 2 * t_dec2, 1),
         "sample": "covariances of 2048 tokens per stream (x64, x2) + the up projection's decomposition (x2)"}
     spent += t_tok + t_dec2
+    progress("oracle: FFN pair sample")
 
     # decoder stack: one 4096 x 4096 decomposition with every component and its Fisher
     # scores on 1024 tokens (x32 to the 32768 tokens), both x224; covariances at the
@@ -188,6 +199,7 @@ def cpu_baseline(d, n, rank):
         "sample": "one 4096x4096 decomposition (x224), its Fisher scores on 1024 tokens (x32, x224), covariances "
                   "at the measured per-token rate, the 917504-component allocation whole"}
     spent += t_dec3 + t_fis + t_alloc3
+    progress("oracle: decoder stack sample")
 
     # per-head K/V: the shared covariance at the measured per-token rate, 64 head
     # decompositions whole
@@ -244,6 +256,7 @@ def workloads(lrc, torch, dev):
     t = _time(cfg0, torch, 5)
     out["single_layer_256"] = {"workload": "256x256 fp32, 4096 fp32 tokens, two-sided, rank 64",
                                "ms": round(t * 1e3, 3)}
+    progress("workload: single layer")
     del a, b, w, xs, gs
 
     # FFN pair: 131072 bf16 tokens per stream, QAW on the activations, two-sided, rank 2048
@@ -263,6 +276,7 @@ def workloads(lrc, torch, dev):
     t = _time(cfg2, torch, 2)
     out["ffn_pair_11008x4096"] = {"workload": "up 11008x4096 + down 4096x11008, 131072 bf16 tokens per stream, "
                                               "int8 QAW, two-sided, rank 2048", "ms": round(t * 1e3, 1)}
+    progress("workload: FFN pair")
     # the QAW pre-pass alone, measured on the library's events (bf16 read, int8 codes and
     # the two bf16 terms written)
     lrc.lrc_profile_start()
@@ -293,6 +307,7 @@ def workloads(lrc, torch, dev):
     cost = torch.tensor([m.d_out + m.d_in for m in cs.matrices] * 32, dtype=torch.int64, device=dev)
     budget = int(0.6 * 32 * sum(m.d_out * m.d_in for m in cs.matrices))
     torch.cuda.synchronize()
+    progress("workload: decoder stack inputs ready")
     t0 = time.perf_counter()
     for layer in range(32):
         for k, c in covs.items():
@@ -310,6 +325,7 @@ def workloads(lrc, torch, dev):
         "workload": "32 layers x (q,k,v,o 4096x4096, gate/up 11008x4096, down 4096x11008), 32768 bf16 tokens per "
                     "stream, every component decomposed and Fisher-scored, allocation of 917504 components at 60%",
         "s": round(t, 2), "matrices_per_s": round(224 / t, 2)}
+    progress(f"workload: decoder stack {t:.1f} s")
     del st, ws, covs, scores
 
     # per-head K/V: 65536 bf16 tokens, 64 head slices of 128 x 4096, K-FAC scores, 40% budget
@@ -332,6 +348,7 @@ def workloads(lrc, torch, dev):
     t = _time(cfg4, torch, 3)
     out["kv_heads_64x128x4096"] = {"workload": "64 heads of 128x4096 sharing one covariance of 65536 bf16 tokens, "
                                                "K-FAC scores, allocation at 40%", "ms": round(t * 1e3, 2)}
+    progress("workload: K/V heads")
     return out
 
 
@@ -368,6 +385,7 @@ def passes(lrc, torch, dev):
     out["fisher_scores"] = {"workload": f"{n} bf16 tokens, {d}x{d} matrix, {k} components", "ms": round(t * 1e3, 3),
                             "TFLOP/s": round(flops / t / 1e12, 2),
                             "mfma_bf16_frac": round(flops / t / 1e12 / PEAK_TFLOPS["bf16"], 4)}
+    progress("pass: Fisher scores")
     del a, b, left, right
     # alternative scores from the singular values (224 matrices x 4096 components)
     n_mat, per = 224, 4096
@@ -437,6 +455,7 @@ def passes(lrc, torch, dev):
                                     "ms": round(t * 1e3, 3), "TFLOP/s": round(flops / t / 1e12, 2),
                                     "mfma_fp32_frac": round(flops / t / 1e12 / PEAK_TFLOPS["f32"], 4)}
     del wg, wu, fg, fu, xsum
+    progress("pass: codec, decode FFN, channel selection")
     for m_items, label in ((917504, "decoder stack: 224 matrices"), (64 * 1024 * 1024, "scaled pool")):
         n_mat = 224 if m_items == 917504 else 16384
         per = m_items // n_mat
@@ -564,6 +583,7 @@ def main():
         scores, _ = lrc.lrc_score_components(sigma=sig, mode="kfac")
         return lrc.lrc_allocate_ranks(scores, offs, cost, budget), info
 
+    progress("inputs resident")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -576,6 +596,7 @@ def main():
     assert int(info[0]) == 0 and int(out[4][0]) == 0
     n_kept = int(out[1][0])
     ms = 1e3 * elapsed / args.steps
+    progress(f"{args.steps} steps: {ms:.2f} ms per step")
     # the covariance alone: K accumulations back to back, timed with events around the loop
     s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s_ev.record()
@@ -596,6 +617,7 @@ def main():
     prof_ms = 1e3 * (time.perf_counter() - t1) / args.steps
     lrc.lrc_profile_stop()
     prof = lrc.lrc_profile_kernels()
+    progress("instrumented steps")
 
     kernels = {}
     for name, k in prof.items():
