@@ -18,16 +18,17 @@
 namespace lrc {
 namespace {
 
-// Eigensolver choice: a single Gram of size >= 512 goes through tridiagonalisation +
-// inverse iteration (O(k^3) once); batches of small Grams through block Jacobi, whose
-// rounds process every item of the batch at once.  LRC_EIGENSOLVER=jacobi|tridiag
-// overrides the choice (tridiag only applies to batch 1).
+// Eigensolver choice: a single Gram goes through tridiagonalisation + inverse iteration
+// (O(k^3) once, a fixed number of launches); batches of Grams through block Jacobi, whose
+// rounds process every item of the batch at once (its fixed sweep count costs more
+// launches than one tridiagonalisation for a single Gram of any size).
+// LRC_EIGENSOLVER=jacobi|tridiag overrides the choice (tridiag only applies to batch 1).
 bool use_tridiag(int64_t k, int64_t batch) {
+  (void)k;
   if (batch != 1) return false;
   const char* e = getenv("LRC_EIGENSOLVER");
   if (e && strcmp(e, "jacobi") == 0) return false;
-  if (e && strcmp(e, "tridiag") == 0) return true;
-  return k >= 512;
+  return true;
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {

@@ -16,7 +16,7 @@
 //   3. Eigenvectors of the wanted (largest) eigenvalues by inverse iteration on T with
 //      partial pivoting, two solves (the eigenvalues are accurate to ~eps ||T||): the
 //      factorisation and both solves of every vector in parallel; after each solve, per
-//      cluster of eigenvalues closer than 1e-7 ||T|| (a lone one is a cluster of one),
+//      cluster of eigenvalues closer than 1e-9 ||T|| (a lone one is a cluster of one),
 //      each iterate is orthogonalised against the cluster's earlier vectors and
 //      normalised (one wave per cluster of up to 32 members, modified Gram-Schmidt; a
 //      workgroup per longer cluster, block Gram-Schmidt applied twice).  Nothing is read
@@ -49,7 +49,13 @@ constexpr int BIS_PTS = 16;     // Sturm points per eigenvalue per multisection 
 constexpr int BIS_ITERS = 12;   // 17^12 > 2^49: width below 2^-48 of the bounds, under a count's own n eps accuracy
 constexpr int BIS_STAGE = 2048; // d, e^2 staged through LDS in chunks of this many
 constexpr int CL_MAX = 32;      // larger clusters are orthogonalised by a whole workgroup
-constexpr double CL_TOL = 1e-7; // eigenvalues closer than CL_TOL ||T|| share a cluster
+// eigenvalues closer than CL_TOL ||T|| share a cluster.  Bisection leaves an eigenvalue
+// within about n eps ||T|| (< 1e-12 ||T|| here), so two inverse iterations reduce a
+// neighbour at distance >= CL_TOL ||T|| to (1e-12 / CL_TOL)^2 = 1e-6 of the start vector
+// or less: such vectors need no orthogonalisation against each other.  A wider tolerance
+// would merge the densely spaced smallest eigenvalues of a whitened Gram (spacing about
+// 1e-7 ||T||) into clusters of thousands, whose orthogonalisation is quadratic in size.
+constexpr double CL_TOL = 1e-9;
 constexpr double EPS = 2.220446049250313e-16;
 
 // first row / column of the 64-row blocks of the trailing matrix that starts at s0: the

@@ -126,7 +126,7 @@ size_t lrc_accumulate_cov_workspace(lrc_dtype dt, int64_t n_tokens, int64_t d, u
  * Outputs (packed, fp32): sigma[batch][k], left[batch][d_out][r], right[batch][r][d_in].
  * info (device int32[batch], written by the call): 0 ok; p in 1..d_in: pivot p of X not
  *    positive (LRC_ENOTPD condition; every slice reports it); d_in + p: pivot p of G not
- *    positive; -1: the Jacobi solver (batches, and k < 512) still rotated after its last
+ *    positive; -1: the Jacobi solver (batch > 1) still rotated after its last
  *    sweep (LRC_ENOCONV condition).  The outputs of a slice with nonzero info are
  *    undefined.  These conditions are found on the device: the call itself returns LRC_OK
  *    once everything is enqueued (the solver's work is fixed in advance, so nothing is

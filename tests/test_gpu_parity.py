@@ -438,7 +438,7 @@ def test_decompose_repeated_singular_values(lrc, mult):
 
 
 def test_decompose_default_solver_mid_size(lrc):
-    """k >= 512 takes the tridiagonal route by default."""
+    """A single Gram takes the tridiagonal route by default (here k = 600, ragged panels)."""
     case = _decompose_case(lrc, 640, 600, 4000, 100, False, 91, dtype=torch.bfloat16)
     _check_decomposition(case, 100)
 
