@@ -8,7 +8,7 @@ sort-and-truncate at the budget of rank 1024.  Inputs are resident in HBM before
 timed region.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-secondary]
-    python bench.py --only syrk|tridiag|ffn-decode [--copy-probe-mib M]
+    python bench.py --only syrk|tridiag|fisher|ffn-decode [--copy-probe-mib M]
 
 The --only modes run one part of the path a few times (and, with --copy-probe-mib, a
 plain device copy of known size first): they are the programs the rocprofv3 summaries
@@ -81,7 +81,7 @@ def parse():
     p.add_argument("--rank", type=int, default=1024)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true", help="skip the other workloads and passes")
-    p.add_argument("--only", choices=["syrk", "tridiag", "ffn-decode"], default=None,
+    p.add_argument("--only", choices=["syrk", "tridiag", "fisher", "ffn-decode"], default=None,
                    help="run one part of the path (for rocprofv3) instead of the benchmark")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="first run a plain elementwise copy (neg) of this many MiB three times: the "
@@ -506,6 +506,28 @@ def only(args, lrc, torch, dev):
         e.record()
         torch.cuda.synchronize()
         res["ms_per_accumulation"] = round(s.elapsed_time(e) / 3, 4)
+    elif args.only == "fisher":
+        # empirical-Fisher scores at the decoder stack's attention shape: 32768 bf16 tokens,
+        # a 4096 x 4096 matrix, all 4096 components; one untimed and five timed calls
+        n, d, k = 32768, 4096, 4096
+        a = synth.activation_stream(n, d, 1.0, 41, dtype=torch.bfloat16, device=dev)
+        b = synth.activation_stream(n, d, 1.5, 42, dtype=torch.bfloat16, device=dev)
+        g = torch.Generator(device=dev)
+        g.manual_seed(43)
+        left = torch.randn(d, k, generator=g, device=dev) / d ** 0.5
+        right = torch.randn(k, d, generator=g, device=dev) / d ** 0.5
+        lrc.lrc_score_components(left=left, right=right, A=a, B=b)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(5):
+            lrc.lrc_score_components(left=left, right=right, A=a, B=b)
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / 5
+        flops = 2.0 * n * k * (d + d) + 3.0 * n * k
+        res["ms_per_call"] = round(ms, 4)
+        res["TFLOP/s"] = round(flops / (ms * 1e-3) / 1e12, 1)
     elif args.only == "tridiag":
         # one covariance and one whitened decomposition of the attention projection
         a = synth.activation_stream(args.tokens, args.d, 1.0, 31, outlier_frac=0.01, dtype=torch.bfloat16,

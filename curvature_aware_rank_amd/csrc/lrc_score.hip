@@ -11,10 +11,10 @@
 // bf16 activations (widths a multiple of 8) run on MFMA: each fp32 factor f is split into
 // bf16 parts f = hi + lo + r with hi = bf16(f), lo = bf16(f - hi), |r| <= 2^-16 |f|, and
 // a . f is taken as (a . hi) + (a . lo) with bf16 x bf16 products (exact) accumulated in
-// fp32.  A workgroup owns 256 tokens x 128 components; each of its four waves holds the
-// P and Q accumulators of 64 tokens x 128 components, reads its own activation rows
-// straight from memory into registers and shares the factor tile (hi and lo) through
-// LDS.  fp32 activations use a VALU kernel of 64 x 64 tiles.
+// fp32.  A workgroup owns 256 tokens x 128 components; each of its eight waves holds the
+// P and Q accumulators of 64 tokens x 64 components; the activation and factor tiles
+// (hi and lo) of each 64-wide reduction chunk are shared through LDS.  fp32 activations
+// use a VALU kernel of 64 x 64 tiles.
 #include "lrc_internal.h"
 
 namespace lrc {
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void fisher_partial_kernel(const T* __restrict
 // ---------------------------------------------------------------------------------
 // MFMA path (bf16 activations)
 // ---------------------------------------------------------------------------------
-constexpr int FT = 256;      // tokens per workgroup (4 waves x 64)
+constexpr int FT = 256;      // tokens per workgroup (4 token groups of 64)
 constexpr int FC = 128;      // components per workgroup
 constexpr int FK = 64;       // reduction chunk
 constexpr int FP = FK + 8;   // LDS row pitch of a factor tile (bf16): 144 B, conflict-free 16-B reads
@@ -156,130 +156,151 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+constexpr int FW = 8;                    // waves per workgroup: 4 token groups of 64 x 2 component halves
+constexpr int FNF = FC / 32 / (FW / 4);  // 32-component blocks per wave
+constexpr int FS_T = 4;       // token tiles per XCD super-tile
+constexpr int FS_C = 8;       // component tiles per XCD super-tile
+
 // acc[f][nf] (32 tokens x 32 components each) += X[tokens, 0:d] . F[components, 0:d]^T
-// with F given as bf16 hi and lo parts (components x d, row-major).  X rows are this
-// wave's 64 tokens; the factor tile goes through LDS buffers fs (2 stages x hi/lo).
-__device__ __forceinline__ void fisher_phase(const uint16_t* __restrict__ X, int d, int64_t n, int64_t tw,
-                                             const uint16_t* __restrict__ Fh, const uint16_t* __restrict__ Fl,
-                                             int k, int c0, uint16_t* fs, f32x16 (&acc)[2][4]) {
+// for this wave's 64 tokens (tile rows 64 tg ..) and its components (32 FNF ch .. of the
+// workgroup's 128), with F given as bf16 hi and lo parts (components x d, row-major).
+// Both the workgroup's activation tile (256 tokens) and its factor tile (128 components,
+// hi and lo) go through LDS, two stages of one 64-wide reduction chunk each: the global
+// loads are whole 128-byte row pieces (8 lanes per row), so every cache line a load
+// instruction touches is used in full; rows are padded to FP so that the fragment reads
+// (one row per lane) are conflict-free.  The next chunk's loads are in flight in registers
+// while the current one is computed.
+__device__ __forceinline__ void fisher_phase(const uint16_t* __restrict__ X, int d, int64_t n, int64_t t0, int tg,
+                                             int ch, const uint16_t* __restrict__ Fh,
+                                             const uint16_t* __restrict__ Fl, int k, int c0, uint16_t* fs,
+                                             uint16_t* xs, f32x16 (&acc)[2][FNF]) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int lr = lane & 31, lh = lane >> 5;
   const int nch = (d + FK - 1) / FK;
-  // activation addresses: row tw + f * 32 + lr (clamped), 16 B at column s * 16 + lh * 8
-  const uint16_t* xrow[2];
-#pragma unroll
-  for (int f = 0; f < 2; ++f) xrow[f] = X + min<int64_t>(tw + f * 32 + lr, n - 1) * d;
-  auto load_a = [&](u32x4 (&a)[2][4], int kc) {
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        const int col = min(kc + s4 * 16 + lh * 8, d - 8);
-        a[f][s4] = *reinterpret_cast<const u32x4*>(xrow[f] + col);
-      }
-  };
-  // factor staging: thread takes 16-B groups g = tid + 256 q: row g / 8, column group g % 8
+  // staging: thread takes 16-B groups g = tid + 64 FW q: row g / 8, column group g % 8
+  constexpr int FQ = FC * 8 / (64 * FW);   // factor groups per thread per part
+  constexpr int XQ = FT * 8 / (64 * FW);   // activation groups per thread
   const int grow = tid >> 3, gcol = (tid & 7) * 8;
-  auto load_f = [&](u32x4 (&g)[2][4], int kc) {
+  auto load_f = [&](u32x4 (&g)[2][FQ], u32x4 (&ga)[XQ], int kc) {
+    const int col = min(kc + gcol, d - 8);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t row = min(c0 + grow + 32 * q, k - 1);
-      const int col = min(kc + gcol, d - 8);
+    for (int q = 0; q < FQ; ++q) {
+      const int64_t row = min(c0 + grow + 8 * FW * q, k - 1);
       g[0][q] = *reinterpret_cast<const u32x4*>(Fh + row * d + col);
       g[1][q] = *reinterpret_cast<const u32x4*>(Fl + row * d + col);
     }
-  };
-  auto store_f = [&](const u32x4 (&g)[2][4], int buf, int kc) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const bool ok = c0 + grow + 32 * q < k && kc + gcol < d;
+    for (int q = 0; q < XQ; ++q) {
+      const int64_t row = min<int64_t>(t0 + grow + 8 * FW * q, n - 1);
+      ga[q] = *reinterpret_cast<const u32x4*>(X + row * d + col);
+    }
+  };
+  auto store_f = [&](const u32x4 (&g)[2][FQ], const u32x4 (&ga)[XQ], int buf, int kc) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const bool colok = kc + gcol < d;
+#pragma unroll
+    for (int q = 0; q < FQ; ++q) {
+      const bool ok = colok && c0 + grow + 8 * FW * q < k;
 #pragma unroll
       for (int hl = 0; hl < 2; ++hl)
-        *reinterpret_cast<u32x4*>(fs + (buf * 2 + hl) * (FC * FP) + (grow + 32 * q) * FP + gcol) = ok ? g[hl][q] : z;
+        *reinterpret_cast<u32x4*>(fs + (buf * 2 + hl) * (FC * FP) + (grow + 8 * FW * q) * FP + gcol) =
+            ok ? g[hl][q] : z;
     }
+    // tokens past the last are clamped copies of it; their products are masked at the end
+#pragma unroll
+    for (int q = 0; q < XQ; ++q)
+      *reinterpret_cast<u32x4*>(xs + buf * (FT * FP) + (grow + 8 * FW * q) * FP + gcol) = colok ? ga[q] : z;
   };
-  // one chunk from LDS buffer buf; each 16-wide step's activation registers are refilled
-  // with the next chunk's (column nkc) as soon as the step's MFMAs have been issued
-  auto compute = [&](int buf, u32x4 (&a)[2][4], int nkc, bool next) {
+  // the four (or eight) hi products of a step, then its lo products: an MFMA never waits
+  // for the result of the one issued just before it
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
+      u32x4 fr[2][FNF], ar[2];
 #pragma unroll
-      for (int nf = 0; nf < 4; ++nf) {
-        const int off = (nf * 32 + lr) * FP + s4 * 16 + lh * 8;
-        const u32x4 fh = *reinterpret_cast<const u32x4*>(fs + (buf * 2 + 0) * (FC * FP) + off);
-        const u32x4 fl = *reinterpret_cast<const u32x4*>(fs + (buf * 2 + 1) * (FC * FP) + off);
+      for (int f = 0; f < 2; ++f)
+        ar[f] = *reinterpret_cast<const u32x4*>(xs + buf * (FT * FP) + (tg * 64 + f * 32 + lr) * FP + s4 * 16 +
+                                                lh * 8);
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          acc[f][nf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[f][s4]), as_bf16x8(fh), acc[f][nf],
-                                                               0, 0, 0);
-          acc[f][nf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[f][s4]), as_bf16x8(fl), acc[f][nf],
-                                                               0, 0, 0);
-        }
+      for (int nf = 0; nf < FNF; ++nf) {
+        const int off = (ch * 32 * FNF + nf * 32 + lr) * FP + s4 * 16 + lh * 8;
+        fr[0][nf] = *reinterpret_cast<const u32x4*>(fs + (buf * 2 + 0) * (FC * FP) + off);
+        fr[1][nf] = *reinterpret_cast<const u32x4*>(fs + (buf * 2 + 1) * (FC * FP) + off);
       }
-      if (next) {
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          const int col = min(nkc + s4 * 16 + lh * 8, d - 8);
-          a[f][s4] = *reinterpret_cast<const u32x4*>(xrow[f] + col);
-        }
-      }
+      for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+        for (int nf = 0; nf < FNF; ++nf)
+#pragma unroll
+          for (int f = 0; f < 2; ++f)
+            acc[f][nf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ar[f]), as_bf16x8(fr[hl][nf]),
+                                                                 acc[f][nf], 0, 0, 0);
     }
   };
-  u32x4 g[2][4], a[2][4];
-  load_f(g, 0);
-  load_a(a, 0);
-  store_f(g, 0, 0);
-  if (nch > 1) load_f(g, FK);
+  u32x4 g[2][FQ], ga[XQ];
+  load_f(g, ga, 0);
+  store_f(g, ga, 0, 0);
+  if (nch > 1) load_f(g, ga, FK);
   __syncthreads();
   for (int c = 0; c < nch; ++c) {
     const int buf = c & 1;
-    compute(buf, a, (c + 1) * FK, c + 1 < nch);
-    if (c + 1 < nch) store_f(g, buf ^ 1, (c + 1) * FK);
-    if (c + 2 < nch) load_f(g, (c + 2) * FK);
+    compute(buf);
+    if (c + 1 < nch) store_f(g, ga, buf ^ 1, (c + 1) * FK);
+    if (c + 2 < nch) load_f(g, ga, (c + 2) * FK);
     __syncthreads();
   }
 }
 
-// Workgroups are numbered so that the components tiles of one token tile share an XCD
-// (consecutive workgroup ids go to consecutive XCDs): the activation rows of a token
-// tile are then fetched into one L2 only.
-__global__ __launch_bounds__(256) void fisher_mfma_kernel(const uint16_t* __restrict__ A,
-                                                          const uint16_t* __restrict__ B, int64_t n, int d_in,
-                                                          int d_out, const uint16_t* __restrict__ Rh,
-                                                          const uint16_t* __restrict__ Rl,
-                                                          const uint16_t* __restrict__ Lh,
-                                                          const uint16_t* __restrict__ Ll, int k, int n_ct, int n_tt,
-                                                          float* __restrict__ partial) {
+// Workgroup numbering (consecutive workgroup ids go to consecutive XCDs): the 32
+// workgroups an XCD runs side by side form one super-tile of 4 token tiles x 8 component
+// tiles, so at every reduction step the L2 of that XCD holds 4 activation slices and 8
+// factor slices, each fetched once and read by 8 or 4 workgroups (a column of 32 component
+// tiles per XCD would fetch every factor byte for one workgroup only).  Eight waves: wave
+// w takes tokens 64 (w / 2) .. of the tile and components 64 (w % 2) .. of the
+// workgroup's 128, so two waves share each SIMD (128 accumulator registers each) and cover
+// each other's latencies; every activation fragment read from LDS feeds four MFMAs (two
+// component blocks, hi and lo), every factor fragment two.
+__global__ __launch_bounds__(64 * FW, 1) void fisher_mfma_kernel(const uint16_t* __restrict__ A,
+                                                                 const uint16_t* __restrict__ B, int64_t n,
+                                                                 int d_in, int d_out, const uint16_t* __restrict__ Rh,
+                                                                 const uint16_t* __restrict__ Rl,
+                                                                 const uint16_t* __restrict__ Lh,
+                                                                 const uint16_t* __restrict__ Ll, int k, int n_ct,
+                                                                 int n_tt, float* __restrict__ partial) {
   __shared__ __attribute__((aligned(16))) uint16_t fs[2 * 2 * FC * FP];
-  __shared__ float red[4][FC];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2 * FT * FP];
+  __shared__ float red[FT / 64][FC];
   const int xcd = blockIdx.x & 7;
   const int i = blockIdx.x >> 3;
-  const int ct = i % n_ct;
-  const int tt = (i / n_ct) * 8 + xcd;
-  if (tt >= n_tt) return;
+  const int w = i % (FS_T * FS_C);
+  const int sup = (i / (FS_T * FS_C)) * 8 + xcd;     // super-tile
+  const int n_sc = (n_ct + FS_C - 1) / FS_C;
+  const int tt = (sup / n_sc) * FS_T + w / FS_C;
+  const int ct = (sup % n_sc) * FS_C + w % FS_C;
+  if (tt >= n_tt || ct >= n_ct) return;
   const int c0 = ct * FC;
   const int64_t t0 = int64_t(tt) * FT;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t tw = t0 + wave * 64;
-  f32x16 accp[2][4], accq[2][4];
+  const int tg = wave / (FW / 4), ch = wave % (FW / 4);
+  const int64_t tw = t0 + tg * 64;
+  f32x16 accp[2][FNF], accq[2][FNF];
 #pragma unroll
   for (int f = 0; f < 2; ++f)
 #pragma unroll
-    for (int nf = 0; nf < 4; ++nf)
+    for (int nf = 0; nf < FNF; ++nf)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         accp[f][nf][e] = 0.f;
         accq[f][nf][e] = 0.f;
       }
-  fisher_phase(A, d_in, n, tw, Rh, Rl, k, c0, fs, accp);
-  fisher_phase(B, d_out, n, tw, Lh, Ll, k, c0, fs, accq);
+  fisher_phase(A, d_in, n, t0, tg, ch, Rh, Rl, k, c0, fs, xs, accp);
+  fisher_phase(B, d_out, n, t0, tg, ch, Lh, Ll, k, c0, fs, xs, accq);
   // output layout of a 32 x 32 block: lane l, element e -> token row 8 (e / 4) + 4 (l / 32) + e % 4,
   // component column l % 32
   const int lr = lane & 31, lh = lane >> 5;
 #pragma unroll
-  for (int nf = 0; nf < 4; ++nf) {
+  for (int nf = 0; nf < FNF; ++nf) {
     float sum = 0.f;
 #pragma unroll
     for (int f = 0; f < 2; ++f)
@@ -291,15 +312,13 @@ __global__ __launch_bounds__(256) void fisher_mfma_kernel(const uint16_t* __rest
         sum = fmaf(t < n ? pv * pv : 0.f, qv * qv, sum);
       }
     sum += __shfl_xor(sum, 32);
-    if (lh == 0) red[wave][nf * 32 + lr] = sum;
+    if (lh == 0) red[tg][ch * 32 * FNF + nf * 32 + lr] = sum;
   }
   __syncthreads();
   if (tid < FC && c0 + tid < k)
     partial[int64_t(tt) * k + c0 + tid] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
 }
 
-// A score is a sum of non-negative terms over the tokens: a NaN or Inf in the tokens or
-// the factors (or an overflow) leaves it non-finite, which sets *info (when given).
 __global__ void fisher_final_kernel(const float* __restrict__ partial, int ntb, int k, int accumulate, int finalize,
                                     double inv2n, float* __restrict__ scores, int32_t* __restrict__ info) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -398,7 +417,9 @@ extern "C" lrc_status lrc_score_components(const void* A, const void* B, lrc_dty
         LRC_LAUNCHED();
       }
       const int n_ct = int(cdiv(k, FC));
-      const int64_t nblk = int64_t(n_ct) * cdiv(n_tt, 8) * 8;
+      // super-tiles of FS_T token tiles x FS_C component tiles, dealt to the 8 XCDs
+      const int64_t n_sup = cdiv(n_tt, FS_T) * cdiv(n_ct, FS_C);
+      const int64_t nblk = cdiv(n_sup, 8) * 8 * FS_T * FS_C;
       if (nblk > (int64_t(1) << 31) - 1) return LRC_EINVAL;
       // algorithmic work as for the VALU kernel below; the bytes count the bf16 hi/lo
       // factor copies this kernel reads
@@ -406,7 +427,7 @@ extern "C" lrc_status lrc_score_components(const void* A, const void* B, lrc_dty
                       2.0 * double(n_tokens) * double(k) * double(d_in + d_out) + 3.0 * double(n_tokens) * double(k),
                       2.0 * double(n_tokens) * double(d_in + d_out) + 4.0 * double(k) * double(d_in + d_out) +
                           4.0 * double(n_tt) * double(k));
-      fisher_mfma_kernel<<<unsigned(nblk), 256, 0, st>>>(static_cast<const uint16_t*>(A),
+      fisher_mfma_kernel<<<unsigned(nblk), 64 * FW, 0, st>>>(static_cast<const uint16_t*>(A),
                                                          static_cast<const uint16_t*>(B), n_tokens, int(d_in),
                                                          int(d_out), w.rh, w.rl, w.lh, w.ll, int(k), n_ct, n_tt,
                                                          w.partial);
