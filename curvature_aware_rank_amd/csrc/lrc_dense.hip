@@ -340,10 +340,12 @@ __global__ __launch_bounds__(64) void potf2_kernel(float* __restrict__ L, int64_
   }
 }
 
-// Rows below a factored diagonal block: X <- X D^-T (one lane per row, 64 rows per wave)
+// Rows below a factored diagonal block: X <- X D^-T (one lane per row, 64 rows per wave).
+// Rows are loaded as 16-byte groups when the pitch and base allow; the solve reads each
+// row of D from LDS four entries at a time (broadcast reads, the FMAs in column order).
 __global__ __launch_bounds__(64) void trsm_panel_kernel(float* __restrict__ L, int64_t ldl, int64_t n, int64_t k0,
                                                         const int* __restrict__ info) {
-  __shared__ float D[NB][NB + 1];
+  __shared__ __align__(16) float D[NB][NB + 4];
   __shared__ float rdiag[NB];
   if (*info != 0) return;
   const int lane = threadIdx.x;
@@ -351,10 +353,28 @@ __global__ __launch_bounds__(64) void trsm_panel_kernel(float* __restrict__ L, i
   const int64_t rc = r < n ? r : n - 1;
   float x[NB], dcol[NB];
   // all loads first: row `lane` of the diagonal block (column of D^T) and this lane's row
+  const float* drow = L + (k0 + lane) * ldl + k0;
+  const float* xrow = L + rc * ldl + k0;
+  if (ldl % 4 == 0 && (reinterpret_cast<uintptr_t>(L) & 15) == 0) {
 #pragma unroll
-  for (int c = 0; c < NB; ++c) {
-    dcol[c] = L[(k0 + lane) * ldl + k0 + c];
-    x[c] = L[rc * ldl + k0 + c];
+    for (int c = 0; c < NB; c += 4) {
+      const float4 dv = *reinterpret_cast<const float4*>(drow + c);
+      const float4 xv = *reinterpret_cast<const float4*>(xrow + c);
+      dcol[c] = dv.x;
+      dcol[c + 1] = dv.y;
+      dcol[c + 2] = dv.z;
+      dcol[c + 3] = dv.w;
+      x[c] = xv.x;
+      x[c + 1] = xv.y;
+      x[c + 2] = xv.z;
+      x[c + 3] = xv.w;
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
+      dcol[c] = drow[c];
+      x[c] = xrow[c];
+    }
   }
   float dl = 1.f;
 #pragma unroll
@@ -368,7 +388,13 @@ __global__ __launch_bounds__(64) void trsm_panel_kernel(float* __restrict__ L, i
   for (int j = 0; j < NB; ++j) {
     float v = x[j];
 #pragma unroll
-    for (int c = 0; c < j; ++c) v = fmaf(-x[c], D[j][c], v);
+    for (int c4 = 0; c4 < j; c4 += 4) {
+      const float4 d = *reinterpret_cast<const float4*>(&D[j][c4]);
+      v = fmaf(-x[c4], d.x, v);
+      if (c4 + 1 < j) v = fmaf(-x[c4 + 1], d.y, v);
+      if (c4 + 2 < j) v = fmaf(-x[c4 + 2], d.z, v);
+      if (c4 + 3 < j) v = fmaf(-x[c4 + 3], d.w, v);
+    }
     x[j] = v * rdiag[j];
   }
   if (r < n) {
