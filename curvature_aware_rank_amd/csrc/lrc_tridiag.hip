@@ -554,11 +554,15 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
     }
   }
   if (!do_next) return;
-  // column s0: rows s0.., C[r][s0] -= sum_c V[r][c] W[s0][c] + W[r][c] V[s0][c], c = 0..jj
+  // column s0: rows s0.., C[r][s0] -= sum_c V[r][c] W[s0][c] + W[r][c] V[s0][c], c = 0..jj.
+  // The diagonal entry goes to d[s0] only: every workgroup of this launch reads the
+  // panel-start C[s0][s0] (a00 above), so it must not be overwritten here (a workgroup
+  // that starts after this one has finished would read the updated value); nothing reads
+  // it later (the next columns' trailing matrices start below and right of it).
   double sq = 0.0;
   if (r >= s0 && r < n && part == 0) {
     const double val = cs0x - (c2 + (v * w0 + w));
-    A[int64_t(r) * lda + s0] = val;
+    if (r > s0) A[int64_t(r) * lda + s0] = val;
     xv_next[r] = val;
     if (r == s0) d[s0] = val;
     if (r == s0 + 1) *x0_next = val;

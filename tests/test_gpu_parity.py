@@ -165,7 +165,7 @@ def _check_decomposition(case, rank, sig_rtol=1e-4, angle_tol=1e-3):
     ref, sig = case["ref"], case["sig"].astype(np.float64)
     s_ref = ref["sigma"]
     assert np.all(case["info"] == 0)
-    # retained singular values: relative error (spec bound 1e-4)
+    # retained singular values: relative error (stated accuracy 1e-4)
     rel = np.abs(sig[:rank] - s_ref[:rank]) / s_ref[:rank]
     assert rel.max() <= sig_rtol, rel.max()
     # every sigma (discarded tail included): absolute error within 1e-4 sigma_1 -- the
@@ -354,6 +354,33 @@ def test_decompose_does_not_wait_for_the_gpu(lrc, monkeypatch, solver_name, k):
     assert pending, f"the stream had drained when the call returned ({t_call * 1e3:.1f} ms)"
     assert t_call < 0.5 * reps * per_mm, (t_call, reps * per_mm)
     assert int(info[0]) == 0 and torch.equal(sig, sig0)
+
+
+def test_decompositions_on_two_streams_match_sequential(lrc):
+    """Independent decompositions issued on two streams at once (each with its own
+    buffers) give the same bits as one after another: no kernel may depend on the order
+    or timing in which its workgroups are dispatched.  A kernel that reads an entry which
+    another of its own workgroups writes goes wrong only when some workgroups start late,
+    as they do while another stream's kernels hold compute units: this is the case that
+    shows it at the attention projection's size."""
+    d, n, r = 4096, 8192, 256
+    a = synth.activation_stream(n, d, 1.0, 91, dtype=torch.bfloat16).to(dev())
+    w = synth.weight(d, d, 92).to(dev())
+    cov = torch.zeros(d, d, device=dev())
+    lrc.lrc_accumulate_cov(a, cov)
+    ref = [t.clone() for t in lrc.lrc_whiten_decompose(w, r, cov, n)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    covs = [cov.clone(), cov.clone()]
+    torch.cuda.synchronize()
+    outs = []
+    for k in range(6):
+        with torch.cuda.stream(streams[k % 2]):
+            outs.append(lrc.lrc_whiten_decompose(w, r, covs[k % 2], n))
+    torch.cuda.synchronize()
+    for k, out in enumerate(outs):
+        for got, want, name in zip(out, ref, ("sigma", "left", "right", "info")):
+            assert torch.equal(got, want), f"call {k} (stream {k % 2}): {name} differs from the sequential result"
 
 
 def test_cov_and_scores_flag_nonfinite_inputs(lrc):
