@@ -139,7 +139,7 @@ def cpu_baseline(d, n, rank):
     progress(f"oracle: attention projection {t_cov + t_dec:.1f} s")
 
     # single linear layer 256 x 256, 4096 fp32 tokens, two-sided, rank 64: whole
-    cs0 = synth.config_spec(0)
+    cs0 = synth.workload_spec("single_layer_256")
     a0 = synth.stream(cs0, "a").numpy()
     b0 = synth.stream(cs0, "b").numpy()
     w0 = synth.weight(256, 256, 3).numpy()
@@ -154,7 +154,7 @@ def cpu_baseline(d, n, rank):
     # FFN pair: covariances per token measured on 2048 tokens of each stream of the up
     # projection (x 131072 / 2048, twice for the pair), the up projection's two-sided
     # decomposition at full size (the down projection's taken as equal)
-    cs2 = synth.config_spec(2, n_tokens=2048)
+    cs2 = synth.workload_spec("ffn_pair_11008x4096", n_tokens=2048)
     t_tok = 0.0
     covs = {}
     for key in ("a_up", "b_up"):
@@ -179,7 +179,7 @@ def cpu_baseline(d, n, rank):
     # scores on 1024 tokens (x32 to the 32768 tokens), both x224; covariances at the
     # measured per-token rate (scaled by width squared); the 917,504-component allocation
     # whole
-    cs3 = synth.config_spec(3, n_tokens=1024)
+    cs3 = synth.workload_spec("decoder_stack_32_layers", n_tokens=1024)
     a3 = synth.stream(cs3, "attn_in").float().numpy()
     b3 = synth.stream(cs3, "g_q").float().numpy()
     w3 = synth.weight(4096, 4096, 1000).numpy()
@@ -238,7 +238,7 @@ def workloads(lrc, torch, dev):
     import synth
     out = {}
     # single linear layer: 256 x 256, 4096 fp32 tokens, two-sided, rank 64
-    cs = synth.config_spec(0)
+    cs = synth.workload_spec("single_layer_256")
     a = synth.stream(cs, "a", device=dev)
     b = synth.stream(cs, "b", device=dev)
     w = synth.weight(256, 256, 3, device=dev)
@@ -260,7 +260,7 @@ def workloads(lrc, torch, dev):
     del a, b, w, xs, gs
 
     # FFN pair: 131072 bf16 tokens per stream, QAW on the activations, two-sided, rank 2048
-    cs = synth.config_spec(2)
+    cs = synth.workload_spec("ffn_pair_11008x4096")
     st = {k: synth.stream(cs, k, device=dev) for k in cs.streams}
     ws = [synth.weight(m.d_out, m.d_in, 45 + i, device=dev) for i, m in enumerate(cs.matrices)]
     covs = {k: torch.empty(v.shape[1], v.shape[1], device=dev) for k, v in st.items()}
@@ -296,7 +296,7 @@ def workloads(lrc, torch, dev):
     # 7 empirical-Fisher score passes) and one allocation over the 917,504 components; one
     # layer's streams and weights are generated once and reused by every layer (the work
     # does not depend on the values)
-    cs = synth.config_spec(3)
+    cs = synth.workload_spec("decoder_stack_32_layers")
     n = cs.n_tokens
     st = {k: synth.stream(cs, k, device=dev) for k in cs.streams}
     ws = [synth.weight(m.d_out, m.d_in, 1000 + i, device=dev) for i, m in enumerate(cs.matrices)]
@@ -329,7 +329,7 @@ def workloads(lrc, torch, dev):
     del st, ws, covs, scores
 
     # per-head K/V: 65536 bf16 tokens, 64 head slices of 128 x 4096, K-FAC scores, 40% budget
-    cs = synth.config_spec(4)
+    cs = synth.workload_spec("kv_heads_64x128x4096")
     a = synth.stream(cs, "a", device=dev)
     w3 = torch.cat([synth.weight(4096, 4096, 137, device=dev), synth.weight(4096, 4096, 139, device=dev)]).view(
         64, 128, 4096)

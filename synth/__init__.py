@@ -26,8 +26,8 @@ from dataclasses import dataclass, field
 import torch
 
 __all__ = [
-    "haar_rotation", "activation_stream", "weight", "CONFIGS", "LayerSpec",
-    "config_spec", "layer_scale",
+    "haar_rotation", "activation_stream", "weight", "WORKLOADS", "LayerSpec",
+    "workload_spec", "layer_scale",
 ]
 
 
@@ -99,8 +99,8 @@ class LayerSpec:
 
 
 @dataclass
-class ConfigSpec:
-    index: int
+class WorkloadSpec:
+    name: str
     workload: str
     n_tokens: int
     rank: int | None               # fixed rank per matrix (None: allocation decides)
@@ -114,37 +114,37 @@ class ConfigSpec:
     head_dim: int = 0
 
 
-CONFIGS = {
-    0: "single linear layer 256x256 fp32, two-sided K-FAC whitening, 4096 tokens, rank 64",
-    1: "attention projection 4096x4096, 65536 bf16 tokens, activation-only whitening, rank 1024",
-    2: "FFN pair up 11008x4096 / down 4096x11008, 131072 bf16 tokens, two-sided, int8 QAW, rank ratio 0.5",
-    3: "32-layer decoder stack (224 matrices), 32768 tokens per layer, Fisher scores, 60% budget",
-    4: "K/V per-head 128x4096 slices (64 heads), 65536 bf16 tokens, 40% budget",
+WORKLOADS = {
+    "single_layer_256": "single linear layer 256x256 fp32, two-sided K-FAC whitening, 4096 tokens, rank 64",
+    "attention_projection_4096": "attention projection 4096x4096, 65536 bf16 tokens, activation-only whitening, rank 1024",
+    "ffn_pair_11008x4096": "FFN pair up 11008x4096 / down 4096x11008, 131072 bf16 tokens, two-sided, int8 QAW, rank ratio 0.5",
+    "decoder_stack_32_layers": "32-layer decoder stack (224 matrices), 32768 tokens per layer, Fisher scores, 60% budget",
+    "kv_heads_64x128x4096": "K/V per-head 128x4096 slices (64 heads), 65536 bf16 tokens, 40% budget",
 }
 
 
-def config_spec(index: int, n_tokens: int | None = None, seed: int = 1234) -> ConfigSpec:
+def workload_spec(name: str, n_tokens: int | None = None, seed: int = 1234) -> WorkloadSpec:
     """Shapes and stream recipes of the five workloads (n_tokens may be shrunk for tests)."""
-    if index == 0:
+    if name == "single_layer_256":
         n = n_tokens or 4096
-        cs = ConfigSpec(0, CONFIGS[0], n, 64, None, None, torch.float32, False)
+        cs = WorkloadSpec("single_layer_256", WORKLOADS["single_layer_256"], n, 64, None, None, torch.float32, False)
         cs.streams = {"a": (256, 1.2, 0.0, seed + 11), "b": (256, 1.2, 0.0, seed + 23)}
         cs.matrices = [LayerSpec("w", 256, 256, "a", "b", True)]
-    elif index == 1:
+    elif name == "attention_projection_4096":
         n = n_tokens or 65536
-        cs = ConfigSpec(1, CONFIGS[1], n, 1024, None, None, torch.bfloat16, False)
+        cs = WorkloadSpec("attention_projection_4096", WORKLOADS["attention_projection_4096"], n, 1024, None, None, torch.bfloat16, False)
         cs.streams = {"a": (4096, 1.0, 0.01, seed + 31)}
         cs.matrices = [LayerSpec("w", 4096, 4096, "a", None, False)]
-    elif index == 2:
+    elif name == "ffn_pair_11008x4096":
         n = n_tokens or 131072
-        cs = ConfigSpec(2, CONFIGS[2], n, None, 0.5, None, torch.bfloat16, True)
+        cs = WorkloadSpec("ffn_pair_11008x4096", WORKLOADS["ffn_pair_11008x4096"], n, None, 0.5, None, torch.bfloat16, True)
         cs.streams = {"a_up": (4096, 1.0, 0.01, seed + 41), "b_up": (11008, 1.5, 0.0, seed + 43),
                       "a_down": (11008, 1.0, 0.01, seed + 47), "b_down": (4096, 1.5, 0.0, seed + 53)}
         cs.matrices = [LayerSpec("up", 11008, 4096, "a_up", "b_up", True),
                        LayerSpec("down", 4096, 11008, "a_down", "b_down", True)]
-    elif index == 3:
+    elif name == "decoder_stack_32_layers":
         n = n_tokens or 32768
-        cs = ConfigSpec(3, CONFIGS[3], n, None, None, 0.6, torch.bfloat16, False)
+        cs = WorkloadSpec("decoder_stack_32_layers", WORKLOADS["decoder_stack_32_layers"], n, None, None, 0.6, torch.bfloat16, False)
         # per layer; the layer index is folded into the seeds by the caller
         cs.streams = {"attn_in": (4096, 1.0, 0.0, seed + 61), "o_in": (4096, 1.0, 0.0, seed + 67),
                       "mlp_in": (4096, 1.0, 0.0, seed + 71), "down_in": (11008, 1.0, 0.0, seed + 73),
@@ -159,23 +159,23 @@ def config_spec(index: int, n_tokens: int | None = None, seed: int = 1234) -> Co
                        LayerSpec("gate", 11008, 4096, "mlp_in", "g_gate", False),
                        LayerSpec("up", 11008, 4096, "mlp_in", "g_up", False),
                        LayerSpec("down", 4096, 11008, "down_in", "g_down", False)]
-    elif index == 4:
+    elif name == "kv_heads_64x128x4096":
         n = n_tokens or 65536
-        cs = ConfigSpec(4, CONFIGS[4], n, None, None, 0.4, torch.bfloat16, False)
+        cs = WorkloadSpec("kv_heads_64x128x4096", WORKLOADS["kv_heads_64x128x4096"], n, None, None, 0.4, torch.bfloat16, False)
         cs.streams = {"a": (4096, 1.0, 0.01, seed + 131)}
         cs.matrices = [LayerSpec("k", 4096, 4096, "a", None, False),
                        LayerSpec("v", 4096, 4096, "a", None, False)]
         cs.heads, cs.head_dim = 32, 128
     else:
-        raise ValueError(f"no workload {index}")
+        raise ValueError(f"no workload {name!r}")
     return cs
 
 
-def stream(cs: ConfigSpec, key: str, *, layer: int = 0, device="cpu", n_tokens: int | None = None,
+def stream(cs: WorkloadSpec, key: str, *, layer: int = 0, device="cpu", n_tokens: int | None = None,
            width: int | None = None) -> torch.Tensor:
     """Draw one calibration stream of a workload (layer folds into the seed for the stack)."""
     d, p, frac, sd = cs.streams[key]
     d = width or d
-    scale = layer_scale(layer, sd) if (cs.index == 3 and not key.startswith("g_")) else 1.0
+    scale = layer_scale(layer, sd) if (cs.name == "decoder_stack_32_layers" and not key.startswith("g_")) else 1.0
     return activation_stream(n_tokens or cs.n_tokens, d, p, sd + 7919 * layer, outlier_frac=frac,
                              scale=scale, dtype=cs.dtype, device=device)

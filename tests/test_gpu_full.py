@@ -138,7 +138,7 @@ def test_ffn_two_sided_qaw(lrc, which):
     4096 x 11008 (output side; 11008-wide activation covariance and Cholesky).  16384
     tokens keep the oracle's fp64 covariances and SVD near a minute."""
     n, r = 16384, 2048
-    cs = synth.config_spec(2, n_tokens=n)
+    cs = synth.workload_spec("ffn_pair_11008x4096", n_tokens=n)
     m = cs.matrices[0 if which == "up" else 1]
     a = synth.stream(cs, m.a_stream, device=dev())
     b = synth.stream(cs, m.b_stream, device=dev())
@@ -166,7 +166,7 @@ def test_ffn_two_sided_qaw(lrc, which):
 def test_ffn_full_token_covariances_sampled(lrc):
     """All 131072 tokens: QAW activation covariance (4096) and gradient covariance
     (11008), sampled entries against the oracle."""
-    cs = synth.config_spec(2)
+    cs = synth.workload_spec("ffn_pair_11008x4096")
     rng = np.random.default_rng(2)
     a = synth.stream(cs, "a_up", device=dev())
     xs = torch.zeros(4096, 4096, device=dev())
@@ -270,7 +270,7 @@ def test_decoder_stack_full(lrc):
     allocation of the layer's own pool from the oracle's fp64 scores, which may differ
     from the GPU's only inside the band of components whose key lies within the measured
     score error of the cut key."""
-    cs = synth.config_spec(3)
+    cs = synth.workload_spec("decoder_stack_32_layers")
     n = cs.n_tokens
     all_scores, costs, sizes, infos = [], [], [], []
     layer0 = {}
