@@ -5,9 +5,12 @@ workload: 65536 bf16 tokens x 4096 channels streamed into the activation covaria
 (SYRK on MFMA), Cholesky, whitening, fp64 Gram + eigensolve, back-map to rank 1024,
 per-component K-FAC scores (this workload has no gradients) and the global
 sort-and-truncate at the budget of rank 1024.  Inputs are resident in HBM before the
-timed region.  Prints one JSON line.
+timed region.  The K timed steps are independent layers issued round robin on --streams
+HIP streams (default 2, each with its own covariance buffer), so two layers are in flight
+at a time; `value` is K / the wall time of the region.  The same K steps one after another
+on one stream give `value_one_stream` (one layer's latency).  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-secondary]
+    python bench.py [--steps K] [--warmup W] [--streams S] [--no-cpu-baseline] [--no-secondary]
     python bench.py --only syrk|tridiag|fisher|ffn-decode [--copy-probe-mib M]
 
 The --only modes run one part of the path a few times (and, with --copy-probe-mib, a
@@ -79,6 +82,8 @@ def parse():
     p.add_argument("--tokens", type=int, default=65536)
     p.add_argument("--d", type=int, default=4096)
     p.add_argument("--rank", type=int, default=1024)
+    p.add_argument("--streams", type=int, default=2,
+                   help="HIP streams the timed steps are issued on, round robin (independent layers in flight)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true", help="skip the other workloads and passes")
     p.add_argument("--only", choices=["syrk", "tridiag", "fisher", "ffn-decode"], default=None,
@@ -233,8 +238,10 @@ def _time(fn, torch, reps):
     return sorted(ts)[len(ts) // 2]
 
 
-def workloads(lrc, torch, dev):
-    """End-to-end GPU times of the other workloads (inputs resident, generation excluded)."""
+def workloads(lrc, torch, dev, workers):
+    """End-to-end GPU times of the other workloads (inputs resident, generation excluded).
+    workers: the streams the decoder stack's matrices are spread over (the ones the timed
+    steps ran on: the GPU has few hardware queues, and streams beyond them share one)."""
     import synth
     out = {}
     # single linear layer: 256 x 256, 4096 fp32 tokens, two-sided, rank 64
@@ -266,16 +273,25 @@ def workloads(lrc, torch, dev):
     covs = {k: torch.empty(v.shape[1], v.shape[1], device=dev) for k, v in st.items()}
 
     def cfg2():
+        # the four covariances on the current stream, then the two decompositions on the
+        # worker streams (independent matrices)
         for k, c in covs.items():
             c.zero_()
             lrc.lrc_accumulate_cov(st[k], c, quant=k.startswith("a"))
-        for m, wm in zip(cs.matrices, ws):
-            lrc.lrc_whiten_decompose(wm, 2048, covs[m.a_stream], cs.n_tokens, covs[m.b_stream], cs.n_tokens)
+        main_st = torch.cuda.current_stream()
+        for wst in workers:
+            wst.wait_stream(main_st)
+        for mi, (m, wm) in enumerate(zip(cs.matrices, ws)):
+            with torch.cuda.stream(workers[mi % len(workers)]):
+                lrc.lrc_whiten_decompose(wm, 2048, covs[m.a_stream], cs.n_tokens, covs[m.b_stream], cs.n_tokens)
+        for wst in workers:
+            main_st.wait_stream(wst)
 
     cfg2()
     t = _time(cfg2, torch, 2)
     out["ffn_pair_11008x4096"] = {"workload": "up 11008x4096 + down 4096x11008, 131072 bf16 tokens per stream, "
-                                              "int8 QAW, two-sided, rank 2048", "ms": round(t * 1e3, 1)}
+                                              "int8 QAW, two-sided, rank 2048", "streams": len(workers),
+                                  "ms": round(t * 1e3, 1)}
     progress("workload: FFN pair")
     # the QAW pre-pass alone, measured on the library's events (bf16 read, int8 codes and
     # the two bf16 terms written)
@@ -295,38 +311,58 @@ def workloads(lrc, torch, dev):
     # decoder stack: 32 layers x (4 covariances + 7 decompositions with every component +
     # 7 empirical-Fisher score passes) and one allocation over the 917,504 components; one
     # layer's streams and weights are generated once and reused by every layer (the work
-    # does not depend on the values)
+    # does not depend on the values).  A layer's covariances are made on the main stream
+    # (two sets, alternating by layer, so that the next layer's accumulate while this
+    # layer's decompositions run); its seven matrices are decomposed and scored on the
+    # worker streams, round robin; the allocation runs once all of them are done.
     cs = synth.workload_spec("decoder_stack_32_layers")
     n = cs.n_tokens
     st = {k: synth.stream(cs, k, device=dev) for k in cs.streams}
     ws = [synth.weight(m.d_out, m.d_in, 1000 + i, device=dev) for i, m in enumerate(cs.matrices)]
-    covs = {k: torch.empty(st[k].shape[1], st[k].shape[1], device=dev) for k in ("attn_in", "o_in", "mlp_in",
-                                                                               "down_in")}
+    cov_keys = ("attn_in", "o_in", "mlp_in", "down_in")
+    cov_sets = [{k: torch.empty(st[k].shape[1], st[k].shape[1], device=dev) for k in cov_keys} for _ in range(2)]
     scores = torch.empty(224 * 4096, device=dev)
     offs = torch.arange(0, 224 * 4096 + 1, 4096, dtype=torch.int64, device=dev)
     cost = torch.tensor([m.d_out + m.d_in for m in cs.matrices] * 32, dtype=torch.int64, device=dev)
     budget = int(0.6 * 32 * sum(m.d_out * m.d_in for m in cs.matrices))
+    ns = len(workers)
+    main_st = torch.cuda.current_stream()
+    done = [[torch.cuda.Event() for _ in range(ns)] for _ in range(2)]   # per covariance set
     torch.cuda.synchronize()
     progress("workload: decoder stack inputs ready")
     t0 = time.perf_counter()
     for layer in range(32):
+        covs = cov_sets[layer % 2]
+        if layer >= 2:   # this set's previous layer has been decomposed
+            for e in done[layer % 2]:
+                main_st.wait_event(e)
         for k, c in covs.items():
             c.zero_()
             lrc.lrc_accumulate_cov(st[k], c)
+        ready = torch.cuda.Event()
+        ready.record(main_st)
+        for wst in workers:
+            wst.wait_event(ready)
         for mi, (m, wm) in enumerate(zip(cs.matrices, ws)):
-            _, left, right, _ = lrc.lrc_whiten_decompose(wm, 4096, covs[m.a_stream], n)
-            j = (layer * 7 + mi) * 4096
-            lrc.lrc_score_components(left, right, A=st[m.a_stream], B=st[m.b_stream], scores=scores[j:j + 4096])
-            del left, right
+            with torch.cuda.stream(workers[mi % ns]):
+                _, left, right, _ = lrc.lrc_whiten_decompose(wm, 4096, covs[m.a_stream], n)
+                j = (layer * 7 + mi) * 4096
+                lrc.lrc_score_components(left, right, A=st[m.a_stream], B=st[m.b_stream],
+                                         scores=scores[j:j + 4096])
+                del left, right
+        for i, wst in enumerate(workers):
+            done[layer % 2][i].record(wst)
+    for wst in workers:
+        main_st.wait_stream(wst)
     lrc.lrc_allocate_ranks(scores, offs, cost, budget)
     torch.cuda.synchronize()
     t = time.perf_counter() - t0
     out["decoder_stack_32_layers"] = {
         "workload": "32 layers x (q,k,v,o 4096x4096, gate/up 11008x4096, down 4096x11008), 32768 bf16 tokens per "
                     "stream, every component decomposed and Fisher-scored, allocation of 917504 components at 60%",
-        "s": round(t, 2), "matrices_per_s": round(224 / t, 2)}
-    progress(f"workload: decoder stack {t:.1f} s")
-    del st, ws, covs, scores
+        "streams": ns, "s": round(t, 2), "matrices_per_s": round(224 / t, 2)}
+    progress(f"workload: decoder stack {t:.1f} s on {ns} stream(s)")
+    del st, ws, cov_sets, scores
 
     # per-head K/V: 65536 bf16 tokens, 64 head slices of 128 x 4096, K-FAC scores, 40% budget
     cs = synth.workload_spec("kv_heads_64x128x4096")
@@ -590,7 +626,10 @@ def main():
     d, n, r = args.d, args.tokens, args.rank
     a = synth.activation_stream(n, d, 1.0, 31, outlier_frac=0.01, dtype=torch.bfloat16, device=dev)
     w = synth.weight(d, d, 35, device=dev)
-    cov = torch.empty(d, d, dtype=torch.float32, device=dev)
+    ns = max(1, args.streams)
+    streams = [torch.cuda.Stream() for _ in range(ns)]
+    covs = [torch.empty(d, d, dtype=torch.float32, device=dev) for _ in range(ns)]
+    cov = covs[0]
     offs = torch.tensor([0, d], dtype=torch.int64, device=dev)
     cost = torch.tensor([2 * d], dtype=torch.int64, device=dev)
     budget = r * 2 * d
@@ -598,27 +637,43 @@ def main():
         copy_probe(torch, dev, args.copy_probe_mib)
     torch.cuda.synchronize()
 
-    def step():
-        cov.zero_()
-        lrc.lrc_accumulate_cov(a, cov)
-        sig, left, right, info = lrc.lrc_whiten_decompose(w, r, cov, n)
+    def step(c=cov):
+        c.zero_()
+        lrc.lrc_accumulate_cov(a, c)
+        sig, left, right, info = lrc.lrc_whiten_decompose(w, r, c, n)
         scores, _ = lrc.lrc_score_components(sigma=sig, mode="kfac")
         return lrc.lrc_allocate_ranks(scores, offs, cost, budget), info
 
+    def run_steps(k_steps, n_streams):
+        """k_steps whole steps, step k on stream k mod n_streams with that stream's own
+        covariance buffer (the layers are independent); returns the last outputs of each."""
+        last = {}
+        for k in range(k_steps):
+            i = k % n_streams
+            with torch.cuda.stream(streams[i]):
+                last[i] = step(covs[i])
+        return last
+
     progress("inputs resident")
-    for _ in range(args.warmup):
-        step()
+    run_steps(max(args.warmup, ns), ns)
     torch.cuda.synchronize()
-    # timed region: K whole steps, nothing else on the stream
+    # timed region: K whole steps issued round robin on the streams, nothing else queued;
+    # the clock stops when every stream has drained
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        out, info = step()
+    last = run_steps(args.steps, ns)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    assert int(info[0]) == 0 and int(out[4][0]) == 0
-    n_kept = int(out[1][0])
+    for out, info in last.values():
+        assert int(info[0]) == 0 and int(out[4][0]) == 0
+    n_kept = int(last[0][0][1][0])
     ms = 1e3 * elapsed / args.steps
-    progress(f"{args.steps} steps: {ms:.2f} ms per step")
+    progress(f"{args.steps} steps on {ns} stream(s): {ms:.2f} ms per step")
+    # the same K steps one after another on one stream: the latency of one layer
+    t0 = time.perf_counter()
+    run_steps(args.steps, 1)
+    torch.cuda.synchronize()
+    ms_one = 1e3 * (time.perf_counter() - t0) / args.steps
+    progress(f"{args.steps} steps on one stream: {ms_one:.2f} ms per step")
     # the covariance alone: K accumulations back to back, timed with events around the loop
     s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s_ev.record()
@@ -660,7 +715,7 @@ def main():
     work = (dk["flops"] if roof["unit"] == "TFLOP/s" else dk["bytes"]) / dk["launches"]
     achieved = work / avg_s / (1e12 if roof["unit"] == "TFLOP/s" else 1e9)
     tr = TRAFFIC.get(dom)
-    dec_ms = ms - cov_ms
+    dec_ms = ms_one - cov_ms   # one layer's own decomposition time (no other layer in flight)
     res = {
         "metric": METRIC,
         "value": round(1e3 / ms, 4),
@@ -669,6 +724,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 3),
+        "steps_in_flight": ns,
+        "ms_per_step_one_stream": round(ms_one, 3),
+        "value_one_stream": round(1e3 / ms_one, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -676,7 +734,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"attention projection W {d}x{d} fp32, {n} bf16 calibration tokens "
                                f"(power-law spectrum, 1% outlier channels x20), activation-only whitening, rank {r}",
-                   "tokens_per_layer": n, "d": d, "rank": r},
+                   "tokens_per_layer": n, "d": d, "rank": r, "streams": ns},
         "cov_tokens_per_s": round(n / (cov_ms * 1e-3), 1),
         "cov_ms": round(cov_ms, 4),
         "cov_mfma_bf16_frac": round(n * d * (d + 1.0) / (cov_ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
@@ -697,7 +755,7 @@ def main():
     }
     if not args.no_secondary:
         res["secondary"] = passes(lrc, torch, dev)
-        res["workloads"] = workloads(lrc, torch, dev)
+        res["workloads"] = workloads(lrc, torch, dev, streams)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(d, n, r)
     print(json.dumps(res), flush=True)
