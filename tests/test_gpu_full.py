@@ -17,15 +17,30 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 U32 = 2.0 ** -24
 _T0 = [0.0]
+_CAP = [None]
+
+
+@pytest.fixture(autouse=True)
+def _progress_past_capture(capsys):
+    """These tests run for minutes: their progress lines go to the terminal even while
+    pytest captures output (a run that prints nothing for minutes looks hung)."""
+    _CAP[0] = capsys
+    yield
+    _CAP[0] = None
 
 
 def step(msg):
-    """Progress line for long full-size runs (shown with pytest -s)."""
+    """Progress line for long full-size runs."""
     import time
     now = time.perf_counter()
     if not _T0[0]:
         _T0[0] = now
-    print(f"  [{now - _T0[0]:7.1f}s] {msg}", flush=True)
+    line = f"  [{now - _T0[0]:7.1f}s] {msg}"
+    if _CAP[0] is not None:
+        with _CAP[0].disabled():
+            print(line, flush=True)
+    else:
+        print(line, flush=True)
 
 
 @pytest.fixture(scope="module")
