@@ -5,10 +5,11 @@ workload: 65536 bf16 tokens x 4096 channels streamed into the activation covaria
 (SYRK on MFMA), Cholesky, whitening, fp64 Gram + eigensolve, back-map to rank 1024,
 per-component K-FAC scores (this workload has no gradients) and the global
 sort-and-truncate at the budget of rank 1024.  Inputs are resident in HBM before the
-timed region.  The K timed steps are independent layers issued round robin on --streams
-HIP streams (default 2, each with its own covariance buffer), so two layers are in flight
-at a time; `value` is K / the wall time of the region.  The same K steps one after another
-on one stream give `value_one_stream` (one layer's latency).  Prints one JSON line.
+timed region.  The K timed steps are independent layers spread over --streams HIP
+streams (default 3, each with its own covariance buffer and its own host thread that
+enqueues its steps), so three layers are in flight at a time; `value` is K / the wall
+time of the region.  The same K steps one after another on one stream give
+`value_one_stream` (one layer's latency).  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--streams S] [--no-cpu-baseline] [--no-secondary]
     python bench.py --only syrk|tridiag|fisher|ffn-decode [--copy-probe-mib M]
@@ -24,7 +25,9 @@ import argparse
 import json
 import os
 import sys
+import threading
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -82,8 +85,9 @@ def parse():
     p.add_argument("--tokens", type=int, default=65536)
     p.add_argument("--d", type=int, default=4096)
     p.add_argument("--rank", type=int, default=1024)
-    p.add_argument("--streams", type=int, default=2,
-                   help="HIP streams the timed steps are issued on, round robin (independent layers in flight)")
+    p.add_argument("--streams", type=int, default=3,
+                   help="HIP streams the timed steps run on, each fed by its own host thread (independent layers "
+                        "in flight)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true", help="skip the other workloads and passes")
     p.add_argument("--only", choices=["syrk", "tridiag", "fisher", "ffn-decode"], default=None,
@@ -281,9 +285,18 @@ def workloads(lrc, torch, dev, workers):
         main_st = torch.cuda.current_stream()
         for wst in workers:
             wst.wait_stream(main_st)
-        for mi, (m, wm) in enumerate(zip(cs.matrices, ws)):
+
+        def feed(mi):
+            m, wm = cs.matrices[mi], ws[mi]
+            torch.cuda.set_device(dev)
             with torch.cuda.stream(workers[mi % len(workers)]):
                 lrc.lrc_whiten_decompose(wm, 2048, covs[m.a_stream], cs.n_tokens, covs[m.b_stream], cs.n_tokens)
+
+        threads = [threading.Thread(target=feed, args=(mi,)) for mi in range(len(cs.matrices))]
+        for th in threads:
+            th.start()
+        for th in threads:
+            th.join()
         for wst in workers:
             main_st.wait_stream(wst)
 
@@ -314,7 +327,8 @@ def workloads(lrc, torch, dev, workers):
     # does not depend on the values).  A layer's covariances are made on the main stream
     # (two sets, alternating by layer, so that the next layer's accumulate while this
     # layer's decompositions run); its seven matrices are decomposed and scored on the
-    # worker streams, round robin; the allocation runs once all of them are done.
+    # worker streams, round robin, each worker stream enqueued by a host thread of its own;
+    # the allocation runs once all of them are done.
     cs = synth.workload_spec("decoder_stack_32_layers")
     n = cs.n_tokens
     st = {k: synth.stream(cs, k, device=dev) for k in cs.streams}
@@ -328,6 +342,7 @@ def workloads(lrc, torch, dev, workers):
     ns = len(workers)
     main_st = torch.cuda.current_stream()
     done = [[torch.cuda.Event() for _ in range(ns)] for _ in range(2)]   # per covariance set
+    pool = ThreadPoolExecutor(max_workers=ns)   # one host thread enqueues each worker stream
     torch.cuda.synchronize()
     progress("workload: decoder stack inputs ready")
     t0 = time.perf_counter()
@@ -343,15 +358,19 @@ def workloads(lrc, torch, dev, workers):
         ready.record(main_st)
         for wst in workers:
             wst.wait_event(ready)
-        for mi, (m, wm) in enumerate(zip(cs.matrices, ws)):
-            with torch.cuda.stream(workers[mi % ns]):
-                _, left, right, _ = lrc.lrc_whiten_decompose(wm, 4096, covs[m.a_stream], n)
-                j = (layer * 7 + mi) * 4096
-                lrc.lrc_score_components(left, right, A=st[m.a_stream], B=st[m.b_stream],
-                                         scores=scores[j:j + 4096])
-                del left, right
-        for i, wst in enumerate(workers):
-            done[layer % 2][i].record(wst)
+        def feed(i, layer=layer, covs=covs):
+            torch.cuda.set_device(dev)
+            with torch.cuda.stream(workers[i]):
+                for mi in range(i, len(cs.matrices), ns):
+                    m, wm = cs.matrices[mi], ws[mi]
+                    _, left, right, _ = lrc.lrc_whiten_decompose(wm, 4096, covs[m.a_stream], n)
+                    j = (layer * 7 + mi) * 4096
+                    lrc.lrc_score_components(left, right, A=st[m.a_stream], B=st[m.b_stream],
+                                             scores=scores[j:j + 4096])
+                    del left, right
+            done[layer % 2][i].record(workers[i])
+
+        list(pool.map(feed, range(ns)))
     for wst in workers:
         main_st.wait_stream(wst)
     lrc.lrc_allocate_ranks(scores, offs, cost, budget)
@@ -362,6 +381,7 @@ def workloads(lrc, torch, dev, workers):
                     "stream, every component decomposed and Fisher-scored, allocation of 917504 components at 60%",
         "streams": ns, "s": round(t, 2), "matrices_per_s": round(224 / t, 2)}
     progress(f"workload: decoder stack {t:.1f} s on {ns} stream(s)")
+    pool.shutdown()
     del st, ws, cov_sets, scores
 
     # per-head K/V: 65536 bf16 tokens, 64 head slices of 128 x 4096, K-FAC scores, 40% budget
@@ -645,13 +665,26 @@ def main():
         return lrc.lrc_allocate_ranks(scores, offs, cost, budget), info
 
     def run_steps(k_steps, n_streams):
-        """k_steps whole steps, step k on stream k mod n_streams with that stream's own
-        covariance buffer (the layers are independent); returns the last outputs of each."""
+        """k_steps whole steps: stream i (its own covariance buffer; the layers are
+        independent) runs steps i, i + n_streams, ..., enqueued by a host thread of its own
+        (an enqueue blocks while the stream's hardware queue is full, which would starve the
+        other streams if one thread fed them all); returns the last outputs of each."""
         last = {}
-        for k in range(k_steps):
-            i = k % n_streams
+
+        def feed(i):
+            torch.cuda.set_device(dev)
             with torch.cuda.stream(streams[i]):
-                last[i] = step(covs[i])
+                for _ in range(i, k_steps, n_streams):
+                    last[i] = step(covs[i])
+
+        if n_streams == 1:
+            feed(0)
+            return last
+        threads = [threading.Thread(target=feed, args=(i,)) for i in range(n_streams)]
+        for t in threads:
+            t.start()
+        for t in threads:
+            t.join()
         return last
 
     progress("inputs resident")
