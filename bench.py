@@ -6,9 +6,9 @@ workload: 65536 bf16 tokens x 4096 channels streamed into the activation covaria
 per-component K-FAC scores (this workload has no gradients) and the global
 sort-and-truncate at the budget of rank 1024.  Inputs are resident in HBM before the
 timed region.  The K timed steps are independent layers spread over --streams HIP
-streams (default 3, each with its own covariance buffer and its own host thread that
-enqueues its steps), so three layers are in flight at a time; `value` is K / the wall
-time of the region.  The same K steps one after another on one stream give
+streams (default 4 on the 8 hardware queues the bench asks HIP for; each stream has its
+own covariance buffer and its own host thread that enqueues its steps), so four layers
+are in flight at a time; `value` is K / the wall time of the region.  The same K steps one after another on one stream give
 `value_one_stream` (one layer's latency).  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--streams S] [--no-cpu-baseline] [--no-secondary]
@@ -31,6 +31,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+
 
 METRIC = "calib tokens/s into cov (4096-d) + whitened-SVD layers/s at 4096×4096, r=1024"
 HBM_PEAK_GBS = 8000.0
@@ -85,9 +86,11 @@ def parse():
     p.add_argument("--tokens", type=int, default=65536)
     p.add_argument("--d", type=int, default=4096)
     p.add_argument("--rank", type=int, default=1024)
-    p.add_argument("--streams", type=int, default=3,
+    p.add_argument("--streams", type=int, default=None,
                    help="HIP streams the timed steps run on, each fed by its own host thread (independent layers "
-                        "in flight)")
+                        "in flight); default: one less than the hardware queues, at most 4")
+    p.add_argument("--hw-queues", type=int, default=8,
+                   help="hardware queues HIP gives this process (GPU_MAX_HW_QUEUES, set before HIP starts)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true", help="skip the other workloads and passes")
     p.add_argument("--only", choices=["syrk", "tridiag", "fisher", "ffn-decode"], default=None,
@@ -634,6 +637,12 @@ def main():
         print("bench.py runs on one GPU only: this path has no multi-GPU mode (covariance sums would be "
               "all-reduced and matrices dealt out to GPUs; that layer is not built).", file=sys.stderr)
         sys.exit(2)
+    # HIP gives a process 4 hardware queues unless GPU_MAX_HW_QUEUES says otherwise (read
+    # when HIP initialises, so before torch touches the GPU).  The default stream takes one,
+    # and streams beyond the queues share one and serialise.  Measured with one host thread
+    # per stream: 3 streams on 4 queues 29.8 layers/s; on 8 queues 4 streams 32.6, 5 or 6
+    # streams 16-19 (more queues active than the command processor serves at once).
+    os.environ["GPU_MAX_HW_QUEUES"] = str(max(1, min(args.hw_queues, 32)))
     import torch
 
     import curvature_aware_rank_amd as lrc
@@ -646,6 +655,8 @@ def main():
     d, n, r = args.d, args.tokens, args.rank
     a = synth.activation_stream(n, d, 1.0, 31, outlier_frac=0.01, dtype=torch.bfloat16, device=dev)
     w = synth.weight(d, d, 35, device=dev)
+    if args.streams is None:
+        args.streams = min(4, max(1, int(os.environ["GPU_MAX_HW_QUEUES"]) - 1))
     ns = max(1, args.streams)
     streams = [torch.cuda.Stream() for _ in range(ns)]
     covs = [torch.empty(d, d, dtype=torch.float32, device=dev) for _ in range(ns)]
@@ -767,7 +778,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"attention projection W {d}x{d} fp32, {n} bf16 calibration tokens "
                                f"(power-law spectrum, 1% outlier channels x20), activation-only whitening, rank {r}",
-                   "tokens_per_layer": n, "d": d, "rank": r, "streams": ns},
+                   "tokens_per_layer": n, "d": d, "rank": r, "streams": ns,
+                   "hw_queues": int(os.environ["GPU_MAX_HW_QUEUES"])},
         "cov_tokens_per_s": round(n / (cov_ms * 1e-3), 1),
         "cov_ms": round(cov_ms, 4),
         "cov_mfma_bf16_frac": round(n * d * (d + 1.0) / (cov_ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
