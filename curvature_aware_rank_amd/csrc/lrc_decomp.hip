@@ -23,12 +23,16 @@ namespace {
 // rounds process every item of the batch at once (its fixed sweep count costs more
 // launches than one tridiagonalisation for a single Gram of any size).
 // LRC_EIGENSOLVER=jacobi|tridiag overrides the choice (tridiag only applies to batch 1).
+// Eigensolver routing: a single Gram, or a batch of large ones (one after another on the
+// stream, through one tridiagonal workspace), takes the tridiagonal route; a batch of small
+// Grams (per-head slices) takes the batched block-Jacobi solver, which handles every item
+// of the batch in each of its launches.  LRC_EIGENSOLVER=jacobi or =tridiag forces one.
+constexpr int64_t TRI_BATCH_MIN_K = 384;
 bool use_tridiag(int64_t k, int64_t batch) {
-  (void)k;
-  if (batch != 1) return false;
   const char* e = getenv("LRC_EIGENSOLVER");
   if (e && strcmp(e, "jacobi") == 0) return false;
-  return true;
+  if (e && strcmp(e, "tridiag") == 0) return true;
+  return batch == 1 || k >= TRI_BATCH_MIN_K;
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
@@ -179,9 +183,10 @@ extern "C" lrc_status lrc_whiten_decompose(const float* W, int64_t d_out, int64_
     LRC_LAUNCHED();
   }
   const int64_t ncols = std::max<int64_t>(rank, 1);
-  if (use_tridiag(k, batch))
-    LRC_TRY(tridiag_eig(st, w.gram, k, kp, ncols, sigma, w.qt, w.jac));
-  else
+  if (use_tridiag(k, batch)) {
+    for (int64_t b = 0; b < batch; ++b)
+      LRC_TRY(tridiag_eig(st, w.gram + b * kp * kp, k, kp, ncols, sigma + b * k, w.qt + b * ncols * k, w.jac));
+  } else
     LRC_TRY(jacobi_eig(st, w.gram, k, batch, ncols, sigma, w.qt, info, w.jac));
   if (rank == 0) return LRC_OK;
 

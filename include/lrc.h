@@ -126,8 +126,11 @@ size_t lrc_accumulate_cov_workspace(lrc_dtype dt, int64_t n_tokens, int64_t d, u
  * Outputs (packed, fp32): sigma[batch][k], left[batch][d_out][r], right[batch][r][d_in].
  * info (device int32[batch], written by the call): 0 ok; p in 1..d_in: pivot p of X not
  *    positive (LRC_ENOTPD condition; every slice reports it); d_in + p: pivot p of G not
- *    positive; -1: the Jacobi solver (batch > 1) still rotated after its last
- *    sweep (LRC_ENOCONV condition).  The outputs of a slice with nonzero info are
+ *    positive; -1: the Jacobi solver still rotated after its last sweep (LRC_ENOCONV
+ *    condition).  Solver: the tridiagonal one (Householder reduction, bisection, inverse
+ *    iteration) for a single slice and for batches with k >= 384, slice after slice; the
+ *    batched block-Jacobi one for batches of smaller slices; the environment variable
+ *    LRC_EIGENSOLVER=jacobi or =tridiag forces one.  The outputs of a slice with nonzero info are
  *    undefined.  These conditions are found on the device: the call itself returns LRC_OK
  *    once everything is enqueued (the solver's work is fixed in advance, so nothing is
  *    read back to the host).

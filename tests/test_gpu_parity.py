@@ -264,6 +264,29 @@ def test_decompose_batched_heads(lrc):
         _check_decomposition(case, rank)
 
 
+def test_decompose_batched_large_slices_take_tridiagonal_route(lrc, monkeypatch):
+    """A batch of slices with k >= 384 (e.g. projections sharing one input covariance) is
+    solved slice after slice by the tridiagonal solver: each slice gives the same bits as
+    decomposing it alone, and matches the oracle."""
+    monkeypatch.delenv("LRC_EIGENSOLVER", raising=False)
+    batch, d_out, d_in, n, rank = 3, 400, 520, 3000, 50
+    a = synth.activation_stream(n, d_in, 1.0, 61, dtype=torch.bfloat16)
+    ws = [synth.weight(d_out, d_in, 62 + b) for b in range(batch)]
+    xs = torch.zeros(d_in, d_in, device=dev())
+    lrc.lrc_accumulate_cov(a.to(dev()), xs)
+    w3 = torch.stack(ws).to(dev())
+    sig, left, right, info = lrc.lrc_whiten_decompose(w3, rank, xs, n)
+    assert torch.all(info == 0)
+    for b in range(batch):
+        s1, l1, r1, i1 = lrc.lrc_whiten_decompose(w3[b], rank, xs, n)
+        assert torch.equal(sig[b], s1) and torch.equal(left[b], l1) and torch.equal(right[b], r1)
+    an = to_np(a)
+    ref = oracle.whiten_decompose(to_np(ws[1]), oracle.covariance_sum(an), n, rank=rank)
+    case = dict(a=an, b=None, w=to_np(ws[1]), sig=to_np(sig[1]), left=to_np(left[1]), right=to_np(right[1]),
+                info=to_np(info[1:2]), ref=ref, n=n)
+    _check_decomposition(case, rank)
+
+
 def test_decompose_identity_covariances_is_plain_svd(lrc, solver):
     """X = G = I (identity sums with count 1): plain truncated SVD of W (Eckart-Young)."""
     w = synth.weight(96, 130, 3)
