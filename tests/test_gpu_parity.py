@@ -406,6 +406,58 @@ def test_decompositions_on_two_streams_match_sequential(lrc):
             assert torch.equal(got, want), f"call {k} (stream {k % 2}): {name} differs from the sequential result"
 
 
+def test_whole_path_on_three_streams_matches_sequential(lrc):
+    """Three independent pipelines (covariance, a tridiagonal and a Jacobi-batched
+    decomposition, Fisher scores, allocation) run at the same time on three streams, each
+    enqueued by its own host thread, give the same bits as one after another."""
+    import threading
+    d_out, d_in, n, r = 700, 900, 4000, 64
+
+    def inputs(seed):
+        a = synth.activation_stream(n, d_in, 1.0, seed, dtype=torch.bfloat16).to(dev())
+        b = synth.activation_stream(n, d_out, 1.3, seed + 1, dtype=torch.bfloat16).to(dev())
+        w = synth.weight(d_out, d_in, seed + 2).to(dev())
+        heads = synth.weight(8 * 32, d_in, seed + 3).to(dev()).view(8, 32, d_in)
+        return a, b, w, heads
+
+    def pipeline(a, b, w, heads):
+        xs = torch.zeros(d_in, d_in, device=dev())
+        ci = lrc.lrc_accumulate_cov(a, xs)
+        sig, left, right, info = lrc.lrc_whiten_decompose(w, r, xs, n)
+        hs, _, _, hinfo = lrc.lrc_whiten_decompose(heads, 8, xs, n)
+        sc, si = lrc.lrc_score_components(left, right, A=a, B=b)
+        pool = torch.cat([sc, hs.reshape(-1)])
+        offs = torch.tensor([0, r] + [r + 32 * (h + 1) for h in range(8)], dtype=torch.int64, device=dev())
+        cost = torch.tensor([d_out + d_in] + [32 + d_in] * 8, dtype=torch.int64, device=dev())
+        order, n_kept, ranks, mask, ainfo = lrc.lrc_allocate_ranks(pool, offs, cost, 40 * (d_out + d_in))
+        return [xs, sig, left, right, info, hs, hinfo, sc, order, n_kept, ranks, mask, ci, si, ainfo]
+
+    data = [inputs(100 + 10 * i) for i in range(3)]
+    torch.cuda.synchronize()
+    ref = []
+    for x in data:
+        ref.append([t.clone() for t in pipeline(*x)])
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    got = [None] * 3
+
+    def feed(i):
+        torch.cuda.set_device(dev())
+        with torch.cuda.stream(streams[i]):
+            got[i] = pipeline(*data[i])
+
+    threads = [threading.Thread(target=feed, args=(i,)) for i in range(3)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    for i in range(3):
+        assert int(ref[i][4][0]) == 0 and int(ref[i][14][0]) == 0
+        for k, (g, want) in enumerate(zip(got[i], ref[i])):
+            assert torch.equal(g, want), f"pipeline {i}: output {k} differs from the sequential run"
+
+
 def test_cov_and_scores_flag_nonfinite_inputs(lrc):
     """A NaN or Inf in the tokens reaches the covariance diagonal (a sum of squares) and
     every Fisher score (sums of non-negative terms): both calls set LRC_ENONFINITE in their
