@@ -23,8 +23,8 @@ namespace {
 // rounds process every item of the batch at once (its fixed sweep count costs more
 // launches than one tridiagonalisation for a single Gram of any size).
 // LRC_EIGENSOLVER=jacobi|tridiag overrides the choice (tridiag only applies to batch 1).
-// Eigensolver routing: a single Gram, or a batch of large ones (one after another on the
-// stream, through one tridiagonal workspace), takes the tridiagonal route; a batch of small
+// Eigensolver routing: a single Gram, or a batch of large ones (reduced together, then
+// solved slice after slice), takes the tridiagonal route; a batch of small
 // Grams (per-head slices) takes the batched block-Jacobi solver, which handles every item
 // of the batch in each of its launches.  LRC_EIGENSOLVER=jacobi or =tridiag forces one.
 constexpr int64_t TRI_BATCH_MIN_K = 384;
@@ -103,7 +103,7 @@ DWs carve_decomp(Carve& cv, int64_t d_out, int64_t d_in, int64_t batch, int64_t 
   w.u = cv.take<float>(size_t(k * std::max<int64_t>(rank, 1)));
   w.p = cv.take<float>(size_t(big * std::max<int64_t>(rank, 1)));
   // one eigensolver runs per call
-  w.jac = cv.take<char>(use_tridiag(k, batch) ? tridiag_workspace(k, std::max<int64_t>(rank, 1))
+  w.jac = cv.take<char>(use_tridiag(k, batch) ? tridiag_workspace(k, std::max<int64_t>(rank, 1), batch)
                                               : jacobi_workspace(k, batch));
   return w;
 }
@@ -183,10 +183,9 @@ extern "C" lrc_status lrc_whiten_decompose(const float* W, int64_t d_out, int64_
     LRC_LAUNCHED();
   }
   const int64_t ncols = std::max<int64_t>(rank, 1);
-  if (use_tridiag(k, batch)) {
-    for (int64_t b = 0; b < batch; ++b)
-      LRC_TRY(tridiag_eig(st, w.gram + b * kp * kp, k, kp, ncols, sigma + b * k, w.qt + b * ncols * k, w.jac));
-  } else
+  if (use_tridiag(k, batch))
+    LRC_TRY(tridiag_eig(st, w.gram, kp * kp, k, kp, ncols, batch, sigma, k, w.qt, ncols * k, w.jac));
+  else
     LRC_TRY(jacobi_eig(st, w.gram, k, batch, ncols, sigma, w.qt, info, w.jac));
   if (rank == 0) return LRC_OK;
 

@@ -29,14 +29,16 @@ size_t jacobi_workspace(int64_t k, int64_t batch);
 lrc_status jacobi_eig(hipStream_t st, double* A, int64_t k, int64_t batch, int64_t ncols, float* sigma,
                       float* Qt, int32_t* info, void* ws);
 
-// Symmetric eigendecomposition of one fp64 k x k Gram (lower triangle of A, leading
-// dimension lda; destroyed): Householder tridiagonalisation, Sturm multisection for all
-// eigenvalues, inverse iteration for the ncols largest, blocked back-transformation.
-// Same outputs as jacobi_eig (batch 1); enqueues a fixed amount of work and never waits.
-// A must be 16-byte aligned with an even lda, and lda > k when k is odd (LRC_EINVAL
-// otherwise).
-size_t tridiag_workspace(int64_t k, int64_t ncols);
-lrc_status tridiag_eig(hipStream_t st, double* A, int64_t k, int64_t lda, int64_t ncols, float* sigma, float* Qt,
-                       void* ws);
+// Symmetric eigendecompositions of a batch of fp64 k x k Grams (lower triangles of A,
+// slice b at A + b sA, leading dimension lda; destroyed): Householder tridiagonalisation
+// of all slices at once (every launch covers the batch), then per slice Sturm multisection
+// for all eigenvalues, inverse iteration for the ncols largest and the blocked
+// back-transformation.  Outputs as jacobi_eig: sigma slice b at sigma + b s_sigma, the
+// eigenvectors (ncols x k rows) at Qt + b s_qt.  Enqueues a fixed amount of work and never
+// waits.  A must be 16-byte aligned with an even lda and an even sA, and lda > k when k is
+// odd (LRC_EINVAL otherwise).
+size_t tridiag_workspace(int64_t k, int64_t ncols, int64_t batch);
+lrc_status tridiag_eig(hipStream_t st, double* A, int64_t sA, int64_t k, int64_t lda, int64_t ncols, int64_t batch,
+                       float* sigma, int64_t s_sigma, float* Qt, int64_t s_qt, void* ws);
 
 }  // namespace lrc

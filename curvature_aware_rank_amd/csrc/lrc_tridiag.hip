@@ -135,8 +135,17 @@ __device__ __forceinline__ double block_sum256(double v, double* red) {
 // and the column as a contiguous vector xv[r] (rows i .. n - 1) for the symv kernel
 __global__ __launch_bounds__(256) void tri_colstart_kernel(const double* __restrict__ A, int64_t lda, int n, int i,
                                                            double* __restrict__ npart, double* __restrict__ x0,
-                                                           double* __restrict__ d, double* __restrict__ xv) {
+                                                           double* __restrict__ d, double* __restrict__ xv, int64_t sA,
+                                                           int64_t wsi) {
   __shared__ double red[256];
+  {   // slice blockIdx.y of a batch: its matrix and its block of loop arrays
+    const int64_t it = blockIdx.y;
+    A += it * sA;
+    npart += it * wsi;
+    x0 += it * wsi;
+    d += it * wsi;
+    xv += it * wsi;
+  }
   const int tid = threadIdx.x;
   const int r = i + blockIdx.x * TS + tid;
   double sq = 0.0;
@@ -168,7 +177,17 @@ __global__ __launch_bounds__(256) void tri_symv_kernel(const double* __restrict_
                                                        int jj, const double* __restrict__ Wp,
                                                        const double* __restrict__ xv, double* __restrict__ P,
                                                        double* __restrict__ S, double* __restrict__ SV,
-                                                       double* __restrict__ SW) {
+                                                       double* __restrict__ SW, int64_t sA, int64_t wsi) {
+  {   // slice blockIdx.y of a batch
+    const int64_t it = blockIdx.y;
+    A += it * sA;
+    Wp += it * wsi;
+    xv += it * wsi;
+    P += it * wsi;
+    S += it * wsi;
+    SV += it * wsi;
+    SW += it * wsi;
+  }
   __shared__ double rsum[TS];
   __shared__ double cpart[16][TS + 1];
   __shared__ double red[8][2][NB];
@@ -338,7 +357,25 @@ __global__ __launch_bounds__(256) void tri_w_kernel(double* __restrict__ A, int6
                                                     const double* __restrict__ SV, const double* __restrict__ SW,
                                                     double* __restrict__ npart_next, double* __restrict__ x0_next,
                                                     double* __restrict__ d, double* __restrict__ e,
-                                                    double* __restrict__ tau_out, double* __restrict__ xv_next) {
+                                                    double* __restrict__ tau_out, double* __restrict__ xv_next,
+                                                    int64_t sA, int64_t wsi) {
+  {   // slice blockIdx.y of a batch
+    const int64_t it = blockIdx.y;
+    A += it * sA;
+    Wp += it * wsi;
+    npart += it * wsi;
+    x0p += it * wsi;
+    P += it * wsi;
+    S += it * wsi;
+    SV += it * wsi;
+    SW += it * wsi;
+    npart_next += it * wsi;
+    x0_next += it * wsi;
+    d += it * wsi;
+    e += it * wsi;
+    tau_out += it * wsi;
+    xv_next += it * wsi;
+  }
   constexpr int RPAIRS = WR / 2;       // row pairs of the symv partials
   constexpr int NCG = 256 / RPAIRS;    // column-block groups (16 or 32)
   constexpr int NPU = TS / NCG;        // column blocks per group below 64 blocks
@@ -581,7 +618,17 @@ constexpr int SYP = 64 + 2;   // LDS pitch (doubles) of an operand k row
 __global__ __launch_bounds__(256) void tri_syr2k_kernel(double* __restrict__ A, int64_t lda, int n, int i0, int pb,
                                                         int j1, const double* __restrict__ Wp,
                                                         double* __restrict__ npart, double* __restrict__ x0,
-                                                        double* __restrict__ d, double* __restrict__ xv) {
+                                                        double* __restrict__ d, double* __restrict__ xv, int64_t sA,
+                                                        int64_t wsi) {
+  {   // slice blockIdx.y of a batch
+    const int64_t it = blockIdx.y;
+    A += it * sA;
+    Wp += it * wsi;
+    npart += it * wsi;
+    x0 += it * wsi;
+    d += it * wsi;
+    xv += it * wsi;
+  }
   // the K = 64 product in two halves through one LDS pair (V_r W_c^T, then W_r V_c^T), so
   // that four workgroups fit on a CU
   __shared__ double opa[NB][SYP], opb[NB][SYP];
@@ -711,7 +758,14 @@ __device__ __forceinline__ double block_sum4w(double v, double* red) {
 
 __global__ __launch_bounds__(256) void tri_tail_kernel(double* __restrict__ A, int64_t lda, int n, int t0,
                                                        double* __restrict__ d, double* __restrict__ e,
-                                                       double* __restrict__ tau_out) {
+                                                       double* __restrict__ tau_out, int64_t sA, int64_t wsi) {
+  {   // slice blockIdx.y of a batch
+    const int64_t it = blockIdx.y;
+    A += it * sA;
+    d += it * wsi;
+    e += it * wsi;
+    tau_out += it * wsi;
+  }
   __shared__ double T[TT][TTP];
   __shared__ double vv[TT], yy[TT];
   __shared__ double red[4];
@@ -1768,29 +1822,47 @@ __global__ __launch_bounds__(256) void tri_out_kernel(const double* __restrict__
 }
 
 struct TWs {
-  double *P, *S, *SV, *SW, *npart, *x0, *xv, *d, *e, *tau, *Wp, *lam, *bounds, *U, *Z, *nrm, *scl, *Gp, *T, *Yp, *Yr, *Y2;
+  // the reduction loop's arrays: one block of `istride` doubles per slice of a batch,
+  // these pointers into slice 0's block
+  double *P, *S, *SV, *SW, *npart, *x0, *xv, *d, *e, *tau, *Wp;
+  int64_t istride;
+  // the later stages (one slice at a time)
+  double *lam, *bounds, *U, *Z, *nrm, *scl, *Gp, *T, *Yp, *Yr, *Y2;
   int *clen, *nbig, *big;
   uint8_t* piv;
 };
 
-TWs carve_tri(Carve& cv, int64_t n, int64_t ncols) {
+TWs carve_tri(Carve& cv, int64_t n, int64_t ncols, int64_t batch) {
   const int64_t nbt = cdiv(n, TS);
   const int64_t nref = std::max<int64_t>(n - 1, 0);
   const int64_t ngroups = std::max<int64_t>(cdiv(nref, BW), 1);
   const int64_t ngc = cdiv(n, G_CHUNK);
   const int64_t nbc = cdiv(n, BT_CHUNK);
   TWs w;
-  w.P = cv.take<double>(size_t(nbt * nbt * TS));
-  w.S = cv.take<double>(size_t(nbt * (nbt + 1) / 2));
-  w.SV = cv.take<double>(size_t(nbt * NB));
-  w.SW = cv.take<double>(size_t(nbt * NB));
-  w.npart = cv.take<double>(size_t(2 * NPB * nbt));   // two columns' partials, NPB per row block
-  w.x0 = cv.take<double>(2);
-  w.xv = cv.take<double>(size_t(2 * n));   // two columns as contiguous vectors
-  w.d = cv.take<double>(size_t(n));
-  w.e = cv.take<double>(size_t(n));
-  w.tau = cv.take<double>(size_t(n));
-  w.Wp = cv.take<double>(size_t(n * NB));
+  // per-slice loop block: every array starts on a 256-byte boundary
+  int64_t o = 0;
+  auto put = [&](int64_t len) {
+    const int64_t at = o;
+    o += (len + 31) / 32 * 32;
+    return at;
+  };
+  const int64_t oP = put(nbt * nbt * TS), oS = put(nbt * (nbt + 1) / 2), oSV = put(nbt * NB), oSW = put(nbt * NB);
+  const int64_t onp = put(2 * NPB * nbt);   // two columns' partials, NPB per row block
+  const int64_t ox0 = put(2), oxv = put(2 * n);   // two columns as contiguous vectors
+  const int64_t od = put(n), oe = put(n), otau = put(n), oWp = put(n * NB);
+  w.istride = o;
+  double* loop = cv.take<double>(size_t(std::max<int64_t>(batch, 1) * o));
+  w.P = loop + oP;
+  w.S = loop + oS;
+  w.SV = loop + oSV;
+  w.SW = loop + oSW;
+  w.npart = loop + onp;
+  w.x0 = loop + ox0;
+  w.xv = loop + oxv;
+  w.d = loop + od;
+  w.e = loop + oe;
+  w.tau = loop + otau;
+  w.Wp = loop + oWp;
   w.lam = cv.take<double>(size_t(n));
   w.bounds = cv.take<double>(4);
   w.U = cv.take<double>(size_t(4 * n * ncols));
@@ -1814,17 +1886,20 @@ __global__ void zero_int_kernel(int* p, int n) {
   if (i < n) p[i] = 0;
 }
 
-// Householder tridiagonalisation of the lower triangle of A (n x n, pitch lda) in place:
-// d, e, tau and the reflectors (below the subdiagonal) land in w and A.
-lrc_status tri_reduce(hipStream_t st, double* A, int n, int64_t lda, const TWs& w) {
+// Householder tridiagonalisation of the lower triangles of a batch of matrices (n x n,
+// pitch lda, slice b at A + b sA) in place: every launch covers all slices (grid y), so a
+// column's fixed launch and latency costs are paid once for the batch; d, e, tau and the
+// reflectors (below the subdiagonal) land in each slice's loop block and matrix.
+lrc_status tri_reduce(hipStream_t st, double* A, int64_t sA, int n, int64_t lda, int batch, const TWs& w) {
+  const int64_t wsi = w.istride;
   // panels up to t0 (a multiple of NB), then the last n - t0 <= TT columns in one workgroup
   const int t0 = n <= TT ? 0 : int(cdiv(n - TT, NB) * NB);
   for (int i0 = 0; i0 < t0; i0 += NB) {
     const int pb = std::min(NB, n - 1 - i0);
     if (i0 == 0) {   // later panels are started by the previous panel's rank-2 update
       const unsigned g = unsigned(cdiv(n - i0, TS));
-      tri_colstart_kernel<<<g, 256, 0, st>>>(A, lda, n, i0, w.npart + (i0 & 1) * NPB * cdiv(n, TS), w.x0 + (i0 & 1),
-                                             w.d, w.xv + (i0 & 1) * n);
+      tri_colstart_kernel<<<dim3(g, unsigned(batch)), 256, 0, st>>>(
+          A, lda, n, i0, w.npart + (i0 & 1) * NPB * cdiv(n, TS), w.x0 + (i0 & 1), w.d, w.xv + (i0 & 1) * n, sA, wsi);
       LRC_LAUNCHED();
     }
     for (int jj = 0; jj < pb; ++jj) {
@@ -1835,69 +1910,78 @@ lrc_status tri_reduce(hipStream_t st, double* A, int n, int64_t lda, const TWs& 
       double* np_cur = w.npart + par * NPB * cdiv(n, TS);
       double* np_next = w.npart + npar * NPB * cdiv(n, TS);
       {
-        ProfKernel pk("tri_symv_kernel", 2.0 * double(m) * double(m), 8.0 * double(m) * double(m + 1) / 2);
+        ProfKernel pk("tri_symv_kernel", 2.0 * double(m) * double(m) * batch, 8.0 * double(m) * double(m + 1) / 2 * batch);
         // 16-byte pairs need an even matrix pitch and base; tiles start at 16-column
         // boundaries (rows and columns before s0 are masked)
         const double* xv = w.xv + par * n;
         // the tiles, then (inside the panel) one workgroup per row block for V^T x, W^T x
-        const dim3 grid(unsigned(nbt * (nbt + 1) / 2 + (jj > 0 ? nbt : 0)));
+        const dim3 grid(unsigned(nbt * (nbt + 1) / 2 + (jj > 0 ? nbt : 0)), unsigned(batch));
         hipExtLaunchKernelGGL(tri_symv_kernel, grid, dim3(256), 0, st, pk.start, pk.stop, 0, (const double*)A, lda, n, i,
-                              i0, jj, (const double*)w.Wp, xv, w.P, w.S, w.SV, w.SW);
+                              i0, jj, (const double*)w.Wp, xv, w.P, w.S, w.SV, w.SW, sA, wsi);
         LRC_LAUNCHED();
       }
       {
         // bytes: the symv partials, the panel rows of V and W, column i (and i+1) read and
         // written, the new column of W
-        ProfKernel pk("tri_w_kernel", 4.0 * double(m) * (jj + 1),
-                      8.0 * (double(nbt) * nbt * TS + 2.0 * double(m) * jj + 5.0 * double(m)));
+        ProfKernel pk("tri_w_kernel", 4.0 * double(m) * (jj + 1) * batch,
+                      8.0 * (double(nbt) * nbt * TS + 2.0 * double(m) * jj + 5.0 * double(m)) * batch);
         const int do_next = jj + 1 < pb ? 1 : 0;
         // columns i, i + 1 form an aligned pair when i is even
-        hipExtLaunchKernelGGL(i % 2 == 0 ? tri_w_kernel<true> : tri_w_kernel<false>, dim3(unsigned(WPB * nbt)), dim3(256), 0,
-                              st, pk.start, pk.stop, 0, A, lda, n, i, i0, jj, do_next, w.Wp, (const double*)np_cur,
-                              (const double*)(w.x0 + par), (const double*)w.P, (const double*)w.S,
-                              (const double*)w.SV, (const double*)w.SW, np_next, w.x0 + npar, w.d, w.e, w.tau,
-                              w.xv + npar * n);
+        hipExtLaunchKernelGGL(i % 2 == 0 ? tri_w_kernel<true> : tri_w_kernel<false>,
+                              dim3(unsigned(WPB * nbt), unsigned(batch)), dim3(256), 0, st, pk.start, pk.stop, 0, A,
+                              lda, n, i, i0, jj, do_next, w.Wp, (const double*)np_cur, (const double*)(w.x0 + par),
+                              (const double*)w.P, (const double*)w.S, (const double*)w.SV, (const double*)w.SW,
+                              np_next, w.x0 + npar, w.d, w.e, w.tau, w.xv + npar * n, sA, wsi);
         LRC_LAUNCHED();
       }
     }
     const int j1 = i0 + pb;
     if (j1 < n) {
       const int nt = int(cdiv(n - j1, TS));
-      ProfScope scope("tri_syr2k_kernel", st, 2.0 * double(n - j1) * double(n - j1 + 1) * pb, 0.0);
+      ProfScope scope("tri_syr2k_kernel", st, 2.0 * double(n - j1) * double(n - j1 + 1) * pb * batch, 0.0);
       // j1 is the next panel's first column (i0 + NB): its start-of-panel state goes to the
       // buffers of its parity
-      tri_syr2k_kernel<<<unsigned(nt * (nt + 1) / 2), 256, 0, st>>>(
+      tri_syr2k_kernel<<<dim3(unsigned(nt * (nt + 1) / 2), unsigned(batch)), 256, 0, st>>>(
           A, lda, n, i0, pb, j1, w.Wp, w.npart + (j1 & 1) * NPB * cdiv(n, TS), w.x0 + (j1 & 1), w.d,
-          w.xv + (j1 & 1) * n);
+          w.xv + (j1 & 1) * n, sA, wsi);
       LRC_LAUNCHED();
     }
   }
-  tri_tail_kernel<<<1, 256, 0, st>>>(A, lda, n, t0, w.d, w.e, w.tau);
+  tri_tail_kernel<<<dim3(1, unsigned(batch)), 256, 0, st>>>(A, lda, n, t0, w.d, w.e, w.tau, sA, wsi);
   LRC_LAUNCHED();
   return LRC_OK;
 }
 
 }  // namespace
 
-size_t tridiag_workspace(int64_t k, int64_t ncols) {
+size_t tridiag_workspace(int64_t k, int64_t ncols, int64_t batch) {
   Carve cv(nullptr);
-  carve_tri(cv, k, std::max<int64_t>(ncols, 1));
+  carve_tri(cv, k, std::max<int64_t>(ncols, 1), std::max<int64_t>(batch, 1));
   return cv.bytes();
 }
 
-lrc_status tridiag_eig(hipStream_t st, double* A, int64_t k, int64_t lda, int64_t ncols_in, float* sigma, float* Qt,
-                       void* ws) {
-  // the symv kernel reads 16-byte column pairs: even pitch, 16-byte base, padding after
-  // an odd last column
-  if (lda % 2 != 0 || (k % 2 != 0 && lda < k + 1) || reinterpret_cast<uintptr_t>(A) % 16 != 0) return LRC_EINVAL;
-  const int n = int(k);
-  const int ncols = int(std::max<int64_t>(ncols_in, 1));
-  Carve cv(ws);
-  TWs w = carve_tri(cv, n, ncols);
+// slice b's view of the loop arrays, with the later-stage arrays shared by all slices
+static TWs tri_slice(const TWs& w0, int64_t b) {
+  TWs w = w0;
+  const int64_t o = b * w0.istride;
+  w.P += o;
+  w.S += o;
+  w.SV += o;
+  w.SW += o;
+  w.npart += o;
+  w.x0 += o;
+  w.xv += o;
+  w.d += o;
+  w.e += o;
+  w.tau += o;
+  w.Wp += o;
+  return w;
+}
 
-  // 1. tridiagonalisation
-  LRC_TRY(tri_reduce(st, A, n, lda, w));
-
+// eigenvalues, the wanted eigenvectors and their back-transformation for one reduced
+// slice: A holds its reflectors, w.d / w.e / w.tau its tridiagonal and scalars
+static lrc_status tri_solve_slice(hipStream_t st, double* A, int n, int64_t lda, int ncols, const TWs& w,
+                                  float* sigma, float* Qt) {
   // 2. eigenvalues
   tri_bounds_kernel<<<1, 256, 0, st>>>(w.d, w.e, n, w.bounds);
   LRC_LAUNCHED();
@@ -1978,6 +2062,27 @@ lrc_status tridiag_eig(hipStream_t st, double* A, int64_t k, int64_t lda, int64_
   }
   tri_out_kernel<<<unsigned(ncols), 256, 0, st>>>(w.Z, w.scl, n, ncols, Qt);
   LRC_LAUNCHED();
+  return LRC_OK;
+}
+
+lrc_status tridiag_eig(hipStream_t st, double* A, int64_t sA, int64_t k, int64_t lda, int64_t ncols_in, int64_t batch,
+                       float* sigma, int64_t s_sigma, float* Qt, int64_t s_qt, void* ws) {
+  // the symv kernel reads 16-byte column pairs: even pitch, 16-byte base (every slice),
+  // padding after an odd last column
+  if (lda % 2 != 0 || (k % 2 != 0 && lda < k + 1) || reinterpret_cast<uintptr_t>(A) % 16 != 0 ||
+      (batch > 1 && sA % 2 != 0) || batch < 1 || batch > 65535)
+    return LRC_EINVAL;
+  const int n = int(k);
+  const int ncols = int(std::max<int64_t>(ncols_in, 1));
+  Carve cv(ws);
+  const TWs w0 = carve_tri(cv, n, ncols, batch);
+
+  // 1. tridiagonalisation of every slice, one launch per step for the batch
+  LRC_TRY(tri_reduce(st, A, sA, n, lda, int(batch), w0));
+
+  // 2.-4. the later stages slice after slice, through one set of arrays
+  for (int64_t b = 0; b < batch; ++b)
+    LRC_TRY(tri_solve_slice(st, A + b * sA, n, lda, ncols, tri_slice(w0, b), sigma + b * s_sigma, Qt + b * s_qt));
   return LRC_OK;
 }
 

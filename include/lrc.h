@@ -128,7 +128,8 @@ size_t lrc_accumulate_cov_workspace(lrc_dtype dt, int64_t n_tokens, int64_t d, u
  *    positive (LRC_ENOTPD condition; every slice reports it); d_in + p: pivot p of G not
  *    positive; -1: the Jacobi solver still rotated after its last sweep (LRC_ENOCONV
  *    condition).  Solver: the tridiagonal one (Householder reduction, bisection, inverse
- *    iteration) for a single slice and for batches with k >= 384, slice after slice; the
+ *    iteration) for a single slice and for batches with k >= 384 (the slices' reductions
+ *    run together, one launch per step for the whole batch); the
  *    batched block-Jacobi one for batches of smaller slices; the environment variable
  *    LRC_EIGENSOLVER=jacobi or =tridiag forces one.  The outputs of a slice with nonzero info are
  *    undefined.  These conditions are found on the device: the call itself returns LRC_OK
