@@ -329,9 +329,9 @@ def workloads(lrc, torch, dev, workers):
     # layer's streams and weights are generated once and reused by every layer (the work
     # does not depend on the values).  A layer's covariances are made on the main stream
     # (two sets, alternating by layer, so that the next layer's accumulate while this
-    # layer's decompositions run); its seven matrices are decomposed and scored on the
-    # worker streams, round robin, each worker stream enqueued by a host thread of its own;
-    # the allocation runs once all of them are done.
+    # layer's decompositions run); its seven matrices, in four groups by input covariance,
+    # are decomposed and scored on the worker streams, round robin, each worker stream
+    # enqueued by a host thread of its own; the allocation runs once all of them are done.
     cs = synth.workload_spec("decoder_stack_32_layers")
     n = cs.n_tokens
     st = {k: synth.stream(cs, k, device=dev) for k in cs.streams}
@@ -342,6 +342,12 @@ def workloads(lrc, torch, dev, workers):
     offs = torch.arange(0, 224 * 4096 + 1, 4096, dtype=torch.int64, device=dev)
     cost = torch.tensor([m.d_out + m.d_in for m in cs.matrices] * 32, dtype=torch.int64, device=dev)
     budget = int(0.6 * 32 * sum(m.d_out * m.d_in for m in cs.matrices))
+    # matrices that share an input covariance (q, k, v; gate, up) are decomposed in one
+    # batched call: their Cholesky is formed once and their reductions share every launch
+    groups = []
+    for key in dict.fromkeys(m.a_stream for m in cs.matrices):
+        members = [mi for mi, m in enumerate(cs.matrices) if m.a_stream == key]
+        groups.append((members, torch.stack([ws[mi] for mi in members]) if len(members) > 1 else ws[members[0]]))
     ns = len(workers)
     main_st = torch.cuda.current_stream()
     done = [[torch.cuda.Event() for _ in range(ns)] for _ in range(2)]   # per covariance set
@@ -364,12 +370,15 @@ def workloads(lrc, torch, dev, workers):
         def feed(i, layer=layer, covs=covs):
             torch.cuda.set_device(dev)
             with torch.cuda.stream(workers[i]):
-                for mi in range(i, len(cs.matrices), ns):
-                    m, wm = cs.matrices[mi], ws[mi]
-                    _, left, right, _ = lrc.lrc_whiten_decompose(wm, 4096, covs[m.a_stream], n)
-                    j = (layer * 7 + mi) * 4096
-                    lrc.lrc_score_components(left, right, A=st[m.a_stream], B=st[m.b_stream],
-                                             scores=scores[j:j + 4096])
+                for gi in range(i, len(groups), ns):
+                    members, wg = groups[gi]
+                    m0 = cs.matrices[members[0]]
+                    _, left, right, _ = lrc.lrc_whiten_decompose(wg, 4096, covs[m0.a_stream], n)
+                    for bi, mi in enumerate(members):
+                        m = cs.matrices[mi]
+                        j = (layer * 7 + mi) * 4096
+                        lf, rt = (left[bi], right[bi]) if wg.dim() == 3 else (left, right)
+                        lrc.lrc_score_components(lf, rt, A=st[m.a_stream], B=st[m.b_stream], scores=scores[j:j + 4096])
                     del left, right
             done[layer % 2][i].record(workers[i])
 
@@ -382,10 +391,10 @@ def workloads(lrc, torch, dev, workers):
     out["decoder_stack_32_layers"] = {
         "workload": "32 layers x (q,k,v,o 4096x4096, gate/up 11008x4096, down 4096x11008), 32768 bf16 tokens per "
                     "stream, every component decomposed and Fisher-scored, allocation of 917504 components at 60%",
-        "streams": ns, "s": round(t, 2), "matrices_per_s": round(224 / t, 2)}
+        "streams": ns, "calls_per_layer": len(groups), "s": round(t, 2), "matrices_per_s": round(224 / t, 2)}
     progress(f"workload: decoder stack {t:.1f} s on {ns} stream(s)")
     pool.shutdown()
-    del st, ws, cov_sets, scores
+    del st, ws, groups, cov_sets, scores
 
     # per-head K/V: 65536 bf16 tokens, 64 head slices of 128 x 4096, K-FAC scores, 40% budget
     cs = synth.workload_spec("kv_heads_64x128x4096")
