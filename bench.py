@@ -25,7 +25,6 @@ import argparse
 import json
 import os
 import sys
-import threading
 import time
 from concurrent.futures import ThreadPoolExecutor
 
@@ -295,11 +294,8 @@ def workloads(lrc, torch, dev, workers):
             with torch.cuda.stream(workers[mi % len(workers)]):
                 lrc.lrc_whiten_decompose(wm, 2048, covs[m.a_stream], cs.n_tokens, covs[m.b_stream], cs.n_tokens)
 
-        threads = [threading.Thread(target=feed, args=(mi,)) for mi in range(len(cs.matrices))]
-        for th in threads:
-            th.start()
-        for th in threads:
-            th.join()
+        with ThreadPoolExecutor(max_workers=len(cs.matrices)) as ex:
+            list(ex.map(feed, range(len(cs.matrices))))   # re-raises a failure of any thread
         for wst in workers:
             main_st.wait_stream(wst)
 
@@ -700,11 +696,8 @@ def main():
         if n_streams == 1:
             feed(0)
             return last
-        threads = [threading.Thread(target=feed, args=(i,)) for i in range(n_streams)]
-        for t in threads:
-            t.start()
-        for t in threads:
-            t.join()
+        with ThreadPoolExecutor(max_workers=n_streams) as ex:
+            list(ex.map(feed, range(n_streams)))   # re-raises a failure of any thread
         return last
 
     progress("inputs resident")
