@@ -32,8 +32,10 @@ namespace lrc {
 namespace {
 
 constexpr int RT = 256;        // threads per sort workgroup (4 waves)
-constexpr int RR = 16;         // items per thread (each wave: RR rounds of 64 consecutive items)
-constexpr int RTILE = RT * RR; // items per workgroup tile
+// items per thread (each wave: RR rounds of 64 consecutive items) and per tile: 16 (4096-item
+// tiles) for large pools, 4 (1024-item tiles) when 4096-item tiles would give fewer than two
+// workgroups per compute unit -- more, shorter workgroups at small sizes
+constexpr int RR_BIG = 16, RR_SMALL = 4;
 constexpr int MAX_SORT_BLOCKS = 1024;   // sort workgroups per pass; each takes a run of tiles
 constexpr int SC = 8;          // items per thread in the int64 scan
 constexpr int STILE = 256 * SC;
@@ -175,8 +177,10 @@ __device__ __forceinline__ uint32_t block_exscan256(uint32_t v, uint32_t* wsum) 
 // Digit counts of each sort block's run of tiles, digit-major: cnt[d * nblk + block].
 // Block b takes tiles [b * tpb, min((b + 1) * tpb, ntiles)); wave w of a tile owns its
 // contiguous items [w * RR * 64, (w + 1) * RR * 64).
+template <int RR>
 __global__ __launch_bounds__(RT) void radix_hist_kernel(const uint64_t* __restrict__ keys, int M, int shift,
                                                         int tpb, uint32_t* __restrict__ cnt, int nblk) {
+  constexpr int RTILE = RT * RR;
   __shared__ uint32_t h[256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   h[tid] = 0;
@@ -238,11 +242,13 @@ __global__ __launch_bounds__(256) void radix_rowscan_kernel(uint32_t* __restrict
 // input position) are computed per wave, the tile is staged in LDS in digit order and
 // written out in that order, so the items of one digit leave as contiguous runs.  The
 // next tile's keys are loaded while the current one is ranked and written.
+template <int RR>
 __global__ __launch_bounds__(RT) void radix_scatter_kernel(const uint64_t* __restrict__ kin,
                                                            const uint32_t* __restrict__ vin,
                                                            uint64_t* __restrict__ kout, uint32_t* __restrict__ vout,
                                                            int M, int shift, int tpb, const uint32_t* __restrict__ cnt,
                                                            const uint32_t* __restrict__ rowtot, int nblk) {
+  constexpr int RTILE = RT * RR;
   __shared__ uint64_t skey[RTILE];
   __shared__ uint32_t sval[RTILE];
   __shared__ uint32_t wc[4][256];
@@ -513,13 +519,15 @@ struct AWs {
   uint64_t* cutkey;
 };
 
-// sort geometry: tiles of RTILE items, runs of tpb tiles per sort workgroup
+// sort geometry: tiles of RT rr items, runs of tpb tiles per sort workgroup
 struct SortGeom {
   int64_t ntiles, tpb, nblk;
+  int rr;
 };
 SortGeom sort_geom(int64_t M) {
   SortGeom g;
-  g.ntiles = std::max<int64_t>(1, cdiv(M, RTILE));
+  g.rr = cdiv(M, int64_t(RT) * RR_BIG) < 512 ? RR_SMALL : RR_BIG;
+  g.ntiles = std::max<int64_t>(1, cdiv(M, int64_t(RT) * g.rr));
   g.tpb = cdiv(g.ntiles, MAX_SORT_BLOCKS);
   g.nblk = cdiv(g.ntiles, g.tpb);
   return g;
@@ -596,12 +604,19 @@ lrc_status allocate_impl(const float* scores, const int64_t* offsets, const int6
       const int shift = pass * 8;
       // the last pass writes the sorted ids straight into the order output
       uint32_t* vdst = pass == 7 ? reinterpret_cast<uint32_t*>(order) : vout;
-      radix_hist_kernel<<<unsigned(nblk), RT, 0, st>>>(kin, M, shift, tpb, w.hist, nblk);
+      if (sg.rr == RR_SMALL)
+        radix_hist_kernel<RR_SMALL><<<unsigned(nblk), RT, 0, st>>>(kin, M, shift, tpb, w.hist, nblk);
+      else
+        radix_hist_kernel<RR_BIG><<<unsigned(nblk), RT, 0, st>>>(kin, M, shift, tpb, w.hist, nblk);
       LRC_LAUNCHED();
       radix_rowscan_kernel<<<256, 256, 0, st>>>(w.hist, nblk, w.rowtot);
       LRC_LAUNCHED();
-      radix_scatter_kernel<<<unsigned(nblk), RT, 0, st>>>(kin, vin, kout, vdst, M, shift, tpb, w.hist,
-                                                          w.rowtot, nblk);
+      if (sg.rr == RR_SMALL)
+        radix_scatter_kernel<RR_SMALL><<<unsigned(nblk), RT, 0, st>>>(kin, vin, kout, vdst, M, shift, tpb, w.hist,
+                                                                      w.rowtot, nblk);
+      else
+        radix_scatter_kernel<RR_BIG><<<unsigned(nblk), RT, 0, st>>>(kin, vin, kout, vdst, M, shift, tpb, w.hist,
+                                                                    w.rowtot, nblk);
       LRC_LAUNCHED();
       std::swap(kin, kout);
       std::swap(vin, vout);
