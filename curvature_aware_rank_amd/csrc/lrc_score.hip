@@ -154,6 +154,9 @@ __global__ __launch_bounds__(256) void split_transpose_kernel(const float* __res
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// source of the zero pieces that pad the Fisher kernel's staged tiles
+__device__ __attribute__((aligned(16))) uint32_t fisher_zero16[4] = {0u, 0u, 0u, 0u};  // never written
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 constexpr int FW = 8;                    // waves per workgroup: 4 token groups of 64 x 2 component halves
@@ -168,8 +171,8 @@ constexpr int FS_C = 8;       // component tiles per XCD super-tile
 // hi and lo) go through LDS, two stages of one 64-wide reduction chunk each: the global
 // loads are whole 128-byte row pieces (8 lanes per row), so every cache line a load
 // instruction touches is used in full; rows are padded to FP so that the fragment reads
-// (one row per lane) are conflict-free.  The next chunk's loads are in flight in registers
-// while the current one is computed.
+// (one row per lane) are conflict-free.  The loads of the next two chunks are in flight in
+// registers while the current one is computed.
 __device__ __forceinline__ void fisher_phase(const uint16_t* __restrict__ X, int d, int64_t n, int64_t t0, int tg,
                                              int ch, const uint16_t* __restrict__ Fh,
                                              const uint16_t* __restrict__ Fl, int k, int c0, uint16_t* fs,
@@ -181,35 +184,37 @@ __device__ __forceinline__ void fisher_phase(const uint16_t* __restrict__ X, int
   constexpr int FQ = FC * 8 / (64 * FW);   // factor groups per thread per part
   constexpr int XQ = FT * 8 / (64 * FW);   // activation groups per thread
   const int grow = tid >> 3, gcol = (tid & 7) * 8;
+  // pieces outside the matrices (columns past d, factor rows past k, tokens past n) are
+  // read from a 16-byte zero constant: the choice is made on the address, so a store to
+  // LDS takes the loaded registers as they are and waits only for its own loads
+  const uint16_t* zero = reinterpret_cast<const uint16_t*>(fisher_zero16);
   auto load_f = [&](u32x4 (&g)[2][FQ], u32x4 (&ga)[XQ], int kc) {
+    const bool colok = kc + gcol < d;
     const int col = min(kc + gcol, d - 8);
 #pragma unroll
     for (int q = 0; q < FQ; ++q) {
-      const int64_t row = min(c0 + grow + 8 * FW * q, k - 1);
-      g[0][q] = *reinterpret_cast<const u32x4*>(Fh + row * d + col);
-      g[1][q] = *reinterpret_cast<const u32x4*>(Fl + row * d + col);
+      const int row = c0 + grow + 8 * FW * q;
+      const bool ok = colok && row < k;
+      const int64_t off = int64_t(min(row, k - 1)) * d + col;
+      g[0][q] = *reinterpret_cast<const u32x4*>(ok ? Fh + off : zero);
+      g[1][q] = *reinterpret_cast<const u32x4*>(ok ? Fl + off : zero);
     }
 #pragma unroll
     for (int q = 0; q < XQ; ++q) {
-      const int64_t row = min<int64_t>(t0 + grow + 8 * FW * q, n - 1);
-      ga[q] = *reinterpret_cast<const u32x4*>(X + row * d + col);
+      const int64_t row = t0 + grow + 8 * FW * q;
+      const bool ok = colok && row < n;
+      ga[q] = *reinterpret_cast<const u32x4*>(ok ? X + min<int64_t>(row, n - 1) * d + col : zero);
     }
   };
-  auto store_f = [&](const u32x4 (&g)[2][FQ], const u32x4 (&ga)[XQ], int buf, int kc) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    const bool colok = kc + gcol < d;
+  auto store_f = [&](const u32x4 (&g)[2][FQ], const u32x4 (&ga)[XQ], int buf) {
 #pragma unroll
-    for (int q = 0; q < FQ; ++q) {
-      const bool ok = colok && c0 + grow + 8 * FW * q < k;
+    for (int q = 0; q < FQ; ++q)
 #pragma unroll
       for (int hl = 0; hl < 2; ++hl)
-        *reinterpret_cast<u32x4*>(fs + (buf * 2 + hl) * (FC * FP) + (grow + 8 * FW * q) * FP + gcol) =
-            ok ? g[hl][q] : z;
-    }
-    // tokens past the last are clamped copies of it; their products are masked at the end
+        *reinterpret_cast<u32x4*>(fs + (buf * 2 + hl) * (FC * FP) + (grow + 8 * FW * q) * FP + gcol) = g[hl][q];
 #pragma unroll
     for (int q = 0; q < XQ; ++q)
-      *reinterpret_cast<u32x4*>(xs + buf * (FT * FP) + (grow + 8 * FW * q) * FP + gcol) = colok ? ga[q] : z;
+      *reinterpret_cast<u32x4*>(xs + buf * (FT * FP) + (grow + 8 * FW * q) * FP + gcol) = ga[q];
   };
   // the four (or eight) hi products of a step, then its lo products: an MFMA never waits
   // for the result of the one issued just before it
@@ -237,16 +242,28 @@ __device__ __forceinline__ void fisher_phase(const uint16_t* __restrict__ X, int
                                                                  acc[f][nf], 0, 0, 0);
     }
   };
-  u32x4 g[2][FQ], ga[XQ];
-  load_f(g, ga, 0);
-  store_f(g, ga, 0, 0);
-  if (nch > 1) load_f(g, ga, FK);
+  // two register sets: the loads of chunk c + 3 are issued after chunk c is computed and
+  // stored to LDS after chunk c + 2 is computed, so two compute phases cover their latency.
+  // The loop body has no branch: the chunk count is rounded up to even (a chunk past the
+  // end loads zeros, whose products add exactly 0), and loads run past the last chunk
+  // (reading the zero constant).  So on every path
+  // the loads a store waits for are followed by exactly one newer set, which the wait
+  // before the store leaves in flight.
+  const int nch2 = (nch + 1) & ~1;
+  u32x4 g0[2][FQ], ga0[XQ], g1[2][FQ], ga1[XQ];
+  load_f(g0, ga0, 0);
+  load_f(g1, ga1, FK);
+  store_f(g0, ga0, 0);
+  load_f(g0, ga0, 2 * FK);
   __syncthreads();
-  for (int c = 0; c < nch; ++c) {
-    const int buf = c & 1;
-    compute(buf);
-    if (c + 1 < nch) store_f(g, ga, buf ^ 1, (c + 1) * FK);
-    if (c + 2 < nch) load_f(g, ga, (c + 2) * FK);
+  for (int c = 0; c < nch2; c += 2) {
+    compute(0);
+    store_f(g1, ga1, 1);
+    load_f(g1, ga1, (c + 3) * FK);
+    __syncthreads();
+    compute(1);
+    store_f(g0, ga0, 0);
+    load_f(g0, ga0, (c + 4) * FK);
     __syncthreads();
   }
 }
@@ -308,7 +325,7 @@ __global__ __launch_bounds__(64 * FW, 1) void fisher_mfma_kernel(const uint16_t*
       for (int e = 0; e < 16; ++e) {
         const int64_t t = tw + f * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
         const float pv = accp[f][nf][e], qv = accq[f][nf][e];
-        // rows past the last token hold a copy of it (clamped loads): they add exactly 0
+        // rows past the last token were staged as zeros; the mask keeps them out in any case
         sum = fmaf(t < n ? pv * pv : 0.f, qv * qv, sum);
       }
     sum += __shfl_xor(sum, 32);

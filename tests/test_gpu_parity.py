@@ -287,6 +287,30 @@ def test_decompose_batched_large_slices_take_tridiagonal_route(lrc, monkeypatch)
     _check_decomposition(case, rank)
 
 
+def test_decompose_batched_ragged_two_sided_large_grid(lrc):
+    """40 two-sided slices of 301 x 517 share both covariances: the whitening products
+    (W Lx, then Lg^T (W Lx)) run as batched launches with sizes that are not multiples of 4
+    (scalar loads, ragged tile edges in every slice).  Slices checked against the oracle:
+    the first and the last."""
+    batch, d_out, d_in, n, rank = 40, 301, 517, 2000, 40
+    a = synth.activation_stream(n, d_in, 1.2, 71, dtype=torch.float32)
+    b = synth.activation_stream(n, d_out, 1.2, 72, dtype=torch.float32)
+    ws = [synth.weight(d_out, d_in, 73 + i) for i in range(batch)]
+    xs = torch.zeros(d_in, d_in, device=dev())
+    gs = torch.zeros(d_out, d_out, device=dev())
+    lrc.lrc_accumulate_cov(a.to(dev()), xs)
+    lrc.lrc_accumulate_cov(b.to(dev()), gs)
+    sig, left, right, info = lrc.lrc_whiten_decompose(torch.stack(ws).to(dev()), rank, xs, n, gs, n)
+    assert torch.all(info == 0)
+    an, bn = to_np(a), to_np(b)
+    xsum, gsum = oracle.covariance_sum(an), oracle.covariance_sum(bn)
+    for i in (0, batch - 1):
+        ref = oracle.whiten_decompose(to_np(ws[i]), xsum, n, gsum, n, rank=rank)
+        case = dict(a=an, b=bn, w=to_np(ws[i]), sig=to_np(sig[i]), left=to_np(left[i]), right=to_np(right[i]),
+                    info=to_np(info[i:i + 1]), ref=ref, n=n)
+        _check_decomposition(case, rank)
+
+
 def test_decompose_identity_covariances_is_plain_svd(lrc, solver):
     """X = G = I (identity sums with count 1): plain truncated SVD of W (Eckart-Young)."""
     w = synth.weight(96, 130, 3)
