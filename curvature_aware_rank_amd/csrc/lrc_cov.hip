@@ -548,6 +548,71 @@ __global__ __launch_bounds__(256) void qaw_prepass_kernel(const T* __restrict__ 
   }
 }
 
+// The same pre-pass for bf16 rows of at most QAW_VROW elements (a multiple of 8, rows
+// 16-byte aligned): each thread holds its 16-byte pieces of the row in registers, so the
+// row is read from memory once, and the three outputs are written as 16-byte pieces.  The
+// arithmetic per element is that of qaw_prepass_kernel, so the outputs are the same bits.
+constexpr int QAW_VPT = 8;                       // 16-byte pieces per thread
+constexpr int QAW_VROW = 256 * 8 * QAW_VPT;      // 16384 elements
+typedef uint32_t qaw_u32x4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void qaw_prepass_vec_kernel(const uint16_t* __restrict__ A, int64_t lda, int d,
+                                                              uint16_t* __restrict__ Q, uint16_t* __restrict__ H,
+                                                              uint16_t* __restrict__ L, int64_t ldq) {
+  __shared__ float red[4];
+  const int64_t t = blockIdx.x;
+  const qaw_u32x4* row = reinterpret_cast<const qaw_u32x4*>(A + t * lda);
+  const int nv = d / 8;
+  qaw_u32x4 v[QAW_VPT];
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < QAW_VPT; ++i) {
+    const int j = threadIdx.x + 256 * i;
+    v[i] = j < nv ? row[j] : qaw_u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      m = fmaxf(m, fabsf(__uint_as_float(v[i][e] << 16)));
+      m = fmaxf(m, fabsf(__uint_as_float(v[i][e] & 0xffff0000u)));
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = __fdiv_rn(m, 127.0f);
+  const float s2 = s * s;
+  qaw_u32x4* q4 = reinterpret_cast<qaw_u32x4*>(Q + t * ldq);
+  qaw_u32x4* h4 = reinterpret_cast<qaw_u32x4*>(H + t * ldq);
+  qaw_u32x4* l4 = reinterpret_cast<qaw_u32x4*>(L + t * ldq);
+#pragma unroll
+  for (int i = 0; i < QAW_VPT; ++i) {
+    const int j = threadIdx.x + 256 * i;
+    if (j >= nv) continue;
+    qaw_u32x4 qo, ho, lo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint32_t qw = 0u, hw = 0u, lw = 0u;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const float a = __uint_as_float(half ? (v[i][e] & 0xffff0000u) : (v[i][e] << 16));
+        float q = 0.f;
+        if (s > 0.f) q = fminf(fmaxf(rintf(__fdiv_rn(a, s)), -127.f), 127.f);
+        const float w = s2 * q;
+        const uint16_t hb = f32_to_bf16_bits(w);
+        const uint16_t lb = f32_to_bf16_bits(w - bf16_bits_to_f32(hb));
+        qw |= uint32_t(f32_to_bf16_bits(q)) << (16 * half);
+        hw |= uint32_t(hb) << (16 * half);
+        lw |= uint32_t(lb) << (16 * half);
+      }
+      qo[e] = qw;
+      ho[e] = hw;
+      lo[e] = lw;
+    }
+    q4[j] = qo;
+    h4[j] = ho;
+    l4[j] = lo;
+  }
+}
+
 // ---- fp32 input: plain LDS-tiled SYRK, 64 x 64 lower tiles, no split (deterministic)
 __global__ __launch_bounds__(256) void syrk_f32_kernel(const float* __restrict__ A, int64_t lda, int64_t n,
                                                        int d, float* __restrict__ C, int64_t ldc,
@@ -736,11 +801,18 @@ extern "C" lrc_status lrc_accumulate_cov(const void* A, lrc_dtype dt, int64_t n_
     const uint16_t* a = static_cast<const uint16_t*>(A);
     return launch_syrk_bf16(st, a, a, lda, n_tokens, d, C, ldc, partial, cap, info);
   }
+  // 16-byte pieces: rows of a multiple of 8 elements, every buffer 16-byte aligned
+  const bool qaw_vec = dt == LRC_BF16 && d % 8 == 0 && d <= QAW_VROW && lda % 8 == 0 &&
+                       reinterpret_cast<uintptr_t>(A) % 16 == 0 && reinterpret_cast<uintptr_t>(q) % 16 == 0 &&
+                       reinterpret_cast<uintptr_t>(h) % 16 == 0 && reinterpret_cast<uintptr_t>(l) % 16 == 0;
   for (int64_t t0 = 0; t0 < n_tokens; t0 += chunk) {
     const int64_t nb = std::min(chunk, n_tokens - t0);
     {
     ProfScope scope("qaw_prepass_kernel", st, 0.0, double(nb) * double(d) * ((dt == LRC_BF16 ? 2 : 4) + 6));
-    if (dt == LRC_BF16)
+    if (qaw_vec)
+      qaw_prepass_vec_kernel<<<unsigned(nb), 256, 0, st>>>(static_cast<const uint16_t*>(A) + t0 * lda, lda, int(d), q,
+                                                           h, l, d);
+    else if (dt == LRC_BF16)
       qaw_prepass_kernel<uint16_t><<<unsigned(nb), 256, 0, st>>>(static_cast<const uint16_t*>(A) + t0 * lda, lda,
                                                                  int(d), q, h, l, d);
     else
