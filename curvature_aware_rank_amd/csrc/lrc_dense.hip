@@ -295,14 +295,27 @@ constexpr int NB = 64;  // Cholesky / triangular-solve block size
 // LDS queue serves after the store), and each lane updates its own row.
 __global__ __launch_bounds__(64) void potf2_kernel(float* __restrict__ L, int64_t ldl, int64_t n, int64_t k0,
                                                    int* __restrict__ info) {
-  __shared__ float colv[NB];
+  __shared__ __align__(16) float colv[NB];
   const int lane = threadIdx.x;
   const int b = int(min<int64_t>(NB, n - k0));
   if (*info != 0) return;
   const int rr = min(lane, b - 1);
   float a[NB];
+  // a full block at a 16-byte aligned position moves in 16-byte pieces
+  const bool vec = b == NB && ldl % 4 == 0 && k0 % 4 == 0 && (reinterpret_cast<uintptr_t>(L) & 15) == 0;
+  if (vec) {
 #pragma unroll
-  for (int c = 0; c < NB; ++c) a[c] = L[(k0 + rr) * ldl + k0 + min(c, b - 1)];
+    for (int c = 0; c < NB; c += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(L + (k0 + lane) * ldl + k0 + c);
+      a[c] = v.x;
+      a[c + 1] = v.y;
+      a[c + 2] = v.z;
+      a[c + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < NB; ++c) a[c] = L[(k0 + rr) * ldl + k0 + min(c, b - 1)];
+  }
 #pragma unroll
   for (int c = 0; c < NB; ++c) a[c] = (c <= lane && lane < b && c < b) ? a[c] : 0.f;
   int fail = 0;   // uniform: the pivot is read from lane j into a scalar register
@@ -323,9 +336,20 @@ __global__ __launch_bounds__(64) void potf2_kernel(float* __restrict__ L, int64_
         colv[lane] = lij;
         // every lane updates its whole row: entries above the diagonal (c > lane) are never
         // read as pivots or multipliers (those come from lanes c > j, column j) and stay
-        // finite; the store writes zeros there
+        // finite; the store writes zeros there.  The column is read back four entries per
+        // LDS read, all reads issued before the first update (the reads of one wave follow
+        // its write in order).
+        float4 cv[NB / 4];
 #pragma unroll
-        for (int c = j + 1; c < NB; ++c) a[c] = fmaf(-lij, colv[c], a[c]);
+        for (int g = (j + 1) / 4; g < NB / 4; ++g) cv[g] = *reinterpret_cast<const float4*>(&colv[4 * g]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int g = (j + 1) / 4; g < NB / 4; ++g) {
+          if (4 * g > j) a[4 * g] = fmaf(-lij, cv[g].x, a[4 * g]);
+          if (4 * g + 1 > j) a[4 * g + 1] = fmaf(-lij, cv[g].y, a[4 * g + 1]);
+          if (4 * g + 2 > j) a[4 * g + 2] = fmaf(-lij, cv[g].z, a[4 * g + 2]);
+          a[4 * g + 3] = fmaf(-lij, cv[g].w, a[4 * g + 3]);
+        }
       }
     }
   }
@@ -333,7 +357,13 @@ __global__ __launch_bounds__(64) void potf2_kernel(float* __restrict__ L, int64_
     if (lane == 0) *info = int(k0 + fail);
     return;
   }
-  if (lane < b) {
+  if (vec) {
+#pragma unroll
+    for (int c = 0; c < NB; c += 4)
+      *reinterpret_cast<float4*>(L + (k0 + lane) * ldl + k0 + c) =
+          float4{c <= lane ? a[c] : 0.f, c + 1 <= lane ? a[c + 1] : 0.f, c + 2 <= lane ? a[c + 2] : 0.f,
+                 c + 3 <= lane ? a[c + 3] : 0.f};
+  } else if (lane < b) {
 #pragma unroll
     for (int c = 0; c < NB; ++c)
       if (c < b) L[(k0 + lane) * ldl + k0 + c] = c <= lane ? a[c] : 0.f;
@@ -491,12 +521,20 @@ lrc_status cholesky_f32(hipStream_t st, const float* S, int64_t lds_, int64_t n,
   sym_scale_kernel<<<g, 256, 0, st>>>(S, lds_, n, 1.0 / double(cnt), damping, L, n);
   LRC_LAUNCHED();
   for (int64_t k0 = 0; k0 < n; k0 += NB) {
-    potf2_kernel<<<1, 64, 0, st>>>(L, n, n, k0, info);
-    LRC_LAUNCHED();
+    {
+      // work: the block's NB^3 / 3 multiply-adds; bytes: the block read and written
+      const double nb = double(std::min<int64_t>(NB, n - k0));
+      ProfScope scope("potf2_kernel", st, nb * nb * nb / 3.0, 8.0 * nb * nb);
+      potf2_kernel<<<1, 64, 0, st>>>(L, n, n, k0, info);
+      LRC_LAUNCHED();
+    }
     const int64_t below = n - k0 - NB;
     if (below <= 0) break;
-    trsm_panel_kernel<<<unsigned(cdiv(below, 64)), 64, 0, st>>>(L, n, n, k0, info);
-    LRC_LAUNCHED();
+    {
+      ProfScope scope("trsm_panel_kernel", st, double(below) * NB * NB, 8.0 * double(below) * NB + 4.0 * NB * NB);
+      trsm_panel_kernel<<<unsigned(cdiv(below, 64)), 64, 0, st>>>(L, n, n, k0, info);
+      LRC_LAUNCHED();
+    }
     float* p = L + (k0 + NB) * n + k0;
     float* c = L + (k0 + NB) * n + (k0 + NB);
     LRC_TRY(gemm_f32(st, GEMM_TB | GEMM_LOWER, below, below, NB, -1.f, p, n, 0, p, n, 0, 1.f, c, n, 0, 1));
