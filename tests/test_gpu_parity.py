@@ -785,13 +785,15 @@ def test_rank_scores_reject_bad_inputs(lrc):
 
 
 # ----------------------------------------------------------------------------- factor codec
-@pytest.mark.parametrize("d_out,r,d_in", [(96, 64, 40), (300, 1024, 257), (5, 1, 3), (64, 2048, 128)])
+@pytest.mark.parametrize("d_out,r,d_in", [(96, 64, 40), (300, 1024, 257), (5, 1, 3), (64, 2048, 128),
+                                         (40, 4096, 130), (24, 8192, 77)])
 def test_rotate_quantize(lrc, d_out, r, d_in):
     """The rotated factors are the fp64 products rounded once to fp32: they match the
     oracle's within one fp32 rounding (the two sides sum in different orders).  The int8
     codes and scales are a decision taken in fp32 on those values, so they are checked bit
     for bit against the oracle's quantiser applied to the GPU's own rotated factors.
-    The shapes include an outlier channel, r = 1 and ragged d_out / d_in."""
+    The shapes include an outlier channel, r = 1, ragged d_out / d_in and the largest
+    ranks (4096, 8192: rows of 32 and 64 KB in LDS)."""
     g = torch.Generator().manual_seed(r + d_in)
     left = torch.randn(d_out, r, generator=g)
     left[:, r // 3] *= 40.0      # an outlier channel, the case the rotation is for
