@@ -80,8 +80,9 @@ def layer_bytes(d):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=3)
-    p.add_argument("--warmup", type=int, default=1)
+    # enough steps to keep every stream busy (the timed region is under a second)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--tokens", type=int, default=65536)
     p.add_argument("--d", type=int, default=4096)
     p.add_argument("--rank", type=int, default=1024)
