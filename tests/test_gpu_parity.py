@@ -572,7 +572,8 @@ def test_decompose_default_solver_mid_size(lrc):
 # ----------------------------------------------------------------------------- a6 scores
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("n,d_out,d_in,k", [(1000, 70, 90, 50), (4096, 256, 128, 128), (65, 16, 300, 16),
-                                             (1000, 72, 88, 50), (777, 200, 136, 300), (513, 1024, 64, 129)])
+                                             (1000, 72, 88, 50), (777, 200, 136, 300), (513, 1024, 64, 129),
+                                             (2100, 264, 520, 600), (20000, 64, 64, 2048)])
 def test_fisher_scores(lrc, dtype, n, d_out, d_in, k):
     """Same synthetic factors and streams into both sides.  fp32 projections then
     squares: relative error per token term ~ 4 * sqrt(d) u on well-scaled terms; the sum
@@ -580,7 +581,8 @@ def test_fisher_scores(lrc, dtype, n, d_out, d_in, k):
     widths a multiple of 8 take the MFMA kernel, whose factors are split into two bf16
     parts (residual <= 2^-16 of each factor entry): the projection error grows to about
     2^-16 relative, 4 of which reach the product of squares, still inside 2e-4.  The
-    shapes cover ragged token, component and reduction tiles of both kernels."""
+    shapes cover ragged token, component and reduction tiles of both kernels, up to 79
+    token tiles by 16 component tiles."""
     a = synth.activation_stream(n, d_in, 1.0, 300 + n, dtype=dtype)
     b = synth.activation_stream(n, d_out, 1.5, 301 + n, dtype=dtype)
     g = torch.Generator().manual_seed(k)
