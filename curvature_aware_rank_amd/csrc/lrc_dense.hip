@@ -35,7 +35,19 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(unsigned flags, int m, in
   A += blockIdx.z * sA;
   B += blockIdx.z * sB;
   C += blockIdx.z * sC;
-  const int row0 = blockIdx.y * GT, col0 = blockIdx.x * GT;
+  // Tiles of a triangular operand carry unequal work; they are dispatched longest first,
+  // so that the launch does not end on a few long tiles started late: with k from the
+  // tile's first column, column by column (rows within a column); with k up to its last
+  // row, bottom row first.  Otherwise row by row, columns within a row.
+  int tr_ = blockIdx.y, tc_ = blockIdx.x;
+  if ((flags & GEMM_K_FROM_COL) && !(flags & GEMM_K_FROM_ROW)) {
+    const int lin = blockIdx.y * gridDim.x + blockIdx.x;
+    tc_ = lin / gridDim.y;
+    tr_ = lin % gridDim.y;
+  } else if (flags & GEMM_K_TO_ROW) {
+    tr_ = gridDim.y - 1 - blockIdx.y;
+  }
+  const int row0 = tr_ * GT, col0 = tc_ * GT;
   if (row0 >= m || col0 >= n) return;
   if ((flags & GEMM_LOWER) && col0 > row0 + GT - 1) return;
   int kb = 0, ke = k;
