@@ -445,12 +445,33 @@ __global__ __launch_bounds__(64) void trsm_panel_kernel(float* __restrict__ L, i
   }
 }
 
+// Y <- D^-T Y for one diagonal block D (b x b, lower, at (k0, k0) of L) and the b rows
+// k0.. of Y (ncol columns, leading dim ldb): one lane per column, the block in LDS.
+// Column-oriented: x_c = y_c / D[c][c], then every y_i with i < c drops D[c][i] x_c, so
+// a step is one division plus independent updates, and row c of D is read four entries
+// per LDS read.
 __global__ __launch_bounds__(64) void trsm_upper_diag_kernel(const float* __restrict__ L, int64_t ldl, int64_t k0, int b,
                                                              float* __restrict__ Bm, int64_t ldb, int64_t ncol) {
-  __shared__ float D[NB][NB + 1];
-  for (int e = threadIdx.x; e < NB * NB; e += 64) {
-    const int i = e / NB, j = e % NB;
-    D[i][j] = (i < b && j < b) ? L[(k0 + i) * ldl + k0 + j] : (i == j ? 1.f : 0.f);
+  __shared__ __align__(16) float D[NB][NB + 4];
+  if (b == NB && ldl % 4 == 0 && k0 % 4 == 0 && (reinterpret_cast<uintptr_t>(L) & 15) == 0) {
+    // a full block in 16-byte pieces, all loads issued before the first LDS store
+    float4 v[NB * NB / 4 / 64];
+#pragma unroll
+    for (int q = 0; q < NB * NB / 4 / 64; ++q) {
+      const int e = threadIdx.x + 64 * q, i = e / (NB / 4), j = 4 * (e % (NB / 4));
+      v[q] = *reinterpret_cast<const float4*>(L + (k0 + i) * ldl + k0 + j);
+    }
+#pragma unroll
+    for (int q = 0; q < NB * NB / 4 / 64; ++q) {
+      const int e = threadIdx.x + 64 * q, i = e / (NB / 4), j = 4 * (e % (NB / 4));
+      *reinterpret_cast<float4*>(&D[i][j]) = v[q];
+    }
+  } else {
+#pragma unroll 16
+    for (int e = threadIdx.x; e < NB * NB; e += 64) {
+      const int i = e / NB, j = e % NB;
+      D[i][j] = (i < b && j < b) ? L[(k0 + i) * ldl + k0 + j] : (i == j ? 1.f : 0.f);
+    }
   }
   __syncthreads();
   const int64_t col = int64_t(blockIdx.x) * 64 + threadIdx.x;
@@ -459,11 +480,18 @@ __global__ __launch_bounds__(64) void trsm_upper_diag_kernel(const float* __rest
 #pragma unroll
   for (int i = 0; i < NB; ++i) y[i] = (i < b) ? Bm[(k0 + i) * ldb + col] : 0.f;
 #pragma unroll
-  for (int i = NB - 1; i >= 0; --i) {
-    float v = y[i];
+  for (int c = NB - 1; c >= 0; --c) {
+    y[c] = y[c] / D[c][c];
+    const float xc = y[c];
 #pragma unroll
-    for (int c = i + 1; c < NB; ++c) v -= D[c][i] * y[c];
-    y[i] = v / D[i][i];
+    for (int g = 0; g < c / 4 + 1; ++g) {
+      if (4 * g >= c) break;
+      const float4 dv = *reinterpret_cast<const float4*>(&D[c][4 * g]);
+      y[4 * g] = fmaf(-dv.x, xc, y[4 * g]);
+      if (4 * g + 1 < c) y[4 * g + 1] = fmaf(-dv.y, xc, y[4 * g + 1]);
+      if (4 * g + 2 < c) y[4 * g + 2] = fmaf(-dv.z, xc, y[4 * g + 2]);
+      if (4 * g + 3 < c) y[4 * g + 3] = fmaf(-dv.w, xc, y[4 * g + 3]);
+    }
   }
 #pragma unroll
   for (int i = 0; i < NB; ++i)
@@ -555,18 +583,22 @@ lrc_status cholesky_f32(hipStream_t st, const float* S, int64_t lds_, int64_t n,
 }
 
 lrc_status trsm_lower_t(hipStream_t st, const float* L, int64_t n, float* Bm, int64_t ldb, int64_t ncol) {
+  // right-looking, last block first: solve the diagonal block, then take its rows'
+  // contribution out of every row above at once (one GEMM over all of them, 64 deep)
   const int64_t nblk = cdiv(n, NB);
   for (int64_t ib = nblk - 1; ib >= 0; --ib) {
     const int64_t k0 = ib * NB;
     const int b = int(std::min<int64_t>(NB, n - k0));
-    const int64_t rest = n - (k0 + b);
-    if (rest > 0) {
-      // B[k0:k0+b] -= L[k0+b:n, k0:k0+b]^T * Y[k0+b:n]
-      LRC_TRY(gemm_f32(st, GEMM_TA, b, ncol, rest, -1.f, L + (k0 + b) * n + k0, n, 0, Bm + (k0 + b) * ldb, ldb, 0,
-                       1.f, Bm + k0 * ldb, ldb, 0, 1));
+    {
+      ProfScope scope("trsm_upper_diag_kernel", st, double(b) * double(b) * double(ncol),
+                      8.0 * double(b) * double(ncol) + 4.0 * double(b) * double(b));
+      trsm_upper_diag_kernel<<<unsigned(cdiv(ncol, 64)), 64, 0, st>>>(L, n, k0, b, Bm, ldb, ncol);
+      LRC_LAUNCHED();
     }
-    trsm_upper_diag_kernel<<<unsigned(cdiv(ncol, 64)), 64, 0, st>>>(L, n, k0, b, Bm, ldb, ncol);
-    LRC_LAUNCHED();
+    if (k0 > 0) {
+      // B[0:k0] -= L[k0:k0+b, 0:k0]^T * X[k0:k0+b]
+      LRC_TRY(gemm_f32(st, GEMM_TA, k0, ncol, b, -1.f, L + k0 * n, n, 0, Bm + k0 * ldb, ldb, 0, 1.f, Bm, ldb, 0, 1));
+    }
   }
   return LRC_OK;
 }
