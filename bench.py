@@ -453,6 +453,21 @@ def passes(lrc, torch, dev):
     shapes (synthetic inputs), and of the follow-on kernels."""
     import synth
     out = {}
+    # a long covariance stream: 1,048,576 bf16 tokens x 4096 in one call (16 copies of a
+    # 65536-token block, 8 GiB resident), so that launches and the split reduction are
+    # amortised over many tokens
+    blk = synth.activation_stream(65536, 4096, 1.0, 40, outlier_frac=0.01, dtype=torch.bfloat16, device=dev)
+    big = blk.repeat(16, 1)
+    del blk
+    cov = torch.zeros(4096, 4096, device=dev)
+    lrc.lrc_accumulate_cov(big, cov)
+    t = _time_queued(lambda: lrc.lrc_accumulate_cov(big, cov), torch, 3)
+    nt = big.shape[0]
+    out["cov_stream_1m"] = {"workload": f"{nt} bf16 tokens x 4096 in one call", "ms": round(t * 1e3, 3),
+                            "tokens_per_s": round(nt / t, 1),
+                            "mfma_bf16_frac": round(nt * 4096 * 4097.0 / t / 1e12 / PEAK_TFLOPS["bf16"], 4)}
+    del big, cov
+    progress("pass: long covariance stream")
     n, d, k = 32768, 4096, 4096
     a = synth.activation_stream(n, d, 1.0, 41, dtype=torch.bfloat16, device=dev)
     b = synth.activation_stream(n, d, 1.5, 42, dtype=torch.bfloat16, device=dev)
