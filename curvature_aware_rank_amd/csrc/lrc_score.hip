@@ -246,9 +246,8 @@ __device__ __forceinline__ void fisher_phase(const uint16_t* __restrict__ X, int
   // stored to LDS after chunk c + 2 is computed, so two compute phases cover their latency.
   // The loop body has no branch: the chunk count is rounded up to even (a chunk past the
   // end loads zeros, whose products add exactly 0), and loads run past the last chunk
-  // (reading the zero constant).  So on every path
-  // the loads a store waits for are followed by exactly one newer set, which the wait
-  // before the store leaves in flight.
+  // (reading the zero constant).  So on every path the loads a store waits for are
+  // followed by exactly one newer set, which the wait before the store leaves in flight.
   const int nch2 = (nch + 1) & ~1;
   u32x4 g0[2][FQ], ga0[XQ], g1[2][FQ], ga1[XQ];
   load_f(g0, ga0, 0);
