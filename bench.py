@@ -12,7 +12,7 @@ are in flight at a time; `value` is K / the wall time of the region.  The same K
 `value_one_stream` (one layer's latency).  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--streams S] [--no-cpu-baseline] [--no-secondary]
-    python bench.py --only syrk|tridiag|fisher|ffn-decode [--copy-probe-mib M]
+    python bench.py --only syrk|tridiag|fisher|alloc|qaw|ffn-decode [--copy-probe-mib M]
 
 The --only modes run one part of the path a few times (and, with --copy-probe-mib, a
 plain device copy of known size first): they are the programs the rocprofv3 summaries
@@ -93,7 +93,7 @@ def parse():
                    help="hardware queues HIP gives this process (GPU_MAX_HW_QUEUES, set before HIP starts)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true", help="skip the other workloads and passes")
-    p.add_argument("--only", choices=["syrk", "tridiag", "fisher", "ffn-decode"], default=None,
+    p.add_argument("--only", choices=["syrk", "tridiag", "fisher", "alloc", "qaw", "ffn-decode"], default=None,
                    help="run one part of the path (for rocprofv3) instead of the benchmark")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="first run a plain elementwise copy (neg) of this many MiB three times: the "
@@ -631,6 +631,47 @@ def only(args, lrc, torch, dev):
         flops = 2.0 * n * k * (d + d) + 3.0 * n * k
         res["ms_per_call"] = round(ms, 4)
         res["TFLOP/s"] = round(flops / (ms * 1e-3) / 1e12, 1)
+    elif args.only == "alloc":
+        # global sort-and-truncate: the decoder stack's 917,504-component pool (224
+        # matrices, costs 8192 / 15104) and a 64M-component pool; one untimed and five
+        # timed calls each, queued back to back
+        g = torch.Generator(device=dev)
+        g.manual_seed(45)
+        for m_items, n_mat in ((917504, 224), (64 * 1024 * 1024, 16384)):
+            per = m_items // n_mat
+            offs = torch.arange(0, m_items + 1, per, dtype=torch.int64, device=dev)
+            cost = torch.where(torch.arange(n_mat, device=dev) % 7 < 4, 8192, 15104).to(torch.int64)
+            scores = torch.rand(m_items, generator=g, device=dev)
+            budget = int(0.6 * float((cost * per).sum()))
+            lrc.lrc_allocate_ranks(scores, offs, cost, budget)
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            s.record()
+            for _ in range(5):
+                lrc.lrc_allocate_ranks(scores, offs, cost, budget)
+            e.record()
+            torch.cuda.synchronize()
+            res[f"ms_per_call_{m_items}"] = round(s.elapsed_time(e) / 5, 4)
+            del offs, cost, scores
+    elif args.only == "qaw":
+        # int8-QAW activation covariance of the FFN pair's down projection: 131072 bf16
+        # tokens x 11008 (per-token fake quantisation pre-pass, then the two-term SYRK into
+        # the 11008 x 11008 sum); one untimed and two timed calls.  The stream's rotation is
+        # drawn on the host: the device QR of an 11008 x 11008 matrix has crashed inside
+        # the vendor solver under rocprofv3's counter collection.
+        cs = synth.workload_spec("ffn_pair_11008x4096")
+        a = synth.stream(cs, "a_down", device=dev, rotation_device="cpu")
+        cov = torch.zeros(a.shape[1], a.shape[1], device=dev)
+        lrc.lrc_accumulate_cov(a, cov, quant=True)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(2):
+            lrc.lrc_accumulate_cov(a, cov, quant=True)
+        e.record()
+        torch.cuda.synchronize()
+        res["tokens"], res["d"] = int(a.shape[0]), int(a.shape[1])
+        res["ms_per_accumulation"] = round(s.elapsed_time(e) / 2, 4)
     elif args.only == "tridiag":
         # one covariance and one whitened decomposition of the attention projection
         a = synth.activation_stream(args.tokens, args.d, 1.0, 31, outlier_frac=0.01, dtype=torch.bfloat16,

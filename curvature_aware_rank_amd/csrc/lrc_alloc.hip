@@ -36,7 +36,7 @@ constexpr int RT = 256;        // threads per sort workgroup (4 waves)
 // tiles) for large pools, 4 (1024-item tiles) when 4096-item tiles would give fewer than two
 // workgroups per compute unit -- more, shorter workgroups at small sizes
 constexpr int RR_BIG = 16, RR_SMALL = 4;
-constexpr int MAX_SORT_BLOCKS = 1024;   // sort workgroups per pass; each takes a run of tiles
+constexpr int MAX_SORT_BLOCKS = 4096;   // sort workgroups per pass; each takes a run of tiles
 constexpr int SC = 8;          // items per thread in the int64 scan
 constexpr int STILE = 256 * SC;
 constexpr int MB_SHIFT = 12;   // item ids per bucket of the matrix lookup table (log2)

@@ -106,6 +106,50 @@ __device__ __forceinline__ bf16x8 frag_tr(const uint16_t* base, int ch0, int k0,
   return f;
 }
 
+// Epilogue of one wave's NI x 4 blocks of 32 x 32 (lane l, element e -> row
+// 8 (e / 4) + 4 (l / 32) + e % 4, column l % 32 of a block).  With several splits the
+// split's partial tile is stored for syrk_reduce_kernel.  With one split there is nothing
+// to order, so the wave adds its blocks to C itself, with the masks and the diagonal check
+// of the reduction kernel: the result is the reduction's C + (0 + p) bit for bit, since an
+// accumulator that starts at +0 never holds -0.
+template <int NI>
+__device__ __forceinline__ void syrk_store_tile(const f32x16 (&acc)[NI][4], int r_base, int c_base, int lane,
+                                                int split, int splits, int tile, int n_tiles, int ti, int tj,
+                                                int d, float* __restrict__ partial, float* __restrict__ C,
+                                                int64_t ldc, int32_t* __restrict__ info) {
+  if (splits > 1) {
+    float* part = partial + (int64_t(split) * n_tiles + tile) * (TB * TB);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int lr = r_base + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          const int lc = c_base + j * 32 + (lane & 31);
+          part[lr * TB + lc] = acc[i][j][e];
+        }
+    return;
+  }
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = ti * TB + r_base + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int col = tj * TB + c_base + j * 32 + (lane & 31);
+        if (row < d && col < d && col <= row) {
+          float* c = C + int64_t(row) * ldc + col;
+          const float v = *c + acc[i][j][e];
+          *c = v;
+          bad |= col == row && !isfinite(v);
+        }
+      }
+  if (info && bad) *info = LRC_ENONFINITE;
+}
+
 // C[lower] += X^T Y over tokens [0, n) (X, Y: n x d bf16 bits, leading dim ldx).
 // Workgroup -> (split, tile): consecutive workgroups land on consecutive XCDs, and XCD x
 // takes one compact group of tiles for every split (grid.x = NXCD * tiles_per_xcd *
@@ -113,7 +157,8 @@ __device__ __forceinline__ bf16x8 frag_tr(const uint16_t* base, int ch0, int k0,
 template <bool VEC>
 __global__ __launch_bounds__(NTH, 1) void syrk_bf16_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Y, int64_t ldx, int64_t n, int d,
-    int n1, int n_tiles, int tiles_per_xcd, int splits, int steps_per_split, float* __restrict__ partial) {
+    int n1, int n_tiles, int tiles_per_xcd, int splits, int steps_per_split, float* __restrict__ partial,
+    float* __restrict__ C, int64_t ldc, int32_t* __restrict__ info) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * OPER];
 
   const int b = blockIdx.x;
@@ -204,20 +249,8 @@ __global__ __launch_bounds__(NTH, 1) void syrk_bf16_kernel(
     __syncthreads();
   }
 
-  // ---- epilogue: this split's partial tile.  Output layout of a 32x32 block: lane l,
-  //      element e -> row 8*(e/4) + 4*(l/32) + e%4, column l%32.
-  const int r_base = wr * 128, c_base = wc * 128;
-  float* part = partial + (int64_t(split) * n_tiles + tile) * (TB * TB);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int lr = r_base + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        const int lc = c_base + j * 32 + (lane & 31);
-        part[lr * TB + lc] = acc[i][j][e];
-      }
+  // ---- epilogue: this split's partial tile, or the tile added to C (one split)
+  syrk_store_tile<4>(acc, wr * 128, wc * 128, lane, split, splits, tile, n_tiles, ti, tj, d, partial, C, ldc, info);
 }
 
 
@@ -269,7 +302,8 @@ __device__ __forceinline__ int frag_off(int ch0, int lane) {
 constexpr int DL_NW = 8;
 __global__ __launch_bounds__(64 * DL_NW, 1) void syrk_bf16_dl_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Y, int64_t ldx, int64_t n, int d, int n1,
-    int n_tiles, int tiles_per_xcd, int splits, int64_t tok_per_split, float* __restrict__ partial) {
+    int n_tiles, int tiles_per_xcd, int splits, int64_t tok_per_split, float* __restrict__ partial,
+    float* __restrict__ C, int64_t ldc, int32_t* __restrict__ info) {
   constexpr int LDPW = OPB / 1024 / DL_NW;  // 1 KB loads per wave per operand per stage
   constexpr int RB = TB / (DL_NW / 2);      // rows of a wave's block
   constexpr int NI = RB / 32;
@@ -450,18 +484,7 @@ __global__ __launch_bounds__(64 * DL_NW, 1) void syrk_bf16_dl_kernel(
   // prologue loads of stages past a short split may still be in flight
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  const int r_base = wr * RB, c_base = wc * 128;
-  float* part = partial + (int64_t(split) * n_tiles + tile) * (TB * TB);
-#pragma unroll
-  for (int i = 0; i < NI; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int lr = r_base + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        const int lc = c_base + j * 32 + (lane & 31);
-        part[lr * TB + lc] = acc[i][j][e];
-      }
+  syrk_store_tile<NI>(acc, wr * RB, wc * 128, lane, split, splits, tile, n_tiles, ti, tj, d, partial, C, ldc, info);
 }
 
 // C[lower] += sum over splits of the partial tiles, in split order (bit-reproducible).
@@ -712,14 +735,15 @@ lrc_status launch_syrk_bf16(hipStream_t st, const uint16_t* X, const uint16_t* Y
   // stages the pipeline may fetch past its end) must stay below 2^31
   if (vec && (tok_per_split + 4 * KS2) * ldx * 2 < (int64_t(1) << 31))
     syrk_bf16_dl_kernel<<<grid, 64 * DL_NW, 0, st>>>(X, Y, ldx, n, int(d), p.n1, p.n_tiles, p.tiles_per_xcd, p.splits,
-                                                 tok_per_split, partial);
+                                                 tok_per_split, partial, C, ldc, info);
   else if (vec)
     syrk_bf16_kernel<true><<<grid, NTH, 0, st>>>(X, Y, ldx, n, int(d), p.n1, p.n_tiles, p.tiles_per_xcd,
-                                                 p.splits, p.steps_per_split, partial);
+                                                 p.splits, p.steps_per_split, partial, C, ldc, info);
   else
     syrk_bf16_kernel<false><<<grid, NTH, 0, st>>>(X, Y, ldx, n, int(d), p.n1, p.n_tiles, p.tiles_per_xcd,
-                                                  p.splits, p.steps_per_split, partial);
+                                                  p.splits, p.steps_per_split, partial, C, ldc, info);
   LRC_LAUNCHED();
+  if (p.splits == 1) return LRC_OK;   // the kernel added its tiles to C
   const int vec4 = (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & 15) == 0);
   syrk_reduce_kernel<<<dim3(unsigned(p.n_tiles), unsigned(TB * TB / 4 / 256)), 256, 0, st>>>(
       partial, p.splits, p.n_tiles, p.n1, int(d), C, ldc, vec4, info);
@@ -741,7 +765,8 @@ size_t cov_workspace(lrc_dtype dt, int64_t n, int64_t d, uint32_t flags, void* b
     cap = p.splits;
     if (quant && n % nb) cap = std::max(cap, plan_syrk(n % nb, d).splits);
     p.splits = cap;
-    pf = syrk_partial_floats(p);
+    // one split everywhere: the SYRK adds its tiles to C itself, no partial tiles
+    pf = cap > 1 ? syrk_partial_floats(p) : 0;
   }
   float* pp = cv.take<float>(pf);
   uint16_t *qq = nullptr, *hh = nullptr, *ll = nullptr;

@@ -48,9 +48,12 @@ def haar_rotation(d: int, seed: int, device="cpu") -> torch.Tensor:
 
 def activation_stream(n: int, d: int, exponent: float, seed: int, *, outlier_frac: float = 0.0,
                       outlier_scale: float = 20.0, scale: float = 1.0,
-                      dtype=torch.bfloat16, device="cpu", block: int = 8192) -> torch.Tensor:
-    """Token-major calibration matrix (n x d) with a power-law covariance spectrum."""
-    q = haar_rotation(d, seed, device)
+                      dtype=torch.bfloat16, device="cpu", block: int = 8192,
+                      rotation_device=None) -> torch.Tensor:
+    """Token-major calibration matrix (n x d) with a power-law covariance spectrum.
+    ``rotation_device`` draws the rotation elsewhere (the host, say) and moves it to
+    ``device``; the draw then differs from one made on ``device``."""
+    q = haar_rotation(d, seed, rotation_device or device).to(device)
     lam_sqrt = torch.arange(1, d + 1, dtype=torch.float64).pow(-0.5 * exponent)
     lam_sqrt = lam_sqrt.to(device=device, dtype=torch.float32)
     g = _gen(seed + 1, device)
@@ -172,10 +175,10 @@ def workload_spec(name: str, n_tokens: int | None = None, seed: int = 1234) -> W
 
 
 def stream(cs: WorkloadSpec, key: str, *, layer: int = 0, device="cpu", n_tokens: int | None = None,
-           width: int | None = None) -> torch.Tensor:
+           width: int | None = None, rotation_device=None) -> torch.Tensor:
     """Draw one calibration stream of a workload (layer folds into the seed for the stack)."""
     d, p, frac, sd = cs.streams[key]
     d = width or d
     scale = layer_scale(layer, sd) if (cs.name == "decoder_stack_32_layers" and not key.startswith("g_")) else 1.0
     return activation_stream(n_tokens or cs.n_tokens, d, p, sd + 7919 * layer, outlier_frac=frac,
-                             scale=scale, dtype=cs.dtype, device=device)
+                             scale=scale, dtype=cs.dtype, device=device, rotation_device=rotation_device)

@@ -43,11 +43,12 @@ def bf16_stream(n, d, exponent, seed, outlier_frac=0.0):
 
 
 # ----------------------------------------------------------------------------- a1 covariance
-@pytest.mark.parametrize("n,d", [(700, 8), (1000, 300), (4100, 520), (130, 1100)])
+@pytest.mark.parametrize("n,d", [(700, 8), (1000, 300), (4100, 520), (130, 1100), (2000, 4000), (64, 1100)])
 def test_cov_bf16_exact_on_small_integers(lrc, n, d):
     """bf16 inputs in {-3..3}: every product and partial sum is an integer below 2^24, so
     fp32 accumulation is exact in any order -> bit-exact against the oracle.  Catches a
-    dropped, repeated or misplaced token, channel or tile."""
+    dropped, repeated or misplaced token, channel or tile.  The last two shapes have few
+    token steps per tile, so each tile is one split that the SYRK adds to C itself."""
     g = torch.Generator().manual_seed(n * 7 + d)
     a = torch.randint(-3, 4, (n, d), generator=g).to(torch.bfloat16)
     c = torch.zeros(d, d, dtype=torch.float32, device=dev())
@@ -104,13 +105,15 @@ def test_cov_fp32(lrc, n, d):
 
 
 # ----------------------------------------------------------------------------- a0 QAW
-def test_qaw_cov_exact_with_power_of_two_scales(lrc):
+@pytest.mark.parametrize("d", [136, 4000])
+def test_qaw_cov_exact_with_power_of_two_scales(lrc, d):
     """Rows whose max |a| is 127 * 2^e have an exact scale s = 2^e, so q, s^2 q (one bf16
     term, the low term is 0) and every product are exact; with 48 tokens, |values| <= 127
     and s >= 1/4 every partial sum is a multiple of 1/16 below 2^20, so fp32 accumulation
-    is exact in any order and the GPU must equal the oracle bit for bit."""
+    is exact in any order and the GPU must equal the oracle bit for bit.  At 4000 channels
+    each tile is one split, added to C by the SYRK itself."""
     g = torch.Generator().manual_seed(5)
-    n, d = 48, 136
+    n = 48
     a = torch.randint(-7, 8, (n, d), generator=g).float()
     a[:, 3] = 127.0                                   # row max exactly 127 -> s = 1
     scale = 2.0 ** torch.randint(-2, 1, (n, 1), generator=g).float()
@@ -516,6 +519,22 @@ def test_cov_and_scores_flag_nonfinite_inputs(lrc):
     assert int(info[0]) == lrc.LRC_ENONFINITE
 
 
+def test_cov_single_split_flags_nonfinite(lrc):
+    """The SYRK that adds its tiles to C itself (one split: few tokens, many tiles) checks
+    the diagonal as the split reduction does: a NaN in channel 3999 sets LRC_ENONFINITE,
+    clean tokens leave info 0, and the entries away from that channel stay finite."""
+    a = synth.activation_stream(100, 4000, 1.0, 64, dtype=torch.bfloat16).to(dev())
+    c = torch.zeros(4000, 4000, device=dev())
+    info = lrc.lrc_accumulate_cov(a, c)
+    assert int(info[0]) == 0
+    bad = a.clone()
+    bad[7, 3999] = float("nan")
+    c = torch.zeros(4000, 4000, device=dev())
+    info = lrc.lrc_accumulate_cov(bad, c)
+    assert int(info[0]) == lrc.LRC_ENONFINITE
+    assert torch.isnan(c[3999, 3999]) and torch.isfinite(c[:3999, :3999]).all()
+
+
 def test_decompose_deterministic(lrc, solver):
     w = synth.weight(128, 200, 5).to(dev())
     a = synth.activation_stream(1500, 200, 1.0, 6, dtype=torch.bfloat16).to(dev())
@@ -685,6 +704,39 @@ def test_allocate_many_tiles_skewed(lrc):
     assert got[4] == 0
     assert got[0].tolist() == ref[0].tolist()
     assert got[1] == ref[1] and got[2].tolist() == ref[2].tolist() and got[3].tolist() == ref[3].tolist()
+
+
+def test_allocate_runs_of_tiles_per_workgroup(lrc):
+    """A pool of 20 million items, large enough that each sort workgroup takes a run of
+    several tiles (its digit counts carry from tile to tile): 224 matrices, half the scores
+    from 64 values (ties inside and across tiles and workgroups), half uniform.  The
+    reference order is the oracle's keys (checked against allocation_keys on a sample)
+    sorted by a stable library sort: key descending, global item id ascending."""
+    rng = np.random.default_rng(31)
+    n_mat, per = 224, 89286
+    m_items = n_mat * per
+    costs = np.where(np.arange(n_mat) % 7 < 4, 8192, 15104).astype(np.int64)
+    s = rng.random(m_items, dtype=np.float32)
+    tied = rng.random(m_items) < 0.5
+    s[tied] = rng.integers(0, 64, int(tied.sum())).astype(np.float32) * np.float32(1.0 / 64)
+    cost_item = np.repeat(costs, per)
+    budget = int(0.6 * int(cost_item.sum()))
+    offs = np.arange(0, m_items + 1, per, dtype=np.int64)
+    order, n_kept, ranks, kept, info = lrc.lrc_allocate_ranks(
+        torch.tensor(s, device=dev()), torch.tensor(offs, device=dev()), torch.tensor(costs, device=dev()), budget)
+    assert int(to_np(info)[0]) == 0
+    key = s.astype(np.float64) / cost_item.astype(np.float64)
+    smp = rng.integers(0, m_items, 5000)
+    assert np.array_equal(np.asarray(oracle.allocation_keys(s[smp].tolist(), cost_item[smp].tolist())), key[smp])
+    ref_order = np.lexsort((np.arange(m_items), -key))
+    assert np.array_equal(to_np(order).astype(np.int64), ref_order)
+    csum = np.cumsum(cost_item[ref_order])
+    ref_kept = int(np.searchsorted(csum, budget, side="right"))
+    assert int(to_np(n_kept)[0]) == ref_kept
+    mask = np.zeros(m_items, np.uint8)
+    mask[ref_order[:ref_kept]] = 1
+    assert np.array_equal(to_np(kept), mask)
+    assert np.array_equal(to_np(ranks), np.bincount(ref_order[:ref_kept] // per, minlength=n_mat).astype(np.int32))
 
 
 def test_allocate_edge_cases(lrc):
