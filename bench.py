@@ -61,7 +61,7 @@ ROOFLINE = {
 # counters were taken on (profiles/counters_tri_symv_attnproj_4096.md: fetch 24.44 MB +
 # write 0.77 MB, the average over the 3968 launches of a 4096-wide tridiagonalisation).
 # A kernel without an entry reports traffic null.
-TRAFFIC = {"tri_symv_kernel": {"bytes": 25.22e6, "kernel_source_commit": "6524d8f"}}
+TRAFFIC = {"tri_symv_kernel": {"bytes": 25.22e6, "kernel_source_commit": "8db424f"}}
 
 
 def layer_flops(d, r):
