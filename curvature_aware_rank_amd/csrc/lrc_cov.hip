@@ -311,6 +311,7 @@ __global__ __launch_bounds__(64 * DL_NW, 1) void syrk_bf16_dl_kernel(
   // of one stage waits only for that stage's loads (with a shared array it would wait for
   // all of them)
   __shared__ __attribute__((aligned(1024))) uint8_t sb0[STB], sb1[STB], sb2[STB], sb3[STB];
+  static_assert(NSTG == 4, "one LDS object per stage: sb0 .. sb3");
 
   const int b = blockIdx.x;
   const int xcd = b % NXCD;
