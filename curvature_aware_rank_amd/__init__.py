@@ -49,6 +49,9 @@ _SIGS = {
     "lrc_whiten_decompose": (_i32, [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
                                     _i64, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "lrc_whiten_decompose_workspace": (_sz, [_i64, _i64, _i64, _i64, _i32, _i32]),
+    "lrc_whiten_decompose_strided": (_i32, [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _vp, _i64,
+                                            _i64, _i64, _i64, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "lrc_whiten_decompose_strided_workspace": (_sz, [_i64, _i64, _i64, _i64, _i64, _i64]),
     "lrc_score_components": (_i32, [_vp, _vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _u32, _i32, _i32,
                                     _i64, _vp, _vp, _vp, _sz, _vp]),
     "lrc_score_components_workspace": (_sz, [_i64, _i64, _i64, _i64, _u32]),
@@ -186,7 +189,9 @@ def lrc_accumulate_cov(A: torch.Tensor, C: torch.Tensor, quant: bool = False, in
 def lrc_whiten_decompose(W: torch.Tensor, rank: int, Xsum=None, n_x: int = 0, Gsum=None, n_g: int = 0,
                          damping: float = 0.0):
     """Whitened truncated decomposition.  W: (d_out, d_in) or (batch, d_out, d_in) fp32;
-    Xsum (d_in, d_in) and Gsum (d_out, d_out) fp32 sums, or None for identity.
+    Xsum (d_in, d_in) and Gsum (d_out, d_out) fp32 sums shared by the batch, or
+    (batch, d_in, d_in) / (batch, d_out, d_out) with one sum per slice (independent
+    layers; the token counts n_x, n_g are common), or None for identity.
 
     Returns (sigma, left, right, info): sigma (batch, k), left (batch, d_out, r),
     right (batch, r, d_in), info (batch,) int32 -- batch dim dropped for 2-D W.  A
@@ -207,18 +212,27 @@ def lrc_whiten_decompose(W: torch.Tensor, rank: int, Xsum=None, n_x: int = 0, Gs
     left = torch.empty(batch, d_out, rank, dtype=torch.float32, device=dev)
     right = torch.empty(batch, rank, d_in, dtype=torch.float32, device=dev)
     info = torch.empty(batch, dtype=torch.int32, device=dev)
-    ldx = ldg = 0
-    if Xsum is not None:
-        _tensor(Xsum, "Xsum", torch.float32, (d_in, d_in), dev)
-        ldx = _rowmajor_ld(Xsum, "Xsum")
-    if Gsum is not None:
-        _tensor(Gsum, "Gsum", torch.float32, (d_out, d_out), dev)
-        ldg = _rowmajor_ld(Gsum, "Gsum")
-    nb = lib.lrc_whiten_decompose_workspace(d_out, d_in, batch, rank, Xsum is not None, Gsum is not None)
+    def cov_arg(S, name, dim):
+        """(pointer tensor, leading dim, slice stride, slices) of a covariance argument"""
+        if S is None:
+            return None, 0, 0, 0
+        if S.dim() == 3 and squeeze:
+            raise ValueError(f"{name}: one sum per slice needs a batched W")
+        if S.dim() == 3:
+            _tensor(S, name, torch.float32, (batch, dim, dim), dev)
+            if S.stride(2) != 1 or S.stride(1) < dim or S.stride(0) < dim * S.stride(1):
+                raise ValueError(f"{name} must be row-major slices")
+            return S, S.stride(1), S.stride(0), batch
+        _tensor(S, name, torch.float32, (dim, dim), dev)
+        return S, _rowmajor_ld(S, name), 0, 1
+
+    Xs, ldx, sx, nxs = cov_arg(Xsum, "Xsum", d_in)
+    Gs, ldg, sg, ngs = cov_arg(Gsum, "Gsum", d_out)
+    nb = lib.lrc_whiten_decompose_strided_workspace(d_out, d_in, batch, rank, nxs, ngs)
     ws = _workspace(nb, dev)
-    st = lib.lrc_whiten_decompose(_ptr(W3), d_out, d_in, ldw, batch, sw, _ptr(Xsum), ldx, int(n_x), _ptr(Gsum), ldg,
-                                  int(n_g), int(rank), float(damping), _ptr(sigma), _ptr(left), _ptr(right),
-                                  _ptr(info), _ptr(ws), ws.numel(), _stream())
+    st = lib.lrc_whiten_decompose_strided(_ptr(W3), d_out, d_in, ldw, batch, sw, _ptr(Xs), ldx, sx, int(n_x),
+                                          _ptr(Gs), ldg, sg, int(n_g), int(rank), float(damping), _ptr(sigma),
+                                          _ptr(left), _ptr(right), _ptr(info), _ptr(ws), ws.numel(), _stream())
     _check(st, "lrc_whiten_decompose")
     if squeeze:
         return sigma[0], left[0], right[0], info

@@ -45,11 +45,12 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
 // and its Gram is replaced by diag(k, k-1, ..., 1): distinct, well separated eigenvalues,
 // so the eigensolver's fixed work runs on benign data.  Nothing is read by the host; the
 // outputs of such a call are undefined.
-__global__ void chol_guard_kernel(const int* __restrict__ chol_info, int d_in, double* __restrict__ G, int64_t ldg,
-                                  int64_t sG, int k, int32_t* __restrict__ info) {
-  const int cx = chol_info[0], cg = chol_info[1];
-  if (cx == 0 && cg == 0) return;
+__global__ void chol_guard_kernel(const int* __restrict__ chol_info, int xstep, int gstep, int d_in,
+                                  double* __restrict__ G, int64_t ldg, int64_t sG, int k, int32_t* __restrict__ info) {
+  // slice b's pivots: chol_info[2 b] for X, [2 b + 1] for G (slot 0 / 1 when shared)
   const int b = blockIdx.y;
+  const int cx = chol_info[2 * b * xstep], cg = chol_info[2 * b * gstep + 1];
+  if (cx == 0 && cg == 0) return;
   double* g = G + b * sG;
   const int64_t kk = int64_t(k) * k;
   for (int64_t e = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; e < kk; e += int64_t(gridDim.x) * blockDim.x) {
@@ -88,14 +89,17 @@ struct DWs {
   void* jac;
 };
 
-DWs carve_decomp(Carve& cv, int64_t d_out, int64_t d_in, int64_t batch, int64_t rank, bool hx, bool hg) {
+// nx, ng: Cholesky factors to hold for X and G (0: no such covariance, 1: shared by the
+// batch, batch: one per slice)
+DWs carve_decomp(Carve& cv, int64_t d_out, int64_t d_in, int64_t batch, int64_t rank, int64_t nx, int64_t ng) {
   const int64_t k = std::min(d_out, d_in);
   const int64_t kp = jacobi_padded(k);
   const int64_t big = std::max(d_out, d_in);
+  const bool hx = nx > 0, hg = ng > 0;
   DWs w;
-  w.lx = hx ? cv.take<float>(size_t(d_in * d_in)) : nullptr;
-  w.lg = hg ? cv.take<float>(size_t(d_out * d_out)) : nullptr;
-  w.chol_info = cv.take<int>(2);
+  w.lx = hx ? cv.take<float>(size_t(nx * d_in * d_in)) : nullptr;
+  w.lg = hg ? cv.take<float>(size_t(ng * d_out * d_out)) : nullptr;
+  w.chol_info = cv.take<int>(size_t(2 * batch));
   w.wt1 = (hx || hg) ? cv.take<float>(size_t(batch * d_out * d_in)) : nullptr;
   w.wt2 = (hx && hg) ? cv.take<float>(size_t(batch * d_out * d_in)) : nullptr;
   w.gram = cv.take<double>(size_t(batch * kp * kp));
@@ -113,19 +117,25 @@ DWs carve_decomp(Carve& cv, int64_t d_out, int64_t d_in, int64_t batch, int64_t 
 
 using namespace lrc;
 
-extern "C" size_t lrc_whiten_decompose_workspace(int64_t d_out, int64_t d_in, int64_t batch, int64_t rank, int has_x,
-                                                 int has_g) {
+namespace lrc {
+namespace {
+
+size_t decompose_workspace(int64_t d_out, int64_t d_in, int64_t batch, int64_t rank, int64_t nx, int64_t ng) {
   if (d_out <= 0 || d_in <= 0 || batch <= 0 || rank < 0) return 0;
   Carve cv(nullptr);
-  carve_decomp(cv, d_out, d_in, batch, rank, has_x != 0, has_g != 0);
+  carve_decomp(cv, d_out, d_in, batch, rank, nx, ng);
   return cv.bytes();
 }
 
-extern "C" lrc_status lrc_whiten_decompose(const float* W, int64_t d_out, int64_t d_in, int64_t ldw, int64_t batch,
-                                           int64_t stride_w, const float* Xsum, int64_t ldx, int64_t n_x,
-                                           const float* Gsum, int64_t ldg, int64_t n_g, int64_t rank, float damping,
-                                           float* sigma, float* left, float* right, int32_t* info, void* ws,
-                                           size_t ws_bytes, void* stream) {
+// slices of a covariance: 0 (absent), 1 (shared by the batch) or batch (one per slice)
+int64_t cov_slices(const void* sum, int64_t stride, int64_t batch) {
+  return sum == nullptr ? 0 : (stride == 0 ? 1 : batch);
+}
+
+lrc_status decompose(const float* W, int64_t d_out, int64_t d_in, int64_t ldw, int64_t batch, int64_t stride_w,
+                     const float* Xsum, int64_t ldx, int64_t stride_x, int64_t n_x, const float* Gsum, int64_t ldg,
+                     int64_t stride_g, int64_t n_g, int64_t rank, float damping, float* sigma, float* left,
+                     float* right, int32_t* info, void* ws, size_t ws_bytes, hipStream_t st) {
   if (W == nullptr || sigma == nullptr || info == nullptr) return LRC_EINVAL;
   if (d_out <= 0 || d_in <= 0 || batch <= 0 || ldw < d_in) return LRC_EINVAL;
   if (d_out > (int64_t(1) << 20) || d_in > (int64_t(1) << 20) || batch > (int64_t(1) << 16)) return LRC_EINVAL;
@@ -135,51 +145,54 @@ extern "C" lrc_status lrc_whiten_decompose(const float* W, int64_t d_out, int64_
   if (rank > 0 && (left == nullptr || right == nullptr)) return LRC_EINVAL;
   if (Xsum != nullptr && (ldx < d_in || n_x <= 0)) return LRC_EINVAL;
   if (Gsum != nullptr && (ldg < d_out || n_g <= 0)) return LRC_EINVAL;
+  // a covariance per slice lies at a stride that keeps the slices apart
+  if (stride_x < 0 || (Xsum != nullptr && stride_x != 0 && stride_x < d_in * ldx)) return LRC_EINVAL;
+  if (stride_g < 0 || (Gsum != nullptr && stride_g != 0 && stride_g < d_out * ldg)) return LRC_EINVAL;
   if (!(damping >= 0.f) || !(damping < 3.0e38f)) return LRC_EINVAL;
-  const bool hx = Xsum != nullptr, hg = Gsum != nullptr;
-  const size_t need = lrc_whiten_decompose_workspace(d_out, d_in, batch, rank, hx, hg);
+  const int64_t nx = cov_slices(Xsum, stride_x, batch), ng = cov_slices(Gsum, stride_g, batch);
+  const bool hx = nx > 0, hg = ng > 0;
+  const size_t need = decompose_workspace(d_out, d_in, batch, rank, nx, ng);
   if (ws == nullptr || ws_bytes < need) return LRC_EWORKSPACE;
-  hipStream_t st = static_cast<hipStream_t>(stream);
   Carve cv(ws);
-  DWs w = carve_decomp(cv, d_out, d_in, batch, rank, hx, hg);
+  DWs w = carve_decomp(cv, d_out, d_in, batch, rank, nx, ng);
   const int64_t kp = jacobi_padded(k);
   const int64_t mn = d_out * d_in;
-
+  const int64_t sLx = nx > 1 ? d_in * d_in : 0, sLg = ng > 1 ? d_out * d_out : 0;
   fill_i32_kernel<<<unsigned(cdiv(batch, 256)), 256, 0, st>>>(info, batch, 0);
   LRC_LAUNCHED();
-  fill_i32_kernel<<<1, 64, 0, st>>>(w.chol_info, 2, 0);
+  fill_i32_kernel<<<unsigned(cdiv(2 * batch, 256)), 256, 0, st>>>(w.chol_info, 2 * batch, 0);
   LRC_LAUNCHED();
-
   // a2: Cholesky factors of the covariances (a failed pivot is recorded in chol_info and
   // acted on after the Gram, on the device)
-  if (hx) LRC_TRY(cholesky_f32(st, Xsum, ldx, d_in, n_x, damping, w.lx, w.chol_info));
-  if (hg) LRC_TRY(cholesky_f32(st, Gsum, ldg, d_out, n_g, damping, w.lg, w.chol_info + 1));
-
+  for (int64_t c = 0; c < nx; ++c)
+    LRC_TRY(cholesky_f32(st, Xsum + c * stride_x, ldx, d_in, n_x, damping, w.lx + c * sLx, w.chol_info + 2 * c));
+  for (int64_t c = 0; c < ng; ++c)
+    LRC_TRY(cholesky_f32(st, Gsum + c * stride_g, ldg, d_out, n_g, damping, w.lg + c * sLg, w.chol_info + 2 * c + 1));
   // a3: whitening  W~ = L_g^T W L_x
   const float* cur = W;
   int64_t ldc = ldw, scur = stride_w;
   if (hx) {
-    LRC_TRY(gemm_f32(st, GEMM_K_FROM_COL, d_out, d_in, d_in, 1.f, cur, ldc, scur, w.lx, d_in, 0, 0.f, w.wt1, d_in, mn,
-                     batch));
+    LRC_TRY(gemm_f32(st, GEMM_K_FROM_COL, d_out, d_in, d_in, 1.f, cur, ldc, scur, w.lx, d_in, sLx, 0.f, w.wt1, d_in,
+                     mn, batch));
     cur = w.wt1;
     ldc = d_in;
     scur = mn;
   }
   if (hg) {
     float* dst = hx ? w.wt2 : w.wt1;
-    LRC_TRY(gemm_f32(st, GEMM_TA | GEMM_K_FROM_ROW, d_out, d_in, d_out, 1.f, w.lg, d_out, 0, cur, ldc, scur, 0.f, dst,
-                     d_in, mn, batch));
+    LRC_TRY(gemm_f32(st, GEMM_TA | GEMM_K_FROM_ROW, d_out, d_in, d_out, 1.f, w.lg, d_out, sLg, cur, ldc, scur, 0.f,
+                     dst, d_in, mn, batch));
     cur = dst;
     ldc = d_in;
     scur = mn;
   }
-
   // a4: fp64 Gram of the smaller side and its eigendecomposition
   const bool left_side = d_out <= d_in;
   LRC_TRY(gram_f64(st, left_side, d_out, d_in, cur, ldc, scur, w.gram, kp, kp * kp, batch));
   if (hx || hg) {
     const dim3 g(unsigned(std::min<int64_t>(cdiv(k * k, 256), 64)), unsigned(batch));
-    chol_guard_kernel<<<g, 256, 0, st>>>(w.chol_info, int(d_in), w.gram, kp, kp * kp, int(k), info);
+    chol_guard_kernel<<<g, 256, 0, st>>>(w.chol_info, nx > 1 ? 1 : 0, ng > 1 ? 1 : 0, int(d_in), w.gram, kp, kp * kp,
+                                         int(k), info);
     LRC_LAUNCHED();
   }
   const int64_t ncols = std::max<int64_t>(rank, 1);
@@ -188,7 +201,6 @@ extern "C" lrc_status lrc_whiten_decompose(const float* W, int64_t d_out, int64_
   else
     LRC_TRY(jacobi_eig(st, w.gram, k, batch, ncols, sigma, w.qt, info, w.jac));
   if (rank == 0) return LRC_OK;
-
   // a5: back-map to weight space
   for (int64_t b = 0; b < batch; ++b) {
     const float* wb = W + b * stride_w;
@@ -196,15 +208,17 @@ extern "C" lrc_status lrc_whiten_decompose(const float* W, int64_t d_out, int64_
     const float* qb = w.qt + b * rank * k;
     float* lb = left + b * d_out * rank;
     float* rb = right + b * rank * d_in;
+    const float* lgb = hg ? w.lg + b * sLg : nullptr;
+    const float* lxb = hx ? w.lx + b * sLx : nullptr;
     LRC_TRY(transpose_f32(st, qb, k, w.u, rank, rank, k));  // u: k x r (singular vectors as columns)
     if (left_side) {
       // Left = L_g^-T U S^1/2
       LRC_TRY(scale_cols(st, w.u, rank, lb, rank, k, rank, sb, 0));
-      if (hg) LRC_TRY(trsm_lower_t(st, w.lg, d_out, lb, rank, rank));
+      if (hg) LRC_TRY(trsm_lower_t(st, lgb, d_out, lb, rank, rank));
       // Right = (L_g U S^-1/2)^T W
       const float* pu = w.u;
       if (hg) {
-        LRC_TRY(gemm_f32(st, GEMM_K_TO_ROW, d_out, rank, d_out, 1.f, w.lg, d_out, 0, w.u, rank, 0, 0.f, w.p, rank, 0, 1));
+        LRC_TRY(gemm_f32(st, GEMM_K_TO_ROW, d_out, rank, d_out, 1.f, lgb, d_out, 0, w.u, rank, 0, 0.f, w.p, rank, 0, 1));
         pu = w.p;
       }
       LRC_TRY(scale_cols(st, pu, rank, w.p, rank, d_out, rank, sb, 1));
@@ -212,12 +226,12 @@ extern "C" lrc_status lrc_whiten_decompose(const float* W, int64_t d_out, int64_
     } else {
       // Right = (L_x^-T V S^1/2)^T
       LRC_TRY(scale_cols(st, w.u, rank, w.p, rank, k, rank, sb, 0));
-      if (hx) LRC_TRY(trsm_lower_t(st, w.lx, d_in, w.p, rank, rank));
+      if (hx) LRC_TRY(trsm_lower_t(st, lxb, d_in, w.p, rank, rank));
       LRC_TRY(transpose_f32(st, w.p, rank, rb, d_in, d_in, rank));
       // Left = W (L_x V S^-1/2)
       const float* pv = w.u;
       if (hx) {
-        LRC_TRY(gemm_f32(st, GEMM_K_TO_ROW, d_in, rank, d_in, 1.f, w.lx, d_in, 0, w.u, rank, 0, 0.f, w.p, rank, 0, 1));
+        LRC_TRY(gemm_f32(st, GEMM_K_TO_ROW, d_in, rank, d_in, 1.f, lxb, d_in, 0, w.u, rank, 0, 0.f, w.p, rank, 0, 1));
         pv = w.p;
       }
       LRC_TRY(scale_cols(st, pv, rank, w.p, rank, d_in, rank, sb, 1));
@@ -225,4 +239,38 @@ extern "C" lrc_status lrc_whiten_decompose(const float* W, int64_t d_out, int64_
     }
   }
   return LRC_OK;
+}
+
+}  // namespace
+}  // namespace lrc
+
+extern "C" size_t lrc_whiten_decompose_workspace(int64_t d_out, int64_t d_in, int64_t batch, int64_t rank, int has_x,
+                                                 int has_g) {
+  return decompose_workspace(d_out, d_in, batch, rank, has_x != 0 ? 1 : 0, has_g != 0 ? 1 : 0);
+}
+
+extern "C" size_t lrc_whiten_decompose_strided_workspace(int64_t d_out, int64_t d_in, int64_t batch, int64_t rank,
+                                                         int64_t x_slices, int64_t g_slices) {
+  if (x_slices < 0 || g_slices < 0 || (x_slices > 1 && x_slices != batch) || (g_slices > 1 && g_slices != batch))
+    return 0;
+  return decompose_workspace(d_out, d_in, batch, rank, x_slices, g_slices);
+}
+
+extern "C" lrc_status lrc_whiten_decompose(const float* W, int64_t d_out, int64_t d_in, int64_t ldw, int64_t batch,
+                                           int64_t stride_w, const float* Xsum, int64_t ldx, int64_t n_x,
+                                           const float* Gsum, int64_t ldg, int64_t n_g, int64_t rank, float damping,
+                                           float* sigma, float* left, float* right, int32_t* info, void* ws,
+                                           size_t ws_bytes, void* stream) {
+  return decompose(W, d_out, d_in, ldw, batch, stride_w, Xsum, ldx, 0, n_x, Gsum, ldg, 0, n_g, rank, damping, sigma,
+                   left, right, info, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+extern "C" lrc_status lrc_whiten_decompose_strided(const float* W, int64_t d_out, int64_t d_in, int64_t ldw,
+                                                   int64_t batch, int64_t stride_w, const float* Xsum, int64_t ldx,
+                                                   int64_t stride_x, int64_t n_x, const float* Gsum, int64_t ldg,
+                                                   int64_t stride_g, int64_t n_g, int64_t rank, float damping,
+                                                   float* sigma, float* left, float* right, int32_t* info, void* ws,
+                                                   size_t ws_bytes, void* stream) {
+  return decompose(W, d_out, d_in, ldw, batch, stride_w, Xsum, ldx, stride_x, n_x, Gsum, ldg, stride_g, n_g, rank,
+                   damping, sigma, left, right, info, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }

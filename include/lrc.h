@@ -147,6 +147,29 @@ size_t lrc_whiten_decompose_workspace(int64_t d_out, int64_t d_in, int64_t batch
                                       int has_x, int has_g);
 
 /*
+ * lrc_whiten_decompose_strided -- lrc_whiten_decompose for a batch of slices that may
+ * each have their own covariances (independent layers, each calibrated on its own
+ * activations and gradients; LASER Methodology 1 applied layer by layer, as the global
+ * allocation of Methodology 2 then pools them).  Slice b is whitened with
+ * Xsum + b*stride_x and Gsum + b*stride_g; a stride of 0 shares one sum over the batch
+ * (stride_x = stride_g = 0 is exactly lrc_whiten_decompose).  A per-slice sum needs
+ * stride_x >= d_in*ldx (stride_g >= d_out*ldg); n_x and n_g are common to the slices.
+ * Outputs, info codes and asynchrony as lrc_whiten_decompose; a covariance that is not
+ * positive definite is reported in the info of the slices it belongs to.  Every slice
+ * gives the same bits as a call of its own.  Workspace: x_slices / g_slices are 0 (no
+ * such sum), 1 (shared) or batch (one per slice); 0 is returned for other values.
+ */
+lrc_status lrc_whiten_decompose_strided(const float* W, int64_t d_out, int64_t d_in, int64_t ldw,
+                                        int64_t batch, int64_t stride_w,
+                                        const float* Xsum, int64_t ldx, int64_t stride_x, int64_t n_x,
+                                        const float* Gsum, int64_t ldg, int64_t stride_g, int64_t n_g,
+                                        int64_t rank, float damping,
+                                        float* sigma, float* left, float* right, int32_t* info,
+                                        void* ws, size_t ws_bytes, void* stream);
+size_t lrc_whiten_decompose_strided_workspace(int64_t d_out, int64_t d_in, int64_t batch, int64_t rank,
+                                              int64_t x_slices, int64_t g_slices);
+
+/*
  * lrc_score_components -- importance score of every singular component.
  * LASER Methodology 2 (empirical-Fisher importance score): a component's contribution
  * to the empirical-Fisher quadratic loss, combining its size with its alignment to the

@@ -83,6 +83,31 @@ def test_whiten_decompose_validation(lib):
     assert call(ws_bytes=need - 1) == EWORKSPACE
 
 
+def test_whiten_decompose_strided_validation(lib):
+    f = lib.lrc_whiten_decompose_strided
+    ok = dict(W=FAKE, d_out=8, d_in=6, ldw=6, batch=3, stride_w=48, X=FAKE, ldx=6, sx=36, nx=10, G=FAKE, ldg=8,
+              sg=64, ng=10, rank=3, damping=0.0, sigma=FAKE, left=FAKE, right=FAKE, info=FAKE)
+
+    def call(ws_bytes=1 << 40, **over):
+        a = dict(ok, **over)
+        return f(a["W"], a["d_out"], a["d_in"], a["ldw"], a["batch"], a["stride_w"], a["X"], a["ldx"], a["sx"],
+                 a["nx"], a["G"], a["ldg"], a["sg"], a["ng"], a["rank"], a["damping"], a["sigma"], a["left"],
+                 a["right"], a["info"], FAKE, ws_bytes, None)
+
+    assert call(sx=35) == EINVAL             # per-slice X sums overlap
+    assert call(sg=63) == EINVAL             # per-slice G sums overlap
+    assert call(sx=-36) == EINVAL
+    assert call(ldx=5) == EINVAL
+    assert call(G=None, ldg=0, ng=0, nx=0) == EINVAL
+    ws = lib.lrc_whiten_decompose_strided_workspace
+    per, shared = ws(8, 6, 3, 3, 3, 3), ws(8, 6, 3, 3, 1, 1)
+    assert per > shared > 0                  # one Cholesky factor per slice
+    assert shared == lib.lrc_whiten_decompose_workspace(8, 6, 3, 3, 1, 1)
+    assert ws(8, 6, 3, 3, 2, 1) == 0 and ws(8, 6, 3, 3, -1, 0) == 0   # slices: 0, 1 or batch
+    assert call(ws_bytes=per - 1) == EWORKSPACE
+    assert call(sx=0, sg=0, ws_bytes=shared - 1) == EWORKSPACE
+
+
 def test_score_components_validation(lib):
     f = lib.lrc_score_components
     # (A, B, dt, n, d_in, d_out, left, right, sigma, k, flags, accumulate, finalize, n_total, scores, info,

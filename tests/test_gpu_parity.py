@@ -314,6 +314,60 @@ def test_decompose_batched_ragged_two_sided_large_grid(lrc):
         _check_decomposition(case, rank)
 
 
+@pytest.mark.parametrize("d_out,d_in,rank,two_sided", [(400, 520, 50, False), (150, 100, 30, True)])
+def test_decompose_slices_with_their_own_covariances(lrc, d_out, d_in, rank, two_sided, monkeypatch):
+    """Independent layers in one call: slice b is whitened with its own X (and G) sums.
+    Every slice gives the same bits as a call of its own on the same eigensolver route
+    (tridiagonal at k = 400; block Jacobi, forced for the single calls too, at k = 100),
+    and one slice is checked against the oracle."""
+    monkeypatch.setenv("LRC_EIGENSOLVER", "tridiag" if min(d_out, d_in) >= 384 else "jacobi")
+    batch, n = 3, 2500
+    streams_a = [synth.activation_stream(n, d_in, 1.0 + 0.1 * b, 80 + b, dtype=torch.bfloat16) for b in range(batch)]
+    streams_b = [synth.activation_stream(n, d_out, 1.3, 90 + b, dtype=torch.bfloat16) for b in range(batch)]
+    w3 = torch.stack([synth.weight(d_out, d_in, 95 + b) for b in range(batch)]).to(dev())
+    xs = torch.zeros(batch, d_in, d_in, device=dev())
+    gs = torch.zeros(batch, d_out, d_out, device=dev()) if two_sided else None
+    for b in range(batch):
+        lrc.lrc_accumulate_cov(streams_a[b].to(dev()), xs[b])
+        if two_sided:
+            lrc.lrc_accumulate_cov(streams_b[b].to(dev()), gs[b])
+    sig, left, right, info = lrc.lrc_whiten_decompose(w3, rank, xs, n, gs, n if two_sided else 0)
+    assert torch.all(info == 0)
+    for b in range(batch):
+        s1, l1, r1, i1 = lrc.lrc_whiten_decompose(w3[b], rank, xs[b], n, gs[b] if two_sided else None,
+                                                 n if two_sided else 0)
+        assert int(i1[0]) == 0
+        assert torch.equal(sig[b], s1) and torch.equal(left[b], l1) and torch.equal(right[b], r1), b
+    an = to_np(streams_a[2])
+    bn = to_np(streams_b[2]) if two_sided else None
+    ref = oracle.whiten_decompose(to_np(w3[2]), oracle.covariance_sum(an), n,
+                                  oracle.covariance_sum(bn) if two_sided else None, n if two_sided else None,
+                                  rank=rank)
+    case = dict(a=an, b=bn, w=to_np(w3[2]), sig=to_np(sig[2]), left=to_np(left[2]), right=to_np(right[2]),
+                info=to_np(info[2:3]), ref=ref, n=n)
+    _check_decomposition(case, rank)
+
+
+def test_decompose_slices_own_covariance_not_positive_definite(lrc, monkeypatch):
+    """A per-slice covariance that is not positive definite is reported in that slice's
+    info only (the first failing pivot); the other slices are unaffected, bit for bit
+    (single calls on the batch's block-Jacobi route)."""
+    monkeypatch.setenv("LRC_EIGENSOLVER", "jacobi")
+    batch, d, n, rank = 3, 96, 1000, 12
+    xs = torch.zeros(batch, d, d, device=dev())
+    for b in range(batch):
+        lrc.lrc_accumulate_cov(synth.activation_stream(n, d, 1.0, 100 + b, dtype=torch.bfloat16).to(dev()), xs[b])
+    xs[1, 40, :] = 0.0
+    xs[1, :, 40] = 0.0          # pivot 41 of slice 1 is zero
+    w3 = torch.stack([synth.weight(64, d, 110 + b) for b in range(batch)]).to(dev())
+    sig, left, right, info = lrc.lrc_whiten_decompose(w3, rank, xs, n)
+    assert to_np(info).tolist() == [0, 41, 0]
+    for b in (0, 2):
+        s1, l1, r1, i1 = lrc.lrc_whiten_decompose(w3[b], rank, xs[b], n)
+        assert int(i1[0]) == 0
+        assert torch.equal(sig[b], s1) and torch.equal(left[b], l1) and torch.equal(right[b], r1)
+
+
 def test_decompose_identity_covariances_is_plain_svd(lrc, solver):
     """X = G = I (identity sums with count 1): plain truncated SVD of W (Eckart-Young)."""
     w = synth.weight(96, 130, 3)
