@@ -7,11 +7,14 @@ per-component K-FAC scores (this workload has no gradients) and the global
 sort-and-truncate at the budget of rank 1024.  Inputs are resident in HBM before the
 timed region.  The K timed steps are independent layers spread over --streams HIP
 streams (default 4 on the 8 hardware queues the bench asks HIP for; each stream has its
-own covariance buffer and its own host thread that enqueues its steps), so four layers
-are in flight at a time; `value` is K / the wall time of the region.  The same K steps one after another on one stream give
+own covariance buffers and its own host thread that enqueues its steps); each stream
+decomposes --layers-per-call of its layers per call (default 3, each layer with its own
+covariance), so up to twelve layers are in flight at a time; `value` is K / the wall time of
+the region.  The same K steps one after another on one stream, one layer per call, give
 `value_one_stream` (one layer's latency).  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--streams S] [--no-cpu-baseline] [--no-secondary]
+    python bench.py [--steps K] [--warmup W] [--streams S] [--layers-per-call L]
+                    [--no-cpu-baseline] [--no-secondary]
     python bench.py --only syrk|tridiag|fisher|alloc|qaw|ffn-decode [--copy-probe-mib M]
 
 The --only modes run one part of the path a few times (and, with --copy-probe-mib, a
@@ -89,6 +92,8 @@ def parse():
     p.add_argument("--streams", type=int, default=None,
                    help="HIP streams the timed steps run on, each fed by its own host thread (independent layers "
                         "in flight); default: one less than the hardware queues, at most 4")
+    p.add_argument("--layers-per-call", type=int, default=3,
+                   help="independent layers a stream decomposes per call (one covariance each)")
     p.add_argument("--hw-queues", type=int, default=8,
                    help="hardware queues HIP gives this process (GPU_MAX_HW_QUEUES, set before HIP starts)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -743,9 +748,12 @@ def main():
     if args.streams is None:
         args.streams = min(4, max(1, int(os.environ["GPU_MAX_HW_QUEUES"]) - 1))
     ns = max(1, args.streams)
+    lpc = max(1, args.layers_per_call)
     streams = [torch.cuda.Stream() for _ in range(ns)]
-    covs = [torch.empty(d, d, dtype=torch.float32, device=dev) for _ in range(ns)]
-    cov = covs[0]
+    # per stream: one covariance buffer per layer of a call
+    covs = [torch.empty(lpc, d, d, dtype=torch.float32, device=dev) for _ in range(ns)]
+    cov = covs[0][0]
+    wb = w.unsqueeze(0).expand(lpc, d, d).contiguous()
     offs = torch.tensor([0, d], dtype=torch.int64, device=dev)
     cost = torch.tensor([2 * d], dtype=torch.int64, device=dev)
     budget = r * 2 * d
@@ -760,18 +768,37 @@ def main():
         scores, _ = lrc.lrc_score_components(sigma=sig, mode="kfac")
         return lrc.lrc_allocate_ranks(scores, offs, cost, budget), info
 
-    def run_steps(k_steps, n_streams):
-        """k_steps whole steps: stream i (its own covariance buffer; the layers are
-        independent) runs steps i, i + n_streams, ..., enqueued by a host thread of its own
-        (an enqueue blocks while the stream's hardware queue is full, which would starve the
-        other streams if one thread fed them all); returns the last outputs of each."""
+    def layers(cs, g):
+        """g whole steps (independent layers) in one decomposition call: each layer's
+        tokens into its own covariance, the g whitened decompositions together (the
+        tridiagonal reductions share their launches), then each layer's scores and
+        allocation."""
+        if g == 1:
+            return step(cs[0])
+        cs[:g].zero_()
+        for j in range(g):
+            lrc.lrc_accumulate_cov(a, cs[j])
+        sig, left, right, info = lrc.lrc_whiten_decompose(wb[:g], r, cs[:g], n)
+        out = None
+        for j in range(g):
+            scores, _ = lrc.lrc_score_components(sigma=sig[j].contiguous(), mode="kfac")
+            out = lrc.lrc_allocate_ranks(scores, offs, cost, budget)
+        return out, info
+
+    def run_steps(k_steps, n_streams, per_call=1):
+        """k_steps whole steps: stream i (its own covariance buffers; the layers are
+        independent) runs steps i, i + n_streams, ..., per_call of them per decomposition
+        call, enqueued by a host thread of its own (an enqueue blocks while the stream's
+        hardware queue is full, which would starve the other streams if one thread fed
+        them all); returns the last outputs of each."""
         last = {}
 
         def feed(i):
             torch.cuda.set_device(dev)
+            mine = len(range(i, k_steps, n_streams))
             with torch.cuda.stream(streams[i]):
-                for _ in range(i, k_steps, n_streams):
-                    last[i] = step(covs[i])
+                for j0 in range(0, mine, per_call):
+                    last[i] = layers(covs[i], min(per_call, mine - j0))
 
         if n_streams == 1:
             feed(0)
@@ -781,19 +808,19 @@ def main():
         return last
 
     progress("inputs resident")
-    run_steps(max(args.warmup, ns), ns)
+    run_steps(max(args.warmup, ns * lpc), ns, lpc)
     torch.cuda.synchronize()
     # timed region: K whole steps issued round robin on the streams, nothing else queued;
     # the clock stops when every stream has drained
     t0 = time.perf_counter()
-    last = run_steps(args.steps, ns)
+    last = run_steps(args.steps, ns, lpc)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     for out, info in last.values():
-        assert int(info[0]) == 0 and int(out[4][0]) == 0
+        assert int(info.max()) == 0 and int(info.min()) == 0 and int(out[4][0]) == 0
     n_kept = int(last[0][0][1][0])
     ms = 1e3 * elapsed / args.steps
-    progress(f"{args.steps} steps on {ns} stream(s): {ms:.2f} ms per step")
+    progress(f"{args.steps} steps on {ns} stream(s), {lpc} per call: {ms:.2f} ms per step")
     # the same K steps one after another on one stream: the latency of one layer
     t0 = time.perf_counter()
     run_steps(args.steps, 1)
@@ -850,7 +877,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 3),
-        "steps_in_flight": ns,
+        "steps_in_flight": ns * lpc,
         "ms_per_step_one_stream": round(ms_one, 3),
         "value_one_stream": round(1e3 / ms_one, 4),
         "higher_is_better": True,
@@ -860,7 +887,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"attention projection W {d}x{d} fp32, {n} bf16 calibration tokens "
                                f"(power-law spectrum, 1% outlier channels x20), activation-only whitening, rank {r}",
-                   "tokens_per_layer": n, "d": d, "rank": r, "streams": ns,
+                   "tokens_per_layer": n, "d": d, "rank": r, "streams": ns, "layers_per_call": lpc,
                    "hw_queues": int(os.environ["GPU_MAX_HW_QUEUES"])},
         "cov_tokens_per_s": round(n / (cov_ms * 1e-3), 1),
         "cov_ms": round(cov_ms, 4),
