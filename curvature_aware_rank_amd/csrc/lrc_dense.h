@@ -31,9 +31,9 @@ lrc_status jacobi_eig(hipStream_t st, double* A, int64_t k, int64_t batch, int64
 
 // Symmetric eigendecompositions of a batch of fp64 k x k Grams (lower triangles of A,
 // slice b at A + b sA, leading dimension lda; destroyed): Householder tridiagonalisation
-// of all slices at once (every launch covers the batch), then per slice Sturm multisection
-// for all eigenvalues, inverse iteration for the ncols largest and the blocked
-// back-transformation.  Outputs as jacobi_eig: sigma slice b at sigma + b s_sigma, the
+// of all slices at once (every launch covers the batch), Sturm multisection for all
+// eigenvalues of every slice (one launch for the batch), then per slice inverse iteration
+// for the ncols largest and the blocked back-transformation.  Outputs as jacobi_eig: sigma slice b at sigma + b s_sigma, the
 // eigenvectors (ncols x k rows) at Qt + b s_qt.  Enqueues a fixed amount of work and never
 // waits.  A must be 16-byte aligned with an even lda and an even sA, and lda > k when k is
 // odd (LRC_EINVAL otherwise).

@@ -838,7 +838,13 @@ __global__ __launch_bounds__(256) void tri_tail_kernel(double* __restrict__ A, i
 // ---- 2. eigenvalues of T
 // bounds: [0] gl, [1] gu, [2] pivmin, [3] ||T|| (max |Gershgorin end|)
 __global__ __launch_bounds__(256) void tri_bounds_kernel(const double* __restrict__ d, const double* __restrict__ e,
-                                                         int n, double* __restrict__ bounds) {
+                                                         int n, double* __restrict__ bounds, int64_t wsi) {
+  {   // slice blockIdx.y of a batch: d, e in its loop block, 4 bounds per slice
+    const int64_t it = blockIdx.y;
+    d += it * wsi;
+    e += it * wsi;
+    bounds += 4 * it;
+  }
   __shared__ double rl[256], rh[256], re[256];
   const int tid = threadIdx.x;
   double lo = 1e300, hi = -1e300, em = 0.0;
@@ -883,7 +889,14 @@ __global__ __launch_bounds__(256) void tri_bounds_kernel(const double* __restric
 // down).
 __global__ __launch_bounds__(256) void tri_bisect_kernel(const double* __restrict__ d, const double* __restrict__ e,
                                                          int n, const double* __restrict__ bounds,
-                                                         double* __restrict__ lam) {
+                                                         double* __restrict__ lam, int64_t wsi) {
+  {   // slice blockIdx.y of a batch: d, e in its loop block, its bounds and n eigenvalues
+    const int64_t it = blockIdx.y;
+    d += it * wsi;
+    e += it * wsi;
+    bounds += 4 * it;
+    lam += it * int64_t(n);
+  }
   __shared__ double sd[BIS_STAGE], se2[BIS_STAGE];
   const int tid = threadIdx.x;
   const int grp = tid >> 4, pt = tid & 15;
@@ -1783,7 +1796,9 @@ __global__ __launch_bounds__(256) void bt_update_kernel(const double* __restrict
 }
 
 // ---- outputs: sigma (all k, descending) and Qt rows = eigenvectors, sign-fixed, fp32
-__global__ void tri_sigma_kernel(const double* __restrict__ lam, int n, float* __restrict__ sigma) {
+__global__ void tri_sigma_kernel(const double* __restrict__ lam, int n, float* __restrict__ sigma, int64_t s_sigma) {
+  lam += int64_t(blockIdx.y) * n;     // slice blockIdx.y
+  sigma += int64_t(blockIdx.y) * s_sigma;
   const int m = blockIdx.x * blockDim.x + threadIdx.x;
   if (m < n) sigma[m] = float(sqrt(fmax(lam[n - 1 - m], 0.0)));
 }
@@ -1826,6 +1841,7 @@ struct TWs {
   // these pointers into slice 0's block
   double *P, *S, *SV, *SW, *npart, *x0, *xv, *d, *e, *tau, *Wp;
   int64_t istride;
+  int64_t lamstride;   // eigenvalues per slice (lam holds every slice's, bounds 4 each)
   // the later stages (one slice at a time)
   double *lam, *bounds, *U, *Z, *nrm, *scl, *Gp, *T, *Yp, *Yr, *Y2;
   int *clen, *nbig, *big;
@@ -1863,8 +1879,10 @@ TWs carve_tri(Carve& cv, int64_t n, int64_t ncols, int64_t batch) {
   w.e = loop + oe;
   w.tau = loop + otau;
   w.Wp = loop + oWp;
-  w.lam = cv.take<double>(size_t(n));
-  w.bounds = cv.take<double>(4);
+  // eigenvalues and spectrum bounds of every slice (found for the whole batch at once)
+  w.lamstride = n;
+  w.lam = cv.take<double>(size_t(std::max<int64_t>(batch, 1) * n));
+  w.bounds = cv.take<double>(size_t(4 * std::max<int64_t>(batch, 1)));
   w.U = cv.take<double>(size_t(4 * n * ncols));
   w.piv = cv.take<uint8_t>(size_t(n * ncols));
   w.Z = cv.take<double>(size_t(n * ncols));
@@ -1975,25 +1993,18 @@ static TWs tri_slice(const TWs& w0, int64_t b) {
   w.e += o;
   w.tau += o;
   w.Wp += o;
+  w.lam += b * w.lamstride;
+  w.bounds += 4 * b;
   return w;
 }
 
-// eigenvalues, the wanted eigenvectors and their back-transformation for one reduced
-// slice: A holds its reflectors, w.d / w.e / w.tau its tridiagonal and scalars
+// the wanted eigenvectors and their back-transformation for one reduced slice whose
+// eigenvalues are known: A holds its reflectors, w.d / w.e / w.tau its tridiagonal and
+// scalars, w.lam / w.bounds its eigenvalues and spectrum bounds
 static lrc_status tri_solve_slice(hipStream_t st, double* A, int n, int64_t lda, int ncols, const TWs& w,
-                                  float* sigma, float* Qt) {
-  // 2. eigenvalues
-  tri_bounds_kernel<<<1, 256, 0, st>>>(w.d, w.e, n, w.bounds);
-  LRC_LAUNCHED();
-  {
-    ProfScope scope("tri_bisect_kernel", st, 0.0, 0.0);
-    tri_bisect_kernel<<<unsigned(cdiv(n, 16)), 256, 0, st>>>(w.d, w.e, n, w.bounds, w.lam);
-    LRC_LAUNCHED();
-  }
-  tri_sigma_kernel<<<unsigned(cdiv(n, 256)), 256, 0, st>>>(w.lam, n, sigma);
-  LRC_LAUNCHED();
-
-  // 3. clusters and inverse iteration
+                                  float* Qt) {
+  // 3. clusters and inverse iteration (the eigenvalues of every slice are found first,
+  // for the whole batch at once)
   zero_int_kernel<<<1, 64, 0, st>>>(w.nbig, 1);
   LRC_LAUNCHED();
   tri_cluster_kernel<<<unsigned(cdiv(ncols, 256)), 256, 0, st>>>(w.lam, n, ncols, w.bounds, w.clen, w.nbig, w.big);
@@ -2080,9 +2091,25 @@ lrc_status tridiag_eig(hipStream_t st, double* A, int64_t sA, int64_t k, int64_t
   // 1. tridiagonalisation of every slice, one launch per step for the batch
   LRC_TRY(tri_reduce(st, A, sA, n, lda, int(batch), w0));
 
-  // 2.-4. the later stages slice after slice, through one set of arrays
+  // 2. all eigenvalues of every slice: one launch per kernel for the batch (each
+  // slice's bisection is latency-bound on one wave per SIMD, so the slices run side by
+  // side at the cost of one)
+  const unsigned nb = unsigned(batch);
+  tri_bounds_kernel<<<dim3(1, nb), 256, 0, st>>>(w0.d, w0.e, n, w0.bounds, w0.istride);
+  LRC_LAUNCHED();
+  {
+    ProfScope scope("tri_bisect_kernel", st, 0.0, 0.0);
+    tri_bisect_kernel<<<dim3(unsigned(cdiv(n, 16)), nb), 256, 0, st>>>(w0.d, w0.e, n, w0.bounds, w0.lam,
+                                                                       w0.istride);
+    LRC_LAUNCHED();
+  }
+  tri_sigma_kernel<<<dim3(unsigned(cdiv(n, 256)), nb), 256, 0, st>>>(w0.lam, n, sigma, s_sigma);
+  LRC_LAUNCHED();
+
+  // 3.-4. eigenvectors and their back-transformation slice after slice, through one set
+  // of arrays
   for (int64_t b = 0; b < batch; ++b)
-    LRC_TRY(tri_solve_slice(st, A + b * sA, n, lda, ncols, tri_slice(w0, b), sigma + b * s_sigma, Qt + b * s_qt));
+    LRC_TRY(tri_solve_slice(st, A + b * sA, n, lda, ncols, tri_slice(w0, b), Qt + b * s_qt));
   return LRC_OK;
 }
 
