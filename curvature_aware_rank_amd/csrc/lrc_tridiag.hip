@@ -969,6 +969,14 @@ __global__ __launch_bounds__(256) void tri_bisect_kernel(const double* __restric
 __global__ void tri_cluster_kernel(const double* __restrict__ lam, int n, int ncols,
                                    const double* __restrict__ bounds, int* __restrict__ clen,
                                    int* __restrict__ nbig, int* __restrict__ big) {
+  {   // slice blockIdx.y of a batch (every array holds one block per slice)
+    const int64_t it = blockIdx.y;
+    lam += it * n;
+    bounds += 4 * it;
+    clen += it * ncols;
+    nbig += it;
+    big += it * ncols;
+  }
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= ncols) return;
   const double ctol = CL_TOL * bounds[3];
@@ -1044,7 +1052,19 @@ __global__ __launch_bounds__(64) void tri_inviter_a_kernel(const double* __restr
                                                            const double* __restrict__ bounds,
                                                            const int* __restrict__ clen,
                                                            double* __restrict__ Rt, uint8_t* __restrict__ PVt,
-                                                           double* __restrict__ Z) {
+                                                           double* __restrict__ Z, int64_t wsi) {
+  {   // slice blockIdx.y of a batch: d, e in its loop block, the rest one block per slice
+    const int64_t it = blockIdx.y;
+    const int64_t nc = int64_t(n) * ncols;
+    d += it * wsi;
+    e += it * wsi;
+    lam += it * n;
+    bounds += 4 * it;
+    clen += it * ncols;
+    Rt += it * 4 * nc;
+    PVt += it * nc;
+    Z += it * nc;
+  }
   const int lane = threadIdx.x;
   const int jr = blockIdx.x * 64 + lane;
   const int jv = min(jr, ncols - 1);   // lanes past the last vector repeat it
@@ -1244,6 +1264,12 @@ __device__ void inv_scale(double* __restrict__ z, int64_t zs, int n, double sc) 
 // first solve's back-substitution, one wave per vector; its squared norm to nrm[j]
 __global__ __launch_bounds__(64) void tri_inviter_u_kernel(int n, int ncols, const double* __restrict__ Rt,
                                                            double* __restrict__ Z, double* __restrict__ nrm) {
+  {   // slice blockIdx.y of a batch
+    const int64_t it = blockIdx.y, nc = int64_t(n) * ncols;
+    Rt += it * 4 * nc;
+    Z += it * nc;
+    nrm += it * ncols;
+  }
   __shared__ double s_in[2][CHL][4];
   __shared__ double s_z[2][CHL];
   __shared__ double s_out[CHL];
@@ -1262,6 +1288,13 @@ __global__ __launch_bounds__(64) void tri_inviter_u_kernel(int n, int ncols, con
 __global__ __launch_bounds__(64) void tri_inviter_o_kernel(int n, int ncols, int final, const int* __restrict__ clen,
                                                            double* __restrict__ Z, const double* __restrict__ nrm,
                                                            double* __restrict__ scl) {
+  {   // slice blockIdx.y of a batch
+    const int64_t it = blockIdx.y;
+    clen += it * ncols;
+    Z += it * int64_t(n) * ncols;
+    nrm += it * ncols;
+    scl += it * ncols;
+  }
   const int j = blockIdx.x;
   const int len = clen[j];
   if (len == 0 || len > CL_MAX || (len == 1 && !final)) return;
@@ -1329,6 +1362,14 @@ __global__ __launch_bounds__(OB_T) void tri_inviter_obig_kernel(int n, int ncols
                                                                const int* __restrict__ nbig,
                                                                const int* __restrict__ big, double* __restrict__ Z,
                                                                double* __restrict__ scl) {
+  {   // slice blockIdx.y of a batch
+    const int64_t it = blockIdx.y;
+    clen += it * ncols;
+    nbig += it;
+    big += it * ncols;
+    Z += it * int64_t(n) * ncols;
+    scl += it * ncols;
+  }
   __shared__ double part[OB_W][OB_CH];
   __shared__ double dots[OB_CH];
   __shared__ double red[OB_W];
@@ -1411,6 +1452,14 @@ __global__ __launch_bounds__(64) void tri_inviter_s_kernel(int n, int ncols, con
                                                            const double* __restrict__ Rt,
                                                            const uint8_t* __restrict__ PVt,
                                                            double* __restrict__ Z, double* __restrict__ nrm) {
+  {   // slice blockIdx.y of a batch
+    const int64_t it = blockIdx.y, nc = int64_t(n) * ncols;
+    clen += it * ncols;
+    Rt += it * 4 * nc;
+    PVt += it * nc;
+    Z += it * nc;
+    nrm += it * ncols;
+  }
   __shared__ double s_in[2][CHL][4];
   __shared__ double s_z[2][CHL];
   __shared__ double s_out[CHL];
@@ -1842,6 +1891,7 @@ struct TWs {
   double *P, *S, *SV, *SW, *npart, *x0, *xv, *d, *e, *tau, *Wp;
   int64_t istride;
   int64_t lamstride;   // eigenvalues per slice (lam holds every slice's, bounds 4 each)
+  int64_t ncols;       // eigenvectors per slice
   // the later stages (one slice at a time)
   double *lam, *bounds, *U, *Z, *nrm, *scl, *Gp, *T, *Yp, *Yr, *Y2;
   int *clen, *nbig, *big;
@@ -1881,21 +1931,24 @@ TWs carve_tri(Carve& cv, int64_t n, int64_t ncols, int64_t batch) {
   w.Wp = loop + oWp;
   // eigenvalues and spectrum bounds of every slice (found for the whole batch at once)
   w.lamstride = n;
+  w.ncols = ncols;
   w.lam = cv.take<double>(size_t(std::max<int64_t>(batch, 1) * n));
   w.bounds = cv.take<double>(size_t(4 * std::max<int64_t>(batch, 1)));
-  w.U = cv.take<double>(size_t(4 * n * ncols));
-  w.piv = cv.take<uint8_t>(size_t(n * ncols));
-  w.Z = cv.take<double>(size_t(n * ncols));
+  // inverse iteration: one block of each array per slice (the batch is solved at once)
+  const int64_t nbat = std::max<int64_t>(batch, 1);
+  w.U = cv.take<double>(size_t(nbat * 4 * n * ncols));
+  w.piv = cv.take<uint8_t>(size_t(nbat * n * ncols));
+  w.Z = cv.take<double>(size_t(nbat * n * ncols));
   w.Gp = cv.take<double>(size_t(ngroups * ngc * BW * BW));
   w.T = cv.take<double>(size_t(ngroups * BW * BW));
   w.Yp = cv.take<double>(size_t(nbc * BW * ncols));
   w.Yr = cv.take<double>(size_t(BW * ncols));
   w.Y2 = cv.take<double>(size_t(BW * ncols));
-  w.nrm = cv.take<double>(size_t(ncols));
-  w.scl = cv.take<double>(size_t(ncols));
-  w.clen = cv.take<int>(size_t(ncols));
-  w.nbig = cv.take<int>(1);
-  w.big = cv.take<int>(size_t(ncols));
+  w.nrm = cv.take<double>(size_t(nbat * ncols));
+  w.scl = cv.take<double>(size_t(nbat * ncols));
+  w.clen = cv.take<int>(size_t(nbat * ncols));
+  w.nbig = cv.take<int>(size_t(nbat));
+  w.big = cv.take<int>(size_t(nbat * ncols));
   return w;
 }
 
@@ -1995,48 +2048,23 @@ static TWs tri_slice(const TWs& w0, int64_t b) {
   w.Wp += o;
   w.lam += b * w.lamstride;
   w.bounds += 4 * b;
+  const int64_t nc = w.lamstride * w.ncols;
+  w.U += b * 4 * nc;
+  w.piv += b * nc;
+  w.Z += b * nc;
+  w.nrm += b * w.ncols;
+  w.scl += b * w.ncols;
+  w.clen += b * w.ncols;
+  w.nbig += b;
+  w.big += b * w.ncols;
   return w;
 }
 
-// the wanted eigenvectors and their back-transformation for one reduced slice whose
-// eigenvalues are known: A holds its reflectors, w.d / w.e / w.tau its tridiagonal and
-// scalars, w.lam / w.bounds its eigenvalues and spectrum bounds
+// the back-transformation of one reduced slice's eigenvectors (found by inverse iteration
+// for the whole batch): A holds its reflectors, w.tau its scalars, w.Z / w.scl its
+// eigenvectors of T and their pending scales
 static lrc_status tri_solve_slice(hipStream_t st, double* A, int n, int64_t lda, int ncols, const TWs& w,
                                   float* Qt) {
-  // 3. clusters and inverse iteration (the eigenvalues of every slice are found first,
-  // for the whole batch at once)
-  zero_int_kernel<<<1, 64, 0, st>>>(w.nbig, 1);
-  LRC_LAUNCHED();
-  tri_cluster_kernel<<<unsigned(cdiv(ncols, 256)), 256, 0, st>>>(w.lam, n, ncols, w.bounds, w.clen, w.nbig, w.big);
-  LRC_LAUNCHED();
-  {
-    ProfScope scope("tri_inviter_a_kernel", st, 0.0, 0.0);
-    tri_inviter_a_kernel<<<unsigned(cdiv(ncols, 64)), 64, 0, st>>>(w.d, w.e, n, w.lam, ncols, w.bounds, w.clen, w.U,
-                                                                    w.piv, w.Z);
-    LRC_LAUNCHED();
-  }
-  {
-    // the solve and orthogonalisation launches together; clusters longer than CL_MAX
-    // (at most ncols / (CL_MAX + 1) of them) get a workgroup each
-    ProfScope scope("tri_inviter_u_o_s_kernels", st, 0.0, 0.0);
-    const int max_big = ncols / (CL_MAX + 1);
-    tri_inviter_u_kernel<<<unsigned(ncols), 64, 0, st>>>(n, ncols, w.U, w.Z, w.nrm);
-    LRC_LAUNCHED();
-    for (int fin = 0; fin < 2; ++fin) {
-      if (fin == 1) {
-        tri_inviter_s_kernel<<<unsigned(ncols), 64, 0, st>>>(n, ncols, w.clen, w.U, w.piv, w.Z, w.nrm);
-        LRC_LAUNCHED();
-      }
-      tri_inviter_o_kernel<<<unsigned(ncols), 64, 0, st>>>(n, ncols, fin, w.clen, w.Z, w.nrm, w.scl);
-      LRC_LAUNCHED();
-      if (max_big > 0) {
-        tri_inviter_obig_kernel<<<unsigned(max_big), OB_T, 0, st>>>(n, ncols, fin, w.clen, w.nbig, w.big, w.Z,
-                                                                     w.scl);
-        LRC_LAUNCHED();
-      }
-    }
-  }
-
   // 4. back-transformation
   const int nref = n - 1;
   if (nref > 0) {
@@ -2106,8 +2134,44 @@ lrc_status tridiag_eig(hipStream_t st, double* A, int64_t sA, int64_t k, int64_t
   tri_sigma_kernel<<<dim3(unsigned(cdiv(n, 256)), nb), 256, 0, st>>>(w0.lam, n, sigma, s_sigma);
   LRC_LAUNCHED();
 
-  // 3.-4. eigenvectors and their back-transformation slice after slice, through one set
-  // of arrays
+  // 3. clusters and inverse iteration for every slice at once (one wave per vector or
+  // cluster, so the slices' latency-bound recurrences run side by side)
+  zero_int_kernel<<<unsigned(cdiv(batch, 256)), 256, 0, st>>>(w0.nbig, int(batch));
+  LRC_LAUNCHED();
+  tri_cluster_kernel<<<dim3(unsigned(cdiv(ncols, 256)), nb), 256, 0, st>>>(w0.lam, n, ncols, w0.bounds, w0.clen,
+                                                                          w0.nbig, w0.big);
+  LRC_LAUNCHED();
+  {
+    ProfScope scope("tri_inviter_a_kernel", st, 0.0, 0.0);
+    tri_inviter_a_kernel<<<dim3(unsigned(cdiv(ncols, 64)), nb), 64, 0, st>>>(w0.d, w0.e, n, w0.lam, ncols,
+                                                                             w0.bounds, w0.clen, w0.U, w0.piv,
+                                                                             w0.Z, w0.istride);
+    LRC_LAUNCHED();
+  }
+  {
+    // the solve and orthogonalisation launches together; clusters longer than CL_MAX
+    // (at most ncols / (CL_MAX + 1) of them per slice) get a workgroup each
+    ProfScope scope("tri_inviter_u_o_s_kernels", st, 0.0, 0.0);
+    const int max_big = ncols / (CL_MAX + 1);
+    tri_inviter_u_kernel<<<dim3(unsigned(ncols), nb), 64, 0, st>>>(n, ncols, w0.U, w0.Z, w0.nrm);
+    LRC_LAUNCHED();
+    for (int fin = 0; fin < 2; ++fin) {
+      if (fin == 1) {
+        tri_inviter_s_kernel<<<dim3(unsigned(ncols), nb), 64, 0, st>>>(n, ncols, w0.clen, w0.U, w0.piv, w0.Z,
+                                                                       w0.nrm);
+        LRC_LAUNCHED();
+      }
+      tri_inviter_o_kernel<<<dim3(unsigned(ncols), nb), 64, 0, st>>>(n, ncols, fin, w0.clen, w0.Z, w0.nrm, w0.scl);
+      LRC_LAUNCHED();
+      if (max_big > 0) {
+        tri_inviter_obig_kernel<<<dim3(unsigned(max_big), nb), OB_T, 0, st>>>(n, ncols, fin, w0.clen, w0.nbig,
+                                                                             w0.big, w0.Z, w0.scl);
+        LRC_LAUNCHED();
+      }
+    }
+  }
+
+  // 4. the back-transformation slice after slice, through one set of arrays
   for (int64_t b = 0; b < batch; ++b)
     LRC_TRY(tri_solve_slice(st, A + b * sA, n, lda, ncols, tri_slice(w0, b), Qt + b * s_qt));
   return LRC_OK;

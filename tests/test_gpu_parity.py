@@ -636,6 +636,31 @@ def test_decompose_repeated_singular_values(lrc, mult):
     assert np.abs(u.T @ u - np.eye(rank)).max() <= 1e-4
 
 
+def test_decompose_batched_clusters_equal_single_calls(lrc, monkeypatch):
+    """Three 600 x 600 slices solved together by the tridiagonal route (the eigenvalues and
+    the inverse iteration of all slices in one launch per kernel): slice 0 has a cluster of
+    8 equal singular values (one-wave orthogonalisation), slice 1 one of 200 (a workgroup
+    per cluster), slice 2 none.  Each slice equals its own call bit for bit."""
+    monkeypatch.setenv("LRC_EIGENSOLVER", "tridiag")
+    d, rank = 600, 350
+    ws = []
+    for b, mult in enumerate((8, 200, 1)):
+        sig = np.linspace(2.0, 0.5, d)
+        sig[100:100 + mult] = sig[100]
+        ws.append(_spectrum_weight(d, d, sig, 177 + b))
+    w3 = torch.stack(ws).to(dev())
+    eye = torch.eye(d, device=dev())
+    sig, left, right, info = lrc.lrc_whiten_decompose(w3, rank, eye, 1)
+    assert torch.all(info == 0)
+    for b in range(3):
+        s1, l1, r1, i1 = lrc.lrc_whiten_decompose(w3[b], rank, eye, 1)
+        assert int(i1[0]) == 0
+        assert torch.equal(sig[b], s1) and torch.equal(left[b], l1) and torch.equal(right[b], r1), b
+    # the 200-member cluster's whitened vectors are orthonormal (G = I: U = Left S^-1/2)
+    u = to_np(left[1]).astype(np.float64) / np.sqrt(to_np(sig[1])[:rank].astype(np.float64))
+    assert np.abs(u.T @ u - np.eye(rank)).max() <= 1e-4
+
+
 def test_decompose_default_solver_mid_size(lrc):
     """A single Gram takes the tridiagonal route by default (here k = 600, ragged panels)."""
     case = _decompose_case(lrc, 640, 600, 4000, 100, False, 91, dtype=torch.bfloat16)
