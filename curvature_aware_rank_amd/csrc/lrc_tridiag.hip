@@ -23,6 +23,9 @@
 //      back to the host: the whole solve is enqueued at once.
 //   4. Back-transformation Z <- Q Z in blocks of 128 reflectors, I - V T V^T (T from the
 //      forward columnwise recurrence on V^T V).
+// A batch of Grams goes through every stage together: each launch covers all slices (a
+// grid dimension indexes the slice), so the per-step launch and latency costs are paid
+// once for the batch.
 // Every reduction has a fixed order, so equal inputs give equal bits.
 #include <math.h>
 #include <stdlib.h>
@@ -1541,8 +1544,19 @@ __device__ __forceinline__ double refl(const double* __restrict__ A, int64_t lda
 }
 
 // partial V^T V of block g over one row chunk
+// element strides between the slices of a batch in the back-transformation's arrays
+struct BtStrides {
+  int64_t a;    // the matrix holding the reflectors
+  int64_t wsi;  // a slice's loop block (tau)
+  int64_t gp, t, yp, y;   // V^T V partials, the T factors, V^T Z partials, V^T Z and T V^T Z
+  int64_t z;    // eigenvectors of T (n x ncols)
+  int64_t qt;   // output rows
+};
+
 __global__ __launch_bounds__(256) void bt_gram_kernel(const double* __restrict__ A, int64_t lda, int n, int nref,
-                                                      int ngc, double* __restrict__ Gp) {
+                                                      int ngc, double* __restrict__ Gp, BtStrides bs) {
+  A += blockIdx.z * bs.a;   // slice blockIdx.z of a batch
+  Gp += blockIdx.z * bs.gp;
   __shared__ double sv[32][BW + 1];
   const int tid = threadIdx.x;
   const int g = blockIdx.x, ch = blockIdx.y;
@@ -1583,7 +1597,8 @@ __global__ __launch_bounds__(256) void bt_gram_kernel(const double* __restrict__
 }
 
 // the row-chunk partials of each group's V^T V summed in chunk order into its first partial
-__global__ __launch_bounds__(256) void bt_gsum_kernel(double* __restrict__ Gp, int ngc) {
+__global__ __launch_bounds__(256) void bt_gsum_kernel(double* __restrict__ Gp, int ngc, BtStrides bs) {
+  Gp += blockIdx.z * bs.gp;   // slice blockIdx.z
   const int g = blockIdx.y;
   const int q = blockIdx.x * 256 + threadIdx.x;   // < BW * BW
   double* base = Gp + int64_t(g) * ngc * BW * BW + q;
@@ -1596,7 +1611,11 @@ __global__ __launch_bounds__(256) void bt_gsum_kernel(double* __restrict__ Gp, i
 // thread i owns row i of T, kept in LDS.  G = V^T V is symmetric, so its column j is
 // row j (one coalesced load per column, the next column's load in flight).
 __global__ __launch_bounds__(BW) void bt_t_kernel(const double* __restrict__ Gp, int ngc, int nsum, int nref,
-                                                  const double* __restrict__ tau, double* __restrict__ Tm) {
+                                                  const double* __restrict__ tau, double* __restrict__ Tm,
+                                                  BtStrides bs) {
+  Gp += blockIdx.y * bs.gp;   // slice blockIdx.y
+  tau += blockIdx.y * bs.wsi;
+  Tm += blockIdx.y * bs.t;
   __shared__ double Ts[BW][BW + 1];
   __shared__ double gcol[2][BW];
   const int tid = threadIdx.x;
@@ -1638,7 +1657,10 @@ constexpr int BZP = 64 + 2;   // LDS pitch of the staged Z rows
 
 __global__ __launch_bounds__(256) void bt_vtz_kernel(const double* __restrict__ A, int64_t lda, int n, int nref,
                                                      int g0, const double* __restrict__ Z, int ncols,
-                                                     double* __restrict__ Yp) {
+                                                     double* __restrict__ Yp, BtStrides bs) {
+  A += blockIdx.z * bs.a;   // slice blockIdx.z
+  Z += blockIdx.z * bs.z;
+  Yp += blockIdx.z * bs.yp;
   __shared__ double sv[32][BVP];
   __shared__ double sz[32][BZP];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1708,7 +1730,9 @@ __global__ __launch_bounds__(256) void bt_vtz_kernel(const double* __restrict__ 
 
 // Y[a][c] = sum_ch Yp[ch][a][c]  (one element per thread, partials in order)
 __global__ __launch_bounds__(256) void bt_reduce_kernel(const double* __restrict__ Yp, int nch, int ncols,
-                                                        double* __restrict__ Y) {
+                                                        double* __restrict__ Y, BtStrides bs) {
+  Yp += blockIdx.y * bs.yp;   // slice blockIdx.y
+  Y += blockIdx.y * bs.y;
   const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
   const int64_t tot = int64_t(BW) * ncols;
   if (e >= tot) return;
@@ -1724,7 +1748,10 @@ __global__ __launch_bounds__(256) void bt_reduce_kernel(const double* __restrict
 
 // Y2 = T Y for 16 rows x 64 columns per workgroup (T upper triangular)
 __global__ __launch_bounds__(256) void bt_ty_kernel(const double* __restrict__ Y, const double* __restrict__ T,
-                                                    int ncols, double* __restrict__ Y2) {
+                                                    int ncols, double* __restrict__ Y2, BtStrides bs) {
+  Y += blockIdx.z * bs.y;   // slice blockIdx.z
+  T += blockIdx.z * bs.t;
+  Y2 += blockIdx.z * bs.y;
   __shared__ double sy[BW][64 + 1];
   __shared__ double st[16][BW + 1];
   const int tid = threadIdx.x;
@@ -1769,7 +1796,10 @@ constexpr int BUP = 32 + 1;   // LDS pitch of the staged V rows (odd: column rea
 
 __global__ __launch_bounds__(256) void bt_update_kernel(const double* __restrict__ A, int64_t lda, int n, int nref,
                                                         int g0, const double* __restrict__ Y2, int ncols,
-                                                        double* __restrict__ Z) {
+                                                        double* __restrict__ Z, BtStrides bs) {
+  A += blockIdx.z * bs.a;   // slice blockIdx.z
+  Y2 += blockIdx.z * bs.y;
+  Z += blockIdx.z * bs.z;
   __shared__ double sv[64][BUP];
   __shared__ double sy[32][BZP];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1853,7 +1883,10 @@ __global__ void tri_sigma_kernel(const double* __restrict__ lam, int n, float* _
 }
 
 __global__ __launch_bounds__(256) void tri_out_kernel(const double* __restrict__ Z, const double* __restrict__ scl,
-                                                      int n, int ncols, float* __restrict__ Qt) {
+                                                      int n, int ncols, float* __restrict__ Qt, BtStrides bs) {
+  Z += blockIdx.y * bs.z;   // slice blockIdx.y
+  scl += int64_t(blockIdx.y) * ncols;
+  Qt += blockIdx.y * bs.qt;
   __shared__ double bv[256];
   __shared__ int bi[256];
   const int j = blockIdx.x, tid = threadIdx.x;
@@ -1890,9 +1923,8 @@ struct TWs {
   // these pointers into slice 0's block
   double *P, *S, *SV, *SW, *npart, *x0, *xv, *d, *e, *tau, *Wp;
   int64_t istride;
-  int64_t lamstride;   // eigenvalues per slice (lam holds every slice's, bounds 4 each)
-  int64_t ncols;       // eigenvectors per slice
-  // the later stages (one slice at a time)
+  // the later stages: one block per slice of each array (lam n, bounds 4, the inverse
+  // iteration's factors, iterates and clusters, the back-transformation's partials)
   double *lam, *bounds, *U, *Z, *nrm, *scl, *Gp, *T, *Yp, *Yr, *Y2;
   int *clen, *nbig, *big;
   uint8_t* piv;
@@ -1930,8 +1962,6 @@ TWs carve_tri(Carve& cv, int64_t n, int64_t ncols, int64_t batch) {
   w.tau = loop + otau;
   w.Wp = loop + oWp;
   // eigenvalues and spectrum bounds of every slice (found for the whole batch at once)
-  w.lamstride = n;
-  w.ncols = ncols;
   w.lam = cv.take<double>(size_t(std::max<int64_t>(batch, 1) * n));
   w.bounds = cv.take<double>(size_t(4 * std::max<int64_t>(batch, 1)));
   // inverse iteration: one block of each array per slice (the batch is solved at once)
@@ -1939,11 +1969,12 @@ TWs carve_tri(Carve& cv, int64_t n, int64_t ncols, int64_t batch) {
   w.U = cv.take<double>(size_t(nbat * 4 * n * ncols));
   w.piv = cv.take<uint8_t>(size_t(nbat * n * ncols));
   w.Z = cv.take<double>(size_t(nbat * n * ncols));
-  w.Gp = cv.take<double>(size_t(ngroups * ngc * BW * BW));
-  w.T = cv.take<double>(size_t(ngroups * BW * BW));
-  w.Yp = cv.take<double>(size_t(nbc * BW * ncols));
-  w.Yr = cv.take<double>(size_t(BW * ncols));
-  w.Y2 = cv.take<double>(size_t(BW * ncols));
+  // back-transformation: one block of each array per slice (the batch is transformed at once)
+  w.Gp = cv.take<double>(size_t(nbat * ngroups * ngc * BW * BW));
+  w.T = cv.take<double>(size_t(nbat * ngroups * BW * BW));
+  w.Yp = cv.take<double>(size_t(nbat * nbc * BW * ncols));
+  w.Yr = cv.take<double>(size_t(nbat * BW * ncols));
+  w.Y2 = cv.take<double>(size_t(nbat * BW * ncols));
   w.nrm = cv.take<double>(size_t(nbat * ncols));
   w.scl = cv.take<double>(size_t(nbat * ncols));
   w.clen = cv.take<int>(size_t(nbat * ncols));
@@ -2031,75 +2062,59 @@ size_t tridiag_workspace(int64_t k, int64_t ncols, int64_t batch) {
   return cv.bytes();
 }
 
-// slice b's view of the loop arrays, with the later-stage arrays shared by all slices
-static TWs tri_slice(const TWs& w0, int64_t b) {
-  TWs w = w0;
-  const int64_t o = b * w0.istride;
-  w.P += o;
-  w.S += o;
-  w.SV += o;
-  w.SW += o;
-  w.npart += o;
-  w.x0 += o;
-  w.xv += o;
-  w.d += o;
-  w.e += o;
-  w.tau += o;
-  w.Wp += o;
-  w.lam += b * w.lamstride;
-  w.bounds += 4 * b;
-  const int64_t nc = w.lamstride * w.ncols;
-  w.U += b * 4 * nc;
-  w.piv += b * nc;
-  w.Z += b * nc;
-  w.nrm += b * w.ncols;
-  w.scl += b * w.ncols;
-  w.clen += b * w.ncols;
-  w.nbig += b;
-  w.big += b * w.ncols;
-  return w;
-}
 
-// the back-transformation of one reduced slice's eigenvectors (found by inverse iteration
-// for the whole batch): A holds its reflectors, w.tau its scalars, w.Z / w.scl its
-// eigenvectors of T and their pending scales
-static lrc_status tri_solve_slice(hipStream_t st, double* A, int n, int64_t lda, int ncols, const TWs& w,
-                                  float* Qt) {
-  // 4. back-transformation
+// the back-transformation of the eigenvectors of every reduced slice of a batch (found by
+// inverse iteration): slice b's reflectors in A + b sA, its scalars in its loop block,
+// its eigenvectors of T and their pending scales in its blocks of w.Z / w.scl; every
+// launch covers the batch (grid z or y)
+static lrc_status tri_backtransform(hipStream_t st, double* A, int64_t sA, int n, int64_t lda, int ncols, int batch,
+                                    const TWs& w, float* Qt, int64_t s_qt) {
   const int nref = n - 1;
+  const int ngroups = int(cdiv(std::max(nref, 1), BW));
+  const int ngc = int(cdiv(n, G_CHUNK));
+  const int nbc = int(cdiv(n, BT_CHUNK));
+  BtStrides bs;
+  bs.a = sA;
+  bs.wsi = w.istride;
+  bs.gp = int64_t(ngroups) * ngc * BW * BW;
+  bs.t = int64_t(ngroups) * BW * BW;
+  bs.yp = int64_t(nbc) * BW * ncols;
+  bs.y = int64_t(BW) * ncols;
+  bs.z = int64_t(n) * ncols;
+  bs.qt = s_qt;
+  const unsigned nb = unsigned(batch);
   if (nref > 0) {
-    const int ngroups = int(cdiv(nref, BW));
-    const int ngc = int(cdiv(n, G_CHUNK));
-    bt_gram_kernel<<<dim3(unsigned(ngroups), unsigned(ngc)), 256, 0, st>>>(A, lda, n, nref, ngc, w.Gp);
+    bt_gram_kernel<<<dim3(unsigned(ngroups), unsigned(ngc), nb), 256, 0, st>>>(A, lda, n, nref, ngc, w.Gp, bs);
     LRC_LAUNCHED();
-    bt_gsum_kernel<<<dim3(unsigned(BW * BW / 256), unsigned(ngroups)), 256, 0, st>>>(w.Gp, ngc);
+    bt_gsum_kernel<<<dim3(unsigned(BW * BW / 256), unsigned(ngroups), nb), 256, 0, st>>>(w.Gp, ngc, bs);
     LRC_LAUNCHED();
-    bt_t_kernel<<<unsigned(ngroups), BW, 0, st>>>(w.Gp, ngc, 1, nref, w.tau, w.T);
+    bt_t_kernel<<<dim3(unsigned(ngroups), nb), BW, 0, st>>>(w.Gp, ngc, 1, nref, w.tau, w.T, bs);
     LRC_LAUNCHED();
     const unsigned ctiles = unsigned(cdiv(ncols, 64));
     for (int g = ngroups - 1; g >= 0; --g) {
       const int g0 = g * BW;
       const int rows = n - 1 - g0;
       const int nch = int(cdiv(rows, BT_CHUNK));
-      const double fl = 2.0 * double(rows) * BW * double(ncols);
+      const double fl = 2.0 * double(rows) * BW * double(ncols) * batch;
       {
         ProfScope scope("bt_vtz_kernel", st, fl, 0.0);
-        bt_vtz_kernel<<<dim3(ctiles, unsigned(nch)), 256, 0, st>>>(A, lda, n, nref, g0, w.Z, ncols, w.Yp);
+        bt_vtz_kernel<<<dim3(ctiles, unsigned(nch), nb), 256, 0, st>>>(A, lda, n, nref, g0, w.Z, ncols, w.Yp, bs);
         LRC_LAUNCHED();
       }
-      bt_reduce_kernel<<<unsigned(cdiv(int64_t(BW) * ncols, 256)), 256, 0, st>>>(w.Yp, nch, ncols, w.Yr);
+      bt_reduce_kernel<<<dim3(unsigned(cdiv(int64_t(BW) * ncols, 256)), nb), 256, 0, st>>>(w.Yp, nch, ncols, w.Yr,
+                                                                                          bs);
       LRC_LAUNCHED();
-      bt_ty_kernel<<<dim3(ctiles, BW / 16), 256, 0, st>>>(w.Yr, w.T + int64_t(g) * BW * BW, ncols, w.Y2);
+      bt_ty_kernel<<<dim3(ctiles, BW / 16, nb), 256, 0, st>>>(w.Yr, w.T + int64_t(g) * BW * BW, ncols, w.Y2, bs);
       LRC_LAUNCHED();
       {
         ProfScope scope("bt_update_kernel", st, fl, 0.0);
-        bt_update_kernel<<<dim3(unsigned(cdiv(rows, 64)), ctiles), 256, 0, st>>>(A, lda, n, nref, g0, w.Y2, ncols,
-                                                                                 w.Z);
+        bt_update_kernel<<<dim3(unsigned(cdiv(rows, 64)), ctiles, nb), 256, 0, st>>>(A, lda, n, nref, g0, w.Y2,
+                                                                                     ncols, w.Z, bs);
         LRC_LAUNCHED();
       }
     }
   }
-  tri_out_kernel<<<unsigned(ncols), 256, 0, st>>>(w.Z, w.scl, n, ncols, Qt);
+  tri_out_kernel<<<dim3(unsigned(ncols), nb), 256, 0, st>>>(w.Z, w.scl, n, ncols, Qt, bs);
   LRC_LAUNCHED();
   return LRC_OK;
 }
@@ -2171,9 +2186,8 @@ lrc_status tridiag_eig(hipStream_t st, double* A, int64_t sA, int64_t k, int64_t
     }
   }
 
-  // 4. the back-transformation slice after slice, through one set of arrays
-  for (int64_t b = 0; b < batch; ++b)
-    LRC_TRY(tri_solve_slice(st, A + b * sA, n, lda, ncols, tri_slice(w0, b), Qt + b * s_qt));
+  // 4. the back-transformation of every slice, one launch per step for the batch
+  LRC_TRY(tri_backtransform(st, A, sA, n, lda, ncols, int(batch), w0, Qt, s_qt));
   return LRC_OK;
 }
 
