@@ -6,9 +6,9 @@ workload: 65536 bf16 tokens x 4096 channels streamed into the activation covaria
 per-component K-FAC scores (this workload has no gradients) and the global
 sort-and-truncate at the budget of rank 1024.  Inputs are resident in HBM before the
 timed region.  The K timed steps are independent layers spread over --streams HIP
-streams (default 4 on the 8 hardware queues the bench asks HIP for; each stream has its
+streams (default 3 on the 8 hardware queues the bench asks HIP for; each stream has its
 own covariance buffers and its own host thread that enqueues its steps); each stream
-decomposes --layers-per-call of its layers per call (default 3, each layer with its own
+decomposes --layers-per-call of its layers per call (default 4, each layer with its own
 covariance), so up to twelve layers are in flight at a time; `value` is K / the wall time of
 the region.  The same K steps one after another on one stream, one layer per call, give
 `value_one_stream` (one layer's latency).  Prints one JSON line.
@@ -91,8 +91,8 @@ def parse():
     p.add_argument("--rank", type=int, default=1024)
     p.add_argument("--streams", type=int, default=None,
                    help="HIP streams the timed steps run on, each fed by its own host thread (independent layers "
-                        "in flight); default: one less than the hardware queues, at most 4")
-    p.add_argument("--layers-per-call", type=int, default=3,
+                        "in flight); default: one less than the hardware queues, at most 3")
+    p.add_argument("--layers-per-call", type=int, default=4,
                    help="independent layers a stream decomposes per call (one covariance each)")
     p.add_argument("--hw-queues", type=int, default=8,
                    help="hardware queues HIP gives this process (GPU_MAX_HW_QUEUES, set before HIP starts)")
@@ -746,7 +746,7 @@ def main():
     a = synth.activation_stream(n, d, 1.0, 31, outlier_frac=0.01, dtype=torch.bfloat16, device=dev)
     w = synth.weight(d, d, 35, device=dev)
     if args.streams is None:
-        args.streams = min(4, max(1, int(os.environ["GPU_MAX_HW_QUEUES"]) - 1))
+        args.streams = min(3, max(1, int(os.environ["GPU_MAX_HW_QUEUES"]) - 1))
     ns = max(1, args.streams)
     lpc = max(1, args.layers_per_call)
     streams = [torch.cuda.Stream() for _ in range(ns)]
