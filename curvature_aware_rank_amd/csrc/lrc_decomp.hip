@@ -164,10 +164,9 @@ lrc_status decompose(const float* W, int64_t d_out, int64_t d_in, int64_t ldw, i
   LRC_LAUNCHED();
   // a2: Cholesky factors of the covariances (a failed pivot is recorded in chol_info and
   // acted on after the Gram, on the device)
-  for (int64_t c = 0; c < nx; ++c)
-    LRC_TRY(cholesky_f32(st, Xsum + c * stride_x, ldx, d_in, n_x, damping, w.lx + c * sLx, w.chol_info + 2 * c));
-  for (int64_t c = 0; c < ng; ++c)
-    LRC_TRY(cholesky_f32(st, Gsum + c * stride_g, ldg, d_out, n_g, damping, w.lg + c * sLg, w.chol_info + 2 * c + 1));
+  // (one covariance per slice: every launch of the factorisation covers the batch)
+  if (hx) LRC_TRY(cholesky_f32_batched(st, Xsum, ldx, stride_x, d_in, n_x, damping, w.lx, w.chol_info, 2, nx));
+  if (hg) LRC_TRY(cholesky_f32_batched(st, Gsum, ldg, stride_g, d_out, n_g, damping, w.lg, w.chol_info + 1, 2, ng));
   // a3: whitening  W~ = L_g^T W L_x
   const float* cur = W;
   int64_t ldc = ldw, scur = stride_w;

@@ -8,6 +8,10 @@ namespace lrc {
 // info (device int, must be 0 on entry) receives the 1-based failing pivot.
 lrc_status cholesky_f32(hipStream_t st, const float* S, int64_t lds_, int64_t n, int64_t cnt, float damping,
                         float* L, int* info);
+// The same for a batch: slice b factors S + b sS into L + b n n, its pivot in info + b sinfo
+// (every info must be 0 on entry); each launch covers the batch.
+lrc_status cholesky_f32_batched(hipStream_t st, const float* S, int64_t lds_, int64_t sS, int64_t n, int64_t cnt,
+                                float damping, float* L, int* info, int sinfo, int64_t batch);
 
 // Solve L^T Y = B in place (L lower n x n, ld n; B n x ncol, ld ldb).
 lrc_status trsm_lower_t(hipStream_t st, const float* L, int64_t n, float* Bm, int64_t ldb, int64_t ncol);

@@ -286,7 +286,9 @@ __global__ __launch_bounds__(256) void gram_f64_kernel(bool rows, int p, int q, 
 // ---------------------------------------------------------------------------------
 // L = lower(S) / cnt + damping * I ; strict upper part zeroed.  S is read lower only.
 __global__ void sym_scale_kernel(const float* __restrict__ S, int64_t lds_, int64_t n, double inv_cnt, float damping,
-                                 float* __restrict__ L, int64_t ldl) {
+                                 float* __restrict__ L, int64_t ldl, int64_t sS, int64_t sL) {
+  S += blockIdx.z * sS;   // slice blockIdx.z of a batch
+  L += blockIdx.z * sL;
   const int64_t i = blockIdx.y;
   for (int64_t j = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; j < n; j += int64_t(gridDim.x) * blockDim.x) {
     float v = 0.f;
@@ -306,7 +308,9 @@ constexpr int NB = 64;  // Cholesky / triangular-solve block size
 // LDS to every lane (one store per lane, then broadcast reads that the wave's in-order
 // LDS queue serves after the store), and each lane updates its own row.
 __global__ __launch_bounds__(64) void potf2_kernel(float* __restrict__ L, int64_t ldl, int64_t n, int64_t k0,
-                                                   int* __restrict__ info) {
+                                                   int* __restrict__ info, int64_t sL, int sinfo) {
+  L += blockIdx.y * sL;   // slice blockIdx.y of a batch
+  info += blockIdx.y * sinfo;
   __shared__ __align__(16) float colv[NB];
   const int lane = threadIdx.x;
   const int b = int(min<int64_t>(NB, n - k0));
@@ -386,7 +390,9 @@ __global__ __launch_bounds__(64) void potf2_kernel(float* __restrict__ L, int64_
 // Rows are loaded as 16-byte groups when the pitch and base allow; the solve reads each
 // row of D from LDS four entries at a time (broadcast reads, the FMAs in column order).
 __global__ __launch_bounds__(64) void trsm_panel_kernel(float* __restrict__ L, int64_t ldl, int64_t n, int64_t k0,
-                                                        const int* __restrict__ info) {
+                                                        const int* __restrict__ info, int64_t sL, int sinfo) {
+  L += blockIdx.y * sL;   // slice blockIdx.y of a batch
+  info += blockIdx.y * sinfo;
   __shared__ __align__(16) float D[NB][NB + 4];
   __shared__ float rdiag[NB];
   if (*info != 0) return;
@@ -555,31 +561,40 @@ lrc_status gram_f64(hipStream_t st, bool rows, int64_t p, int64_t q, const float
   return LRC_OK;
 }
 
-lrc_status cholesky_f32(hipStream_t st, const float* S, int64_t lds_, int64_t n, int64_t cnt, float damping, float* L,
-                        int* info) {
-  const dim3 g(unsigned(std::min<int64_t>(cdiv(n, 256), 64)), unsigned(n));
-  sym_scale_kernel<<<g, 256, 0, st>>>(S, lds_, n, 1.0 / double(cnt), damping, L, n);
+lrc_status cholesky_f32_batched(hipStream_t st, const float* S, int64_t lds_, int64_t sS, int64_t n, int64_t cnt,
+                                float damping, float* L, int* info, int sinfo, int64_t batch) {
+  if (batch <= 0 || n <= 0) return LRC_OK;
+  const int64_t sL = n * n;
+  const unsigned nb_ = unsigned(batch);
+  const dim3 g(unsigned(std::min<int64_t>(cdiv(n, 256), 64)), unsigned(n), nb_);
+  sym_scale_kernel<<<g, 256, 0, st>>>(S, lds_, n, 1.0 / double(cnt), damping, L, n, sS, sL);
   LRC_LAUNCHED();
   for (int64_t k0 = 0; k0 < n; k0 += NB) {
     {
       // work: the block's NB^3 / 3 multiply-adds; bytes: the block read and written
       const double nb = double(std::min<int64_t>(NB, n - k0));
-      ProfScope scope("potf2_kernel", st, nb * nb * nb / 3.0, 8.0 * nb * nb);
-      potf2_kernel<<<1, 64, 0, st>>>(L, n, n, k0, info);
+      ProfScope scope("potf2_kernel", st, nb * nb * nb / 3.0 * batch, 8.0 * nb * nb * batch);
+      potf2_kernel<<<dim3(1, nb_), 64, 0, st>>>(L, n, n, k0, info, sL, sinfo);
       LRC_LAUNCHED();
     }
     const int64_t below = n - k0 - NB;
     if (below <= 0) break;
     {
-      ProfScope scope("trsm_panel_kernel", st, double(below) * NB * NB, 8.0 * double(below) * NB + 4.0 * NB * NB);
-      trsm_panel_kernel<<<unsigned(cdiv(below, 64)), 64, 0, st>>>(L, n, n, k0, info);
+      ProfScope scope("trsm_panel_kernel", st, double(below) * NB * NB * batch,
+                      (8.0 * double(below) * NB + 4.0 * NB * NB) * batch);
+      trsm_panel_kernel<<<dim3(unsigned(cdiv(below, 64)), nb_), 64, 0, st>>>(L, n, n, k0, info, sL, sinfo);
       LRC_LAUNCHED();
     }
     float* p = L + (k0 + NB) * n + k0;
     float* c = L + (k0 + NB) * n + (k0 + NB);
-    LRC_TRY(gemm_f32(st, GEMM_TB | GEMM_LOWER, below, below, NB, -1.f, p, n, 0, p, n, 0, 1.f, c, n, 0, 1));
+    LRC_TRY(gemm_f32(st, GEMM_TB | GEMM_LOWER, below, below, NB, -1.f, p, n, sL, p, n, sL, 1.f, c, n, sL, batch));
   }
   return LRC_OK;
+}
+
+lrc_status cholesky_f32(hipStream_t st, const float* S, int64_t lds_, int64_t n, int64_t cnt, float damping, float* L,
+                        int* info) {
+  return cholesky_f32_batched(st, S, lds_, 0, n, cnt, damping, L, info, 0, 1);
 }
 
 lrc_status trsm_lower_t(hipStream_t st, const float* L, int64_t n, float* Bm, int64_t ldb, int64_t ncol) {
