@@ -581,6 +581,19 @@ def passes(lrc, torch, dev):
                                         "ms_queued": round(tq * 1e3, 4), "items_per_s": round(m_items / tq, 1),
                                         "GB/s": round(byt / tq / 1e9, 1),
                                         "hbm_frac": round(byt / tq / 1e9 / HBM_PEAK_GBS, 4)}
+        # the same cut without the order (radix select weighted by cost): bytes per item are
+        # the scores read by the three full select levels and the mask pass (4 x 4 B), the
+        # mask written (1 B) and read by the rank count (1 B); the candidate list of the
+        # later levels (a few percent of the items) is left out
+        sel = lambda: lrc.lrc_allocate_ranks(scores, offs, cost, budget, want_order=False)
+        sel()
+        t = _time(sel, torch, 5)
+        tq = _time_queued(sel, torch, 20)
+        byt = m_items * (4 * 4.0 + 2.0)
+        out[f"allocation_{m_items}_no_order"] = {
+            "workload": f"{m_items} components ({label}), n_kept/ranks/mask only", "ms": round(t * 1e3, 3),
+            "ms_queued": round(tq * 1e3, 4), "items_per_s": round(m_items / tq, 1), "GB/s": round(byt / tq / 1e9, 1),
+            "hbm_frac": round(byt / tq / 1e9 / HBM_PEAK_GBS, 4)}
     return out
 
 
@@ -639,7 +652,8 @@ def only(args, lrc, torch, dev):
     elif args.only == "alloc":
         # global sort-and-truncate: the decoder stack's 917,504-component pool (224
         # matrices, costs 8192 / 15104) and a 64M-component pool; one untimed and five
-        # timed calls each, queued back to back
+        # timed calls each, queued back to back, with the order (sort) and without it
+        # (select)
         g = torch.Generator(device=dev)
         g.manual_seed(45)
         for m_items, n_mat in ((917504, 224), (64 * 1024 * 1024, 16384)):
@@ -648,15 +662,16 @@ def only(args, lrc, torch, dev):
             cost = torch.where(torch.arange(n_mat, device=dev) % 7 < 4, 8192, 15104).to(torch.int64)
             scores = torch.rand(m_items, generator=g, device=dev)
             budget = int(0.6 * float((cost * per).sum()))
-            lrc.lrc_allocate_ranks(scores, offs, cost, budget)
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            s.record()
-            for _ in range(5):
-                lrc.lrc_allocate_ranks(scores, offs, cost, budget)
-            e.record()
-            torch.cuda.synchronize()
-            res[f"ms_per_call_{m_items}"] = round(s.elapsed_time(e) / 5, 4)
+            for want, tag in ((True, ""), (False, "_no_order")):   # sort, then the order-free select
+                lrc.lrc_allocate_ranks(scores, offs, cost, budget, want_order=want)
+                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                s.record()
+                for _ in range(5):
+                    lrc.lrc_allocate_ranks(scores, offs, cost, budget, want_order=want)
+                e.record()
+                torch.cuda.synchronize()
+                res[f"ms_per_call_{m_items}{tag}"] = round(s.elapsed_time(e) / 5, 4)
             del offs, cost, scores
     elif args.only == "qaw":
         # int8-QAW activation covariance of the FFN pair's down projection: 131072 bf16

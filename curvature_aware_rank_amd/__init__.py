@@ -293,10 +293,13 @@ def lrc_score_components(left=None, right=None, sigma=None, A=None, B=None, mode
     return scores, info
 
 
-def lrc_allocate_ranks(scores: torch.Tensor, offsets: torch.Tensor, cost: torch.Tensor, budget: int):
+def lrc_allocate_ranks(scores: torch.Tensor, offsets: torch.Tensor, cost: torch.Tensor, budget: int,
+                       want_order: bool = True):
     """Global sort-and-truncate.  scores: (M,) fp32; offsets: (n_mat+1,) int64; cost: (n_mat,) int64.
 
-    Returns (order int32 (M,), n_kept int64 (1,), ranks int32 (n_mat,), kept_mask uint8 (M,), info int32 (1,))."""
+    Returns (order int32 (M,), n_kept int64 (1,), ranks int32 (n_mat,), kept_mask uint8 (M,), info int32 (1,)).
+    With want_order=False the library selects the cut without sorting (the same n_kept,
+    ranks and mask) and order is None."""
     _dev(scores, "scores")
     dev = scores.device
     n_mat = cost.numel() if isinstance(cost, torch.Tensor) else 0
@@ -305,13 +308,14 @@ def lrc_allocate_ranks(scores: torch.Tensor, offsets: torch.Tensor, cost: torch.
     _tensor(cost, "cost", torch.int64, (n_mat,), dev)
     M = scores.numel()
     sc, offs, cst = scores.contiguous(), offsets.contiguous(), cost.contiguous()
-    order = torch.empty(M, dtype=torch.int32, device=dev)
+    order = torch.empty(M, dtype=torch.int32, device=dev) if want_order else None
     n_kept = torch.empty(1, dtype=torch.int64, device=dev)
     ranks = torch.empty(n_mat, dtype=torch.int32, device=dev)
     kept = torch.empty(M, dtype=torch.uint8, device=dev)
     info = torch.empty(1, dtype=torch.int32, device=dev)
     ws = _workspace(lib.lrc_allocate_ranks_workspace(n_mat, M), dev)
-    _check(lib.lrc_allocate_ranks(_ptr(sc), _ptr(offs), _ptr(cst), n_mat, M, int(budget), _ptr(order), _ptr(n_kept),
+    _check(lib.lrc_allocate_ranks(_ptr(sc), _ptr(offs), _ptr(cst), n_mat, M, int(budget),
+                                  _ptr(order) if want_order else None, _ptr(n_kept),
                                   _ptr(ranks), _ptr(kept), _ptr(info), _ptr(ws), ws.numel(), _stream()),
            "lrc_allocate_ranks")
     return order, n_kept, ranks, kept, info

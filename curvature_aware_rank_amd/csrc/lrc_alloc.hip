@@ -14,16 +14,26 @@
 // input order), stages it in LDS in digit order and writes contiguous runs.  The cut
 // sums the sorted costs per block of positions (int64, exact), finds the block where the
 // running total first exceeds the budget, and resolves the position inside it; the mask
-// is then written in item order by comparing each item's (key, id) with the last kept
-// item's.  Matrix costs are looked up per 4096-item bucket.
+// is then written in item order by comparing each item's (key, id) with that of the first
+// excluded item.  Matrix costs are looked up per 4096-item bucket.
+//
+// A caller that needs no order gets the same cut without sorting: the first excluded item
+// E is found by a radix select weighted by cost.  Level 0 sums the costs of every item per
+// top 8-bit digit of its key bits; the digit whose bucket carries the running total past
+// the budget is fixed, the cost of every lower bucket is carried, and the next level sums
+// the next 8 bits over the items of that bucket only.  After eight levels the bucket holds
+// the items whose key equals E's; among them E is the first, in id order, at which the
+// running total exceeds the budget, found by four more such levels over the 32-bit id.
+// Only the first three levels read every key; the third also lists the items of its
+// bucket, and the later levels read only that list.
 #include <mutex>
 
 #include "lrc_internal.h"
 
 // ---- scratch of the allocation-free variant (lrc_allocate_ranks_noalloc): one array per
 // GPU, held until the process ends.  carve_alloc at NOALLOC_MAX_ITEMS needs 24 B per item
-// (two key and two id buffers) plus at most ~1.1 MB of histogram, lookup and cut tables;
-// the entry point checks the carve against the array's size at run time.
+// (two key and two id buffers) plus about 1.6 MB of histogram, lookup, cut and select
+// tables; the entry point checks the carve against the array's size at run time.
 constexpr int64_t NOALLOC_MAX_ITEMS = int64_t(1) << 21;
 constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(24) * NOALLOC_MAX_ITEMS + (size_t(2) << 20);
 static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
@@ -96,19 +106,24 @@ struct CostLookup {
   }
 };
 
-// sort key of item j: ~bits(fp64(score) / fp64(cost)); 0 (first in the order) for a
-// rejected item, whose call reports an error and keeps nothing
-__device__ __forceinline__ uint64_t item_key(const float* __restrict__ scores, const CostLookup& cl, int64_t j,
-                                             bool inputs_bad, bool& nonfinite) {
+// sort key of a score at a cost: ~bits(fp64(score) / fp64(cost)); 0 (first in the order)
+// for a NaN, infinite or negative score, whose call reports an error and keeps nothing
+__device__ __forceinline__ uint64_t score_key(float sc, int64_t c, bool& nonfinite) {
   nonfinite = false;
-  if (inputs_bad) return 0;
-  const float sc = scores[j];
   if (!isfinite(sc) || sc < 0.f) {
     nonfinite = true;
     return 0;
   }
-  const double key = (double(sc) + 0.0) / double(cl(j));   // +0.0: -0 -> +0
+  const double key = (double(sc) + 0.0) / double(c);   // +0.0: -0 -> +0
   return ~uint64_t(__double_as_longlong(key));
+}
+
+// sort key of item j (0 for every item when the offsets or costs were rejected)
+__device__ __forceinline__ uint64_t item_key(const float* __restrict__ scores, const CostLookup& cl, int64_t j,
+                                             bool inputs_bad, bool& nonfinite) {
+  nonfinite = false;
+  if (inputs_bad) return 0;
+  return score_key(scores[j], cl(j), nonfinite);
 }
 
 __global__ void alloc_check_kernel(const int64_t* __restrict__ offs, const int64_t* __restrict__ cost, int n_mat,
@@ -450,45 +465,360 @@ __global__ __launch_bounds__(256) void cost_cut_kernel(const int32_t* __restrict
 
 __global__ void set_i64_kernel(int64_t* __restrict__ p, int64_t v) { *p = v; }
 
-// key and id of the last kept position (or an empty marker) for the mask.  A call whose
-// inputs were rejected (info != 0: a score NaN, infinite or negative, or inconsistent
-// offsets or costs) keeps nothing: n_kept = 0, and the mask and ranks come out zero.
+// The cut for the mask: key bits and id of the first excluded item E, so that the kept
+// items are exactly those whose (key bits, id) pair is below E's.  (~0, M) keeps every
+// item, (0, 0) none.  A call whose inputs were rejected (info != 0: a score NaN, infinite
+// or negative, or inconsistent offsets or costs) keeps nothing: n_kept = 0, and the mask
+// and ranks come out zero.
 __global__ void cut_key_kernel(const float* __restrict__ scores, CostLookup cl,
                                const int32_t* __restrict__ order, int M, int64_t* __restrict__ n_kept,
                                const int32_t* __restrict__ info, uint64_t* __restrict__ cutkey) {
-  if (*info != 0) *n_kept = 0;
+  if (*info != 0) {
+    *n_kept = 0;
+    cutkey[0] = 0;
+    cutkey[1] = 0;
+    return;
+  }
   const int64_t nk = *n_kept;
-  if (nk <= 0) {
-    cutkey[1] = ~uint64_t(0);   // no id is <= this as a signed int64: nothing kept
+  if (nk >= M) {
+    cutkey[0] = ~uint64_t(0);
+    cutkey[1] = uint64_t(M);
     return;
   }
   bool nf;
-  const int32_t id = order_id(order, nk - 1, M);
-  cutkey[0] = item_key(scores, cl, id, *info == int32_t(LRC_EINVAL), nf);
+  const int32_t id = order_id(order, nk < 0 ? 0 : nk, M);
+  cutkey[0] = item_key(scores, cl, id, false, nf);
   cutkey[1] = uint64_t(id);
 }
 
-// kept_mask in item order: the kept items are the sorted prefix, i.e. exactly those whose
-// (key bits, id) pair is at most that of the last kept item.  The key is recomputed here
-// so that the mask is written in item order rather than scattered through the order.
+// kept_mask in item order: an item is kept when its (key bits, id) pair is below the cut's.
+// The key is recomputed here so that the mask is written in item order rather than
+// scattered through the order.  With part given, part[workgroup] = its kept count.
 // MASK_PER items per workgroup, consecutive lanes on consecutive items.
 constexpr int MASK_PER = 256 * 16;
 __global__ __launch_bounds__(256) void mask_kernel(const float* __restrict__ scores, CostLookup cl, int M,
                                                    const uint64_t* __restrict__ cutkey,
-                                                   const int32_t* __restrict__ info, uint8_t* __restrict__ kept) {
+                                                   const int32_t* __restrict__ info, uint8_t* __restrict__ kept,
+                                                   int64_t* __restrict__ part) {
   const uint64_t ck = cutkey[0];
   const int64_t cid = int64_t(cutkey[1]);
   const bool bad = *info == int32_t(LRC_EINVAL);
   const int64_t base = int64_t(blockIdx.x) * MASK_PER;
+  int nk = 0;
 #pragma unroll 4
   for (int i = 0; i < MASK_PER / 256; ++i) {
     const int64_t j = base + i * 256 + threadIdx.x;
     if (j < M) {
       bool nf;
       const uint64_t key = item_key(scores, cl, j, bad, nf);
-      kept[j] = (cid >= 0 && (key < ck || (key == ck && j <= cid))) ? 1 : 0;
+      const bool k = key < ck || (key == ck && j < cid);
+      kept[j] = k ? 1 : 0;
+      nk += k;
     }
   }
+  if (part != nullptr) {
+    __shared__ int wn[4];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) nk += __shfl_xor(nk, o);
+    if ((threadIdx.x & 63) == 0) wn[threadIdx.x >> 6] = nk;
+    __syncthreads();
+    if (threadIdx.x == 0) part[blockIdx.x] = wn[0] + wn[1] + wn[2] + wn[3];
+  }
+}
+
+// ---- radix select of the first excluded item (the call without an order)
+// Select state: sel[0] = the key bits fixed so far (8 per level), sel[1] = the cost of every
+// item whose key lies below that bucket, sel[2] = 1 when the whole pool fits the budget.
+// Id state (the items whose key equals the selected key): seli[0] = the id bits fixed so
+// far, seli[1] = the cost of every item below that id bucket.
+// Select workgroup b takes SEL_PER-item tiles b, b + gridDim.x, ..., consecutive lanes on
+// consecutive items.  Levels 0 to 2 read every score and recompute its key (4 bytes read
+// per item instead of 8, and no key array written); level 2 also writes the items of its
+// bucket (the 16 fixed bits: a few percent of a realistic pool) to the candidate list:
+// wave w of a tile, which owns 1024 of its items, fills the quarter w of the tile's range,
+// placing its matches by ballot, and records their count (so the list needs no more room
+// than the tiles and no global counter or barrier).  Key levels 3 to 7 and the four id
+// levels read only the candidates.  A thread sums the costs of its consecutive equal
+// digits before one LDS atomic (the top digits of a realistic pool take few values).
+// Every sum is an integer add, so none depends on order.
+constexpr int SEL_PER = 256 * 16;
+constexpr int SEL_RR = SEL_PER / 256;
+constexpr int SEL_MAX_BLOCKS = 2048;
+static_assert(SEL_PER == (1 << MB_SHIFT), "a select tile is one bucket of the cost table");
+
+__device__ __forceinline__ void sel_run_add(unsigned long long* hc, uint32_t& cd, unsigned long long& cc,
+                                            uint32_t d, int64_t c) {
+  if (d != cd) {
+    if (cc != 0) atomicAdd(&hc[cd], cc);
+    cd = d;
+    cc = 0;
+  }
+  cc += (unsigned long long)c;
+}
+
+// the workgroup's digit sums into the level's histogram (atomics: for levels whose
+// workgroups fill few digits), or stored as the workgroup's row of a table that
+// sel_reduce_kernel sums (levels whose workgroups fill many digits: the atomics of 2048
+// workgroups on one 2 KB histogram serialise)
+__device__ __forceinline__ void sel_flush(unsigned long long* hc, uint32_t cd, unsigned long long cc,
+                                          unsigned long long* __restrict__ hist) {
+  if (cc != 0) atomicAdd(&hc[cd], cc);
+  __syncthreads();
+  const unsigned long long v = hc[threadIdx.x];
+  if (v != 0) atomicAdd(&hist[threadIdx.x], v);
+}
+__device__ __forceinline__ void sel_flush_row(unsigned long long* hc, uint32_t cd, unsigned long long cc,
+                                              unsigned long long* __restrict__ rows) {
+  if (cc != 0) atomicAdd(&hc[cd], cc);
+  __syncthreads();
+  rows[int64_t(blockIdx.x) * 256 + threadIdx.x] = hc[threadIdx.x];
+}
+
+// the level histogram from the rows of nrows workgroups: workgroup g sums rows g,
+// g + gridDim.x, ... and adds its 256 sums
+constexpr int SEL_REDUCE_BLOCKS = 64;
+__global__ __launch_bounds__(256) void sel_reduce_kernel(const unsigned long long* __restrict__ rows, int nrows,
+                                                         const uint64_t* __restrict__ sel,
+                                                         unsigned long long* __restrict__ hist) {
+  if (sel[2] != 0) return;
+  unsigned long long v = 0;
+  for (int r = blockIdx.x; r < nrows; r += gridDim.x) v += rows[int64_t(r) * 256 + threadIdx.x];
+  if (v != 0) atomicAdd(&hist[threadIdx.x], v);
+}
+
+// key bits and cost of item j as every select pass sees them (the keys are recomputed from
+// the scores in each full pass rather than stored: 4 bytes read per item instead of 8, and
+// no 8-byte write); rejected offsets or costs give every item key 0 and cost 0
+__device__ __forceinline__ void sel_item(const float* __restrict__ scores, const CostLookup& cl, int64_t j, bool bad,
+                                         uint64_t& u, int64_t& c, bool& nf) {
+  nf = false;
+  u = 0;
+  c = 0;
+  if (bad) return;
+  c = cl(j);
+  u = score_key(scores[j], c, nf);
+}
+
+// zero the level histogram
+__global__ __launch_bounds__(256) void sel_init_kernel(unsigned long long* __restrict__ hist) {
+  hist[threadIdx.x] = 0;
+}
+
+// level 0: the cost of the items of each top digit; flags NaN, infinite or negative scores
+__global__ __launch_bounds__(256) void sel_key_kernel(const float* __restrict__ scores, CostLookup cl, int M,
+                                                      unsigned long long* __restrict__ hist,
+                                                      int32_t* __restrict__ info) {
+  __shared__ unsigned long long hc[256];
+  hc[threadIdx.x] = 0;
+  __syncthreads();
+  const bool bad = *info == int32_t(LRC_EINVAL);
+  bool any_nf = false;
+  uint32_t cd = 0;
+  unsigned long long cc = 0;
+  for (int64_t base = int64_t(blockIdx.x) * SEL_PER; base < M; base += int64_t(gridDim.x) * SEL_PER) {
+#pragma unroll 4
+    for (int i = 0; i < SEL_RR; ++i) {
+      const int64_t j = base + i * 256 + threadIdx.x;
+      if (j < M) {
+        uint64_t u;
+        int64_t c;
+        bool nf;
+        sel_item(scores, cl, j, bad, u, c, nf);
+        any_nf |= nf;
+        sel_run_add(hc, cd, cc, uint32_t(u >> 56), c);
+      }
+    }
+  }
+  sel_flush(hc, cd, cc, hist);
+  if (any_nf) atomicExch(info, int32_t(LRC_ENONFINITE));
+}
+
+// level 1: over the items of the chosen top-digit bucket, the cost of each next digit
+__global__ __launch_bounds__(256) void sel_hist_kernel(const float* __restrict__ scores, CostLookup cl, int M,
+                                                       const int32_t* __restrict__ info,
+                                                       const uint64_t* __restrict__ sel,
+                                                       unsigned long long* __restrict__ rows) {
+  if (sel[2] != 0) return;
+  const bool bad = *info == int32_t(LRC_EINVAL);
+  __shared__ unsigned long long hc[256];
+  const uint64_t pre = sel[0];   // 8 bits
+  hc[threadIdx.x] = 0;
+  __syncthreads();
+  uint32_t cd = 0;
+  unsigned long long cc = 0;
+  for (int64_t base = int64_t(blockIdx.x) * SEL_PER; base < M; base += int64_t(gridDim.x) * SEL_PER) {
+#pragma unroll 4
+    for (int i = 0; i < SEL_RR; ++i) {
+      const int64_t j = base + i * 256 + threadIdx.x;
+      if (j < M) {
+        uint64_t u;
+        int64_t c;
+        bool nf;
+        sel_item(scores, cl, j, bad, u, c, nf);
+        if ((u >> 56) == pre) sel_run_add(hc, cd, cc, uint32_t(u >> 48) & 255u, c);
+      }
+    }
+  }
+  sel_flush_row(hc, cd, cc, rows);
+}
+
+// level 2 over every item, writing the items of the chosen 16-bit bucket to the candidate
+// list: wave w of tile k writes its matches to [k SEL_PER + w SEL_WQ, ...) and their count
+// to ccnt[4 k + w]
+constexpr int SEL_WQ = SEL_PER / 4;   // items of a tile owned by one wave
+__global__ __launch_bounds__(256) void sel_hist_compact_kernel(const float* __restrict__ scores, CostLookup cl,
+                                                               int M, const int32_t* __restrict__ info,
+                                                               const uint64_t* __restrict__ sel,
+                                                               unsigned long long* __restrict__ rows,
+                                                               uint64_t* __restrict__ ckeys,
+                                                               uint32_t* __restrict__ cids,
+                                                               uint32_t* __restrict__ ccnt) {
+  if (sel[2] != 0) return;
+  __shared__ unsigned long long hc[256];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const uint64_t pre = sel[0];   // 16 bits
+  const bool bad = *info == int32_t(LRC_EINVAL);
+  const uint64_t below = (uint64_t(1) << lane) - 1;
+  hc[t] = 0;
+  __syncthreads();
+  uint32_t cd = 0;
+  unsigned long long cc = 0;
+  for (int64_t base = int64_t(blockIdx.x) * SEL_PER; base < M; base += int64_t(gridDim.x) * SEL_PER) {
+    const int64_t region = base + wave * SEL_WQ;
+    uint32_t filled = 0;   // the same in every lane of the wave
+#pragma unroll 4
+    for (int i = 0; i < SEL_RR; ++i) {
+      const int64_t j = base + i * 256 + t;
+      uint64_t u = 0;
+      int64_t c = 0;
+      bool nf;
+      if (j < M) sel_item(scores, cl, j, bad, u, c, nf);
+      const bool m = j < M && (u >> 48) == pre;
+      const uint64_t bal = __ballot(m);
+      if (m) {
+        const int64_t p = region + filled + __popcll(bal & below);
+        ckeys[p] = u;
+        cids[p] = uint32_t(j);
+        sel_run_add(hc, cd, cc, uint32_t(u >> 40) & 255u, c);
+      }
+      filled += uint32_t(__popcll(bal));
+    }
+    if (lane == 0) ccnt[(base / SEL_PER) * 4 + wave] = filled;
+  }
+  sel_flush_row(hc, cd, cc, rows);
+}
+
+// key levels 3 to 7 (idlevel < 0) and id levels 0 to 3 (idlevel >= 0: candidates whose key
+// equals the selected key, digits of the id), over the candidate regions only
+__global__ __launch_bounds__(256) void sel_hist_cand_kernel(const uint64_t* __restrict__ ckeys,
+                                                            const uint32_t* __restrict__ cids,
+                                                            const uint32_t* __restrict__ ccnt, int M, CostLookup cl,
+                                                            int level, int idlevel, const uint64_t* __restrict__ sel,
+                                                            const uint64_t* __restrict__ seli,
+                                                            unsigned long long* __restrict__ hist) {
+  if (sel[2] != 0) return;
+  __shared__ unsigned long long hc[256];
+  hc[threadIdx.x] = 0;
+  __syncthreads();
+  uint32_t cd = 0;
+  unsigned long long cc = 0;
+  const bool by_id = idlevel >= 0;
+  const int shift = by_id ? 24 - 8 * idlevel : 56 - 8 * level;   // ids: 24 .. 0; keys: 32 .. 0
+  const uint64_t ks = sel[0];
+  const uint64_t pre = by_id ? (idlevel == 0 ? 0 : seli[0]) : ks;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int64_t base = int64_t(blockIdx.x) * SEL_PER; base < M; base += int64_t(gridDim.x) * SEL_PER) {
+    // wave w reads the candidates of the tile's quarter w
+    const int64_t r0 = base + wave * SEL_WQ;
+    const int64_t end = r0 + ccnt[(base / SEL_PER) * 4 + wave];
+    for (int64_t p = r0 + lane; p < end; p += 64) {
+      const uint64_t u = ckeys[p];
+      const uint64_t id = cids[p];
+      if (by_id) {
+        if (u == ks && (id >> (shift + 8)) == pre) sel_run_add(hc, cd, cc, uint32_t(id >> shift) & 255u, cl(id));
+      } else if ((u >> (shift + 8)) == pre) {
+        sel_run_add(hc, cd, cc, uint32_t(u >> shift) & 255u, cl(id));
+      }
+    }
+  }
+  sel_flush(hc, cd, cc, hist);
+}
+
+// One workgroup, thread t owning digit t: fix the digit whose bucket carries the running
+// cost past the budget and carry the cost of the buckets below it; the histogram is
+// cleared for the next level.  Key levels (idlevel < 0) update sel: at level 0 a pool that
+// fits whole sets sel[2].  Id levels update seli, starting from the cost carried below the
+// selected key.  Below level 0 a chosen bucket's digits split its cost exactly, so exactly
+// one digit crosses.
+__global__ __launch_bounds__(256) void sel_step_kernel(unsigned long long* __restrict__ hist, int level, int idlevel,
+                                                       int64_t budget, uint64_t* __restrict__ sel,
+                                                       uint64_t* __restrict__ seli) {
+  __shared__ int64_t wsum[4];
+  __shared__ uint64_t cur[3];   // prefix, cost below, pool fits
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  if (t == 0) {
+    if (idlevel < 0) {
+      cur[0] = level == 0 ? 0 : sel[0];
+      cur[1] = level == 0 ? 0 : sel[1];
+      cur[2] = level == 0 ? 0 : sel[2];
+    } else {
+      cur[0] = idlevel == 0 ? 0 : seli[0];
+      cur[1] = idlevel == 0 ? sel[1] : seli[1];
+      cur[2] = sel[2];
+    }
+  }
+  const int64_t v = int64_t(hist[t]);
+  hist[t] = 0;
+  __syncthreads();
+  if (cur[2] != 0) return;
+  int64_t inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t x = __shfl_up(inc, o);
+    if (lane >= o) inc += x;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  int64_t below = int64_t(cur[1]) + inc - v;
+  for (int w = 0; w < wave; ++w) below += wsum[w];
+  uint64_t* out = idlevel < 0 ? sel : seli;
+  if (below <= budget && below + v > budget) {
+    out[0] = (cur[0] << 8) | uint64_t(t);
+    out[1] = uint64_t(below);
+    if (idlevel < 0) out[2] = 0;
+  } else if (idlevel < 0 && level == 0 && t == 255 && below + v <= budget) {
+    sel[0] = 0;
+    sel[1] = uint64_t(below + v);
+    sel[2] = 1;
+  }
+}
+
+// The cut for the mask: the selected key and the first excluded id among its items.
+__global__ void sel_cut_kernel(const uint64_t* __restrict__ sel, const uint64_t* __restrict__ seli, int M,
+                               const int32_t* __restrict__ info, uint64_t* __restrict__ cutkey) {
+  if (*info != 0) {   // rejected inputs: nothing kept
+    cutkey[0] = 0;
+    cutkey[1] = 0;
+  } else if (sel[2] != 0) {   // the whole pool fits
+    cutkey[0] = ~uint64_t(0);
+    cutkey[1] = uint64_t(M);
+  } else {
+    cutkey[0] = sel[0];
+    cutkey[1] = seli[0];
+  }
+}
+
+// n_kept = the sum of the mask workgroups' kept counts (one workgroup, fixed order)
+__global__ __launch_bounds__(256) void sum_parts_kernel(const int64_t* __restrict__ part, int n,
+                                                        int64_t* __restrict__ out) {
+  __shared__ int64_t red[4];
+  int64_t s = 0;
+  for (int i = threadIdx.x; i < n; i += 256) s += part[i];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) *out = red[0] + red[1] + red[2] + red[3];
 }
 
 __global__ __launch_bounds__(256) void ranks_kernel(const uint8_t* __restrict__ kept, const int64_t* __restrict__ offs,
@@ -517,6 +847,11 @@ struct AWs {
   int64_t* ctab;
   int64_t *bsum, *cut;
   uint64_t* cutkey;
+  unsigned long long* sel_hist;   // 256 digit sums of one select level
+  uint64_t *sel, *seli;           // select states (key, id)
+  uint32_t* ccnt;                 // candidate count per wave of a select tile
+  unsigned long long* sel_rows;   // per-workgroup digit sums of a select level
+  int64_t* mpart;                 // kept count per mask workgroup
 };
 
 // sort geometry: tiles of RT rr items, runs of tpb tiles per sort workgroup
@@ -538,8 +873,11 @@ AWs carve_alloc(Carve& cv, int64_t M) {
   const int64_t nsb = std::max<int64_t>(1, cdiv(M, STILE));
   AWs w;
   w.ka = cv.take<uint64_t>(size_t(std::max<int64_t>(M, 1)));
-  w.kb = cv.take<uint64_t>(size_t(std::max<int64_t>(M, 1)));
-  w.va = cv.take<uint32_t>(size_t(std::max<int64_t>(M, 1)));
+  // kb and va also hold the select's candidate list, laid out by tile quarters: rounded
+  // up to whole tiles
+  const int64_t m_tiles = std::max<int64_t>(1, cdiv(M, SEL_PER)) * SEL_PER;
+  w.kb = cv.take<uint64_t>(size_t(m_tiles));
+  w.va = cv.take<uint32_t>(size_t(m_tiles));
   w.vb = cv.take<uint32_t>(size_t(std::max<int64_t>(M, 1)));
   w.hist = cv.take<uint32_t>(size_t(256 * nblk));
   w.rowtot = cv.take<uint32_t>(256);
@@ -548,6 +886,13 @@ AWs carve_alloc(Carve& cv, int64_t M) {
   w.bsum = cv.take<int64_t>(size_t(nsb));
   w.cut = cv.take<int64_t>(2);
   w.cutkey = cv.take<uint64_t>(2);
+  w.sel_hist = cv.take<unsigned long long>(256);
+  w.sel = cv.take<uint64_t>(4);
+  w.seli = cv.take<uint64_t>(4);
+  w.ccnt = cv.take<uint32_t>(size_t(4 * std::max<int64_t>(1, cdiv(M, SEL_PER))));
+  w.sel_rows = cv.take<unsigned long long>(size_t(256) * size_t(std::min<int64_t>(
+      std::max<int64_t>(1, cdiv(M, SEL_PER)), SEL_MAX_BLOCKS)));
+  w.mpart = cv.take<int64_t>(size_t(std::max<int64_t>(1, cdiv(M, MASK_PER))));
   return w;
 }
 
@@ -574,7 +919,7 @@ lrc_status alloc_check_args(const float* scores, const int64_t* offsets, const i
     return LRC_EINVAL;
   if (n_mat <= 0 || n_mat > (int64_t(1) << 30) || n_items < 0 || n_items >= (int64_t(1) << 31) || budget < 0)
     return LRC_EINVAL;
-  if (n_items > 0 && (scores == nullptr || order == nullptr || kept_mask == nullptr)) return LRC_EINVAL;
+  if (n_items > 0 && (scores == nullptr || kept_mask == nullptr)) return LRC_EINVAL;   // order may be null
   return LRC_OK;
 }
 
@@ -594,6 +939,43 @@ lrc_status allocate_impl(const float* scores, const int64_t* offsets, const int6
     mtab_kernel<<<unsigned(cdiv(nbk + 1, 256)), 256, 0, st>>>(offsets, cost, nm, M, nbk, w.mtab, w.ctab);
     LRC_LAUNCHED();
     const CostLookup cl{offsets, w.mtab, w.ctab, cost};
+    const int nsb = int(cdiv(M, STILE));
+    if (order == nullptr) {   // no order wanted: select the cut instead of sorting
+      const unsigned nsel = unsigned(std::min<int64_t>(cdiv(M, SEL_PER), SEL_MAX_BLOCKS));
+      sel_init_kernel<<<1, 256, 0, st>>>(w.sel_hist);
+      LRC_LAUNCHED();
+      sel_key_kernel<<<nsel, 256, 0, st>>>(scores, cl, M, w.sel_hist, info);
+      LRC_LAUNCHED();
+      // key levels, then the id levels among the items of the selected key; candidates:
+      // keys in kb, ids in va
+      for (int level = 0; level < 12; ++level) {
+        const int kl = level < 8 ? level : -1, il = level < 8 ? -1 : level - 8;
+        if (level == 1)
+          sel_hist_kernel<<<nsel, 256, 0, st>>>(scores, cl, M, info, w.sel, w.sel_rows);
+        else if (level == 2)
+          sel_hist_compact_kernel<<<nsel, 256, 0, st>>>(scores, cl, M, info, w.sel, w.sel_rows, w.kb, w.va, w.ccnt);
+        if (level == 1 || level == 2) {
+          LRC_LAUNCHED();
+          sel_reduce_kernel<<<SEL_REDUCE_BLOCKS, 256, 0, st>>>(w.sel_rows, int(nsel), w.sel, w.sel_hist);
+        }
+        else if (level > 2)
+          sel_hist_cand_kernel<<<nsel, 256, 0, st>>>(w.kb, w.va, w.ccnt, M, cl, kl, il, w.sel, w.seli,
+                                                     w.sel_hist);
+        if (level > 0) LRC_LAUNCHED();
+        sel_step_kernel<<<1, 256, 0, st>>>(w.sel_hist, kl, il, budget, w.sel, w.seli);
+        LRC_LAUNCHED();
+      }
+      sel_cut_kernel<<<1, 1, 0, st>>>(w.sel, w.seli, M, info, w.cutkey);
+      LRC_LAUNCHED();
+      const int nmask = int(cdiv(M, MASK_PER));
+      mask_kernel<<<unsigned(nmask), 256, 0, st>>>(scores, cl, M, w.cutkey, info, kept_mask, w.mpart);
+      LRC_LAUNCHED();
+      sum_parts_kernel<<<1, 256, 0, st>>>(w.mpart, nmask, n_kept);
+      LRC_LAUNCHED();
+      ranks_kernel<<<unsigned(nm), 256, 0, st>>>(kept_mask, offsets, n_items, info, ranks);
+      LRC_LAUNCHED();
+      return LRC_OK;
+    }
     key_kernel<<<unsigned(cdiv(M, KEY_PER)), 256, 0, st>>>(scores, cl, M, w.ka, w.va, info);
     LRC_LAUNCHED();
     const SortGeom sg = sort_geom(M);
@@ -621,7 +1003,6 @@ lrc_status allocate_impl(const float* scores, const int64_t* offsets, const int6
       std::swap(kin, kout);
       std::swap(vin, vout);
     }
-    const int nsb = int(cdiv(M, STILE));
     cost_bsum_kernel<<<unsigned(nsb), 256, 0, st>>>(order, cl, M, w.bsum);
     LRC_LAUNCHED();
     cost_cut_block_kernel<<<1, 1024, 0, st>>>(w.bsum, nsb, M, budget, w.cut, n_kept);
@@ -630,7 +1011,7 @@ lrc_status allocate_impl(const float* scores, const int64_t* offsets, const int6
     LRC_LAUNCHED();
     cut_key_kernel<<<1, 1, 0, st>>>(scores, cl, order, M, n_kept, info, w.cutkey);
     LRC_LAUNCHED();
-    mask_kernel<<<unsigned(cdiv(M, MASK_PER)), 256, 0, st>>>(scores, cl, M, w.cutkey, info, kept_mask);
+    mask_kernel<<<unsigned(cdiv(M, MASK_PER)), 256, 0, st>>>(scores, cl, M, w.cutkey, info, kept_mask, nullptr);
     LRC_LAUNCHED();
   } else {
     set_i64_kernel<<<1, 1, 0, st>>>(n_kept, 0);

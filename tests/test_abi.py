@@ -128,6 +128,9 @@ def test_allocate_ranks_validation(lib):
     assert f(FAKE, None, FAKE, 2, 10, 5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == EINVAL
     need = lib.lrc_allocate_ranks_workspace(2, 10)
     assert f(FAKE, FAKE, FAKE, 2, 10, 5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == EWORKSPACE
+    # order may be null (the cut is then selected without sorting); the mask may not
+    assert f(FAKE, FAKE, FAKE, 2, 10, 5, None, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == EWORKSPACE
+    assert f(FAKE, FAKE, FAKE, 2, 10, 5, None, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None) == EINVAL
 
 
 def test_rank_scores_validation(lib):

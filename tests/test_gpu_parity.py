@@ -717,25 +717,38 @@ def test_kfac_scores(lrc):
 
 
 # ----------------------------------------------------------------------------- a7 allocation
-def _alloc_case(lrc, scores_list, costs, budget):
+def _alloc_case(lrc, scores_list, costs, budget, want_order=True):
+    """The allocation of a pool on the device and by the oracle.  With want_order False the
+    library selects the cut without sorting and the returned order is None."""
     offs = np.concatenate([[0], np.cumsum([len(s) for s in scores_list])]).astype(np.int64)
     flat = np.concatenate(scores_list).astype(np.float32) if scores_list else np.zeros(0, np.float32)
     order, n_kept, ranks, kept, info = lrc.lrc_allocate_ranks(
         torch.tensor(flat, device=dev()), torch.tensor(offs, device=dev()),
-        torch.tensor(np.asarray(costs, np.int64), device=dev()), budget)
+        torch.tensor(np.asarray(costs, np.int64), device=dev()), budget, want_order=want_order)
     ref = oracle.allocate(scores_list, costs, budget)
-    return (to_np(order), int(to_np(n_kept)[0]), to_np(ranks), to_np(kept), int(to_np(info)[0])), ref
+    return (to_np(order) if want_order else None, int(to_np(n_kept)[0]), to_np(ranks), to_np(kept),
+            int(to_np(info)[0])), ref
 
 
-def test_allocate_golden_fixture(lrc):
-    got, ref = _alloc_case(lrc, [np.array([10, 1], np.float32), np.array([16, 8, 8, 0.8], np.float32)], [5, 8], 22)
+def _same_order(got, ref):
+    return got[0] is None or got[0].tolist() == ref[0].tolist()
+
+
+WANT_ORDER = pytest.mark.parametrize("want_order", [True, False], ids=["sort", "select"])
+
+
+@WANT_ORDER
+def test_allocate_golden_fixture(lrc, want_order):
+    got, ref = _alloc_case(lrc, [np.array([10, 1], np.float32), np.array([16, 8, 8, 0.8], np.float32)], [5, 8], 22,
+                           want_order)
     assert got[4] == 0
-    assert got[0].tolist() == [0, 2, 3, 4, 1, 5] == ref[0].tolist()
+    assert ref[0].tolist() == [0, 2, 3, 4, 1, 5] and _same_order(got, ref)
     assert got[1] == 3 and got[2].tolist() == [1, 2] and got[3].tolist() == [1, 0, 1, 1, 0, 0]
 
 
+@WANT_ORDER
 @pytest.mark.parametrize("seed", range(6))
-def test_allocate_bit_exact_random(lrc, seed):
+def test_allocate_bit_exact_random(lrc, seed, want_order):
     """Identical fp32 score arrays into both sides: order, n_kept, ranks and mask equal."""
     rng = np.random.default_rng(seed)
     nm = int(rng.integers(1, 40))
@@ -749,24 +762,27 @@ def test_allocate_bit_exact_random(lrc, seed):
         lst.append(s)
     total = sum(int(c) * int(z) for c, z in zip(costs, sizes))
     budget = int(rng.integers(0, total + 1)) if total else 0
-    got, ref = _alloc_case(lrc, lst, costs, budget)
+    got, ref = _alloc_case(lrc, lst, costs, budget, want_order)
     assert got[4] == 0
-    assert got[0].tolist() == ref[0].tolist()
+    assert _same_order(got, ref)
     assert got[1] == ref[1]
     assert got[2].tolist() == ref[2].tolist()
     assert got[3].tolist() == ref[3].tolist()
 
 
-def test_allocate_large_ties(lrc):
+@WANT_ORDER
+def test_allocate_large_ties(lrc, want_order):
     """Tens of thousands of items (several sort tiles), keys drawn from 50 values."""
     rng = np.random.default_rng(9)
     lst = [rng.integers(0, 50, 9000).astype(np.float32) for _ in range(7)]
     costs = [8192, 8192, 8192, 8192, 15104, 15104, 15104]
-    got, ref = _alloc_case(lrc, lst, costs, 200_000_000)
-    assert got[0].tolist() == ref[0].tolist() and got[1] == ref[1] and got[2].tolist() == ref[2].tolist()
+    got, ref = _alloc_case(lrc, lst, costs, 200_000_000, want_order)
+    assert _same_order(got, ref) and got[1] == ref[1] and got[2].tolist() == ref[2].tolist()
+    assert got[3].tolist() == ref[3].tolist()
 
 
-def test_allocate_many_tiles_skewed(lrc):
+@WANT_ORDER
+def test_allocate_many_tiles_skewed(lrc, want_order):
     """About a million items (hundreds of sort tiles and a ragged last tile): half the keys
     share one value, the rest are spread over a few hundred values, so whole tiles fall
     into one digit and the stable order of equal keys spans tiles."""
@@ -779,9 +795,9 @@ def test_allocate_many_tiles_skewed(lrc):
         s[rng.random(sizes[m]) < 0.5] = np.float32(costs[m])   # key exactly 1.0
         lst.append(s)
     total = sum(c * int(z) for c, z in zip(costs, sizes))
-    got, ref = _alloc_case(lrc, lst, costs, total // 3)
+    got, ref = _alloc_case(lrc, lst, costs, total // 3, want_order)
     assert got[4] == 0
-    assert got[0].tolist() == ref[0].tolist()
+    assert _same_order(got, ref)
     assert got[1] == ref[1] and got[2].tolist() == ref[2].tolist() and got[3].tolist() == ref[3].tolist()
 
 
@@ -816,39 +832,103 @@ def test_allocate_runs_of_tiles_per_workgroup(lrc):
     mask[ref_order[:ref_kept]] = 1
     assert np.array_equal(to_np(kept), mask)
     assert np.array_equal(to_np(ranks), np.bincount(ref_order[:ref_kept] // per, minlength=n_mat).astype(np.int32))
+    # the selection without an order reaches the same cut on the same pool
+    _, n_kept2, ranks2, kept2, info2 = lrc.lrc_allocate_ranks(
+        torch.tensor(s, device=dev()), torch.tensor(offs, device=dev()), torch.tensor(costs, device=dev()), budget,
+        want_order=False)
+    assert int(to_np(info2)[0]) == 0 and int(to_np(n_kept2)[0]) == ref_kept
+    assert np.array_equal(to_np(kept2), mask) and np.array_equal(to_np(ranks2), to_np(ranks))
 
 
-def test_allocate_edge_cases(lrc):
+def test_allocate_select_64m_items(lrc):
+    """The benchmark's scaled pool, 16384 matrices x 4096 uniform scores (67,108,864 items,
+    costs 8192 and 15104, 60% budget), both ways: the sort and the order-free selection
+    give the same n_kept, ranks and mask, and the kept set is checked against the plain
+    definition on the host: every kept (key, id) lies below every excluded one in the
+    order (key descending, id ascending), the kept cost fits the budget and adding the
+    first excluded item would not."""
+    n_mat, per = 16384, 4096
+    m_items = n_mat * per
+    costs = np.where(np.arange(n_mat) % 2 == 0, 8192, 15104).astype(np.int64)
+    g = torch.Generator(device=dev()).manual_seed(64)
+    sc = torch.rand(m_items, generator=g, device=dev())
+    offs = torch.arange(0, m_items + 1, per, dtype=torch.int64, device=dev())
+    cost_item = np.repeat(costs, per)
+    budget = int(0.6 * int(cost_item.sum()))
+    order, n_kept, ranks, kept, info = lrc.lrc_allocate_ranks(sc, offs, torch.tensor(costs, device=dev()), budget)
+    _, n_kept2, ranks2, kept2, info2 = lrc.lrc_allocate_ranks(sc, offs, torch.tensor(costs, device=dev()), budget,
+                                                              want_order=False)
+    assert int(to_np(info)[0]) == 0 == int(to_np(info2)[0])
+    nk = int(to_np(n_kept)[0])
+    assert nk == int(to_np(n_kept2)[0])
+    mask = to_np(kept).astype(bool)
+    assert np.array_equal(mask, to_np(kept2).astype(bool)) and np.array_equal(to_np(ranks), to_np(ranks2))
+    del order
+    key = to_np(sc).astype(np.float64) / cost_item.astype(np.float64)
+    assert int(mask.sum()) == nk
+    kept_cost = int(cost_item[mask].sum())
+    assert kept_cost <= budget
+    kk, ek = key[mask], key[~mask]
+    lo = kk.min()
+    assert ek.max() <= lo
+    ids = np.arange(m_items)
+    tie_ex = ids[~mask][ek == lo]
+    if tie_ex.size:   # excluded items with the smallest kept key come after every kept one
+        assert tie_ex.min() > ids[mask][kk == lo].max()
+    first_ex = tie_ex.min() if tie_ex.size else ids[~mask][ek == ek.max()].min()
+    assert kept_cost + int(cost_item[first_ex]) > budget
+    assert np.array_equal(to_np(ranks), mask.reshape(n_mat, per).sum(1).astype(np.int32))
+
+
+@WANT_ORDER
+def test_allocate_edge_cases(lrc, want_order):
     # zero budget keeps nothing, a budget above the total keeps everything
     lst = [np.array([1, 2, 3], np.float32), np.zeros(0, np.float32), np.array([5], np.float32)]
-    got, ref = _alloc_case(lrc, lst, [3, 4, 5], 0)
-    assert got[1] == 0 == ref[1] and got[2].tolist() == [0, 0, 0]
-    got, ref = _alloc_case(lrc, lst, [3, 4, 5], 10 ** 12)
-    assert got[1] == 4 == ref[1] and got[2].tolist() == [3, 0, 1]
-    # -0.0 and +0.0 are the same key
-    got, ref = _alloc_case(lrc, [np.array([0.0, -0.0, 0.0], np.float32)], [2], 4)
-    assert got[0].tolist() == ref[0].tolist() == [0, 1, 2]
+    got, ref = _alloc_case(lrc, lst, [3, 4, 5], 0, want_order)
+    assert got[1] == 0 == ref[1] and got[2].tolist() == [0, 0, 0] and got[3].tolist() == [0, 0, 0, 0]
+    got, ref = _alloc_case(lrc, lst, [3, 4, 5], 10 ** 12, want_order)
+    assert got[1] == 4 == ref[1] and got[2].tolist() == [3, 0, 1] and got[3].tolist() == [1, 1, 1, 1]
+    # a budget equal to the total keeps everything, one less drops the last in the order
+    got, ref = _alloc_case(lrc, lst, [3, 4, 5], 14, want_order)
+    assert got[1] == 4 == ref[1]
+    got, ref = _alloc_case(lrc, lst, [3, 4, 5], 13, want_order)
+    assert got[1] == ref[1] and got[3].tolist() == ref[3].tolist()
+    # -0.0 and +0.0 are the same key; equal keys are kept in id order
+    got, ref = _alloc_case(lrc, [np.array([0.0, -0.0, 0.0], np.float32)], [2], 4, want_order)
+    assert ref[0].tolist() == [0, 1, 2] and _same_order(got, ref)
+    assert got[1] == 2 and got[3].tolist() == [1, 1, 0]
+    # every score zero (one key over the whole pool), several sort tiles
+    got, ref = _alloc_case(lrc, [np.zeros(5000, np.float32), np.zeros(3000, np.float32)], [7, 7], 7 * 4321,
+                           want_order)
+    assert got[1] == 4321 == ref[1] and got[2].tolist() == [4321, 0] and got[3].tolist() == ref[3].tolist()
+    # no items at all
+    got, ref = _alloc_case(lrc, [np.zeros(0, np.float32)], [3], 10, want_order)
+    assert got[1] == 0 and got[2].tolist() == [0]
 
 
+@WANT_ORDER
 @pytest.mark.parametrize("bad", [float("nan"), float("inf"), float("-inf"), -1.0])
-def test_allocate_rejects_invalid_scores(lrc, bad):
+def test_allocate_rejects_invalid_scores(lrc, bad, want_order):
     """A score that is NaN, infinite or negative is rejected (LRC_ENONFINITE) and nothing is
     kept, like the oracle's allocator, which raises on the same input."""
     flat = torch.tensor([1.0, bad, 2.0], device=dev())
     offs = torch.tensor([0, 3], dtype=torch.int64, device=dev())
     _, n_kept, ranks, kept, info = lrc.lrc_allocate_ranks(flat, offs,
-                                                          torch.tensor([4], dtype=torch.int64, device=dev()), 10)
+                                                          torch.tensor([4], dtype=torch.int64, device=dev()), 10,
+                                                          want_order=want_order)
     assert int(info[0]) == lrc.LRC_ENONFINITE
     assert int(n_kept[0]) == 0 and int(ranks[0]) == 0 and int(kept.sum()) == 0
     with pytest.raises(ValueError):
         oracle.allocate([to_np(flat)], [4], 10)
 
 
-def test_allocate_rejects_bad_cost(lrc):
+@WANT_ORDER
+def test_allocate_rejects_bad_cost(lrc, want_order):
     flat = torch.tensor([1.0, 2.0, 2.0], device=dev())
     offs = torch.tensor([0, 3], dtype=torch.int64, device=dev())
     _, n_kept, ranks, kept, info = lrc.lrc_allocate_ranks(flat, offs,
-                                                          torch.tensor([0], dtype=torch.int64, device=dev()), 10)
+                                                          torch.tensor([0], dtype=torch.int64, device=dev()), 10,
+                                                          want_order=want_order)
     assert int(info[0]) == lrc.LRC_EINVAL
     assert int(n_kept[0]) == 0 and int(ranks[0]) == 0 and int(kept.sum()) == 0
 
