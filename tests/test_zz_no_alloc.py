@@ -2,7 +2,8 @@
 workspace entry point (lrc_allocate_ranks), both called through the C ABI on the same
 inputs: identical order, n_kept, ranks, kept_mask and info (integer results, bit for
 bit), on two calls in a row with the second on a smaller pool, and the size limit
-reported as LRC_EWORKSPACE."""
+reported as LRC_EWORKSPACE; and the same entry point without the order (the selected cut)
+against the sort."""
 import ctypes
 
 import numpy as np
@@ -71,6 +72,26 @@ def test_noalloc_matches_workspace_entry_point(lrc):
     small = _inputs(rng, 9, 700, dev, tie_heavy=False)
     r2 = _run_both(lrc, small, dev)
     assert int(r2[4][0]) == 0
+
+
+def test_noalloc_without_order_matches_sort(lrc):
+    """order = NULL (the cut selected without sorting) through the allocation-free entry
+    point: n_kept, ranks, kept_mask and info equal the workspace entry point's sort, on
+    two calls in a row with the second on a smaller pool."""
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(6)
+    for inp in (_inputs(rng, 224, 8192, dev, tie_heavy=True), _inputs(rng, 9, 700, dev, tie_heavy=False)):
+        scores, offs, cost, n_mat, M, budget = inp
+        ref = _run_both(lrc, inp, dev)
+        got = _outputs(M, n_mat, dev)
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        st = lrc.lib.lrc_allocate_ranks_noalloc(_p(scores), _p(offs), _p(cost), n_mat, M, budget, None,
+                                                *[_p(t) for t in got[1:]], stream)
+        assert st == 0
+        torch.cuda.synchronize()
+        assert int(got[0][0]) == -1   # order untouched
+        for a, b in zip(ref[1:], got[1:]):
+            assert torch.equal(a, b)
 
 
 def test_noalloc_limit(lrc):
