@@ -582,14 +582,14 @@ def passes(lrc, torch, dev):
                                         "GB/s": round(byt / tq / 1e9, 1),
                                         "hbm_frac": round(byt / tq / 1e9 / HBM_PEAK_GBS, 4)}
         # the same cut without the order (radix select weighted by cost): bytes per item are
-        # the scores read by the three full select levels and the mask pass (4 x 4 B), the
-        # mask written (1 B) and read by the rank count (1 B); the candidate list of the
-        # later levels (a few percent of the items) is left out
+        # the scores read by the three full select levels and the mask pass (4 x 4 B) and
+        # the mask written (1 B; the mask pass also counts the ranks); the candidate list of
+        # the later levels (a few percent of the items) is left out
         sel = lambda: lrc.lrc_allocate_ranks(scores, offs, cost, budget, want_order=False)
         sel()
         t = _time(sel, torch, 5)
         tq = _time_queued(sel, torch, 20)
-        byt = m_items * (4 * 4.0 + 2.0)
+        byt = m_items * (4 * 4.0 + 1.0)
         out[f"allocation_{m_items}_no_order"] = {
             "workload": f"{m_items} components ({label}), n_kept/ranks/mask only", "ms": round(t * 1e3, 3),
             "ms_queued": round(tq * 1e3, 4), "items_per_s": round(m_items / tq, 1), "GB/s": round(byt / tq / 1e9, 1),

@@ -126,16 +126,19 @@ __device__ __forceinline__ uint64_t item_key(const float* __restrict__ scores, c
   return score_key(scores[j], cl(j), nonfinite);
 }
 
-__global__ void alloc_check_kernel(const int64_t* __restrict__ offs, const int64_t* __restrict__ cost, int n_mat,
-                                   int64_t M, int32_t* __restrict__ info) {
-  // one workgroup: offsets start at 0, end at M, never decrease; every cost is > 0
-  __shared__ int bad;
-  if (threadIdx.x == 0) bad = (offs[0] != 0 || offs[n_mat] != M) ? 1 : 0;
-  __syncthreads();
-  for (int m = threadIdx.x; m < n_mat; m += blockDim.x)
-    if (offs[m + 1] < offs[m] || cost[m] <= 0) atomicOr(&bad, 1);
-  __syncthreads();
-  if (threadIdx.x == 0) *info = bad ? int32_t(LRC_EINVAL) : 0;
+// argument checks on the device, in two launches: the offsets start at 0 and end at M
+// (info = 0 or LRC_EINVAL), then one thread per matrix: offsets never decrease and every
+// cost is > 0 (a wave that finds a failure sets LRC_EINVAL once)
+__global__ void alloc_check_ends_kernel(const int64_t* __restrict__ offs, int n_mat, int64_t M,
+                                        int32_t* __restrict__ info) {
+  *info = (offs[0] != 0 || offs[n_mat] != M) ? int32_t(LRC_EINVAL) : 0;
+}
+__global__ __launch_bounds__(256) void alloc_check_kernel(const int64_t* __restrict__ offs,
+                                                          const int64_t* __restrict__ cost, int n_mat,
+                                                          int32_t* __restrict__ info) {
+  const int64_t m = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const bool bad = m < n_mat && (offs[m + 1] < offs[m] || cost[m] <= 0);
+  if (__ballot(bad) != 0 && (threadIdx.x & 63) == 0) atomicExch(info, int32_t(LRC_EINVAL));
 }
 
 // KEY_PER items per workgroup, consecutive lanes on consecutive items
@@ -464,6 +467,10 @@ __global__ __launch_bounds__(256) void cost_cut_kernel(const int32_t* __restrict
 }
 
 __global__ void set_i64_kernel(int64_t* __restrict__ p, int64_t v) { *p = v; }
+__global__ __launch_bounds__(256) void zero_i32_kernel(int32_t* __restrict__ p, int n) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
 
 // The cut for the mask: key bits and id of the first excluded item E, so that the kept
 // items are exactly those whose (key bits, id) pair is below E's.  (~0, M) keeps every
@@ -493,18 +500,23 @@ __global__ void cut_key_kernel(const float* __restrict__ scores, CostLookup cl,
 
 // kept_mask in item order: an item is kept when its (key bits, id) pair is below the cut's.
 // The key is recomputed here so that the mask is written in item order rather than
-// scattered through the order.  With part given, part[workgroup] = its kept count.
-// MASK_PER items per workgroup, consecutive lanes on consecutive items.
+// scattered through the order.  With part given, part[workgroup] = its kept count, and the
+// kept items are also counted into rank_acc (zeroed before) per matrix: a workgroup's
+// items are one bucket of the cost table, so a bucket inside one matrix adds its count
+// with one atomic, and a bucket across matrix boundaries adds each kept item to its own
+// matrix.  MASK_PER items per workgroup, consecutive lanes on consecutive items.
 constexpr int MASK_PER = 256 * 16;
+static_assert(MASK_PER == (1 << MB_SHIFT), "a mask workgroup is one bucket of the cost table");
 __global__ __launch_bounds__(256) void mask_kernel(const float* __restrict__ scores, CostLookup cl, int M,
                                                    const uint64_t* __restrict__ cutkey,
                                                    const int32_t* __restrict__ info, uint8_t* __restrict__ kept,
-                                                   int64_t* __restrict__ part) {
+                                                   int64_t* __restrict__ part, int32_t* __restrict__ rank_acc) {
   const uint64_t ck = cutkey[0];
   const int64_t cid = int64_t(cutkey[1]);
   const bool bad = *info == int32_t(LRC_EINVAL);
   const int64_t base = int64_t(blockIdx.x) * MASK_PER;
   int nk = 0;
+  uint32_t kbits = 0;   // which of this thread's items were kept
 #pragma unroll 4
   for (int i = 0; i < MASK_PER / 256; ++i) {
     const int64_t j = base + i * 256 + threadIdx.x;
@@ -514,15 +526,26 @@ __global__ __launch_bounds__(256) void mask_kernel(const float* __restrict__ sco
       const bool k = key < ck || (key == ck && j < cid);
       kept[j] = k ? 1 : 0;
       nk += k;
+      kbits |= uint32_t(k) << i;
     }
   }
   if (part != nullptr) {
     __shared__ int wn[4];
+    const bool one_matrix = cl.ctab[blockIdx.x] >= 0;
+    if (!one_matrix && kbits != 0) {
+      for (int i = 0; i < MASK_PER / 256; ++i)
+        if ((kbits >> i) & 1u)
+          atomicAdd(&rank_acc[matrix_of_item(cl.offs, cl.mtab, base + i * 256 + threadIdx.x)], 1);
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) nk += __shfl_xor(nk, o);
     if ((threadIdx.x & 63) == 0) wn[threadIdx.x >> 6] = nk;
     __syncthreads();
-    if (threadIdx.x == 0) part[blockIdx.x] = wn[0] + wn[1] + wn[2] + wn[3];
+    if (threadIdx.x == 0) {
+      const int tot = wn[0] + wn[1] + wn[2] + wn[3];
+      part[blockIdx.x] = tot;
+      if (one_matrix && tot != 0) atomicAdd(&rank_acc[cl.mtab[blockIdx.x]], tot);
+    }
   }
 }
 
@@ -932,7 +955,9 @@ lrc_status allocate_impl(const float* scores, const int64_t* offsets, const int6
   const int M = int(n_items);
   const int nm = int(n_mat);
 
-  alloc_check_kernel<<<1, 256, 0, st>>>(offsets, cost, nm, n_items, info);
+  alloc_check_ends_kernel<<<1, 1, 0, st>>>(offsets, nm, n_items, info);
+  LRC_LAUNCHED();
+  alloc_check_kernel<<<unsigned(cdiv(int64_t(nm), 256)), 256, 0, st>>>(offsets, cost, nm, info);
   LRC_LAUNCHED();
   if (M > 0) {
     const int nbk = int((int64_t(M) - 1) >> MB_SHIFT) + 1;
@@ -943,6 +968,8 @@ lrc_status allocate_impl(const float* scores, const int64_t* offsets, const int6
     if (order == nullptr) {   // no order wanted: select the cut instead of sorting
       const unsigned nsel = unsigned(std::min<int64_t>(cdiv(M, SEL_PER), SEL_MAX_BLOCKS));
       sel_init_kernel<<<1, 256, 0, st>>>(w.sel_hist);
+      LRC_LAUNCHED();
+      zero_i32_kernel<<<unsigned(cdiv(int64_t(nm), 256)), 256, 0, st>>>(ranks, nm);   // counted by the mask pass
       LRC_LAUNCHED();
       sel_key_kernel<<<nsel, 256, 0, st>>>(scores, cl, M, w.sel_hist, info);
       LRC_LAUNCHED();
@@ -968,11 +995,9 @@ lrc_status allocate_impl(const float* scores, const int64_t* offsets, const int6
       sel_cut_kernel<<<1, 1, 0, st>>>(w.sel, w.seli, M, info, w.cutkey);
       LRC_LAUNCHED();
       const int nmask = int(cdiv(M, MASK_PER));
-      mask_kernel<<<unsigned(nmask), 256, 0, st>>>(scores, cl, M, w.cutkey, info, kept_mask, w.mpart);
+      mask_kernel<<<unsigned(nmask), 256, 0, st>>>(scores, cl, M, w.cutkey, info, kept_mask, w.mpart, ranks);
       LRC_LAUNCHED();
       sum_parts_kernel<<<1, 256, 0, st>>>(w.mpart, nmask, n_kept);
-      LRC_LAUNCHED();
-      ranks_kernel<<<unsigned(nm), 256, 0, st>>>(kept_mask, offsets, n_items, info, ranks);
       LRC_LAUNCHED();
       return LRC_OK;
     }
@@ -1011,7 +1036,8 @@ lrc_status allocate_impl(const float* scores, const int64_t* offsets, const int6
     LRC_LAUNCHED();
     cut_key_kernel<<<1, 1, 0, st>>>(scores, cl, order, M, n_kept, info, w.cutkey);
     LRC_LAUNCHED();
-    mask_kernel<<<unsigned(cdiv(M, MASK_PER)), 256, 0, st>>>(scores, cl, M, w.cutkey, info, kept_mask, nullptr);
+    mask_kernel<<<unsigned(cdiv(M, MASK_PER)), 256, 0, st>>>(scores, cl, M, w.cutkey, info, kept_mask, nullptr,
+                                                             nullptr);
     LRC_LAUNCHED();
   } else {
     set_i64_kernel<<<1, 1, 0, st>>>(n_kept, 0);
