@@ -517,12 +517,21 @@ __global__ __launch_bounds__(256) void mask_kernel(const float* __restrict__ sco
   const int64_t base = int64_t(blockIdx.x) * MASK_PER;
   int nk = 0;
   uint32_t kbits = 0;   // which of this thread's items were kept
-#pragma unroll 4
+  // every score of the thread loaded before any is used; the workgroup's items are one
+  // bucket of the cost table, so their cost is looked up once when they share a matrix
+  float sv[MASK_PER / 256];
+#pragma unroll
+  for (int i = 0; i < MASK_PER / 256; ++i) {
+    const int64_t j = base + i * 256 + threadIdx.x;
+    sv[i] = j < M ? scores[j] : 0.f;
+  }
+  const int64_t ct = bad ? 0 : cl.ctab[blockIdx.x];
+#pragma unroll
   for (int i = 0; i < MASK_PER / 256; ++i) {
     const int64_t j = base + i * 256 + threadIdx.x;
     if (j < M) {
-      bool nf;
-      const uint64_t key = item_key(scores, cl, j, bad, nf);
+      bool nf = false;
+      const uint64_t key = bad ? 0 : score_key(sv[i], ct >= 0 ? ct : cl(j), nf);
       const bool k = key < ck || (key == ck && j < cid);
       kept[j] = k ? 1 : 0;
       nk += k;
@@ -531,7 +540,7 @@ __global__ __launch_bounds__(256) void mask_kernel(const float* __restrict__ sco
   }
   if (part != nullptr) {
     __shared__ int wn[4];
-    const bool one_matrix = cl.ctab[blockIdx.x] >= 0;
+    const bool one_matrix = ct >= 0;
     if (!one_matrix && kbits != 0) {
       for (int i = 0; i < MASK_PER / 256; ++i)
         if ((kbits >> i) & 1u)
@@ -609,17 +618,31 @@ __global__ __launch_bounds__(256) void sel_reduce_kernel(const unsigned long lon
   if (v != 0) atomicAdd(&hist[threadIdx.x], v);
 }
 
-// key bits and cost of item j as every select pass sees them (the keys are recomputed from
-// the scores in each full pass rather than stored: 4 bytes read per item instead of 8, and
-// no 8-byte write); rejected offsets or costs give every item key 0 and cost 0
-__device__ __forceinline__ void sel_item(const float* __restrict__ scores, const CostLookup& cl, int64_t j, bool bad,
+// A full select pass loads its thread's SEL_RR scores of a tile before using any (all the
+// loads in flight at once), and looks the tile's cost up once: a tile is one bucket of the
+// cost table, so ctab[tile] is the cost of every item when they share a matrix, else -1.
+// The keys are recomputed from the scores in each full pass rather than stored (4 bytes
+// read per item instead of 8, and no 8-byte write); rejected offsets or costs give every
+// item key 0 and cost 0.
+__device__ __forceinline__ int64_t sel_load_tile(const float* __restrict__ scores, const CostLookup& cl, int M,
+                                                 int64_t base, bool bad, float (&sv)[SEL_PER / 256]) {
+#pragma unroll
+  for (int i = 0; i < SEL_PER / 256; ++i) {
+    const int64_t j = base + i * 256 + threadIdx.x;
+    sv[i] = j < M ? scores[j] : 0.f;
+  }
+  return bad ? 0 : cl.ctab[base >> MB_SHIFT];
+}
+
+// key bits and cost of item j from its loaded score (the same as item_key's)
+__device__ __forceinline__ void sel_item(float sc, int64_t ct, const CostLookup& cl, int64_t j, bool bad,
                                          uint64_t& u, int64_t& c, bool& nf) {
   nf = false;
   u = 0;
   c = 0;
   if (bad) return;
-  c = cl(j);
-  u = score_key(scores[j], c, nf);
+  c = ct >= 0 ? ct : cl(j);
+  u = score_key(sc, c, nf);
 }
 
 // zero the level histogram
@@ -639,14 +662,16 @@ __global__ __launch_bounds__(256) void sel_key_kernel(const float* __restrict__ 
   uint32_t cd = 0;
   unsigned long long cc = 0;
   for (int64_t base = int64_t(blockIdx.x) * SEL_PER; base < M; base += int64_t(gridDim.x) * SEL_PER) {
-#pragma unroll 4
+    float sv[SEL_RR];
+    const int64_t ct = sel_load_tile(scores, cl, M, base, bad, sv);
+#pragma unroll
     for (int i = 0; i < SEL_RR; ++i) {
       const int64_t j = base + i * 256 + threadIdx.x;
       if (j < M) {
         uint64_t u;
         int64_t c;
         bool nf;
-        sel_item(scores, cl, j, bad, u, c, nf);
+        sel_item(sv[i], ct, cl, j, bad, u, c, nf);
         any_nf |= nf;
         sel_run_add(hc, cd, cc, uint32_t(u >> 56), c);
       }
@@ -670,14 +695,16 @@ __global__ __launch_bounds__(256) void sel_hist_kernel(const float* __restrict__
   uint32_t cd = 0;
   unsigned long long cc = 0;
   for (int64_t base = int64_t(blockIdx.x) * SEL_PER; base < M; base += int64_t(gridDim.x) * SEL_PER) {
-#pragma unroll 4
+    float sv[SEL_RR];
+    const int64_t ct = sel_load_tile(scores, cl, M, base, bad, sv);
+#pragma unroll
     for (int i = 0; i < SEL_RR; ++i) {
       const int64_t j = base + i * 256 + threadIdx.x;
       if (j < M) {
         uint64_t u;
         int64_t c;
         bool nf;
-        sel_item(scores, cl, j, bad, u, c, nf);
+        sel_item(sv[i], ct, cl, j, bad, u, c, nf);
         if ((u >> 56) == pre) sel_run_add(hc, cd, cc, uint32_t(u >> 48) & 255u, c);
       }
     }
@@ -709,13 +736,15 @@ __global__ __launch_bounds__(256) void sel_hist_compact_kernel(const float* __re
   for (int64_t base = int64_t(blockIdx.x) * SEL_PER; base < M; base += int64_t(gridDim.x) * SEL_PER) {
     const int64_t region = base + wave * SEL_WQ;
     uint32_t filled = 0;   // the same in every lane of the wave
-#pragma unroll 4
+    float sv[SEL_RR];
+    const int64_t ct = sel_load_tile(scores, cl, M, base, bad, sv);
+#pragma unroll
     for (int i = 0; i < SEL_RR; ++i) {
       const int64_t j = base + i * 256 + t;
       uint64_t u = 0;
       int64_t c = 0;
       bool nf;
-      if (j < M) sel_item(scores, cl, j, bad, u, c, nf);
+      if (j < M) sel_item(sv[i], ct, cl, j, bad, u, c, nf);
       const bool m = j < M && (u >> 48) == pre;
       const uint64_t bal = __ballot(m);
       if (m) {
