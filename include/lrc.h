@@ -213,13 +213,14 @@ size_t lrc_score_components_workspace(int64_t n_tokens, int64_t d_in, int64_t d_
  * cumulative cost is <= budget.
  * Outputs (device): order[M] (int32 item ids in sorted order), n_kept (one int64),
  *   ranks[n_mat] (int32 kept count per matrix), kept_mask[M] (uint8 0/1),
- *   order may be NULL: the library then finds the first excluded item by a radix select
- *   weighted by cost instead of sorting the pool (same n_kept, ranks and kept_mask, bit
- *   for bit),
  *   info (one int32: 0 ok, LRC_ENONFINITE if a score is NaN/Inf or negative,
  *   LRC_EINVAL if a cost is <= 0 or offsets are inconsistent).  A call with nonzero info
  *   keeps nothing: n_kept = 0, kept_mask and ranks all zero (order is still a
  *   permutation, with no meaning).
+ * order may be NULL (here and in lrc_allocate_ranks_noalloc): the library then finds the
+ *   first excluded item by a radix select weighted by cost instead of sorting the pool,
+ *   and writes the same n_kept, ranks, kept_mask and info bit for bit, with the same
+ *   workspace.  The kept set depends only on that item, so no order is needed for it.
  * Identical inputs give identical outputs bit for bit.  M must be < 2^31.
  */
 lrc_status lrc_allocate_ranks(const float* scores, const int64_t* offsets, const int64_t* cost,
